@@ -1,0 +1,156 @@
+"""Float64 references for block-scaled FP8 GEMM, D = C + A @ B^T.  Test infrastructure only.
+
+Follows the plain definition on the pages:
+  * page "02 · DeepGEMM 技术解析" §2.2: per 128-long K block the low-precision
+    partial is multiplied by scale_a * scale_b and added into an FP32 final
+    accumulator that starts at 0; §1.1: activations carry one FP32 scale per
+    1x128 K group, weights one per 128x128 block.
+  * page "第13章 DeepGEMM" §13.3: ``fp8_gemm_nt`` computes D = C + A @ B.T with A
+    row-major [M, K] and B stored [N, K]; the algorithm box accumulates
+    ``scale_x * scale_w * (x_block @ w_block.T)`` per K tile.
+  * page "第13章 DeepGEMM" §13.6: M-grouped GEMM is the per-expert loop
+    ``y[idx] += expert(x[idx])`` with only M grouped (N and K fixed).
+  * page "02 · DeepGEMM 技术解析" §5.2: the masked layout computes only the
+    valid rows of each group.
+
+Each block partial ``P_b = dec(A_b) @ dec(B_b)^T`` is exact in float64 whatever
+order the library matmul sums it in: every product of two E4M3 values is a
+multiple of 2^-18 below 2^18, so any partial sum of up to 2^13 of them is an
+integer number of 2^-18 units below 2^53.  The FP32 scale product is exact in
+float64 (24 + 24 significand bits); ``(sa * sb) * P_b`` and the sum over
+blocks round once each.
+
+The scale arguments are the plain logical layouts (not the MN-major device
+layout): ``sa[i, b]`` per row and K block, ``sb[jb, b]`` per weight block
+(``jb = j // gran_n``; ``gran_n`` is 128 for 128x128 weight blocks and 1 for
+per-row weight scales).  K need not be a multiple of 128: the last block is
+then shorter.
+"""
+import numpy as np
+
+from .codecs import e4m3_decode
+
+BLOCK_K = 128
+
+
+def _sf_k(K):
+    return (K + BLOCK_K - 1) // BLOCK_K
+
+
+def expand_scales_b(sb, N, gran_n):
+    """Weight scales [ceil(N / gran_n), sf_k] -> one row per output column [N, sf_k]."""
+    sb = np.asarray(sb, dtype=np.float64)
+    return sb[np.arange(N) // gran_n]
+
+
+def gemm_nt(a_codes, sa, b_codes, sb, gran_n=128, c=None, want_abs=False):
+    """Dense NT reference.
+
+    a_codes: uint8 [M, K] E4M3 codes; sa: [M, sf_k] scales (any float dtype).
+    b_codes: uint8 [N, K]; sb: [ceil(N / gran_n), sf_k].
+    c: None or [M, N].
+    Returns D float64 [M, N]; with ``want_abs`` also T[i, j] = sum_k |A'_ik * B'_jk|
+    (A', B' the dequantized values), which the tolerances are stated against.
+    """
+    A = e4m3_decode(a_codes)
+    B = e4m3_decode(b_codes)
+    M, K = A.shape
+    N = B.shape[0]
+    assert B.shape[1] == K
+    sf_k = _sf_k(K)
+    sa = np.asarray(sa, dtype=np.float64)
+    assert sa.shape == (M, sf_k)
+    sbe = expand_scales_b(sb, N, gran_n)
+    assert sbe.shape == (N, sf_k)
+    D = np.zeros((M, N), dtype=np.float64)
+    T = np.zeros((M, N), dtype=np.float64) if want_abs else None
+    for b in range(sf_k):
+        ks = slice(b * BLOCK_K, min((b + 1) * BLOCK_K, K))
+        P = A[:, ks] @ B[:, ks].T                      # exact block partial
+        S = sa[:, b][:, None] * sbe[:, b][None, :]     # exact scale product
+        D += S * P
+        if want_abs:
+            T += np.abs(S) * (np.abs(A[:, ks]) @ np.abs(B[:, ks]).T)
+    if c is not None:
+        D = np.asarray(c, dtype=np.float64) + D
+    return (D, T) if want_abs else D
+
+
+def gemm_nt_points(a_codes, sa, b_codes, sb, ii, jj, gran_n=128, c=None, chunk=4096):
+    """The same definition evaluated only at output positions (ii[p], jj[p]).
+
+    Returns (D, T) as float64 vectors.  Used for sampled checks at sizes where
+    the full product would take too long.
+    """
+    ii = np.asarray(ii, dtype=np.int64)
+    jj = np.asarray(jj, dtype=np.int64)
+    K = a_codes.shape[1]
+    sf_k = _sf_k(K)
+    sa = np.asarray(sa, dtype=np.float64)
+    sb = np.asarray(sb, dtype=np.float64)
+    Kp = sf_k * BLOCK_K
+    D = np.empty(len(ii), dtype=np.float64)
+    T = np.empty(len(ii), dtype=np.float64)
+    for s in range(0, len(ii), chunk):
+        i = ii[s:s + chunk]
+        j = jj[s:s + chunk]
+        prod = np.zeros((len(i), Kp), dtype=np.float64)
+        prod[:, :K] = e4m3_decode(a_codes[i]) * e4m3_decode(b_codes[j])
+        blk = prod.reshape(len(i), sf_k, BLOCK_K)
+        P = blk.sum(axis=2)                             # exact block partials
+        Pabs = np.abs(blk).sum(axis=2)
+        S = sa[i] * sb[j // gran_n]                     # [n, sf_k], exact
+        D[s:s + chunk] = (S * P).sum(axis=1)
+        T[s:s + chunk] = (np.abs(S) * Pabs).sum(axis=1)
+    if c is not None:
+        D = np.asarray(c, dtype=np.float64)[ii, jj] + D
+    return D, T
+
+
+def grouped_contiguous(a_codes, sa, b_codes, sb, grouped_layout, gran_n=128, want_abs=False):
+    """M-grouped contiguous reference: rows of A concatenated by group.
+
+    a_codes [sumM, K], sa [sumM, sf_k]; b_codes [G, N, K], sb [G, nb, sf_k];
+    grouped_layout [sumM] int: the group of each row, negative = no output.
+    Returns D [sumM, N] float64 with NaN in rows that produce no output.
+    """
+    gl = np.asarray(grouped_layout)
+    G, N, _ = b_codes.shape
+    M = a_codes.shape[0]
+    D = np.full((M, N), np.nan)
+    T = np.full((M, N), np.nan) if want_abs else None
+    for g in range(G):                      # the per-expert loop
+        idx = np.nonzero(gl == g)[0]
+        if len(idx) == 0:
+            continue
+        r = gemm_nt(a_codes[idx], np.asarray(sa)[idx], b_codes[g], sb[g], gran_n,
+                    want_abs=want_abs)
+        if want_abs:
+            D[idx], T[idx] = r
+        else:
+            D[idx] = r
+    return (D, T) if want_abs else D
+
+
+def grouped_masked(a_codes, sa, b_codes, sb, masked_m, gran_n=128, want_abs=False):
+    """M-grouped masked reference: A [G, M_max, K]; only rows i < masked_m[g] are valid.
+
+    sa [G, M_max, sf_k]; b_codes [G, N, K]; sb [G, nb, sf_k].
+    masked_m[g] is clamped to [0, M_max].  Returns D [G, M_max, N] with NaN
+    in rows that produce no output.
+    """
+    G, Mmax, _ = a_codes.shape
+    N = b_codes.shape[1]
+    D = np.full((G, Mmax, N), np.nan)
+    T = np.full((G, Mmax, N), np.nan) if want_abs else None
+    for g in range(G):
+        m = int(min(max(int(masked_m[g]), 0), Mmax))
+        if m == 0:
+            continue
+        r = gemm_nt(a_codes[g, :m], np.asarray(sa)[g, :m], b_codes[g], sb[g], gran_n,
+                    want_abs=want_abs)
+        if want_abs:
+            D[g, :m], T[g, :m] = r
+        else:
+            D[g, :m] = r
+    return (D, T) if want_abs else D

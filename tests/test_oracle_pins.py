@@ -1,0 +1,328 @@
+"""Pins for the float64 oracle: each oracle function is checked against
+something other than itself -- closed forms, worked examples printed on the
+pages (tests/golden/), exact rational brute force on tiny inputs, library
+routines on special cases, and invariants.  CPU only."""
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import codecs, layout, gemm
+from tests import gen
+from tests.tolerance import check_bf16, check_fp32
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rows(name):
+    out = []
+    for line in open(os.path.join(GOLDEN, name)):
+        line = line.strip()
+        if line and not line.startswith("#"):
+            out.append(line.split())
+    return out
+
+
+# ---------------------------------------------------------------- E4M3 decode
+def test_e4m3_hand_values():
+    t = codecs.e4m3_decode_table()
+    assert t[0x38] == 1.0
+    assert t[0x7E] == 448.0 and t[0xFE] == -448.0
+    assert t[0x08] == 2.0 ** -6          # smallest normal
+    assert t[0x01] == 2.0 ** -9          # smallest subnormal
+    assert t[0x07] == 7 * 2.0 ** -9      # largest subnormal
+    assert t[0x00] == 0.0 and np.signbit(t[0x80])
+    assert np.isnan(t[0x7F]) and np.isnan(t[0xFF])
+    assert np.isnan(t).sum() == 2
+
+
+def test_e4m3_table_matches_torch():
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    ref = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    t = codecs.e4m3_decode_table()
+    same = (t == ref) | (np.isnan(t) & np.isnan(ref))
+    assert same.all()
+
+
+# ---------------------------------------------------------------- UE8M0
+@pytest.mark.parametrize("fixture", ["ue8m0_examples.txt", "ue8m0_closed_form.txt"])
+def test_ue8m0_examples(fixture):
+    for val, code, dec, bad in _rows(fixture):
+        x = np.float32(float(val))
+        c = codecs.ue8m0_encode(np.array([x]))[0]
+        assert int(c) == int(code), (val, c)
+        assert codecs.ue8m0_decode(np.array([c]))[0] == float(dec)
+        assert bool(codecs.pow2_violation(np.array([x]))[0]) == bool(int(bad))
+
+
+def test_ue8m0_special_codes():
+    assert np.isnan(codecs.ue8m0_decode(np.array([255], np.uint8))[0])
+    assert codecs.ue8m0_decode(np.array([0], np.uint8))[0] == 0.0
+    # every code 1..254 decodes to 2^(code - 127)
+    c = np.arange(1, 255, dtype=np.uint8)
+    assert (codecs.ue8m0_decode(c) == np.ldexp(1.0, c.astype(np.int32) - 127)).all()
+
+
+# ---------------------------------------------------------------- BF16 RNE
+def _bf16_exact(x):
+    """Correct RNE of a float64 to BF16 by exact rationals (brute force)."""
+    if x == 0:
+        return 0x8000 if np.signbit(x) else 0
+    sign = 0x8000 if x < 0 else 0
+    fx = abs(Fraction(x))
+    e = -126
+    while fx >= Fraction(2) ** (e + 1):
+        e += 1
+    while e > -126 and fx < Fraction(2) ** e:
+        e -= 1
+    sp = Fraction(2) ** (e - 7)
+    q = fx / sp
+    fl = q.numerator // q.denominator
+    rem = q - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    val = fl * sp
+    if val > Fraction(2) ** 127 * (2 - Fraction(1, 128)):
+        return sign | 0x7F80
+    bits = int(np.float32(float(val)).view(np.uint32)) >> 16
+    return sign | bits
+
+
+def test_bf16_constructed_ties():
+    cases = [(1 + 2.0 ** -8, 0x3F80), (1 + 3 * 2.0 ** -8, 0x3F82), (1 + 2.0 ** -8 + 2.0 ** -30, 0x3F81),
+             (-(1 + 2.0 ** -8), 0xBF80), (0.0, 0x0000), (-0.0, 0x8000),
+             ((2 - 2.0 ** -8) * 2.0 ** 127, 0x7F80),       # tie at the top rounds up to infinity
+             ((2 - 2.0 ** -7) * 2.0 ** 127, 0x7F7F),
+             (2.0 ** -133, 0x0001), (2.0 ** -134, 0x0000), (3 * 2.0 ** -135, 0x0001), (3 * 2.0 ** -134, 0x0002), (2.0 ** -134 + 2.0 ** -140, 0x0001)]
+    for x, bits in cases:
+        assert int(codecs.bf16_rne(np.array([x]))[0]) == bits, (x, hex(bits))
+
+
+def test_bf16_random_vs_exact_rationals():
+    rng = np.random.default_rng(1)
+    xs = np.concatenate([
+        rng.standard_normal(1500) * np.exp2(rng.integers(-140, 130, 1500)),
+        rng.standard_normal(300),
+        # exact ties between neighbouring BF16 values
+        (rng.integers(256, 512, 200) * 2 + 1) * np.exp2(rng.integers(-20, 20, 200) - 9.0),
+    ])
+    got = codecs.bf16_rne(xs)
+    for x, g in zip(xs, got):
+        assert int(g) == _bf16_exact(float(x)), x
+
+
+def test_bf16_matches_torch_on_float32_inputs():
+    # torch's float32 -> bfloat16 cast is a single RNE step; on float32 inputs it must agree
+    rng = np.random.default_rng(2)
+    x32 = (rng.standard_normal(100000) * np.exp2(rng.integers(-60, 60, 100000))).astype(np.float32)
+    ref = torch.from_numpy(x32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert (codecs.bf16_rne(x32.astype(np.float64)) == ref).all()
+
+
+# ---------------------------------------------------------------- layout transform
+def test_transform_hand_example_fp32():
+    # mn = 6 rows, sf_k = 5 K-blocks: align4(6) = 8, element (r, kb) lands at kb*8 + r
+    sf = np.arange(30, dtype=np.float32).reshape(6, 5) + 1      # value = 5r + kb + 1
+    out, _ = layout.transform_sf(sf, 6, 1, False)
+    assert out.shape == (5, 8)
+    flat = out.reshape(-1)
+    assert flat[0] == 1 and flat[1] == 6 and flat[5] == 26       # kb=0: rows 0, 1, 5
+    assert flat[8] == 2 and flat[8 * 4 + 5] == 30               # kb=1 row 0; kb=4 row 5
+    assert (out[:, 6:] == 0).all()                              # padding rows are 0
+
+
+def test_transform_hand_example_packed():
+    # exponents chosen so that the codes are 100 + 10r + kb
+    codes = np.array([[100 + 10 * r + kb for kb in range(5)] for r in range(6)], dtype=np.uint32)
+    sf = (codes << np.uint32(23)).view(np.float32)
+    out, cnt = layout.transform_sf(sf, 6, 1, True)
+    assert cnt == 0 and out.shape == (2, 8) and out.dtype == np.int32
+    w = out.view(np.uint32)
+    # word (r=2, q=0) = codes of K-blocks 0..3 of row 2, little-endian: 120,121,122,123
+    assert w[0, 2] == 120 | 121 << 8 | 122 << 16 | 123 << 24
+    # word (r=2, q=1): only K-block 4 exists -> byte 0 = 124, bytes 1..3 = 0
+    assert w[1, 2] == 124
+    assert (w[:, 6:] == 0).all()
+
+
+def test_transform_broadcast_gran128_and_count():
+    sf = np.array([[0.75, 1.0], [3.0, 0.5]], dtype=np.float32)   # two 128-row blocks, sf_k = 2
+    out, cnt = layout.transform_sf(sf, 200, 128, True)
+    assert cnt == 2                                             # 0.75 and 3.0 are not powers of two
+    w = out.view(np.uint32)
+    assert out.shape == (1, 200)
+    assert w[0, 0] == 126 | 127 << 8 and w[0, 127] == 126 | 127 << 8
+    assert w[0, 128] == 128 | 126 << 8 and w[0, 199] == 128 | 126 << 8
+    fp, _ = layout.transform_sf(sf, 200, 128, False)
+    assert fp.shape == (2, 200) and fp[0, 127] == np.float32(0.75) and fp[1, 128] == np.float32(0.5)
+
+
+def test_unpack_roundtrip():
+    rng = np.random.default_rng(3)
+    sf = np.exp2(rng.integers(-20, 20, size=(3, 37, 7))).astype(np.float32)
+    out, cnt = layout.transform_sf(sf, 37, 1, True)
+    assert cnt == 0
+    back = layout.unpack_ue8m0(out, 37, 7)
+    assert (back == sf).all()
+
+
+# ---------------------------------------------------------------- GEMM core vs brute force
+def _brute(a, sa, b, sb, gran_n, c=None):
+    """Exact rational value of the definition, and sum |A'B'|."""
+    M, K = a.shape
+    N = b.shape[0]
+    t = codecs.e4m3_decode_table()
+    D = np.empty((M, N))
+    T = np.empty((M, N))
+    for i in range(M):
+        for j in range(N):
+            acc = Fraction(0)
+            tot = Fraction(0)
+            for k in range(K):
+                s = Fraction(float(sa[i, k // 128])) * Fraction(float(sb[j // gran_n, k // 128]))
+                p = Fraction(float(t[a[i, k]])) * Fraction(float(t[b[j, k]])) * s
+                acc += p
+                tot += abs(p)
+            if c is not None:
+                acc += Fraction(float(c[i, j]))
+            D[i, j] = float(acc)
+            T[i, j] = float(tot)
+    return D, T
+
+
+def _random_tiny(rng, M, N, K, gran_n):
+    codes = np.concatenate([np.arange(0, 0x7F), np.arange(0x80, 0xFF)]).astype(np.uint8)  # no NaN
+    a = rng.choice(codes, size=(M, K))
+    b = rng.choice(codes, size=(N, K))
+    sf_k = (K + 127) // 128
+    sa = (rng.random((M, sf_k)) * 3 + 1e-3).astype(np.float32)
+    nb = (N + gran_n - 1) // gran_n
+    sb = (rng.random((nb, sf_k)) * 3 + 1e-3).astype(np.float32)
+    return a, sa, b, sb
+
+
+@pytest.mark.parametrize("K", [128, 256, 384, 200])
+@pytest.mark.parametrize("gran_n", [128, 1])
+def test_gemm_vs_brute_force(K, gran_n):
+    rng = np.random.default_rng(K + gran_n)
+    M, N = 5, 7
+    a, sa, b, sb = _random_tiny(rng, M, N, K, gran_n)
+    c = rng.standard_normal((M, N)).astype(np.float32)
+    D, T = gemm.gemm_nt(a, sa, b, sb, gran_n, c=c, want_abs=True)
+    Dx, Tx = _brute(a, sa, b, sb, gran_n, c)
+    assert np.all(np.abs(D - Dx) <= 2.0 ** -48 * (Tx + np.abs(c)))
+    assert np.allclose(T, Tx, rtol=1e-14, atol=0)
+    ii, jj = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
+    Dp, Tp = gemm.gemm_nt_points(a, sa, b, sb, ii.ravel(), jj.ravel(), gran_n, c=c)
+    assert np.all(np.abs(Dp - Dx.ravel()) <= 2.0 ** -48 * (Tx.ravel() + np.abs(c).ravel()))
+
+
+def test_gemm_1d2d_block_boundary_brute_force():
+    # N = 300 crosses two 128-column weight-scale boundaries; check columns around them
+    rng = np.random.default_rng(7)
+    a, sa, b, sb = _random_tiny(rng, 3, 300, 256, 128)
+    D = gemm.gemm_nt(a, sa, b, sb, 128)
+    for j in [0, 127, 128, 255, 256, 299]:
+        Dj, _ = _brute(a, sa, b[j:j + 1], sb[j // 128:j // 128 + 1], 128)
+        assert np.all(np.abs(D[:, j] - Dj[:, 0]) <= 1e-12 * np.abs(Dj[:, 0]).max())
+
+
+def test_all_ones_scales_equal_plain_fp8_matmul():
+    d = gen.tiny_dense(seed=5)
+    sa = np.ones_like(d["sa"])
+    sb = np.ones_like(d["sb"])
+    D = gemm.gemm_nt(d["a"], sa, d["b"], sb, 128)
+    ref = codecs.e4m3_decode(d["a"]) @ codecs.e4m3_decode(d["b"]).T
+    assert np.array_equal(D, ref)     # bitwise: every block partial and their sum are exact
+
+
+def test_dequantize_then_matmul_formulation():
+    # the dequantize-then-matmul statement: (A * S_A) @ (B * S_B)^T + C with the scales expanded
+    d = gen.dense(64, 300, 384, seed=6, with_c=True)
+    A = codecs.e4m3_decode(d["a"]) * np.repeat(d["sa"].astype(np.float64), 128, axis=1)[:, :384]
+    sbe = gemm.expand_scales_b(d["sb"], 300, 128)
+    B = codecs.e4m3_decode(d["b"]) * np.repeat(sbe, 128, axis=1)[:, :384]
+    ref = A @ B.T + d["c"]
+    D, T = gemm.gemm_nt(d["a"], d["sa"], d["b"], d["sb"], 128, c=d["c"], want_abs=True)
+    assert np.all(np.abs(D - ref) <= 1e-13 * (T + np.abs(d["c"])))
+
+
+def test_scale_linearity_exact_on_pow2_inputs():
+    d = gen.pow2_exact(16, 40, 512, seed=8)
+    D0 = gemm.gemm_nt(d["a"], d["sa"], d["b"], d["sb"], 128)
+    sa2 = d["sa"].copy()
+    sa2[:, 2] *= 8
+    D1 = gemm.gemm_nt(d["a"], sa2, d["b"], d["sb"], 128)
+    A = codecs.e4m3_decode(d["a"])[:, 256:384]
+    B = codecs.e4m3_decode(d["b"])[:, 256:384]
+    contrib = (d["sa"][:, 2:3].astype(np.float64) * d["sb"][0, 2]) * (A @ B.T)
+    assert np.array_equal(D1 - D0, 7 * contrib)
+
+
+def test_grouped_contiguous_vs_brute_force():
+    rng = np.random.default_rng(9)
+    G, N, K = 3, 6, 256
+    rows = np.array([0, 0, 2, 2, 2, -1, 1, 1], dtype=np.int32)   # a padding row included
+    M = len(rows)
+    a, sa, _, _ = _random_tiny(rng, M, 1, K, 128)
+    b = np.stack([_random_tiny(rng, 1, N, K, 128)[2] for _ in range(G)])
+    sb = np.stack([_random_tiny(rng, 1, N, K, 128)[3] for _ in range(G)])
+    D = gemm.grouped_contiguous(a, sa, b, sb, rows)
+    for i, g in enumerate(rows):
+        if g < 0:
+            assert np.isnan(D[i]).all()
+            continue
+        Dx, _ = _brute(a[i:i + 1], sa[i:i + 1], b[g], sb[g], 128)
+        assert np.allclose(D[i], Dx[0], rtol=1e-13, atol=0)
+
+
+def test_grouped_masked_vs_brute_force():
+    rng = np.random.default_rng(10)
+    G, Mmax, N, K = 3, 4, 5, 128
+    a = np.stack([_random_tiny(rng, Mmax, 1, K, 128)[0] for _ in range(G)])
+    sa = np.stack([_random_tiny(rng, Mmax, 1, K, 128)[1] for _ in range(G)])
+    b = np.stack([_random_tiny(rng, 1, N, K, 128)[2] for _ in range(G)])
+    sb = np.stack([_random_tiny(rng, 1, N, K, 128)[3] for _ in range(G)])
+    masked = np.array([2, 0, 9])        # 9 is clamped to M_max
+    D = gemm.grouped_masked(a, sa, b, sb, masked)
+    assert np.isnan(D[0, 2:]).all() and np.isnan(D[1]).all() and not np.isnan(D[2]).any()
+    for g, m in [(0, 2), (2, 4)]:
+        Dx, _ = _brute(a[g, :m], sa[g, :m], b[g], sb[g], 128)
+        assert np.allclose(D[g, :m], Dx, rtol=1e-13, atol=0)
+
+
+def test_per_row_weight_scales_equal_broadcast_block_scales():
+    # 1d1d per-row weight scales that repeat the 128x128 block value give the 1d2d result
+    d = gen.dense(8, 260, 256, seed=11)
+    per_row = gemm.expand_scales_b(d["sb"], 260, 128)
+    D2 = gemm.gemm_nt(d["a"], d["sa"], d["b"], d["sb"], 128)
+    D1 = gemm.gemm_nt(d["a"], d["sa"], d["b"], per_row, 1)
+    assert np.array_equal(D1, D2)
+
+
+# ---------------------------------------------------------------- the tolerance checks have teeth
+def test_tolerance_catches_planted_mistakes():
+    d = gen.dense(32, 256, 512, seed=12, with_c=True)
+    D, T = gemm.gemm_nt(d["a"], d["sa"], d["b"], d["sb"], 128, c=d["c"], want_abs=True)
+    ok, _ = check_fp32(D.astype(np.float32), D, T)
+    assert ok.all()
+    # a dropped K block
+    sa_drop = d["sa"].copy()
+    sa_drop[:, 1] = 0
+    bad = gemm.gemm_nt(d["a"], sa_drop, d["b"], d["sb"], 128, c=d["c"])
+    assert not check_fp32(bad, D, T)[0].all()
+    # the wrong weight-scale block for the second half of the columns
+    sb_wrong = d["sb"].copy()
+    sb_wrong[1] = sb_wrong[0]
+    bad = gemm.gemm_nt(d["a"], d["sa"], d["b"], sb_wrong, 128, c=d["c"])
+    assert not check_fp32(bad, D, T)[0].all()
+    # a missing C term
+    bad = gemm.gemm_nt(d["a"], d["sa"], d["b"], d["sb"], 128)
+    assert not check_fp32(bad, D, T)[0].all()
+    # BF16: correct rounding passes, a one-row shift fails
+    bits = oracle.bf16_rne(D)
+    assert check_bf16(bits, D, T)[0].all()
+    assert not check_bf16(np.roll(bits, 1, axis=0), D, T)[0].all()
