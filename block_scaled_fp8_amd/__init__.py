@@ -1,0 +1,285 @@
+"""Python binding for libdg.so, the MI355X (gfx950) block-scaled FP8 GEMM library.
+
+Argument marshalling only: every step of the computation runs in the library's
+HIP kernels.  PyTorch supplies device memory and the current stream.  The entry
+points follow the library's C ABI (include/dg.h) and the Python API the pages
+describe (page "第13章 DeepGEMM" §13.3 and §13.6): ``fp8_gemm_nt((a, sfa), (b, sfb),
+d, c=None, recipe=None)`` computes D = C + A @ B.T.
+
+Scale arguments may be given
+  * already transformed (path B of page "02 · DeepGEMM 技术解析" §3.2): an
+    MN-major tensor, i.e. shape [.., mn, sf_k] (FP32) or [.., mn, ceil(sf_k/4)]
+    (int32, packed UE8M0) with strides [.., 1, align4(mn)], as returned by
+    ``get_mn_major_tma_aligned_tensor`` / ``..._packed_ue8m0_tensor``; or
+  * raw (path A): FP32 [.., mn_blocks, sf_k] contiguous (K-major), in which case the
+    library's transform kernel converts them first, on the same stream.
+Weight scales for 128x128 blocks (recipe (1, 128, 128)) are passed untransformed,
+FP32 [.., ceil(n/128), sf_k] K-major.
+"""
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "DGError", "lib", "fp8_gemm_nt", "m_grouped_fp8_gemm_nt_contiguous", "m_grouped_fp8_gemm_nt_masked",
+    "transform_sf", "get_mn_major_tma_aligned_tensor", "get_mn_major_tma_aligned_packed_ue8m0_tensor",
+    "get_tma_aligned_size", "get_mk_alignment_for_contiguous_layout", "set_num_sms", "get_num_sms",
+    "get_gemm_config", "LIB_PATH",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdg.so")
+
+DG_OUT_BF16, DG_OUT_F32 = 1, 2
+DG_SF_F32, DG_SF_UE8M0X4 = 0, 1
+
+_i32, _i64, _p = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
+_SIGS = {
+    "dg_fp8_gemm_nt": (_i32, [_i32, _i32, _i32, _p, _i64, _p, _i64, _p, _i64, _p, _i64, _i32, _i32,
+                              _p, _i64, _p, _i64, _i32, _p]),
+    "dg_m_grouped_fp8_gemm_nt_contiguous": (_i32, [_i32, _i32, _i32, _i32, _p, _i64, _p, _i64, _p, _i64, _i64,
+                                                   _p, _i64, _i64, _i32, _i32, _p, _i64, _i32, _p, _p]),
+    "dg_m_grouped_fp8_gemm_nt_masked": (_i32, [_i32, _i32, _i32, _i32, _p, _i64, _i64, _p, _i64, _i64, _p, _i64,
+                                               _i64, _p, _i64, _i64, _i32, _i32, _p, _i64, _i64, _i32, _p, _i32, _p]),
+    "dg_transform_sf": (_i32, [_p, _i32, _i32, _i32, _i32, _i32, _p, _p, _p]),
+    "dg_get_tma_aligned_size": (_i64, [_i64, _i32]),
+    "dg_get_mk_alignment_for_contiguous_layout": (_i32, []),
+    "dg_set_num_sms": (_i32, [_i32]),
+    "dg_get_num_sms": (_i32, []),
+    "dg_get_gemm_config": (_i32, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                  ctypes.POINTER(_i32), ctypes.POINTER(_i32), ctypes.POINTER(_i32),
+                                  ctypes.POINTER(_i32)]),
+    "dg_get_last_error": (ctypes.c_char_p, []),
+}
+
+_lib = None
+
+
+class DGError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"dg status {status}: {msg}")
+        self.status = status
+
+
+def lib():
+    """Load libdg.so (raises if it has not been built: there is no fallback path)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run `python -m block_scaled_fp8_amd.build`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def _check(status):
+    if status != 0:
+        raise DGError(status, lib().dg_get_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _a4(x):
+    return (int(x) + 3) // 4 * 4
+
+
+def _codes(t):
+    if t.dtype not in (torch.uint8, torch.float8_e4m3fn):
+        raise TypeError(f"E4M3 operands must be uint8 codes or float8_e4m3fn, got {t.dtype}")
+    if t.stride(-1) != 1:
+        raise ValueError("E4M3 operands must be K-contiguous")
+    return t
+
+
+def _out_dtype(d):
+    if d.dtype == torch.bfloat16:
+        return DG_OUT_BF16
+    if d.dtype == torch.float32:
+        return DG_OUT_F32
+    raise TypeError(f"output must be bfloat16 or float32, got {d.dtype}")
+
+
+# ---------------------------------------------------------------- layout helpers
+def get_tma_aligned_size(mn, elem_bytes):
+    return int(lib().dg_get_tma_aligned_size(int(mn), int(elem_bytes)))
+
+
+def get_mk_alignment_for_contiguous_layout():
+    return int(lib().dg_get_mk_alignment_for_contiguous_layout())
+
+
+def set_num_sms(n):
+    _check(lib().dg_set_num_sms(int(n)))
+
+
+def get_num_sms():
+    return int(lib().dg_get_num_sms())
+
+
+def get_gemm_config(kind, m, n, k, num_groups=1, expected_m=0, sf_format=DG_SF_F32, gran_n=128,
+                    d_dtype=DG_OUT_BF16, num_sms=256):
+    """Tile shape the heuristic picks: (block_m, block_n, num_tiles, grid).  Host only."""
+    out = [_i32() for _ in range(4)]
+    _check(lib().dg_get_gemm_config(kind, m, n, k, num_groups, expected_m, sf_format, gran_n, d_dtype,
+                                    num_sms, *[ctypes.byref(o) for o in out]))
+    return tuple(o.value for o in out)
+
+
+def transform_sf(sf, mn, gran_mn=1, pack_ue8m0=False, nonpow2_count=None):
+    """Raw FP32 scales [(G,) mn_blocks, sf_k] -> MN-major [(G,) mn, sf_k or ceil(sf_k/4)]
+    with strides [.., 1, align4(mn)] (FP32, or int32 holding four UE8M0 codes)."""
+    if sf.dtype != torch.float32 or not sf.is_contiguous():
+        raise ValueError("raw scales must be contiguous float32")
+    squeeze = sf.dim() == 2
+    sf3 = sf.unsqueeze(0) if squeeze else sf
+    G, mnb, sf_k = sf3.shape
+    if mnb != (mn + gran_mn - 1) // gran_mn:
+        raise ValueError(f"scale rows {mnb} do not match mn={mn} at granularity {gran_mn}")
+    a4 = _a4(mn)
+    cols = (sf_k + 3) // 4 if pack_ue8m0 else sf_k
+    dt = torch.int32 if pack_ue8m0 else torch.float32
+    # allocate the whole padded buffer: the kernel writes the padding rows [mn, align4(mn)) too
+    flat = torch.empty((G * cols * a4,), dtype=dt, device=sf.device)
+    out = flat.as_strided((G, mn, cols), (cols * a4, 1, a4))
+    _check(lib().dg_transform_sf(_ptr(sf3), G, mn, sf_k, gran_mn, int(bool(pack_ue8m0)), _ptr(out),
+                                 _ptr(nonpow2_count), _stream(sf)))
+    return out[0] if squeeze else out
+
+
+def get_mn_major_tma_aligned_tensor(sf):
+    return transform_sf(sf.contiguous(), sf.shape[-2], 1, False)
+
+
+def get_mn_major_tma_aligned_packed_ue8m0_tensor(sf, gran_mn=1, mn=None):
+    sf = sf.contiguous()
+    mn = sf.shape[-2] * gran_mn if mn is None else mn
+    return transform_sf(sf, mn, gran_mn, True)
+
+
+# ---------------------------------------------------------------- scale marshalling
+def _is_mn_major(t):
+    """Shape [.., mn, cols] with strides [.., 1, align4(mn)] (the transform's output)."""
+    return t.dim() >= 2 and t.stride(-2) == 1 and (t.shape[-2] == 0 or t.stride(-1) == _a4(t.shape[-2]))
+
+
+def _act_scales(sfa, mn, sf_k, pack):
+    """Return (tensor, sf_format) for the activation scales of mn rows (per group)."""
+    if sfa.dtype == torch.int32:
+        if not _is_mn_major(sfa):
+            raise ValueError("packed UE8M0 scales must be MN-major")
+        return sfa, DG_SF_UE8M0X4
+    if sfa.dtype != torch.float32:
+        raise TypeError("scales must be float32 or int32 (packed UE8M0)")
+    if _is_mn_major(sfa) and not pack:
+        return sfa, DG_SF_F32
+    if _is_mn_major(sfa):
+        raise ValueError("cannot pack already-transformed FP32 scales; pass them raw")
+    t = transform_sf(sfa.contiguous(), mn, 1, pack)
+    return t, (DG_SF_UE8M0X4 if pack else DG_SF_F32)
+
+
+def _weight_scales(sfb, n, sf_k, gran_n, fmt):
+    """Return (tensor, stride) for the weight scales of one group."""
+    if gran_n == 128:
+        if sfb.dtype != torch.float32 or sfb.stride(-1) != 1:
+            raise ValueError("128x128 weight scales must be K-major float32 [.., ceil(n/128), sf_k]")
+        return sfb, sfb.stride(-2)
+    # per-row weight scales, MN-major
+    if fmt == DG_SF_UE8M0X4:
+        if sfb.dtype == torch.int32:
+            return sfb, sfb.stride(-1)
+        gran = 128 if sfb.shape[-2] == (n + 127) // 128 and n > 128 else 1
+        t = transform_sf(sfb.contiguous(), n, gran, True)
+        return t, t.stride(-1)
+    if _is_mn_major(sfb):
+        return sfb, sfb.stride(-1)
+    gran = 128 if sfb.shape[-2] == (n + 127) // 128 and n > 128 else 1
+    t = transform_sf(sfb.contiguous(), n, gran, False)
+    return t, t.stride(-1)
+
+
+def _recipe_gran_n(recipe, sfa, sfb, n, pack):
+    if recipe is not None:
+        if tuple(recipe) not in ((1, 128, 128), (1, 1, 128)):
+            raise ValueError(f"unsupported recipe {recipe}; use (1, 128, 128) or (1, 1, 128)")
+        return recipe[1]
+    if sfa.dtype == torch.int32 or pack or sfb.dtype == torch.int32:
+        return 1
+    if _is_mn_major(sfb) and sfb.shape[-2] == n and n > 1:
+        return 1
+    return 128
+
+
+# ---------------------------------------------------------------- GEMMs
+def fp8_gemm_nt(a, b, d, c=None, recipe=None, pack_ue8m0=False):
+    """D = C + A @ B.T.  ``a = (A [M, K], sfa)``, ``b = (B [N, K], sfb)``, ``d`` [M, N]
+    BF16 or FP32 (preallocated); ``c`` optional FP32 [M, N] (may be ``d`` itself)."""
+    A, sfa = a
+    B, sfb = b
+    _codes(A)
+    _codes(B)
+    M, K = A.shape
+    N = B.shape[0]
+    sf_k = (K + 127) // 128
+    gran_n = _recipe_gran_n(recipe, sfa, sfb, N, pack_ue8m0)
+    sfa_t, fmt = _act_scales(sfa, M, sf_k, pack_ue8m0)
+    sfb_t, sfb_stride = _weight_scales(sfb, N, sf_k, gran_n, fmt)
+    _check(lib().dg_fp8_gemm_nt(M, N, K, _ptr(A), A.stride(0), _ptr(sfa_t), sfa_t.stride(-1) if M > 0 else 0,
+                                _ptr(B), B.stride(0), _ptr(sfb_t), sfb_stride, fmt, gran_n,
+                                _ptr(c), c.stride(0) if c is not None else 0,
+                                _ptr(d), d.stride(0), _out_dtype(d), _stream(d)))
+    return d
+
+
+def m_grouped_fp8_gemm_nt_contiguous(a, b, d, grouped_layout, recipe=None, pack_ue8m0=False):
+    """Rows of A [sum M_g, K] grouped by ``grouped_layout`` (int32 [sum M_g], -1 = padding);
+    ``b = (B [G, N, K], sfb [G, ...])``; D [sum M_g, N]."""
+    A, sfa = a
+    B, sfb = b
+    _codes(A)
+    _codes(B)
+    M, K = A.shape
+    G, N, _ = B.shape
+    sf_k = (K + 127) // 128
+    gran_n = _recipe_gran_n(recipe, sfa, sfb, N, pack_ue8m0)
+    sfa_t, fmt = _act_scales(sfa, M, sf_k, pack_ue8m0)
+    sfb_t, sfb_stride = _weight_scales(sfb, N, sf_k, gran_n, fmt)
+    if grouped_layout.dtype != torch.int32 or not grouped_layout.is_contiguous():
+        raise ValueError("grouped_layout must be contiguous int32")
+    _check(lib().dg_m_grouped_fp8_gemm_nt_contiguous(
+        M, N, K, G, _ptr(A), A.stride(0), _ptr(sfa_t), sfa_t.stride(-1), _ptr(B), B.stride(1), B.stride(0),
+        _ptr(sfb_t), sfb_stride, sfb_t.stride(0), fmt, gran_n, _ptr(d), d.stride(0), _out_dtype(d),
+        _ptr(grouped_layout), _stream(d)))
+    return d
+
+
+def m_grouped_fp8_gemm_nt_masked(a, b, d, masked_m, expected_m=0, recipe=None, pack_ue8m0=False):
+    """A [G, M_max, K] with ``masked_m`` (int32 [G], device) valid rows per group;
+    ``b = (B [G, N, K], sfb [G, ...])``; D [G, M_max, N] (rows past masked_m untouched)."""
+    A, sfa = a
+    B, sfb = b
+    _codes(A)
+    _codes(B)
+    G, Mmax, K = A.shape
+    N = B.shape[1]
+    sf_k = (K + 127) // 128
+    gran_n = _recipe_gran_n(recipe, sfa, sfb, N, pack_ue8m0)
+    sfa_t, fmt = _act_scales(sfa, Mmax, sf_k, pack_ue8m0)
+    sfb_t, sfb_stride = _weight_scales(sfb, N, sf_k, gran_n, fmt)
+    if masked_m.dtype != torch.int32 or not masked_m.is_contiguous():
+        raise ValueError("masked_m must be contiguous int32")
+    _check(lib().dg_m_grouped_fp8_gemm_nt_masked(
+        G, Mmax, N, K, _ptr(A), A.stride(1), A.stride(0), _ptr(sfa_t), sfa_t.stride(-1), sfa_t.stride(0),
+        _ptr(B), B.stride(1), B.stride(0), _ptr(sfb_t), sfb_stride, sfb_t.stride(0), fmt, gran_n,
+        _ptr(d), d.stride(1), d.stride(0), _out_dtype(d), _ptr(masked_m), int(expected_m), _stream(d)))
+    return d

@@ -1,0 +1,331 @@
+// C ABI of libdg.so: argument validation, tile heuristic, persistent-grid sizing
+// and launch.  Validation runs before any HIP call, so every error path can be
+// exercised on a machine without a GPU.
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+
+#include "../../include/dg.h"
+#include "dg_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+std::atomic<int> g_num_sms_override{0};
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return DG_OK;
+}
+
+int64_t align4(int64_t x) { return (x + 3) / 4 * 4; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int device_cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return -1;
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
+  return n;
+}
+
+int env_int(const char* name, int dflt) {
+  const char* s = getenv(name);
+  return (s && *s) ? atoi(s) : dflt;
+}
+
+// ---------------------------------------------------------------- tile heuristic
+// Relative throughput of a tile shape: the operand bytes a workgroup moves per MFMA
+// fall with its arithmetic intensity BM*BN/(BM+BN), so efficiency is modelled as
+// AI / (AI + 30).  Used only to rank candidates.
+double tile_efficiency(const dg::TileCfg& t) {
+  const double ai = double(t.bm) * t.bn / double(t.bm + t.bn);
+  return ai / (ai + 30.0);
+}
+
+int tile_occupancy(const dg::TileCfg& t) {
+  // workgroups per CU: limited by the 160 KiB of LDS and by one wave per SIMD (4 SIMDs)
+  const int lds = dg::gemm_lds_bytes(int(&t - dg::kTiles));
+  const int by_lds = (160 * 1024) / lds;
+  const int waves = t.wm * t.wn;
+  const int by_simd = waves >= 4 ? 1 : 4 / waves;
+  const int occ = by_lds < by_simd ? by_lds : by_simd;
+  return occ < 1 ? 1 : occ;
+}
+
+struct Plan {
+  int tile = -1;
+  int num_m_tiles = 0, num_n_tiles = 0, tiles = 0, grid = 0;
+};
+
+// kind: 0 dense, 1 contiguous, 2 masked.  m: rows (masked: expected rows per group).
+Plan plan_gemm(int kind, int m, int n, int k, int groups, int m_max, int sfm, int out, int num_sms) {
+  Plan best;
+  double best_cost = 1e300;
+  const char* force = getenv("DG_FORCE_TILE");
+  int fbm = 0, fbn = 0;
+  if (force && sscanf(force, "%dx%d", &fbm, &fbn) != 2) fbm = fbn = 0;
+  for (int t = 0; t < dg::kNumTiles; ++t) {
+    const dg::TileCfg& c = dg::kTiles[t];
+    if (!dg::gemm_instantiated(t, sfm, kind, out)) continue;
+    if (fbm && (c.bm != fbm || c.bn != fbn)) continue;
+    const int64_t mt = (kind == 2) ? (m + c.bm - 1) / c.bm : (m + c.bm - 1) / c.bm;
+    const int64_t nt = (n + c.bn - 1) / c.bn;
+    const int64_t tiles = (kind == 2) ? int64_t(groups) * mt * nt : mt * nt;
+    const int occ = tile_occupancy(c);
+    const int64_t slots = int64_t(num_sms) * occ;
+    const int64_t waves = (tiles + slots - 1) / slots;
+    // compute time per wave of tiles ~ tile area / efficiency; occupancy shares a CU
+    double cost = double(waves) * c.bm * c.bn * occ / tile_efficiency(c);
+    // padding waste along M when the tile is much taller than the rows present
+    if (kind == 2 && m_max > 0) {
+      const double rows_done = double(mt) * c.bm;
+      cost *= 1.0 + 0.15 * (rows_done / (m > 0 ? m : 1) - 1.0);
+    }
+    if (cost < best_cost - 1e-9) {
+      best_cost = cost;
+      best.tile = t;
+      best.num_m_tiles = int(mt);
+      best.num_n_tiles = int(nt);
+      best.tiles = int(tiles);
+      const int64_t g = tiles < slots ? tiles : slots;
+      best.grid = int(g < 1 ? 1 : g);
+    }
+  }
+  return best;
+}
+
+int sf_mode_of(int32_t sf_format, int32_t gran_n) {
+  if (sf_format == DG_SF_UE8M0X4) return dg::SF_1D1D_UE8M0;
+  return gran_n == 128 ? dg::SF_1D2D_F32 : dg::SF_1D1D_F32;
+}
+
+// Checks shared by the three GEMM entry points.
+int check_common(int32_t n, int32_t k, const void* a, int64_t lda, const void* sfa, const void* b,
+                 int64_t ldb, const void* sfb, int64_t sfb_stride, int32_t sf_format, int32_t gran_n,
+                 const void* d, int64_t ldd, int32_t d_dtype) {
+  if (d_dtype != DG_OUT_BF16 && d_dtype != DG_OUT_F32) return fail(DG_ERR_DTYPE, "d_dtype %d is not DG_OUT_BF16 or DG_OUT_F32", d_dtype);
+  if (sf_format != DG_SF_F32 && sf_format != DG_SF_UE8M0X4) return fail(DG_ERR_DTYPE, "sf_format %d is not DG_SF_F32 or DG_SF_UE8M0X4", sf_format);
+  if (gran_n != 1 && gran_n != 128) return fail(DG_ERR_UNSUPPORTED, "gran_n %d: weight scales are per 128x128 block (128) or per row (1)", gran_n);
+  if (sf_format == DG_SF_UE8M0X4 && gran_n != 1)
+    return fail(DG_ERR_UNSUPPORTED, "packed UE8M0 weight scales must be broadcast per row (gran_n == 1)");
+  if (k <= 0 || k % 128 != 0) return fail(DG_ERR_SHAPE, "k = %d must be a positive multiple of 128", k);
+  if (n < 0) return fail(DG_ERR_SHAPE, "n = %d is negative", n);
+  if (!a || !sfa || !b || !sfb || !d) return fail(DG_ERR_NULL, "a, sfa, b, sfb and d must not be NULL");
+  if (lda < k || lda % 16 != 0) return fail(DG_ERR_LAYOUT, "lda = %lld must be >= k and a multiple of 16", (long long)lda);
+  if (ldb < k || ldb % 16 != 0) return fail(DG_ERR_LAYOUT, "ldb = %lld must be >= k and a multiple of 16", (long long)ldb);
+  if (lda > (int64_t(1) << 23) || ldb > (int64_t(1) << 23)) return fail(DG_ERR_LAYOUT, "lda and ldb must be <= 2^23 (tile offsets are 32-bit)");
+  if (!aligned16(a) || !aligned16(b)) return fail(DG_ERR_LAYOUT, "a and b must be 16-byte aligned");
+  if (!aligned16(sfa) || !aligned16(sfb)) return fail(DG_ERR_LAYOUT, "sfa and sfb must be 16-byte aligned");
+  const int64_t sf_k = k / 128;
+  if (gran_n == 128) {
+    if (sfb_stride < sf_k) return fail(DG_ERR_LAYOUT, "sfb_stride = %lld must be >= sf_k = %lld for 128x128 weight scales", (long long)sfb_stride, (long long)sf_k);
+  } else if (sfb_stride != align4(n)) {
+    return fail(DG_ERR_LAYOUT, "per-row weight scales must be MN-major with stride align4(n) = %lld, got %lld", (long long)align4(n), (long long)sfb_stride);
+  }
+  if (ldd < n) return fail(DG_ERR_LAYOUT, "ldd = %lld must be >= n", (long long)ldd);
+  const uintptr_t esz = d_dtype == DG_OUT_BF16 ? 2 : 4;
+  if ((reinterpret_cast<uintptr_t>(d) & (esz - 1)) != 0) return fail(DG_ERR_LAYOUT, "d is not aligned to its element size");
+  return DG_OK;
+}
+
+int do_launch(dg::GemmParams& p, int kind, int32_t m_rows_for_plan, int32_t m_max, int sfm, int out,
+              hipStream_t stream) {
+  int num_sms = g_num_sms_override.load();
+  if (num_sms <= 0) num_sms = device_cu_count();
+  if (num_sms <= 0) return fail(DG_ERR_HIP, "could not query the device's compute-unit count");
+  Plan pl = plan_gemm(kind, m_rows_for_plan, p.n, p.k, p.num_groups, m_max, sfm, out, num_sms);
+  if (pl.tile < 0) return fail(DG_ERR_UNSUPPORTED, "no tile configuration for this combination (check DG_FORCE_TILE)");
+  const dg::TileCfg& c = dg::kTiles[pl.tile];
+  p.num_n_tiles = pl.num_n_tiles;
+  if (kind == 2) {
+    // masked: the tile count is known on the device only; plan for every row present
+    const int64_t mt = (m_max + c.bm - 1) / c.bm;
+    p.num_m_tiles = int(mt);
+    const int64_t upper = int64_t(p.num_groups) * mt * p.num_n_tiles;
+    const int64_t slots = int64_t(num_sms) * tile_occupancy(c);
+    pl.grid = int(upper < slots ? (upper < 1 ? 1 : upper) : slots);
+  } else {
+    p.num_m_tiles = pl.num_m_tiles;
+  }
+  p.total_tiles = pl.tiles;
+  const int sw_default = c.bm >= 256 ? 4 : 8;
+  int sw = env_int("DG_SWIZZLE_M", sw_default);
+  if (sw < 1) sw = 1;
+  p.swizzle_m = sw < p.num_m_tiles ? sw : (p.num_m_tiles > 0 ? p.num_m_tiles : 1);
+  p.xcd_remap = (pl.grid % 8 == 0) ? 1 : 0;
+  // vector epilogue accesses need every row (and group) start 16-byte aligned
+  const int esz = out == dg::OUT_BF16 ? 2 : 4;
+  p.d_vec = (p.ldd % 4 == 0 && (p.d_gstride * esz) % 16 == 0 && aligned16(p.d)) ? 1 : 0;
+  p.c_vec = (p.c && p.ldc % 4 == 0 && aligned16(p.c)) ? 1 : 0;
+  if (env_int("DG_PRINT_CONFIGS", 0))
+    fprintf(stderr, "[dg] kind=%d m=%d n=%d k=%d groups=%d sf_mode=%d out=%d -> tile %dx%d (waves %dx%d) tiles=%d grid=%d swizzle_m=%d\n",
+            kind, p.m, p.n, p.k, p.num_groups, sfm, out, c.bm, c.bn, c.wm, c.wn, p.total_tiles, pl.grid,
+            p.swizzle_m);
+  const hipError_t e = dg::launch_gemm(p, pl.tile, sfm, kind, out, pl.grid, stream);
+  if (e != hipSuccess) return fail(DG_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int dg_fp8_gemm_nt(int32_t m, int32_t n, int32_t k, const void* a, int64_t lda, const void* sfa,
+                   int64_t sfa_stride, const void* b, int64_t ldb, const void* sfb, int64_t sfb_stride,
+                   int32_t sf_format, int32_t gran_n, const float* c, int64_t ldc, void* d, int64_t ldd,
+                   int32_t d_dtype, hipStream_t stream) {
+  if (m < 0) return fail(DG_ERR_SHAPE, "m = %d is negative", m);
+  int st = check_common(n, k, a, lda, sfa, b, ldb, sfb, sfb_stride, sf_format, gran_n, d, ldd, d_dtype);
+  if (st != DG_OK) return st;
+  if (sfa_stride != align4(m)) return fail(DG_ERR_LAYOUT, "sfa must be MN-major with stride align4(m) = %lld, got %lld", (long long)align4(m), (long long)sfa_stride);
+  if (c) {
+    if (d_dtype != DG_OUT_F32) return fail(DG_ERR_UNSUPPORTED, "a C term requires an FP32 output");
+    if (ldc < n || (reinterpret_cast<uintptr_t>(c) & 3u) != 0) return fail(DG_ERR_LAYOUT, "c needs ldc >= n and 4-byte alignment");
+    if ((const void*)c == d && ldc != ldd) return fail(DG_ERR_LAYOUT, "c aliases d, so ldc must equal ldd");
+  }
+  if (m == 0 || n == 0) return ok();
+  dg::GemmParams p{};
+  p.a = (const uint8_t*)a; p.lda = lda;
+  p.sfa = sfa; p.sfa_stride = sfa_stride;
+  p.b = (const uint8_t*)b; p.ldb = ldb;
+  p.sfb = sfb; p.sfb_stride = sfb_stride;
+  p.c = c; p.ldc = ldc;
+  p.d = d; p.ldd = ldd;
+  p.m = m; p.n = n; p.k = k; p.num_groups = 1; p.sf_k = k / 128;
+  const int out = c ? dg::OUT_F32_C : (d_dtype == DG_OUT_BF16 ? dg::OUT_BF16 : dg::OUT_F32);
+  return do_launch(p, dg::GRP_DENSE, m, 0, sf_mode_of(sf_format, gran_n), out, stream);
+}
+
+int dg_m_grouped_fp8_gemm_nt_contiguous(int32_t m_total, int32_t n, int32_t k, int32_t num_groups,
+                                        const void* a, int64_t lda, const void* sfa, int64_t sfa_stride,
+                                        const void* b, int64_t ldb, int64_t b_group_stride,
+                                        const void* sfb, int64_t sfb_stride, int64_t sfb_group_stride,
+                                        int32_t sf_format, int32_t gran_n, void* d, int64_t ldd,
+                                        int32_t d_dtype, const int32_t* grouped_layout, hipStream_t stream) {
+  if (m_total < 0) return fail(DG_ERR_SHAPE, "m_total = %d is negative", m_total);
+  if (num_groups <= 0) return fail(DG_ERR_SHAPE, "num_groups = %d must be positive", num_groups);
+  int st = check_common(n, k, a, lda, sfa, b, ldb, sfb, sfb_stride, sf_format, gran_n, d, ldd, d_dtype);
+  if (st != DG_OK) return st;
+  if (!grouped_layout) return fail(DG_ERR_NULL, "grouped_layout must not be NULL");
+  if (sfa_stride != align4(m_total)) return fail(DG_ERR_LAYOUT, "sfa must be MN-major with stride align4(m_total) = %lld, got %lld", (long long)align4(m_total), (long long)sfa_stride);
+  if (b_group_stride < int64_t(n) * ldb || b_group_stride % 16 != 0) return fail(DG_ERR_LAYOUT, "b_group_stride must be >= n*ldb and a multiple of 16");
+  const int64_t sfb_min = gran_n == 128 ? int64_t((n + 127) / 128) * sfb_stride
+                                        : (sf_format == DG_SF_UE8M0X4 ? int64_t((k / 128 + 3) / 4) : int64_t(k / 128)) * sfb_stride;
+  if (sfb_group_stride < sfb_min || (gran_n == 1 && sfb_group_stride % 4 != 0)) return fail(DG_ERR_LAYOUT, "sfb_group_stride = %lld is smaller than one group's scales (%lld) or misaligned", (long long)sfb_group_stride, (long long)sfb_min);
+  if (m_total == 0 || n == 0) return ok();
+  dg::GemmParams p{};
+  p.a = (const uint8_t*)a; p.lda = lda;
+  p.sfa = sfa; p.sfa_stride = sfa_stride;
+  p.b = (const uint8_t*)b; p.ldb = ldb; p.b_gstride = b_group_stride;
+  p.sfb = sfb; p.sfb_stride = sfb_stride; p.sfb_gstride = sfb_group_stride;
+  p.d = d; p.ldd = ldd;
+  p.grouped_layout = grouped_layout;
+  p.m = m_total; p.n = n; p.k = k; p.num_groups = num_groups; p.sf_k = k / 128;
+  const int out = d_dtype == DG_OUT_BF16 ? dg::OUT_BF16 : dg::OUT_F32;
+  return do_launch(p, dg::GRP_CONTIG, m_total, 0, sf_mode_of(sf_format, gran_n), out, stream);
+}
+
+int dg_m_grouped_fp8_gemm_nt_masked(int32_t num_groups, int32_t m_max, int32_t n, int32_t k, const void* a,
+                                    int64_t lda, int64_t a_group_stride, const void* sfa, int64_t sfa_stride,
+                                    int64_t sfa_group_stride, const void* b, int64_t ldb, int64_t b_group_stride,
+                                    const void* sfb, int64_t sfb_stride, int64_t sfb_group_stride,
+                                    int32_t sf_format, int32_t gran_n, void* d, int64_t ldd, int64_t d_group_stride,
+                                    int32_t d_dtype, const int32_t* masked_m, int32_t expected_m,
+                                    hipStream_t stream) {
+  if (num_groups <= 0) return fail(DG_ERR_SHAPE, "num_groups = %d must be positive", num_groups);
+  if (m_max < 0) return fail(DG_ERR_SHAPE, "m_max = %d is negative", m_max);
+  int st = check_common(n, k, a, lda, sfa, b, ldb, sfb, sfb_stride, sf_format, gran_n, d, ldd, d_dtype);
+  if (st != DG_OK) return st;
+  if (!masked_m) return fail(DG_ERR_NULL, "masked_m must not be NULL");
+  if (sfa_stride != align4(m_max)) return fail(DG_ERR_LAYOUT, "sfa must be MN-major with stride align4(m_max) = %lld, got %lld", (long long)align4(m_max), (long long)sfa_stride);
+  if (a_group_stride < int64_t(m_max) * lda || a_group_stride % 16 != 0) return fail(DG_ERR_LAYOUT, "a_group_stride must be >= m_max*lda and a multiple of 16");
+  if (b_group_stride < int64_t(n) * ldb || b_group_stride % 16 != 0) return fail(DG_ERR_LAYOUT, "b_group_stride must be >= n*ldb and a multiple of 16");
+  const int64_t sf_rows = sf_format == DG_SF_UE8M0X4 ? (k / 128 + 3) / 4 : k / 128;
+  if (sfa_group_stride < sf_rows * sfa_stride || sfa_group_stride % 4 != 0) return fail(DG_ERR_LAYOUT, "sfa_group_stride is smaller than one group's scales or not a multiple of 4");
+  const int64_t sfb_min = gran_n == 128 ? int64_t((n + 127) / 128) * sfb_stride : sf_rows * sfb_stride;
+  if (sfb_group_stride < sfb_min || (gran_n == 1 && sfb_group_stride % 4 != 0)) return fail(DG_ERR_LAYOUT, "sfb_group_stride is smaller than one group's scales or misaligned");
+  if (d_group_stride < int64_t(m_max) * ldd) return fail(DG_ERR_LAYOUT, "d_group_stride must be >= m_max*ldd");
+  if (m_max == 0 || n == 0) return ok();
+  dg::GemmParams p{};
+  p.a = (const uint8_t*)a; p.lda = lda; p.a_gstride = a_group_stride;
+  p.sfa = sfa; p.sfa_stride = sfa_stride; p.sfa_gstride = sfa_group_stride;
+  p.b = (const uint8_t*)b; p.ldb = ldb; p.b_gstride = b_group_stride;
+  p.sfb = sfb; p.sfb_stride = sfb_stride; p.sfb_gstride = sfb_group_stride;
+  p.d = d; p.ldd = ldd; p.d_gstride = d_group_stride;
+  p.masked_m = masked_m;
+  p.m = m_max; p.n = n; p.k = k; p.num_groups = num_groups; p.sf_k = k / 128;
+  const int out = d_dtype == DG_OUT_BF16 ? dg::OUT_BF16 : dg::OUT_F32;
+  const int em = (expected_m > 0 && expected_m < m_max) ? expected_m : m_max;
+  return do_launch(p, dg::GRP_MASKED, em, m_max, sf_mode_of(sf_format, gran_n), out, stream);
+}
+
+int dg_transform_sf(const float* sf_in, int32_t num_groups, int32_t mn, int32_t sf_k, int32_t gran_mn,
+                    int32_t pack_ue8m0, void* sf_out, int32_t* nonpow2_count, hipStream_t stream) {
+  if (num_groups <= 0 || mn < 0 || sf_k <= 0) return fail(DG_ERR_SHAPE, "need num_groups > 0, mn >= 0, sf_k > 0");
+  if (gran_mn != 1 && gran_mn != 128) return fail(DG_ERR_UNSUPPORTED, "gran_mn %d must be 1 or 128", gran_mn);
+  if (pack_ue8m0 != 0 && pack_ue8m0 != 1) return fail(DG_ERR_DTYPE, "pack_ue8m0 must be 0 or 1");
+  if (!sf_in || !sf_out) return fail(DG_ERR_NULL, "sf_in and sf_out must not be NULL");
+  if (!aligned16(sf_out)) return fail(DG_ERR_LAYOUT, "sf_out must be 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(sf_in) & 3u) != 0) return fail(DG_ERR_LAYOUT, "sf_in must be 4-byte aligned");
+  if (mn == 0) return ok();
+  const hipError_t e = dg::launch_transform_sf(sf_in, num_groups, mn, sf_k, gran_mn, pack_ue8m0, sf_out,
+                                               nonpow2_count, stream);
+  if (e != hipSuccess) return fail(DG_ERR_HIP, "transform launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int64_t dg_get_tma_aligned_size(int64_t mn, int32_t elem_bytes) {
+  if (elem_bytes != 1 && elem_bytes != 2 && elem_bytes != 4 && elem_bytes != 8 && elem_bytes != 16) return -1;
+  const int64_t al = 16 / elem_bytes;
+  return (mn + al - 1) / al * al;
+}
+
+int32_t dg_get_mk_alignment_for_contiguous_layout(void) { return 128; }
+
+int dg_set_num_sms(int32_t n) {
+  if (n < 0) return fail(DG_ERR_SHAPE, "num_sms %d is negative", n);
+  g_num_sms_override.store(n);
+  return ok();
+}
+
+int32_t dg_get_num_sms(void) {
+  const int o = g_num_sms_override.load();
+  return o > 0 ? o : device_cu_count();
+}
+
+int dg_get_gemm_config(int32_t kind, int32_t m, int32_t n, int32_t k, int32_t num_groups, int32_t expected_m,
+                       int32_t sf_format, int32_t gran_n, int32_t d_dtype, int32_t num_sms, int32_t* block_m,
+                       int32_t* block_n, int32_t* num_tiles, int32_t* grid) {
+  if (kind < 0 || kind > 2) return fail(DG_ERR_UNSUPPORTED, "kind %d must be 0, 1 or 2", kind);
+  if (m < 0 || n <= 0 || k <= 0 || k % 128 != 0 || num_sms <= 0) return fail(DG_ERR_SHAPE, "bad sizes");
+  if (d_dtype != DG_OUT_BF16 && d_dtype != DG_OUT_F32) return fail(DG_ERR_DTYPE, "bad d_dtype");
+  if (sf_format != DG_SF_F32 && sf_format != DG_SF_UE8M0X4) return fail(DG_ERR_DTYPE, "bad sf_format");
+  const int groups = kind == 0 ? 1 : (num_groups > 0 ? num_groups : 1);
+  const int em = kind == 2 ? ((expected_m > 0 && expected_m < m) ? expected_m : m) : m;
+  const int out = d_dtype == DG_OUT_BF16 ? dg::OUT_BF16 : dg::OUT_F32;
+  Plan pl = plan_gemm(kind, em, n, k, groups, kind == 2 ? m : 0, sf_mode_of(sf_format, gran_n), out, num_sms);
+  if (pl.tile < 0) return fail(DG_ERR_UNSUPPORTED, "no tile configuration");
+  if (block_m) *block_m = dg::kTiles[pl.tile].bm;
+  if (block_n) *block_n = dg::kTiles[pl.tile].bn;
+  if (num_tiles) *num_tiles = pl.tiles;
+  if (grid) *grid = pl.grid;
+  return ok();
+}
+
+const char* dg_get_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,65 @@
+// Internal interface between the host library (dg_api.cpp) and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dg {
+
+// How the weight scales are laid out and applied (page "02 · DeepGEMM 技术解析" §2.3).
+enum SfMode {
+  SF_1D2D_F32 = 0,    // sfa FP32 MN-major per row; sfb FP32 per 128x128 block, K-major
+  SF_1D1D_F32 = 1,    // sfa and sfb FP32 MN-major, one scale per row and K block
+  SF_1D1D_UE8M0 = 2,  // sfa and sfb UE8M0 packed four per int32, MN-major
+};
+
+enum GroupMode { GRP_DENSE = 0, GRP_CONTIG = 1, GRP_MASKED = 2 };
+
+enum OutMode { OUT_BF16 = 0, OUT_F32 = 1, OUT_F32_C = 2 };
+
+// Everything a GEMM launch needs.  Sizes in elements; pointers are device memory.
+struct GemmParams {
+  const uint8_t* a;
+  int64_t lda, a_gstride;
+  const void* sfa;
+  int64_t sfa_stride, sfa_gstride;
+  const uint8_t* b;
+  int64_t ldb, b_gstride;
+  const void* sfb;
+  int64_t sfb_stride, sfb_gstride;
+  const float* c;
+  int64_t ldc;
+  void* d;
+  int64_t ldd, d_gstride;
+  const int32_t* grouped_layout;  // contiguous mode
+  const int32_t* masked_m;        // masked mode
+  int32_t m;                      // dense: M; contiguous: total rows; masked: m_max
+  int32_t n, k, num_groups;
+  int32_t sf_k;
+  int32_t num_m_tiles;            // dense / contiguous (masked: per group, from m_max)
+  int32_t num_n_tiles;
+  int32_t total_tiles;            // dense / contiguous; masked computes it on the device
+  int32_t swizzle_m;              // m tiles per swizzle super-row
+  int32_t xcd_remap;              // 1: map consecutive logical workgroups onto one XCD
+  int32_t d_vec;                  // 1: D rows allow 4-element vector stores (ldd % 4 == 0, 16-B base)
+  int32_t c_vec;                  // 1: C rows allow 4-element vector loads
+};
+
+struct TileCfg {
+  int bm, bn, wm, wn;  // workgroup tile, waves along M and N
+};
+
+constexpr int kNumTiles = 9;
+extern const TileCfg kTiles[kNumTiles];
+
+// Launch the GEMM kernel instantiated for (tile, sf_mode, group, out).  Returns
+// hipErrorInvalidValue for a combination that is not instantiated.
+hipError_t launch_gemm(const GemmParams& p, int tile, int sf_mode, int group, int out, int grid,
+                       hipStream_t stream);
+bool gemm_instantiated(int tile, int sf_mode, int group, int out);
+int gemm_lds_bytes(int tile);
+
+hipError_t launch_transform_sf(const float* in, int num_groups, int mn, int sf_k, int gran_mn,
+                               int pack, void* out, int32_t* count, hipStream_t stream);
+
+}  // namespace dg

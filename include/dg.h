@@ -1,0 +1,203 @@
+/*
+ * dg.h -- C ABI of the MI355X (gfx950) block-scaled FP8 GEMM library (libdg.so).
+ *
+ * The library computes the fine-grained block-scaled FP8 GEMM
+ *
+ *     D = C + A . B^T
+ *
+ * where A holds OCP E4M3 activations with one scale per 1x128 group along K
+ * and B holds E4M3 weights with one scale per 128x128 block (or one per row
+ * and 128 K values).  K is consumed in 128-long blocks; each block's partial
+ * product is promoted into an FP32 accumulator as
+ *     final += scale_a * scale_b * partial
+ * Definitions: page "02 · DeepGEMM 技术解析" (PaperTrace) §1.1 (the
+ * quantisation recipe), §2.2 (two-level accumulation), §2.3 (1-D / 2-D weight
+ * scales), §3.1-3.2 (scale layouts and the two ways of providing them), §5.1-5.2
+ * (M-grouped contiguous and masked layouts); page "第13章 DeepGEMM：FP4 / FP8
+ * 矩阵乘法内核" §13.3 (interface D = C + A @ B.T, the "nt" naming, the
+ * algorithm box) and §13.6 (M-grouped GEMM).
+ *
+ * Conventions for every entry point
+ *  - Every data pointer is DEVICE memory owned and allocated by the caller.
+ *    The library allocates nothing and keeps no per-call state; the only
+ *    global is the persistent grid size (dg_set_num_sms).
+ *  - Strides are in ELEMENTS of the pointed-to type.  "E4M3" buffers are
+ *    bytes (uint8 codes), "F32" are float, "UE8M0x4" are int32 words each
+ *    holding four UE8M0 codes (byte t = K-block 4q+t, little-endian by K).
+ *  - sf_k = ceil(k / 128); packed_sf_k = ceil(sf_k / 4); align4(x) = 4*ceil(x/4).
+ *  - Every call is enqueued on `stream` and returns without synchronising.
+ *  - Arguments are validated on the host before any HIP call.  A bad argument
+ *    returns a negative dg_status and leaves a message for dg_get_last_error();
+ *    nothing is launched.  A failed launch returns DG_ERR_HIP.  Nothing aborts.
+ *  - Device-side anomalies are skipped, never trapped: rows whose group index
+ *    is negative or >= num_groups produce no output.
+ */
+#ifndef DG_H
+#define DG_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DG_OK = 0,
+  DG_ERR_NULL = -1,        /* a required pointer is NULL */
+  DG_ERR_DTYPE = -2,       /* unknown output dtype or scale format */
+  DG_ERR_SHAPE = -3,       /* sizes out of range or inconsistent */
+  DG_ERR_LAYOUT = -4,      /* strides / alignment do not match the contract */
+  DG_ERR_UNSUPPORTED = -5, /* a valid but unsupported combination (e.g. C with BF16 D) */
+  DG_ERR_HIP = -6          /* a HIP runtime call or launch failed */
+} dg_status;
+
+typedef enum { DG_OUT_BF16 = 1, DG_OUT_F32 = 2 } dg_out_dtype;
+typedef enum { DG_SF_F32 = 0, DG_SF_UE8M0X4 = 1 } dg_sf_format;
+
+/*
+ * Dense NT GEMM: D[m, n] = C[m, n] + sum_b sa[m, b] * sb[.., b] * sum_{k in block b} A[m, k] * B[n, k]
+ * (page "第13章 DeepGEMM" §13.3: fp8_gemm_nt computes D = C + A @ B.T).
+ *
+ *  m, n, k      : problem sizes; m, n >= 0 (0 is a no-op), k > 0 and k % 128 == 0.
+ *  a, lda       : A E4M3 [m, k], element (i, kk) at a[i*lda + kk]; k <= lda <= 2^23, lda % 16 == 0,
+ *                 a 16-byte aligned.
+ *  sfa, sfa_stride : activation scales, MN-major (the LHS scale must be transposed and
+ *                 aligned, page "第13章 DeepGEMM" §13.3 constraint 1; layout page
+ *                 "02 · DeepGEMM 技术解析" §3.1).  F32: element (i, b) at sfa[b*sfa_stride + i];
+ *                 UE8M0x4: word (i, q) at sfa[q*sfa_stride + i].  sfa_stride == align4(m).
+ *  b, ldb       : B E4M3 [n, k], element (j, kk) at b[j*ldb + kk]; same rules as A.
+ *  sfb, sfb_stride : weight scales.
+ *                 gran_n == 128 (128x128 blocks, "1d2d"): F32 only, K-major [ceil(n/128), sf_k],
+ *                   element (jb, b) at sfb[jb*sfb_stride + b]; sfb_stride >= sf_k.  Only the
+ *                   LHS scale needs transposing (§13.3 constraint 1).
+ *                 gran_n == 1 (one scale per weight row, "1d1d"; path B of §3.2 broadcasts the
+ *                   128x128 block scale to every row): MN-major like sfa, stride == align4(n).
+ *  sf_format    : DG_SF_F32 or DG_SF_UE8M0X4 (applies to both sfa and sfb; UE8M0x4 requires
+ *                 gran_n == 1).
+ *  c, ldc       : NULL, or FP32 [m, n] at c[i*ldc + j] (requires d_dtype == DG_OUT_F32),
+ *                 ldc >= n, 4-byte aligned.  c may alias d (then ldc must equal ldd): D
+ *                 accumulates in place.
+ *  d, ldd, d_dtype : output [m, n] at d[i*ldd + j], BF16 (round to nearest even) or FP32;
+ *                 ldd >= n, d aligned to its element size.  Rows are written with 4-element
+ *                 vector stores when ldd % 4 == 0 and d is 16-byte aligned, element stores
+ *                 otherwise.
+ * Returns DG_OK or a negative dg_status.
+ */
+int dg_fp8_gemm_nt(int32_t m, int32_t n, int32_t k,
+                   const void* a, int64_t lda,
+                   const void* sfa, int64_t sfa_stride,
+                   const void* b, int64_t ldb,
+                   const void* sfb, int64_t sfb_stride,
+                   int32_t sf_format, int32_t gran_n,
+                   const float* c, int64_t ldc,
+                   void* d, int64_t ldd, int32_t d_dtype,
+                   hipStream_t stream);
+
+/*
+ * M-grouped contiguous GEMM (page "02 · DeepGEMM 技术解析" §5.1; page "第13章 DeepGEMM"
+ * §13.6): the rows of A are the concatenated tokens of num_groups experts; row i uses
+ * expert g = grouped_layout[i], i.e. D[i, :] = A[i, :] . B[g]^T with g's scales.  Only M is
+ * grouped: N and K are the same for every group.
+ *
+ *  m_total      : rows of A and D (sum of the group segments, including padding rows).
+ *  grouped_layout : device int32 [m_total], the group of each row; a negative value marks a
+ *                 padding row whose D row is not written.  Precondition (not checked, it would
+ *                 need a device read): every aligned block of
+ *                 dg_get_mk_alignment_for_contiguous_layout() rows belongs to one group, padding
+ *                 rows of a block come after its group's rows, and the group of a block is read
+ *                 from its first row (a block whose first row is negative is skipped).
+ *  b, b_group_stride : B [num_groups, n, k]; group g starts at b + g*b_group_stride.
+ *  sfb_group_stride  : group g's weight scales start at sfb + g*sfb_group_stride.
+ *  Other arguments as in dg_fp8_gemm_nt (sfa covers all m_total rows, stride align4(m_total)).
+ *  No C term (BF16 or FP32 D).
+ */
+int dg_m_grouped_fp8_gemm_nt_contiguous(int32_t m_total, int32_t n, int32_t k, int32_t num_groups,
+                                        const void* a, int64_t lda,
+                                        const void* sfa, int64_t sfa_stride,
+                                        const void* b, int64_t ldb, int64_t b_group_stride,
+                                        const void* sfb, int64_t sfb_stride, int64_t sfb_group_stride,
+                                        int32_t sf_format, int32_t gran_n,
+                                        void* d, int64_t ldd, int32_t d_dtype,
+                                        const int32_t* grouped_layout,
+                                        hipStream_t stream);
+
+/*
+ * M-grouped masked GEMM (page "02 · DeepGEMM 技术解析" §5.2): A is [num_groups, m_max, k]
+ * with a static shape (so the call can sit in a captured graph); group g has
+ * masked_m[g] valid rows, read on the device.  Only rows i < clamp(masked_m[g], 0, m_max)
+ * are computed and written; the other rows of D are left untouched.
+ *
+ *  a, lda, a_group_stride : row i of group g at a + g*a_group_stride + i*lda.
+ *  sfa, sfa_stride, sfa_group_stride : group g's activation scales (MN-major over m_max rows,
+ *                 sfa_stride == align4(m_max)) start at sfa + g*sfa_group_stride.
+ *  b, ..., sfb_group_stride : as in the contiguous variant.
+ *  d, ldd, d_group_stride : row i of group g at d + g*d_group_stride + i*ldd.
+ *  masked_m     : device int32 [num_groups].
+ *  expected_m   : host hint (typical valid rows per group) used only to choose the tile
+ *                 shape; it never changes which rows are computed.  <= 0 means m_max.
+ */
+int dg_m_grouped_fp8_gemm_nt_masked(int32_t num_groups, int32_t m_max, int32_t n, int32_t k,
+                                    const void* a, int64_t lda, int64_t a_group_stride,
+                                    const void* sfa, int64_t sfa_stride, int64_t sfa_group_stride,
+                                    const void* b, int64_t ldb, int64_t b_group_stride,
+                                    const void* sfb, int64_t sfb_stride, int64_t sfb_group_stride,
+                                    int32_t sf_format, int32_t gran_n,
+                                    void* d, int64_t ldd, int64_t d_group_stride, int32_t d_dtype,
+                                    const int32_t* masked_m, int32_t expected_m,
+                                    hipStream_t stream);
+
+/*
+ * Scale-layout transform (page "02 · DeepGEMM 技术解析" §3.1 and §3.2; page "第13章
+ * DeepGEMM" §13.3, second constraint): converts FP32 scales to the MN-major, 16-byte
+ * aligned layout the GEMMs read, optionally broadcasting 128-row blocks to every row and
+ * packing UE8M0 codes four per int32.
+ *
+ *  sf_in        : FP32 [num_groups, ceil(mn / gran_mn), sf_k], K-major, contiguous.
+ *  gran_mn      : 1 (one scale per row) or 128 (one per 128-row block, broadcast per row).
+ *  pack_ue8m0   : 0 -> sf_out is FP32 [num_groups, sf_k, align4(mn)]:
+ *                      element (r, b) of group g at g*sf_k*align4(mn) + b*align4(mn) + r.
+ *                 1 -> sf_out is int32 [num_groups, packed_sf_k, align4(mn)]: word (r, q) holds
+ *                      the UE8M0 codes of K-blocks 4q..4q+3 of row r, byte t = block 4q+t.
+ *                      The code of an FP32 scale is its exponent field, (bits >> 23) & 0xff:
+ *                      the mantissa is dropped (0.75 -> 0.5, 3 -> 2).
+ *                 Padding rows [mn, align4(mn)) and tail bytes (4q+t >= sf_k) are written 0.
+ *  nonpow2_count: NULL, or device int32; when packing, the number of input scales that are
+ *                 not exact powers of two ((bits & 0x807fffff) != 0) is ADDED to it (the
+ *                 caller zeroes it).  The library counts instead of trapping.
+ */
+int dg_transform_sf(const float* sf_in, int32_t num_groups, int32_t mn, int32_t sf_k,
+                    int32_t gran_mn, int32_t pack_ue8m0, void* sf_out,
+                    int32_t* nonpow2_count, hipStream_t stream);
+
+/* align(mn, 16 / elem_bytes): the padded MN extent of an MN-major scale tensor whose
+ * K slices start on 16-byte boundaries (page "02 · DeepGEMM 技术解析" §3.1, ALIGN_MN).
+ * elem_bytes must be 1, 2, 4, 8 or 16; returns -1 otherwise. */
+int64_t dg_get_tma_aligned_size(int64_t mn, int32_t elem_bytes);
+
+/* Row alignment of each group segment in the contiguous layout: the M block, 128
+ * (page "02 · DeepGEMM 技术解析" §5.1). */
+int32_t dg_get_mk_alignment_for_contiguous_layout(void);
+
+/* Persistent grid size (the number of compute units the scheduler spreads tiles over).
+ * n > 0 sets it, n == 0 restores the default (the device's CU count); n < 0 is an error. */
+int dg_set_num_sms(int32_t n);
+int32_t dg_get_num_sms(void);
+
+/* Tile configuration the heuristic picks, without launching anything (host only).
+ *  kind: 0 dense, 1 contiguous, 2 masked.  For masked, m is m_max and expected_m the hint.
+ *  num_sms: grid size to plan for (> 0).  Outputs may be NULL.  *num_tiles is the
+ *  number of output tiles (masked: assuming every group has expected_m valid rows). */
+int dg_get_gemm_config(int32_t kind, int32_t m, int32_t n, int32_t k, int32_t num_groups,
+                       int32_t expected_m, int32_t sf_format, int32_t gran_n, int32_t d_dtype,
+                       int32_t num_sms, int32_t* block_m, int32_t* block_n,
+                       int32_t* num_tiles, int32_t* grid);
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char* dg_get_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DG_H */

@@ -1,0 +1,344 @@
+"""GPU parity: the HIP path (through libdg.so's C ABI) against the float64 oracle
+on the same seeded inputs, element by element, under the tolerances in
+tests/tolerance.py.  Integer/byte work (the scale transform) is compared bitwise.
+Every case prints its name before it touches the GPU."""
+import contextlib
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import block_scaled_fp8_amd as dg
+import oracle
+from tests import gen
+from tests.tolerance import check_bf16, check_fp32
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+@contextlib.contextmanager
+def force_tile(tile):
+    old = os.environ.get("DG_FORCE_TILE")
+    if tile:
+        os.environ["DG_FORCE_TILE"] = tile
+    else:
+        os.environ.pop("DG_FORCE_TILE", None)
+    try:
+        yield
+    finally:
+        if old is None:
+            os.environ.pop("DG_FORCE_TILE", None)
+        else:
+            os.environ["DG_FORCE_TILE"] = old
+
+
+def cuda(x):
+    return torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
+
+
+def bf16_bits(t):
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def run_dense(p, out=torch.bfloat16, tile=None, with_c=False, c_alias=False, recipe=None, pack=False,
+              sb_per_row=False):
+    M, N = p["M"], p["N"]
+    a, b = cuda(p["a"]), cuda(p["b"])
+    sa = cuda(p["sa"])
+    sb = cuda(p["sb"])
+    if sb_per_row:   # weight scales broadcast to one per row (the per-row "1d1d" recipe)
+        sb = cuda(oracle.expand_scales_b(p["sb"], N, 128).astype(np.float32))
+        recipe = recipe or (1, 1, 128)
+    d = torch.full((M, N), float("nan"), dtype=out, device=DEV)
+    c = None
+    if with_c:
+        c = cuda(p["c"])
+        if c_alias:
+            d.copy_(c)
+            c = d
+    with force_tile(tile):
+        dg.fp8_gemm_nt((a, sa), (b, sb), d, c=c, recipe=recipe, pack_ue8m0=pack)
+    torch.cuda.synchronize()
+    return d
+
+
+def check_dense(p, d, with_c=False, gran_n=128, name=""):
+    o, T = oracle.gemm_nt(p["a"], p["sa"], p["b"], p["sb"], 128, c=p["c"] if with_c else None, want_abs=True)
+    if d.dtype == torch.bfloat16:
+        ok, st = check_bf16(bf16_bits(d), o, T)
+    else:
+        ok, st = check_fp32(d.cpu().numpy(), o, T)
+    say(name, st)
+    assert ok.all(), (name, st)
+    return st
+
+
+# ---------------------------------------------------------------- transform (bitwise)
+@pytest.mark.parametrize("G,mn,sf_k,gran", [(1, 6, 5, 1), (1, 4096, 16, 1), (3, 37, 7, 1), (2, 300, 56, 128),
+                                            (32, 7168, 16, 128), (1, 1, 1, 1)])
+@pytest.mark.parametrize("pack", [False, True])
+def test_transform_matches_oracle_bitwise(G, mn, sf_k, gran, pack):
+    say("transform", G, mn, sf_k, gran, pack)
+    rng = np.random.default_rng(G * 1000 + mn + sf_k)
+    mnb = (mn + gran - 1) // gran
+    sf = (rng.random((G, mnb, sf_k)) * 4 + 1e-3).astype(np.float32)
+    sf[..., ::3] = np.exp2(rng.integers(-10, 5, size=sf[..., ::3].shape)).astype(np.float32)
+    ref, cnt = oracle.transform_sf(sf, mn, gran, pack)
+    count = torch.zeros(1, dtype=torch.int32, device=DEV)
+    out = dg.transform_sf(cuda(sf), mn, gran, pack, nonpow2_count=count)
+    torch.cuda.synchronize()
+    # the whole underlying buffer, padding rows included
+    a4 = (mn + 3) // 4 * 4
+    cols = out.shape[-1]
+    raw = torch.as_strided(out, (G, cols, a4), (cols * a4, a4, 1)).cpu().numpy()
+    assert raw.dtype == ref.dtype
+    assert np.array_equal(raw.view(np.uint32), ref.reshape(G, cols, a4).view(np.uint32))
+    if pack:
+        assert int(count.item()) == cnt
+
+
+def test_transform_page_examples():
+    # 0.75 -> UE8M0 0.5 (code 126), 3 -> 2 (code 128); both counted as non-powers of two
+    say("transform page examples")
+    sf = np.array([[0.75, 3.0, 1.0, 0.5]], dtype=np.float32)
+    count = torch.zeros(1, dtype=torch.int32, device=DEV)
+    out = dg.transform_sf(cuda(sf), 1, 1, True, nonpow2_count=count)
+    w = int(out.cpu().numpy().view(np.uint32)[0, 0])
+    assert [(w >> (8 * t)) & 0xFF for t in range(4)] == [126, 128, 127, 126]
+    assert int(count.item()) == 2
+
+
+# ---------------------------------------------------------------- dense
+def test_config1_tiny_bf16():
+    p = gen.config1()
+    say("config1 tiny", p["M"], p["N"], p["K"])
+    d = run_dense(p)
+    check_dense(p, d, name="config1")
+
+
+DENSE_TILES = ["256x224", "256x256", "128x224", "128x256", "128x128", "64x128", "128x192", "256x192", "64x32"]
+
+
+@pytest.mark.parametrize("tile", DENSE_TILES)
+@pytest.mark.parametrize("shape", [(200, 300, 384), (257, 513, 256), (33, 129, 640)])
+def test_dense_ragged_every_tile(tile, shape):
+    M, N, K = shape
+    p = gen.dense(M, N, K, seed=M + N + K)
+    say("dense ragged", shape, tile)
+    d = run_dense(p, out=torch.bfloat16, tile=tile)
+    check_dense(p, d, name=f"dense bf16 {shape} {tile}")
+    d32 = run_dense(p, out=torch.float32, tile=tile)
+    check_dense(p, d32, name=f"dense f32 {shape} {tile}")
+
+
+@pytest.mark.parametrize("tile", ["256x224", "128x192", "128x128", "64x32"])
+def test_pow2_inputs_are_bitwise_exact(tile):
+    # integer payloads and power-of-two scales: every FP32 partial sum is exact, so the
+    # FP32 result equals the oracle bitwise and BF16 is its correct rounding
+    p = gen.pow2_exact(300, 520, 1024, seed=3, with_c=True)
+    say("pow2 exact", tile)
+    o = oracle.gemm_nt(p["a"], p["sa"], p["b"], p["sb"], 128, c=p["c"])
+    d = run_dense(p, out=torch.float32, tile=tile, with_c=True)
+    assert np.array_equal(d.cpu().numpy().astype(np.float64), o)
+    o0 = oracle.gemm_nt(p["a"], p["sa"], p["b"], p["sb"], 128)
+    d = run_dense(p, out=torch.bfloat16, tile=tile)
+    assert np.array_equal(bf16_bits(d), oracle.bf16_rne(o0))
+
+
+def test_c_accumulation_and_aliasing():
+    p = gen.dense(256, 384, 512, seed=4, with_c=True)
+    say("C accumulation")
+    d = run_dense(p, out=torch.float32, with_c=True)
+    check_dense(p, d, with_c=True, name="C separate")
+    d2 = run_dense(p, out=torch.float32, with_c=True, c_alias=True)
+    check_dense(p, d2, with_c=True, name="C aliased")
+    assert torch.equal(d, d2)
+
+
+def test_straddling_tiles_equal_aligned_tiles_bitwise():
+    # the same problem with N tiles that straddle 128-wide weight-scale blocks (224, 192)
+    # and tiles that do not (128, 256): each output element sees the same MFMA and the same
+    # promotion order, so the results are identical
+    p = gen.dense(512, 1536, 1024, seed=5, with_c=True)
+    say("straddle vs aligned")
+    outs = {t: run_dense(p, out=torch.float32, tile=t, with_c=True).cpu() for t in
+            ["128x128", "256x256", "256x224", "128x192", "256x192", "128x224", "64x32"]}
+    check_dense(p, outs["256x224"].to(DEV), with_c=True, name="straddle 256x224")
+    ref = outs["128x128"]
+    for t, v in outs.items():
+        assert torch.equal(v, ref), t
+
+
+@pytest.mark.parametrize("pack", [False, True])
+def test_per_row_weight_scales(pack):
+    # recipe (1, 1, 128): weight scales broadcast per row, FP32 or packed UE8M0
+    p = gen.grouped_masked(1, 300, 520, 768, seed=6, pow2_scales=True)
+    q = dict(a=p["a"][0], sa=p["sa"][0], b=p["b"][0], sb=p["sb"][0], c=None, M=300, N=520, K=768)
+    say("per-row weight scales", pack)
+    d = run_dense(q, out=torch.float32, sb_per_row=True, pack=pack)
+    check_dense(q, d, name=f"1d1d pack={pack}")
+    d2 = run_dense(q, out=torch.float32)
+    check_dense(q, d2, name="1d2d same data")
+
+
+def test_deterministic_and_batch_invariant():
+    p = gen.dense(1024, 768, 1024, seed=7)
+    say("determinism / batch invariance")
+    d1 = run_dense(p, tile="128x128")
+    d2 = run_dense(p, tile="128x128")
+    assert torch.equal(d1, d2)
+    q = dict(p, a=p["a"][:64], sa=p["sa"][:64], M=64)
+    d3 = run_dense(q, tile="128x128")
+    assert torch.equal(d3, d1[:64])
+
+
+def test_empty_and_tiny_problems():
+    say("empty / tiny")
+    p = gen.dense(1, 8, 128, seed=8)
+    d = run_dense(p)
+    check_dense(p, d, name="1x8x128")
+    a = torch.zeros((0, 256), dtype=torch.uint8, device=DEV)
+    sa = torch.zeros((0, 2), dtype=torch.float32, device=DEV)
+    b = torch.zeros((64, 256), dtype=torch.uint8, device=DEV)
+    sb = torch.ones((1, 2), dtype=torch.float32, device=DEV)
+    d = torch.zeros((0, 64), dtype=torch.bfloat16, device=DEV)
+    dg.fp8_gemm_nt((a, sa), (b, sb), d)
+    torch.cuda.synchronize()
+
+
+def test_sentinel_coverage_ragged():
+    # every valid element written exactly where it belongs; the padding of a strided D untouched
+    p = gen.dense(130, 200, 256, seed=9)
+    say("sentinel coverage")
+    a, b, sa, sb = cuda(p["a"]), cuda(p["b"]), cuda(p["sa"]), cuda(p["sb"])
+    big = torch.full((130, 264), -12345.0, dtype=torch.float32, device=DEV)
+    d = big[:, :200]
+    dg.fp8_gemm_nt((a, sa), (b, sb), d)
+    torch.cuda.synchronize()
+    h = big.cpu().numpy()
+    assert (h[:, 200:] == -12345.0).all()
+    o, T = oracle.gemm_nt(p["a"], p["sa"], p["b"], p["sb"], 128, want_abs=True)
+    ok, st = check_fp32(h[:, :200], o, T)
+    assert ok.all(), st
+
+
+# ---------------------------------------------------------------- grouped (small)
+def test_contiguous_small_with_padding_rows():
+    G, N, K = 4, 384, 512
+    p = gen.grouped_contiguous(G, N, K, seed=10, m_units=(1, 3))
+    layout = p["layout"].copy()
+    # pad the last 60 rows of group 1's segment: they must not be written
+    seg = np.nonzero(layout == 1)[0]
+    layout[seg[-60:]] = -1
+    say("contiguous small", p["sizes"])
+    a, sa = cuda(p["a"]), cuda(p["sa"])
+    b, sb = cuda(p["b"]), cuda(p["sb"])
+    d = torch.full((p["M"], N), float("nan"), dtype=torch.bfloat16, device=DEV)
+    dg.m_grouped_fp8_gemm_nt_contiguous((a, sa), (b, sb), d, cuda(layout))
+    torch.cuda.synchronize()
+    o, T = oracle.grouped_contiguous(p["a"], p["sa"], p["b"], p["sb"], layout, want_abs=True)
+    bits = bf16_bits(d)
+    live = layout >= 0
+    ok, st = check_bf16(bits[live], o[live], T[live])
+    say("contiguous small", st)
+    assert ok.all(), st
+    assert np.isnan(d.float().cpu().numpy()[~live]).all()
+
+
+@pytest.mark.parametrize("tile", [None, "128x128", "256x224", "64x32"])
+def test_masked_small_with_sentinels(tile):
+    G, Mmax, N, K = 5, 200, 300, 256
+    p = gen.grouped_masked(G, Mmax, N, K, seed=11, pow2_scales=False)
+    masked = np.array([0, 200, 1, 129, 77], dtype=np.int32)
+    say("masked small", tile, masked)
+    a, sa = cuda(p["a"]), cuda(p["sa"])
+    b, sb = cuda(p["b"]), cuda(p["sb"])
+    d = torch.full((G, Mmax, N), float("nan"), dtype=torch.bfloat16, device=DEV)
+    with force_tile(tile):
+        dg.m_grouped_fp8_gemm_nt_masked((a, sa), (b, sb), d, cuda(masked), expected_m=100)
+    torch.cuda.synchronize()
+    o, T = oracle.grouped_masked(p["a"], p["sa"], p["b"], p["sb"], masked, want_abs=True)
+    bits = bf16_bits(d)
+    live = ~np.isnan(o)
+    ok, st = check_bf16(bits[live], o[live], T[live])
+    say("masked small", st)
+    assert ok.all(), st
+    assert np.isnan(d.float().cpu().numpy()[~live]).all()
+
+
+# ---------------------------------------------------------------- the five workloads at full size
+def test_config2_dense_full():
+    p = gen.config2()
+    say("config2 4096x7168x2048 bf16")
+    d = run_dense(p)
+    check_dense(p, d, name="config2")
+
+
+def test_config2_decode_m64_full():
+    p = gen.config2(M=64)
+    say("config2 M=64")
+    d = run_dense(p)
+    check_dense(p, d, name="config2 M64")
+
+
+def test_config3_1d2d_with_c_full():
+    p = gen.config3()
+    say("config3 4096x1536x7168 f32 + C")
+    d = run_dense(p, out=torch.float32, with_c=True)
+    st = check_dense(p, d, with_c=True, name="config3")
+    bm, bn, _, _ = dg.get_gemm_config(0, 4096, 1536, 7168, d_dtype=2, num_sms=dg.get_num_sms())
+    say("config3 tile", bm, bn)
+
+
+def test_config4_contiguous_sampled_rows():
+    p = gen.config4()
+    G, N = p["G"], p["N"]
+    say("config4 contiguous", p["M"], "rows")
+    a, sa = cuda(p["a"]), cuda(p["sa"])
+    b, sb = cuda(p["b"]), cuda(p["sb"])
+    d = torch.full((p["M"], N), float("nan"), dtype=torch.bfloat16, device=DEV)
+    dg.m_grouped_fp8_gemm_nt_contiguous((a, sa), (b, sb), d, cuda(p["layout"]))
+    torch.cuda.synchronize()
+    bits = bf16_bits(d)
+    assert not np.isnan(d.float().cpu().numpy()).any()
+    # all rows of 4 groups and 64 random rows of every other group
+    rng = np.random.default_rng(123)
+    starts = np.concatenate([[0], np.cumsum(p["sizes"])])
+    full = set(rng.choice(G, 4, replace=False).tolist())
+    rows = []
+    for g in range(G):
+        seg = np.arange(starts[g], starts[g + 1])
+        rows.append(seg if g in full else rng.choice(seg, 64, replace=False))
+    rows = np.sort(np.concatenate(rows))
+    sub_layout = p["layout"][rows]
+    o, T = oracle.grouped_contiguous(p["a"][rows], p["sa"][rows], p["b"], p["sb"], sub_layout, want_abs=True)
+    ok, st = check_bf16(bits[rows], o, T)
+    say("config4", len(rows), "rows", st)
+    assert ok.all(), st
+
+
+def test_config5_masked_full_with_sentinels():
+    p = gen.config5()
+    G, Mmax, N = p["G"], p["M_max"], p["N"]
+    say("config5 masked", p["masked_m"].tolist())
+    a, b = cuda(p["a"]), cuda(p["b"])
+    sa = dg.get_mn_major_tma_aligned_packed_ue8m0_tensor(cuda(p["sa"]))
+    sb = dg.get_mn_major_tma_aligned_packed_ue8m0_tensor(cuda(p["sb"]), gran_mn=128, mn=N)
+    d = torch.full((G, Mmax, N), float("nan"), dtype=torch.bfloat16, device=DEV)
+    dg.m_grouped_fp8_gemm_nt_masked((a, sa), (b, sb), d, cuda(p["masked_m"]), expected_m=128)
+    torch.cuda.synchronize()
+    o, T = oracle.grouped_masked(p["a"], p["sa"], p["b"], p["sb"], p["masked_m"], want_abs=True)
+    bits = bf16_bits(d)
+    live = ~np.isnan(o)
+    ok, st = check_bf16(bits[live], o[live], T[live])
+    say("config5", st)
+    assert ok.all(), st
+    assert np.isnan(d.float().cpu().numpy()[~live]).all()

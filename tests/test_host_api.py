@@ -1,0 +1,178 @@
+"""CPU tests of the C ABI: the library loads, exports every symbol include/dg.h
+declares, validates arguments on the host before any HIP call, and plans tiles
+with the expected arithmetic.  No compute call is made (no GPU here)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import block_scaled_fp8_amd as dg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dg.h")
+GOLDEN = os.path.join(ROOT, "tests", "golden")
+
+DG_OK, DG_ERR_NULL, DG_ERR_DTYPE, DG_ERR_SHAPE, DG_ERR_LAYOUT, DG_ERR_UNSUPPORTED = 0, -1, -2, -3, -4, -5
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dg_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ["dg_fp8_gemm_nt", "dg_m_grouped_fp8_gemm_nt_contiguous", "dg_m_grouped_fp8_gemm_nt_masked",
+                     "dg_transform_sf"]:
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = dg.lib()
+    out = subprocess.run(["nm", "-D", "--defined-only", dg.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (dg_\w+)", out))
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert name in exported, name
+
+
+def test_binding_signatures_cover_the_header():
+    from block_scaled_fp8_amd import _SIGS
+    assert set(_SIGS) == set(declared_functions())
+
+
+# ---------------------------------------------------------------- helpers without a GPU
+def test_tma_aligned_size_and_alignment():
+    assert dg.get_tma_aligned_size(6, 4) == 8
+    assert dg.get_tma_aligned_size(8, 4) == 8
+    assert dg.get_tma_aligned_size(9, 1) == 16
+    assert dg.get_tma_aligned_size(5, 2) == 8
+    assert dg.lib().dg_get_tma_aligned_size(5, 3) == -1
+    assert dg.get_mk_alignment_for_contiguous_layout() == 128
+
+
+def test_set_num_sms_validation():
+    lib = dg.lib()
+    assert lib.dg_set_num_sms(-1) == DG_ERR_SHAPE
+    assert b"negative" in lib.dg_get_last_error()
+    assert lib.dg_set_num_sms(0) == DG_OK
+
+
+# ---------------------------------------------------------------- validation (before any HIP call)
+P = ctypes.c_void_p(4096)          # a 16-byte aligned fake address: never dereferenced
+P_MIS = ctypes.c_void_p(4100)
+
+
+def _dense(**kw):
+    args = dict(m=64, n=128, k=256, a=P, lda=256, sfa=P, sfa_stride=64, b=P, ldb=256, sfb=P, sfb_stride=2,
+                sf_format=0, gran_n=128, c=None, ldc=0, d=P, ldd=128, d_dtype=1, stream=None)
+    args.update(kw)
+    return dg.lib().dg_fp8_gemm_nt(*args.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(k=200), DG_ERR_SHAPE),
+    (dict(k=0), DG_ERR_SHAPE),
+    (dict(m=-1), DG_ERR_SHAPE),
+    (dict(d_dtype=7), DG_ERR_DTYPE),
+    (dict(sf_format=3), DG_ERR_DTYPE),
+    (dict(gran_n=64), DG_ERR_UNSUPPORTED),
+    (dict(sf_format=1, gran_n=128), DG_ERR_UNSUPPORTED),
+    (dict(a=None), DG_ERR_NULL),
+    (dict(sfb=None), DG_ERR_NULL),
+    (dict(d=None), DG_ERR_NULL),
+    (dict(lda=200), DG_ERR_LAYOUT),
+    (dict(lda=264), DG_ERR_LAYOUT),
+    (dict(a=P_MIS), DG_ERR_LAYOUT),
+    (dict(sfa_stride=65), DG_ERR_LAYOUT),
+    (dict(sfb_stride=1), DG_ERR_LAYOUT),
+    (dict(gran_n=1, sfb_stride=2), DG_ERR_LAYOUT),
+    (dict(ldd=100), DG_ERR_LAYOUT),
+    (dict(c=P, ldc=128), DG_ERR_UNSUPPORTED),                 # C with a BF16 output
+    (dict(c=P, ldc=96, d_dtype=2), DG_ERR_LAYOUT),
+    (dict(c=P, ldc=136, d=P, ldd=128, d_dtype=2), DG_ERR_LAYOUT),  # aliasing with different strides
+])
+def test_dense_validation(kw, code):
+    assert _dense(**kw) == code
+    assert dg.lib().dg_get_last_error() != b""
+
+
+def test_empty_problem_is_a_noop():
+    assert _dense(m=0, sfa_stride=0) == DG_OK
+    assert _dense(n=0, ldd=0, sfb_stride=2) == DG_OK
+
+
+def test_grouped_validation():
+    lib = dg.lib()
+    # contiguous: missing layout, too-small group stride
+    st = lib.dg_m_grouped_fp8_gemm_nt_contiguous(256, 128, 256, 4, P, 256, P, 256, P, 256, 128 * 256, P, 2, 2, 0,
+                                                 128, P, 128, 1, None, None)
+    assert st == DG_ERR_NULL
+    st = lib.dg_m_grouped_fp8_gemm_nt_contiguous(256, 128, 256, 4, P, 256, P, 256, P, 256, 100, P, 2, 2, 0,
+                                                 128, P, 128, 1, P, None)
+    assert st == DG_ERR_LAYOUT
+    st = lib.dg_m_grouped_fp8_gemm_nt_contiguous(256, 128, 256, 0, P, 256, P, 256, P, 256, 128 * 256, P, 2, 2,
+                                                 0, 128, P, 128, 1, P, None)
+    assert st == DG_ERR_SHAPE
+    # masked: missing mask, bad group strides
+    args = [4, 64, 128, 256, P, 256, 64 * 256, P, 64, 2 * 64, P, 256, 128 * 256, P, 2, 2, 0, 128,
+            P, 128, 64 * 128, 1, P, 32, None]
+    assert lib.dg_m_grouped_fp8_gemm_nt_masked(*args[:22], None, *args[23:]) == DG_ERR_NULL
+    bad = list(args)
+    bad[6] = 100
+    assert lib.dg_m_grouped_fp8_gemm_nt_masked(*bad) == DG_ERR_LAYOUT
+    bad = list(args)
+    bad[20] = 10
+    assert lib.dg_m_grouped_fp8_gemm_nt_masked(*bad) == DG_ERR_LAYOUT
+
+
+def test_transform_validation():
+    lib = dg.lib()
+    assert lib.dg_transform_sf(P, 1, 16, 4, 64, 0, P, None, None) == DG_ERR_UNSUPPORTED
+    assert lib.dg_transform_sf(P, 1, 16, 4, 1, 2, P, None, None) == DG_ERR_DTYPE
+    assert lib.dg_transform_sf(None, 1, 16, 4, 1, 0, P, None, None) == DG_ERR_NULL
+    assert lib.dg_transform_sf(P, 1, 16, 4, 1, 0, P_MIS, None, None) == DG_ERR_LAYOUT
+    assert lib.dg_transform_sf(P, 0, 16, 4, 1, 0, P, None, None) == DG_ERR_SHAPE
+    assert lib.dg_transform_sf(P, 1, 0, 4, 1, 0, P, None, None) == DG_OK
+
+
+# ---------------------------------------------------------------- tile planning
+def _golden(name):
+    rows = []
+    for line in open(os.path.join(GOLDEN, name)):
+        line = line.strip()
+        if line and not line.startswith("#"):
+            rows.append([int(x) for x in line.split()])
+    return rows
+
+
+def test_tile_count_arithmetic_example(monkeypatch):
+    # the pages' example: M=256, N=7168 at BLOCK_M=128 and BLOCK_N=128 gives 112 tiles
+    M, N, BM, BN, tiles = _golden("tile_counts.txt")[0]
+    monkeypatch.setenv("DG_FORCE_TILE", f"{BM}x{BN}")
+    bm, bn, nt, grid = dg.get_gemm_config(0, M, N, 2048, num_sms=132)
+    assert (bm, bn, nt, grid) == (BM, BN, tiles, tiles)
+    # and BLOCK_N=112 would give 128 tiles (the count the heuristic compares)
+    M2, N2, BM2, BN2, tiles2 = _golden("tile_counts.txt")[1]
+    assert ((M2 + BM2 - 1) // BM2) * ((N2 + BN2 - 1) // BN2) == tiles2
+
+
+def test_heuristic_avoids_partial_waves_on_256_cus(monkeypatch):
+    monkeypatch.delenv("DG_FORCE_TILE", raising=False)
+    # 4096 x 7168: 256x224 tiles give 512 tiles = exactly two waves of 256 workgroups,
+    # where 256x256 would give 448 (1.75 waves)
+    bm, bn, nt, grid = dg.get_gemm_config(0, 4096, 7168, 2048, num_sms=256)
+    assert (bm, bn, nt, grid) == (256, 224, 512, 256)
+    # 4096 x 1536 x 7168 with FP32 output: 128x192 tiles give exactly 256 tiles, straddling
+    # 128-wide weight-scale blocks
+    bm, bn, nt, grid = dg.get_gemm_config(0, 4096, 1536, 7168, d_dtype=2, num_sms=256)
+    assert (bm, bn, nt) == (128, 192, 256)
+
+
+def test_heuristic_contiguous_uses_the_alignment(monkeypatch):
+    monkeypatch.delenv("DG_FORCE_TILE", raising=False)
+    bm, bn, nt, grid = dg.get_gemm_config(1, 18432, 4096, 7168, num_groups=32, num_sms=256)
+    assert bm <= dg.get_mk_alignment_for_contiguous_layout()
