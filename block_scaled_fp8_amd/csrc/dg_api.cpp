@@ -116,7 +116,7 @@ int sf_mode_of(int32_t sf_format, int32_t gran_n) {
 // Checks shared by the three GEMM entry points.
 int check_common(int32_t n, int32_t k, const void* a, int64_t lda, const void* sfa, const void* b,
                  int64_t ldb, const void* sfb, int64_t sfb_stride, int32_t sf_format, int32_t gran_n,
-                 const void* d, int64_t ldd, int32_t d_dtype) {
+                 const void* d, int64_t ldd, int32_t d_dtype, bool empty) {
   if (d_dtype != DG_OUT_BF16 && d_dtype != DG_OUT_F32) return fail(DG_ERR_DTYPE, "d_dtype %d is not DG_OUT_BF16 or DG_OUT_F32", d_dtype);
   if (sf_format != DG_SF_F32 && sf_format != DG_SF_UE8M0X4) return fail(DG_ERR_DTYPE, "sf_format %d is not DG_SF_F32 or DG_SF_UE8M0X4", sf_format);
   if (gran_n != 1 && gran_n != 128) return fail(DG_ERR_UNSUPPORTED, "gran_n %d: weight scales are per 128x128 block (128) or per row (1)", gran_n);
@@ -124,6 +124,7 @@ int check_common(int32_t n, int32_t k, const void* a, int64_t lda, const void* s
     return fail(DG_ERR_UNSUPPORTED, "packed UE8M0 weight scales must be broadcast per row (gran_n == 1)");
   if (k <= 0 || k % 128 != 0) return fail(DG_ERR_SHAPE, "k = %d must be a positive multiple of 128", k);
   if (n < 0) return fail(DG_ERR_SHAPE, "n = %d is negative", n);
+  if (empty) return DG_OK;  // nothing is read or written: pointers may be NULL
   if (!a || !sfa || !b || !sfb || !d) return fail(DG_ERR_NULL, "a, sfa, b, sfb and d must not be NULL");
   if (lda < k || lda % 16 != 0) return fail(DG_ERR_LAYOUT, "lda = %lld must be >= k and a multiple of 16", (long long)lda);
   if (ldb < k || ldb % 16 != 0) return fail(DG_ERR_LAYOUT, "ldb = %lld must be >= k and a multiple of 16", (long long)ldb);
@@ -189,15 +190,16 @@ int dg_fp8_gemm_nt(int32_t m, int32_t n, int32_t k, const void* a, int64_t lda, 
                    int32_t sf_format, int32_t gran_n, const float* c, int64_t ldc, void* d, int64_t ldd,
                    int32_t d_dtype, hipStream_t stream) {
   if (m < 0) return fail(DG_ERR_SHAPE, "m = %d is negative", m);
-  int st = check_common(n, k, a, lda, sfa, b, ldb, sfb, sfb_stride, sf_format, gran_n, d, ldd, d_dtype);
+  int st = check_common(n, k, a, lda, sfa, b, ldb, sfb, sfb_stride, sf_format, gran_n, d, ldd, d_dtype,
+                        m == 0 || n == 0);
   if (st != DG_OK) return st;
+  if (m == 0 || n == 0) return ok();
   if (sfa_stride != align4(m)) return fail(DG_ERR_LAYOUT, "sfa must be MN-major with stride align4(m) = %lld, got %lld", (long long)align4(m), (long long)sfa_stride);
   if (c) {
     if (d_dtype != DG_OUT_F32) return fail(DG_ERR_UNSUPPORTED, "a C term requires an FP32 output");
     if (ldc < n || (reinterpret_cast<uintptr_t>(c) & 3u) != 0) return fail(DG_ERR_LAYOUT, "c needs ldc >= n and 4-byte alignment");
     if ((const void*)c == d && ldc != ldd) return fail(DG_ERR_LAYOUT, "c aliases d, so ldc must equal ldd");
   }
-  if (m == 0 || n == 0) return ok();
   dg::GemmParams p{};
   p.a = (const uint8_t*)a; p.lda = lda;
   p.sfa = sfa; p.sfa_stride = sfa_stride;
@@ -218,15 +220,16 @@ int dg_m_grouped_fp8_gemm_nt_contiguous(int32_t m_total, int32_t n, int32_t k, i
                                         int32_t d_dtype, const int32_t* grouped_layout, hipStream_t stream) {
   if (m_total < 0) return fail(DG_ERR_SHAPE, "m_total = %d is negative", m_total);
   if (num_groups <= 0) return fail(DG_ERR_SHAPE, "num_groups = %d must be positive", num_groups);
-  int st = check_common(n, k, a, lda, sfa, b, ldb, sfb, sfb_stride, sf_format, gran_n, d, ldd, d_dtype);
+  int st = check_common(n, k, a, lda, sfa, b, ldb, sfb, sfb_stride, sf_format, gran_n, d, ldd, d_dtype,
+                        m_total == 0 || n == 0);
   if (st != DG_OK) return st;
+  if (m_total == 0 || n == 0) return ok();
   if (!grouped_layout) return fail(DG_ERR_NULL, "grouped_layout must not be NULL");
   if (sfa_stride != align4(m_total)) return fail(DG_ERR_LAYOUT, "sfa must be MN-major with stride align4(m_total) = %lld, got %lld", (long long)align4(m_total), (long long)sfa_stride);
   if (b_group_stride < int64_t(n) * ldb || b_group_stride % 16 != 0) return fail(DG_ERR_LAYOUT, "b_group_stride must be >= n*ldb and a multiple of 16");
   const int64_t sfb_min = gran_n == 128 ? int64_t((n + 127) / 128) * sfb_stride
                                         : (sf_format == DG_SF_UE8M0X4 ? int64_t((k / 128 + 3) / 4) : int64_t(k / 128)) * sfb_stride;
   if (sfb_group_stride < sfb_min || (gran_n == 1 && sfb_group_stride % 4 != 0)) return fail(DG_ERR_LAYOUT, "sfb_group_stride = %lld is smaller than one group's scales (%lld) or misaligned", (long long)sfb_group_stride, (long long)sfb_min);
-  if (m_total == 0 || n == 0) return ok();
   dg::GemmParams p{};
   p.a = (const uint8_t*)a; p.lda = lda;
   p.sfa = sfa; p.sfa_stride = sfa_stride;
@@ -248,8 +251,10 @@ int dg_m_grouped_fp8_gemm_nt_masked(int32_t num_groups, int32_t m_max, int32_t n
                                     hipStream_t stream) {
   if (num_groups <= 0) return fail(DG_ERR_SHAPE, "num_groups = %d must be positive", num_groups);
   if (m_max < 0) return fail(DG_ERR_SHAPE, "m_max = %d is negative", m_max);
-  int st = check_common(n, k, a, lda, sfa, b, ldb, sfb, sfb_stride, sf_format, gran_n, d, ldd, d_dtype);
+  int st = check_common(n, k, a, lda, sfa, b, ldb, sfb, sfb_stride, sf_format, gran_n, d, ldd, d_dtype,
+                        m_max == 0 || n == 0);
   if (st != DG_OK) return st;
+  if (m_max == 0 || n == 0) return ok();
   if (!masked_m) return fail(DG_ERR_NULL, "masked_m must not be NULL");
   if (sfa_stride != align4(m_max)) return fail(DG_ERR_LAYOUT, "sfa must be MN-major with stride align4(m_max) = %lld, got %lld", (long long)align4(m_max), (long long)sfa_stride);
   if (a_group_stride < int64_t(m_max) * lda || a_group_stride % 16 != 0) return fail(DG_ERR_LAYOUT, "a_group_stride must be >= m_max*lda and a multiple of 16");
@@ -259,7 +264,6 @@ int dg_m_grouped_fp8_gemm_nt_masked(int32_t num_groups, int32_t m_max, int32_t n
   const int64_t sfb_min = gran_n == 128 ? int64_t((n + 127) / 128) * sfb_stride : sf_rows * sfb_stride;
   if (sfb_group_stride < sfb_min || (gran_n == 1 && sfb_group_stride % 4 != 0)) return fail(DG_ERR_LAYOUT, "sfb_group_stride is smaller than one group's scales or misaligned");
   if (d_group_stride < int64_t(m_max) * ldd) return fail(DG_ERR_LAYOUT, "d_group_stride must be >= m_max*ldd");
-  if (m_max == 0 || n == 0) return ok();
   dg::GemmParams p{};
   p.a = (const uint8_t*)a; p.lda = lda; p.a_gstride = a_group_stride;
   p.sfa = sfa; p.sfa_stride = sfa_stride; p.sfa_gstride = sfa_group_stride;
@@ -278,10 +282,10 @@ int dg_transform_sf(const float* sf_in, int32_t num_groups, int32_t mn, int32_t 
   if (num_groups <= 0 || mn < 0 || sf_k <= 0) return fail(DG_ERR_SHAPE, "need num_groups > 0, mn >= 0, sf_k > 0");
   if (gran_mn != 1 && gran_mn != 128) return fail(DG_ERR_UNSUPPORTED, "gran_mn %d must be 1 or 128", gran_mn);
   if (pack_ue8m0 != 0 && pack_ue8m0 != 1) return fail(DG_ERR_DTYPE, "pack_ue8m0 must be 0 or 1");
+  if (mn == 0) return ok();  // nothing is read or written
   if (!sf_in || !sf_out) return fail(DG_ERR_NULL, "sf_in and sf_out must not be NULL");
   if (!aligned16(sf_out)) return fail(DG_ERR_LAYOUT, "sf_out must be 16-byte aligned");
   if ((reinterpret_cast<uintptr_t>(sf_in) & 3u) != 0) return fail(DG_ERR_LAYOUT, "sf_in must be 4-byte aligned");
-  if (mn == 0) return ok();
   const hipError_t e = dg::launch_transform_sf(sf_in, num_groups, mn, sf_k, gran_mn, pack_ue8m0, sf_out,
                                                nonpow2_count, stream);
   if (e != hipSuccess) return fail(DG_ERR_HIP, "transform launch failed: %s", hipGetErrorString(e));

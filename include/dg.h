@@ -59,7 +59,8 @@ typedef enum { DG_SF_F32 = 0, DG_SF_UE8M0X4 = 1 } dg_sf_format;
  * Dense NT GEMM: D[m, n] = C[m, n] + sum_b sa[m, b] * sb[.., b] * sum_{k in block b} A[m, k] * B[n, k]
  * (page "第13章 DeepGEMM" §13.3: fp8_gemm_nt computes D = C + A @ B.T).
  *
- *  m, n, k      : problem sizes; m, n >= 0 (0 is a no-op), k > 0 and k % 128 == 0.
+ *  m, n, k      : problem sizes; k > 0 and k % 128 == 0; m, n >= 0.  m == 0 or n == 0 is a
+ *                 no-op that reads and writes nothing (its pointers may then be NULL).
  *  a, lda       : A E4M3 [m, k], element (i, kk) at a[i*lda + kk]; k <= lda <= 2^23, lda % 16 == 0,
  *                 a 16-byte aligned.
  *  sfa, sfa_stride : activation scales, MN-major (the LHS scale must be transposed and
@@ -162,6 +163,7 @@ int dg_m_grouped_fp8_gemm_nt_masked(int32_t num_groups, int32_t m_max, int32_t n
  *                      The code of an FP32 scale is its exponent field, (bits >> 23) & 0xff:
  *                      the mantissa is dropped (0.75 -> 0.5, 3 -> 2).
  *                 Padding rows [mn, align4(mn)) and tail bytes (4q+t >= sf_k) are written 0.
+ *  mn == 0 is a no-op (pointers may be NULL).
  *  nonpow2_count: NULL, or device int32; when packing, the number of input scales that are
  *                 not exact powers of two ((bits & 0x807fffff) != 0) is ADDED to it (the
  *                 caller zeroes it).  The library counts instead of trapping.
