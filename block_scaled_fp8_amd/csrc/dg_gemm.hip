@@ -17,7 +17,13 @@
 //    fragment, and 8- or 16-byte contiguous stores in the epilogue.
 //  * A and B tiles go HBM -> LDS with global_load_lds_dwordx4 (no register
 //    staging), 2 LDS stages, each 128-byte row stored with its 16-byte chunks
-//    XOR-swizzled by (row & 7) so fragment reads are bank-conflict free.
+//    XOR-swizzled by (row & 7) ^ ((row >> 3) & 1): measured with the LDS
+//    bank-conflict counter on gfx950, this key makes the fragment reads (16
+//    rows x one 16-byte chunk per lane group) conflict free, where plain
+//    (row & 7) or ((row >> 1) & 7) keys are 2-way conflicted.
+//  * The pipeline runs across tiles: the first stage of a workgroup's next tile
+//    is enqueued during the current tile's last K block, and barriers wait on
+//    explicit vmcnt values, so epilogue stores do not block the next loads.
 //  * Persistent workgroups walk output tiles with stride gridDim.x (page
 //    "02 · DeepGEMM 技术解析" §4.3); logical workgroup ids are remapped so
 //    consecutive ids share an XCD (and its L2), and tiles are ordered in
@@ -64,6 +70,9 @@ struct Tile {
   int m_valid;  // rows < m_valid exist
   bool skip;
 };
+
+// LDS slot of 16-byte chunk c of stage row r is c ^ swz(r).
+__device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
 
@@ -135,49 +144,89 @@ struct BlockScales {
   int eb[SFM == SF_1D1D_UE8M0 ? FN : 1];
 };
 
-// One output tile: prologue, the K loop over 128-long blocks, epilogue.
+// Where one wave's share of a tile's stage loads comes from: wave-load q covers 8
+// stage rows of 128 bytes; lane L fills LDS bytes [16L, 16L+16) of it = stage row
+// r = 8q + L/8, slot L%8, which holds 16-byte chunk (L%8) ^ swz(r) of that row, and
+// swz(8q + L/8) = (L/8) ^ (q & 1).  The wave-uniform part of each address lives in
+// scalar registers; the per-lane part is one 32-bit offset per chunk parity.  Rows
+// past the end of A or B are not loaded (their LDS rows keep stale bytes, which only
+// reach output rows or columns that are never stored).
+template <int BM, int BN, int WM, int WN>
+struct Loader {
+  const uint8_t* a_tile;  // row tile.m0 of A (this tile's group)
+  const uint8_t* b_tile;  // row tile.n0 of B
+  int a_rows, b_rows;     // rows that exist from there on
+};
+
+template <int BM, int BN, int WM, int WN, int GRP>
+__device__ __forceinline__ void make_loader(const GemmParams& p, const Tile& tl, Loader<BM, BN, WM, WN>& ld) {
+  const uint8_t* A = p.a + (GRP == GRP_MASKED ? (int64_t)tl.g * p.a_gstride : 0);
+  const uint8_t* B = p.b + (GRP != GRP_DENSE ? (int64_t)tl.g * p.b_gstride : 0);
+  ld.a_tile = A + (int64_t)tl.m0 * p.lda;
+  ld.b_tile = B + (int64_t)tl.n0 * p.ldb;
+  ld.a_rows = p.m - tl.m0;  // m_max rows when masked
+  ld.b_rows = p.n - tl.n0;
+}
+
+// Enqueue the HBM -> LDS copy of K block kb of a tile into stage s.
+template <int BM, int BN, int WM, int WN>
+__device__ __forceinline__ void issue_stage(const GemmParams& p, const Loader<BM, BN, WM, WN>& ld, uint8_t* smem,
+                                            int kb, int s, const int wave, const int lane) {
+  using S = Shape<BM, BN, WM, WN>;
+  static_assert((BM / 8) % S::NW == 0, "A and B wave-loads must split at a fixed u");
+  constexpr int UA = BM / 8 / S::NW;  // wave-loads u < UA fill A rows, the rest B rows
+  const int lr8 = lane >> 3;
+  const int lda = (int)p.lda, ldb = (int)p.ldb;
+  const bool full = ld.a_rows >= BM && ld.b_rows >= BN;  // uniform: no row to skip
+  // per-lane address parts, opaque to the optimiser so it rebuilds each address from a
+  // scalar base every K block instead of keeping 64-bit per-lane pointers live
+  uint32_t off_a = (uint32_t)(lr8 * lda), off_b = (uint32_t)(lr8 * ldb);
+  uint32_t chunk_off = (uint32_t)((lane & 7) ^ lr8) << 4;
+  asm volatile("" : "+v"(off_a), "+v"(off_b), "+v"(chunk_off));
+#pragma unroll
+  for (int u = 0; u < S::LPW; ++u) {
+    const int q = wave + u * S::NW;
+    if (q < S::LOADS) {
+      const int par = (S::NW % 2 == 0) ? (wave & 1) : (u & 1);
+      const bool is_a = u < UA;
+      const int ld_rows = is_a ? lda : ldb;
+      const int row0 = 8 * q - (is_a ? 0 : BM);  // first row of this wave-load (uniform)
+      const uint8_t* base = (is_a ? ld.a_tile : ld.b_tile) + (int64_t)kb * BK + (int64_t)row0 * ld_rows;
+      const uint32_t lane_off = (is_a ? off_a : off_b) + (chunk_off ^ ((uint32_t)par << 4));
+      if (full || lr8 < (is_a ? ld.a_rows : ld.b_rows) - row0)
+        __builtin_amdgcn_global_load_lds((const void*)(base + lane_off),
+                                         (DG_LDS void*)(smem + s * S::STAGE_BYTES + q * 1024), 16, 0, 0);
+    }
+  }
+}
+
+// Wait until at most N vector-memory operations of this wave are outstanding and no
+// LDS operation is, then synchronise the workgroup.
+template <int N>
+__device__ __forceinline__ void wait_and_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit field");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+  __builtin_amdgcn_s_barrier();
+}
+
+// One output tile: the K loop over 128-long blocks, then the epilogue.  K block 0 of
+// this tile is already in flight into stage `stage0`; during the last K block the
+// first stage of the next tile (if any) is enqueued into the other stage, so it
+// overlaps this tile's last block and epilogue.  `vm_after_prefetch` is a lower bound
+// on this wave's vector-memory operations issued after that prefetch, before this
+// tile's first wait (the previous tile's epilogue stores).
 template <int BM, int BN, int WM, int WN, int SFM, int GRP, int OUT, int NF>
-__device__ __forceinline__ void gemm_tile(const GemmParams& p, uint8_t* smem, const Tile& tl,
-                                          const int wave, const int lane) {
+__device__ __forceinline__ int gemm_tile(const GemmParams& p, uint8_t* smem, const Tile& tl,
+                                         const Loader<BM, BN, WM, WN>& ld, const bool has_next,
+                                         const Loader<BM, BN, WM, WN>& ld_next, const int stage0,
+                                         const int vm_after_prefetch, const int wave, const int lane) {
   using S = Shape<BM, BN, WM, WN>;
   constexpr int FM = S::FM, FN = S::FN, TM = S::TM, TN = S::TN;
   const int wm = wave / WN, wn = wave % WN;
   const int lr = lane & 15, lg = lane >> 4;
   const int nkb = p.sf_k;
   const int g = tl.g;
-
-  const uint8_t* A = p.a + (GRP == GRP_MASKED ? (int64_t)g * p.a_gstride : 0);
-  const uint8_t* B = p.b + (GRP != GRP_DENSE ? (int64_t)g * p.b_gstride : 0);
   const int a_rows = p.m;  // addressable rows of A (m_max for masked)
-
-  // ---- this wave's share of the stage loads: wave-load q covers 8 rows of 128 bytes;
-  // lane L fills LDS bytes [16L, 16L+16) of it = row 8q + L/8, slot L%8, which holds
-  // 16-byte chunk (L%8) ^ (row & 7) of the row.  Addresses are a wave-uniform 64-bit
-  // tile base plus a 32-bit per-lane offset.
-  const uint8_t* a_tile = A + (int64_t)tl.m0 * p.lda;
-  const uint8_t* b_tile = B + (int64_t)tl.n0 * p.ldb;
-  const int a_left = a_rows - 1 - tl.m0;  // last addressable row, relative to the tile
-  const int b_left = p.n - 1 - tl.n0;
-  uint32_t off[S::LPW];
-#pragma unroll
-  for (int u = 0; u < S::LPW; ++u) {
-    const int q = wave + u * S::NW;
-    const int r = 8 * q + (lane >> 3);
-    const int chunk = (lane & 7) ^ ((lane >> 3) & 7);
-    if (r < BM) off[u] = (uint32_t)(min(r, a_left) * (int)p.lda + chunk * 16);
-    else off[u] = (uint32_t)(min(r - BM, b_left) * (int)p.ldb + chunk * 16);
-  }
-  auto issue_stage = [&](int kb, int s) {
-#pragma unroll
-    for (int u = 0; u < S::LPW; ++u) {
-      const int q = wave + u * S::NW;
-      if (q < S::LOADS) {
-        const uint8_t* base = (8 * q < BM) ? a_tile : b_tile;
-        __builtin_amdgcn_global_load_lds((const void*)(base + (int64_t)kb * BK + off[u]),
-                                         (DG_LDS void*)(smem + s * S::STAGE_BYTES + q * 1024), 16, 0, 0);
-      }
-    }
-  };
 
   // ---- scales
   const int row0 = tl.m0 + wm * TM + lr;       // lane's row in fragment 0
@@ -228,22 +277,28 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, uint8_t* smem, co
       for (int v = 0; v < 4; ++v) fin[i][j][v] = 0.f;
 
   const v4f zero = {0.f, 0.f, 0.f, 0.f};
-  const int sw = lr & 7;  // fragment rows start on multiples of 16: row & 7 == lr & 7
+  const int sw = swz(lr);  // fragment rows start on multiples of 16: swz(row) == swz(lr)
   const int off_lo = ((2 * lg) ^ sw) * 16, off_hi = ((2 * lg + 1) ^ sw) * 16;
 
   BlockScales<SFM, FM, FN> cur, nxt;
-  issue_stage(0, 0);
   load_scales(0, cur);
 
   for (int kb = 0; kb < nkb; ++kb) {
-    const int s = kb & 1;
-    __syncthreads();  // stage s has landed everywhere; nobody still reads stage s^1
+    const int s = (stage0 + kb) & 1;
+    // stage s has landed everywhere and nobody still reads stage s^1
+    if (kb == 0) {
+      if (vm_after_prefetch >= FM * FN) wait_and_barrier<FM * FN>();
+      else wait_and_barrier<0>();
+    } else {
+      wait_and_barrier<0>();
+    }
     if (kb + 1 < nkb) {
-      issue_stage(kb + 1, s ^ 1);
+      issue_stage(p, ld, smem, kb + 1, s ^ 1, wave, lane);
       load_scales(kb + 1, nxt);
+    } else if (has_next) {
+      issue_stage(p, ld_next, smem, 0, s ^ 1, wave, lane);
     }
     const uint8_t* st = smem + s * S::STAGE_BYTES;
-
     // promotion factors for this block
     float s0[FM], s1[FM];
 #pragma unroll
@@ -314,7 +369,11 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, uint8_t* smem, co
     cur = nxt;
   }
 
-  // ---- epilogue: lane owns row (m0 + wm*TM + 16i + lr), columns (nw0 + 16j + 4lg .. +3)
+  // ---- epilogue: lane owns row (m0 + wm*TM + 16i + lr), columns (nw0 + 16j + 4lg .. +3).
+  // Returns a lower bound on the vector-memory operations this wave issued here: FM*FN
+  // vector stores when the whole tile is inside D and rows need no group check, else 0.
+  const bool interior = (GRP != GRP_CONTIG) && (OUT != OUT_F32_C || p.c_vec) && p.d_vec &&
+                        tl.m0 + BM <= tl.m_valid && tl.n0 + BN <= p.n;
   char* Dg = (char*)p.d;
   const int esz = (OUT == OUT_BF16) ? 2 : 4;
   if (GRP == GRP_MASKED) Dg += (int64_t)g * p.d_gstride * esz;
@@ -366,6 +425,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, uint8_t* smem, co
       }
     }
   }
+  return interior ? FM * FN : 0;
 }
 
 template <int BM, int BN, int WM, int WN, int SFM, int GRP, int OUT>
@@ -380,18 +440,36 @@ __global__ void __launch_bounds__(WM* WN * 64, 1) gemm_kernel(const GemmParams p
     const int per = gridDim.x / 8;
     bid = (bid % 8) * per + bid / 8;
   }
-  for (int t = bid;; t += gridDim.x) {
-    Tile tl;
-    if (!get_tile<GRP, BM, BN>(p, t, tl)) break;
-    if (tl.skip) continue;
+  // next non-skipped tile at or after logical index t
+  auto advance = [&](int& t, Tile& tl) -> bool {
+    for (;; t += gridDim.x) {
+      if (!get_tile<GRP, BM, BN>(p, t, tl)) return false;
+      if (!tl.skip) return true;
+    }
+  };
+  int t = bid;
+  Tile cur;
+  if (!advance(t, cur)) return;
+  Loader<BM, BN, WM, WN> ld_cur, ld_next;
+  make_loader<BM, BN, WM, WN, GRP>(p, cur, ld_cur);
+  issue_stage(p, ld_cur, smem, 0, 0, wave, lane);
+  int stage0 = 0;
+  int vm_after = 0;
+  for (;;) {
+    Tile nxt;
+    int tn = t + gridDim.x;
+    const bool has_next = advance(tn, nxt);
+    if (has_next) make_loader<BM, BN, WM, WN, GRP>(p, nxt, ld_next);
     if (SFM == SF_1D2D_F32) {
       // leading 16-column fragments of this wave that use the first weight-scale block
-      const int ph = ((tl.n0 + wn * S::TN) & 127) >> 4;
+      const int ph = ((cur.n0 + wn * S::TN) & 127) >> 4;
       const int nf = min(S::FN, 8 - ph);
       switch (nf) {
-#define DG_NF_CASE(X)                                                                \
-  case X:                                                                            \
-    if constexpr (X <= S::FN) gemm_tile<BM, BN, WM, WN, SFM, GRP, OUT, X>(p, smem, tl, wave, lane); \
+#define DG_NF_CASE(X)                                                                                  \
+  case X:                                                                                              \
+    if constexpr (X <= S::FN)                                                                          \
+      vm_after = gemm_tile<BM, BN, WM, WN, SFM, GRP, OUT, X>(p, smem, cur, ld_cur, has_next, ld_next,  \
+                                                             stage0, vm_after, wave, lane);            \
     break;
         DG_NF_CASE(1) DG_NF_CASE(2) DG_NF_CASE(3) DG_NF_CASE(4)
         DG_NF_CASE(5) DG_NF_CASE(6) DG_NF_CASE(7) DG_NF_CASE(8)
@@ -399,9 +477,14 @@ __global__ void __launch_bounds__(WM* WN * 64, 1) gemm_kernel(const GemmParams p
         default: break;
       }
     } else {
-      gemm_tile<BM, BN, WM, WN, SFM, GRP, OUT, S::FN>(p, smem, tl, wave, lane);
+      vm_after = gemm_tile<BM, BN, WM, WN, SFM, GRP, OUT, S::FN>(p, smem, cur, ld_cur, has_next, ld_next,
+                                                                stage0, vm_after, wave, lane);
     }
-    __syncthreads();  // the next tile's first stage overwrites LDS this tile read last
+    if (!has_next) break;
+    stage0 = (stage0 + p.sf_k) & 1;
+    cur = nxt;
+    ld_cur = ld_next;
+    t = tn;
   }
 }
 
