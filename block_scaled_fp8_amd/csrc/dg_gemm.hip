@@ -55,13 +55,21 @@ struct Shape {
   static constexpr int TN = BN / WN;
   static constexpr int FM = TM / 16;
   static constexpr int FN = TN / 16;
-  static constexpr int STAGE_BYTES = (BM + BN) * BK;
-  static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
-  static constexpr int LOADS = (BM + BN) / 8;           // 1 KiB wave-loads per stage
-  static constexpr int LPW = (LOADS + NW - 1) / NW;     // wave-loads per wave
+  static constexpr int AB_BYTES = (BM + BN) * BK;       // A rows, then B rows, 128 bytes each
+  static constexpr int SA_OFF = AB_BYTES;               // activation scales of the K block (<= 1 KiB)
+  static constexpr int SB_OFF = AB_BYTES + 1024;        // per-row weight scales of the K block (<= 1 KiB)
+  static constexpr int STAGE_BYTES = AB_BYTES + 2048;
+  static constexpr int TRASH_OFF = STAGES * STAGE_BYTES;  // 1 KiB sink for loads that are not needed
+  static constexpr int LDS_BYTES = TRASH_OFF + 1024;
+  static constexpr int LOADS = (BM + BN) / 8;           // 1 KiB row wave-loads per stage
+  // wave-load slots per wave: every wave issues LPW per stage; slot q = wave + u*NW is a
+  // row load for q < LOADS, the activation scales for q == LOADS, the per-row weight
+  // scales for q == LOADS + 1, and a load into the trash region otherwise
+  static constexpr int LPW = (LOADS + 2 + NW - 1) / NW;
   static_assert(TM % 16 == 0 && TN % 16 == 0, "wave tile must be a multiple of 16");
   static_assert(TN <= 128, "a wave's N range may touch at most two weight-scale blocks");
   static_assert(BM % 8 == 0 && BN % 8 == 0, "rows are loaded 8 per wave-load");
+  static_assert(BM <= 256 && BN <= 256, "one scale wave-load covers at most 256 rows");
 };
 
 struct Tile {
@@ -120,45 +128,33 @@ __device__ __forceinline__ bool get_tile(const GemmParams& p, int t, Tile& tl) {
   return true;
 }
 
-__device__ __forceinline__ float ue8m0_byte(unsigned int word, int byte) {
-  return __uint_as_float(((word >> (8 * byte)) & 0xFFu) << 23);
-}
-
 __device__ __forceinline__ unsigned int pack_bf16x2(float x, float y) {
   v2bf v = {(__bf16)x, (__bf16)y};
   return __builtin_bit_cast(unsigned int, v);
 }
 
-// Scales of one K block as this lane needs them.
-//  1d2d FP32: the lane's activation scale per fragment row, and the (at most two)
-//             weight-block scales of the wave's N range.
-//  1d1d FP32: the activation scales; weight scales are read per column fragment
-//             at promotion time.
-//  1d1d UE8M0: raw UE8M0 codes of the lane's activation rows and weight rows; the
-//             power-of-two scaling is applied by the MFMA itself.
-template <int SFM, int FM, int FN>
-struct BlockScales {
-  float sa[FM];
-  float sb0, sb1;
-  int ea[SFM == SF_1D1D_UE8M0 ? FM : 1];
-  int eb[SFM == SF_1D1D_UE8M0 ? FN : 1];
-};
-
-// Where one wave's share of a tile's stage loads comes from: wave-load q covers 8
-// stage rows of 128 bytes; lane L fills LDS bytes [16L, 16L+16) of it = stage row
+// Where a tile's stage loads come from (all wave-uniform).  Row wave-load q covers 8
+// stage rows of 128 bytes: lane L fills LDS bytes [16L, 16L+16) = stage row
 // r = 8q + L/8, slot L%8, which holds 16-byte chunk (L%8) ^ swz(r) of that row, and
-// swz(8q + L/8) = (L/8) ^ (q & 1).  The wave-uniform part of each address lives in
-// scalar registers; the per-lane part is one 32-bit offset per chunk parity.  Rows
-// past the end of A or B are not loaded (their LDS rows keep stale bytes, which only
-// reach output rows or columns that are never stored).
+// swz(8q + L/8) = (L/8) ^ (q & 1).  Rows past the end of A or B are not loaded (their
+// LDS rows keep stale bytes, which only reach output rows or columns that are never
+// stored).  The K block's scales are copied into the same stage:
+//  * activation scales of rows m0..m0+BM-1 (FP32, or the UE8M0 word holding the
+//    block), contiguous in the MN-major layout: lane L copies rows 4L..4L+3;
+//  * per-row weight scales of columns n0..n0+BN-1 the same way, or, for 128x128
+//    weight blocks, the (at most three) block scales the tile touches, 4 bytes each.
 template <int BM, int BN, int WM, int WN>
 struct Loader {
   const uint8_t* a_tile;  // row tile.m0 of A (this tile's group)
   const uint8_t* b_tile;  // row tile.n0 of B
-  int a_rows, b_rows;     // rows that exist from there on
+  const uint8_t* sa;      // activation scale of row tile.m0, K block 0
+  const uint8_t* sb;      // per-row: weight scale of row tile.n0, K block 0; 1d2d: block scale (n0/128, 0)
+  int a_rows, b_rows;     // rows of A / B that exist from the tile start
+  int sa_rows, sb_rows;   // scale entries that exist from the tile start (align4 padded)
+  int sb_blocks;          // 1d2d: weight-scale blocks that exist from n0/128
 };
 
-template <int BM, int BN, int WM, int WN, int GRP>
+template <int BM, int BN, int WM, int WN, int SFM, int GRP>
 __device__ __forceinline__ void make_loader(const GemmParams& p, const Tile& tl, Loader<BM, BN, WM, WN>& ld) {
   const uint8_t* A = p.a + (GRP == GRP_MASKED ? (int64_t)tl.g * p.a_gstride : 0);
   const uint8_t* B = p.b + (GRP != GRP_DENSE ? (int64_t)tl.g * p.b_gstride : 0);
@@ -166,38 +162,82 @@ __device__ __forceinline__ void make_loader(const GemmParams& p, const Tile& tl,
   ld.b_tile = B + (int64_t)tl.n0 * p.ldb;
   ld.a_rows = p.m - tl.m0;  // m_max rows when masked
   ld.b_rows = p.n - tl.n0;
+  const int64_t sfa_goff = (GRP == GRP_MASKED) ? (int64_t)tl.g * p.sfa_gstride : 0;
+  const int64_t sfb_goff = (GRP != GRP_DENSE) ? (int64_t)tl.g * p.sfb_gstride : 0;
+  ld.sa = (const uint8_t*)p.sfa + 4 * (sfa_goff + tl.m0);
+  ld.sa_rows = (int)p.sfa_stride - tl.m0;
+  if (SFM == SF_1D2D_F32) {
+    const int blk0 = tl.n0 / 128;
+    ld.sb = (const uint8_t*)p.sfb + 4 * (sfb_goff + (int64_t)blk0 * p.sfb_stride);
+    ld.sb_blocks = (p.n + 127) / 128 - blk0;
+    ld.sb_rows = 4;  // unused: 128x128 block scales are read with scalar loads
+  } else {
+    ld.sb = (const uint8_t*)p.sfb + 4 * (sfb_goff + tl.n0);
+    ld.sb_rows = (int)p.sfb_stride - tl.n0;
+  }
 }
 
-// Enqueue the HBM -> LDS copy of K block kb of a tile into stage s.
-template <int BM, int BN, int WM, int WN>
+// Enqueue part `u` of the HBM -> LDS copy of K block kb of a tile into stage s (or,
+// with `sink`, the same loads into the trash region: used when there is nothing left
+// to prefetch, so the instruction stream has no branches).  Parts are spread over
+// the MFMA stream so that load instructions that stall at issue (the memory pipe is
+// the busiest unit here) do not hold back the MFMAs.  Rows past the end of A or B
+// are clamped to the last row; they only reach outputs that are never stored.
+template <int BM, int BN, int WM, int WN, int SFM>
+__device__ __forceinline__ void issue_part(const GemmParams& p, const Loader<BM, BN, WM, WN>& ld, uint8_t* smem,
+                                           int kb, int s, const int u, const bool sink, const int wave,
+                                           const int lane) {
+  using S = Shape<BM, BN, WM, WN>;
+  static_assert((BM / 8) % S::NW == 0, "A and B wave-loads must split at a fixed u");
+  constexpr int UA = BM / 8 / S::NW;  // wave-loads u < UA fill A rows
+  const int q = wave + u * S::NW;
+  const int lr8 = lane >> 3;
+  // per-lane parts of the addresses, opaque to the optimiser so that it rebuilds each
+  // address from scalar values here instead of keeping 64-bit per-lane pointers live
+  uint32_t lane_v = (uint32_t)lane;
+  asm volatile("" : "+v"(lane_v));
+  const uint8_t* src;
+  uint32_t voff;
+  int dst;
+  if (u < UA) {  // A rows (compile-time: the split is at a fixed u)
+    // row within the A tile, clamped to the last row that exists (never negative)
+    const int row = min(8 * q + (int)(lane_v >> 3), ld.a_rows - 1);
+    const int par = (S::NW % 2 == 0) ? (wave & 1) : (u & 1);
+    src = ld.a_tile + (int64_t)kb * BK;
+    voff = (uint32_t)(row * (int)p.lda) + ((((lane_v & 7) ^ (lane_v >> 3)) ^ (uint32_t)par) << 4);
+    dst = s * S::STAGE_BYTES + q * 1024;
+  } else {
+    const bool is_row = q < S::LOADS;
+    // row within the B tile, clamped to the last row that exists (never negative)
+    const int row = min(8 * q - BM + (int)(lane_v >> 3), ld.b_rows - 1);
+    const int par = (S::NW % 2 == 0) ? (wave & 1) : (u & 1);
+    const uint8_t* src_b = ld.b_tile + (int64_t)kb * BK;
+    const uint32_t voff_b = (uint32_t)(row * (int)p.ldb) + ((((lane_v & 7) ^ (lane_v >> 3)) ^ (uint32_t)par) << 4);
+    // scale parts: 4-byte entries, K block kb at kb * stride (FP32) or (kb / 4) * stride (UE8M0
+    // words); lane L copies entries 4L..4L+3, clamped to the entries that exist
+    const int64_t kb_row = (SFM == SF_1D1D_UE8M0) ? (kb >> 2) : kb;
+    const bool is_sa = q == S::LOADS;
+    const bool is_sb = (SFM != SF_1D2D_F32) && q == S::LOADS + 1;
+    const int sc_rows = is_sa ? ld.sa_rows : ld.sb_rows;
+    const uint8_t* src_s = is_sa ? ld.sa + 4 * kb_row * p.sfa_stride : ld.sb + 4 * kb_row * p.sfb_stride;
+    const uint32_t voff_s = (uint32_t)(min((int)(lane_v << 2), sc_rows - 4) << 2);
+    const bool is_sc = is_sa || is_sb;
+    src = is_row ? src_b : (is_sc ? src_s : ld.a_tile + (int64_t)kb * BK);
+    voff = is_row ? voff_b : (is_sc ? voff_s : ((lane_v & 7) << 4));
+    dst = is_row ? s * S::STAGE_BYTES + q * 1024
+                 : (is_sa ? s * S::STAGE_BYTES + S::SA_OFF : (is_sb ? s * S::STAGE_BYTES + S::SB_OFF : S::TRASH_OFF));
+  }
+  if (sink) dst = S::TRASH_OFF;
+  __builtin_amdgcn_global_load_lds((const void*)(src + voff), (DG_LDS void*)(smem + dst), 16, 0, 0);
+}
+
+// The whole copy of K block kb into stage s at once (prologue and tile hand-over).
+template <int BM, int BN, int WM, int WN, int SFM>
 __device__ __forceinline__ void issue_stage(const GemmParams& p, const Loader<BM, BN, WM, WN>& ld, uint8_t* smem,
                                             int kb, int s, const int wave, const int lane) {
   using S = Shape<BM, BN, WM, WN>;
-  static_assert((BM / 8) % S::NW == 0, "A and B wave-loads must split at a fixed u");
-  constexpr int UA = BM / 8 / S::NW;  // wave-loads u < UA fill A rows, the rest B rows
-  const int lr8 = lane >> 3;
-  const int lda = (int)p.lda, ldb = (int)p.ldb;
-  const bool full = ld.a_rows >= BM && ld.b_rows >= BN;  // uniform: no row to skip
-  // per-lane address parts, opaque to the optimiser so it rebuilds each address from a
-  // scalar base every K block instead of keeping 64-bit per-lane pointers live
-  uint32_t off_a = (uint32_t)(lr8 * lda), off_b = (uint32_t)(lr8 * ldb);
-  uint32_t chunk_off = (uint32_t)((lane & 7) ^ lr8) << 4;
-  asm volatile("" : "+v"(off_a), "+v"(off_b), "+v"(chunk_off));
 #pragma unroll
-  for (int u = 0; u < S::LPW; ++u) {
-    const int q = wave + u * S::NW;
-    if (q < S::LOADS) {
-      const int par = (S::NW % 2 == 0) ? (wave & 1) : (u & 1);
-      const bool is_a = u < UA;
-      const int ld_rows = is_a ? lda : ldb;
-      const int row0 = 8 * q - (is_a ? 0 : BM);  // first row of this wave-load (uniform)
-      const uint8_t* base = (is_a ? ld.a_tile : ld.b_tile) + (int64_t)kb * BK + (int64_t)row0 * ld_rows;
-      const uint32_t lane_off = (is_a ? off_a : off_b) + (chunk_off ^ ((uint32_t)par << 4));
-      if (full || lr8 < (is_a ? ld.a_rows : ld.b_rows) - row0)
-        __builtin_amdgcn_global_load_lds((const void*)(base + lane_off),
-                                         (DG_LDS void*)(smem + s * S::STAGE_BYTES + q * 1024), 16, 0, 0);
-    }
-  }
+  for (int u = 0; u < S::LPW; ++u) issue_part<BM, BN, WM, WN, SFM>(p, ld, smem, kb, s, u, false, wave, lane);
 }
 
 // Wait until at most N vector-memory operations of this wave are outstanding and no
@@ -209,64 +249,32 @@ __device__ __forceinline__ void wait_and_barrier() {
   __builtin_amdgcn_s_barrier();
 }
 
-// One output tile: the K loop over 128-long blocks, then the epilogue.  K block 0 of
-// this tile is already in flight into stage `stage0`; during the last K block the
-// first stage of the next tile (if any) is enqueued into the other stage, so it
-// overlaps this tile's last block and epilogue.  `vm_after_prefetch` is a lower bound
-// on this wave's vector-memory operations issued after that prefetch, before this
-// tile's first wait (the previous tile's epilogue stores).
+// One output tile: the K loop over 128-long blocks, then the epilogue.
+//  * K block 0 of this tile (and K block 1 when `pre2`) is already in flight into
+//    stage `stage0` (and the other stage).
+//  * `vm_after` is a lower bound on this wave's vector-memory operations issued after
+//    those prefetches (the previous tile's epilogue stores), so the first waits can
+//    leave the stores in flight.
+//  * During the last K block the first stage of the next tile is enqueued; after it,
+//    once every wave has read the last stage, the next tile's second stage too.
+// Returns the number of vector-memory operations this wave's epilogue issued (a lower
+// bound) and sets `next_pre2`.
 template <int BM, int BN, int WM, int WN, int SFM, int GRP, int OUT, int NF>
 __device__ __forceinline__ int gemm_tile(const GemmParams& p, uint8_t* smem, const Tile& tl,
                                          const Loader<BM, BN, WM, WN>& ld, const bool has_next,
-                                         const Loader<BM, BN, WM, WN>& ld_next, const int stage0,
-                                         const int vm_after_prefetch, const int wave, const int lane) {
+                                         const Loader<BM, BN, WM, WN>& ld_next, const int stage0, const bool pre2,
+                                         const int vm_after, bool& next_pre2, const int wave, const int lane) {
   using S = Shape<BM, BN, WM, WN>;
   constexpr int FM = S::FM, FN = S::FN, TM = S::TM, TN = S::TN;
   const int wm = wave / WN, wn = wave % WN;
   const int lr = lane & 15, lg = lane >> 4;
   const int nkb = p.sf_k;
   const int g = tl.g;
-  const int a_rows = p.m;  // addressable rows of A (m_max for masked)
-
-  // ---- scales
-  const int row0 = tl.m0 + wm * TM + lr;       // lane's row in fragment 0
-  const int nw0 = tl.n0 + wn * TN;             // wave's first column
-  const int64_t sfa_goff = (GRP == GRP_MASKED) ? (int64_t)g * p.sfa_gstride : 0;
-  const int64_t sfb_goff = (GRP != GRP_DENSE) ? (int64_t)g * p.sfb_gstride : 0;
-  int sa_idx[FM];
-#pragma unroll
-  for (int i = 0; i < FM; ++i) sa_idx[i] = min(row0 + 16 * i, a_rows - 1);
+  const int row0 = tl.m0 + wm * TM + lr;  // lane's row in fragment 0
+  const int nw0 = tl.n0 + wn * TN;        // wave's first column
+  // 1d2d: the (at most two) weight-scale blocks of the wave's N range
   const int nb = (p.n + 127) / 128;
   const int blk0 = min(nw0 / 128, nb - 1), blk1 = min(nw0 / 128 + 1, nb - 1);
-  const int n_a4 = (p.n + 3) & ~3;
-  int sb_col[FN];   // 1d1d FP32: first of the lane's four columns in fragment j
-  int sb_row[FN];   // 1d1d UE8M0: the weight row the lane feeds to the MFMA in fragment j
-#pragma unroll
-  for (int j = 0; j < FN; ++j) {
-    sb_col[j] = min(nw0 + 16 * j + 4 * lg, n_a4 - 4);
-    sb_row[j] = min(nw0 + 16 * j + lr, p.n - 1);
-  }
-
-  auto load_scales = [&](int kb, BlockScales<SFM, FM, FN>& sc) {
-    if (SFM == SF_1D1D_UE8M0) {
-      const unsigned int* sa = (const unsigned int*)p.sfa + sfa_goff + (int64_t)(kb >> 2) * p.sfa_stride;
-      const unsigned int* sb = (const unsigned int*)p.sfb + sfb_goff + (int64_t)(kb >> 2) * p.sfb_stride;
-      const int sh = 8 * (kb & 3);
-#pragma unroll
-      for (int i = 0; i < FM; ++i) sc.ea[i] = (sa[sa_idx[i]] >> sh) & 0xFF;
-#pragma unroll
-      for (int j = 0; j < FN; ++j) sc.eb[j] = (sb[sb_row[j]] >> sh) & 0xFF;
-    } else {
-      const float* sa = (const float*)p.sfa + sfa_goff + (int64_t)kb * p.sfa_stride;
-#pragma unroll
-      for (int i = 0; i < FM; ++i) sc.sa[i] = sa[sa_idx[i]];
-      if (SFM == SF_1D2D_F32) {
-        const float* sb = (const float*)p.sfb + sfb_goff;
-        sc.sb0 = sb[(int64_t)blk0 * p.sfb_stride + kb];
-        sc.sb1 = (NF < FN) ? sb[(int64_t)blk1 * p.sfb_stride + kb] : sc.sb0;
-      }
-    }
-  };
 
   float fin[FM][FN][4];
 #pragma unroll
@@ -280,51 +288,64 @@ __device__ __forceinline__ int gemm_tile(const GemmParams& p, uint8_t* smem, con
   const int sw = swz(lr);  // fragment rows start on multiples of 16: swz(row) == swz(lr)
   const int off_lo = ((2 * lg) ^ sw) * 16, off_hi = ((2 * lg + 1) ^ sw) * 16;
 
-  BlockScales<SFM, FM, FN> cur, nxt;
-  load_scales(0, cur);
-
   for (int kb = 0; kb < nkb; ++kb) {
     const int s = (stage0 + kb) & 1;
     // stage s has landed everywhere and nobody still reads stage s^1
-    if (kb == 0) {
-      if (vm_after_prefetch >= FM * FN) wait_and_barrier<FM * FN>();
-      else wait_and_barrier<0>();
-    } else {
-      wait_and_barrier<0>();
-    }
-    if (kb + 1 < nkb) {
-      issue_stage(p, ld, smem, kb + 1, s ^ 1, wave, lane);
-      load_scales(kb + 1, nxt);
-    } else if (has_next) {
-      issue_stage(p, ld_next, smem, 0, s ^ 1, wave, lane);
-    }
+    if ((kb == 0 || (kb == 1 && pre2)) && vm_after >= FM * FN) wait_and_barrier<FM * FN>();
+    else wait_and_barrier<0>();
+    // what this K block enqueues into the free stage s^1, spread over its MFMAs: the
+    // next K block, or the next tile's first block during the last one; with nothing to
+    // prefetch the same loads go to the trash region (no branches in the MFMA stream)
+    const bool last = kb + 1 >= nkb;
+    const bool sink = last ? !has_next : (kb == 0 && pre2);
+    Loader<BM, BN, WM, WN> ld_issue = (last && has_next) ? ld_next : ld;
+    const int kb_issue = last ? (has_next ? 0 : kb) : kb + 1;
+    auto issue_slot = [&](int j) {  // parts issued just before MFMA group j: two per group
+#pragma unroll
+      for (int u = 0; u < S::LPW; ++u)
+        if (min(u / 2, FN - 1) == j)
+          issue_part<BM, BN, WM, WN, SFM>(p, ld_issue, smem, kb_issue, s ^ 1, u, sink, wave, lane);
+    };
     const uint8_t* st = smem + s * S::STAGE_BYTES;
-    // promotion factors for this block
-    float s0[FM], s1[FM];
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      if (SFM == SF_1D2D_F32) {
-        s0[i] = cur.sa[i] * cur.sb0;
-        s1[i] = (NF < FN) ? cur.sa[i] * cur.sb1 : s0[i];
-      } else {
-        s0[i] = s1[i] = cur.sa[i];
-      }
-    }
-    const float* sb_blk = (const float*)p.sfb + sfb_goff + (int64_t)kb * p.sfb_stride;  // 1d1d FP32
-
-    v8i af[FM];
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      const uint8_t* rp = st + (wm * TM + 16 * i + lr) * BK;
-      const v4i lo = *(const v4i*)(rp + off_lo);
-      const v4i hi = *(const v4i*)(rp + off_hi);
-      af[i] = (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-    }
-    auto read_b = [&](int j) -> v8i {
-      const uint8_t* rp = st + (BM + wn * TN + 16 * j + lr) * BK;
+    auto read_frag = [&](int row) -> v8i {
+      const uint8_t* rp = st + row * BK;
       const v4i lo = *(const v4i*)(rp + off_lo);
       const v4i hi = *(const v4i*)(rp + off_hi);
       return (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    };
+    // fragments needed by the first MFMA first, so it waits for as few reads as possible
+    v8i af[FM];
+    v8i bf = read_frag(BM + wn * TN + lr);
+    af[0] = read_frag(wm * TM + lr);
+#pragma unroll
+    for (int i = 1; i < FM; ++i) af[i] = read_frag(wm * TM + 16 * i + lr);
+
+    // promotion factors for this block: activation scales from the stage's scale region,
+    // 128x128 weight-block scales (two per wave at most) by scalar loads
+    float sb_blk0 = 0.f, sb_blk1 = 0.f;
+    if (SFM == SF_1D2D_F32) {
+      const float* sbg = (const float*)p.sfb + (GRP != GRP_DENSE ? (int64_t)g * p.sfb_gstride : 0);
+      sb_blk0 = sbg[__builtin_amdgcn_readfirstlane(blk0 * (int)p.sfb_stride + kb)];
+      if (NF < FN) sb_blk1 = sbg[__builtin_amdgcn_readfirstlane(blk1 * (int)p.sfb_stride + kb)];
+    }
+    float s0[FM], s1[FM];
+    int ea[FM];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const float* sa_l = (const float*)(st + S::SA_OFF);
+      const float sa = sa_l[wm * TM + 16 * i + lr];
+      if (SFM == SF_1D2D_F32) {
+        s0[i] = sa * sb_blk0;
+        s1[i] = (NF < FN) ? sa * sb_blk1 : s0[i];
+      } else if (SFM == SF_1D1D_F32) {
+        s0[i] = s1[i] = sa;
+      } else {
+        ea[i] = (int)((__float_as_uint(sa) >> (8 * (kb & 3))) & 0xFFu);
+      }
+    }
+    auto weight_code = [&](int j) -> int {  // UE8M0 code of the weight row the lane feeds in fragment j
+      const unsigned int* sbw = (const unsigned int*)(st + S::SB_OFF);
+      return (int)((sbw[wn * TN + 16 * j + lr] >> (8 * (kb & 3))) & 0xFFu);
     };
     auto promote = [&](int i, int j, const v4f& acc) {
       if (SFM == SF_1D2D_F32) {
@@ -332,7 +353,7 @@ __device__ __forceinline__ int gemm_tile(const GemmParams& p, uint8_t* smem, con
 #pragma unroll
         for (int v = 0; v < 4; ++v) fin[i][j][v] = __builtin_fmaf(sc, acc[v], fin[i][j][v]);
       } else if (SFM == SF_1D1D_F32) {
-        const v4f w = *(const v4f*)(sb_blk + sb_col[j]);
+        const v4f w = *(const v4f*)(st + S::SB_OFF + 4 * (wn * TN + 16 * j + 4 * lg));
 #pragma unroll
         for (int v = 0; v < 4; ++v) fin[i][j][v] = __builtin_fmaf(s0[i] * w[v], acc[v], fin[i][j][v]);
       } else {
@@ -341,32 +362,47 @@ __device__ __forceinline__ int gemm_tile(const GemmParams& p, uint8_t* smem, con
         for (int v = 0; v < 4; ++v) fin[i][j][v] += acc[v];
       }
     };
-    auto mfma = [&](const v8i& bfr, int i, int j) -> v4f {
-      if (SFM == SF_1D1D_UE8M0)
-        return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bfr, af[i], zero, 0, 0, 0, cur.eb[j], 0,
-                                                                cur.ea[i]);
-      return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bfr, af[i], zero, 0, 0, 0, 0, 0, 0);
-    };
     // Software pipeline: the partial of MFMA t is promoted while MFMA t+1 runs.
     // The weight fragment is the first MFMA operand, so the lane owns row lr and
     // columns 4*lg + v of each 16x16 block.
-    v8i bf = read_b(0);
     v4f acc_prev = zero;
+    int eb = (SFM == SF_1D1D_UE8M0) ? weight_code(0) : 0;
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
+      // pin this slot's loads between MFMA groups (keeps their address arithmetic local)
+      __builtin_amdgcn_sched_barrier(0);
+      issue_slot(j);
+      __builtin_amdgcn_sched_barrier(0);
       v8i bf_next = bf;
-      if (j + 1 < FN) bf_next = read_b(j + 1);
+      int eb_next = eb;
+      if (j + 1 < FN) {
+        bf_next = read_frag(BM + wn * TN + 16 * (j + 1) + lr);
+        if (SFM == SF_1D1D_UE8M0) eb_next = weight_code(j + 1);
+      }
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
-        const v4f acc = mfma(bf, i, j);
+        v4f acc;
+        if (SFM == SF_1D1D_UE8M0)
+          acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf, af[i], zero, 0, 0, 0, eb, 0, ea[i]);
+        else
+          acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf, af[i], zero, 0, 0, 0, 0, 0, 0);
         if (i > 0) promote(i - 1, j, acc_prev);
         else if (j > 0) promote(FM - 1, j - 1, acc_prev);
         acc_prev = acc;
       }
       bf = bf_next;
+      eb = eb_next;
     }
     promote(FM - 1, FN - 1, acc_prev);
-    cur = nxt;
+  }
+
+  // the next tile's second stage goes into the stage this tile read last, once every
+  // wave is done with it
+  next_pre2 = false;
+  if (has_next && nkb >= 2) {
+    wait_and_barrier<63>();
+    issue_stage<BM, BN, WM, WN, SFM>(p, ld_next, smem, 1, (stage0 + nkb - 1) & 1, wave, lane);
+    next_pre2 = true;
   }
 
   // ---- epilogue: lane owns row (m0 + wm*TM + 16i + lr), columns (nw0 + 16j + 4lg .. +3).
@@ -451,25 +487,28 @@ __global__ void __launch_bounds__(WM* WN * 64, 1) gemm_kernel(const GemmParams p
   Tile cur;
   if (!advance(t, cur)) return;
   Loader<BM, BN, WM, WN> ld_cur, ld_next;
-  make_loader<BM, BN, WM, WN, GRP>(p, cur, ld_cur);
-  issue_stage(p, ld_cur, smem, 0, 0, wave, lane);
+  make_loader<BM, BN, WM, WN, SFM, GRP>(p, cur, ld_cur);
+  issue_stage<BM, BN, WM, WN, SFM>(p, ld_cur, smem, 0, 0, wave, lane);
   int stage0 = 0;
   int vm_after = 0;
+  bool pre2 = false;
   for (;;) {
     Tile nxt;
     int tn = t + gridDim.x;
     const bool has_next = advance(tn, nxt);
-    if (has_next) make_loader<BM, BN, WM, WN, GRP>(p, nxt, ld_next);
+    if (has_next) make_loader<BM, BN, WM, WN, SFM, GRP>(p, nxt, ld_next);
+    bool next_pre2 = false;
     if (SFM == SF_1D2D_F32) {
       // leading 16-column fragments of this wave that use the first weight-scale block
       const int ph = ((cur.n0 + wn * S::TN) & 127) >> 4;
       const int nf = min(S::FN, 8 - ph);
       switch (nf) {
-#define DG_NF_CASE(X)                                                                                  \
-  case X:                                                                                              \
-    if constexpr (X <= S::FN)                                                                          \
-      vm_after = gemm_tile<BM, BN, WM, WN, SFM, GRP, OUT, X>(p, smem, cur, ld_cur, has_next, ld_next,  \
-                                                             stage0, vm_after, wave, lane);            \
+#define DG_NF_CASE(X)                                                                                   \
+  case X:                                                                                               \
+    if constexpr (X <= S::FN)                                                                           \
+      vm_after = gemm_tile<BM, BN, WM, WN, SFM, GRP, OUT, X>(p, smem, cur, ld_cur, has_next, ld_next,   \
+                                                             stage0, pre2, vm_after, next_pre2, wave,   \
+                                                             lane);                                     \
     break;
         DG_NF_CASE(1) DG_NF_CASE(2) DG_NF_CASE(3) DG_NF_CASE(4)
         DG_NF_CASE(5) DG_NF_CASE(6) DG_NF_CASE(7) DG_NF_CASE(8)
@@ -477,11 +516,12 @@ __global__ void __launch_bounds__(WM* WN * 64, 1) gemm_kernel(const GemmParams p
         default: break;
       }
     } else {
-      vm_after = gemm_tile<BM, BN, WM, WN, SFM, GRP, OUT, S::FN>(p, smem, cur, ld_cur, has_next, ld_next,
-                                                                stage0, vm_after, wave, lane);
+      vm_after = gemm_tile<BM, BN, WM, WN, SFM, GRP, OUT, S::FN>(p, smem, cur, ld_cur, has_next, ld_next, stage0,
+                                                                pre2, vm_after, next_pre2, wave, lane);
     }
     if (!has_next) break;
     stage0 = (stage0 + p.sf_k) & 1;
+    pre2 = next_pre2;
     cur = nxt;
     ld_cur = ld_next;
     t = tn;
