@@ -92,6 +92,19 @@ def make_dense(spec, nsets, dev):
     return p, sets, flops, alg_bytes
 
 
+def copy_calibration(args, dev):
+    """One plain device copy of a known size: the reference that scales the FETCH_SIZE and
+    WRITE_SIZE counters of the GEMM launches taken in the same profiler run."""
+    if not args.copy_calibration_mb:
+        return
+    src = torch.empty(args.copy_calibration_mb << 20, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -132,13 +145,7 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    if args.copy_calibration_mb:
-        src = torch.empty(args.copy_calibration_mb << 20, dtype=torch.uint8, device=dev).fill_(1)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+    copy_calibration(args, dev)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -252,6 +259,7 @@ def bench_grouped(args, spec, dg, dev):
     for _ in range(args.warmup):
         launch()
     torch.cuda.synchronize()
+    copy_calibration(args, dev)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     e0.record(stream)
