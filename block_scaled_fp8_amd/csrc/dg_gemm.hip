@@ -32,6 +32,8 @@
 //    number of leading 16-column fragments that use the first block's scale is
 //    a template parameter, selected once per tile: the choice per fragment is
 //    resolved at compile time (page "02 · DeepGEMM 技术解析" §2.3).
+#include <utility>
+
 #include "dg_internal.h"
 
 namespace dg {
@@ -84,6 +86,14 @@ __device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
 
+// Wave-uniform read of kernel input that no launch writes (scales, group tables), through
+// the constant address space: it becomes a scalar load, which is not counted in vmcnt, so
+// using its value never waits for the HBM -> LDS copies in flight.
+template <class T>
+__device__ __forceinline__ T load_uniform(const T* base, int64_t i) {
+  return ((const __attribute__((address_space(4))) T*)base)[i];
+}
+
 // Persistent scheduler: logical tile index -> (group, m0, n0).
 template <int GRP, int BM, int BN>
 __device__ __forceinline__ bool get_tile(const GemmParams& p, int t, Tile& tl) {
@@ -93,7 +103,7 @@ __device__ __forceinline__ bool get_tile(const GemmParams& p, int t, Tile& tl) {
     // that share a weight slice run next to each other.
     int base = 0;
     for (int g = 0; g < p.num_groups; ++g) {
-      const int mg = clampi(p.masked_m[g], 0, p.m);
+      const int mg = clampi(load_uniform(p.masked_m, g), 0, p.m);
       const int mt = (mg + BM - 1) / BM;
       const int cnt = mt * p.num_n_tiles;
       if (t < base + cnt) {
@@ -121,7 +131,7 @@ __device__ __forceinline__ bool get_tile(const GemmParams& p, int t, Tile& tl) {
   tl.m_valid = p.m;
   tl.g = 0;
   if (GRP == GRP_CONTIG) {
-    const int g = p.grouped_layout[tl.m0];
+    const int g = load_uniform(p.grouped_layout, tl.m0);
     tl.g = g;
     tl.skip = g < 0 || g >= p.num_groups;
   }
@@ -177,67 +187,115 @@ __device__ __forceinline__ void make_loader(const GemmParams& p, const Tile& tl,
   }
 }
 
-// Enqueue part `u` of the HBM -> LDS copy of K block kb of a tile into stage s (or,
-// with `sink`, the same loads into the trash region: used when there is nothing left
-// to prefetch, so the instruction stream has no branches).  Parts are spread over
-// the MFMA stream so that load instructions that stall at issue (the memory pipe is
-// the busiest unit here) do not hold back the MFMAs.  Rows past the end of A or B
-// are clamped to the last row; they only reach outputs that are never stored.
-template <int BM, int BN, int WM, int WN, int SFM>
+// Per-lane byte offsets of the buffer loads, fixed for the whole kernel.  A row wave-load
+// covers 8 stage rows of 128 bytes: lane L fills LDS bytes [16L, 16L+16) = stage row
+// 8q + L/8, slot L%8, which holds 16-byte chunk (L%8) ^ swz(row) of that row, and
+// swz(8q + L/8) = (L/8) ^ (q & 1).  So the source offset is (L/8) * ld + 16 * chunk,
+// with one variant per parity of q.
+// The parity of q = wave + U * NW is the wave's own parity, flipped by U when NW is odd,
+// so each wave keeps the offsets for its own parity ("same") and the other ("flip"), and
+// every load picks one at compile time.  (Plain scalar members chosen at compile time: a
+// runtime choice between members can turn into a memory access.)
+struct LaneOffsets {
+  uint32_t a_same, a_flip, b_same, b_flip;
+  uint32_t s;  // scale wave-loads: lane L copies 4-byte entries 4L..4L+3
+};
+
+__device__ __forceinline__ LaneOffsets make_lane_offsets(const GemmParams& p, int wave, int lane) {
+  LaneOffsets o;
+  const uint32_t r = (uint32_t)lane >> 3, c = (uint32_t)lane & 7, w = (uint32_t)wave & 1;
+  o.a_same = r * (uint32_t)p.lda + ((c ^ r ^ w) << 4);
+  o.a_flip = r * (uint32_t)p.lda + ((c ^ r ^ w ^ 1u) << 4);
+  o.b_same = r * (uint32_t)p.ldb + ((c ^ r ^ w) << 4);
+  o.b_flip = r * (uint32_t)p.ldb + ((c ^ r ^ w ^ 1u) << 4);
+  o.s = (uint32_t)lane << 4;
+  return o;
+}
+
+// Buffer descriptor over [base, base + bytes): loads at offsets >= bytes return zeros
+// without touching memory, which is how rows past the end of A or B are handled.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  // the values are wave-uniform; say so, so that the descriptor is built in scalar registers
+  const uint64_t b = (uint64_t)base;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+  void* ub = (void*)(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(ub, (short)0, __builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+}
+
+// Enqueue part U of the HBM -> LDS copy of K block kb of a tile into stage s.  Wave-load
+// slot q = wave + U * NW is a row load for q < LOADS, the activation scales for
+// q == LOADS, the per-row weight scales for q == LOADS + 1, and otherwise an empty load
+// (zero bytes: no memory access) into the trash region, so every wave runs the same
+// branch-free instruction stream.  Which kind a slot is depends on the wave only in the
+// last slot; all address arithmetic is on wave-uniform values and the only per-lane term
+// is the fixed lane offset.
+template <int U, int BM, int BN, int WM, int WN, int SFM>
 __device__ __forceinline__ void issue_part(const GemmParams& p, const Loader<BM, BN, WM, WN>& ld, uint8_t* smem,
-                                           int kb, int s, const int u, const bool sink, const int wave,
-                                           const int lane) {
+                                           int kb, int s, const int wave, const LaneOffsets lo) {
   using S = Shape<BM, BN, WM, WN>;
-  static_assert((BM / 8) % S::NW == 0, "A and B wave-loads must split at a fixed u");
-  constexpr int UA = BM / 8 / S::NW;  // wave-loads u < UA fill A rows
-  const int q = wave + u * S::NW;
-  const int lr8 = lane >> 3;
-  // per-lane parts of the addresses, opaque to the optimiser so that it rebuilds each
-  // address from scalar values here instead of keeping 64-bit per-lane pointers live
-  uint32_t lane_v = (uint32_t)lane;
-  asm volatile("" : "+v"(lane_v));
-  const uint8_t* src;
+  static_assert((BM / 8) % S::NW == 0, "A and B wave-loads must split at a fixed slot");
+  constexpr int UA = BM / 8 / S::NW;                         // slots U < UA fill A rows
+  constexpr bool ALL_B = U >= UA && (S::NW - 1) + U * S::NW < S::LOADS;  // every wave loads B rows
+  const int q = wave + U * S::NW;
+  constexpr bool FLIP = (S::NW & 1) && (U & 1);  // parity of q differs from the wave's
+  const uint8_t* base;
+  int bytes;
   uint32_t voff;
   int dst;
-  if (u < UA) {  // A rows (compile-time: the split is at a fixed u)
-    // row within the A tile, clamped to the last row that exists (never negative)
-    const int row = min(8 * q + (int)(lane_v >> 3), ld.a_rows - 1);
-    const int par = (S::NW % 2 == 0) ? (wave & 1) : (u & 1);
-    src = ld.a_tile + (int64_t)kb * BK;
-    voff = (uint32_t)(row * (int)p.lda) + ((((lane_v & 7) ^ (lane_v >> 3)) ^ (uint32_t)par) << 4);
+  if constexpr (U < UA) {  // A rows 8q .. 8q+7 of the tile
+    const int rem = ld.a_rows - 8 * q;
+    base = ld.a_tile + (int64_t)(8 * q) * p.lda + kb * BK;
+    bytes = rem > 0 ? min(rem, 8) * (int)p.lda - kb * BK : 0;
+    voff = FLIP ? lo.a_flip : lo.a_same;
     dst = s * S::STAGE_BYTES + q * 1024;
   } else {
-    const bool is_row = q < S::LOADS;
-    // row within the B tile, clamped to the last row that exists (never negative)
-    const int row = min(8 * q - BM + (int)(lane_v >> 3), ld.b_rows - 1);
-    const int par = (S::NW % 2 == 0) ? (wave & 1) : (u & 1);
-    const uint8_t* src_b = ld.b_tile + (int64_t)kb * BK;
-    const uint32_t voff_b = (uint32_t)(row * (int)p.ldb) + ((((lane_v & 7) ^ (lane_v >> 3)) ^ (uint32_t)par) << 4);
-    // scale parts: 4-byte entries, K block kb at kb * stride (FP32) or (kb / 4) * stride (UE8M0
-    // words); lane L copies entries 4L..4L+3, clamped to the entries that exist
-    const int64_t kb_row = (SFM == SF_1D1D_UE8M0) ? (kb >> 2) : kb;
-    const bool is_sa = q == S::LOADS;
-    const bool is_sb = (SFM != SF_1D2D_F32) && q == S::LOADS + 1;
-    const int sc_rows = is_sa ? ld.sa_rows : ld.sb_rows;
-    const uint8_t* src_s = is_sa ? ld.sa + 4 * kb_row * p.sfa_stride : ld.sb + 4 * kb_row * p.sfb_stride;
-    const uint32_t voff_s = (uint32_t)(min((int)(lane_v << 2), sc_rows - 4) << 2);
-    const bool is_sc = is_sa || is_sb;
-    src = is_row ? src_b : (is_sc ? src_s : ld.a_tile + (int64_t)kb * BK);
-    voff = is_row ? voff_b : (is_sc ? voff_s : ((lane_v & 7) << 4));
-    dst = is_row ? s * S::STAGE_BYTES + q * 1024
-                 : (is_sa ? s * S::STAGE_BYTES + S::SA_OFF : (is_sb ? s * S::STAGE_BYTES + S::SB_OFF : S::TRASH_OFF));
+    // B rows 8q - BM .. 8q - BM + 7 of the tile
+    const int r0 = 8 * q - BM;
+    const int rem = ld.b_rows - r0;
+    const uint8_t* b_base = ld.b_tile + (int64_t)r0 * p.ldb + kb * BK;
+    const int b_bytes = rem > 0 ? min(rem, 8) * (int)p.ldb - kb * BK : 0;
+    const uint32_t b_voff = FLIP ? lo.b_flip : lo.b_same;
+    if constexpr (ALL_B) {
+      base = b_base;
+      bytes = b_bytes;
+      voff = b_voff;
+      dst = s * S::STAGE_BYTES + q * 1024;
+    } else {
+      // scale parts: 4-byte entries, K block kb at kb * stride (FP32) or (kb / 4) * stride
+      // (UE8M0 words); entries exist up to the padded (multiple of 4) scale length
+      const int64_t kb_row = (SFM == SF_1D1D_UE8M0) ? (kb >> 2) : kb;
+      const bool is_row = q < S::LOADS;
+      const bool is_sa = q == S::LOADS;
+      const bool is_sb = (SFM != SF_1D2D_F32) && q == S::LOADS + 1;
+      const uint8_t* sa_base = ld.sa + 4 * kb_row * p.sfa_stride;
+      const uint8_t* sb_base = ld.sb + 4 * kb_row * p.sfb_stride;
+      const int sa_bytes = 4 * max(0, min(ld.sa_rows, BM));
+      const int sb_bytes = 4 * max(0, min(ld.sb_rows, BN));
+      base = is_row ? b_base : (is_sa ? sa_base : sb_base);
+      bytes = is_row ? b_bytes : (is_sa ? sa_bytes : (is_sb ? sb_bytes : 0));
+      voff = is_row ? b_voff : lo.s;
+      dst = is_row ? s * S::STAGE_BYTES + q * 1024
+                   : (is_sa ? s * S::STAGE_BYTES + S::SA_OFF
+                            : (is_sb ? s * S::STAGE_BYTES + S::SB_OFF : S::TRASH_OFF));
+    }
   }
-  if (sink) dst = S::TRASH_OFF;
-  __builtin_amdgcn_global_load_lds((const void*)(src + voff), (DG_LDS void*)(smem + dst), 16, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(base, bytes), (DG_LDS void*)(smem + dst), 16, voff, 0, 0, 0);
+}
+
+template <int BM, int BN, int WM, int WN, int SFM, int... Us>
+__device__ __forceinline__ void issue_parts(const GemmParams& p, const Loader<BM, BN, WM, WN>& ld, uint8_t* smem,
+                                            int kb, int s, const int wave, const LaneOffsets lo,
+                                            std::integer_sequence<int, Us...>) {
+  (issue_part<Us, BM, BN, WM, WN, SFM>(p, ld, smem, kb, s, wave, lo), ...);
 }
 
 // The whole copy of K block kb into stage s at once (prologue and tile hand-over).
 template <int BM, int BN, int WM, int WN, int SFM>
 __device__ __forceinline__ void issue_stage(const GemmParams& p, const Loader<BM, BN, WM, WN>& ld, uint8_t* smem,
-                                            int kb, int s, const int wave, const int lane) {
+                                            int kb, int s, const int wave, const LaneOffsets lo) {
   using S = Shape<BM, BN, WM, WN>;
-#pragma unroll
-  for (int u = 0; u < S::LPW; ++u) issue_part<BM, BN, WM, WN, SFM>(p, ld, smem, kb, s, u, false, wave, lane);
+  issue_parts<BM, BN, WM, WN, SFM>(p, ld, smem, kb, s, wave, lo, std::make_integer_sequence<int, S::LPW>{});
 }
 
 // Wait until at most N vector-memory operations of this wave are outstanding and no
@@ -263,7 +321,8 @@ template <int BM, int BN, int WM, int WN, int SFM, int GRP, int OUT, int NF>
 __device__ __forceinline__ int gemm_tile(const GemmParams& p, uint8_t* smem, const Tile& tl,
                                          const Loader<BM, BN, WM, WN>& ld, const bool has_next,
                                          const Loader<BM, BN, WM, WN>& ld_next, const int stage0, const bool pre2,
-                                         const int vm_after, bool& next_pre2, const int wave, const int lane) {
+                                         const int vm_after, bool& next_pre2, const int wave, const int lane,
+                                         const LaneOffsets lo) {
   using S = Shape<BM, BN, WM, WN>;
   constexpr int FM = S::FM, FN = S::FN, TM = S::TM, TN = S::TN;
   const int wm = wave / WN, wn = wave % WN;
@@ -288,30 +347,31 @@ __device__ __forceinline__ int gemm_tile(const GemmParams& p, uint8_t* smem, con
   const int sw = swz(lr);  // fragment rows start on multiples of 16: swz(row) == swz(lr)
   const int off_lo = ((2 * lg) ^ sw) * 16, off_hi = ((2 * lg + 1) ^ sw) * 16;
 
-  for (int kb = 0; kb < nkb; ++kb) {
+  // One K block.  SPREAD: the copy of K block kb+1 of this tile into the other stage goes
+  // out spread evenly over the block's MFMAs (the memory pipe is the scarcest unit).
+  // Otherwise the block issues no loads, except that the last block of a tile starts by
+  // enqueueing the next tile's first K block into the free stage.
+  auto run_block = [&]<bool SPREAD>(const int kb) {
     const int s = (stage0 + kb) & 1;
     // stage s has landed everywhere and nobody still reads stage s^1
     if ((kb == 0 || (kb == 1 && pre2)) && vm_after >= FM * FN) wait_and_barrier<FM * FN>();
     else wait_and_barrier<0>();
-    // what this K block enqueues into the free stage s^1, spread over its MFMAs: the
-    // next K block, or the next tile's first block during the last one; with nothing to
-    // prefetch the same loads go to the trash region (no branches in the MFMA stream)
-    const bool last = kb + 1 >= nkb;
-    const bool sink = last ? !has_next : (kb == 0 && pre2);
-    Loader<BM, BN, WM, WN> ld_issue = (last && has_next) ? ld_next : ld;
-    const int kb_issue = last ? (has_next ? 0 : kb) : kb + 1;
-    auto issue_slot = [&](int j) {  // parts issued just before MFMA group j: two per group
-#pragma unroll
-      for (int u = 0; u < S::LPW; ++u)
-        if (min(u / 2, FN - 1) == j)
-          issue_part<BM, BN, WM, WN, SFM>(p, ld_issue, smem, kb_issue, s ^ 1, u, sink, wave, lane);
+    if (!SPREAD && kb + 1 >= nkb && has_next) issue_stage<BM, BN, WM, WN, SFM>(p, ld_next, smem, 0, s ^ 1, wave, lo);
+    // slot U goes out just before MFMA number U * FM * FN / LPW of the block
+    auto issue_before = [&]<int U>(const int t) {
+      if constexpr (SPREAD) {
+        if ((U * FM * FN) / S::LPW == t) issue_part<U, BM, BN, WM, WN, SFM>(p, ld, smem, kb + 1, s ^ 1, wave, lo);
+      }
+    };
+    auto issue_all_before = [&]<int... Us>(const int t, std::integer_sequence<int, Us...>) {
+      (issue_before.template operator()<Us>(t), ...);
     };
     const uint8_t* st = smem + s * S::STAGE_BYTES;
     auto read_frag = [&](int row) -> v8i {
       const uint8_t* rp = st + row * BK;
-      const v4i lo = *(const v4i*)(rp + off_lo);
-      const v4i hi = *(const v4i*)(rp + off_hi);
-      return (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+      const v4i lo4 = *(const v4i*)(rp + off_lo);
+      const v4i hi4 = *(const v4i*)(rp + off_hi);
+      return (v8i){lo4.x, lo4.y, lo4.z, lo4.w, hi4.x, hi4.y, hi4.z, hi4.w};
     };
     // fragments needed by the first MFMA first, so it waits for as few reads as possible
     v8i af[FM];
@@ -325,8 +385,8 @@ __device__ __forceinline__ int gemm_tile(const GemmParams& p, uint8_t* smem, con
     float sb_blk0 = 0.f, sb_blk1 = 0.f;
     if (SFM == SF_1D2D_F32) {
       const float* sbg = (const float*)p.sfb + (GRP != GRP_DENSE ? (int64_t)g * p.sfb_gstride : 0);
-      sb_blk0 = sbg[__builtin_amdgcn_readfirstlane(blk0 * (int)p.sfb_stride + kb)];
-      if (NF < FN) sb_blk1 = sbg[__builtin_amdgcn_readfirstlane(blk1 * (int)p.sfb_stride + kb)];
+      sb_blk0 = load_uniform(sbg, __builtin_amdgcn_readfirstlane(blk0 * (int)p.sfb_stride + kb));
+      if (NF < FN) sb_blk1 = load_uniform(sbg, __builtin_amdgcn_readfirstlane(blk1 * (int)p.sfb_stride + kb));
     }
     float s0[FM], s1[FM];
     int ea[FM];
@@ -361,18 +421,19 @@ __device__ __forceinline__ int gemm_tile(const GemmParams& p, uint8_t* smem, con
 #pragma unroll
         for (int v = 0; v < 4; ++v) fin[i][j][v] += acc[v];
       }
+      // keep the promotion at this point of the instruction stream (the compiler would
+      // otherwise gather all of a block's promotions after its MFMAs, keeping every
+      // partial alive at once)
+      asm volatile("" : "+v"(fin[i][j][0]), "+v"(fin[i][j][1]), "+v"(fin[i][j][2]), "+v"(fin[i][j][3]));
     };
-    // Software pipeline: the partial of MFMA t is promoted while MFMA t+1 runs.
+    // Software pipeline: the partial of MFMA t is promoted while MFMA t+1 runs, and each
+    // step (loads, MFMA, promotion of the previous partial) is pinned in program order.
     // The weight fragment is the first MFMA operand, so the lane owns row lr and
     // columns 4*lg + v of each 16x16 block.
     v4f acc_prev = zero;
     int eb = (SFM == SF_1D1D_UE8M0) ? weight_code(0) : 0;
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
-      // pin this slot's loads between MFMA groups (keeps their address arithmetic local)
-      __builtin_amdgcn_sched_barrier(0);
-      issue_slot(j);
-      __builtin_amdgcn_sched_barrier(0);
       v8i bf_next = bf;
       int eb_next = eb;
       if (j + 1 < FN) {
@@ -381,27 +442,37 @@ __device__ __forceinline__ int gemm_tile(const GemmParams& p, uint8_t* smem, con
       }
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
+        issue_all_before(j * FM + i, std::make_integer_sequence<int, S::LPW>{});
         v4f acc;
         if (SFM == SF_1D1D_UE8M0)
           acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf, af[i], zero, 0, 0, 0, eb, 0, ea[i]);
         else
           acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf, af[i], zero, 0, 0, 0, 0, 0, 0);
+        asm volatile("" : "+v"(acc));  // the MFMA stays in this step
         if (i > 0) promote(i - 1, j, acc_prev);
         else if (j > 0) promote(FM - 1, j - 1, acc_prev);
         acc_prev = acc;
+        __builtin_amdgcn_sched_barrier(0);
       }
       bf = bf_next;
       eb = eb_next;
     }
     promote(FM - 1, FN - 1, acc_prev);
-  }
+  };
+
+  // K block 0 prefetches block 1 unless the previous tile already did; the last block
+  // prefetches the next tile's first block
+  if (pre2 || nkb == 1) run_block.template operator()<false>(0);
+  else run_block.template operator()<true>(0);
+  for (int kb = 1; kb + 1 < nkb; ++kb) run_block.template operator()<true>(kb);
+  if (nkb >= 2) run_block.template operator()<false>(nkb - 1);
 
   // the next tile's second stage goes into the stage this tile read last, once every
   // wave is done with it
   next_pre2 = false;
   if (has_next && nkb >= 2) {
     wait_and_barrier<63>();
-    issue_stage<BM, BN, WM, WN, SFM>(p, ld_next, smem, 1, (stage0 + nkb - 1) & 1, wave, lane);
+    issue_stage<BM, BN, WM, WN, SFM>(p, ld_next, smem, 1, (stage0 + nkb - 1) & 1, wave, lo);
     next_pre2 = true;
   }
 
@@ -471,6 +542,7 @@ __global__ void __launch_bounds__(WM* WN * 64, 1) gemm_kernel(const GemmParams p
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int wn = wave % WN;
+  const LaneOffsets lo = make_lane_offsets(p, wave, lane);
   int bid = blockIdx.x;
   if (p.xcd_remap) {  // workgroups are dealt round-robin to the 8 XCDs
     const int per = gridDim.x / 8;
@@ -488,7 +560,7 @@ __global__ void __launch_bounds__(WM* WN * 64, 1) gemm_kernel(const GemmParams p
   if (!advance(t, cur)) return;
   Loader<BM, BN, WM, WN> ld_cur, ld_next;
   make_loader<BM, BN, WM, WN, SFM, GRP>(p, cur, ld_cur);
-  issue_stage<BM, BN, WM, WN, SFM>(p, ld_cur, smem, 0, 0, wave, lane);
+  issue_stage<BM, BN, WM, WN, SFM>(p, ld_cur, smem, 0, 0, wave, lo);
   int stage0 = 0;
   int vm_after = 0;
   bool pre2 = false;
@@ -508,7 +580,7 @@ __global__ void __launch_bounds__(WM* WN * 64, 1) gemm_kernel(const GemmParams p
     if constexpr (X <= S::FN)                                                                           \
       vm_after = gemm_tile<BM, BN, WM, WN, SFM, GRP, OUT, X>(p, smem, cur, ld_cur, has_next, ld_next,   \
                                                              stage0, pre2, vm_after, next_pre2, wave,   \
-                                                             lane);                                     \
+                                                             lane, lo);                                 \
     break;
         DG_NF_CASE(1) DG_NF_CASE(2) DG_NF_CASE(3) DG_NF_CASE(4)
         DG_NF_CASE(5) DG_NF_CASE(6) DG_NF_CASE(7) DG_NF_CASE(8)
@@ -517,7 +589,7 @@ __global__ void __launch_bounds__(WM* WN * 64, 1) gemm_kernel(const GemmParams p
       }
     } else {
       vm_after = gemm_tile<BM, BN, WM, WN, SFM, GRP, OUT, S::FN>(p, smem, cur, ld_cur, has_next, ld_next, stage0,
-                                                                pre2, vm_after, next_pre2, wave, lane);
+                                                                pre2, vm_after, next_pre2, wave, lane, lo);
     }
     if (!has_next) break;
     stage0 = (stage0 + p.sf_k) & 1;
