@@ -42,6 +42,8 @@ def build(verbose=False, jobs=None):
                       "-o", os.path.join(bdir, f"dg_gemm_t{t}.o")])
     steps.append([HIPCC, *FLAGS, "-c", os.path.join(CSRC, "dg_gemm.hip"),
                   "-o", os.path.join(bdir, "dg_gemm_dispatch.o")])
+    steps.append([HIPCC, *FLAGS, "-c", os.path.join(CSRC, "dg_gemm_pipe.hip"),
+                  "-o", os.path.join(bdir, "dg_gemm_pipe.o")])
     steps.append([HIPCC, *FLAGS, "-c", os.path.join(CSRC, "dg_transform.hip"),
                   "-o", os.path.join(bdir, "dg_transform.o")])
     steps.append([HIPCC, "-O2", "-std=c++20", "-fPIC", f"--offload-arch={ARCH}", "-c", os.path.join(CSRC, "dg_api.cpp"),

@@ -176,7 +176,19 @@ int do_launch(dg::GemmParams& p, int kind, int32_t m_rows_for_plan, int32_t m_ma
     fprintf(stderr, "[dg] kind=%d m=%d n=%d k=%d groups=%d sf_mode=%d out=%d -> tile %dx%d (waves %dx%d) tiles=%d grid=%d swizzle_m=%d\n",
             kind, p.m, p.n, p.k, p.num_groups, sfm, out, c.bm, c.bn, c.wm, c.wn, p.total_tiles, pl.grid,
             p.swizzle_m);
-  const hipError_t e = dg::launch_gemm(p, pl.tile, sfm, kind, out, pl.grid, stream);
+  // dense problems with at least two K blocks run the deep-pipelined kernel when it has the
+  // chosen tile (one workgroup per CU: its LDS stages take most of the 160 KiB)
+  const bool use_pipe = kind == dg::GRP_DENSE && p.sf_k >= 2 && !env_int("DG_NO_PIPE", 0) &&
+                        dg::pipe_instantiated(c.bm, c.bn, sfm, kind, out);
+  if (use_pipe) {
+    const int occ = (160 * 1024) / dg::pipe_lds_bytes(c.bm, c.bn, sfm);
+    const int64_t slots = int64_t(num_sms) * (occ < 1 ? 1 : occ);
+    pl.grid = int(pl.tiles < slots ? pl.tiles : slots);
+    p.xcd_remap = (pl.grid % 8 == 0) ? 1 : 0;
+  }
+  if (env_int("DG_PRINT_CONFIGS", 0) && use_pipe) fprintf(stderr, "[dg] deep-pipelined kernel, grid %d\n", pl.grid);
+  const hipError_t e = use_pipe ? dg::launch_pipe(p, c.bm, c.bn, sfm, out, pl.grid, stream)
+                                : dg::launch_gemm(p, pl.tile, sfm, kind, out, pl.grid, stream);
   if (e != hipSuccess) return fail(DG_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return ok();
 }

@@ -1,0 +1,649 @@
+// Deep-pipelined block-scaled FP8 GEMM main loop for gfx950 (MI355X, CDNA4), dense
+// problems with K >= 256.
+//
+// Computes D = C + A . B^T exactly as the kernels in dg_gemm.hip do (E4M3 operands, one
+// activation scale per row and 128-long K block, weight scales per 128x128 block or per
+// row; each 128-K block's partial product promoted into an FP32 accumulator as
+// final += scale_a * scale_b * partial: page "02 · DeepGEMM 技术解析" §2.2, page
+// "第13章 DeepGEMM" §13.3 algorithm box).  What differs is how the work is pipelined:
+//
+//  * LDS holds three A stages and two B stages (256x224 tile: 96 + 56 KiB).  During K
+//    block g the copy of A block g+2 streams in, spread over the block's MFMAs; B block
+//    g+2 goes out in one burst right after the block's single workgroup barrier.  Every
+//    copy therefore has at least one full K block of time to land, and A (the larger
+//    operand) about two.
+//  * The barrier sits at the start of the block's last 16-column group, after the last
+//    LDS read of the block's B stage: it certifies both that block g+1 has landed (each
+//    wave first waits for its own copies with an explicit vmcnt) and that B stage g may
+//    be overwritten.  Right after it every wave reads block g+1's first B fragment and,
+//    one after each of its last MFMAs, the A fragments of block g+1, so the next block
+//    starts with its operands already in registers instead of a burst of LDS reads.
+//  * Promotion runs two MFMAs behind: the FMAs after MFMA t consume the partial of
+//    MFMA t-2, which has finished by then, so no wave stalls on a matrix result; the
+//    scale of a partial is the one of its own K block, also across block boundaries.
+//  * LDS fragment reads use one per-lane base per operand half plus immediate offsets,
+//    so the inner loop spends no VALU on addresses.
+//  * The 16-column fragments of a wave that straddle two 128-wide weight-scale blocks
+//    take the second block's scale from a compile-time split chosen once per tile
+//    (page "02 · DeepGEMM 技术解析" §2.3).
+#include <utility>
+
+#include "dg_internal.h"
+
+namespace dg {
+namespace pipe {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+#define DG_LDS __attribute__((address_space(3)))
+
+constexpr int BK = 128;  // K values per scale block and per MFMA
+constexpr int NA = 3;    // A stages
+constexpr int NB = 2;    // B stages
+
+template <int BM, int BN, int WM, int WN, int SFM>
+struct Geo {
+  static constexpr int NW = WM * WN;
+  static constexpr int TM = BM / WM, TN = BN / WN;
+  static constexpr int FM = TM / 16, FN = TN / 16;
+  static constexpr int A_SLOT = BM * BK, B_SLOT = BN * BK;
+  static constexpr int SA_SLOT = (BM * 4 + 1023) / 1024 * 1024;
+  static constexpr int SB_SLOT = (SFM == SF_1D2D_F32) ? 0 : (BN * 4 + 1023) / 1024 * 1024;
+  static constexpr int A_OFF = 0;
+  static constexpr int B_OFF = A_OFF + NA * A_SLOT;
+  static constexpr int SA_OFF = B_OFF + NB * B_SLOT;
+  static constexpr int SB_OFF = SA_OFF + NA * SA_SLOT;
+  static constexpr int TRASH_OFF = SB_OFF + NB * SB_SLOT;  // 1 KiB sink for padding copies
+  static constexpr int LDS_BYTES = TRASH_OFF + 1024;
+  static constexpr int A_ROWL = BM / 8;  // 1 KiB wave-loads of A rows per block
+  static constexpr int B_ROWL = BN / 8;
+  // wave-loads per wave and block: A rows + activation scales; B rows (+ per-row weight scales)
+  static constexpr int LA = (A_ROWL + 1 + NW - 1) / NW;
+  static constexpr int LB = (B_ROWL + (SFM == SF_1D2D_F32 ? 0 : 1) + NW - 1) / NW;
+  static constexpr int STEPS = FM * FN;
+  static constexpr int TB = (FN - 1) * FM;  // step that holds the barrier
+  static_assert(NW % 2 == 0, "the swizzle parity of a wave's copies must not depend on the copy index");
+  static_assert(TM % 16 == 0 && TN % 16 == 0, "wave tiles are made of 16x16 fragments");
+  static_assert(TN <= 128, "a wave's N range may touch at most two weight-scale blocks");
+  static_assert(BM <= 256 && BN <= 256, "one scale wave-load covers at most 256 rows");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+  static_assert(TB >= LA, "the A copies are spread over the steps before the barrier");
+};
+
+// LDS slot of 16-byte chunk c of row r (rows counted within an operand stage) is
+// c ^ swz(r).  With this key the fragment reads of gfx950's 64-bank LDS are free of bank
+// conflicts: 16 lanes read rows r..r+15 of one chunk column in the same cycle.
+__device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+template <class T>
+__device__ __forceinline__ T load_uniform(const T* base, int64_t i) {
+  return ((const __attribute__((address_space(4))) T*)base)[i];
+}
+
+__device__ __forceinline__ unsigned int pack_bf16x2(float x, float y) {
+  v2bf v = {(__bf16)x, (__bf16)y};
+  return __builtin_bit_cast(unsigned int, v);
+}
+
+// Buffer descriptor over [base, base + bytes): reads at offsets >= bytes return zeros
+// without touching memory (rows past the end of A or B, padding copies).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  const uint64_t b = (uint64_t)base;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+  void* ub = (void*)(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(ub, (short)0, __builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+}
+
+__device__ __forceinline__ void copy_to_lds(const void* base, int bytes, uint32_t voff, uint8_t* smem, int dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(base, bytes), (DG_LDS void*)(smem + dst), 16, voff, 0, 0, 0);
+}
+
+// Keep a promoted fragment at this point of the instruction stream: its FMAs are pure
+// arithmetic that the compiler would otherwise sink to the end of the block, keeping every
+// block partial alive at once.
+__device__ __forceinline__ void pin(float (&f)[4]) {
+  asm volatile("" : "+v"(f[0]), "+v"(f[1]), "+v"(f[2]), "+v"(f[3]));
+}
+
+// Wait until at most N vector-memory operations of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit field");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Wait until at most N vector-memory operations of this wave are outstanding and no
+// LDS or scalar-memory operation is, then synchronise the workgroup.
+template <int N>
+__device__ __forceinline__ void wait_and_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit field");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+  __builtin_amdgcn_s_barrier();
+}
+
+// Output tile t of the workgroup's persistent walk: super-rows of swizzle_m m tiles,
+// walked column by column, so the tiles that run at the same time share A and B rows.
+struct TilePos {
+  int m0, n0;
+  bool valid;  // false past the last tile: its copies are empty
+};
+
+template <int BM, int BN>
+__device__ __forceinline__ TilePos tile_pos(const GemmParams& p, int t) {
+  TilePos r;
+  r.valid = t < p.total_tiles;
+  if (!r.valid) t = 0;
+  const int per_super = p.swizzle_m * p.num_n_tiles;
+  const int sr = t / per_super;
+  const int rem = t - sr * per_super;
+  const int rows = min(p.swizzle_m, p.num_m_tiles - sr * p.swizzle_m);
+  r.m0 = (sr * p.swizzle_m + rem % rows) * BM;
+  r.n0 = (rem / rows) * BN;
+  return r;
+}
+
+// Source of one K block of R operand rows starting at row r0: the buffer range covers the
+// rows that exist, so the copies of missing rows return zeros without touching memory.
+struct OpBlock {
+  const uint8_t* base;  // row r0, byte kb * 128
+  int bytes;
+};
+
+__device__ __forceinline__ OpBlock op_block(const uint8_t* X, int64_t ld, int r0, int rows_total, int R, int kb,
+                                            bool valid) {
+  const int rows = valid ? max(0, min(rows_total - r0, R)) : 0;
+  OpBlock o;
+  o.base = X + (int64_t)r0 * ld + kb * BK;
+  o.bytes = rows > 0 ? rows * (int)ld - kb * BK : 0;
+  return o;
+}
+
+// The K block `ahead` blocks after block kb of tile cur: in cur or in the next tile.
+__device__ __forceinline__ void ahead_block(const TilePos& cur, const TilePos& nxt, int kb, int ahead, int nkb,
+                                            TilePos& t, int& k) {
+  const bool same = kb + ahead < nkb;
+  t.m0 = same ? cur.m0 : nxt.m0;
+  t.n0 = same ? cur.n0 : nxt.n0;
+  t.valid = same ? cur.valid : nxt.valid;
+  k = same ? kb + ahead : kb + ahead - nkb;
+}
+
+// State carried from one K block to the next (and across tiles).
+template <int FM>
+struct Carry {
+  v8i af[FM];           // A fragments of the block about to run
+  v8i bf;               // its first B fragment
+  float sa[FM];         // its activation scales (UE8M0 mode: the packed words, as bits)
+  float sbw0, sbw1;     // 1d2d: its weight-block scales
+  v4f acc1, acc2;       // partials of the previous block's last two MFMAs, not yet promoted
+  float pscale[2];      // their promotion factors (1d2d)
+};
+
+template <int BM, int BN, int WM, int WN, int SFM, int OUT>
+struct Kernel {
+  using G = Geo<BM, BN, WM, WN, SFM>;
+  static constexpr int FM = G::FM, FN = G::FN, TM = G::TM, TN = G::TN, STEPS = G::STEPS;
+  static constexpr int NW = G::NW;
+
+  const GemmParams& p;
+  uint8_t* smem;
+  int wave, lane, wm, wn, lr, lg;
+  // per-lane source offsets of the copies.  Row copy q (q = wave + u*NW) fills 1 KiB of
+  // LDS: lane L writes row 8q + L/8, slot L%8, which holds 16-byte chunk
+  // (L%8) ^ swz(8q + L/8) = (L%8) ^ (L/8) ^ (q&1) of that row; NW is even, so q&1 = wave&1.
+  uint32_t off_a, off_b;  // part 0; part u adds u * 8 * NW * ld
+  uint32_t off_s;         // scale copies: lane L copies the 4-byte entries 4L..4L+3
+  uint32_t a_lo, a_hi, b_lo, b_hi;  // per-lane LDS fragment bases (stage 0)
+  uint32_t sa_lds;                  // per-lane LDS address of its rows' activation scales (stage 0)
+  uint32_t sb_lds;                  // per-lane LDS address of its columns' weight scales (stage 0, 1d1d)
+  int ustep_a, ustep_b;             // 8 * NW * ld
+
+  __device__ __forceinline__ Kernel(const GemmParams& p_, uint8_t* smem_) : p(p_), smem(smem_) {
+    wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    lane = threadIdx.x & 63;
+    wm = wave / WN;
+    wn = wave % WN;
+    lr = lane & 15;
+    lg = lane >> 4;
+    const uint32_t r = (uint32_t)lane >> 3, c = (uint32_t)lane & 7, w = (uint32_t)wave & 1;
+    const uint32_t chunk = (c ^ r ^ w) << 4;
+    off_a = (8u * (uint32_t)wave + r) * (uint32_t)p.lda + chunk;
+    off_b = (8u * (uint32_t)wave + r) * (uint32_t)p.ldb + chunk;
+    off_s = (uint32_t)lane << 4;
+    ustep_a = __builtin_amdgcn_readfirstlane(8 * NW * (int)p.lda);
+    ustep_b = __builtin_amdgcn_readfirstlane(8 * NW * (int)p.ldb);
+    const int sw = swz(lr);
+    const uint32_t lo = (uint32_t)(((2 * lg) ^ sw) * 16), hi = (uint32_t)(((2 * lg + 1) ^ sw) * 16);
+    a_lo = G::A_OFF + (wm * TM + lr) * BK + lo;
+    a_hi = G::A_OFF + (wm * TM + lr) * BK + hi;
+    b_lo = G::B_OFF + (wn * TN + lr) * BK + lo;
+    b_hi = G::B_OFF + (wn * TN + lr) * BK + hi;
+    sa_lds = G::SA_OFF + 4 * (wm * TM + lr);
+    sb_lds = G::SB_OFF + 4 * (wn * TN + 4 * lg);
+  }
+
+  // ---- copies HBM -> LDS --------------------------------------------------------------
+  // Part U of the copy of one A block: rows for the waves whose copy index is below the
+  // row-copy count, the activation scales for the one right after, empty otherwise.  Which
+  // case applies is fixed at compile time except for the one part that straddles them.
+  template <int U>
+  __device__ __forceinline__ void copy_a(const TilePos& t, int kb, int slot) const {
+    constexpr int Q0 = U * NW;
+    const OpBlock ob = op_block(p.a, p.lda, t.m0, p.m, BM, kb, t.valid);
+    const int q = wave + Q0;
+    const int row_dst = G::A_OFF + slot * G::A_SLOT + q * 1024;
+    const uint32_t row_off = off_a + (uint32_t)(U * ustep_a);
+    if constexpr (Q0 + NW <= G::A_ROWL) {
+      copy_to_lds(ob.base, ob.bytes, row_off, smem, row_dst);
+    } else {
+      const int64_t srow = (SFM == SF_1D1D_UE8M0) ? (kb >> 2) : kb;  // UE8M0 words hold four K blocks
+      const uint8_t* sbase = (const uint8_t*)p.sfa + 4 * (srow * p.sfa_stride + t.m0);
+      const int sbytes = t.valid ? 4 * max(0, min((int)p.sfa_stride - t.m0, BM)) : 0;
+      const bool is_row = q < G::A_ROWL, is_s = q == G::A_ROWL;
+      const uint8_t* base = is_row ? ob.base : sbase;
+      const int bytes = is_row ? ob.bytes : (is_s ? sbytes : 0);
+      const int dst = is_row ? row_dst : (is_s ? G::SA_OFF + slot * G::SA_SLOT : G::TRASH_OFF);
+      copy_to_lds(base, bytes, is_row ? row_off : off_s, smem, dst);
+    }
+  }
+
+  // Part U of the copy of one B block (rows, then per-row weight scales in 1d1d modes).
+  template <int U>
+  __device__ __forceinline__ void copy_b(const TilePos& t, int kb, int slot) const {
+    constexpr int Q0 = U * NW;
+    const OpBlock ob = op_block(p.b, p.ldb, t.n0, p.n, BN, kb, t.valid);
+    const int q = wave + Q0;
+    const int row_dst = G::B_OFF + slot * G::B_SLOT + q * 1024;
+    const uint32_t row_off = off_b + (uint32_t)(U * ustep_b);
+    if constexpr (Q0 + NW <= G::B_ROWL) {
+      copy_to_lds(ob.base, ob.bytes, row_off, smem, row_dst);
+    } else {
+      const int64_t srow = (SFM == SF_1D1D_UE8M0) ? (kb >> 2) : kb;
+      const uint8_t* sbase = (const uint8_t*)p.sfb + 4 * (srow * p.sfb_stride + t.n0);
+      const int sbytes = (SFM != SF_1D2D_F32 && t.valid) ? 4 * max(0, min((int)p.sfb_stride - t.n0, BN)) : 0;
+      const bool is_row = q < G::B_ROWL, is_s = (SFM != SF_1D2D_F32) && q == G::B_ROWL;
+      const uint8_t* base = is_row ? ob.base : sbase;
+      const int bytes = is_row ? ob.bytes : (is_s ? sbytes : 0);
+      const int dst = is_row ? row_dst : (is_s ? G::SB_OFF + slot * G::SB_SLOT : G::TRASH_OFF);
+      copy_to_lds(base, bytes, is_row ? row_off : off_s, smem, dst);
+    }
+  }
+
+  template <int... Us>
+  __device__ __forceinline__ void copy_a_all(const TilePos& t, int kb, int slot, std::integer_sequence<int, Us...>) const {
+    (copy_a<Us>(t, kb, slot), ...);
+  }
+  template <int... Us>
+  __device__ __forceinline__ void copy_b_all(const TilePos& t, int kb, int slot, std::integer_sequence<int, Us...>) const {
+    (copy_b<Us>(t, kb, slot), ...);
+  }
+  __device__ __forceinline__ void copy_a_block(const TilePos& t, int kb, int slot) const {
+    copy_a_all(t, kb, slot, std::make_integer_sequence<int, G::LA>{});
+  }
+  __device__ __forceinline__ void copy_b_block(const TilePos& t, int kb, int slot) const {
+    copy_b_all(t, kb, slot, std::make_integer_sequence<int, G::LB>{});
+  }
+
+  // ---- LDS -> registers ---------------------------------------------------------------
+  __device__ __forceinline__ v8i frag(uint32_t lo, uint32_t hi, int off) const {
+    const v4i l4 = *(const v4i*)(smem + lo + off);
+    const v4i h4 = *(const v4i*)(smem + hi + off);
+    return (v8i){l4.x, l4.y, l4.z, l4.w, h4.x, h4.y, h4.z, h4.w};
+  }
+  __device__ __forceinline__ v8i a_frag(int aslot, int i) const {
+    const uint32_t so = (uint32_t)(aslot * G::A_SLOT);
+    return frag(a_lo + so, a_hi + so, i * 16 * BK);
+  }
+  __device__ __forceinline__ v8i b_frag(int bslot, int j) const {
+    const uint32_t so = (uint32_t)(bslot * G::B_SLOT);
+    return frag(b_lo + so, b_hi + so, j * 16 * BK);
+  }
+  __device__ __forceinline__ void read_scales(Carry<FM>& c, int aslot) const {
+    const uint32_t a = sa_lds + (uint32_t)(aslot * G::SA_SLOT);
+#pragma unroll
+    for (int i = 0; i < FM; ++i) c.sa[i] = *(const float*)(smem + a + 64 * i);
+  }
+
+  // 1d2d: weight-block scales of this wave's (at most two) 128-wide column blocks
+  __device__ __forceinline__ void weight_block_scales(const TilePos& t, int kb, float& s0, float& s1) const {
+    const int nw0 = t.n0 + wn * TN;
+    const int nb = (p.n + 127) / 128;
+    const int blk0 = min(nw0 / 128, nb - 1), blk1 = min(nw0 / 128 + 1, nb - 1);
+    const float* sbg = (const float*)p.sfb;
+    s0 = load_uniform(sbg, __builtin_amdgcn_readfirstlane(blk0 * (int)p.sfb_stride + kb));
+    s1 = load_uniform(sbg, __builtin_amdgcn_readfirstlane(blk1 * (int)p.sfb_stride + kb));
+  }
+
+  // ---- one K block ------------------------------------------------------------------
+  // Block g = (tile cur, K index kb) runs out of A stage `as` and B stage `bs`; nxt is the
+  // tile after cur.  `stores_pending`: the previous tile's epilogue issued FM*FN vector
+  // stores since the last barrier.
+  __device__ __forceinline__ void block(Carry<FM>& c, float (&fin)[FM][FN][4], const TilePos& cur,
+                                        const TilePos& nxt, int kb, int nkb, int as, int bs, int nf,
+                                        bool stores_pending) const {
+    // promotion factor of fragment (i, j) of this block: activation scale of row i times the
+    // weight-block scale of column fragment j (the first block's for j < nf, else the second's;
+    // both wave-uniform)
+    float sa[FM];
+    int ea[FM];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      sa[i] = c.sa[i];
+      ea[i] = (int)((__float_as_uint(c.sa[i]) >> (8 * (kb & 3))) & 0xFFu);
+    }
+    const float sbw0 = c.sbw0, sbw1 = c.sbw1;
+    auto factor = [&](int i, int j) -> float {
+      if (SFM == SF_1D2D_F32) return sa[i] * (j < nf ? sbw0 : sbw1);
+      return sa[i];
+    };
+    const uint32_t sbl = sb_lds + (uint32_t)(bs * G::SB_SLOT);
+
+    // copies of A block g+2 go out spread over the steps before the barrier
+    TilePos ta;
+    int kb_a;
+    ahead_block(cur, nxt, kb, 2, nkb, ta, kb_a);
+    const int as2 = as >= NA - 2 ? as - (NA - 2) : as + 2;
+    const int as1 = as >= NA - 1 ? as - (NA - 1) : as + 1;
+
+    const v4f zero = {0.f, 0.f, 0.f, 0.f};
+    v4f r1 = c.acc1, r2 = c.acc2;  // partials of MFMAs t-1 and t-2
+    v8i bf = c.bf, bfn = c.bf;
+    float sbn0 = 0.f, sbn1 = 0.f;
+
+    auto step = [&]<int t>() {
+      constexpr int j = t / FM, i = t % FM;
+      // A copies for block g+2
+      [&]<int... Us>(std::integer_sequence<int, Us...>) {
+        ((t == (Us * G::TB) / G::LA ? copy_a<Us>(ta, kb_a, as2) : void()), ...);
+      }(std::make_integer_sequence<int, G::LA>{});
+      if constexpr (t == G::TB) {
+        // block g+1 has landed everywhere and B stage bs is no longer read by anyone
+        // (only the vmcnt wait depends on the branch: the LDS wait and the barrier stay in
+        // straight-line code, so the compiler knows every earlier LDS read has landed)
+        if (stores_pending) wait_vm<G::LA + FM * FN>();
+        else wait_vm<G::LA>();
+        wait_and_barrier<63>();
+        __builtin_amdgcn_sched_barrier(0);
+        // B block g+2 into the stage block g used
+        TilePos tb;
+        int kb_b;
+        ahead_block(cur, nxt, kb, 2, nkb, tb, kb_b);
+        copy_b_block(tb, kb_b, bs);
+        // first B fragment and scales of block g+1
+        bfn = b_frag(bs ^ 1, 0);
+        TilePos t1;
+        int kb1;
+        ahead_block(cur, nxt, kb, 1, nkb, t1, kb1);
+        if (SFM == SF_1D2D_F32) weight_block_scales(t1, kb1, sbn0, sbn1);
+        read_scales(c, as1);
+      } else if constexpr (i == 0 && j + 1 < FN) {
+        bfn = b_frag(bs, j + 1);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      v4f acc;
+      if (SFM == SF_1D1D_UE8M0) {
+        const unsigned int w = *(const unsigned int*)(smem + G::SB_OFF + bs * G::SB_SLOT + 4 * (wn * TN + 16 * j + lr));
+        const int eb = (int)((w >> (8 * (kb & 3))) & 0xFFu);
+        acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf, c.af[i], zero, 0, 0, 0, eb, 0, ea[i]);
+      } else {
+        acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf, c.af[i], zero, 0, 0, 0, 0, 0, 0);
+      }
+      asm volatile("" : "+v"(acc));
+      __builtin_amdgcn_sched_barrier(0);
+      // after its last use, fragment i of A is replaced by block g+1's
+      if constexpr (t >= G::TB) c.af[i] = a_frag(as1, i);
+      // promote the partial of MFMA t-2 (for t < 2: of the previous block, with its factor)
+      if constexpr (t >= 2) {
+        constexpr int tp = t - 2, jp = tp / FM, ip = tp % FM;
+        if (SFM == SF_1D1D_UE8M0) {
+#pragma unroll
+          for (int v = 0; v < 4; ++v) fin[ip][jp][v] += r2[v];
+        } else if (SFM == SF_1D1D_F32) {
+          const v4f w = *(const v4f*)(smem + sbl + 64 * jp);
+#pragma unroll
+          for (int v = 0; v < 4; ++v) fin[ip][jp][v] = __builtin_fmaf(sa[ip] * w[v], r2[v], fin[ip][jp][v]);
+        } else {
+          const float sc = factor(ip, jp);
+#pragma unroll
+          for (int v = 0; v < 4; ++v) fin[ip][jp][v] = __builtin_fmaf(sc, r2[v], fin[ip][jp][v]);
+        }
+        pin(fin[ip][jp]);
+      } else if constexpr (SFM != SF_1D1D_F32) {
+        constexpr int tp = t - 2 + STEPS, jp = tp / FM, ip = tp % FM;
+        if (SFM == SF_1D1D_UE8M0) {
+#pragma unroll
+          for (int v = 0; v < 4; ++v) fin[ip][jp][v] += r2[v];
+        } else {
+#pragma unroll
+          for (int v = 0; v < 4; ++v) fin[ip][jp][v] = __builtin_fmaf(c.pscale[t], r2[v], fin[ip][jp][v]);
+        }
+        pin(fin[ip][jp]);
+      }
+      r2 = r1;
+      r1 = acc;
+      if constexpr (i == FM - 1) bf = bfn;
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    [&]<int... Ts>(std::integer_sequence<int, Ts...>) {
+      (step.template operator()<Ts>(), ...);
+    }(std::make_integer_sequence<int, STEPS>{});
+
+    c.bf = bfn;
+    c.sbw0 = sbn0;
+    c.sbw1 = sbn1;
+    if (SFM == SF_1D1D_F32) {
+      // the per-column weight scales of the last two partials live in this block's B stage
+      // only: promote them now
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int tp = STEPS - 2 + s, jp = tp / FM, ip = tp % FM;
+        const v4f w = *(const v4f*)(smem + sbl + 64 * jp);
+        const v4f a = s == 0 ? r2 : r1;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) fin[ip][jp][v] = __builtin_fmaf(sa[ip] * w[v], a[v], fin[ip][jp][v]);
+      }
+      c.acc1 = zero;
+      c.acc2 = zero;
+    } else {
+      c.acc1 = r1;
+      c.acc2 = r2;
+      constexpr int t0 = STEPS - 2, t1 = STEPS - 1;
+      c.pscale[0] = factor(t0 % FM, t0 / FM);
+      c.pscale[1] = factor(t1 % FM, t1 / FM);
+    }
+  }
+
+  // Promote the two partials still pending (end of a tile).
+  __device__ __forceinline__ void flush(Carry<FM>& c, float (&fin)[FM][FN][4]) const {
+    const v4f zero = {0.f, 0.f, 0.f, 0.f};
+    if (SFM != SF_1D1D_F32) {
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int tp = STEPS - 2 + s, jp = tp / FM, ip = tp % FM;
+        const v4f a = s == 0 ? c.acc2 : c.acc1;
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          fin[ip][jp][v] = (SFM == SF_1D1D_UE8M0) ? fin[ip][jp][v] + a[v]
+                                                  : __builtin_fmaf(c.pscale[s], a[v], fin[ip][jp][v]);
+      }
+    }
+    c.acc1 = zero;
+    c.acc2 = zero;
+    c.pscale[0] = c.pscale[1] = 0.f;
+  }
+
+  // Store the tile; returns true when every lane issued all FM*FN vector stores.
+  __device__ __forceinline__ bool epilogue(const float (&fin)[FM][FN][4], const TilePos& tr) const {
+    const bool interior = (OUT != OUT_F32_C || p.c_vec) && p.d_vec && tr.m0 + BM <= p.m && tr.n0 + BN <= p.n;
+    char* Dg = (char*)p.d;
+    const int esz = (OUT == OUT_BF16) ? 2 : 4;
+    const int row0 = tr.m0 + wm * TM + lr;
+    const int nw0 = tr.n0 + wn * TN;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int row = row0 + 16 * i;
+      if (row >= p.m) continue;
+      char* drow = Dg + (int64_t)row * p.ldd * esz;
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int col = nw0 + 16 * j + 4 * lg;
+        if (col >= p.n) continue;
+        float o[4] = {fin[i][j][0], fin[i][j][1], fin[i][j][2], fin[i][j][3]};
+        const bool full4 = col + 3 < p.n;
+        if (OUT == OUT_F32_C) {
+          const float* crow = p.c + (int64_t)row * p.ldc;
+          if (full4 && p.c_vec) {
+            const v4f cv = *(const v4f*)(crow + col);
+            o[0] += cv.x; o[1] += cv.y; o[2] += cv.z; o[3] += cv.w;
+          } else {
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+              if (col + v < p.n) o[v] += crow[col + v];
+          }
+        }
+        if (OUT == OUT_BF16) {
+          unsigned short* dp = (unsigned short*)drow + col;
+          const unsigned int w0 = pack_bf16x2(o[0], o[1]), w1 = pack_bf16x2(o[2], o[3]);
+          if (full4 && p.d_vec) {
+            *(v2u*)dp = (v2u){w0, w1};
+          } else {
+            const unsigned short h[4] = {(unsigned short)w0, (unsigned short)(w0 >> 16), (unsigned short)w1,
+                                         (unsigned short)(w1 >> 16)};
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+              if (col + v < p.n) dp[v] = h[v];
+          }
+        } else {
+          float* dp = (float*)drow + col;
+          if (full4 && p.d_vec) {
+            *(v4f*)dp = (v4f){o[0], o[1], o[2], o[3]};
+          } else {
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+              if (col + v < p.n) dp[v] = o[v];
+          }
+        }
+      }
+    }
+    return interior;
+  }
+
+  // All K blocks of one tile, then its epilogue.
+  __device__ __forceinline__ void tile(Carry<FM>& c, const TilePos& cur, const TilePos& nxt, int nkb, int& as,
+                                       int& bs, bool& stores_pending) const {
+    // leading 16-column fragments of this wave that use its first weight-scale block
+    const int nf = __builtin_amdgcn_readfirstlane(min(FN, 8 - (((cur.n0 + wn * TN) & 127) >> 4)));
+    float fin[FM][FN][4];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) fin[i][j][v] = 0.f;
+    for (int kb = 0; kb < nkb; ++kb) {
+      block(c, fin, cur, nxt, kb, nkb, as, bs, nf, stores_pending);
+      stores_pending = false;
+      as = as == NA - 1 ? 0 : as + 1;
+      bs ^= 1;
+    }
+    flush(c, fin);
+    stores_pending = epilogue(fin, cur);
+  }
+};
+
+template <int BM, int BN, int WM, int WN, int SFM, int OUT>
+__global__ void __launch_bounds__(WM* WN * 64, 1) pipe_kernel(const GemmParams p) {
+  using G = Geo<BM, BN, WM, WN, SFM>;
+  using K = Kernel<BM, BN, WM, WN, SFM, OUT>;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[G::LDS_BYTES];
+  const K k(p, smem);
+  int bid = blockIdx.x;
+  if (p.xcd_remap) {  // workgroups are dealt round-robin to the 8 XCDs
+    const int per = gridDim.x / 8;
+    bid = (bid % 8) * per + bid / 8;
+  }
+  int t = bid;
+  TilePos cur = tile_pos<BM, BN>(p, t);
+  if (!cur.valid) return;
+  TilePos nxt = tile_pos<BM, BN>(p, t + gridDim.x);
+  const int nkb = p.sf_k;  // >= 2
+
+  // prologue: blocks 0 and 1 of the first tile, then block 0's operands into registers
+  k.copy_a_block(cur, 0, 0);
+  k.copy_b_block(cur, 0, 0);
+  k.copy_a_block(cur, 1, 1);
+  k.copy_b_block(cur, 1, 1);
+  Carry<K::FM> c;
+  c.sbw0 = c.sbw1 = 0.f;
+  if (SFM == SF_1D2D_F32) k.weight_block_scales(cur, 0, c.sbw0, c.sbw1);
+  wait_and_barrier<G::LA + G::LB>();
+#pragma unroll
+  for (int i = 0; i < K::FM; ++i) c.af[i] = k.a_frag(0, i);
+  c.bf = k.b_frag(0, 0);
+  k.read_scales(c, 0);
+  const v4f zero = {0.f, 0.f, 0.f, 0.f};
+  c.acc1 = zero;
+  c.acc2 = zero;
+  c.pscale[0] = c.pscale[1] = 0.f;
+
+  int as = 0, bs = 0;
+  bool stores_pending = false;
+  for (;;) {
+    k.tile(c, cur, nxt, nkb, as, bs, stores_pending);
+    if (!nxt.valid) break;
+    cur = nxt;
+    t += gridDim.x;
+    nxt = tile_pos<BM, BN>(p, t + gridDim.x);
+  }
+  // no copy may still be writing LDS when the workgroup ends
+  __builtin_amdgcn_s_waitcnt(0 | (7 << 4));
+}
+
+template <int BM, int BN, int WM, int WN, int SFM, int OUT>
+static hipError_t launch_one(const GemmParams& p, int grid, hipStream_t stream) {
+  hipLaunchKernelGGL((pipe_kernel<BM, BN, WM, WN, SFM, OUT>), dim3(grid), dim3(WM * WN * 64), 0, stream, p);
+  return hipGetLastError();
+}
+
+template <int BM, int BN, int WM, int WN>
+static hipError_t launch_tile(const GemmParams& p, int sfm, int out, int grid, hipStream_t s) {
+#define DG_CASE(SF, O) \
+  if (sfm == SF && out == O) return launch_one<BM, BN, WM, WN, SF, O>(p, grid, s);
+  DG_CASE(SF_1D2D_F32, OUT_BF16)
+  DG_CASE(SF_1D2D_F32, OUT_F32)
+  DG_CASE(SF_1D2D_F32, OUT_F32_C)
+#undef DG_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pipe
+
+// Tile shapes with a deep-pipelined instantiation (dense, K >= 256, 1d2d FP32 scales).
+bool pipe_instantiated(int bm, int bn, int sfm, int grp, int out) {
+  if (grp != GRP_DENSE || sfm != SF_1D2D_F32) return false;
+  if (out < OUT_BF16 || out > OUT_F32_C) return false;
+  return (bm == 256 && bn == 224) || (bm == 128 && bn == 192) || (bm == 256 && bn == 192) ||
+         (bm == 128 && bn == 224) || (bm == 128 && bn == 256) || (bm == 128 && bn == 128);
+}
+
+int pipe_lds_bytes(int bm, int bn, int sfm) {
+  const int sa_slot = (bm * 4 + 1023) / 1024 * 1024;
+  const int sb_slot = sfm == SF_1D2D_F32 ? 0 : (bn * 4 + 1023) / 1024 * 1024;
+  return pipe::NA * (bm * pipe::BK + sa_slot) + pipe::NB * (bn * pipe::BK + sb_slot) + 1024;
+}
+
+hipError_t launch_pipe(const GemmParams& p, int bm, int bn, int sfm, int out, int grid, hipStream_t stream) {
+  if (bm == 256 && bn == 224) return pipe::launch_tile<256, 224, 4, 2>(p, sfm, out, grid, stream);
+  if (bm == 256 && bn == 192) return pipe::launch_tile<256, 192, 4, 2>(p, sfm, out, grid, stream);
+  if (bm == 128 && bn == 192) return pipe::launch_tile<128, 192, 2, 2>(p, sfm, out, grid, stream);
+  if (bm == 128 && bn == 224) return pipe::launch_tile<128, 224, 2, 2>(p, sfm, out, grid, stream);
+  if (bm == 128 && bn == 256) return pipe::launch_tile<128, 256, 2, 2>(p, sfm, out, grid, stream);
+  if (bm == 128 && bn == 128) return pipe::launch_tile<128, 128, 2, 2>(p, sfm, out, grid, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace dg
