@@ -172,6 +172,7 @@ int do_launch(dg::GemmParams& p, int kind, int32_t m_rows_for_plan, int32_t m_ma
   const int esz = out == dg::OUT_BF16 ? 2 : 4;
   p.d_vec = (p.ldd % 4 == 0 && (p.d_gstride * esz) % 16 == 0 && aligned16(p.d)) ? 1 : 0;
   p.c_vec = (p.c && p.ldc % 4 == 0 && aligned16(p.c)) ? 1 : 0;
+  p.d_vec16 = ((p.ldd * esz) % 16 == 0 && (p.d_gstride * esz) % 16 == 0 && aligned16(p.d)) ? 1 : 0;
   if (env_int("DG_PRINT_CONFIGS", 0))
     fprintf(stderr, "[dg] kind=%d m=%d n=%d k=%d groups=%d sf_mode=%d out=%d -> tile %dx%d (waves %dx%d) tiles=%d grid=%d swizzle_m=%d\n",
             kind, p.m, p.n, p.k, p.num_groups, sfm, out, c.bm, c.bn, c.wm, c.wn, p.total_tiles, pl.grid,

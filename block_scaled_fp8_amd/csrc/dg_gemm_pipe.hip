@@ -146,20 +146,39 @@ __device__ __forceinline__ TilePos tile_pos(const GemmParams& p, int t) {
   return r;
 }
 
-// Source of one K block of R operand rows starting at row r0: the buffer range covers the
-// rows that exist, so the copies of missing rows return zeros without touching memory.
-struct OpBlock {
-  const uint8_t* base;  // row r0, byte kb * 128
+// Wave-uniform source of the copies of one K block of one operand: its rows (buffer range
+// over the rows that exist, so copies of missing rows return zeros without touching
+// memory) and its scales.  Kept as plain 32-bit values so that they can be computed early
+// and pinned in scalar registers.
+struct Src {
+  uint32_t lo, hi;    // row r0, byte kb * 128
   int bytes;
+  uint32_t slo, shi;  // scale entry of row r0, K block kb
+  int sbytes;
 };
 
-__device__ __forceinline__ OpBlock op_block(const uint8_t* X, int64_t ld, int r0, int rows_total, int R, int kb,
-                                            bool valid) {
+__device__ __forceinline__ void pin_src(Src& s) {
+  asm volatile("" : "+s"(s.lo), "+s"(s.hi), "+s"(s.bytes), "+s"(s.slo), "+s"(s.shi), "+s"(s.sbytes));
+}
+
+__device__ __forceinline__ Src make_src(const uint8_t* X, int64_t ld, int r0, int rows_total, int R, int kb,
+                                        bool valid, const void* sf, int64_t sf_stride, int64_t sf_row,
+                                        bool has_scales) {
   const int rows = valid ? max(0, min(rows_total - r0, R)) : 0;
-  OpBlock o;
-  o.base = X + (int64_t)r0 * ld + kb * BK;
-  o.bytes = rows > 0 ? rows * (int)ld - kb * BK : 0;
-  return o;
+  const uint64_t base = (uint64_t)(X + (int64_t)r0 * ld + kb * BK);
+  const uint64_t sbase = (uint64_t)((const uint8_t*)sf + 4 * (sf_row * sf_stride + r0));
+  Src s;
+  s.lo = __builtin_amdgcn_readfirstlane((uint32_t)base);
+  s.hi = __builtin_amdgcn_readfirstlane((uint32_t)(base >> 32));
+  s.bytes = __builtin_amdgcn_readfirstlane(rows > 0 ? rows * (int)ld - kb * BK : 0);
+  s.slo = __builtin_amdgcn_readfirstlane((uint32_t)sbase);
+  s.shi = __builtin_amdgcn_readfirstlane((uint32_t)(sbase >> 32));
+  s.sbytes = __builtin_amdgcn_readfirstlane((has_scales && valid) ? 4 * max(0, min((int)sf_stride - r0, R)) : 0);
+  return s;
+}
+
+__device__ __forceinline__ const void* src_ptr(uint32_t lo, uint32_t hi) {
+  return (const void*)(((uint64_t)hi << 32) | lo);
 }
 
 // The K block `ahead` blocks after block kb of tile cur: in cur or in the next tile.
@@ -227,65 +246,62 @@ struct Kernel {
   }
 
   // ---- copies HBM -> LDS --------------------------------------------------------------
-  // Part U of the copy of one A block: rows for the waves whose copy index is below the
-  // row-copy count, the activation scales for the one right after, empty otherwise.  Which
+  __device__ __forceinline__ Src a_src(const TilePos& t, int kb) const {
+    const int64_t srow = (SFM == SF_1D1D_UE8M0) ? (kb >> 2) : kb;  // UE8M0 words hold four K blocks
+    return make_src(p.a, p.lda, t.m0, p.m, BM, kb, t.valid, p.sfa, p.sfa_stride, srow, true);
+  }
+  __device__ __forceinline__ Src b_src(const TilePos& t, int kb) const {
+    const int64_t srow = (SFM == SF_1D1D_UE8M0) ? (kb >> 2) : kb;
+    return make_src(p.b, p.ldb, t.n0, p.n, BN, kb, t.valid, p.sfb, p.sfb_stride, srow, SFM != SF_1D2D_F32);
+  }
+
+  // Part U of the copy of one operand block into the stage at LDS offset `dst` (its scales
+  // into `sdst`): rows for the waves whose copy index is below the row-copy count ROWL, the
+  // scales for the one right after (when the operand carries them), empty otherwise.  Which
   // case applies is fixed at compile time except for the one part that straddles them.
-  template <int U>
-  __device__ __forceinline__ void copy_a(const TilePos& t, int kb, int slot) const {
+  template <int U, int ROWL, bool SCALES>
+  __device__ __forceinline__ void copy_part(const Src& s, int dst, int sdst, uint32_t off, int ustep) const {
     constexpr int Q0 = U * NW;
-    const OpBlock ob = op_block(p.a, p.lda, t.m0, p.m, BM, kb, t.valid);
     const int q = wave + Q0;
-    const int row_dst = G::A_OFF + slot * G::A_SLOT + q * 1024;
-    const uint32_t row_off = off_a + (uint32_t)(U * ustep_a);
-    if constexpr (Q0 + NW <= G::A_ROWL) {
-      copy_to_lds(ob.base, ob.bytes, row_off, smem, row_dst);
+    const int row_dst = dst + q * 1024;
+    const uint32_t row_off = off + (uint32_t)(U * ustep);
+    if constexpr (Q0 + NW <= ROWL) {
+      copy_to_lds(src_ptr(s.lo, s.hi), s.bytes, row_off, smem, row_dst);
+    } else if constexpr (Q0 >= ROWL) {
+      const bool is_s = SCALES && q == ROWL;
+      copy_to_lds(src_ptr(s.slo, s.shi), is_s ? s.sbytes : 0, off_s, smem, is_s ? sdst : (int)G::TRASH_OFF);
     } else {
-      const int64_t srow = (SFM == SF_1D1D_UE8M0) ? (kb >> 2) : kb;  // UE8M0 words hold four K blocks
-      const uint8_t* sbase = (const uint8_t*)p.sfa + 4 * (srow * p.sfa_stride + t.m0);
-      const int sbytes = t.valid ? 4 * max(0, min((int)p.sfa_stride - t.m0, BM)) : 0;
-      const bool is_row = q < G::A_ROWL, is_s = q == G::A_ROWL;
-      const uint8_t* base = is_row ? ob.base : sbase;
-      const int bytes = is_row ? ob.bytes : (is_s ? sbytes : 0);
-      const int dst = is_row ? row_dst : (is_s ? G::SA_OFF + slot * G::SA_SLOT : G::TRASH_OFF);
-      copy_to_lds(base, bytes, is_row ? row_off : off_s, smem, dst);
+      const bool is_row = q < ROWL, is_s = SCALES && q == ROWL;
+      if (SCALES) {
+        copy_to_lds(src_ptr(is_row ? s.lo : s.slo, is_row ? s.hi : s.shi), is_row ? s.bytes : (is_s ? s.sbytes : 0),
+                    is_row ? row_off : off_s, smem, is_row ? row_dst : (is_s ? sdst : (int)G::TRASH_OFF));
+      } else {
+        copy_to_lds(src_ptr(s.lo, s.hi), is_row ? s.bytes : 0, row_off, smem, is_row ? row_dst : (int)G::TRASH_OFF);
+      }
     }
   }
-
-  // Part U of the copy of one B block (rows, then per-row weight scales in 1d1d modes).
   template <int U>
-  __device__ __forceinline__ void copy_b(const TilePos& t, int kb, int slot) const {
-    constexpr int Q0 = U * NW;
-    const OpBlock ob = op_block(p.b, p.ldb, t.n0, p.n, BN, kb, t.valid);
-    const int q = wave + Q0;
-    const int row_dst = G::B_OFF + slot * G::B_SLOT + q * 1024;
-    const uint32_t row_off = off_b + (uint32_t)(U * ustep_b);
-    if constexpr (Q0 + NW <= G::B_ROWL) {
-      copy_to_lds(ob.base, ob.bytes, row_off, smem, row_dst);
-    } else {
-      const int64_t srow = (SFM == SF_1D1D_UE8M0) ? (kb >> 2) : kb;
-      const uint8_t* sbase = (const uint8_t*)p.sfb + 4 * (srow * p.sfb_stride + t.n0);
-      const int sbytes = (SFM != SF_1D2D_F32 && t.valid) ? 4 * max(0, min((int)p.sfb_stride - t.n0, BN)) : 0;
-      const bool is_row = q < G::B_ROWL, is_s = (SFM != SF_1D2D_F32) && q == G::B_ROWL;
-      const uint8_t* base = is_row ? ob.base : sbase;
-      const int bytes = is_row ? ob.bytes : (is_s ? sbytes : 0);
-      const int dst = is_row ? row_dst : (is_s ? G::SB_OFF + slot * G::SB_SLOT : G::TRASH_OFF);
-      copy_to_lds(base, bytes, is_row ? row_off : off_s, smem, dst);
-    }
+  __device__ __forceinline__ void copy_a(const Src& s, int slot) const {
+    copy_part<U, G::A_ROWL, true>(s, G::A_OFF + slot * G::A_SLOT, G::SA_OFF + slot * G::SA_SLOT, off_a, ustep_a);
   }
-
-  template <int... Us>
-  __device__ __forceinline__ void copy_a_all(const TilePos& t, int kb, int slot, std::integer_sequence<int, Us...>) const {
-    (copy_a<Us>(t, kb, slot), ...);
+  template <int U>
+  __device__ __forceinline__ void copy_b(const Src& s, int slot) const {
+    copy_part<U, G::B_ROWL, SFM != SF_1D2D_F32>(s, G::B_OFF + slot * G::B_SLOT, G::SB_OFF + slot * G::SB_SLOT,
+                                                 off_b, ustep_b);
   }
   template <int... Us>
-  __device__ __forceinline__ void copy_b_all(const TilePos& t, int kb, int slot, std::integer_sequence<int, Us...>) const {
-    (copy_b<Us>(t, kb, slot), ...);
+  __device__ __forceinline__ void copy_a_all(const Src& s, int slot, std::integer_sequence<int, Us...>) const {
+    (copy_a<Us>(s, slot), ...);
+  }
+  template <int... Us>
+  __device__ __forceinline__ void copy_b_all(const Src& s, int slot, std::integer_sequence<int, Us...>) const {
+    (copy_b<Us>(s, slot), ...);
   }
   __device__ __forceinline__ void copy_a_block(const TilePos& t, int kb, int slot) const {
-    copy_a_all(t, kb, slot, std::make_integer_sequence<int, G::LA>{});
+    copy_a_all(a_src(t, kb), slot, std::make_integer_sequence<int, G::LA>{});
   }
   __device__ __forceinline__ void copy_b_block(const TilePos& t, int kb, int slot) const {
-    copy_b_all(t, kb, slot, std::make_integer_sequence<int, G::LB>{});
+    copy_b_all(b_src(t, kb), slot, std::make_integer_sequence<int, G::LB>{});
   }
 
   // ---- LDS -> registers ---------------------------------------------------------------
@@ -308,23 +324,29 @@ struct Kernel {
     for (int i = 0; i < FM; ++i) c.sa[i] = *(const float*)(smem + a + 64 * i);
   }
 
-  // 1d2d: weight-block scales of this wave's (at most two) 128-wide column blocks
-  __device__ __forceinline__ void weight_block_scales(const TilePos& t, int kb, float& s0, float& s1) const {
+  // 1d2d: indices of the weight-block scales of this wave's (at most two) 128-wide column
+  // blocks for K block kb of tile t
+  __device__ __forceinline__ void weight_block_index(const TilePos& t, int kb, int& i0, int& i1) const {
     const int nw0 = t.n0 + wn * TN;
     const int nb = (p.n + 127) / 128;
     const int blk0 = min(nw0 / 128, nb - 1), blk1 = min(nw0 / 128 + 1, nb - 1);
-    const float* sbg = (const float*)p.sfb;
-    s0 = load_uniform(sbg, __builtin_amdgcn_readfirstlane(blk0 * (int)p.sfb_stride + kb));
-    s1 = load_uniform(sbg, __builtin_amdgcn_readfirstlane(blk1 * (int)p.sfb_stride + kb));
+    i0 = __builtin_amdgcn_readfirstlane(blk0 * (int)p.sfb_stride + kb);
+    i1 = __builtin_amdgcn_readfirstlane(blk1 * (int)p.sfb_stride + kb);
+  }
+  __device__ __forceinline__ void weight_block_scales(const TilePos& t, int kb, float& s0, float& s1) const {
+    int i0, i1;
+    weight_block_index(t, kb, i0, i1);
+    s0 = load_uniform((const float*)p.sfb, i0);
+    s1 = load_uniform((const float*)p.sfb, i1);
   }
 
   // ---- one K block ------------------------------------------------------------------
   // Block g = (tile cur, K index kb) runs out of A stage `as` and B stage `bs`; nxt is the
-  // tile after cur.  `stores_pending`: the previous tile's epilogue issued FM*FN vector
+  // tile after cur.  `stores`: lower bound on the vector stores the previous epilogue issued
   // stores since the last barrier.
   __device__ __forceinline__ void block(Carry<FM>& c, float (&fin)[FM][FN][4], const TilePos& cur,
                                         const TilePos& nxt, int kb, int nkb, int as, int bs, int nf,
-                                        bool stores_pending) const {
+                                        int stores) const {
     // promotion factor of fragment (i, j) of this block: activation scale of row i times the
     // weight-block scale of column fragment j (the first block's for j < nf, else the second's;
     // both wave-uniform)
@@ -342,10 +364,14 @@ struct Kernel {
     };
     const uint32_t sbl = sb_lds + (uint32_t)(bs * G::SB_SLOT);
 
-    // copies of A block g+2 go out spread over the steps before the barrier
-    TilePos ta;
-    int kb_a;
-    ahead_block(cur, nxt, kb, 2, nkb, ta, kb_a);
+    // copies of A block g+2 go out spread over the steps before the barrier (in the first
+    // block of a tile: right after the barrier, because their stage served as the previous
+    // tile's epilogue scratch until every wave has passed it); their source,
+    // the B source of block g+2 and the weight-scale indices of block g+1 are computed in the
+    // first steps (in the shadow of the MFMAs) and pinned, so the scalar work does not pile
+    // up right after the barrier
+    Src asrc = {}, bsrc = {};
+    int wi0 = 0, wi1 = 0;
     const int as2 = as >= NA - 2 ? as - (NA - 2) : as + 2;
     const int as1 = as >= NA - 1 ? as - (NA - 1) : as + 1;
 
@@ -358,27 +384,35 @@ struct Kernel {
       constexpr int j = t / FM, i = t % FM;
       // A copies for block g+2
       [&]<int... Us>(std::integer_sequence<int, Us...>) {
-        ((t == (Us * G::TB) / G::LA ? copy_a<Us>(ta, kb_a, as2) : void()), ...);
+        ((t == 1 + (Us * (G::TB - 1)) / G::LA ? (kb != 0 ? copy_a<Us>(asrc, as2) : void()) : void()), ...);
       }(std::make_integer_sequence<int, G::LA>{});
       if constexpr (t == G::TB) {
-        // block g+1 has landed everywhere and B stage bs is no longer read by anyone
-        // (only the vmcnt wait depends on the branch: the LDS wait and the barrier stay in
-        // straight-line code, so the compiler knows every earlier LDS read has landed)
-        if (stores_pending) wait_vm<G::LA + FM * FN>();
-        else wait_vm<G::LA>();
+        // block g+1 has landed everywhere and B stage bs is no longer read by anyone.  Issued
+        // after this wave's last copy of block g+1: the A copies of block g+2 (LA) or, in a
+        // tile's first block, the previous epilogue's stores (a lower bound is counted).
+        // (Only the vmcnt wait depends on the branch: the LDS wait and the barrier stay in
+        // straight-line code, so the compiler knows every earlier LDS read has landed.)
+        if (kb != 0) {
+          wait_vm<G::LA>();
+        } else if (stores >= STORES_N) {
+          wait_vm<STORES_N>();
+        } else if (stores > 0) {
+          if constexpr (TRANSPOSE) wait_vm<STORES_T>();
+          else wait_vm<0>();
+        } else {
+          wait_vm<0>();
+        }
         wait_and_barrier<63>();
         __builtin_amdgcn_sched_barrier(0);
         // B block g+2 into the stage block g used
-        TilePos tb;
-        int kb_b;
-        ahead_block(cur, nxt, kb, 2, nkb, tb, kb_b);
-        copy_b_block(tb, kb_b, bs);
+        copy_b_all(bsrc, bs, std::make_integer_sequence<int, G::LB>{});
+        if (kb == 0) copy_a_all(asrc, as2, std::make_integer_sequence<int, G::LA>{});
         // first B fragment and scales of block g+1
         bfn = b_frag(bs ^ 1, 0);
-        TilePos t1;
-        int kb1;
-        ahead_block(cur, nxt, kb, 1, nkb, t1, kb1);
-        if (SFM == SF_1D2D_F32) weight_block_scales(t1, kb1, sbn0, sbn1);
+        if (SFM == SF_1D2D_F32) {
+          sbn0 = load_uniform((const float*)p.sfb, wi0);
+          sbn1 = load_uniform((const float*)p.sfb, wi1);
+        }
         read_scales(c, as1);
       } else if constexpr (i == 0 && j + 1 < FN) {
         bfn = b_frag(bs, j + 1);
@@ -394,6 +428,27 @@ struct Kernel {
       }
       asm volatile("" : "+v"(acc));
       __builtin_amdgcn_sched_barrier(0);
+      if constexpr (t == 0) {
+        TilePos ta;
+        int kb_a;
+        ahead_block(cur, nxt, kb, 2, nkb, ta, kb_a);
+        asrc = a_src(ta, kb_a);
+        pin_src(asrc);
+      }
+      if constexpr (t == 1) {
+        TilePos tb;
+        int kb_b;
+        ahead_block(cur, nxt, kb, 2, nkb, tb, kb_b);
+        bsrc = b_src(tb, kb_b);
+        pin_src(bsrc);
+        if (SFM == SF_1D2D_F32) {
+          TilePos t1;
+          int kb1;
+          ahead_block(cur, nxt, kb, 1, nkb, t1, kb1);
+          weight_block_index(t1, kb1, wi0, wi1);
+          asm volatile("" : "+s"(wi0), "+s"(wi1));
+        }
+      }
       // after its last use, fragment i of A is replaced by block g+1's
       if constexpr (t >= G::TB) c.af[i] = a_frag(as1, i);
       // promote the partial of MFMA t-2 (for t < 2: of the previous block, with its factor)
@@ -476,9 +531,49 @@ struct Kernel {
     c.pscale[0] = c.pscale[1] = 0.f;
   }
 
-  // Store the tile; returns true when every lane issued all FM*FN vector stores.
-  __device__ __forceinline__ bool epilogue(const float (&fin)[FM][FN][4], const TilePos& tr) const {
-    const bool interior = (OUT != OUT_F32_C || p.c_vec) && p.d_vec && tr.m0 + BM <= p.m && tr.n0 + BN <= p.n;
+  // Store the tile.  Returns a lower bound on the vector-memory operations every lane of
+  // this wave issued (0 when it cannot tell).
+  //
+  // BF16 interior tiles go through LDS: a lane holds 4 consecutive columns of one row per
+  // fragment, so storing straight from registers makes every 16 lanes of a store touch 16
+  // different rows.  Instead each wave writes one 16-row fragment row at a time into 4 KiB
+  // of scratch (the A stage of the tile's last K block, which no wave reads any more), reads
+  // it back row-major, 16 bytes per lane, and stores it with consecutive lanes on
+  // consecutive addresses.
+  static constexpr int RS = 2 * TN + 16;       // scratch row stride in bytes (spreads rows over banks)
+  static constexpr int CH = TN / 8;            // 16-byte chunks per scratch row
+  static constexpr int SCR = G::A_SLOT / NW;   // scratch bytes per wave
+  static constexpr bool TRANSPOSE = OUT == OUT_BF16 && 16 * RS <= SCR && TN % 8 == 0;
+  static constexpr int RD = (16 * CH + 63) / 64;  // read-back rounds per fragment row
+  static constexpr int STORES_T = TRANSPOSE ? FM * (16 * CH / 64) : 0;  // rounds with every lane active
+  static constexpr int STORES_N = FM * FN < 63 ? FM * FN : 63;
+  static_assert(STORES_T < STORES_N && STORES_N < 64, "vmcnt is a 6-bit field; the two store counts must differ");
+
+  __device__ __forceinline__ int epilogue(const float (&fin)[FM][FN][4], const TilePos& tr, int aslot) const {
+    const bool interior = tr.m0 + BM <= p.m && tr.n0 + BN <= p.n;
+    if (TRANSPOSE && interior && p.d_vec16) {
+      const uint32_t scr = G::A_OFF + aslot * G::A_SLOT + wave * SCR;
+      uint8_t* drow0 = (uint8_t*)p.d + ((int64_t)(tr.m0 + wm * TM) * p.ldd + tr.n0 + wn * TN) * 2;
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const v2u w = {pack_bf16x2(fin[i][j][0], fin[i][j][1]), pack_bf16x2(fin[i][j][2], fin[i][j][3])};
+          *(v2u*)(smem + scr + lr * RS + (16 * j + 4 * lg) * 2) = w;
+        }
+#pragma unroll
+        for (int k = 0; k < RD; ++k) {
+          const int cidx = lane + 64 * k;
+          if (cidx < 16 * CH) {
+            const int r = cidx / CH, cc = cidx - r * CH;
+            const v4i x = *(const v4i*)(smem + scr + r * RS + cc * 16);
+            *(v4i*)(drow0 + ((int64_t)(16 * i + r) * p.ldd + 8 * cc) * 2) = x;
+          }
+        }
+      }
+      return STORES_T;
+    }
+    const bool vec = (OUT != OUT_F32_C || p.c_vec) && p.d_vec && interior;
     char* Dg = (char*)p.d;
     const int esz = (OUT == OUT_BF16) ? 2 : 4;
     const int row0 = tr.m0 + wm * TM + lr;
@@ -529,12 +624,12 @@ struct Kernel {
         }
       }
     }
-    return interior;
+    return vec ? STORES_N : 0;
   }
 
   // All K blocks of one tile, then its epilogue.
   __device__ __forceinline__ void tile(Carry<FM>& c, const TilePos& cur, const TilePos& nxt, int nkb, int& as,
-                                       int& bs, bool& stores_pending) const {
+                                       int& bs, int& stores) const {
     // leading 16-column fragments of this wave that use its first weight-scale block
     const int nf = __builtin_amdgcn_readfirstlane(min(FN, 8 - (((cur.n0 + wn * TN) & 127) >> 4)));
     float fin[FM][FN][4];
@@ -545,13 +640,13 @@ struct Kernel {
 #pragma unroll
         for (int v = 0; v < 4; ++v) fin[i][j][v] = 0.f;
     for (int kb = 0; kb < nkb; ++kb) {
-      block(c, fin, cur, nxt, kb, nkb, as, bs, nf, stores_pending);
-      stores_pending = false;
+      block(c, fin, cur, nxt, kb, nkb, as, bs, nf, stores);
+      stores = 0;
       as = as == NA - 1 ? 0 : as + 1;
       bs ^= 1;
     }
     flush(c, fin);
-    stores_pending = epilogue(fin, cur);
+    stores = epilogue(fin, cur, as == 0 ? NA - 1 : as - 1);
   }
 };
 
@@ -591,9 +686,9 @@ __global__ void __launch_bounds__(WM* WN * 64, 1) pipe_kernel(const GemmParams p
   c.pscale[0] = c.pscale[1] = 0.f;
 
   int as = 0, bs = 0;
-  bool stores_pending = false;
+  int stores = 0;
   for (;;) {
-    k.tile(c, cur, nxt, nkb, as, bs, stores_pending);
+    k.tile(c, cur, nxt, nkb, as, bs, stores);
     if (!nxt.valid) break;
     cur = nxt;
     t += gridDim.x;

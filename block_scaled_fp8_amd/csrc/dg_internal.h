@@ -43,6 +43,7 @@ struct GemmParams {
   int32_t xcd_remap;              // 1: map consecutive logical workgroups onto one XCD
   int32_t d_vec;                  // 1: D rows allow 4-element vector stores (ldd % 4 == 0, 16-B base)
   int32_t c_vec;                  // 1: C rows allow 4-element vector loads
+  int32_t d_vec16;                // 1: D rows and base are 16-byte aligned
 };
 
 struct TileCfg {
