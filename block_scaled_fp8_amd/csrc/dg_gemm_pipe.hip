@@ -344,8 +344,9 @@ struct Kernel {
   // Block g = (tile cur, K index kb) runs out of A stage `as` and B stage `bs`; nxt is the
   // tile after cur.  `stores`: lower bound on the vector stores the previous epilogue issued
   // stores since the last barrier.
+  template <int NF>
   __device__ __forceinline__ void block(Carry<FM>& c, float (&fin)[FM][FN][4], const TilePos& cur,
-                                        const TilePos& nxt, int kb, int nkb, int as, int bs, int nf,
+                                        const TilePos& nxt, int kb, int nkb, int as, int bs,
                                         int stores) const {
     // promotion factor of fragment (i, j) of this block: activation scale of row i times the
     // weight-block scale of column fragment j (the first block's for j < nf, else the second's;
@@ -357,11 +358,14 @@ struct Kernel {
       sa[i] = c.sa[i];
       ea[i] = (int)((__float_as_uint(c.sa[i]) >> (8 * (kb & 3))) & 0xFFu);
     }
-    const float sbw0 = c.sbw0, sbw1 = c.sbw1;
-    auto factor = [&](int i, int j) -> float {
-      if (SFM == SF_1D2D_F32) return sa[i] * (j < nf ? sbw0 : sbw1);
-      return sa[i];
-    };
+    // 1d2d: the factors of fragments j < NF (first weight block) and of the others
+    float f0[FM], f1[FM];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      f0[i] = SFM == SF_1D2D_F32 ? sa[i] * c.sbw0 : sa[i];
+      f1[i] = SFM == SF_1D2D_F32 && NF < FN ? sa[i] * c.sbw1 : f0[i];
+    }
+    auto factor = [&](int i, int j) -> float { return j < NF ? f0[i] : f1[i]; };
     const uint32_t sbl = sb_lds + (uint32_t)(bs * G::SB_SLOT);
 
     // copies of A block g+2 go out spread over the steps before the barrier (in the first
@@ -630,8 +634,6 @@ struct Kernel {
   // All K blocks of one tile, then its epilogue.
   __device__ __forceinline__ void tile(Carry<FM>& c, const TilePos& cur, const TilePos& nxt, int nkb, int& as,
                                        int& bs, int& stores) const {
-    // leading 16-column fragments of this wave that use its first weight-scale block
-    const int nf = __builtin_amdgcn_readfirstlane(min(FN, 8 - (((cur.n0 + wn * TN) & 127) >> 4)));
     float fin[FM][FN][4];
 #pragma unroll
     for (int i = 0; i < FM; ++i)
@@ -639,12 +641,20 @@ struct Kernel {
       for (int j = 0; j < FN; ++j)
 #pragma unroll
         for (int v = 0; v < 4; ++v) fin[i][j][v] = 0.f;
-    for (int kb = 0; kb < nkb; ++kb) {
-      block(c, fin, cur, nxt, kb, nkb, as, bs, nf, stores);
-      stores = 0;
-      as = as == NA - 1 ? 0 : as + 1;
-      bs ^= 1;
-    }
+    // leading 16-column fragments of this wave that use its first weight-scale block: a
+    // compile-time split, so each fragment's factor is chosen without any instruction
+    const int nf = SFM == SF_1D2D_F32 ? min(FN, 8 - (((cur.n0 + wn * TN) & 127) >> 4)) : FN;
+    auto run = [&]<int NF>() {
+      for (int kb = 0; kb < nkb; ++kb) {
+        block<NF>(c, fin, cur, nxt, kb, nkb, as, bs, stores);
+        stores = 0;
+        as = as == NA - 1 ? 0 : as + 1;
+        bs ^= 1;
+      }
+    };
+    [&]<int... Ns>(std::integer_sequence<int, Ns...>) {
+      ((nf == Ns + 1 ? run.template operator()<Ns + 1>() : void()), ...);
+    }(std::make_integer_sequence<int, FN>{});
     flush(c, fin);
     stores = epilogue(fin, cur, as == 0 ? NA - 1 : as - 1);
   }
