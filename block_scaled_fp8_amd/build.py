@@ -42,7 +42,10 @@ def build(verbose=False, jobs=None):
                       "-o", os.path.join(bdir, f"dg_gemm_t{t}.o")])
     steps.append([HIPCC, *FLAGS, "-c", os.path.join(CSRC, "dg_gemm.hip"),
                   "-o", os.path.join(bdir, "dg_gemm_dispatch.o")])
-    steps.append([HIPCC, *FLAGS, "-c", os.path.join(CSRC, "dg_gemm_pipe.hip"),
+    # MFMA results in VGPRs: the block partials feed VALU promotion FMAs directly instead of
+    # being copied out of accumulation registers (matters for the 4-wave tiles, whose
+    # operands spill into AGPRs)
+    steps.append([HIPCC, *FLAGS, "-mllvm", "-amdgpu-mfma-vgpr-form", "-c", os.path.join(CSRC, "dg_gemm_pipe.hip"),
                   "-o", os.path.join(bdir, "dg_gemm_pipe.o")])
     steps.append([HIPCC, *FLAGS, "-c", os.path.join(CSRC, "dg_transform.hip"),
                   "-o", os.path.join(bdir, "dg_transform.o")])

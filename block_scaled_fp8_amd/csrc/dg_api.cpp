@@ -163,7 +163,7 @@ int do_launch(dg::GemmParams& p, int kind, int32_t m_rows_for_plan, int32_t m_ma
     p.num_m_tiles = pl.num_m_tiles;
   }
   p.total_tiles = pl.tiles;
-  const int sw_default = c.bm >= 256 ? 4 : 8;
+  const int sw_default = 8;
   int sw = env_int("DG_SWIZZLE_M", sw_default);
   if (sw < 1) sw = 1;
   p.swizzle_m = sw < p.num_m_tiles ? sw : (p.num_m_tiles > 0 ? p.num_m_tiles : 1);
@@ -179,16 +179,19 @@ int do_launch(dg::GemmParams& p, int kind, int32_t m_rows_for_plan, int32_t m_ma
             p.swizzle_m);
   // dense problems with at least two K blocks run the deep-pipelined kernel when it has the
   // chosen tile (one workgroup per CU: its LDS stages take most of the 160 KiB)
-  const bool use_pipe = kind == dg::GRP_DENSE && p.sf_k >= 2 && !env_int("DG_NO_PIPE", 0) &&
+  const bool use_pipe = (kind == dg::GRP_DENSE || kind == dg::GRP_MASKED) &&
+                        p.sf_k >= dg::pipe_stages_b(kind) && !env_int("DG_NO_PIPE", 0) &&
                         dg::pipe_instantiated(c.bm, c.bn, sfm, kind, out);
   if (use_pipe) {
-    const int occ = (160 * 1024) / dg::pipe_lds_bytes(c.bm, c.bn, sfm);
+    const int occ = (160 * 1024) / dg::pipe_lds_bytes(c.bm, c.bn, sfm, kind);
     const int64_t slots = int64_t(num_sms) * (occ < 1 ? 1 : occ);
-    pl.grid = int(pl.tiles < slots ? pl.tiles : slots);
+    // masked: the tile count is known on the device only; size for every row present
+    const int64_t want = kind == dg::GRP_MASKED ? int64_t(p.num_groups) * p.num_m_tiles * p.num_n_tiles : pl.tiles;
+    pl.grid = int(want < slots ? (want < 1 ? 1 : want) : slots);
     p.xcd_remap = (pl.grid % 8 == 0) ? 1 : 0;
   }
   if (env_int("DG_PRINT_CONFIGS", 0) && use_pipe) fprintf(stderr, "[dg] deep-pipelined kernel, grid %d\n", pl.grid);
-  const hipError_t e = use_pipe ? dg::launch_pipe(p, c.bm, c.bn, sfm, out, pl.grid, stream)
+  const hipError_t e = use_pipe ? dg::launch_pipe(p, c.bm, c.bn, sfm, kind, out, pl.grid, stream)
                                 : dg::launch_gemm(p, pl.tile, sfm, kind, out, pl.grid, stream);
   if (e != hipSuccess) return fail(DG_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return ok();

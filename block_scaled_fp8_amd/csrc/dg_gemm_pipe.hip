@@ -42,10 +42,11 @@ typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 
 constexpr int BK = 128;  // K values per scale block and per MFMA
 constexpr int NA = 3;    // A stages
-constexpr int NB = 2;    // B stages
 
-template <int BM, int BN, int WM, int WN, int SFM>
+// NB_: B stages (2 for dense problems; masked problems stream B from HBM with 3)
+template <int BM, int BN, int WM, int WN, int SFM, int NB_ = 2>
 struct Geo {
+  static constexpr int NB = NB_;
   static constexpr int NW = WM * WN;
   static constexpr int TM = BM / WM, TN = BN / WN;
   static constexpr int FM = TM / 16, FN = TN / 16;
@@ -71,6 +72,7 @@ struct Geo {
   static_assert(BM <= 256 && BN <= 256, "one scale wave-load covers at most 256 rows");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
   static_assert(TB >= LA, "the A copies are spread over the steps before the barrier");
+  static_assert(NB == 2 || NB == 3, "B stages");
 };
 
 // LDS slot of 16-byte chunk c of row r (rows counted within an operand stage) is
@@ -125,16 +127,45 @@ __device__ __forceinline__ void wait_and_barrier() {
   __builtin_amdgcn_s_barrier();
 }
 
-// Output tile t of the workgroup's persistent walk: super-rows of swizzle_m m tiles,
-// walked column by column, so the tiles that run at the same time share A and B rows.
+// Output tile t of the workgroup's persistent walk.
+//  * Dense: super-rows of swizzle_m m tiles, walked column by column, so the tiles that run
+//    at the same time share A and B rows.
+//  * Masked (page "02 · DeepGEMM 技术解析" §5.2): only the tiles holding valid rows exist.
+//    Groups in order; within a group n tiles outer and m tiles inner, so the m tiles that
+//    read the same weight slice run next to each other.  masked_m is read on the device and
+//    clamped to [0, M_max].
 struct TilePos {
-  int m0, n0;
+  int g;       // group (masked)
+  int m0, n0;  // first row (within the group) and first column
+  int mv;      // rows that exist: M (dense) or the group's valid rows (masked)
   bool valid;  // false past the last tile: its copies are empty
 };
 
-template <int BM, int BN>
+template <int BM, int BN, int GRP>
 __device__ __forceinline__ TilePos tile_pos(const GemmParams& p, int t) {
   TilePos r;
+  r.g = 0;
+  if (GRP == GRP_MASKED) {
+    r.valid = false;
+    r.m0 = r.n0 = r.mv = 0;
+    int base = 0;
+    for (int g = 0; g < p.num_groups; ++g) {
+      const int mg = min(max(load_uniform(p.masked_m, g), 0), p.m);
+      const int mt = (mg + BM - 1) / BM;
+      const int cnt = mt * p.num_n_tiles;
+      if (t < base + cnt) {
+        const int loc = t - base;
+        r.g = g;
+        r.n0 = (loc / mt) * BN;
+        r.m0 = (loc % mt) * BM;
+        r.mv = mg;
+        r.valid = true;
+        break;
+      }
+      base += cnt;
+    }
+    return r;
+  }
   r.valid = t < p.total_tiles;
   if (!r.valid) t = 0;
   const int per_super = p.swizzle_m * p.num_n_tiles;
@@ -143,6 +174,7 @@ __device__ __forceinline__ TilePos tile_pos(const GemmParams& p, int t) {
   const int rows = min(p.swizzle_m, p.num_m_tiles - sr * p.swizzle_m);
   r.m0 = (sr * p.swizzle_m + rem % rows) * BM;
   r.n0 = (rem / rows) * BN;
+  r.mv = p.m;
   return r;
 }
 
@@ -185,8 +217,10 @@ __device__ __forceinline__ const void* src_ptr(uint32_t lo, uint32_t hi) {
 __device__ __forceinline__ void ahead_block(const TilePos& cur, const TilePos& nxt, int kb, int ahead, int nkb,
                                             TilePos& t, int& k) {
   const bool same = kb + ahead < nkb;
+  t.g = same ? cur.g : nxt.g;
   t.m0 = same ? cur.m0 : nxt.m0;
   t.n0 = same ? cur.n0 : nxt.n0;
+  t.mv = same ? cur.mv : nxt.mv;
   t.valid = same ? cur.valid : nxt.valid;
   k = same ? kb + ahead : kb + ahead - nkb;
 }
@@ -200,13 +234,15 @@ struct Carry {
   float sbw0, sbw1;     // 1d2d: its weight-block scales
   v4f acc1, acc2;       // partials of the previous block's last two MFMAs, not yet promoted
   float pscale[2];      // their promotion factors (1d2d)
+  unsigned int ebw;     // UE8M0: packed weight-scale word of the lane's row in the first B fragment
 };
 
-template <int BM, int BN, int WM, int WN, int SFM, int OUT>
+template <int BM, int BN, int WM, int WN, int SFM, int OUT, int GRP, int NB>
 struct Kernel {
-  using G = Geo<BM, BN, WM, WN, SFM>;
+  using G = Geo<BM, BN, WM, WN, SFM, NB>;
   static constexpr int FM = G::FM, FN = G::FN, TM = G::TM, TN = G::TN, STEPS = G::STEPS;
   static constexpr int NW = G::NW;
+  static __device__ __forceinline__ int next_b(int b) { return b == NB - 1 ? 0 : b + 1; }
 
   const GemmParams& p;
   uint8_t* smem;
@@ -248,11 +284,23 @@ struct Kernel {
   // ---- copies HBM -> LDS --------------------------------------------------------------
   __device__ __forceinline__ Src a_src(const TilePos& t, int kb) const {
     const int64_t srow = (SFM == SF_1D1D_UE8M0) ? (kb >> 2) : kb;  // UE8M0 words hold four K blocks
-    return make_src(p.a, p.lda, t.m0, p.m, BM, kb, t.valid, p.sfa, p.sfa_stride, srow, true);
+    const uint8_t* A = p.a;
+    const uint8_t* SA = (const uint8_t*)p.sfa;
+    if (GRP == GRP_MASKED) {
+      A += (int64_t)t.g * p.a_gstride;
+      SA += 4 * (int64_t)t.g * p.sfa_gstride;
+    }
+    return make_src(A, p.lda, t.m0, t.mv, BM, kb, t.valid, SA, p.sfa_stride, srow, true);
   }
   __device__ __forceinline__ Src b_src(const TilePos& t, int kb) const {
     const int64_t srow = (SFM == SF_1D1D_UE8M0) ? (kb >> 2) : kb;
-    return make_src(p.b, p.ldb, t.n0, p.n, BN, kb, t.valid, p.sfb, p.sfb_stride, srow, SFM != SF_1D2D_F32);
+    const uint8_t* B = p.b;
+    const uint8_t* SB = (const uint8_t*)p.sfb;
+    if (GRP == GRP_MASKED) {
+      B += (int64_t)t.g * p.b_gstride;
+      SB += 4 * (int64_t)t.g * p.sfb_gstride;
+    }
+    return make_src(B, p.ldb, t.n0, p.n, BN, kb, t.valid, SB, p.sfb_stride, srow, SFM != SF_1D2D_F32);
   }
 
   // Part U of the copy of one operand block into the stage at LDS offset `dst` (its scales
@@ -318,6 +366,10 @@ struct Kernel {
     const uint32_t so = (uint32_t)(bslot * G::B_SLOT);
     return frag(b_lo + so, b_hi + so, j * 16 * BK);
   }
+  // UE8M0: the packed weight-scale word of the lane's B row in fragment j of B stage bslot
+  __device__ __forceinline__ unsigned int weight_word(int bslot, int j) const {
+    return *(const unsigned int*)(smem + G::SB_OFF + bslot * G::SB_SLOT + 4 * (wn * TN + 16 * j + lr));
+  }
   __device__ __forceinline__ void read_scales(Carry<FM>& c, int aslot) const {
     const uint32_t a = sa_lds + (uint32_t)(aslot * G::SA_SLOT);
 #pragma unroll
@@ -330,8 +382,9 @@ struct Kernel {
     const int nw0 = t.n0 + wn * TN;
     const int nb = (p.n + 127) / 128;
     const int blk0 = min(nw0 / 128, nb - 1), blk1 = min(nw0 / 128 + 1, nb - 1);
-    i0 = __builtin_amdgcn_readfirstlane(blk0 * (int)p.sfb_stride + kb);
-    i1 = __builtin_amdgcn_readfirstlane(blk1 * (int)p.sfb_stride + kb);
+    const int gofs = GRP == GRP_MASKED ? t.g * (int)p.sfb_gstride : 0;
+    i0 = __builtin_amdgcn_readfirstlane(gofs + blk0 * (int)p.sfb_stride + kb);
+    i1 = __builtin_amdgcn_readfirstlane(gofs + blk1 * (int)p.sfb_stride + kb);
   }
   __device__ __forceinline__ void weight_block_scales(const TilePos& t, int kb, float& s0, float& s1) const {
     int i0, i1;
@@ -378,10 +431,13 @@ struct Kernel {
     int wi0 = 0, wi1 = 0;
     const int as2 = as >= NA - 2 ? as - (NA - 2) : as + 2;
     const int as1 = as >= NA - 1 ? as - (NA - 1) : as + 1;
+    const int bs1 = next_b(bs);
+    const int kshift = 8 * (kb & 3);  // UE8M0: byte of this K block in the packed words
 
     const v4f zero = {0.f, 0.f, 0.f, 0.f};
     v4f r1 = c.acc1, r2 = c.acc2;  // partials of MFMAs t-1 and t-2
     v8i bf = c.bf, bfn = c.bf;
+    unsigned int ebw = c.ebw, ebwn = c.ebw;
     float sbn0 = 0.f, sbn1 = 0.f;
 
     auto step = [&]<int t>() {
@@ -391,28 +447,37 @@ struct Kernel {
         ((t == 1 + (Us * (G::TB - 1)) / G::LA ? (kb != 0 ? copy_a<Us>(asrc, as2) : void()) : void()), ...);
       }(std::make_integer_sequence<int, G::LA>{});
       if constexpr (t == G::TB) {
-        // block g+1 has landed everywhere and B stage bs is no longer read by anyone.  Issued
-        // after this wave's last copy of block g+1: the A copies of block g+2 (LA) or, in a
-        // tile's first block, the previous epilogue's stores (a lower bound is counted).
+        // Block g+1 has landed everywhere and B stage bs is no longer read by anyone.  Each
+        // wave first waits until its own copies of block g+1 have landed; what it issued after
+        // the last of them may stay in flight:
+        //  * 2 B stages: the last is B(g+1) (previous barrier); after it come the A copies of
+        //    block g+2 (LA), or, in a tile's first block (whose A copies wait for the barrier),
+        //    only the previous epilogue's stores (a lower bound is counted);
+        //  * 3 B stages: the last is A(g+1) (previous block); after it come B(g+2) (LB) and
+        //    A(g+2) (LA); in a tile's first block B(g+2) and the stores; in its second block
+        //    only A(g+2), because the first block issued A(g+1) after B(g+2).
         // (Only the vmcnt wait depends on the branch: the LDS wait and the barrier stay in
         // straight-line code, so the compiler knows every earlier LDS read has landed.)
-        if (kb != 0) {
+        if (kb > 1 || (kb == 1 && NB == 2)) {
+          wait_vm<(NB == 2 ? G::LA : G::LA + G::LB)>();
+        } else if (kb == 1) {
           wait_vm<G::LA>();
         } else if (stores >= STORES_N) {
-          wait_vm<STORES_N>();
+          wait_vm<(NB == 2 ? 0 : G::LB) + STORES_N>();
         } else if (stores > 0) {
-          if constexpr (TRANSPOSE) wait_vm<STORES_T>();
-          else wait_vm<0>();
+          if constexpr (TRANSPOSE) wait_vm<(NB == 2 ? 0 : G::LB) + STORES_T>();
+          else wait_vm<(NB == 2 ? 0 : G::LB)>();
         } else {
-          wait_vm<0>();
+          wait_vm<(NB == 2 ? 0 : G::LB)>();
         }
         wait_and_barrier<63>();
         __builtin_amdgcn_sched_barrier(0);
-        // B block g+2 into the stage block g used
+        // B block g+NB into the stage block g used
         copy_b_all(bsrc, bs, std::make_integer_sequence<int, G::LB>{});
         if (kb == 0) copy_a_all(asrc, as2, std::make_integer_sequence<int, G::LA>{});
         // first B fragment and scales of block g+1
-        bfn = b_frag(bs ^ 1, 0);
+        bfn = b_frag(bs1, 0);
+        if (SFM == SF_1D1D_UE8M0) ebwn = weight_word(bs1, 0);
         if (SFM == SF_1D2D_F32) {
           sbn0 = load_uniform((const float*)p.sfb, wi0);
           sbn1 = load_uniform((const float*)p.sfb, wi1);
@@ -420,12 +485,12 @@ struct Kernel {
         read_scales(c, as1);
       } else if constexpr (i == 0 && j + 1 < FN) {
         bfn = b_frag(bs, j + 1);
+        if (SFM == SF_1D1D_UE8M0) ebwn = weight_word(bs, j + 1);
       }
       __builtin_amdgcn_sched_barrier(0);
       v4f acc;
       if (SFM == SF_1D1D_UE8M0) {
-        const unsigned int w = *(const unsigned int*)(smem + G::SB_OFF + bs * G::SB_SLOT + 4 * (wn * TN + 16 * j + lr));
-        const int eb = (int)((w >> (8 * (kb & 3))) & 0xFFu);
+        const int eb = (int)((ebw >> kshift) & 0xFFu);
         acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf, c.af[i], zero, 0, 0, 0, eb, 0, ea[i]);
       } else {
         acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf, c.af[i], zero, 0, 0, 0, 0, 0, 0);
@@ -442,7 +507,7 @@ struct Kernel {
       if constexpr (t == 1) {
         TilePos tb;
         int kb_b;
-        ahead_block(cur, nxt, kb, 2, nkb, tb, kb_b);
+        ahead_block(cur, nxt, kb, NB, nkb, tb, kb_b);
         bsrc = b_src(tb, kb_b);
         pin_src(bsrc);
         if (SFM == SF_1D2D_F32) {
@@ -484,7 +549,10 @@ struct Kernel {
       }
       r2 = r1;
       r1 = acc;
-      if constexpr (i == FM - 1) bf = bfn;
+      if constexpr (i == FM - 1) {
+        bf = bfn;
+        ebw = ebwn;
+      }
       __builtin_amdgcn_sched_barrier(0);
     };
     [&]<int... Ts>(std::integer_sequence<int, Ts...>) {
@@ -492,6 +560,7 @@ struct Kernel {
     }(std::make_integer_sequence<int, STEPS>{});
 
     c.bf = bfn;
+    c.ebw = ebwn;
     c.sbw0 = sbn0;
     c.sbw1 = sbn1;
     if (SFM == SF_1D1D_F32) {
@@ -554,10 +623,13 @@ struct Kernel {
   static_assert(STORES_T < STORES_N && STORES_N < 64, "vmcnt is a 6-bit field; the two store counts must differ");
 
   __device__ __forceinline__ int epilogue(const float (&fin)[FM][FN][4], const TilePos& tr, int aslot) const {
-    const bool interior = tr.m0 + BM <= p.m && tr.n0 + BN <= p.n;
+    const bool interior = tr.m0 + BM <= tr.mv && tr.n0 + BN <= p.n;
+    const int esz = (OUT == OUT_BF16) ? 2 : 4;
+    char* Dg = (char*)p.d;
+    if (GRP == GRP_MASKED) Dg += (int64_t)tr.g * p.d_gstride * esz;
     if (TRANSPOSE && interior && p.d_vec16) {
       const uint32_t scr = G::A_OFF + aslot * G::A_SLOT + wave * SCR;
-      uint8_t* drow0 = (uint8_t*)p.d + ((int64_t)(tr.m0 + wm * TM) * p.ldd + tr.n0 + wn * TN) * 2;
+      uint8_t* drow0 = (uint8_t*)Dg + ((int64_t)(tr.m0 + wm * TM) * p.ldd + tr.n0 + wn * TN) * 2;
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
 #pragma unroll
@@ -578,14 +650,12 @@ struct Kernel {
       return STORES_T;
     }
     const bool vec = (OUT != OUT_F32_C || p.c_vec) && p.d_vec && interior;
-    char* Dg = (char*)p.d;
-    const int esz = (OUT == OUT_BF16) ? 2 : 4;
     const int row0 = tr.m0 + wm * TM + lr;
     const int nw0 = tr.n0 + wn * TN;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       const int row = row0 + 16 * i;
-      if (row >= p.m) continue;
+      if (row >= tr.mv) continue;
       char* drow = Dg + (int64_t)row * p.ldd * esz;
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
@@ -649,7 +719,7 @@ struct Kernel {
         block<NF>(c, fin, cur, nxt, kb, nkb, as, bs, stores);
         stores = 0;
         as = as == NA - 1 ? 0 : as + 1;
-        bs ^= 1;
+        bs = next_b(bs);
       }
     };
     [&]<int... Ns>(std::integer_sequence<int, Ns...>) {
@@ -660,10 +730,10 @@ struct Kernel {
   }
 };
 
-template <int BM, int BN, int WM, int WN, int SFM, int OUT>
+template <int BM, int BN, int WM, int WN, int SFM, int OUT, int GRP, int NB>
 __global__ void __launch_bounds__(WM* WN * 64, 1) pipe_kernel(const GemmParams p) {
-  using G = Geo<BM, BN, WM, WN, SFM>;
-  using K = Kernel<BM, BN, WM, WN, SFM, OUT>;
+  using G = Geo<BM, BN, WM, WN, SFM, NB>;
+  using K = Kernel<BM, BN, WM, WN, SFM, OUT, GRP, NB>;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[G::LDS_BYTES];
   const K k(p, smem);
   int bid = blockIdx.x;
@@ -672,23 +742,26 @@ __global__ void __launch_bounds__(WM* WN * 64, 1) pipe_kernel(const GemmParams p
     bid = (bid % 8) * per + bid / 8;
   }
   int t = bid;
-  TilePos cur = tile_pos<BM, BN>(p, t);
+  TilePos cur = tile_pos<BM, BN, GRP>(p, t);
   if (!cur.valid) return;
-  TilePos nxt = tile_pos<BM, BN>(p, t + gridDim.x);
-  const int nkb = p.sf_k;  // >= 2
+  TilePos nxt = tile_pos<BM, BN, GRP>(p, t + gridDim.x);
+  const int nkb = p.sf_k;  // >= NB
 
-  // prologue: blocks 0 and 1 of the first tile, then block 0's operands into registers
+  // prologue: A blocks 0 and 1 and B blocks 0..NB-1 of the first tile, then block 0's
+  // operands into registers
   k.copy_a_block(cur, 0, 0);
   k.copy_b_block(cur, 0, 0);
   k.copy_a_block(cur, 1, 1);
   k.copy_b_block(cur, 1, 1);
+  if (NB == 3) k.copy_b_block(cur, 2, 2);
   Carry<K::FM> c;
   c.sbw0 = c.sbw1 = 0.f;
   if (SFM == SF_1D2D_F32) k.weight_block_scales(cur, 0, c.sbw0, c.sbw1);
-  wait_and_barrier<G::LA + G::LB>();
+  wait_and_barrier<G::LA + (NB - 1) * G::LB>();
 #pragma unroll
   for (int i = 0; i < K::FM; ++i) c.af[i] = k.a_frag(0, i);
   c.bf = k.b_frag(0, 0);
+  c.ebw = SFM == SF_1D1D_UE8M0 ? k.weight_word(0, 0) : 0u;
   k.read_scales(c, 0);
   const v4f zero = {0.f, 0.f, 0.f, 0.f};
   c.acc1 = zero;
@@ -702,22 +775,22 @@ __global__ void __launch_bounds__(WM* WN * 64, 1) pipe_kernel(const GemmParams p
     if (!nxt.valid) break;
     cur = nxt;
     t += gridDim.x;
-    nxt = tile_pos<BM, BN>(p, t + gridDim.x);
+    nxt = tile_pos<BM, BN, GRP>(p, t + gridDim.x);
   }
   // no copy may still be writing LDS when the workgroup ends
   __builtin_amdgcn_s_waitcnt(0 | (7 << 4));
 }
 
-template <int BM, int BN, int WM, int WN, int SFM, int OUT>
+template <int BM, int BN, int WM, int WN, int SFM, int OUT, int GRP, int NB>
 static hipError_t launch_one(const GemmParams& p, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((pipe_kernel<BM, BN, WM, WN, SFM, OUT>), dim3(grid), dim3(WM * WN * 64), 0, stream, p);
+  hipLaunchKernelGGL((pipe_kernel<BM, BN, WM, WN, SFM, OUT, GRP, NB>), dim3(grid), dim3(WM * WN * 64), 0, stream, p);
   return hipGetLastError();
 }
 
 template <int BM, int BN, int WM, int WN>
-static hipError_t launch_tile(const GemmParams& p, int sfm, int out, int grid, hipStream_t s) {
+static hipError_t launch_dense(const GemmParams& p, int sfm, int out, int grid, hipStream_t s) {
 #define DG_CASE(SF, O) \
-  if (sfm == SF && out == O) return launch_one<BM, BN, WM, WN, SF, O>(p, grid, s);
+  if (sfm == SF && out == O) return launch_one<BM, BN, WM, WN, SF, O, GRP_DENSE, 2>(p, grid, s);
   DG_CASE(SF_1D2D_F32, OUT_BF16)
   DG_CASE(SF_1D2D_F32, OUT_F32)
   DG_CASE(SF_1D2D_F32, OUT_F32_C)
@@ -725,29 +798,53 @@ static hipError_t launch_tile(const GemmParams& p, int sfm, int out, int grid, h
   return hipErrorInvalidValue;
 }
 
+template <int BM, int BN, int WM, int WN>
+static hipError_t launch_masked(const GemmParams& p, int sfm, int out, int grid, hipStream_t s) {
+#define DG_CASE(SF, O) \
+  if (sfm == SF && out == O) return launch_one<BM, BN, WM, WN, SF, O, GRP_MASKED, 3>(p, grid, s);
+  DG_CASE(SF_1D2D_F32, OUT_BF16)
+  DG_CASE(SF_1D1D_UE8M0, OUT_BF16)
+#undef DG_CASE
+  return hipErrorInvalidValue;
+}
+
 }  // namespace pipe
 
-// Tile shapes with a deep-pipelined instantiation (dense, K >= 256, 1d2d FP32 scales).
+// Shapes with a deep-pipelined instantiation: dense problems (1d2d FP32 scales, any output),
+// and masked problems streaming B through three stages (1d2d FP32 or UE8M0 scales, BF16).
 bool pipe_instantiated(int bm, int bn, int sfm, int grp, int out) {
-  if (grp != GRP_DENSE || sfm != SF_1D2D_F32) return false;
-  if (out < OUT_BF16 || out > OUT_F32_C) return false;
-  return (bm == 256 && bn == 224) || (bm == 128 && bn == 192) || (bm == 256 && bn == 192) ||
-         (bm == 128 && bn == 224) || (bm == 128 && bn == 256) || (bm == 128 && bn == 128);
+  if (grp == GRP_DENSE) {
+    if (sfm != SF_1D2D_F32 || out < OUT_BF16 || out > OUT_F32_C) return false;
+    return (bm == 256 && bn == 224) || (bm == 128 && bn == 192) || (bm == 256 && bn == 192) ||
+           (bm == 128 && bn == 224) || (bm == 128 && bn == 256) || (bm == 128 && bn == 128);
+  }
+  if (grp == GRP_MASKED) {
+    if ((sfm != SF_1D2D_F32 && sfm != SF_1D1D_UE8M0) || out != OUT_BF16) return false;
+    return bm == 128 && bn == 224;
+  }
+  return false;
 }
 
-int pipe_lds_bytes(int bm, int bn, int sfm) {
+int pipe_stages_b(int grp) { return grp == GRP_MASKED ? 3 : 2; }
+
+int pipe_lds_bytes(int bm, int bn, int sfm, int grp) {
   const int sa_slot = (bm * 4 + 1023) / 1024 * 1024;
   const int sb_slot = sfm == SF_1D2D_F32 ? 0 : (bn * 4 + 1023) / 1024 * 1024;
-  return pipe::NA * (bm * pipe::BK + sa_slot) + pipe::NB * (bn * pipe::BK + sb_slot) + 1024;
+  return pipe::NA * (bm * pipe::BK + sa_slot) + pipe_stages_b(grp) * (bn * pipe::BK + sb_slot) + 1024;
 }
 
-hipError_t launch_pipe(const GemmParams& p, int bm, int bn, int sfm, int out, int grid, hipStream_t stream) {
-  if (bm == 256 && bn == 224) return pipe::launch_tile<256, 224, 4, 2>(p, sfm, out, grid, stream);
-  if (bm == 256 && bn == 192) return pipe::launch_tile<256, 192, 4, 2>(p, sfm, out, grid, stream);
-  if (bm == 128 && bn == 192) return pipe::launch_tile<128, 192, 2, 2>(p, sfm, out, grid, stream);
-  if (bm == 128 && bn == 224) return pipe::launch_tile<128, 224, 2, 2>(p, sfm, out, grid, stream);
-  if (bm == 128 && bn == 256) return pipe::launch_tile<128, 256, 2, 2>(p, sfm, out, grid, stream);
-  if (bm == 128 && bn == 128) return pipe::launch_tile<128, 128, 2, 2>(p, sfm, out, grid, stream);
+hipError_t launch_pipe(const GemmParams& p, int bm, int bn, int sfm, int grp, int out, int grid,
+                       hipStream_t stream) {
+  if (grp == GRP_MASKED) {
+    if (bm == 128 && bn == 224) return pipe::launch_masked<128, 224, 2, 2>(p, sfm, out, grid, stream);
+    return hipErrorInvalidValue;
+  }
+  if (bm == 256 && bn == 224) return pipe::launch_dense<256, 224, 4, 2>(p, sfm, out, grid, stream);
+  if (bm == 256 && bn == 192) return pipe::launch_dense<256, 192, 4, 2>(p, sfm, out, grid, stream);
+  if (bm == 128 && bn == 192) return pipe::launch_dense<128, 192, 2, 2>(p, sfm, out, grid, stream);
+  if (bm == 128 && bn == 224) return pipe::launch_dense<128, 224, 2, 2>(p, sfm, out, grid, stream);
+  if (bm == 128 && bn == 256) return pipe::launch_dense<128, 256, 2, 2>(p, sfm, out, grid, stream);
+  if (bm == 128 && bn == 128) return pipe::launch_dense<128, 128, 2, 2>(p, sfm, out, grid, stream);
   return hipErrorInvalidValue;
 }
 

@@ -60,10 +60,13 @@ hipError_t launch_gemm(const GemmParams& p, int tile, int sf_mode, int group, in
 bool gemm_instantiated(int tile, int sf_mode, int group, int out);
 int gemm_lds_bytes(int tile);
 
-// Deep-pipelined dense kernels (dg_gemm_pipe.hip): dense problems with K >= 256.
+// Deep-pipelined kernels (dg_gemm_pipe.hip): dense problems and masked groups.  They need
+// at least pipe_stages_b(group) K blocks.
 bool pipe_instantiated(int bm, int bn, int sf_mode, int group, int out);
-int pipe_lds_bytes(int bm, int bn, int sf_mode);
-hipError_t launch_pipe(const GemmParams& p, int bm, int bn, int sf_mode, int out, int grid, hipStream_t stream);
+int pipe_stages_b(int group);
+int pipe_lds_bytes(int bm, int bn, int sf_mode, int group);
+hipError_t launch_pipe(const GemmParams& p, int bm, int bn, int sf_mode, int group, int out, int grid,
+                       hipStream_t stream);
 
 hipError_t launch_transform_sf(const float* in, int num_groups, int mn, int sf_k, int gran_mn,
                                int pack, void* out, int32_t* count, hipStream_t stream);

@@ -274,6 +274,34 @@ def test_masked_small_with_sentinels(tile):
     assert np.isnan(d.float().cpu().numpy()[~live]).all()
 
 
+@pytest.mark.parametrize("pack", [False, True])
+def test_masked_three_b_stages_ragged(pack):
+    """Masked groups on the 128x224 tile with enough K blocks for the three-stage B pipeline:
+    empty, one-row, full, straddling and exact-multiple groups, a ragged last n tile, and
+    (pack) UE8M0 scales applied inside the MFMA."""
+    G, Mmax, N, K = 6, 300, 500, 768
+    p = gen.grouped_masked(G, Mmax, N, K, seed=12, pow2_scales=pack)
+    masked = np.array([0, 300, 1, 129, 255, 128], dtype=np.int32)
+    say("masked 3-stage", pack, masked)
+    a, b = cuda(p["a"]), cuda(p["b"])
+    if pack:
+        sa = dg.get_mn_major_tma_aligned_packed_ue8m0_tensor(cuda(p["sa"]))
+        sb = dg.get_mn_major_tma_aligned_packed_ue8m0_tensor(cuda(p["sb"]), gran_mn=128, mn=N)
+    else:
+        sa, sb = cuda(p["sa"]), cuda(p["sb"])
+    d = torch.full((G, Mmax, N), float("nan"), dtype=torch.bfloat16, device=DEV)
+    with force_tile("128x224"):
+        dg.m_grouped_fp8_gemm_nt_masked((a, sa), (b, sb), d, cuda(masked), expected_m=128)
+    torch.cuda.synchronize()
+    o, T = oracle.grouped_masked(p["a"], p["sa"], p["b"], p["sb"], masked, want_abs=True)
+    bits = bf16_bits(d)
+    live = ~np.isnan(o)
+    ok, st = check_bf16(bits[live], o[live], T[live])
+    say("masked 3-stage", st)
+    assert ok.all(), st
+    assert np.isnan(d.float().cpu().numpy()[~live]).all()
+
+
 # ---------------------------------------------------------------- the five workloads at full size
 def test_config2_dense_full():
     p = gen.config2()
