@@ -64,7 +64,7 @@ def read_traffic(workload):
 def kernel_source_hash():
     import hashlib
     h = hashlib.sha1()
-    for f in ("dg_gemm.hip", "dg_internal.h"):
+    for f in ("dg_gemm.hip", "dg_gemm_pipe.hip", "dg_internal.h"):
         with open(os.path.join(ROOT, "block_scaled_fp8_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
@@ -186,7 +186,7 @@ def main():
                    "step": "transform_sf(act scales) + gemm", "buffer_sets": len(sets)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP8_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP8_TFLOPS, 4),
-                     "traffic": traffic, "kernel": "dg::gemm_kernel (GEMM launch alone)",
+                     "traffic": traffic, "kernel": "dg::pipe::pipe_kernel (GEMM launch alone)",
                      "gemm_avg_ms": round(gemm_avg_ms, 5), "gemm_min_ms": round(float(np.min(gemm_ms)), 5),
                      "alg_bytes": alg_bytes, "alg_flops": flops},
         "cpu_baseline": cpu,
