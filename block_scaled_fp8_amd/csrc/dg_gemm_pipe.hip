@@ -256,6 +256,9 @@ struct Kernel {
   uint32_t sa_lds;                  // per-lane LDS address of its rows' activation scales (stage 0)
   uint32_t sb_lds;                  // per-lane LDS address of its columns' weight scales (stage 0, 1d1d)
   int ustep_a, ustep_b;             // 8 * NW * ld
+  // masked groups (at most 64): lane g holds group g's valid rows and the inclusive prefix
+  // sum of the tiles of groups 0..g, so a tile index maps to its group with one ballot
+  int grp_rows = 0, grp_incl = 0;
 
   __device__ __forceinline__ Kernel(const GemmParams& p_, uint8_t* smem_) : p(p_), smem(smem_) {
     wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -279,6 +282,35 @@ struct Kernel {
     b_hi = G::B_OFF + (wn * TN + lr) * BK + hi;
     sa_lds = G::SA_OFF + 4 * (wm * TM + lr);
     sb_lds = G::SB_OFF + 4 * (wn * TN + 4 * lg);
+    if (GRP == GRP_MASKED && p.num_groups <= 64) {
+      const int mg = lane < p.num_groups ? min(max(p.masked_m[lane], 0), p.m) : 0;
+      int incl = ((mg + BM - 1) / BM) * p.num_n_tiles;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int v = __shfl_up(incl, d);
+        if (lane >= d) incl += v;
+      }
+      grp_rows = mg;
+      grp_incl = incl;
+    }
+  }
+
+  __device__ __forceinline__ TilePos tile_at(int t) const {
+    if (GRP == GRP_MASKED && p.num_groups <= 64) {
+      TilePos r;
+      const uint64_t hit = __ballot(grp_incl > t);
+      r.valid = hit != 0;
+      const int g = r.valid ? (int)__builtin_ctzll(hit) : 0;
+      const int mg = __builtin_amdgcn_readlane(grp_rows, g);
+      const int mt = max(1, (mg + BM - 1) / BM);
+      const int loc = t - (__builtin_amdgcn_readlane(grp_incl, g) - ((mg + BM - 1) / BM) * p.num_n_tiles);
+      r.g = g;
+      r.mv = r.valid ? mg : 0;
+      r.n0 = r.valid ? (loc / mt) * BN : 0;
+      r.m0 = r.valid ? (loc % mt) * BM : 0;
+      return r;
+    }
+    return tile_pos<BM, BN, GRP>(p, t);
   }
 
   // ---- copies HBM -> LDS --------------------------------------------------------------
@@ -397,10 +429,14 @@ struct Kernel {
   // Block g = (tile cur, K index kb) runs out of A stage `as` and B stage `bs`; nxt is the
   // tile after cur.  `stores`: lower bound on the vector stores the previous epilogue issued
   // stores since the last barrier.
-  template <int NF>
+  // NF: leading 16-column fragments that use the wave's first weight-scale block (1d2d);
+  // 0 means the split is only known at run time (`nf`).  FA: this wave's 16-row fragments
+  // that hold rows of the problem (masked groups: the others are padding, and their MFMAs,
+  // promotions and stores are skipped).
+  template <int NF, int FA>
   __device__ __forceinline__ void block(Carry<FM>& c, float (&fin)[FM][FN][4], const TilePos& cur,
                                         const TilePos& nxt, int kb, int nkb, int as, int bs,
-                                        int stores) const {
+                                        int stores, int nf) const {
     // promotion factor of fragment (i, j) of this block: activation scale of row i times the
     // weight-block scale of column fragment j (the first block's for j < nf, else the second's;
     // both wave-uniform)
@@ -418,7 +454,10 @@ struct Kernel {
       f0[i] = SFM == SF_1D2D_F32 ? sa[i] * c.sbw0 : sa[i];
       f1[i] = SFM == SF_1D2D_F32 && NF < FN ? sa[i] * c.sbw1 : f0[i];
     }
-    auto factor = [&](int i, int j) -> float { return j < NF ? f0[i] : f1[i]; };
+    auto factor = [&](int i, int j) -> float {
+      if constexpr (NF == 0) return j < nf ? f0[i] : f1[i];
+      else return j < NF ? f0[i] : f1[i];
+    };
     const uint32_t sbl = sb_lds + (uint32_t)(bs * G::SB_SLOT);
 
     // copies of A block g+2 go out spread over the steps before the barrier (in the first
@@ -488,14 +527,16 @@ struct Kernel {
         if (SFM == SF_1D1D_UE8M0) ebwn = weight_word(bs, j + 1);
       }
       __builtin_amdgcn_sched_barrier(0);
-      v4f acc;
-      if (SFM == SF_1D1D_UE8M0) {
-        const int eb = (int)((ebw >> kshift) & 0xFFu);
-        acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf, c.af[i], zero, 0, 0, 0, eb, 0, ea[i]);
-      } else {
-        acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf, c.af[i], zero, 0, 0, 0, 0, 0, 0);
+      v4f acc = zero;
+      if constexpr (i < FA) {
+        if (SFM == SF_1D1D_UE8M0) {
+          const int eb = (int)((ebw >> kshift) & 0xFFu);
+          acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf, c.af[i], zero, 0, 0, 0, eb, 0, ea[i]);
+        } else {
+          acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf, c.af[i], zero, 0, 0, 0, 0, 0, 0);
+        }
+        asm volatile("" : "+v"(acc));
       }
-      asm volatile("" : "+v"(acc));
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (t == 0) {
         TilePos ta;
@@ -521,7 +562,7 @@ struct Kernel {
       // after its last use, fragment i of A is replaced by block g+1's
       if constexpr (t >= G::TB) c.af[i] = a_frag(as1, i);
       // promote the partial of MFMA t-2 (for t < 2: of the previous block, with its factor)
-      if constexpr (t >= 2) {
+      if constexpr (t >= 2 && (t - 2) % FM < FA) {
         constexpr int tp = t - 2, jp = tp / FM, ip = tp % FM;
         if (SFM == SF_1D1D_UE8M0) {
 #pragma unroll
@@ -536,7 +577,7 @@ struct Kernel {
           for (int v = 0; v < 4; ++v) fin[ip][jp][v] = __builtin_fmaf(sc, r2[v], fin[ip][jp][v]);
         }
         pin(fin[ip][jp]);
-      } else if constexpr (SFM != SF_1D1D_F32) {
+      } else if constexpr (t < 2 && SFM != SF_1D1D_F32 && (t - 2 + STEPS) % FM < FA) {
         constexpr int tp = t - 2 + STEPS, jp = tp / FM, ip = tp % FM;
         if (SFM == SF_1D1D_UE8M0) {
 #pragma unroll
@@ -627,27 +668,38 @@ struct Kernel {
     const int esz = (OUT == OUT_BF16) ? 2 : 4;
     char* Dg = (char*)p.d;
     if (GRP == GRP_MASKED) Dg += (int64_t)tr.g * p.d_gstride * esz;
-    if (TRANSPOSE && interior && p.d_vec16) {
+    // (tiles with missing rows take this path only for masked groups, where nearly every
+    // tile has some; dense edge tiles use the element path below)
+    if (TRANSPOSE && tr.n0 + BN <= p.n && p.d_vec16 && (GRP == GRP_MASKED || interior)) {
       const uint32_t scr = G::A_OFF + aslot * G::A_SLOT + wave * SCR;
       uint8_t* drow0 = (uint8_t*)Dg + ((int64_t)(tr.m0 + wm * TM) * p.ldd + tr.n0 + wn * TN) * 2;
+      // rows of this wave's part that exist (all of them for interior tiles)
+      const int rows = interior ? TM : tr.mv - tr.m0 - wm * TM;
+      auto store_rows = [&]<bool ALL>() {
 #pragma unroll
-      for (int i = 0; i < FM; ++i) {
+        for (int i = 0; i < FM; ++i) {
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const v2u w = {pack_bf16x2(fin[i][j][0], fin[i][j][1]), pack_bf16x2(fin[i][j][2], fin[i][j][3])};
-          *(v2u*)(smem + scr + lr * RS + (16 * j + 4 * lg) * 2) = w;
-        }
+          for (int j = 0; j < FN; ++j) {
+            const v2u w = {pack_bf16x2(fin[i][j][0], fin[i][j][1]), pack_bf16x2(fin[i][j][2], fin[i][j][3])};
+            *(v2u*)(smem + scr + lr * RS + (16 * j + 4 * lg) * 2) = w;
+          }
 #pragma unroll
-        for (int k = 0; k < RD; ++k) {
-          const int cidx = lane + 64 * k;
-          if (cidx < 16 * CH) {
+          for (int k = 0; k < RD; ++k) {
+            const int cidx = lane + 64 * k;
             const int r = cidx / CH, cc = cidx - r * CH;
-            const v4i x = *(const v4i*)(smem + scr + r * RS + cc * 16);
-            *(v4i*)(drow0 + ((int64_t)(16 * i + r) * p.ldd + 8 * cc) * 2) = x;
+            if (cidx < 16 * CH && (ALL || 16 * i + r < rows)) {
+              const v4i x = *(const v4i*)(smem + scr + r * RS + cc * 16);
+              *(v4i*)(drow0 + ((int64_t)(16 * i + r) * p.ldd + 8 * cc) * 2) = x;
+            }
           }
         }
+      };
+      if (interior) {
+        store_rows.template operator()<true>();
+        return STORES_T;
       }
-      return STORES_T;
+      if constexpr (GRP == GRP_MASKED) store_rows.template operator()<false>();
+      return 0;
     }
     const bool vec = (OUT != OUT_F32_C || p.c_vec) && p.d_vec && interior;
     const int row0 = tr.m0 + wm * TM + lr;
@@ -714,17 +766,25 @@ struct Kernel {
     // leading 16-column fragments of this wave that use its first weight-scale block: a
     // compile-time split, so each fragment's factor is chosen without any instruction
     const int nf = SFM == SF_1D2D_F32 ? min(FN, 8 - (((cur.n0 + wn * TN) & 127) >> 4)) : FN;
-    auto run = [&]<int NF>() {
+    auto run = [&]<int NF, int FA>() {
       for (int kb = 0; kb < nkb; ++kb) {
-        block<NF>(c, fin, cur, nxt, kb, nkb, as, bs, stores);
+        block<NF, FA>(c, fin, cur, nxt, kb, nkb, as, bs, stores, nf);
         stores = 0;
         as = as == NA - 1 ? 0 : as + 1;
         bs = next_b(bs);
       }
     };
-    [&]<int... Ns>(std::integer_sequence<int, Ns...>) {
-      ((nf == Ns + 1 ? run.template operator()<Ns + 1>() : void()), ...);
-    }(std::make_integer_sequence<int, FN>{});
+    if constexpr (GRP == GRP_MASKED) {
+      // 16-row fragments of this wave that hold valid rows of the group
+      const int live = min(FM, max(0, (cur.mv - cur.m0 - wm * TM + 15) / 16));
+      [&]<int... Fs>(std::integer_sequence<int, Fs...>) {
+        ((live == Fs ? run.template operator()<SFM == SF_1D2D_F32 ? 0 : FN, Fs>() : void()), ...);
+      }(std::make_integer_sequence<int, FM + 1>{});
+    } else {
+      [&]<int... Ns>(std::integer_sequence<int, Ns...>) {
+        ((nf == Ns + 1 ? run.template operator()<Ns + 1, FM>() : void()), ...);
+      }(std::make_integer_sequence<int, FN>{});
+    }
     flush(c, fin);
     stores = epilogue(fin, cur, as == 0 ? NA - 1 : as - 1);
   }
@@ -742,9 +802,9 @@ __global__ void __launch_bounds__(WM* WN * 64, 1) pipe_kernel(const GemmParams p
     bid = (bid % 8) * per + bid / 8;
   }
   int t = bid;
-  TilePos cur = tile_pos<BM, BN, GRP>(p, t);
+  TilePos cur = k.tile_at(t);
   if (!cur.valid) return;
-  TilePos nxt = tile_pos<BM, BN, GRP>(p, t + gridDim.x);
+  TilePos nxt = k.tile_at(t + gridDim.x);
   const int nkb = p.sf_k;  // >= NB
 
   // prologue: A blocks 0 and 1 and B blocks 0..NB-1 of the first tile, then block 0's
@@ -775,7 +835,7 @@ __global__ void __launch_bounds__(WM* WN * 64, 1) pipe_kernel(const GemmParams p
     if (!nxt.valid) break;
     cur = nxt;
     t += gridDim.x;
-    nxt = tile_pos<BM, BN, GRP>(p, t + gridDim.x);
+    nxt = k.tile_at(t + gridDim.x);
   }
   // no copy may still be writing LDS when the workgroup ends
   __builtin_amdgcn_s_waitcnt(0 | (7 << 4));
