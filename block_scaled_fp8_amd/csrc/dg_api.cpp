@@ -177,10 +177,10 @@ int do_launch(dg::GemmParams& p, int kind, int32_t m_rows_for_plan, int32_t m_ma
     fprintf(stderr, "[dg] kind=%d m=%d n=%d k=%d groups=%d sf_mode=%d out=%d -> tile %dx%d (waves %dx%d) tiles=%d grid=%d swizzle_m=%d\n",
             kind, p.m, p.n, p.k, p.num_groups, sfm, out, c.bm, c.bn, c.wm, c.wn, p.total_tiles, pl.grid,
             p.swizzle_m);
-  // dense problems with at least two K blocks run the deep-pipelined kernel when it has the
-  // chosen tile (one workgroup per CU: its LDS stages take most of the 160 KiB)
-  const bool use_pipe = (kind == dg::GRP_DENSE || kind == dg::GRP_MASKED) &&
-                        p.sf_k >= dg::pipe_stages_b(kind) && !env_int("DG_NO_PIPE", 0) &&
+  // problems with at least as many K blocks as the deep-pipelined kernel keeps B stages run
+  // that kernel when it has the chosen tile (one workgroup per CU: its LDS stages take most
+  // of the 160 KiB)
+  const bool use_pipe = p.sf_k >= dg::pipe_stages_b(kind) && !env_int("DG_NO_PIPE", 0) &&
                         dg::pipe_instantiated(c.bm, c.bn, sfm, kind, out);
   if (use_pipe) {
     const int occ = (160 * 1024) / dg::pipe_lds_bytes(c.bm, c.bn, sfm, kind);

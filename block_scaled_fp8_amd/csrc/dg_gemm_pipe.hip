@@ -1,5 +1,5 @@
-// Deep-pipelined block-scaled FP8 GEMM main loop for gfx950 (MI355X, CDNA4), dense
-// problems with K >= 256.
+// Deep-pipelined block-scaled FP8 GEMM main loop for gfx950 (MI355X, CDNA4): dense and
+// contiguous-grouped problems with K >= 256, masked-grouped problems with K >= 384.
 //
 // Computes D = C + A . B^T exactly as the kernels in dg_gemm.hip do (E4M3 operands, one
 // activation scale per row and 128-long K block, weight scales per 128x128 block or per
@@ -130,21 +130,29 @@ __device__ __forceinline__ void wait_and_barrier() {
 // Output tile t of the workgroup's persistent walk.
 //  * Dense: super-rows of swizzle_m m tiles, walked column by column, so the tiles that run
 //    at the same time share A and B rows.
+//  * Contiguous groups (page "02 · DeepGEMM 技术解析" §5.1): the dense walk over all rows;
+//    a tile's group is the one of its first row.  A tile whose first row is padding (or
+//    names no group) gets no rows: its copies are empty, it issues no MFMAs and stores
+//    nothing.  The rows of a tile whose last row is in another group than its first (the
+//    padding at the end of a group's last block) are checked one by one when stored.
 //  * Masked (page "02 · DeepGEMM 技术解析" §5.2): only the tiles holding valid rows exist.
 //    Groups in order; within a group n tiles outer and m tiles inner, so the m tiles that
 //    read the same weight slice run next to each other.  masked_m is read on the device and
 //    clamped to [0, M_max].
 struct TilePos {
-  int g;       // group (masked)
+  int g;       // group (contiguous, masked)
   int m0, n0;  // first row (within the group) and first column
-  int mv;      // rows that exist: M (dense) or the group's valid rows (masked)
+  int mv;      // rows that exist: M (dense, contiguous; 0 for a skipped contiguous tile) or
+               // the group's valid rows (masked)
   bool valid;  // false past the last tile: its copies are empty
+  bool chk;    // contiguous: store only the rows whose group is g
 };
 
 template <int BM, int BN, int GRP>
 __device__ __forceinline__ TilePos tile_pos(const GemmParams& p, int t) {
   TilePos r;
   r.g = 0;
+  r.chk = false;
   if (GRP == GRP_MASKED) {
     r.valid = false;
     r.m0 = r.n0 = r.mv = 0;
@@ -175,6 +183,14 @@ __device__ __forceinline__ TilePos tile_pos(const GemmParams& p, int t) {
   r.m0 = (sr * p.swizzle_m + rem % rows) * BM;
   r.n0 = (rem / rows) * BN;
   r.mv = p.m;
+  if (GRP == GRP_CONTIG) {
+    const int g = load_uniform(p.grouped_layout, r.m0);
+    const int last = load_uniform(p.grouped_layout, min(r.m0 + BM, p.m) - 1);
+    const bool ok = g >= 0 && g < p.num_groups;
+    r.g = ok ? g : 0;
+    r.mv = ok ? p.m : 0;
+    r.chk = ok && last != g;
+  }
   return r;
 }
 
@@ -222,6 +238,7 @@ __device__ __forceinline__ void ahead_block(const TilePos& cur, const TilePos& n
   t.n0 = same ? cur.n0 : nxt.n0;
   t.mv = same ? cur.mv : nxt.mv;
   t.valid = same ? cur.valid : nxt.valid;
+  t.chk = same ? cur.chk : nxt.chk;
   k = same ? kb + ahead : kb + ahead - nkb;
 }
 
@@ -328,11 +345,13 @@ struct Kernel {
     const int64_t srow = (SFM == SF_1D1D_UE8M0) ? (kb >> 2) : kb;
     const uint8_t* B = p.b;
     const uint8_t* SB = (const uint8_t*)p.sfb;
-    if (GRP == GRP_MASKED) {
+    if (GRP != GRP_DENSE) {
       B += (int64_t)t.g * p.b_gstride;
       SB += 4 * (int64_t)t.g * p.sfb_gstride;
     }
-    return make_src(B, p.ldb, t.n0, p.n, BN, kb, t.valid, SB, p.sfb_stride, srow, SFM != SF_1D2D_F32);
+    // (a skipped contiguous tile reads no weights either)
+    const bool valid = GRP == GRP_CONTIG ? t.valid && t.mv > 0 : t.valid;
+    return make_src(B, p.ldb, t.n0, p.n, BN, kb, valid, SB, p.sfb_stride, srow, SFM != SF_1D2D_F32);
   }
 
   // Part U of the copy of one operand block into the stage at LDS offset `dst` (its scales
@@ -414,7 +433,7 @@ struct Kernel {
     const int nw0 = t.n0 + wn * TN;
     const int nb = (p.n + 127) / 128;
     const int blk0 = min(nw0 / 128, nb - 1), blk1 = min(nw0 / 128 + 1, nb - 1);
-    const int gofs = GRP == GRP_MASKED ? t.g * (int)p.sfb_gstride : 0;
+    const int gofs = GRP != GRP_DENSE ? t.g * (int)p.sfb_gstride : 0;
     i0 = __builtin_amdgcn_readfirstlane(gofs + blk0 * (int)p.sfb_stride + kb);
     i1 = __builtin_amdgcn_readfirstlane(gofs + blk1 * (int)p.sfb_stride + kb);
   }
@@ -664,7 +683,7 @@ struct Kernel {
   static_assert(STORES_T < STORES_N && STORES_N < 64, "vmcnt is a 6-bit field; the two store counts must differ");
 
   __device__ __forceinline__ int epilogue(const float (&fin)[FM][FN][4], const TilePos& tr, int aslot) const {
-    const bool interior = tr.m0 + BM <= tr.mv && tr.n0 + BN <= p.n;
+    const bool interior = tr.m0 + BM <= tr.mv && tr.n0 + BN <= p.n && !(GRP == GRP_CONTIG && tr.chk);
     const int esz = (OUT == OUT_BF16) ? 2 : 4;
     char* Dg = (char*)p.d;
     if (GRP == GRP_MASKED) Dg += (int64_t)tr.g * p.d_gstride * esz;
@@ -708,6 +727,7 @@ struct Kernel {
     for (int i = 0; i < FM; ++i) {
       const int row = row0 + 16 * i;
       if (row >= tr.mv) continue;
+      if (GRP == GRP_CONTIG && tr.chk && p.grouped_layout[row] != tr.g) continue;
       char* drow = Dg + (int64_t)row * p.ldd * esz;
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
@@ -774,7 +794,16 @@ struct Kernel {
         bs = next_b(bs);
       }
     };
-    if constexpr (GRP == GRP_MASKED) {
+    if constexpr (GRP == GRP_CONTIG) {
+      // a skipped tile runs its K blocks without MFMAs (its copies are empty)
+      if (cur.mv == 0) {
+        run.template operator()<FN, 0>();
+      } else {
+        [&]<int... Ns>(std::integer_sequence<int, Ns...>) {
+          ((nf == Ns + 1 ? run.template operator()<Ns + 1, FM>() : void()), ...);
+        }(std::make_integer_sequence<int, FN>{});
+      }
+    } else if constexpr (GRP == GRP_MASKED) {
       // 16-row fragments of this wave that hold valid rows of the group
       const int live = min(FM, max(0, (cur.mv - cur.m0 - wm * TM + 15) / 16));
       [&]<int... Fs>(std::integer_sequence<int, Fs...>) {
@@ -859,6 +888,17 @@ static hipError_t launch_dense(const GemmParams& p, int sfm, int out, int grid, 
 }
 
 template <int BM, int BN, int WM, int WN>
+static hipError_t launch_contig(const GemmParams& p, int sfm, int out, int grid, hipStream_t s) {
+#define DG_CASE(SF, O) \
+  if (sfm == SF && out == O) return launch_one<BM, BN, WM, WN, SF, O, GRP_CONTIG, 2>(p, grid, s);
+  DG_CASE(SF_1D2D_F32, OUT_BF16)
+  DG_CASE(SF_1D2D_F32, OUT_F32)
+  DG_CASE(SF_1D1D_UE8M0, OUT_BF16)
+#undef DG_CASE
+  return hipErrorInvalidValue;
+}
+
+template <int BM, int BN, int WM, int WN>
 static hipError_t launch_masked(const GemmParams& p, int sfm, int out, int grid, hipStream_t s) {
 #define DG_CASE(SF, O) \
   if (sfm == SF && out == O) return launch_one<BM, BN, WM, WN, SF, O, GRP_MASKED, 3>(p, grid, s);
@@ -871,8 +911,14 @@ static hipError_t launch_masked(const GemmParams& p, int sfm, int out, int grid,
 }  // namespace pipe
 
 // Shapes with a deep-pipelined instantiation: dense problems (1d2d FP32 scales, any output),
-// and masked problems streaming B through three stages (1d2d FP32 or UE8M0 scales, BF16).
+// contiguous groups (1d2d FP32 scales with BF16 or FP32 output, UE8M0 scales with BF16), and
+// masked problems streaming B through three stages (1d2d FP32 or UE8M0 scales, BF16).
 bool pipe_instantiated(int bm, int bn, int sfm, int grp, int out) {
+  if (grp == GRP_CONTIG) {
+    const bool ok = (sfm == SF_1D2D_F32 && (out == OUT_BF16 || out == OUT_F32)) ||
+                    (sfm == SF_1D1D_UE8M0 && out == OUT_BF16);
+    return ok && bm == 128 && (bn == 224 || bn == 256);
+  }
   if (grp == GRP_DENSE) {
     if (sfm != SF_1D2D_F32 || out < OUT_BF16 || out > OUT_F32_C) return false;
     return (bm == 256 && bn == 224) || (bm == 128 && bn == 192) || (bm == 256 && bn == 192) ||
@@ -897,6 +943,11 @@ hipError_t launch_pipe(const GemmParams& p, int bm, int bn, int sfm, int grp, in
                        hipStream_t stream) {
   if (grp == GRP_MASKED) {
     if (bm == 128 && bn == 224) return pipe::launch_masked<128, 224, 2, 2>(p, sfm, out, grid, stream);
+    return hipErrorInvalidValue;
+  }
+  if (grp == GRP_CONTIG) {
+    if (bm == 128 && bn == 224) return pipe::launch_contig<128, 224, 2, 2>(p, sfm, out, grid, stream);
+    if (bm == 128 && bn == 256) return pipe::launch_contig<128, 256, 2, 2>(p, sfm, out, grid, stream);
     return hipErrorInvalidValue;
   }
   if (bm == 256 && bn == 224) return pipe::launch_dense<256, 224, 4, 2>(p, sfm, out, grid, stream);

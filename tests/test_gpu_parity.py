@@ -253,6 +253,63 @@ def test_contiguous_small_with_padding_rows():
     assert np.isnan(d.float().cpu().numpy()[~live]).all()
 
 
+@contextlib.contextmanager
+def grid_size(n):
+    if n:
+        dg.set_num_sms(n)
+    try:
+        yield
+    finally:
+        if n:
+            dg.set_num_sms(0)
+
+
+def pow2_floor(s):
+    """Largest power of two <= each (positive, normal) scale: inputs that UE8M0 holds exactly."""
+    return np.exp2(np.floor(np.log2(s))).astype(np.float32)
+
+
+@pytest.mark.parametrize("tile,out,pack,sms", [("128x256", torch.bfloat16, False, None),
+                                               ("128x256", torch.bfloat16, False, 5),
+                                               ("128x224", torch.float32, False, 3),
+                                               ("128x224", torch.bfloat16, True, 5),
+                                               ("128x256", torch.bfloat16, True, None)])
+def test_contiguous_pipelined_ragged(tile, out, pack, sms):
+    """Contiguous groups on the pipelined tiles: full blocks, a block ending in padding rows
+    (rows checked one by one), a block that is all padding and one naming no group (both
+    skipped), m_total cut short inside the last block, a ragged last n tile; a small grid
+    makes every workgroup walk several tiles across those cases."""
+    G, N, K = 5, 500, 768
+    p = gen.grouped_contiguous(G, N, K, seed=16, m_units=(1, 3))
+    starts = np.concatenate([[0], np.cumsum(p["sizes"])])
+    assert list(p["sizes"]) == [256, 256, 384, 256, 384]
+    layout = p["layout"].copy()
+    layout[starts[2] - 60:starts[2]] = -1          # group 1 ends in 60 padding rows
+    layout[starts[2]:starts[2] + 128] = -1         # group 2's first block is all padding
+    layout[starts[3]:starts[3] + 128] = G + 2      # a block naming no group
+    M = p["M"] - 50                                # the last block has 78 rows
+    a, sa, layout = p["a"][:M], p["sa"][:M], layout[:M]
+    sb = p["sb"]
+    if pack:
+        sa, sb = pow2_floor(sa), pow2_floor(sb)
+    say("contiguous pipelined", tile, out, pack, sms, M)
+    d = torch.full((M, N), float("nan"), dtype=out, device=DEV)
+    with force_tile(tile), grid_size(sms):
+        dg.m_grouped_fp8_gemm_nt_contiguous((cuda(a), cuda(sa)), (cuda(p["b"]), cuda(sb)), d, cuda(layout),
+                                            pack_ue8m0=pack)
+    torch.cuda.synchronize()
+    o, T = oracle.grouped_contiguous(a, sa, p["b"], sb, layout, want_abs=True)
+    live = ~np.isnan(o)
+    assert live.sum() == (M - 60 - 256) * N
+    if out == torch.bfloat16:
+        ok, st = check_bf16(bf16_bits(d)[live], o[live], T[live])
+    else:
+        ok, st = check_fp32(d.cpu().numpy()[live], o[live], T[live])
+    say("contiguous pipelined", st)
+    assert ok.all(), st
+    assert np.isnan(d.float().cpu().numpy()[~live]).all()
+
+
 @pytest.mark.parametrize("tile", [None, "128x128", "256x224", "64x32"])
 def test_masked_small_with_sentinels(tile):
     G, Mmax, N, K = 5, 200, 300, 256
