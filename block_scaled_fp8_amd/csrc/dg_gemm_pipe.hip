@@ -229,18 +229,34 @@ __device__ __forceinline__ const void* src_ptr(uint32_t lo, uint32_t hi) {
   return (const void*)(((uint64_t)hi << 32) | lo);
 }
 
-// The K block `ahead` blocks after block kb of tile cur: in cur or in the next tile.
-__device__ __forceinline__ void ahead_block(const TilePos& cur, const TilePos& nxt, int kb, int ahead, int nkb,
-                                            TilePos& t, int& k) {
-  const bool same = kb + ahead < nkb;
-  t.g = same ? cur.g : nxt.g;
-  t.m0 = same ? cur.m0 : nxt.m0;
-  t.n0 = same ? cur.n0 : nxt.n0;
-  t.mv = same ? cur.mv : nxt.mv;
-  t.valid = same ? cur.valid : nxt.valid;
-  t.chk = same ? cur.chk : nxt.chk;
-  k = same ? kb + ahead : kb + ahead - nkb;
+// Source of K block k (counted from the start of tile `c`; k >= nkb lies in the next tile
+// `n`) from the two tiles' block-0 sources: rows advance by k * 128 bytes, scales by
+// srow(k) scale rows of `sstep` bytes (srow = k, or k / 4 for UE8M0 words).  A few scalar
+// instructions instead of rebuilding the source from the tile position every block.
+template <bool UE8M0>
+__device__ __forceinline__ Src src_at(const Src& c, const Src& n, int k, int nkb, uint32_t sstep) {
+  const bool same = k < nkb;
+  const int kk = same ? k : k - nkb;
+  const uint64_t base = ((uint64_t)(same ? c.hi : n.hi) << 32 | (same ? c.lo : n.lo)) + (uint32_t)(kk * BK);
+  const int srow = UE8M0 ? kk >> 2 : kk;
+  const uint64_t sbase = ((uint64_t)(same ? c.shi : n.shi) << 32 | (same ? c.slo : n.slo)) + (uint32_t)srow * sstep;
+  Src s;
+  s.lo = __builtin_amdgcn_readfirstlane((uint32_t)base);
+  s.hi = __builtin_amdgcn_readfirstlane((uint32_t)(base >> 32));
+  // (a tile with rows has bytes > (nkb-1) * 128)
+  s.bytes = __builtin_amdgcn_readfirstlane(max((same ? c.bytes : n.bytes) - kk * BK, 0));
+  s.slo = __builtin_amdgcn_readfirstlane((uint32_t)sbase);
+  s.shi = __builtin_amdgcn_readfirstlane((uint32_t)(sbase >> 32));
+  s.sbytes = __builtin_amdgcn_readfirstlane(same ? c.sbytes : n.sbytes);
+  return s;
 }
+
+// Block-0 sources of the current and the next tile, and (1d2d) the weight-scale indices
+// of their block 0.
+struct Bases {
+  Src ac, an, bc, bn;
+  int wc0, wc1, wn0, wn1;
+};
 
 // State carried from one K block to the next (and across tiles).
 template <int FM>
@@ -273,6 +289,7 @@ struct Kernel {
   uint32_t sa_lds;                  // per-lane LDS address of its rows' activation scales (stage 0)
   uint32_t sb_lds;                  // per-lane LDS address of its columns' weight scales (stage 0, 1d1d)
   int ustep_a, ustep_b;             // 8 * NW * ld
+  uint32_t sstep_a, sstep_b;        // bytes per K-block row of the activation / per-row weight scales
   // masked groups (at most 64): lane g holds group g's valid rows and the inclusive prefix
   // sum of the tiles of groups 0..g, so a tile index maps to its group with one ballot
   int grp_rows = 0, grp_incl = 0;
@@ -291,6 +308,8 @@ struct Kernel {
     off_s = (uint32_t)lane << 4;
     ustep_a = __builtin_amdgcn_readfirstlane(8 * NW * (int)p.lda);
     ustep_b = __builtin_amdgcn_readfirstlane(8 * NW * (int)p.ldb);
+    sstep_a = __builtin_amdgcn_readfirstlane(4u * (uint32_t)p.sfa_stride);
+    sstep_b = __builtin_amdgcn_readfirstlane(4u * (uint32_t)p.sfb_stride);
     const int sw = swz(lr);
     const uint32_t lo = (uint32_t)(((2 * lg) ^ sw) * 16), hi = (uint32_t)(((2 * lg + 1) ^ sw) * 16);
     a_lo = G::A_OFF + (wm * TM + lr) * BK + lo;
@@ -453,9 +472,8 @@ struct Kernel {
   // that hold rows of the problem (masked groups: the others are padding, and their MFMAs,
   // promotions and stores are skipped).
   template <int NF, int FA>
-  __device__ __forceinline__ void block(Carry<FM>& c, float (&fin)[FM][FN][4], const TilePos& cur,
-                                        const TilePos& nxt, int kb, int nkb, int as, int bs,
-                                        int stores, int nf) const {
+  __device__ __forceinline__ void block(Carry<FM>& c, float (&fin)[FM][FN][4], const Bases& sb, int kb, int nkb,
+                                        int as, int bs, int stores, int nf) const {
     // promotion factor of fragment (i, j) of this block: activation scale of row i times the
     // weight-block scale of column fragment j (the first block's for j < nf, else the second's;
     // both wave-uniform)
@@ -486,7 +504,8 @@ struct Kernel {
     // first steps (in the shadow of the MFMAs) and pinned, so the scalar work does not pile
     // up right after the barrier
     Src asrc = {}, bsrc = {};
-    int wi0 = 0, wi1 = 0;
+    const __attribute__((address_space(4))) float* wp0 = nullptr;  // 1d2d: weight-block scales of block g+1
+    const __attribute__((address_space(4))) float* wp1 = nullptr;
     const int as2 = as >= NA - 2 ? as - (NA - 2) : as + 2;
     const int as1 = as >= NA - 1 ? as - (NA - 1) : as + 1;
     const int bs1 = next_b(bs);
@@ -529,18 +548,8 @@ struct Kernel {
           wait_vm<(NB == 2 ? 0 : G::LB)>();
         }
         wait_and_barrier<63>();
-        __builtin_amdgcn_sched_barrier(0);
-        // B block g+NB into the stage block g used
-        copy_b_all(bsrc, bs, std::make_integer_sequence<int, G::LB>{});
-        if (kb == 0) copy_a_all(asrc, as2, std::make_integer_sequence<int, G::LA>{});
-        // first B fragment and scales of block g+1
-        bfn = b_frag(bs1, 0);
-        if (SFM == SF_1D1D_UE8M0) ebwn = weight_word(bs1, 0);
-        if (SFM == SF_1D2D_F32) {
-          sbn0 = load_uniform((const float*)p.sfb, wi0);
-          sbn1 = load_uniform((const float*)p.sfb, wi1);
-        }
-        read_scales(c, as1);
+        // (the copies and reads that the barrier releases follow this step's MFMA, so the
+        // matrix unit is fed first)
       } else if constexpr (i == 0 && j + 1 < FN) {
         bfn = b_frag(bs, j + 1);
         if (SFM == SF_1D1D_UE8M0) ebwn = weight_word(bs, j + 1);
@@ -557,25 +566,34 @@ struct Kernel {
         asm volatile("" : "+v"(acc));
       }
       __builtin_amdgcn_sched_barrier(0);
+      if constexpr (t == G::TB) {
+        // B block g+NB into the stage block g used
+        copy_b_all(bsrc, bs, std::make_integer_sequence<int, G::LB>{});
+        if (kb == 0) copy_a_all(asrc, as2, std::make_integer_sequence<int, G::LA>{});
+        // first B fragment and scales of block g+1
+        bfn = b_frag(bs1, 0);
+        if (SFM == SF_1D1D_UE8M0) ebwn = weight_word(bs1, 0);
+        if (SFM == SF_1D2D_F32) {
+          sbn0 = *wp0;
+          sbn1 = *wp1;
+        }
+        read_scales(c, as1);
+      }
       if constexpr (t == 0) {
-        TilePos ta;
-        int kb_a;
-        ahead_block(cur, nxt, kb, 2, nkb, ta, kb_a);
-        asrc = a_src(ta, kb_a);
+        asrc = src_at<SFM == SF_1D1D_UE8M0>(sb.ac, sb.an, kb + 2, nkb, sstep_a);
         pin_src(asrc);
       }
       if constexpr (t == 1) {
-        TilePos tb;
-        int kb_b;
-        ahead_block(cur, nxt, kb, NB, nkb, tb, kb_b);
-        bsrc = b_src(tb, kb_b);
+        bsrc = src_at<SFM == SF_1D1D_UE8M0>(sb.bc, sb.bn, kb + NB, nkb, sstep_b);
         pin_src(bsrc);
         if (SFM == SF_1D2D_F32) {
-          TilePos t1;
-          int kb1;
-          ahead_block(cur, nxt, kb, 1, nkb, t1, kb1);
-          weight_block_index(t1, kb1, wi0, wi1);
-          asm volatile("" : "+s"(wi0), "+s"(wi1));
+          const bool same = kb + 1 < nkb;
+          const int k1 = same ? kb + 1 : kb + 1 - nkb;
+          const int wi0 = __builtin_amdgcn_readfirstlane((same ? sb.wc0 : sb.wn0) + k1);
+          const int wi1 = __builtin_amdgcn_readfirstlane((same ? sb.wc1 : sb.wn1) + k1);
+          wp0 = (const __attribute__((address_space(4))) float*)p.sfb + wi0;
+          wp1 = (const __attribute__((address_space(4))) float*)p.sfb + wi1;
+          asm volatile("" : "+s"(wp0), "+s"(wp1));
         }
       }
       // after its last use, fragment i of A is replaced by block g+1's
@@ -786,9 +804,19 @@ struct Kernel {
     // leading 16-column fragments of this wave that use its first weight-scale block: a
     // compile-time split, so each fragment's factor is chosen without any instruction
     const int nf = SFM == SF_1D2D_F32 ? min(FN, 8 - (((cur.n0 + wn * TN) & 127) >> 4)) : FN;
+    Bases sb;
+    sb.ac = a_src(cur, 0);
+    sb.an = a_src(nxt, 0);
+    sb.bc = b_src(cur, 0);
+    sb.bn = b_src(nxt, 0);
+    sb.wc0 = sb.wc1 = sb.wn0 = sb.wn1 = 0;
+    if (SFM == SF_1D2D_F32) {
+      weight_block_index(cur, 0, sb.wc0, sb.wc1);
+      weight_block_index(nxt, 0, sb.wn0, sb.wn1);
+    }
     auto run = [&]<int NF, int FA>() {
       for (int kb = 0; kb < nkb; ++kb) {
-        block<NF, FA>(c, fin, cur, nxt, kb, nkb, as, bs, stores, nf);
+        block<NF, FA>(c, fin, sb, kb, nkb, as, bs, stores, nf);
         stores = 0;
         as = as == NA - 1 ? 0 : as + 1;
         bs = next_b(bs);
