@@ -95,6 +95,10 @@ Plan plan_gemm(int kind, int m, int n, int k, int groups, int m_max, int sfm, in
       const double rows_done = double(mt) * c.bm;
       cost *= 1.0 + 0.15 * (rows_done / (m > 0 ? m : 1) - 1.0);
     }
+    // masked problems stream their weights: the kernel that keeps four weight blocks in
+    // flight is worth some extra tiles
+    if (kind == 2 && k / 128 >= dg::pipe_stages_b(kind) && dg::pipe_instantiated(c.bm, c.bn, sfm, kind, out))
+      cost *= 0.8;
     if (cost < best_cost - 1e-9) {
       best_cost = cost;
       best.tile = t;

@@ -43,7 +43,8 @@ typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 constexpr int BK = 128;  // K values per scale block and per MFMA
 constexpr int NA = 3;    // A stages
 
-// NB_: B stages (2 for dense problems; masked problems stream B from HBM with 3)
+// NB_: B stages (2 for dense and contiguous problems; masked problems, which stream their
+// weights from HBM with little reuse, keep 3 in flight; up to 4 are supported)
 template <int BM, int BN, int WM, int WN, int SFM, int NB_ = 2>
 struct Geo {
   static constexpr int NB = NB_;
@@ -72,7 +73,7 @@ struct Geo {
   static_assert(BM <= 256 && BN <= 256, "one scale wave-load covers at most 256 rows");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
   static_assert(TB >= LA, "the A copies are spread over the steps before the barrier");
-  static_assert(NB == 2 || NB == 3, "B stages");
+  static_assert(NB >= 2 && NB <= 4, "B stages");
 };
 
 // LDS slot of 16-byte chunk c of row r (rows counted within an operand stage) is
@@ -530,9 +531,11 @@ struct Kernel {
         //  * 2 B stages: the last is B(g+1) (previous barrier); after it come the A copies of
         //    block g+2 (LA), or, in a tile's first block (whose A copies wait for the barrier),
         //    only the previous epilogue's stores (a lower bound is counted);
-        //  * 3 B stages: the last is A(g+1) (previous block); after it come B(g+2) (LB) and
-        //    A(g+2) (LA); in a tile's first block B(g+2) and the stores; in its second block
-        //    only A(g+2), because the first block issued A(g+1) after B(g+2).
+        //  * NB = 3 or 4 B stages: the last is A(g+1) (previous block); after it come
+        //    B(g+NB-1) (LB) and A(g+2) (LA); in a tile's first block B(g+NB-1) and the stores;
+        //    in its second block only A(g+2), because the first block issued A(g+1) after
+        //    B(g+NB).  (In the very first block the prologue's later B blocks are also waited
+        //    for: stricter than needed.)
         // (Only the vmcnt wait depends on the branch: the LDS wait and the barrier stay in
         // straight-line code, so the compiler knows every earlier LDS read has landed.)
         if (kb > 1 || (kb == 1 && NB == 2)) {
@@ -557,9 +560,14 @@ struct Kernel {
       __builtin_amdgcn_sched_barrier(0);
       v4f acc = zero;
       if constexpr (i < FA) {
-        if (SFM == SF_1D1D_UE8M0) {
+        if constexpr (SFM == SF_1D1D_UE8M0) {
+          // power-of-two scales: the matrix unit applies 2^(e_b + e_a) to the block's products
+          // and adds them to the FP32 accumulator itself, so the promotion needs no VALU work
           const int eb = (int)((ebw >> kshift) & 0xFFu);
-          acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf, c.af[i], zero, 0, 0, 0, eb, 0, ea[i]);
+          const v4f cin = {fin[i][j][0], fin[i][j][1], fin[i][j][2], fin[i][j][3]};
+          const v4f r = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf, c.af[i], cin, 0, 0, 0, eb, 0, ea[i]);
+#pragma unroll
+          for (int v = 0; v < 4; ++v) fin[i][j][v] = r[v];
         } else {
           acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf, c.af[i], zero, 0, 0, 0, 0, 0, 0);
         }
@@ -599,12 +607,9 @@ struct Kernel {
       // after its last use, fragment i of A is replaced by block g+1's
       if constexpr (t >= G::TB) c.af[i] = a_frag(as1, i);
       // promote the partial of MFMA t-2 (for t < 2: of the previous block, with its factor)
-      if constexpr (t >= 2 && (t - 2) % FM < FA) {
+      if constexpr (SFM != SF_1D1D_UE8M0 && t >= 2 && (t - 2) % FM < FA) {
         constexpr int tp = t - 2, jp = tp / FM, ip = tp % FM;
-        if (SFM == SF_1D1D_UE8M0) {
-#pragma unroll
-          for (int v = 0; v < 4; ++v) fin[ip][jp][v] += r2[v];
-        } else if (SFM == SF_1D1D_F32) {
+        if (SFM == SF_1D1D_F32) {
           const v4f w = *(const v4f*)(smem + sbl + 64 * jp);
 #pragma unroll
           for (int v = 0; v < 4; ++v) fin[ip][jp][v] = __builtin_fmaf(sa[ip] * w[v], r2[v], fin[ip][jp][v]);
@@ -614,19 +619,16 @@ struct Kernel {
           for (int v = 0; v < 4; ++v) fin[ip][jp][v] = __builtin_fmaf(sc, r2[v], fin[ip][jp][v]);
         }
         pin(fin[ip][jp]);
-      } else if constexpr (t < 2 && SFM != SF_1D1D_F32 && (t - 2 + STEPS) % FM < FA) {
+      } else if constexpr (t < 2 && SFM == SF_1D2D_F32 && (t - 2 + STEPS) % FM < FA) {
         constexpr int tp = t - 2 + STEPS, jp = tp / FM, ip = tp % FM;
-        if (SFM == SF_1D1D_UE8M0) {
 #pragma unroll
-          for (int v = 0; v < 4; ++v) fin[ip][jp][v] += r2[v];
-        } else {
-#pragma unroll
-          for (int v = 0; v < 4; ++v) fin[ip][jp][v] = __builtin_fmaf(c.pscale[t], r2[v], fin[ip][jp][v]);
-        }
+        for (int v = 0; v < 4; ++v) fin[ip][jp][v] = __builtin_fmaf(c.pscale[t], r2[v], fin[ip][jp][v]);
         pin(fin[ip][jp]);
       }
-      r2 = r1;
-      r1 = acc;
+      if constexpr (SFM != SF_1D1D_UE8M0) {
+        r2 = r1;
+        r1 = acc;
+      }
       if constexpr (i == FM - 1) {
         bf = bfn;
         ebw = ebwn;
@@ -655,26 +657,24 @@ struct Kernel {
       c.acc1 = zero;
       c.acc2 = zero;
     } else {
-      c.acc1 = r1;
-      c.acc2 = r2;
+      c.acc1 = SFM == SF_1D1D_UE8M0 ? zero : r1;
+      c.acc2 = SFM == SF_1D1D_UE8M0 ? zero : r2;
       constexpr int t0 = STEPS - 2, t1 = STEPS - 1;
-      c.pscale[0] = factor(t0 % FM, t0 / FM);
-      c.pscale[1] = factor(t1 % FM, t1 / FM);
+      c.pscale[0] = SFM == SF_1D2D_F32 ? factor(t0 % FM, t0 / FM) : 0.f;
+      c.pscale[1] = SFM == SF_1D2D_F32 ? factor(t1 % FM, t1 / FM) : 0.f;
     }
   }
 
   // Promote the two partials still pending (end of a tile).
   __device__ __forceinline__ void flush(Carry<FM>& c, float (&fin)[FM][FN][4]) const {
     const v4f zero = {0.f, 0.f, 0.f, 0.f};
-    if (SFM != SF_1D1D_F32) {
+    if (SFM == SF_1D2D_F32) {
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         const int tp = STEPS - 2 + s, jp = tp / FM, ip = tp % FM;
         const v4f a = s == 0 ? c.acc2 : c.acc1;
 #pragma unroll
-        for (int v = 0; v < 4; ++v)
-          fin[ip][jp][v] = (SFM == SF_1D1D_UE8M0) ? fin[ip][jp][v] + a[v]
-                                                  : __builtin_fmaf(c.pscale[s], a[v], fin[ip][jp][v]);
+        for (int v = 0; v < 4; ++v) fin[ip][jp][v] = __builtin_fmaf(c.pscale[s], a[v], fin[ip][jp][v]);
       }
     }
     c.acc1 = zero;
@@ -870,7 +870,8 @@ __global__ void __launch_bounds__(WM* WN * 64, 1) pipe_kernel(const GemmParams p
   k.copy_b_block(cur, 0, 0);
   k.copy_a_block(cur, 1, 1);
   k.copy_b_block(cur, 1, 1);
-  if (NB == 3) k.copy_b_block(cur, 2, 2);
+  if (NB >= 3) k.copy_b_block(cur, 2, 2);
+  if (NB >= 4) k.copy_b_block(cur, 3, 3);
   Carry<K::FM> c;
   c.sbw0 = c.sbw1 = 0.f;
   if (SFM == SF_1D2D_F32) k.weight_block_scales(cur, 0, c.sbw0, c.sbw1);
