@@ -269,17 +269,19 @@ def pow2_floor(s):
     return np.exp2(np.floor(np.log2(s))).astype(np.float32)
 
 
-@pytest.mark.parametrize("tile,out,pack,sms", [("128x256", torch.bfloat16, False, None),
-                                               ("128x256", torch.bfloat16, False, 5),
-                                               ("128x224", torch.float32, False, 3),
-                                               ("128x224", torch.bfloat16, True, 5),
-                                               ("128x256", torch.bfloat16, True, None)])
-def test_contiguous_pipelined_ragged(tile, out, pack, sms):
+@pytest.mark.parametrize("tile,out,pack,sms,K", [("128x256", torch.bfloat16, False, None, 768),
+                                                 ("128x256", torch.bfloat16, False, 5, 768),
+                                                 ("128x224", torch.float32, False, 3, 768),
+                                                 ("128x224", torch.bfloat16, True, 5, 768),
+                                                 ("128x256", torch.bfloat16, True, None, 768),
+                                                 ("128x256", torch.bfloat16, False, 5, 256)])
+def test_contiguous_pipelined_ragged(tile, out, pack, sms, K):
     """Contiguous groups on the pipelined tiles: full blocks, a block ending in padding rows
     (rows checked one by one), a block that is all padding and one naming no group (both
     skipped), m_total cut short inside the last block, a ragged last n tile; a small grid
-    makes every workgroup walk several tiles across those cases."""
-    G, N, K = 5, 500, 768
+    makes every workgroup walk several tiles across those cases.  K = 256 is the pipelined
+    kernel's minimum: two K blocks, so every copy a block issues is for the next tile."""
+    G, N = 5, 500
     p = gen.grouped_contiguous(G, N, K, seed=16, m_units=(1, 3))
     starts = np.concatenate([[0], np.cumsum(p["sizes"])])
     assert list(p["sizes"]) == [256, 256, 384, 256, 384]
@@ -292,7 +294,7 @@ def test_contiguous_pipelined_ragged(tile, out, pack, sms):
     sb = p["sb"]
     if pack:
         sa, sb = pow2_floor(sa), pow2_floor(sb)
-    say("contiguous pipelined", tile, out, pack, sms, M)
+    say("contiguous pipelined", tile, out, pack, sms, K, M)
     d = torch.full((M, N), float("nan"), dtype=out, device=DEV)
     with force_tile(tile), grid_size(sms):
         dg.m_grouped_fp8_gemm_nt_contiguous((cuda(a), cuda(sa)), (cuda(p["b"]), cuda(sb)), d, cuda(layout),
@@ -331,15 +333,16 @@ def test_masked_small_with_sentinels(tile):
     assert np.isnan(d.float().cpu().numpy()[~live]).all()
 
 
-@pytest.mark.parametrize("pack", [False, True])
-def test_masked_three_b_stages_ragged(pack):
+@pytest.mark.parametrize("pack,K", [(False, 768), (True, 768), (True, 384)])
+def test_masked_three_b_stages_ragged(pack, K):
     """Masked groups on the 128x224 tile with enough K blocks for the three-stage B pipeline:
     empty, one-row, full, straddling and exact-multiple groups, a ragged last n tile, and
     (pack) UE8M0 scales applied inside the MFMA."""
-    G, Mmax, N, K = 6, 300, 500, 768
+    # (K = 384: exactly as many K blocks as B stages, so every prefetch crosses into the next tile)
+    G, Mmax, N = 6, 300, 500
     p = gen.grouped_masked(G, Mmax, N, K, seed=12, pow2_scales=pack)
     masked = np.array([0, 300, 1, 129, 255, 128], dtype=np.int32)
-    say("masked 3-stage", pack, masked)
+    say("masked 3-stage", pack, K, masked)
     a, b = cuda(p["a"]), cuda(p["b"])
     if pack:
         sa = dg.get_mn_major_tma_aligned_packed_ue8m0_tensor(cuda(p["sa"]))
