@@ -905,6 +905,9 @@ static hipError_t launch_one(const GemmParams& p, int grid, hipStream_t stream) 
   return hipGetLastError();
 }
 
+// dense tiles that also run UE8M0 scales (the planner's choices for large problems)
+constexpr bool dense_ue8m0_tile(int bm, int bn) { return (bm == 256 && bn == 224) || (bm == 128 && bn == 192); }
+
 template <int BM, int BN, int WM, int WN>
 static hipError_t launch_dense(const GemmParams& p, int sfm, int out, int grid, hipStream_t s) {
 #define DG_CASE(SF, O) \
@@ -912,6 +915,10 @@ static hipError_t launch_dense(const GemmParams& p, int sfm, int out, int grid, 
   DG_CASE(SF_1D2D_F32, OUT_BF16)
   DG_CASE(SF_1D2D_F32, OUT_F32)
   DG_CASE(SF_1D2D_F32, OUT_F32_C)
+  if constexpr (dense_ue8m0_tile(BM, BN)) {
+    DG_CASE(SF_1D1D_UE8M0, OUT_BF16)
+    DG_CASE(SF_1D1D_UE8M0, OUT_F32)
+  }
 #undef DG_CASE
   return hipErrorInvalidValue;
 }
@@ -939,9 +946,10 @@ static hipError_t launch_masked(const GemmParams& p, int sfm, int out, int grid,
 
 }  // namespace pipe
 
-// Shapes with a deep-pipelined instantiation: dense problems (1d2d FP32 scales, any output),
-// contiguous groups (1d2d FP32 scales with BF16 or FP32 output, UE8M0 scales with BF16), and
-// masked problems streaming B through three stages (1d2d FP32 or UE8M0 scales, BF16).
+// Shapes with a deep-pipelined instantiation: dense problems (1d2d FP32 scales, any output;
+// UE8M0 scales with BF16 or FP32 output on two tiles), contiguous groups (1d2d FP32 scales
+// with BF16 or FP32 output, UE8M0 scales with BF16), and masked problems streaming B through
+// three stages (1d2d FP32 or UE8M0 scales, BF16).
 bool pipe_instantiated(int bm, int bn, int sfm, int grp, int out) {
   if (grp == GRP_CONTIG) {
     const bool ok = (sfm == SF_1D2D_F32 && (out == OUT_BF16 || out == OUT_F32)) ||
@@ -949,6 +957,7 @@ bool pipe_instantiated(int bm, int bn, int sfm, int grp, int out) {
     return ok && bm == 128 && (bn == 224 || bn == 256);
   }
   if (grp == GRP_DENSE) {
+    if (sfm == SF_1D1D_UE8M0) return (out == OUT_BF16 || out == OUT_F32) && pipe::dense_ue8m0_tile(bm, bn);
     if (sfm != SF_1D2D_F32 || out < OUT_BF16 || out > OUT_F32_C) return false;
     return (bm == 256 && bn == 224) || (bm == 128 && bn == 192) || (bm == 256 && bn == 192) ||
            (bm == 128 && bn == 224) || (bm == 128 && bn == 256) || (bm == 128 && bn == 128);

@@ -153,6 +153,23 @@ def test_pow2_inputs_are_bitwise_exact(tile):
     assert np.array_equal(bf16_bits(d), oracle.bf16_rne(o0))
 
 
+@pytest.mark.parametrize("tile", ["256x224", "128x192"])
+def test_ue8m0_long_k_accumulation_is_fp32_exact(tile):
+    """UE8M0 scales: the scaled MFMA adds every block's product into the FP32 accumulator.
+    Integer payloads in [-8, 8] and scales 2^e, e in [-3, 0], over K = 4096 (32 blocks): every
+    partial sum fits 24 significant bits, so an FP32 accumulation is exact and the result must
+    equal the oracle bitwise.  An accumulator narrower than FP32 (the concern the pages raise
+    for FP8 tensor cores, which is why they promote every 128) would round typical sums of
+    about 15 significant bits."""
+    p = gen.pow2_exact(300, 520, 4096, seed=21)
+    say("ue8m0 long-K exact", tile)
+    o = oracle.gemm_nt(p["a"], p["sa"], p["b"], p["sb"], 128)
+    d = run_dense(p, out=torch.float32, tile=tile, pack=True, sb_per_row=True)
+    assert np.array_equal(d.cpu().numpy().astype(np.float64), o)
+    d = run_dense(p, out=torch.bfloat16, tile=tile, pack=True, sb_per_row=True)
+    assert np.array_equal(bf16_bits(d), oracle.bf16_rne(o))
+
+
 def test_c_accumulation_and_aliasing():
     p = gen.dense(256, 384, 512, seed=4, with_c=True)
     say("C accumulation")
