@@ -95,10 +95,14 @@ Plan plan_gemm(int kind, int m, int n, int k, int groups, int m_max, int sfm, in
       const double rows_done = double(mt) * c.bm;
       cost *= 1.0 + 0.15 * (rows_done / (m > 0 ? m : 1) - 1.0);
     }
-    // masked problems stream their weights: the kernel that keeps four weight blocks in
-    // flight is worth some extra tiles
-    if (kind == 2 && k / 128 >= dg::pipe_stages_b(kind) && dg::pipe_instantiated(c.bm, c.bn, sfm, kind, out))
-      cost *= 0.8;
+    // masked problems stream their weights: the pipelined kernel is worth some extra tiles,
+    // and a pipelined tile that holds a whole group (m_max rows) streams each weight slice
+    // exactly once whatever the group's row count, while its padding fragments issue no
+    // MFMAs.  The area model above cannot see that (with rows spread over 0..m_max the
+    // 128-row tile re-streams the weights of every group above 128 rows): measured
+    // 136 against 143 us for 32 groups of up to 256 rows, so such a tile is taken outright.
+    if (kind == 2 && k / 128 >= dg::pipe_stages_b(c.bm, c.bn, kind) && dg::pipe_instantiated(c.bm, c.bn, sfm, kind, out))
+      cost *= c.bm >= m_max ? 0.01 : 0.8;
     if (cost < best_cost - 1e-9) {
       best_cost = cost;
       best.tile = t;
@@ -184,7 +188,7 @@ int do_launch(dg::GemmParams& p, int kind, int32_t m_rows_for_plan, int32_t m_ma
   // problems with at least as many K blocks as the deep-pipelined kernel keeps B stages run
   // that kernel when it has the chosen tile (one workgroup per CU: its LDS stages take most
   // of the 160 KiB)
-  const bool use_pipe = p.sf_k >= dg::pipe_stages_b(kind) && !env_int("DG_NO_PIPE", 0) &&
+  const bool use_pipe = p.sf_k >= dg::pipe_stages_b(c.bm, c.bn, kind) && !env_int("DG_NO_PIPE", 0) &&
                         dg::pipe_instantiated(c.bm, c.bn, sfm, kind, out);
   if (use_pipe) {
     const int occ = (160 * 1024) / dg::pipe_lds_bytes(c.bm, c.bn, sfm, kind);

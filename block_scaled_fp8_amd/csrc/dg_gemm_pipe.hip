@@ -934,10 +934,10 @@ static hipError_t launch_contig(const GemmParams& p, int sfm, int out, int grid,
   return hipErrorInvalidValue;
 }
 
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, int NB>
 static hipError_t launch_masked(const GemmParams& p, int sfm, int out, int grid, hipStream_t s) {
 #define DG_CASE(SF, O) \
-  if (sfm == SF && out == O) return launch_one<BM, BN, WM, WN, SF, O, GRP_MASKED, 3>(p, grid, s);
+  if (sfm == SF && out == O) return launch_one<BM, BN, WM, WN, SF, O, GRP_MASKED, NB>(p, grid, s);
   DG_CASE(SF_1D2D_F32, OUT_BF16)
   DG_CASE(SF_1D1D_UE8M0, OUT_BF16)
 #undef DG_CASE
@@ -948,8 +948,8 @@ static hipError_t launch_masked(const GemmParams& p, int sfm, int out, int grid,
 
 // Shapes with a deep-pipelined instantiation: dense problems (1d2d FP32 scales, any output;
 // UE8M0 scales with BF16 or FP32 output on two tiles), contiguous groups (1d2d FP32 scales
-// with BF16 or FP32 output, UE8M0 scales with BF16), and masked problems streaming B through
-// three stages (1d2d FP32 or UE8M0 scales, BF16).
+// with BF16 or FP32 output, UE8M0 scales with BF16), and masked problems (1d2d FP32 or UE8M0
+// scales, BF16) on a 128-row tile streaming B through three stages or a 256-row tile with two.
 bool pipe_instantiated(int bm, int bn, int sfm, int grp, int out) {
   if (grp == GRP_CONTIG) {
     const bool ok = (sfm == SF_1D2D_F32 && (out == OUT_BF16 || out == OUT_F32)) ||
@@ -964,23 +964,26 @@ bool pipe_instantiated(int bm, int bn, int sfm, int grp, int out) {
   }
   if (grp == GRP_MASKED) {
     if ((sfm != SF_1D2D_F32 && sfm != SF_1D1D_UE8M0) || out != OUT_BF16) return false;
-    return bm == 128 && bn == 224;
+    return (bm == 128 || bm == 256) && bn == 224;
   }
   return false;
 }
 
-int pipe_stages_b(int grp) { return grp == GRP_MASKED ? 3 : 2; }
+// (the 256-row masked tile holds a whole group of up to 256 rows, so each weight slice is
+// streamed once; its A stages leave room for two B stages only)
+int pipe_stages_b(int bm, int bn, int grp) { return grp == GRP_MASKED && bm == 128 ? 3 : 2; }
 
 int pipe_lds_bytes(int bm, int bn, int sfm, int grp) {
   const int sa_slot = (bm * 4 + 1023) / 1024 * 1024;
   const int sb_slot = sfm == SF_1D2D_F32 ? 0 : (bn * 4 + 1023) / 1024 * 1024;
-  return pipe::NA * (bm * pipe::BK + sa_slot) + pipe_stages_b(grp) * (bn * pipe::BK + sb_slot) + 1024;
+  return pipe::NA * (bm * pipe::BK + sa_slot) + pipe_stages_b(bm, bn, grp) * (bn * pipe::BK + sb_slot) + 1024;
 }
 
 hipError_t launch_pipe(const GemmParams& p, int bm, int bn, int sfm, int grp, int out, int grid,
                        hipStream_t stream) {
   if (grp == GRP_MASKED) {
-    if (bm == 128 && bn == 224) return pipe::launch_masked<128, 224, 2, 2>(p, sfm, out, grid, stream);
+    if (bm == 128 && bn == 224) return pipe::launch_masked<128, 224, 2, 2, 3>(p, sfm, out, grid, stream);
+    if (bm == 256 && bn == 224) return pipe::launch_masked<256, 224, 4, 2, 2>(p, sfm, out, grid, stream);
     return hipErrorInvalidValue;
   }
   if (grp == GRP_CONTIG) {

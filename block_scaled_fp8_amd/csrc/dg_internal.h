@@ -60,10 +60,10 @@ hipError_t launch_gemm(const GemmParams& p, int tile, int sf_mode, int group, in
 bool gemm_instantiated(int tile, int sf_mode, int group, int out);
 int gemm_lds_bytes(int tile);
 
-// Deep-pipelined kernels (dg_gemm_pipe.hip): dense problems and masked groups.  They need
-// at least pipe_stages_b(group) K blocks.
+// Deep-pipelined kernels (dg_gemm_pipe.hip): dense problems, contiguous and masked groups.
+// A tile needs at least pipe_stages_b(bm, bn, group) K blocks.
 bool pipe_instantiated(int bm, int bn, int sf_mode, int group, int out);
-int pipe_stages_b(int group);
+int pipe_stages_b(int bm, int bn, int group);
 int pipe_lds_bytes(int bm, int bn, int sf_mode, int group);
 hipError_t launch_pipe(const GemmParams& p, int bm, int bn, int sf_mode, int group, int out, int grid,
                        hipStream_t stream);

@@ -350,16 +350,17 @@ def test_masked_small_with_sentinels(tile):
     assert np.isnan(d.float().cpu().numpy()[~live]).all()
 
 
-@pytest.mark.parametrize("pack,K", [(False, 768), (True, 768), (True, 384)])
-def test_masked_three_b_stages_ragged(pack, K):
-    """Masked groups on the 128x224 tile with enough K blocks for the three-stage B pipeline:
+@pytest.mark.parametrize("tile,pack,K", [("128x224", False, 768), ("128x224", True, 768), ("128x224", True, 384),
+                                         ("256x224", False, 768), ("256x224", True, 768), ("256x224", True, 256)])
+def test_masked_pipelined_ragged(tile, pack, K):
+    """Masked groups on the pipelined tiles (128 rows with three B stages, 256 rows with two):
     empty, one-row, full, straddling and exact-multiple groups, a ragged last n tile, and
     (pack) UE8M0 scales applied inside the MFMA."""
     # (K = 384: exactly as many K blocks as B stages, so every prefetch crosses into the next tile)
     G, Mmax, N = 6, 300, 500
     p = gen.grouped_masked(G, Mmax, N, K, seed=12, pow2_scales=pack)
     masked = np.array([0, 300, 1, 129, 255, 128], dtype=np.int32)
-    say("masked 3-stage", pack, K, masked)
+    say("masked pipelined", tile, pack, K, masked)
     a, b = cuda(p["a"]), cuda(p["b"])
     if pack:
         sa = dg.get_mn_major_tma_aligned_packed_ue8m0_tensor(cuda(p["sa"]))
@@ -367,14 +368,14 @@ def test_masked_three_b_stages_ragged(pack, K):
     else:
         sa, sb = cuda(p["sa"]), cuda(p["sb"])
     d = torch.full((G, Mmax, N), float("nan"), dtype=torch.bfloat16, device=DEV)
-    with force_tile("128x224"):
+    with force_tile(tile):
         dg.m_grouped_fp8_gemm_nt_masked((a, sa), (b, sb), d, cuda(masked), expected_m=128)
     torch.cuda.synchronize()
     o, T = oracle.grouped_masked(p["a"], p["sa"], p["b"], p["sb"], masked, want_abs=True)
     bits = bf16_bits(d)
     live = ~np.isnan(o)
     ok, st = check_bf16(bits[live], o[live], T[live])
-    say("masked 3-stage", st)
+    say("masked pipelined", st)
     assert ok.all(), st
     assert np.isnan(d.float().cpu().numpy()[~live]).all()
 
