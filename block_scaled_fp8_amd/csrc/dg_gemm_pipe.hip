@@ -289,6 +289,7 @@ struct Kernel {
   uint32_t a_lo, a_hi, b_lo, b_hi;  // per-lane LDS fragment bases (stage 0)
   uint32_t sa_lds;                  // per-lane LDS address of its rows' activation scales (stage 0)
   uint32_t sb_lds;                  // per-lane LDS address of its columns' weight scales (stage 0, 1d1d)
+  uint32_t ww_lds;                  // UE8M0: per-lane LDS address of its B row's packed weight scales (stage 0)
   int ustep_a, ustep_b;             // 8 * NW * ld
   uint32_t sstep_a, sstep_b;        // bytes per K-block row of the activation / per-row weight scales
   // masked groups (at most 64): lane g holds group g's valid rows and the inclusive prefix
@@ -319,6 +320,7 @@ struct Kernel {
     b_hi = G::B_OFF + (wn * TN + lr) * BK + hi;
     sa_lds = G::SA_OFF + 4 * (wm * TM + lr);
     sb_lds = G::SB_OFF + 4 * (wn * TN + 4 * lg);
+    ww_lds = G::SB_OFF + 4 * (wn * TN + lr);
     if (GRP == GRP_MASKED && p.num_groups <= 64) {
       const int mg = lane < p.num_groups ? min(max(p.masked_m[lane], 0), p.m) : 0;
       int incl = ((mg + BM - 1) / BM) * p.num_n_tiles;
@@ -439,7 +441,7 @@ struct Kernel {
   }
   // UE8M0: the packed weight-scale word of the lane's B row in fragment j of B stage bslot
   __device__ __forceinline__ unsigned int weight_word(int bslot, int j) const {
-    return *(const unsigned int*)(smem + G::SB_OFF + bslot * G::SB_SLOT + 4 * (wn * TN + 16 * j + lr));
+    return *(const unsigned int*)(smem + ww_lds + (uint32_t)(bslot * G::SB_SLOT) + 64 * j);
   }
   __device__ __forceinline__ void read_scales(Carry<FM>& c, int aslot) const {
     const uint32_t a = sa_lds + (uint32_t)(aslot * G::SA_SLOT);
@@ -570,8 +572,8 @@ struct Kernel {
           for (int v = 0; v < 4; ++v) fin[i][j][v] = r[v];
         } else {
           acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf, c.af[i], zero, 0, 0, 0, 0, 0, 0);
+          asm volatile("" : "+v"(acc));
         }
-        asm volatile("" : "+v"(acc));
       }
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (t == G::TB) {
