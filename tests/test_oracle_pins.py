@@ -326,3 +326,58 @@ def test_tolerance_catches_planted_mistakes():
     bits = oracle.bf16_rne(D)
     assert check_bf16(bits, D, T)[0].all()
     assert not check_bf16(np.roll(bits, 1, axis=0), D, T)[0].all()
+
+
+# ---------------------------------------------------------------- the per-token-group cast
+def test_e4m3_encode_hand_values():
+    from oracle import quant
+    vals = [1.0625, 1.1875, 2.0 ** -9, 2.0 ** -10, 3 * 2.0 ** -10, 448.0, -448.0, -0.0, 0.0, 0.5, -1.5]
+    want = [0x38, 0x3A, 0x01, 0x00, 0x02, 0x7E, 0xFE, 0x80, 0x00, 0x30, 0xBC]
+    assert quant.e4m3_encode_rne(vals).tolist() == want
+
+
+def test_e4m3_encode_inverts_decode():
+    from oracle import quant
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    assert np.array_equal(quant.e4m3_encode_rne(codecs.e4m3_decode(codes)), codes)
+
+
+def test_e4m3_encode_matches_torch_including_ties():
+    # torch's float8_e4m3fn cast rounds to nearest even: a library routine on the same values,
+    # here on random values and on every midpoint between neighbouring finite values
+    from oracle import quant
+    rng = np.random.default_rng(31)
+    pos = np.sort(codecs.e4m3_decode(np.arange(0x7F, dtype=np.uint8)))
+    mids = (pos[1:] + pos[:-1]) / 2
+    x = np.concatenate([rng.uniform(-448, 448, 20000), rng.standard_normal(20000) * 0.01, mids, -mids])
+    x = x.astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(quant.e4m3_encode_rne(x), ref)
+
+
+def test_per_token_group_cast_closed_forms():
+    from oracle import quant
+    rng = np.random.default_rng(32)
+    # a group whose amax is 448 * 2^e has the scale 2^e exactly, and E4M3 values times 2^e
+    # come back as the same codes
+    codes = rng.integers(0, 0x7E, size=(3, 256)).astype(np.uint8)
+    codes[:, 0] = 0x7E                                   # amax 448 in both groups
+    codes[:, 128] = 0x7E
+    sign = rng.integers(0, 2, size=codes.shape).astype(np.uint8) << 7
+    codes = codes | sign
+    e = np.array([[-3, 2], [0, -7], [5, 0]])
+    x = codecs.e4m3_decode(codes) * np.repeat(2.0 ** e, 128, axis=1)
+    q, s = quant.per_token_group_cast(x.astype(np.float32))
+    assert np.array_equal(s, (2.0 ** e).astype(np.float32))
+    assert np.array_equal(q, codes)
+    # an all-zero group: scale 1, codes 0
+    q, s = quant.per_token_group_cast(np.zeros((2, 128), np.float32))
+    assert np.array_equal(s, np.ones((2, 1), np.float32)) and not q.any()
+    # any input: the dequantized value is within half an E4M3 step of x (relative to the scale)
+    x = (rng.standard_normal((4, 512)) * np.exp(rng.uniform(-8, 8, (4, 1)))).astype(np.float32)
+    q, s = quant.per_token_group_cast(x)
+    deq = codecs.e4m3_decode(q) * np.repeat(s.astype(np.float64), 128, axis=1)
+    y = np.abs(x.astype(np.float64) / np.repeat(s.astype(np.float64), 128, axis=1))
+    step = np.where(y < 2.0 ** -6, 2.0 ** -9, 2.0 ** (np.floor(np.log2(np.maximum(y, 2.0 ** -6))) - 3))
+    assert np.all(np.abs(deq - x) <= (step / 2 + 1e-6 * y) * np.repeat(s.astype(np.float64), 128, axis=1))
+    assert np.all(codecs.e4m3_decode(q).max(axis=1) <= 448)
