@@ -24,7 +24,7 @@ import torch
 __all__ = [
     "DGError", "lib", "fp8_gemm_nt", "m_grouped_fp8_gemm_nt_contiguous", "m_grouped_fp8_gemm_nt_masked",
     "transform_sf", "get_mn_major_tma_aligned_tensor", "get_mn_major_tma_aligned_packed_ue8m0_tensor",
-    "get_tma_aligned_size", "get_mk_alignment_for_contiguous_layout", "set_num_sms", "get_num_sms",
+    "per_token_group_cast_fp8", "get_tma_aligned_size", "get_mk_alignment_for_contiguous_layout", "set_num_sms", "get_num_sms",
     "get_gemm_config", "LIB_PATH",
 ]
 
@@ -32,6 +32,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdg.so")
 
 DG_OUT_BF16, DG_OUT_F32 = 1, 2
 DG_SF_F32, DG_SF_UE8M0X4 = 0, 1
+DG_IN_BF16, DG_IN_F32 = 1, 2
 
 _i32, _i64, _p = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
 _SIGS = {
@@ -42,6 +43,7 @@ _SIGS = {
     "dg_m_grouped_fp8_gemm_nt_masked": (_i32, [_i32, _i32, _i32, _i32, _p, _i64, _i64, _p, _i64, _i64, _p, _i64,
                                                _i64, _p, _i64, _i64, _i32, _i32, _p, _i64, _i64, _i32, _p, _i32, _p]),
     "dg_transform_sf": (_i32, [_p, _i32, _i32, _i32, _i32, _i32, _p, _p, _p]),
+    "dg_per_token_group_cast_fp8": (_i32, [_i32, _i32, _p, _i64, _i32, _p, _i64, _p, _i64, _p]),
     "dg_get_tma_aligned_size": (_i64, [_i64, _i32]),
     "dg_get_mk_alignment_for_contiguous_layout": (_i32, []),
     "dg_set_num_sms": (_i32, [_i32]),
@@ -154,6 +156,21 @@ def transform_sf(sf, mn, gran_mn=1, pack_ue8m0=False, nonpow2_count=None):
     _check(lib().dg_transform_sf(_ptr(sf3), G, mn, sf_k, gran_mn, int(bool(pack_ue8m0)), _ptr(out),
                                  _ptr(nonpow2_count), _stream(sf)))
     return out[0] if squeeze else out
+
+
+def per_token_group_cast_fp8(x):
+    """BF16 or FP32 activations [m, k] (k a multiple of 128) -> (E4M3 codes [m, k] uint8,
+    FP32 scales [m, k // 128] MN-major with stride align4(m)), ready for ``fp8_gemm_nt``."""
+    if x.dim() != 2 or x.dtype not in (torch.bfloat16, torch.float32) or x.stride(1) != 1:
+        raise ValueError("x must be a row-major 2-D bfloat16 or float32 tensor")
+    m, k = x.shape
+    a4 = _a4(m)
+    q = torch.empty((m, k), dtype=torch.uint8, device=x.device)
+    flat = torch.empty((max(k // 128, 1) * a4,), dtype=torch.float32, device=x.device)
+    sf = flat.as_strided((m, k // 128), (1, a4))
+    _check(lib().dg_per_token_group_cast_fp8(m, k, _ptr(x), x.stride(0), DG_IN_BF16 if x.dtype == torch.bfloat16 else DG_IN_F32,
+                                             _ptr(q), q.stride(0), _ptr(sf), a4, _stream(x)))
+    return q, sf
 
 
 def get_mn_major_tma_aligned_tensor(sf):

@@ -49,6 +49,8 @@ def build(verbose=False, jobs=None):
                   "-o", os.path.join(bdir, "dg_gemm_pipe.o")])
     steps.append([HIPCC, *FLAGS, "-c", os.path.join(CSRC, "dg_transform.hip"),
                   "-o", os.path.join(bdir, "dg_transform.o")])
+    steps.append([HIPCC, *FLAGS, "-c", os.path.join(CSRC, "dg_quant.hip"),
+                  "-o", os.path.join(bdir, "dg_quant.o")])
     steps.append([HIPCC, "-O2", "-std=c++20", "-fPIC", f"--offload-arch={ARCH}", "-c", os.path.join(CSRC, "dg_api.cpp"),
                   "-o", os.path.join(bdir, "dg_api.o")])
     jobs = jobs or min(16, os.cpu_count() or 4)

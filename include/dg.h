@@ -54,6 +54,7 @@ typedef enum {
 
 typedef enum { DG_OUT_BF16 = 1, DG_OUT_F32 = 2 } dg_out_dtype;
 typedef enum { DG_SF_F32 = 0, DG_SF_UE8M0X4 = 1 } dg_sf_format;
+typedef enum { DG_IN_BF16 = 1, DG_IN_F32 = 2 } dg_in_dtype;
 
 /*
  * Dense NT GEMM: D[m, n] = C[m, n] + sum_b sa[m, b] * sb[.., b] * sum_{k in block b} A[m, k] * B[n, k]
@@ -147,6 +148,27 @@ int dg_m_grouped_fp8_gemm_nt_masked(int32_t num_groups, int32_t m_max, int32_t n
                                     void* d, int64_t ldd, int64_t d_group_stride, int32_t d_dtype,
                                     const int32_t* masked_m, int32_t expected_m,
                                     hipStream_t stream);
+
+/*
+ * Per-token-group FP8 cast (page "02 · DeepGEMM 技术解析" §1.1: activations in 1x128 groups
+ * along K, one FP32 scale per group; page "第13章 DeepGEMM" §13.3: the scale is amax / 448):
+ * produces the A operand and its scales for the GEMMs above, already in their layout.
+ *
+ *   s[r, b] = max_{k in group b} |x[r, k]| / 448   (FP32; 1 for an all-zero group)
+ *   q[r, k] = E4M3(clamp(x[r, k] / s[r, b], -448, 448)), rounded to nearest, ties to even
+ *
+ * Both divisions are correctly rounded FP32 divisions.
+ *  x, ldx, x_dtype : BF16 or FP32 [m, k], row stride ldx elements; rows and start 16-byte aligned.
+ *  q, ldq          : E4M3 codes [m, k] (uint8), row stride ldq (a multiple of 8), 8-byte aligned.
+ *  sf, sf_stride   : FP32 scales, MN-major: element (r, b) at sf[b*sf_stride + r], sf_stride ==
+ *                    align4(m) (what dg_fp8_gemm_nt takes as sfa).  Padding rows [m, align4(m))
+ *                    are not written.
+ *  k must be a positive multiple of 128.  m == 0 is a no-op (pointers may be NULL).
+ *  Non-finite inputs give unspecified codes and scales.
+ */
+int dg_per_token_group_cast_fp8(int32_t m, int32_t k, const void* x, int64_t ldx, int32_t x_dtype,
+                                void* q, int64_t ldq, float* sf, int64_t sf_stride,
+                                hipStream_t stream);
 
 /*
  * Scale-layout transform (page "02 · DeepGEMM 技术解析" §3.1 and §3.2; page "第13章

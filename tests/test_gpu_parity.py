@@ -116,6 +116,56 @@ def test_transform_page_examples():
     assert int(count.item()) == 2
 
 
+# ---------------------------------------------------------------- per-token-group cast (bitwise)
+def _cast_input(m, k, seed):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((m, k)).astype(np.float32)
+    n = max(1, (m * k) // 1000)
+    x.reshape(-1)[rng.choice(m * k, size=n, replace=False)] *= np.float32(50.0)   # outliers
+    x[0, :128] = 0.0                                                            # an all-zero group
+    if k >= 256:
+        # amax 448 makes the scale 1, so these quotients sit exactly on E4M3 rounding ties
+        pos = np.sort(oracle.e4m3_decode(np.arange(0x7F, dtype=np.uint8)))
+        mids = ((pos[1:] + pos[:-1]) / 2).astype(np.float32)
+        row = np.resize(np.concatenate([mids, -mids]), 128)
+        row[0] = 448.0
+        x[-1, 128:256] = row
+    return x
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("m,k", [(1, 128), (3, 384), (5, 640), (37, 1152), (130, 7168)])
+def test_per_token_group_cast_bitwise(dtype, m, k):
+    """Codes and scales of the per-token-group cast against the oracle, bit for bit.  The rows
+    mix N(0,1) values, x50 outliers, an all-zero group and exact rounding ties; k/128 not a
+    multiple of 4 leaves the last wave of each row partly idle."""
+    x = _cast_input(m, k, seed=m * 7 + k)
+    say("cast", dtype, m, k)
+    xt = torch.from_numpy(x).to(DEV).to(dtype)
+    q, sf = dg.per_token_group_cast_fp8(xt)
+    torch.cuda.synchronize()
+    seen = xt.float().cpu().numpy()          # the values the kernel read (BF16-rounded for BF16)
+    qo, so = oracle.per_token_group_cast(seen)
+    assert np.array_equal(q.cpu().numpy(), qo)
+    assert np.array_equal(sf.cpu().numpy().view(np.uint32), so.view(np.uint32))
+
+
+def test_cast_feeds_the_gemm():
+    """The cast's outputs are the GEMM's A operand and activation scales as they stand."""
+    p = gen.dense(200, 384, 512, seed=41)
+    x = _cast_input(200, 512, seed=42)
+    say("cast -> gemm")
+    q, sf = dg.per_token_group_cast_fp8(torch.from_numpy(x).to(DEV))
+    d = torch.full((200, 384), float("nan"), dtype=torch.bfloat16, device=DEV)
+    dg.fp8_gemm_nt((q, sf), (cuda(p["b"]), cuda(p["sb"])), d)
+    torch.cuda.synchronize()
+    qo, so = oracle.per_token_group_cast(x)
+    o, T = oracle.gemm_nt(qo, so, p["b"], p["sb"], 128, want_abs=True)
+    ok, st = check_bf16(bf16_bits(d), o, T)
+    say("cast -> gemm", st)
+    assert ok.all(), st
+
+
 # ---------------------------------------------------------------- dense
 def test_config1_tiny_bf16():
     p = gen.config1()
