@@ -34,6 +34,7 @@ WORKLOADS = {
     "dense_c_4096x1536x7168": dict(kind="dense_c", M=4096, N=1536, K=7168),
     "masked_32x256x7168x2048": dict(kind="masked"),
     "contiguous_32x4096x7168": dict(kind="contig"),
+    "cast_4096x7168_bf16": dict(kind="cast", M=4096, K=7168),
 }
 DEFAULT = "dense_4096x7168x2048"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
@@ -126,6 +127,8 @@ def main():
     dev = "cuda:0"
     torch.cuda.init()
     spec = WORKLOADS[args.workload]
+    if spec["kind"] == "cast":
+        return bench_cast(args, spec, dg, dev)
     if spec["kind"] not in ("dense", "dense_c"):
         return bench_grouped(args, spec, dg, dev)
 
@@ -189,6 +192,54 @@ def main():
                      "traffic": traffic, "kernel": "dg::pipe::pipe_kernel (GEMM launch alone)",
                      "gemm_avg_ms": round(gemm_avg_ms, 5), "gemm_min_ms": round(float(np.min(gemm_ms)), 5),
                      "alg_bytes": alg_bytes, "alg_flops": flops},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def bench_cast(args, spec, dg, dev):
+    """The per-token-group FP8 cast of a BF16 activation matrix (the A operand of the dense
+    workload before quantization); HBM-bound."""
+    M, K = spec["M"], spec["K"]
+    g = torch.Generator(device=dev).manual_seed(0)
+    sets = [torch.randn((M, K), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16) for _ in range(8)]
+    alg_bytes = M * K * 2 + M * K + 4 * M * (K // 128)
+    stream = torch.cuda.current_stream()
+    for i in range(args.warmup):
+        dg.per_token_group_cast_fp8(sets[i % len(sets)])
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    outs = []
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        evs[i][0].record(stream)
+        outs.append(dg.per_token_group_cast_fp8(sets[i % len(sets)]))
+        evs[i][1].record(stream)
+        if len(outs) > 2:
+            outs.pop(0)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms = [a.elapsed_time(b) for a, b in evs]
+    avg = float(np.mean(ms))
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        x = sets[0][:256].float().cpu().numpy()
+        t = time.perf_counter()
+        oracle.per_token_group_cast(x)
+        dt = time.perf_counter() - t
+        cpu = {"value": round(256 * (K * 3 + 4 * (K // 128)) / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
+               "kind": "oracle", "seconds": round(dt, 2), "sample": "rows 0..255 of the 4096x7168 BF16 input, numpy"}
+    out = {
+        "metric": f"GB/s, per-token-group FP8 cast {args.workload}",
+        "value": round(alg_bytes * args.steps / elapsed / 1e9, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(elapsed * 1e3 / args.steps, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16 -> fp8_e4m3",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "M": M, "K": K, "buffer_sets": len(sets)},
+        "roofline": {"bound": "hbm", "achieved": round(alg_bytes / (avg * 1e-3) / 1e9, 2), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(alg_bytes / (avg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4), "traffic": None,
+                     "kernel": "dg::cast_kernel<true>", "avg_ms": round(avg, 5), "alg_bytes": alg_bytes},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -3,11 +3,12 @@
 // MN-major with the stride align4(m) that the GEMM reads (page "02 · DeepGEMM 技术解析"
 // §1.1 and §3.1; page "第13章 DeepGEMM" §13.3).
 //
-// One wave casts four consecutive groups of one row: lane l holds elements 8l..8l+7 (one
+// An item is four consecutive groups of one row: lane l holds elements 8l..8l+7 (one
 // 16-byte load for BF16, two for FP32), so 16 lanes cover a group and the group's amax is
-// a 4-step xor shuffle inside those 16 lanes.  The scale and every quotient are correctly
-// rounded FP32 divisions; the E4M3 code is rounded to nearest, ties to even, from the FP32
-// bits.  HBM-bound: (2 or 4) + 1 bytes per element plus 4 per 128 elements.
+// a 4-step xor shuffle inside those 16 lanes.  A wave loads four items before casting any,
+// to keep enough bytes in flight.  The scale and every quotient are correctly rounded FP32
+// divisions; the E4M3 code is rounded to nearest, ties to even, by the hardware conversion.
+// Algorithmic traffic: (2 or 4) + 1 bytes per element plus 4 per 128 elements.
 #include "dg_internal.h"
 
 namespace dg {
@@ -16,75 +17,90 @@ namespace {
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 typedef unsigned int v2u __attribute__((ext_vector_type(2)));
 
-// OCP E4M3 (bias 7, subnormals, largest 448) code of a finite FP32 value with |v| <= 448,
-// rounded to nearest with ties to even.  The sign goes to bit 7.
-__device__ __forceinline__ uint32_t e4m3_rne(float v) {
-  const uint32_t bits = __float_as_uint(v);
-  const uint32_t sign = (bits >> 24) & 0x80u;
-  const float a = fabsf(v);
-  if (a < 0.015625f) {  // below 2^-6: a multiple of 2^-9; a * 512 is exact, rint ties to even
-    return sign | (uint32_t)rintf(a * 512.0f);  // 8 lands on the smallest normal, code 0x08
-  }
-  const uint32_t ab = __float_as_uint(a);
-  uint32_t e = (ab >> 23) - 127u + 7u;  // 1..15
-  uint32_t m = (ab >> 20) & 7u;
-  const uint32_t rest = ab & 0xFFFFFu;  // the 20 mantissa bits below the kept three
-  if (rest > 0x80000u || (rest == 0x80000u && (m & 1u))) ++m;
-  if (m == 8u) {
-    m = 0u;
-    ++e;
-  }
-  return sign | (e << 3) | m;  // |v| <= 448 keeps this at or below 0x7E
+// E4M3 codes of two FP32 values in [-448, 448], rounded to nearest with ties to even, into
+// 16-bit half HI of `word`: gfx950's v_cvt_pk_fp8_f32 writes the OCP E4M3 format (bias 7,
+// subnormals, largest 448).  Its rounding is checked bit for bit against the oracle's
+// nearest-value encoder, rounding ties and subnormals included, by the parity tests.
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3_pair(float a, float b, uint32_t word) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)word, HI);
 }
+
+constexpr int ITEMS = 4;  // (row, chunk) items per wave, all loaded before any is cast
 
 template <bool BF16>
 __global__ void __launch_bounds__(256) cast_kernel(const void* __restrict__ x, int64_t ldx, uint8_t* __restrict__ q,
                                                    int64_t ldq, float* __restrict__ sf, int64_t sf_stride,
-                                                   int64_t waves, int chunks, int sf_k) {
+                                                   uint32_t items, uint32_t chunks, int sf_k) {
   const int lane = threadIdx.x & 63;
-  const int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // (row, chunk of 4 groups)
-  if (w >= waves) return;                                          // whole waves only
-  const int64_t row = w / chunks;
-  const int chunk = (int)(w - row * chunks);
-  const int g = chunk * 4 + (lane >> 4);
-  const bool active = g < sf_k;  // the last chunk of a row may hold fewer than 4 groups
-  const int64_t col = (int64_t)g * 128 + (lane & 15) * 8;
-  float v[8];
+  const uint32_t w0 = (blockIdx.x * 4u + (threadIdx.x >> 6)) * ITEMS;  // first (row, chunk of 4 groups)
+  if (w0 >= items) return;                                              // whole waves only
+  float v[ITEMS][8];
+  int64_t rows[ITEMS];
+  int gs[ITEMS];
+  bool act[ITEMS];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) v[i] = 0.f;
-  if (active) {
-    if (BF16) {
-      const v4u r = *(const v4u*)((const uint16_t*)x + row * ldx + col);
+  for (int it = 0; it < ITEMS; ++it) {
+    const uint32_t w = w0 + it;
+    const uint32_t row = w / chunks;
+    const int chunk = (int)(w - row * chunks);
+    rows[it] = row;
+    gs[it] = chunk * 4 + (lane >> 4);
+    act[it] = w < items && gs[it] < sf_k;  // the last chunk of a row may hold fewer than 4 groups
+    const int64_t col = (int64_t)gs[it] * 128 + (lane & 15) * 8;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        v[2 * i] = __uint_as_float(r[i] << 16);
-        v[2 * i + 1] = __uint_as_float(r[i] & 0xFFFF0000u);
-      }
-    } else {
-      const float* p = (const float*)x + row * ldx + col;
-      const v4u r0 = *(const v4u*)p, r1 = *(const v4u*)(p + 4);
+    for (int i = 0; i < 8; ++i) v[it][i] = 0.f;
+    if (act[it]) {
+      if (BF16) {
+        const v4u r = *(const v4u*)((const uint16_t*)x + rows[it] * ldx + col);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        v[i] = __uint_as_float(r0[i]);
-        v[4 + i] = __uint_as_float(r1[i]);
+        for (int i = 0; i < 4; ++i) {
+          v[it][2 * i] = __uint_as_float(r[i] << 16);
+          v[it][2 * i + 1] = __uint_as_float(r[i] & 0xFFFF0000u);
+        }
+      } else {
+        const float* p = (const float*)x + rows[it] * ldx + col;
+        const v4u r0 = *(const v4u*)p, r1 = *(const v4u*)(p + 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          v[it][i] = __uint_as_float(r0[i]);
+          v[it][4 + i] = __uint_as_float(r1[i]);
+        }
       }
     }
   }
-  float amax = 0.f;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  for (int it = 0; it < ITEMS; ++it) {
+    float amax = 0.f;
 #pragma unroll
-  for (int d = 8; d >= 1; d >>= 1) amax = fmaxf(amax, __shfl_xor(amax, d));  // within 16 lanes
-  const float s = amax == 0.f ? 1.f : __fdiv_rn(amax, 448.f);
-  uint32_t lo = 0, hi = 0;
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[it][i]));
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    lo |= e4m3_rne(fminf(fmaxf(__fdiv_rn(v[i], s), -448.f), 448.f)) << (8 * i);
-    hi |= e4m3_rne(fminf(fmaxf(__fdiv_rn(v[4 + i], s), -448.f), 448.f)) << (8 * i);
-  }
-  if (active) {
-    *(v2u*)(q + row * ldq + col) = (v2u){lo, hi};
-    if ((lane & 15) == 0) sf[(int64_t)g * sf_stride + row] = s;
+    for (int d = 8; d >= 1; d >>= 1) amax = fmaxf(amax, __shfl_xor(amax, d));  // within 16 lanes
+    const float s = amax == 0.f ? 1.f : __fdiv_rn(amax, 448.f);
+    // v / s correctly rounded, from the correctly rounded reciprocal y: q0 = v*y is within an
+    // ulp, the FMA gives its exact remainder, and one more FMA rounds correctly (Markstein's
+    // theorem).  Three instructions instead of a full division per element; a scale so small
+    // that 1/s would overflow takes the plain division.
+    const float y = __fdiv_rn(1.f, s);
+    const bool fast = s >= 0x1p-100f;
+    auto quot = [&](float xv) -> float {
+      if (fast) {
+        const float q0 = xv * y;
+        return __builtin_fmaf(__builtin_fmaf(-q0, s, xv), y, q0);
+      }
+      return __fdiv_rn(xv, s);
+    };
+    float c[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) c[i] = fminf(fmaxf(quot(v[it][i]), -448.f), 448.f);
+    uint32_t lo = e4m3_pair<false>(c[0], c[1], 0u), hi = e4m3_pair<false>(c[4], c[5], 0u);
+    lo = e4m3_pair<true>(c[2], c[3], lo);
+    hi = e4m3_pair<true>(c[6], c[7], hi);
+    if (act[it]) {
+      const int64_t col = (int64_t)gs[it] * 128 + (lane & 15) * 8;
+      *(v2u*)(q + rows[it] * ldq + col) = (v2u){lo, hi};
+      if ((lane & 15) == 0) sf[(int64_t)gs[it] * sf_stride + rows[it]] = s;
+    }
   }
 }
 
@@ -94,15 +110,16 @@ hipError_t launch_cast(const void* x, int64_t ldx, bool bf16, uint8_t* q, int64_
                        int m, int k, hipStream_t stream) {
   const int sf_k = k / 128;
   const int chunks = (sf_k + 3) / 4;
-  const int64_t waves = (int64_t)m * chunks;
+  const int64_t items = (int64_t)m * chunks;
+  const int64_t waves = (items + ITEMS - 1) / ITEMS;
   const int64_t blocks = (waves + 3) / 4;
-  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  if (blocks * 4 * ITEMS > 0xFFFFFFFFll) return hipErrorInvalidValue;  // item indices are 32-bit
   if (bf16)
     hipLaunchKernelGGL(cast_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream, x, ldx, q, ldq, sf,
-                       sf_stride, waves, chunks, sf_k);
+                       sf_stride, (uint32_t)items, (uint32_t)chunks, sf_k);
   else
     hipLaunchKernelGGL(cast_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream, x, ldx, q, ldq, sf,
-                       sf_stride, waves, chunks, sf_k);
+                       sf_stride, (uint32_t)items, (uint32_t)chunks, sf_k);
   return hipGetLastError();
 }
 
