@@ -381,3 +381,19 @@ def test_per_token_group_cast_closed_forms():
     step = np.where(y < 2.0 ** -6, 2.0 ** -9, 2.0 ** (np.floor(np.log2(np.maximum(y, 2.0 ** -6))) - 3))
     assert np.all(np.abs(deq - x) <= (step / 2 + 1e-6 * y) * np.repeat(s.astype(np.float64), 128, axis=1))
     assert np.all(codecs.e4m3_decode(q).max(axis=1) <= 448)
+
+
+def test_per_token_group_cast_ue8m0_scales():
+    from oracle import quant
+    # amax/448 already a power of two stays; anything above it goes to the next power
+    t = np.array([1.0, 0.75, 3.0, 2.0 ** -20, 1.5 * 2.0 ** 10, 0.0, np.nextafter(np.float32(4.0), np.float32(5.0))],
+                 dtype=np.float32)
+    want = np.array([1.0, 1.0, 4.0, 2.0 ** -20, 2.0 ** 11, 1.0, 8.0], dtype=np.float32)
+    assert np.array_equal(quant.pow2_ceil(t), want)
+    rng = np.random.default_rng(33)
+    x = (rng.standard_normal((3, 384)) * np.exp(rng.uniform(-10, 10, (3, 1)))).astype(np.float32)
+    q, s = quant.per_token_group_cast(x, ue8m0=True)
+    q32, s32 = quant.per_token_group_cast(x)
+    assert np.all(s >= s32) and np.all(s < 2 * s32)                       # the next power of two
+    assert np.array_equal(codecs.ue8m0_decode(codecs.ue8m0_encode(s)), s.astype(np.float64))  # exact in UE8M0
+    assert np.all(np.abs(codecs.e4m3_decode(q)) <= 448)
