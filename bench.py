@@ -35,6 +35,7 @@ WORKLOADS = {
     "masked_32x256x7168x2048": dict(kind="masked"),
     "contiguous_32x4096x7168": dict(kind="contig"),
     "cast_4096x7168_bf16": dict(kind="cast", M=4096, K=7168),
+    "cast_ue8m0_4096x7168_bf16": dict(kind="cast", M=4096, K=7168, ue8m0=True),
 }
 DEFAULT = "dense_4096x7168x2048"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
@@ -201,22 +202,23 @@ def bench_cast(args, spec, dg, dev):
     """The per-token-group FP8 cast of a BF16 activation matrix (the A operand of the dense
     workload before quantization); HBM-bound."""
     M, K = spec["M"], spec["K"]
+    ue8m0 = spec.get("ue8m0", False)
     g = torch.Generator(device=dev).manual_seed(0)
     sets = [torch.randn((M, K), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16) for _ in range(8)]
-    alg_bytes = M * K * 2 + M * K + 4 * M * (K // 128)
+    sf_bytes = 4 * (K // 512) if ue8m0 else 4 * (K // 128)   # per row: packed codes or FP32 scales
+    alg_bytes = M * K * 2 + M * K + M * sf_bytes
     stream = torch.cuda.current_stream()
+    # two output sets, allocated once and overwritten in turn
+    outs = [dg.per_token_group_cast_fp8(sets[i], pack_ue8m0=ue8m0) for i in range(2)]
     for i in range(args.warmup):
-        dg.per_token_group_cast_fp8(sets[i % len(sets)])
+        dg.per_token_group_cast_fp8(sets[i % len(sets)], pack_ue8m0=ue8m0, out=outs[i % 2])
     torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    outs = []
     t0 = time.perf_counter()
     for i in range(args.steps):
         evs[i][0].record(stream)
-        outs.append(dg.per_token_group_cast_fp8(sets[i % len(sets)]))
+        dg.per_token_group_cast_fp8(sets[i % len(sets)], pack_ue8m0=ue8m0, out=outs[i % 2])
         evs[i][1].record(stream)
-        if len(outs) > 2:
-            outs.pop(0)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms = [a.elapsed_time(b) for a, b in evs]
@@ -226,9 +228,9 @@ def bench_cast(args, spec, dg, dev):
         import oracle
         x = sets[0][:256].float().cpu().numpy()
         t = time.perf_counter()
-        oracle.per_token_group_cast(x)
+        oracle.per_token_group_cast(x, ue8m0=ue8m0)
         dt = time.perf_counter() - t
-        cpu = {"value": round(256 * (K * 3 + 4 * (K // 128)) / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
+        cpu = {"value": round(256 * (K * 3 + sf_bytes) / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
                "kind": "oracle", "seconds": round(dt, 2), "sample": "rows 0..255 of the 4096x7168 BF16 input, numpy"}
     out = {
         "metric": f"GB/s, per-token-group FP8 cast {args.workload}",
@@ -236,10 +238,11 @@ def bench_cast(args, spec, dg, dev):
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(elapsed * 1e3 / args.steps, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16 -> fp8_e4m3",
         "data": "synthetic",
-        "config": {"workload": args.workload, "M": M, "K": K, "buffer_sets": len(sets)},
+        "config": {"workload": args.workload, "M": M, "K": K, "buffer_sets": len(sets),
+                   "scales": "ue8m0x4" if ue8m0 else "f32"},
         "roofline": {"bound": "hbm", "achieved": round(alg_bytes / (avg * 1e-3) / 1e9, 2), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(alg_bytes / (avg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4), "traffic": None,
-                     "kernel": "dg::cast_kernel<true>", "avg_ms": round(avg, 5), "alg_bytes": alg_bytes},
+                     "kernel": f"dg::cast_kernel<true, {'true' if ue8m0 else 'false'}>", "avg_ms": round(avg, 5), "alg_bytes": alg_bytes},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -43,7 +43,7 @@ _SIGS = {
     "dg_m_grouped_fp8_gemm_nt_masked": (_i32, [_i32, _i32, _i32, _i32, _p, _i64, _i64, _p, _i64, _i64, _p, _i64,
                                                _i64, _p, _i64, _i64, _i32, _i32, _p, _i64, _i64, _i32, _p, _i32, _p]),
     "dg_transform_sf": (_i32, [_p, _i32, _i32, _i32, _i32, _i32, _p, _p, _p]),
-    "dg_per_token_group_cast_fp8": (_i32, [_i32, _i32, _p, _i64, _i32, _p, _i64, _p, _i64, _p]),
+    "dg_per_token_group_cast_fp8": (_i32, [_i32, _i32, _p, _i64, _i32, _p, _i64, _p, _i64, _i32, _p]),
     "dg_get_tma_aligned_size": (_i64, [_i64, _i32]),
     "dg_get_mk_alignment_for_contiguous_layout": (_i32, []),
     "dg_set_num_sms": (_i32, [_i32]),
@@ -158,18 +158,29 @@ def transform_sf(sf, mn, gran_mn=1, pack_ue8m0=False, nonpow2_count=None):
     return out[0] if squeeze else out
 
 
-def per_token_group_cast_fp8(x):
+def per_token_group_cast_fp8(x, pack_ue8m0=False, out=None):
     """BF16 or FP32 activations [m, k] (k a multiple of 128) -> (E4M3 codes [m, k] uint8,
-    FP32 scales [m, k // 128] MN-major with stride align4(m)), ready for ``fp8_gemm_nt``."""
+    scales MN-major with stride align4(m)), ready for ``fp8_gemm_nt``: FP32 [m, k // 128],
+    or with ``pack_ue8m0`` power-of-two scales as int32 [m, ceil(k / 512)] words of four
+    UE8M0 codes.  ``out``: an earlier result of the same shape and format to overwrite."""
     if x.dim() != 2 or x.dtype not in (torch.bfloat16, torch.float32) or x.stride(1) != 1:
         raise ValueError("x must be a row-major 2-D bfloat16 or float32 tensor")
     m, k = x.shape
     a4 = _a4(m)
-    q = torch.empty((m, k), dtype=torch.uint8, device=x.device)
-    flat = torch.empty((max(k // 128, 1) * a4,), dtype=torch.float32, device=x.device)
-    sf = flat.as_strided((m, k // 128), (1, a4))
+    cols = (k // 128 + 3) // 4 if pack_ue8m0 else k // 128
+    if out is not None:
+        q, sf = out
+        want = torch.int32 if pack_ue8m0 else torch.float32
+        if (q.dtype != torch.uint8 or tuple(q.shape) != (m, k) or q.stride(1) != 1 or sf.dtype != want
+                or tuple(sf.shape) != (m, cols) or not _is_mn_major(sf)):
+            raise ValueError("out must be (uint8 [m, k] codes, MN-major scales) as this call returns them")
+    else:
+        q = torch.empty((m, k), dtype=torch.uint8, device=x.device)
+        flat = torch.empty((max(cols, 1) * a4,), dtype=torch.int32 if pack_ue8m0 else torch.float32, device=x.device)
+        sf = flat.as_strided((m, cols), (1, a4))
     _check(lib().dg_per_token_group_cast_fp8(m, k, _ptr(x), x.stride(0), DG_IN_BF16 if x.dtype == torch.bfloat16 else DG_IN_F32,
-                                             _ptr(q), q.stride(0), _ptr(sf), a4, _stream(x)))
+                                             _ptr(q), q.stride(0), _ptr(sf), a4,
+                                             DG_SF_UE8M0X4 if pack_ue8m0 else DG_SF_F32, _stream(x)))
     return q, sf
 
 

@@ -317,8 +317,9 @@ int dg_transform_sf(const float* sf_in, int32_t num_groups, int32_t mn, int32_t 
 }
 
 int dg_per_token_group_cast_fp8(int32_t m, int32_t k, const void* x, int64_t ldx, int32_t x_dtype, void* q,
-                                int64_t ldq, float* sf, int64_t sf_stride, hipStream_t stream) {
+                                int64_t ldq, void* sf, int64_t sf_stride, int32_t sf_format, hipStream_t stream) {
   if (x_dtype != DG_IN_BF16 && x_dtype != DG_IN_F32) return fail(DG_ERR_DTYPE, "x_dtype %d is not DG_IN_BF16 or DG_IN_F32", x_dtype);
+  if (sf_format != DG_SF_F32 && sf_format != DG_SF_UE8M0X4) return fail(DG_ERR_DTYPE, "sf_format %d is not DG_SF_F32 or DG_SF_UE8M0X4", sf_format);
   if (m < 0) return fail(DG_ERR_SHAPE, "m = %d is negative", m);
   if (k <= 0 || k % 128 != 0) return fail(DG_ERR_SHAPE, "k = %d must be a positive multiple of 128", k);
   if (m == 0) return ok();  // nothing is read or written: pointers may be NULL
@@ -328,7 +329,8 @@ int dg_per_token_group_cast_fp8(int32_t m, int32_t k, const void* x, int64_t ldx
   if (ldq < k || ldq % 8 != 0 || (reinterpret_cast<uintptr_t>(q) & 7u) != 0) return fail(DG_ERR_LAYOUT, "q needs ldq >= k, ldq a multiple of 8 and an 8-byte aligned start");
   if (sf_stride != align4(m)) return fail(DG_ERR_LAYOUT, "sf must be MN-major with stride align4(m) = %lld, got %lld", (long long)align4(m), (long long)sf_stride);
   if ((reinterpret_cast<uintptr_t>(sf) & 3u) != 0) return fail(DG_ERR_LAYOUT, "sf must be 4-byte aligned");
-  const hipError_t e = dg::launch_cast(x, ldx, x_dtype == DG_IN_BF16, (uint8_t*)q, ldq, sf, sf_stride, m, k, stream);
+  const hipError_t e = dg::launch_cast(x, ldx, x_dtype == DG_IN_BF16, (uint8_t*)q, ldq, sf, sf_stride,
+                                       sf_format == DG_SF_UE8M0X4, m, k, stream);
   if (e != hipSuccess) return fail(DG_ERR_HIP, "cast launch failed: %s", hipGetErrorString(e));
   return ok();
 }

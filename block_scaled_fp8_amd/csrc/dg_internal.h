@@ -68,8 +68,8 @@ int pipe_lds_bytes(int bm, int bn, int sf_mode, int group);
 hipError_t launch_pipe(const GemmParams& p, int bm, int bn, int sf_mode, int group, int out, int grid,
                        hipStream_t stream);
 
-hipError_t launch_cast(const void* x, int64_t ldx, bool bf16, uint8_t* q, int64_t ldq, float* sf, int64_t sf_stride,
-                       int m, int k, hipStream_t stream);
+hipError_t launch_cast(const void* x, int64_t ldx, bool bf16, uint8_t* q, int64_t ldq, void* sf, int64_t sf_stride,
+                       bool ue8m0, int m, int k, hipStream_t stream);
 
 hipError_t launch_transform_sf(const float* in, int num_groups, int mn, int sf_k, int gran_mn,
                                int pack, void* out, int32_t* count, hipStream_t stream);

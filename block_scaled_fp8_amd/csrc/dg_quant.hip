@@ -28,9 +28,21 @@ __device__ __forceinline__ uint32_t e4m3_pair(float a, float b, uint32_t word) {
 
 constexpr int ITEMS = 4;  // (row, chunk) items per wave, all loaded before any is cast
 
-template <bool BF16>
+// UE8M0 code of the smallest power of two >= t (t >= 0 a finite FP32 scale; 1 for t == 0,
+// at least 2^-126): the exponent field, plus one when any mantissa bit is set.
+__device__ __forceinline__ uint32_t ue8m0_ceil(float t) {
+  const uint32_t b = __float_as_uint(t);
+  const uint32_t e = b >> 23;
+  if (t == 0.f) return 127u;
+  if (e == 0u) return 1u;
+  return e + ((b & 0x7FFFFFu) != 0u);
+}
+
+// UE8M0: the scales are written as packed codes, the word of a row and item holding its four
+// groups (byte t = group 4*item + t; bytes past the last group are 0), at sf[item*sf_stride + row].
+template <bool BF16, bool UE8M0>
 __global__ void __launch_bounds__(256) cast_kernel(const void* __restrict__ x, int64_t ldx, uint8_t* __restrict__ q,
-                                                   int64_t ldq, float* __restrict__ sf, int64_t sf_stride,
+                                                   int64_t ldq, void* __restrict__ sf, int64_t sf_stride,
                                                    uint32_t items, uint32_t chunks, int sf_k) {
   const int lane = threadIdx.x & 63;
   const uint32_t w0 = (blockIdx.x * 4u + (threadIdx.x >> 6)) * ITEMS;  // first (row, chunk of 4 groups)
@@ -76,7 +88,12 @@ __global__ void __launch_bounds__(256) cast_kernel(const void* __restrict__ x, i
     for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[it][i]));
 #pragma unroll
     for (int d = 8; d >= 1; d >>= 1) amax = fmaxf(amax, __shfl_xor(amax, d));  // within 16 lanes
-    const float s = amax == 0.f ? 1.f : __fdiv_rn(amax, 448.f);
+    float s = amax == 0.f ? 1.f : __fdiv_rn(amax, 448.f);
+    uint32_t code = 0;
+    if constexpr (UE8M0) {
+      code = ue8m0_ceil(s);
+      s = __uint_as_float(code << 23);
+    }
     // v / s correctly rounded, from the correctly rounded reciprocal y: q0 = v*y is within an
     // ulp, the FMA gives its exact remainder, and one more FMA rounds correctly (Markstein's
     // theorem).  Three instructions instead of a full division per element; a scale so small
@@ -99,27 +116,41 @@ __global__ void __launch_bounds__(256) cast_kernel(const void* __restrict__ x, i
     if (act[it]) {
       const int64_t col = (int64_t)gs[it] * 128 + (lane & 15) * 8;
       *(v2u*)(q + rows[it] * ldq + col) = (v2u){lo, hi};
-      if ((lane & 15) == 0) sf[(int64_t)gs[it] * sf_stride + rows[it]] = s;
+      if (!UE8M0 && (lane & 15) == 0) ((float*)sf)[(int64_t)gs[it] * sf_stride + rows[it]] = s;
+    }
+    if constexpr (UE8M0) {
+      // the four groups' codes into lane 0's word (inactive groups contribute 0)
+      const uint32_t mine = act[it] ? code : 0u;
+      const uint32_t word = __shfl(mine, 0) | (__shfl(mine, 16) << 8) | (__shfl(mine, 32) << 16) |
+                            (__shfl(mine, 48) << 24);
+      const uint32_t w = w0 + it;
+      if (lane == 0 && w < items) {
+        const uint32_t chunk = w - (uint32_t)rows[it] * chunks;
+        ((uint32_t*)sf)[(int64_t)chunk * sf_stride + rows[it]] = word;
+      }
     }
   }
 }
 
 }  // namespace
 
-hipError_t launch_cast(const void* x, int64_t ldx, bool bf16, uint8_t* q, int64_t ldq, float* sf, int64_t sf_stride,
-                       int m, int k, hipStream_t stream) {
+hipError_t launch_cast(const void* x, int64_t ldx, bool bf16, uint8_t* q, int64_t ldq, void* sf, int64_t sf_stride,
+                       bool ue8m0, int m, int k, hipStream_t stream) {
   const int sf_k = k / 128;
   const int chunks = (sf_k + 3) / 4;
   const int64_t items = (int64_t)m * chunks;
   const int64_t waves = (items + ITEMS - 1) / ITEMS;
   const int64_t blocks = (waves + 3) / 4;
   if (blocks * 4 * ITEMS > 0xFFFFFFFFll) return hipErrorInvalidValue;  // item indices are 32-bit
-  if (bf16)
-    hipLaunchKernelGGL(cast_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream, x, ldx, q, ldq, sf,
+#define DG_CAST(B, U)                                                                                     \
+  if (bf16 == B && ue8m0 == U)                                                                          \
+    hipLaunchKernelGGL((cast_kernel<B, U>), dim3((unsigned)blocks), dim3(256), 0, stream, x, ldx, q, ldq, sf, \
                        sf_stride, (uint32_t)items, (uint32_t)chunks, sf_k);
-  else
-    hipLaunchKernelGGL(cast_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream, x, ldx, q, ldq, sf,
-                       sf_stride, (uint32_t)items, (uint32_t)chunks, sf_k);
+  DG_CAST(true, false)
+  DG_CAST(false, false)
+  DG_CAST(true, true)
+  DG_CAST(false, true)
+#undef DG_CAST
   return hipGetLastError();
 }
 

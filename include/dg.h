@@ -160,14 +160,21 @@ int dg_m_grouped_fp8_gemm_nt_masked(int32_t num_groups, int32_t m_max, int32_t n
  * Both divisions are correctly rounded FP32 divisions.
  *  x, ldx, x_dtype : BF16 or FP32 [m, k], row stride ldx elements; rows and start 16-byte aligned.
  *  q, ldq          : E4M3 codes [m, k] (uint8), row stride ldq (a multiple of 8), 8-byte aligned.
- *  sf, sf_stride   : FP32 scales, MN-major: element (r, b) at sf[b*sf_stride + r], sf_stride ==
- *                    align4(m) (what dg_fp8_gemm_nt takes as sfa).  Padding rows [m, align4(m))
- *                    are not written.
+ *  sf, sf_stride   : the scales, MN-major with sf_stride == align4(m) (what dg_fp8_gemm_nt takes
+ *                    as sfa in the same sf_format).  Padding rows [m, align4(m)) are not written.
+ *  sf_format       : DG_SF_F32: FP32 s[r, b] at sf[b*sf_stride + r], 4-byte aligned.
+ *                    DG_SF_UE8M0X4 (scales restricted to powers of two, page
+ *                    "02 · DeepGEMM 技术解析" §3.1): s[r, b] is amax / 448 (FP32) raised to the
+ *                    next power of two (1 for an all-zero group, at least 2^-126), so every
+ *                    quotient stays within +-448; its 8-bit exponent code goes to byte b % 4 of
+ *                    int32 word (r, b / 4) at sf[(b/4)*sf_stride + r] (bytes past the last group
+ *                    are 0), sf 4-byte aligned.  The codes equal dg_transform_sf's packing of
+ *                    the same scales.
  *  k must be a positive multiple of 128.  m == 0 is a no-op (pointers may be NULL).
  *  Non-finite inputs give unspecified codes and scales.
  */
 int dg_per_token_group_cast_fp8(int32_t m, int32_t k, const void* x, int64_t ldx, int32_t x_dtype,
-                                void* q, int64_t ldq, float* sf, int64_t sf_stride,
+                                void* q, int64_t ldq, void* sf, int64_t sf_stride, int32_t sf_format,
                                 hipStream_t stream);
 
 /*

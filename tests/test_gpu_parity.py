@@ -166,6 +166,56 @@ def test_cast_feeds_the_gemm():
     assert ok.all(), st
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("m,k", [(1, 128), (3, 384), (5, 640), (9, 1664), (37, 1152), (130, 7168)])
+def test_per_token_group_cast_ue8m0_bitwise(dtype, m, k):
+    """The cast with power-of-two scales: E4M3 codes bit for bit against the oracle, and the
+    packed scale words against the oracle's own packing of its scales (k/128 = 1, 3, 5, 13,
+    9, 56 groups: one, partly and exactly filled last words)."""
+    x = _cast_input(m, k, seed=m * 11 + k)
+    say("cast ue8m0", dtype, m, k)
+    xt = torch.from_numpy(x).to(DEV).to(dtype)
+    q, sf = dg.per_token_group_cast_fp8(xt, pack_ue8m0=True)
+    torch.cuda.synchronize()
+    seen = xt.float().cpu().numpy()
+    qo, so = oracle.per_token_group_cast(seen, ue8m0=True)
+    words, _ = oracle.transform_sf(so, m, 1, True)            # [ceil(sf_k/4), align4(m)]
+    assert np.array_equal(q.cpu().numpy(), qo)
+    assert np.array_equal(sf.cpu().numpy().view(np.uint32), words[:, :m].T.view(np.uint32))
+
+
+@pytest.mark.parametrize("pack", [False, True])
+def test_cast_out_overwrites_an_earlier_result(pack):
+    """``out=`` reuses the buffers of an earlier call on a smaller-valued input: every code and
+    scale is rewritten (no stale value from the first call survives)."""
+    x1, x2 = _cast_input(70, 640, seed=3), _cast_input(70, 640, seed=4) * np.float32(0.01)
+    say("cast out=", pack)
+    first = dg.per_token_group_cast_fp8(torch.from_numpy(x1).to(DEV), pack_ue8m0=pack)
+    q, sf = dg.per_token_group_cast_fp8(torch.from_numpy(x2).to(DEV), pack_ue8m0=pack, out=first)
+    fresh_q, fresh_sf = dg.per_token_group_cast_fp8(torch.from_numpy(x2).to(DEV), pack_ue8m0=pack)
+    torch.cuda.synchronize()
+    assert q.data_ptr() == first[0].data_ptr() and sf.data_ptr() == first[1].data_ptr()
+    assert torch.equal(q.cpu(), fresh_q.cpu())
+    assert np.array_equal(sf.cpu().numpy().view(np.uint32), fresh_sf.cpu().numpy().view(np.uint32))
+
+
+def test_cast_ue8m0_feeds_the_gemm():
+    """Packed UE8M0 output of the cast is the GEMM's activation scale operand as it stands."""
+    p = gen.grouped_masked(1, 200, 384, 640, seed=43, pow2_scales=True)
+    x = _cast_input(200, 640, seed=44)
+    say("cast ue8m0 -> gemm")
+    q, sf = dg.per_token_group_cast_fp8(torch.from_numpy(x).to(DEV), pack_ue8m0=True)
+    sb = dg.get_mn_major_tma_aligned_packed_ue8m0_tensor(cuda(p["sb"][0]), gran_mn=128, mn=384)
+    d = torch.full((200, 384), float("nan"), dtype=torch.bfloat16, device=DEV)
+    dg.fp8_gemm_nt((q, sf), (cuda(p["b"][0]), sb), d)
+    torch.cuda.synchronize()
+    qo, so = oracle.per_token_group_cast(x, ue8m0=True)
+    o, T = oracle.gemm_nt(qo, so, p["b"][0], p["sb"][0], 128, want_abs=True)
+    ok, st = check_bf16(bf16_bits(d), o, T)
+    say("cast ue8m0 -> gemm", st)
+    assert ok.all(), st
+
+
 # ---------------------------------------------------------------- dense
 def test_config1_tiny_bf16():
     p = gen.config1()

@@ -141,16 +141,17 @@ def test_transform_validation():
 
 def test_cast_validation():
     lib = dg.lib()
-    # (m, k, x, ldx, x_dtype, q, ldq, sf, sf_stride, stream); x_dtype 1 = BF16, 2 = FP32
-    assert lib.dg_per_token_group_cast_fp8(16, 256, P, 256, 3, P, 256, P, 16, None) == DG_ERR_DTYPE
-    assert lib.dg_per_token_group_cast_fp8(16, 200, P, 256, 1, P, 256, P, 16, None) == DG_ERR_SHAPE
-    assert lib.dg_per_token_group_cast_fp8(-1, 256, P, 256, 1, P, 256, P, 16, None) == DG_ERR_SHAPE
-    assert lib.dg_per_token_group_cast_fp8(16, 256, None, 256, 1, P, 256, P, 16, None) == DG_ERR_NULL
-    assert lib.dg_per_token_group_cast_fp8(15, 256, P, 256, 1, P, 256, P, 15, None) == DG_ERR_LAYOUT   # stride align4(15) = 16
-    assert lib.dg_per_token_group_cast_fp8(16, 256, P, 260, 1, P, 256, P, 16, None) == DG_ERR_LAYOUT   # 520-byte rows
-    assert lib.dg_per_token_group_cast_fp8(16, 256, P, 256, 1, P, 252, P, 16, None) == DG_ERR_LAYOUT   # ldq < k
-    assert lib.dg_per_token_group_cast_fp8(16, 256, P_MIS, 256, 1, P, 256, P, 16, None) == DG_ERR_LAYOUT
-    assert lib.dg_per_token_group_cast_fp8(0, 256, None, 0, 1, None, 0, None, 0, None) == DG_OK
+    # (m, k, x, ldx, x_dtype, q, ldq, sf, sf_stride, sf_format, stream); x_dtype 1 = BF16, 2 = FP32
+    assert lib.dg_per_token_group_cast_fp8(16, 256, P, 256, 3, P, 256, P, 16, 0, None) == DG_ERR_DTYPE
+    assert lib.dg_per_token_group_cast_fp8(16, 200, P, 256, 1, P, 256, P, 16, 0, None) == DG_ERR_SHAPE
+    assert lib.dg_per_token_group_cast_fp8(-1, 256, P, 256, 1, P, 256, P, 16, 0, None) == DG_ERR_SHAPE
+    assert lib.dg_per_token_group_cast_fp8(16, 256, None, 256, 1, P, 256, P, 16, 0, None) == DG_ERR_NULL
+    assert lib.dg_per_token_group_cast_fp8(15, 256, P, 256, 1, P, 256, P, 15, 0, None) == DG_ERR_LAYOUT   # stride align4(15) = 16
+    assert lib.dg_per_token_group_cast_fp8(16, 256, P, 260, 1, P, 256, P, 16, 0, None) == DG_ERR_LAYOUT   # 520-byte rows
+    assert lib.dg_per_token_group_cast_fp8(16, 256, P, 256, 1, P, 252, P, 16, 0, None) == DG_ERR_LAYOUT   # ldq < k
+    assert lib.dg_per_token_group_cast_fp8(16, 256, P_MIS, 256, 1, P, 256, P, 16, 0, None) == DG_ERR_LAYOUT
+    assert lib.dg_per_token_group_cast_fp8(0, 256, None, 0, 1, None, 0, None, 0, 0, None) == DG_OK
+    assert lib.dg_per_token_group_cast_fp8(16, 256, P, 256, 1, P, 256, P, 16, 2, None) == DG_ERR_DTYPE   # sf_format
 
 
 # ---------------------------------------------------------------- tile planning
