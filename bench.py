@@ -45,8 +45,12 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def read_traffic(workload):
-    """HBM bytes per launch of the GEMM kernel from the committed rocprofv3 counter summary,
+GEMM_SOURCES = ("dg_gemm.hip", "dg_gemm_pipe.hip", "dg_internal.h")
+CAST_SOURCES = ("dg_quant.hip", "dg_internal.h")
+
+
+def read_traffic(workload, hash_key="kernel_source_sha1", sources=GEMM_SOURCES):
+    """HBM bytes per launch of the timed kernel from the committed rocprofv3 counter summary,
     or None if absent or taken from an older kernel build."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
@@ -57,16 +61,16 @@ def read_traffic(workload):
             k, v = line.split("=", 1)
             vals[k.strip()] = v.strip()
     key = f"{workload}.bytes_per_launch"
-    src_hash = vals.get("kernel_source_sha1")
-    if key not in vals or src_hash != kernel_source_hash():
+    src_hash = vals.get(hash_key)
+    if key not in vals or src_hash != kernel_source_hash(sources):
         return None
     return float(vals[key])
 
 
-def kernel_source_hash():
+def kernel_source_hash(sources=GEMM_SOURCES):
     import hashlib
     h = hashlib.sha1()
-    for f in ("dg_gemm.hip", "dg_gemm_pipe.hip", "dg_internal.h"):
+    for f in sources:
         with open(os.path.join(ROOT, "block_scaled_fp8_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
@@ -207,6 +211,7 @@ def bench_cast(args, spec, dg, dev):
     sets = [torch.randn((M, K), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16) for _ in range(8)]
     sf_bytes = 4 * (K // 512) if ue8m0 else 4 * (K // 128)   # per row: packed codes or FP32 scales
     alg_bytes = M * K * 2 + M * K + M * sf_bytes
+    copy_calibration(args, dev)
     stream = torch.cuda.current_stream()
     # two output sets, allocated once and overwritten in turn
     outs = [dg.per_token_group_cast_fp8(sets[i], pack_ue8m0=ue8m0) for i in range(2)]
@@ -241,7 +246,8 @@ def bench_cast(args, spec, dg, dev):
         "config": {"workload": args.workload, "M": M, "K": K, "buffer_sets": len(sets),
                    "scales": "ue8m0x4" if ue8m0 else "f32"},
         "roofline": {"bound": "hbm", "achieved": round(alg_bytes / (avg * 1e-3) / 1e9, 2), "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": round(alg_bytes / (avg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(alg_bytes / (avg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                     "traffic": read_traffic(args.workload, "cast_source_sha1", CAST_SOURCES),
                      "kernel": f"dg::cast_kernel<true, {'true' if ue8m0 else 'false'}>", "avg_ms": round(avg, 5), "alg_bytes": alg_bytes},
         "cpu_baseline": cpu,
     }

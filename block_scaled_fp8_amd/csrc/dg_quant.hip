@@ -5,10 +5,12 @@
 //
 // An item is four consecutive groups of one row: lane l holds elements 8l..8l+7 (one
 // 16-byte load for BF16, two for FP32), so 16 lanes cover a group and the group's amax is
-// a 4-step xor shuffle inside those 16 lanes.  A wave loads four items before casting any,
-// to keep enough bytes in flight.  The scale and every quotient are correctly rounded FP32
-// divisions; the E4M3 code is rounded to nearest, ties to even, by the hardware conversion.
-// Algorithmic traffic: (2 or 4) + 1 bytes per element plus 4 per 128 elements.
+// a 4-step xor shuffle inside those 16 lanes.  A wave loads two items before casting either
+// (measured on the 4096x7168 BF16 cast: two items per wave 20.5 us, four 23.5 us, eight
+// 28 us; more, smaller waves keep more loads in flight across the chip).  The scale and every
+// quotient are correctly rounded FP32 divisions; the E4M3 code is rounded to nearest, ties to
+// even, by the hardware conversion.  Algorithmic traffic: (2 or 4) + 1 bytes per element plus
+// 4 per 128 elements (FP32 scales) or 4 per 512 (packed UE8M0 codes).
 #include "dg_internal.h"
 
 namespace dg {
@@ -26,7 +28,7 @@ __device__ __forceinline__ uint32_t e4m3_pair(float a, float b, uint32_t word) {
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)word, HI);
 }
 
-constexpr int ITEMS = 4;  // (row, chunk) items per wave, all loaded before any is cast
+constexpr int ITEMS = 2;  // (row, chunk) items per wave, both loaded before either is cast
 
 // UE8M0 code of the smallest power of two >= t (t >= 0 a finite FP32 scale; 1 for t == 0,
 // at least 2^-126): the exponent field, plus one when any mantissa bit is set.
@@ -45,7 +47,12 @@ __global__ void __launch_bounds__(256) cast_kernel(const void* __restrict__ x, i
                                                    int64_t ldq, void* __restrict__ sf, int64_t sf_stride,
                                                    uint32_t items, uint32_t chunks, int sf_k) {
   const int lane = threadIdx.x & 63;
-  const uint32_t w0 = (blockIdx.x * 4u + (threadIdx.x >> 6)) * ITEMS;  // first (row, chunk of 4 groups)
+  // Workgroups are dealt to the eight XCDs in turn; renumber them so that each XCD takes one
+  // contiguous run of items.  Neighbouring rows then share an L2, whose write-back merges
+  // their 4-byte scale stores (MN-major, adjacent rows adjacent in memory) into whole lines.
+  const uint32_t nb = gridDim.x, per = nb >> 3, extra = nb & 7, xcd = blockIdx.x & 7, idx = blockIdx.x >> 3;
+  const uint32_t blk = xcd < extra ? xcd * (per + 1) + idx : extra * (per + 1) + (xcd - extra) * per + idx;
+  const uint32_t w0 = (blk * 4u + (threadIdx.x >> 6)) * ITEMS;  // first (row, chunk of 4 groups)
   if (w0 >= items) return;                                              // whole waves only
   float v[ITEMS][8];
   int64_t rows[ITEMS];
