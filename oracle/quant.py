@@ -12,9 +12,9 @@ E4M3; page "第13章 DeepGEMM" §13.3 names the same amax/448 scale):
 Every step is done in FP32, as the GPU does it, because the quotient decides an integer
 code.  For scales stored as UE8M0 (page "02 · DeepGEMM 技术解析" §3.1: powers of two only)
 the FP32 scale is raised to the next power of two before the division (reading: rounding
-it down, as the layout transform does for a given scale, would push quotients past 448).  The E4M3 rounding here is written as a nearest-value search over the 127
-non-negative finite E4M3 values (ties to the even code), independent of any bit-level
-encoder.
+it down, as the layout transform does for a given scale, would push quotients past 448).
+The E4M3 rounding here is written as a nearest-value search over the 127 non-negative
+finite E4M3 values (ties to the even code), independent of any bit-level encoder.
 """
 import numpy as np
 
