@@ -21,7 +21,7 @@ over blocks round (one float64 rounding each).
 Modules:
   codecs  -- E4M3 decode, UE8M0 encode/decode, float64 -> BF16 round-to-nearest-even
   layout  -- the scale-layout transform (MN-major, 4-aligned stride, UE8M0 x4 packing)
-  gemm    -- dense NT, M-grouped contiguous and M-grouped masked references
+  gemm    -- dense NT, M-grouped contiguous, M-grouped masked and K-grouped references
   quant   -- the per-token-group FP8 cast (E4M3 codes and 1x128 FP32 scales)
 
 Parity pins: every function here is pinned by a `-m "not gpu"` test in
@@ -34,6 +34,6 @@ from . import codecs, layout, gemm, quant  # noqa: F401
 from .codecs import (e4m3_decode_table, e4m3_decode, ue8m0_encode, ue8m0_decode,
                      bf16_rne, bf16_bits_to_f64, pow2_violation)  # noqa: F401
 from .layout import align4, transform_sf, unpack_ue8m0  # noqa: F401
-from .gemm import (gemm_nt, gemm_nt_points, grouped_contiguous, grouped_masked,
+from .gemm import (gemm_nt, gemm_nt_points, grouped_contiguous, grouped_masked, k_grouped,
                    expand_scales_b)  # noqa: F401
 from .quant import e4m3_encode_rne, per_token_group_cast  # noqa: F401

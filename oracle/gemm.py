@@ -154,3 +154,36 @@ def grouped_masked(a_codes, sa, b_codes, sb, masked_m, gran_n=128, want_abs=Fals
         else:
             D[g, :m] = r
     return (D, T) if want_abs else D
+
+
+def k_grouped(a_codes, sa, b_codes, sb, ks, c, want_abs=False):
+    """K-grouped contiguous reference (the MoE weight-gradient form: page "02 · DeepGEMM
+    技术解析" §3.3 and page "第13章 DeepGEMM" §13.6 and §13.13): M and N are fixed, the
+    groups are concatenated along K, and group g accumulates its own K range into its
+    own output, starting from the required C term:
+
+        D[g] = C[g] + sum_{b in group g's K blocks} sa[:, b] * sb[:, b] * P_b
+
+    a_codes [M, sum K], b_codes [N, sum K]; sa [M, sum sf_k], sb [N, sum sf_k] (one scale
+    per row and 128-long K block on both sides, logical layout); ks: the K of each group,
+    each a multiple of 128 (0 allowed: then D[g] = C[g]); c [G, M, N].  Returns D [G, M, N].
+    """
+    ks = [int(k) for k in ks]
+    assert all(k >= 0 and k % BLOCK_K == 0 for k in ks)
+    c = np.asarray(c, dtype=np.float64)
+    G, M, N = c.shape
+    assert len(ks) == G and a_codes.shape == (M, sum(ks)) and b_codes.shape == (N, sum(ks))
+    D = c.copy()
+    T = np.zeros((G, M, N)) if want_abs else None
+    k0 = 0
+    for g, k in enumerate(ks):              # one dense NT product per group
+        if k:
+            kr, br = slice(k0, k0 + k), slice(k0 // BLOCK_K, (k0 + k) // BLOCK_K)
+            r = gemm_nt(a_codes[:, kr], np.asarray(sa)[:, br], b_codes[:, kr], np.asarray(sb)[:, br], 1,
+                        c=c[g], want_abs=want_abs)
+            if want_abs:
+                D[g], T[g] = r
+            else:
+                D[g] = r
+        k0 += k
+    return (D, T) if want_abs else D

@@ -397,3 +397,63 @@ def test_per_token_group_cast_ue8m0_scales():
     assert np.all(s >= s32) and np.all(s < 2 * s32)                       # the next power of two
     assert np.array_equal(codecs.ue8m0_decode(codecs.ue8m0_encode(s)), s.astype(np.float64))  # exact in UE8M0
     assert np.all(np.abs(codecs.e4m3_decode(q)) <= 448)
+
+
+def test_k_grouped_brute_force_exact():
+    """K-grouped oracle against exact rational arithmetic written from the definition: each
+    group sums the scaled products of its own K range only, into its own output, on top of
+    its own C (an empty group returns C)."""
+    from fractions import Fraction
+    rng = np.random.default_rng(71)
+    M, N, ks = 2, 3, [128, 0, 256, 128]
+    K = sum(ks)
+    a = rng.integers(0, 256, (M, K), dtype=np.uint8)
+    b = rng.integers(0, 256, (N, K), dtype=np.uint8)
+    a[(a & 0x7F) == 0x7F] = 0x30          # no NaN codes
+    b[(b & 0x7F) == 0x7F] = 0x30
+    sa = np.exp2(rng.uniform(-6, 2, (M, K // 128))).astype(np.float32)
+    sb = np.exp2(rng.uniform(-6, 2, (N, K // 128))).astype(np.float32)
+    c = rng.standard_normal((len(ks), M, N)).astype(np.float32)
+    A, B = oracle.e4m3_decode(a), oracle.e4m3_decode(b)
+    got = oracle.k_grouped(a, sa, b, sb, ks, c)
+    k0 = 0
+    for g, kg in enumerate(ks):
+        for i in range(M):
+            for j in range(N):
+                exact = Fraction(float(c[g, i, j]))
+                mag = abs(exact)
+                for k in range(k0, k0 + kg):
+                    t = Fraction(float(sa[i, k // 128])) * Fraction(float(sb[j, k // 128])) * \
+                        Fraction(float(A[i, k])) * Fraction(float(B[j, k]))
+                    exact += t
+                    mag += abs(t)
+                assert abs(Fraction(float(got[g, i, j])) - exact) <= Fraction(1, 10 ** 14) * mag, (g, i, j)
+        k0 += kg
+    assert np.array_equal(got[1], c[1].astype(np.float64))          # the empty group is C itself
+
+
+def test_k_grouped_single_group_is_the_dense_product():
+    """One group covering all of K is the dense NT product with per-row scales on both sides
+    (a special case that reduces to the pinned dense reference), and permuting the groups
+    permutes the outputs."""
+    rng = np.random.default_rng(72)
+    M, N, K = 5, 7, 512
+    a = (rng.integers(0, 0x7E, (M, K)) | (rng.integers(0, 2, (M, K)) << 7)).astype(np.uint8)
+    b = (rng.integers(0, 0x7E, (N, K)) | (rng.integers(0, 2, (N, K)) << 7)).astype(np.uint8)
+    sa = rng.uniform(0.01, 1, (M, 4)).astype(np.float32)
+    sb = rng.uniform(0.01, 1, (N, 4)).astype(np.float32)
+    c = rng.standard_normal((1, M, N)).astype(np.float32)
+    d = oracle.k_grouped(a, sa, b, sb, [K], c)
+    assert np.array_equal(d[0], oracle.gemm_nt(a, sa, b, sb, 1, c=c[0]))
+    # two groups [256, 256] vs the same groups swapped: outputs swap
+    c2 = rng.standard_normal((2, M, N)).astype(np.float32)
+    d2 = oracle.k_grouped(a, sa, b, sb, [256, 256], c2)
+    sw = lambda x: np.concatenate([x[:, 256:], x[:, :256]], axis=1)
+    sws = lambda s: np.concatenate([s[:, 2:], s[:, :2]], axis=1)
+    d3 = oracle.k_grouped(sw(a), sws(sa), sw(b), sws(sb), [256, 256], c2[::-1])
+    assert np.array_equal(d2, d3[::-1])
+    # the two halves of K add up to the whole, up to the rounding of the sum
+    z = np.zeros((2, M, N), dtype=np.float32)
+    halves = oracle.k_grouped(a, sa, b, sb, [256, 256], z)
+    whole = oracle.k_grouped(a, sa, b, sb, [K], z[:1])[0]
+    assert np.allclose(halves[0] + halves[1], whole, rtol=1e-13, atol=1e-13)
