@@ -24,7 +24,7 @@ import torch
 __all__ = [
     "DGError", "lib", "fp8_gemm_nt", "m_grouped_fp8_gemm_nt_contiguous", "m_grouped_fp8_gemm_nt_masked",
     "transform_sf", "get_mn_major_tma_aligned_tensor", "get_mn_major_tma_aligned_packed_ue8m0_tensor",
-    "per_token_group_cast_fp8", "get_tma_aligned_size", "get_mk_alignment_for_contiguous_layout", "set_num_sms", "get_num_sms",
+    "per_token_group_cast_fp8", "k_grouped_fp8_gemm_nt_contiguous", "get_tma_aligned_size", "get_mk_alignment_for_contiguous_layout", "set_num_sms", "get_num_sms",
     "get_gemm_config", "LIB_PATH",
 ]
 
@@ -43,6 +43,7 @@ _SIGS = {
     "dg_m_grouped_fp8_gemm_nt_masked": (_i32, [_i32, _i32, _i32, _i32, _p, _i64, _i64, _p, _i64, _i64, _p, _i64,
                                                _i64, _p, _i64, _i64, _i32, _i32, _p, _i64, _i64, _i32, _p, _i32, _p]),
     "dg_transform_sf": (_i32, [_p, _i32, _i32, _i32, _i32, _i32, _p, _p, _p]),
+    "dg_k_grouped_fp8_gemm_nt_contiguous": (_i32, [_i32, _i32, _i32, _p, _p, _i64, _p, _p, _i64, _p, _p, _p, _p]),
     "dg_per_token_group_cast_fp8": (_i32, [_i32, _i32, _p, _i64, _i32, _p, _i64, _p, _i64, _i32, _p]),
     "dg_get_tma_aligned_size": (_i64, [_i64, _i32]),
     "dg_get_mk_alignment_for_contiguous_layout": (_i32, []),
@@ -266,6 +267,34 @@ def fp8_gemm_nt(a, b, d, c=None, recipe=None, pack_ue8m0=False):
                                 _ptr(B), B.stride(0), _ptr(sfb_t), sfb_stride, fmt, gran_n,
                                 _ptr(c), c.stride(0) if c is not None else 0,
                                 _ptr(d), d.stride(0), _out_dtype(d), _stream(d)))
+    return d
+
+
+def k_grouped_fp8_gemm_nt_contiguous(a, b, d, ks, c):
+    """K-grouped GEMM (MoE weight gradient): ``a = (A [m, sum ks], sfa [sum ks // 128, m])``,
+    ``b = (B [n, sum ks], sfb [sum ks // 128, n])`` with FP32 per-row scales, ``ks`` the K of
+    each group (multiples of 128), ``d`` and ``c`` FP32 [G, m, n]; ``c`` is required and may be
+    ``d`` itself.  D[g] = C[g] + A[:, group g] @ B[:, group g].T (scaled per 128-long block)."""
+    A, sfa = a
+    B, sfb = b
+    _codes(A)
+    _codes(B)
+    ks = [int(k) for k in ks]
+    G = len(ks)
+    m, n = A.shape[0], B.shape[0]
+    if c is None:
+        raise ValueError("the K-grouped GEMM requires c (pass d itself to accumulate in place)")
+    for t, name in ((sfa, "sfa"), (sfb, "sfb"), (c, "c"), (d, "d")):
+        if t.dtype != torch.float32 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous float32 tensor")
+    if tuple(d.shape) != (G, m, n) or tuple(c.shape) != (G, m, n):
+        raise ValueError(f"c and d must be [{G}, {m}, {n}]")
+    if tuple(sfa.shape) != (sum(ks) // 128, m) or tuple(sfb.shape) != (sum(ks) // 128, n):
+        raise ValueError("sfa and sfb must be [sum(ks) // 128, m] and [sum(ks) // 128, n]")
+    ks_host = (ctypes.c_int32 * G)(*ks)
+    _check(lib().dg_k_grouped_fp8_gemm_nt_contiguous(G, m, n, ks_host, _ptr(A), A.stride(0), _ptr(sfa),
+                                                     _ptr(B), B.stride(0), _ptr(sfb), _ptr(c), _ptr(d),
+                                                     _stream(d)))
     return d
 
 

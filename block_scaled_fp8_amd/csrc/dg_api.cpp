@@ -301,6 +301,56 @@ int dg_m_grouped_fp8_gemm_nt_masked(int32_t num_groups, int32_t m_max, int32_t n
   return do_launch(p, dg::GRP_MASKED, em, m_max, sf_mode_of(sf_format, gran_n), out, stream);
 }
 
+int dg_k_grouped_fp8_gemm_nt_contiguous(int32_t num_groups, int32_t m, int32_t n, const int32_t* ks,
+                                        const void* a, int64_t lda, const float* sfa, const void* b, int64_t ldb,
+                                        const float* sfb, const float* c, float* d, hipStream_t stream) {
+  if (num_groups <= 0) return fail(DG_ERR_SHAPE, "num_groups = %d must be positive", num_groups);
+  if (m < 0 || n < 0) return fail(DG_ERR_SHAPE, "m = %d and n = %d must not be negative", m, n);
+  if (!ks) return fail(DG_ERR_NULL, "ks (host array of num_groups K sizes) must not be NULL");
+  int64_t sum_k = 0;
+  for (int g = 0; g < num_groups; ++g) {
+    if (ks[g] < 0 || ks[g] % 128 != 0) return fail(DG_ERR_SHAPE, "ks[%d] = %d must be a non-negative multiple of 128", g, ks[g]);
+    sum_k += ks[g];
+  }
+  if (m % 4 != 0 || n % 4 != 0) return fail(DG_ERR_SHAPE, "m = %d and n = %d must be multiples of 4", m, n);
+  if (m == 0 || n == 0) return ok();
+  if (!c || !d) return fail(DG_ERR_NULL, "c and d must not be NULL (c may equal d)");
+  if (sum_k > 0 && (!a || !b || !sfa || !sfb)) return fail(DG_ERR_NULL, "a, sfa, b and sfb must not be NULL");
+  if (lda < sum_k || ldb < sum_k) return fail(DG_ERR_LAYOUT, "lda and ldb must be >= sum(ks) = %lld", (long long)sum_k);
+  // every group is checked before any is launched, so an error writes nothing
+  const int64_t mn = (int64_t)m * n;
+  int64_t k0 = 0;
+  for (int pass = 0; pass < 2; ++pass) {
+    k0 = 0;
+    for (int g = 0; g < num_groups; ++g) {
+      const float* cg = c + g * mn;
+      float* dg = d + g * mn;
+      if (ks[g] == 0) {
+        if (pass == 1 && cg != dg) {
+          const hipError_t e = hipMemcpyAsync(dg, cg, mn * sizeof(float), hipMemcpyDeviceToDevice, stream);
+          if (e != hipSuccess) return fail(DG_ERR_HIP, "copy of C into D failed: %s", hipGetErrorString(e));
+        }
+        continue;
+      }
+      const uint8_t* ag = (const uint8_t*)a + k0;
+      const uint8_t* bg = (const uint8_t*)b + k0;
+      const float* sag = sfa + (k0 / 128) * m;
+      const float* sbg = sfb + (k0 / 128) * n;
+      if (pass == 0) {
+        const int st = check_common(n, ks[g], ag, lda, sag, bg, ldb, sbg, n, DG_SF_F32, 1, dg, n, DG_OUT_F32, false);
+        if (st != DG_OK) return st;
+        if ((reinterpret_cast<uintptr_t>(cg) & 3u) != 0) return fail(DG_ERR_LAYOUT, "c must be 4-byte aligned");
+      } else {
+        const int st = dg_fp8_gemm_nt(m, n, ks[g], ag, lda, sag, m, bg, ldb, sbg, n, DG_SF_F32, 1, cg, n, dg, n,
+                                      DG_OUT_F32, stream);
+        if (st != DG_OK) return st;
+      }
+      k0 += ks[g];
+    }
+  }
+  return ok();
+}
+
 int dg_transform_sf(const float* sf_in, int32_t num_groups, int32_t mn, int32_t sf_k, int32_t gran_mn,
                     int32_t pack_ue8m0, void* sf_out, int32_t* nonpow2_count, hipStream_t stream) {
   if (num_groups <= 0 || mn < 0 || sf_k <= 0) return fail(DG_ERR_SHAPE, "need num_groups > 0, mn >= 0, sf_k > 0");

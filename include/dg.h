@@ -150,6 +150,32 @@ int dg_m_grouped_fp8_gemm_nt_masked(int32_t num_groups, int32_t m_max, int32_t n
                                     hipStream_t stream);
 
 /*
+ * K-grouped contiguous GEMM, the MoE weight-gradient form (page "02 · DeepGEMM 技术解析" §3.3:
+ * groups concatenated along K, two-dimensional [sum_sf_k, mn] FP32 scales, mn % 4 == 0, C
+ * required and best passed as D itself; page "第13章 DeepGEMM" §13.6 and §13.13: M and N
+ * fixed, the groups split K):
+ *
+ *   D[g] = C[g] + sum_{b in group g's K blocks} sa[b, i] * sb[b, j] * sum_{k in block b} A[i, k] * B[j, k]
+ *
+ *  num_groups   : > 0.  ks: HOST int32 [num_groups], group g's K (a multiple of 128, 0 allowed:
+ *                 then D[g] = C[g]); group g covers K columns [sum_{h<g} ks[h], +ks[g]).
+ *  m, n         : output sizes, both multiples of 4 (the scales carry no padding).  m == 0 or
+ *                 n == 0 is a no-op.
+ *  a, lda       : A E4M3 [m, sum(ks)], element (i, kk) at a[i*lda + kk]; lda >= sum(ks),
+ *                 lda % 16 == 0, 16-byte aligned.  b, ldb: B E4M3 [n, sum(ks)], the same rules.
+ *  sfa, sfb     : FP32 [sum(ks)/128, m] and [sum(ks)/128, n], row-major (block b of row i at
+ *                 sfa[b*m + i]): one scale per row and 128-long K block on both sides;
+ *                 16-byte aligned.
+ *  c, d         : FP32 [num_groups, m, n], contiguous (group g at + g*m*n); c must not be NULL
+ *                 and may equal d (in-place accumulation; otherwise C is read, D written).
+ * Every group is validated before any work is queued.  Returns DG_OK or a negative dg_status.
+ */
+int dg_k_grouped_fp8_gemm_nt_contiguous(int32_t num_groups, int32_t m, int32_t n, const int32_t* ks,
+                                        const void* a, int64_t lda, const float* sfa,
+                                        const void* b, int64_t ldb, const float* sfb,
+                                        const float* c, float* d, hipStream_t stream);
+
+/*
  * Per-token-group FP8 cast (page "02 · DeepGEMM 技术解析" §1.1: activations in 1x128 groups
  * along K, one FP32 scale per group; page "第13章 DeepGEMM" §13.3: the scale is amax / 448):
  * produces the A operand and its scales for the GEMMs above, already in their layout.

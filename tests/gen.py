@@ -171,3 +171,21 @@ def config4(seed=0):
 
 def config5(seed=0):
     return grouped_masked(32, 256, 7168, 2048, seed=seed, pow2_scales=True)
+
+
+def k_grouped(m, n, ks, seed=0):
+    """K-grouped weight-gradient problem: both operands are activation-like ([m, sum ks] and
+    [n, sum ks], N(0, 1) with x50 outliers quantized in 1x128 groups along K, so both carry
+    one scale per row and K block), and a C term [G, m, n] of N(0, 1)."""
+    rng = np.random.default_rng(seed)
+    K = int(sum(ks))
+    xa = rng.standard_normal((m, K), dtype=np.float32)
+    xb = rng.standard_normal((n, K), dtype=np.float32)
+    for x in (xa, xb):
+        if x.size:
+            idx = rng.choice(x.size, size=max(1, x.size // 1000), replace=False)
+            x.reshape(-1)[idx] *= np.float32(50.0)
+    a, sa = quantize_act(xa) if K else (np.zeros((m, 0), np.uint8), np.zeros((m, 0), np.float32))
+    b, sb = quantize_act(xb) if K else (np.zeros((n, 0), np.uint8), np.zeros((n, 0), np.float32))
+    c = rng.standard_normal((len(ks), m, n), dtype=np.float32)
+    return dict(a=a, sa=sa, b=b, sb=sb, c=c, ks=list(ks), m=m, n=n)

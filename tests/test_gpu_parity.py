@@ -216,6 +216,37 @@ def test_cast_ue8m0_feeds_the_gemm():
     assert ok.all(), st
 
 
+# ---------------------------------------------------------------- K-grouped
+@pytest.mark.parametrize("alias", [True, False])
+@pytest.mark.parametrize("m,n,ks", [(260, 196, [256, 0, 384, 128, 512]), (64, 520, [128]), (4, 4, [0, 128, 0]),
+                                    (516, 388, [1024, 128, 0, 640])])
+def test_k_grouped_contiguous(m, n, ks, alias):
+    """K-grouped GEMM against the oracle: groups of 1 to 8 K blocks and empty groups (D = C),
+    m and n ragged against every tile, C read separately or accumulated in place in D."""
+    p = gen.k_grouped(m, n, ks, seed=m + n + len(ks))
+    say("k-grouped", m, n, ks, "alias" if alias else "separate C")
+    a, b = cuda(p["a"]), cuda(p["b"])
+    sfa, sfb = cuda(np.ascontiguousarray(p["sa"].T)), cuda(np.ascontiguousarray(p["sb"].T))
+    c = cuda(p["c"])
+    if alias:
+        d = c.clone()
+        dg.k_grouped_fp8_gemm_nt_contiguous((a, sfa), (b, sfb), d, ks, d)
+    else:
+        d = torch.full_like(c, float("nan"))
+        dg.k_grouped_fp8_gemm_nt_contiguous((a, sfa), (b, sfb), d, ks, c)
+    torch.cuda.synchronize()
+    o, T = oracle.k_grouped(p["a"], p["sa"], p["b"], p["sb"], ks, p["c"], want_abs=True)
+    got = d.cpu().numpy()
+    ok, st = check_fp32(got, o, T)
+    say("k-grouped", st)
+    assert ok.all(), st
+    for g, k in enumerate(ks):
+        if k == 0:
+            assert np.array_equal(got[g], p["c"][g])      # an empty group is C, bit for bit
+    if not alias:
+        assert torch.equal(c.cpu(), torch.from_numpy(p["c"]))   # C is only read
+
+
 # ---------------------------------------------------------------- dense
 def test_config1_tiny_bf16():
     p = gen.config1()

@@ -191,3 +191,17 @@ def test_heuristic_contiguous_uses_the_alignment(monkeypatch):
     monkeypatch.delenv("DG_FORCE_TILE", raising=False)
     bm, bn, nt, grid = dg.get_gemm_config(1, 18432, 4096, 7168, num_groups=32, num_sms=256)
     assert bm <= dg.get_mk_alignment_for_contiguous_layout()
+
+
+def test_k_grouped_validation():
+    lib = dg.lib()
+    ks = lambda *v: (ctypes.c_int32 * len(v))(*v)
+    # (G, m, n, ks, a, lda, sfa, b, ldb, sfb, c, d, stream)
+    assert lib.dg_k_grouped_fp8_gemm_nt_contiguous(0, 8, 8, ks(128), P, 128, P, P, 128, P, P, P, None) == DG_ERR_SHAPE
+    assert lib.dg_k_grouped_fp8_gemm_nt_contiguous(2, 8, 8, ks(128, 100), P, 256, P, P, 256, P, P, P, None) == DG_ERR_SHAPE
+    assert lib.dg_k_grouped_fp8_gemm_nt_contiguous(1, 6, 8, ks(128), P, 128, P, P, 128, P, P, P, None) == DG_ERR_SHAPE   # m % 4
+    assert lib.dg_k_grouped_fp8_gemm_nt_contiguous(1, 8, 8, None, P, 128, P, P, 128, P, P, P, None) == DG_ERR_NULL
+    assert lib.dg_k_grouped_fp8_gemm_nt_contiguous(1, 8, 8, ks(128), P, 128, P, P, 128, P, None, P, None) == DG_ERR_NULL  # C required
+    assert lib.dg_k_grouped_fp8_gemm_nt_contiguous(2, 8, 8, ks(128, 128), P, 128, P, P, 256, P, P, P, None) == DG_ERR_LAYOUT  # lda < sum
+    assert lib.dg_k_grouped_fp8_gemm_nt_contiguous(1, 8, 8, ks(128), P_MIS, 128, P, P, 128, P, P, P, None) == DG_ERR_LAYOUT
+    assert lib.dg_k_grouped_fp8_gemm_nt_contiguous(1, 0, 8, ks(128), None, 0, None, None, 0, None, None, None, None) == DG_OK
