@@ -36,6 +36,9 @@ WORKLOADS = {
     "contiguous_32x4096x7168": dict(kind="contig"),
     "cast_4096x7168_bf16": dict(kind="cast", M=4096, K=7168),
     "cast_ue8m0_4096x7168_bf16": dict(kind="cast", M=4096, K=7168, ue8m0=True),
+    # MoE weight gradient: 8 experts' token counts (multiples of 128, 16384 in all) split K
+    "k_grouped_8x7168x2048_k16384": dict(kind="k_grouped", M=7168, N=2048,
+                                         ks=[1792, 2304, 2048, 1536, 2560, 2048, 1920, 2176]),
 }
 DEFAULT = "dense_4096x7168x2048"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
@@ -134,6 +137,8 @@ def main():
     spec = WORKLOADS[args.workload]
     if spec["kind"] == "cast":
         return bench_cast(args, spec, dg, dev)
+    if spec["kind"] == "k_grouped":
+        return bench_k_grouped(args, spec, dg, dev)
     if spec["kind"] not in ("dense", "dense_c"):
         return bench_grouped(args, spec, dg, dev)
 
@@ -197,6 +202,75 @@ def main():
                      "traffic": traffic, "kernel": "dg::pipe::pipe_kernel (GEMM launch alone)",
                      "gemm_avg_ms": round(gemm_avg_ms, 5), "gemm_min_ms": round(float(np.min(gemm_ms)), 5),
                      "alg_bytes": alg_bytes, "alg_flops": flops},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def bench_k_grouped(args, spec, dg, dev):
+    """The K-grouped GEMM of the MoE weight gradient, accumulating in place (C = D).  Both
+    operands are N(0, 1) activations cast per 1x128 group by the library's cast, whose scale
+    output is already the [sum ks / 128, mn] layout this GEMM takes."""
+    M, N, ks = spec["M"], spec["N"], spec["ks"]
+    K, G = sum(ks), len(ks)
+    g = torch.Generator(device=dev).manual_seed(0)
+    sets = []
+    for _ in range(2):
+        qa, sa = dg.per_token_group_cast_fp8(torch.randn((M, K), generator=g, device=dev).to(torch.bfloat16))
+        qb, sb = dg.per_token_group_cast_fp8(torch.randn((N, K), generator=g, device=dev).to(torch.bfloat16))
+        sets.append(dict(a=qa, sa=sa.t(), b=qb, sb=sb.t(), d=torch.zeros((G, M, N), device=dev)))
+    flops = 2.0 * M * N * K
+    alg_bytes = M * K + N * K + 4 * (M + N) * (K // 128) + 2 * 4 * G * M * N
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        s = sets[i % len(sets)]
+        if ev is not None:
+            ev[0].record(stream)
+        dg.k_grouped_fp8_gemm_nt_contiguous((s["a"], s["sa"]), (s["b"], s["sb"]), s["d"], ks, s["d"])
+        if ev is not None:
+            ev[1].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    copy_calibration(args, dev)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    avg = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        rows = 512
+        s = sets[0]
+        a = s["a"][:rows].cpu().numpy()
+        sa = s["sa"][:, :rows].t().cpu().numpy()
+        b, sb = s["b"].cpu().numpy(), s["sb"].t().cpu().numpy()
+        c = np.zeros((G, rows, N), dtype=np.float32)
+        t = time.perf_counter()
+        oracle.k_grouped(a, sa, b, sb, ks, c)
+        dt = time.perf_counter() - t
+        cpu = {"value": round(2.0 * rows * N * K / dt / 1e12, 6), "unit": "TFLOP/s", "cores": os.cpu_count(),
+               "kind": "oracle", "seconds": round(dt, 2),
+               "sample": f"rows 0..{rows - 1} of A (all {G} groups, all of B), float64 numpy"}
+    out = {
+        "metric": f"TFLOP/s, K-grouped FP8 GEMM {args.workload}",
+        "value": round(flops * args.steps / elapsed / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(elapsed * 1e3 / args.steps, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8_e4m3 (fp32 accumulate)", "data": "synthetic",
+        "config": {"workload": args.workload, "M": M, "N": N, "ks": ks, "out": "fp32, C = D in place",
+                   "scales": "fp32 1x128 on both operands", "buffer_sets": len(sets)},
+        "roofline": {"bound": "mfma", "achieved": round(flops / (avg * 1e-3) / 1e12, 2), "peak": PEAK_FP8_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(flops / (avg * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4),
+                     "traffic": read_traffic(args.workload),
+                     "kernel": f"dg::gemm_kernel, {G} launches per step (one per group)",
+                     "step_gpu_ms": round(avg, 5), "alg_bytes": alg_bytes, "alg_flops": flops},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
