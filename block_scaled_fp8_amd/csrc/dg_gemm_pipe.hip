@@ -273,6 +273,9 @@ struct Carry {
 
 template <int BM, int BN, int WM, int WN, int SFM, int OUT, int GRP, int NB>
 struct Kernel {
+  // Per-row FP32 weight scales run on the generic kernel: here the B stage that holds a
+  // block's scales is refilled before its last two partials are promoted.
+  static_assert(SFM == SF_1D2D_F32 || SFM == SF_1D1D_UE8M0, "1d2d FP32 or 1d1d UE8M0 scales only");
   using G = Geo<BM, BN, WM, WN, SFM, NB>;
   static constexpr int FM = G::FM, FN = G::FN, TM = G::TM, TN = G::TN, STEPS = G::STEPS;
   static constexpr int NW = G::NW;
@@ -288,7 +291,6 @@ struct Kernel {
   uint32_t off_s;         // scale copies: lane L copies the 4-byte entries 4L..4L+3
   uint32_t a_lo, a_hi, b_lo, b_hi;  // per-lane LDS fragment bases (stage 0)
   uint32_t sa_lds;                  // per-lane LDS address of its rows' activation scales (stage 0)
-  uint32_t sb_lds;                  // per-lane LDS address of its columns' weight scales (stage 0, 1d1d)
   uint32_t ww_lds;                  // UE8M0: per-lane LDS address of its B row's packed weight scales (stage 0)
   int ustep_a, ustep_b;             // 8 * NW * ld
   uint32_t sstep_a, sstep_b;        // bytes per K-block row of the activation / per-row weight scales
@@ -319,7 +321,6 @@ struct Kernel {
     b_lo = G::B_OFF + (wn * TN + lr) * BK + lo;
     b_hi = G::B_OFF + (wn * TN + lr) * BK + hi;
     sa_lds = G::SA_OFF + 4 * (wm * TM + lr);
-    sb_lds = G::SB_OFF + 4 * (wn * TN + 4 * lg);
     ww_lds = G::SB_OFF + 4 * (wn * TN + lr);
     if (GRP == GRP_MASKED && p.num_groups <= 64) {
       const int mg = lane < p.num_groups ? min(max(p.masked_m[lane], 0), p.m) : 0;
@@ -498,7 +499,6 @@ struct Kernel {
       if constexpr (NF == 0) return j < nf ? f0[i] : f1[i];
       else return j < NF ? f0[i] : f1[i];
     };
-    const uint32_t sbl = sb_lds + (uint32_t)(bs * G::SB_SLOT);
 
     // copies of A block g+2 go out spread over the steps before the barrier (in the first
     // block of a tile: right after the barrier, because their stage served as the previous
@@ -611,15 +611,9 @@ struct Kernel {
       // promote the partial of MFMA t-2 (for t < 2: of the previous block, with its factor)
       if constexpr (SFM != SF_1D1D_UE8M0 && t >= 2 && (t - 2) % FM < FA) {
         constexpr int tp = t - 2, jp = tp / FM, ip = tp % FM;
-        if (SFM == SF_1D1D_F32) {
-          const v4f w = *(const v4f*)(smem + sbl + 64 * jp);
+        const float sc = factor(ip, jp);
 #pragma unroll
-          for (int v = 0; v < 4; ++v) fin[ip][jp][v] = __builtin_fmaf(sa[ip] * w[v], r2[v], fin[ip][jp][v]);
-        } else {
-          const float sc = factor(ip, jp);
-#pragma unroll
-          for (int v = 0; v < 4; ++v) fin[ip][jp][v] = __builtin_fmaf(sc, r2[v], fin[ip][jp][v]);
-        }
+        for (int v = 0; v < 4; ++v) fin[ip][jp][v] = __builtin_fmaf(sc, r2[v], fin[ip][jp][v]);
         pin(fin[ip][jp]);
       } else if constexpr (t < 2 && SFM == SF_1D2D_F32 && (t - 2 + STEPS) % FM < FA) {
         constexpr int tp = t - 2 + STEPS, jp = tp / FM, ip = tp % FM;
@@ -645,26 +639,11 @@ struct Kernel {
     c.ebw = ebwn;
     c.sbw0 = sbn0;
     c.sbw1 = sbn1;
-    if (SFM == SF_1D1D_F32) {
-      // the per-column weight scales of the last two partials live in this block's B stage
-      // only: promote them now
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const int tp = STEPS - 2 + s, jp = tp / FM, ip = tp % FM;
-        const v4f w = *(const v4f*)(smem + sbl + 64 * jp);
-        const v4f a = s == 0 ? r2 : r1;
-#pragma unroll
-        for (int v = 0; v < 4; ++v) fin[ip][jp][v] = __builtin_fmaf(sa[ip] * w[v], a[v], fin[ip][jp][v]);
-      }
-      c.acc1 = zero;
-      c.acc2 = zero;
-    } else {
-      c.acc1 = SFM == SF_1D1D_UE8M0 ? zero : r1;
-      c.acc2 = SFM == SF_1D1D_UE8M0 ? zero : r2;
-      constexpr int t0 = STEPS - 2, t1 = STEPS - 1;
-      c.pscale[0] = SFM == SF_1D2D_F32 ? factor(t0 % FM, t0 / FM) : 0.f;
-      c.pscale[1] = SFM == SF_1D2D_F32 ? factor(t1 % FM, t1 / FM) : 0.f;
-    }
+    c.acc1 = SFM == SF_1D1D_UE8M0 ? zero : r1;
+    c.acc2 = SFM == SF_1D1D_UE8M0 ? zero : r2;
+    constexpr int t0 = STEPS - 2, t1 = STEPS - 1;
+    c.pscale[0] = SFM == SF_1D2D_F32 ? factor(t0 % FM, t0 / FM) : 0.f;
+    c.pscale[1] = SFM == SF_1D2D_F32 ? factor(t1 % FM, t1 / FM) : 0.f;
   }
 
   // Promote the two partials still pending (end of a tile).

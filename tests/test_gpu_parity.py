@@ -337,6 +337,31 @@ def test_per_row_weight_scales(pack):
     check_dense(q, d2, name="1d2d same data")
 
 
+@pytest.mark.parametrize("tile", ["256x224", "128x192"])
+@pytest.mark.parametrize("out", ["bf16", "f32", "f32+c"])
+def test_pipelined_per_row_fp32_weight_scales(tile, out):
+    """FP32 per-row weight scales on the pipelined tiles: every weight row has its own scale
+    per K block (so a lane that read a neighbouring column's scale would fail), ragged m and
+    n, K from the minimum two blocks up, BF16, FP32 and FP32 + C output."""
+    for M, N, K in [(300, 520, 512), (37, 200, 256)]:
+        p = gen.dense(M, N, K, seed=M + K, with_c=out == "f32+c")
+        rng = np.random.default_rng(M + N)
+        sb = rng.uniform(0.002, 0.03, (N, K // 128)).astype(np.float32)
+        say("pipelined 1d1d fp32", tile, out, M, N, K)
+        c = cuda(p["c"]) if out == "f32+c" else None
+        d = torch.full((M, N), float("nan"), dtype=torch.bfloat16 if out == "bf16" else torch.float32, device=DEV)
+        with force_tile(tile):
+            dg.fp8_gemm_nt((cuda(p["a"]), cuda(p["sa"])), (cuda(p["b"]), cuda(sb)), d, c=c, recipe=(1, 1, 128))
+        torch.cuda.synchronize()
+        o, T = oracle.gemm_nt(p["a"], p["sa"], p["b"], sb, 1, c=p["c"] if c is not None else None, want_abs=True)
+        if out == "bf16":
+            ok, st = check_bf16(bf16_bits(d), o, T)
+        else:
+            ok, st = check_fp32(d.cpu().numpy(), o, T)
+        say("pipelined 1d1d fp32", st)
+        assert ok.all(), st
+
+
 def test_deterministic_and_batch_invariant():
     p = gen.dense(1024, 768, 1024, seed=7)
     say("determinism / batch invariance")
