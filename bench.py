@@ -268,7 +268,7 @@ def bench_k_grouped(args, spec, dg, dev):
                    "scales": "fp32 1x128 on both operands", "buffer_sets": len(sets)},
         "roofline": {"bound": "mfma", "achieved": round(flops / (avg * 1e-3) / 1e12, 2), "peak": PEAK_FP8_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(flops / (avg * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4),
-                     "traffic": read_traffic(args.workload),
+                     "traffic": read_traffic(args.workload),   # per step, like alg_bytes
                      "kernel": f"dg::gemm_kernel, {G} launches per step (one per group)",
                      "step_gpu_ms": round(avg, 5), "alg_bytes": alg_bytes, "alg_flops": flops},
         "cpu_baseline": cpu,
