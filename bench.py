@@ -127,8 +127,8 @@ def main():
                          "calibrates the FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(see DESIGN.md for how the GEMM would shard).", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path (the dense GEMM "
+              "would shard along M or N with no exchange, the grouped forms by expert).", file=sys.stderr)
         sys.exit(2)
 
     import block_scaled_fp8_amd as dg
