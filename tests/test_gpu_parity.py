@@ -247,6 +247,33 @@ def test_k_grouped_contiguous(m, n, ks, alias):
         assert torch.equal(c.cpu(), torch.from_numpy(p["c"]))   # C is only read
 
 
+def test_k_grouped_full_size_sampled():
+    """The K-grouped weight-gradient workload at the size the benchmark times (m = 7168,
+    n = 2048, eight groups, K = 16384 in all), accumulated in place as the benchmark runs it,
+    checked on 1024 sampled outputs per group against the oracle evaluated point by point."""
+    ks = [1792, 2304, 2048, 1536, 2560, 2048, 1920, 2176]
+    m, n = 7168, 2048
+    p = gen.k_grouped(m, n, ks, seed=9)
+    say("k-grouped full size", m, n, ks)
+    d = cuda(p["c"])
+    dg.k_grouped_fp8_gemm_nt_contiguous((cuda(p["a"]), cuda(np.ascontiguousarray(p["sa"].T))),
+                                        (cuda(p["b"]), cuda(np.ascontiguousarray(p["sb"].T))), d, ks, d)
+    torch.cuda.synchronize()
+    got = d.cpu().numpy()
+    rng = np.random.default_rng(10)
+    k0 = 0
+    for g, k in enumerate(ks):
+        ii, jj = rng.integers(0, m, 1024), rng.integers(0, n, 1024)
+        ii[:2], jj[:2] = [0, m - 1], [0, n - 1]                       # the corners
+        kr, br = slice(k0, k0 + k), slice(k0 // 128, (k0 + k) // 128)
+        o, T = oracle.gemm_nt_points(p["a"][:, kr], p["sa"][:, br], p["b"][:, kr], p["sb"][:, br], ii, jj, 1,
+                                     c=p["c"][g])
+        ok, st = check_fp32(got[g][ii, jj], o, T)
+        say("k-grouped full size group", g, st)
+        assert ok.all(), (g, st)
+        k0 += k
+
+
 # ---------------------------------------------------------------- dense
 def test_config1_tiny_bf16():
     p = gen.config1()
