@@ -199,6 +199,29 @@ def test_cast_out_overwrites_an_earlier_result(pack):
     assert np.array_equal(sf.cpu().numpy().view(np.uint32), fresh_sf.cpu().numpy().view(np.uint32))
 
 
+@pytest.mark.parametrize("pack", [False, True])
+def test_cast_full_size_sampled_rows(pack):
+    """The cast at the size the benchmark times (4096 x 7168 BF16), in the same launch
+    configuration; rows are cast independently, so 66 sampled rows (first and last included)
+    are checked bit for bit against the oracle run on those rows."""
+    m, k = 4096, 7168
+    x = _cast_input(m, k, seed=77)
+    say("cast full size", pack)
+    xt = torch.from_numpy(x).to(DEV).to(torch.bfloat16)
+    q, sf = dg.per_token_group_cast_fp8(xt, pack_ue8m0=pack)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([[0, m - 1], np.random.default_rng(78).integers(0, m, 64)]))
+    seen = xt[torch.from_numpy(rows).to(DEV)].float().cpu().numpy()
+    qo, so = oracle.per_token_group_cast(seen, ue8m0=pack)
+    assert np.array_equal(q.cpu().numpy()[rows], qo)
+    got = sf.cpu().numpy()[rows].view(np.uint32)
+    if pack:
+        words, _ = oracle.transform_sf(so, len(rows), 1, True)
+        assert np.array_equal(got, words[:, :len(rows)].T.view(np.uint32))
+    else:
+        assert np.array_equal(got, so.view(np.uint32))
+
+
 def test_cast_ue8m0_feeds_the_gemm():
     """Packed UE8M0 output of the cast is the GEMM's activation scale operand as it stands."""
     p = gen.grouped_masked(1, 200, 384, 640, seed=43, pow2_scales=True)
