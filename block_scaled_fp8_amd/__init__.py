@@ -24,7 +24,7 @@ import torch
 __all__ = [
     "DGError", "lib", "fp8_gemm_nt", "m_grouped_fp8_gemm_nt_contiguous", "m_grouped_fp8_gemm_nt_masked",
     "transform_sf", "get_mn_major_tma_aligned_tensor", "get_mn_major_tma_aligned_packed_ue8m0_tensor",
-    "per_token_group_cast_fp8", "k_grouped_fp8_gemm_nt_contiguous", "get_tma_aligned_size", "get_mk_alignment_for_contiguous_layout", "set_num_sms", "get_num_sms",
+    "per_token_group_cast_fp8", "k_grouped_fp8_gemm_nt_contiguous", "transform_sf_into_required_layout", "get_tma_aligned_size", "get_mk_alignment_for_contiguous_layout", "set_num_sms", "get_num_sms",
     "get_gemm_config", "LIB_PATH",
 ]
 
@@ -185,6 +185,41 @@ def per_token_group_cast_fp8(x, pack_ue8m0=False, out=None):
     return q, sf
 
 
+def transform_sf_into_required_layout(sf, mn, recipe=(1, 128, 128), is_sfa=True, pack_ue8m0=False,
+                                      num_groups=None):
+    """One entry for both ways of providing scales (page "02 · DeepGEMM 技术解析" §3.2):
+    already transformed scales (MN-major FP32, or int32 packed UE8M0 words) are only checked
+    and returned; raw FP32 scales ``[(G,) mn_blocks, sf_k]`` are converted on the device.
+
+    ``recipe`` is (gran_m, gran_n, gran_k) with gran_k == 128.  The activation side
+    (``is_sfa``) is always per row.  On the weight side gran_n == 128 keeps the 128x128 block
+    scales K-major and untransformed (only the LHS scale needs the transposed layout, page
+    "第13章 DeepGEMM" §13.3), unless they are to be packed, which broadcasts them per row;
+    gran_n == 1 broadcasts raw block scales to every row (or takes per-row scales as they are).
+    """
+    gran_m, gran_n, gran_k = recipe
+    if gran_k != 128 or gran_m != 1 or gran_n not in (1, 128):
+        raise ValueError(f"unsupported recipe {recipe}")
+    if num_groups is not None and (sf.dim() != 3 or sf.shape[0] != num_groups):
+        raise ValueError(f"expected {num_groups} groups of scales, got shape {tuple(sf.shape)}")
+    if sf.dtype == torch.int32:
+        if not _is_mn_major(sf) or sf.shape[-2] != mn:
+            raise ValueError("packed UE8M0 scales must be MN-major [.., mn, ceil(sf_k / 4)]")
+        return sf
+    if sf.dtype != torch.float32:
+        raise TypeError("scales must be float32 or int32 (packed UE8M0)")
+    if _is_mn_major(sf) and sf.shape[-2] == mn and sf.shape[-2] > 1:
+        if pack_ue8m0:
+            raise ValueError("cannot pack already-transformed FP32 scales; pass them raw")
+        return sf
+    if not is_sfa and gran_n == 128 and not pack_ue8m0:
+        if sf.stride(-1) != 1 or sf.shape[-2] != (mn + 127) // 128:
+            raise ValueError("128x128 weight scales must be K-major float32 [.., ceil(mn / 128), sf_k]")
+        return sf
+    gran = 1 if is_sfa else _raw_gran(sf.shape[-2], mn)
+    return transform_sf(sf.contiguous(), mn, gran, pack_ue8m0)
+
+
 def get_mn_major_tma_aligned_tensor(sf):
     return transform_sf(sf.contiguous(), sf.shape[-2], 1, False)
 
@@ -227,14 +262,19 @@ def _weight_scales(sfb, n, sf_k, gran_n, fmt):
     if fmt == DG_SF_UE8M0X4:
         if sfb.dtype == torch.int32:
             return sfb, sfb.stride(-1)
-        gran = 128 if sfb.shape[-2] == (n + 127) // 128 and n > 128 else 1
-        t = transform_sf(sfb.contiguous(), n, gran, True)
+        t = transform_sf(sfb.contiguous(), n, _raw_gran(sfb.shape[-2], n), True)
         return t, t.stride(-1)
     if _is_mn_major(sfb):
         return sfb, sfb.stride(-1)
-    gran = 128 if sfb.shape[-2] == (n + 127) // 128 and n > 128 else 1
-    t = transform_sf(sfb.contiguous(), n, gran, False)
+    t = transform_sf(sfb.contiguous(), n, _raw_gran(sfb.shape[-2], n), False)
     return t, t.stride(-1)
+
+
+def _raw_gran(rows, n):
+    """MN granularity of raw (K-major) weight scales with ``rows`` rows for n weight rows:
+    128 when there is one row per 128-row block, else 1.  The two readings coincide only
+    for n == 1, where they give the same broadcast."""
+    return 128 if rows == (n + 127) // 128 and rows != n else 1
 
 
 def _recipe_gran_n(recipe, sfa, sfb, n, pack):

@@ -136,7 +136,8 @@ int check_common(int32_t n, int32_t k, const void* a, int64_t lda, const void* s
   if (!a || !sfa || !b || !sfb || !d) return fail(DG_ERR_NULL, "a, sfa, b, sfb and d must not be NULL");
   if (lda < k || lda % 16 != 0) return fail(DG_ERR_LAYOUT, "lda = %lld must be >= k and a multiple of 16", (long long)lda);
   if (ldb < k || ldb % 16 != 0) return fail(DG_ERR_LAYOUT, "ldb = %lld must be >= k and a multiple of 16", (long long)ldb);
-  if (lda > (int64_t(1) << 23) || ldb > (int64_t(1) << 23)) return fail(DG_ERR_LAYOUT, "lda and ldb must be <= 2^23 (tile offsets are 32-bit)");
+  // a tile's byte range (up to 256 rows of ld bytes) is a 32-bit signed count
+  if (lda >= (int64_t(1) << 23) || ldb >= (int64_t(1) << 23)) return fail(DG_ERR_LAYOUT, "lda and ldb must be < 2^23 (tile byte ranges are 32-bit)");
   if (!aligned16(a) || !aligned16(b)) return fail(DG_ERR_LAYOUT, "a and b must be 16-byte aligned");
   if (!aligned16(sfa) || !aligned16(sfb)) return fail(DG_ERR_LAYOUT, "sfa and sfb must be 16-byte aligned");
   const int64_t sf_k = k / 128;

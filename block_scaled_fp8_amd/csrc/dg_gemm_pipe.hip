@@ -386,7 +386,7 @@ struct Kernel {
     constexpr int Q0 = U * NW;
     const int q = wave + Q0;
     const int row_dst = dst + q * 1024;
-    const uint32_t row_off = off + (uint32_t)(U * ustep);
+    const uint32_t row_off = off + (uint32_t)U * (uint32_t)ustep;
     if constexpr (Q0 + NW <= ROWL) {
       copy_to_lds(src_ptr(s.lo, s.hi), s.bytes, row_off, smem, row_dst);
     } else if constexpr (Q0 >= ROWL) {

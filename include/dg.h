@@ -62,7 +62,7 @@ typedef enum { DG_IN_BF16 = 1, DG_IN_F32 = 2 } dg_in_dtype;
  *
  *  m, n, k      : problem sizes; k > 0 and k % 128 == 0; m, n >= 0.  m == 0 or n == 0 is a
  *                 no-op that reads and writes nothing (its pointers may then be NULL).
- *  a, lda       : A E4M3 [m, k], element (i, kk) at a[i*lda + kk]; k <= lda <= 2^23, lda % 16 == 0,
+ *  a, lda       : A E4M3 [m, k], element (i, kk) at a[i*lda + kk]; k <= lda < 2^23, lda % 16 == 0,
  *                 a 16-byte aligned.
  *  sfa, sfa_stride : activation scales, MN-major (the LHS scale must be transposed and
  *                 aligned, page "第13章 DeepGEMM" §13.3 constraint 1; layout page

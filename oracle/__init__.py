@@ -19,9 +19,12 @@ number whatever order it is summed in; only the scale products and the sum
 over blocks round (one float64 rounding each).
 
 Modules:
-  codecs  -- E4M3 decode, UE8M0 encode/decode, float64 -> BF16 round-to-nearest-even
+  codecs  -- E4M3 and E2M1 decode, FP4 unpacking, UE8M0 encode/decode,
+             float64 -> BF16 round-to-nearest-even
   layout  -- the scale-layout transform (MN-major, 4-aligned stride, UE8M0 x4 packing)
-  gemm    -- dense NT, M-grouped contiguous, M-grouped masked and K-grouped references
+  gemm    -- dense NT, M-grouped contiguous, M-grouped masked and K-grouped references,
+             and the FP8 x FP4 GEMM (E2M1 weights with one scale per 32 K) in the dense and
+             M-grouped forms
   quant   -- the per-token-group FP8 cast (E4M3 codes and 1x128 FP32 scales)
 
 Parity pins: every function here is pinned by a `-m "not gpu"` test in
@@ -32,8 +35,10 @@ comparison with the original CUDA library itself cannot be made here.
 """
 from . import codecs, layout, gemm, quant  # noqa: F401
 from .codecs import (e4m3_decode_table, e4m3_decode, ue8m0_encode, ue8m0_decode,
-                     bf16_rne, bf16_bits_to_f64, pow2_violation)  # noqa: F401
+                     bf16_rne, bf16_bits_to_f64, pow2_violation, e2m1_decode_table, e2m1_decode,
+                     unpack_fp4)  # noqa: F401
 from .layout import align4, transform_sf, unpack_ue8m0  # noqa: F401
 from .gemm import (gemm_nt, gemm_nt_points, grouped_contiguous, grouped_masked, k_grouped,
-                   expand_scales_b)  # noqa: F401
+                   expand_scales_b, gemm_fp8_fp4_nt, gemm_fp8_fp4_nt_points, grouped_contiguous_fp8_fp4,
+                   grouped_masked_fp8_fp4)  # noqa: F401
 from .quant import e4m3_encode_rne, per_token_group_cast  # noqa: F401

@@ -28,7 +28,7 @@ then shorter.
 """
 import numpy as np
 
-from .codecs import e4m3_decode
+from .codecs import e4m3_decode, e2m1_decode, unpack_fp4
 
 BLOCK_K = 128
 
@@ -186,4 +186,108 @@ def k_grouped(a_codes, sa, b_codes, sb, ks, c, want_abs=False):
             else:
                 D[g] = r
         k0 += k
+    return (D, T) if want_abs else D
+
+
+BLOCK_K_FP4 = 32
+
+
+def gemm_fp8_fp4_nt(a_codes, sa, b_packed, sb, c=None, want_abs=False):
+    """FP8 activations x FP4 weights, D = C + A @ B^T (page "第13章 DeepGEMM" §13.1: the V4
+    routed-expert recipe, FP8 activations and FP4 weights with one weight scale per 32 K
+    elements; §13.5: FP4 weights fed to the matrix unit together with FP8 activations, the
+    scales applied inside the MMA; page "02 · DeepGEMM 技术解析" §3.1: the scales are UE8M0
+    powers of two).
+
+    a_codes: uint8 [M, K] E4M3 codes; sa: [M, ceil(K/128)] activation scales (one per row
+    and 128-long K block).  b_packed: uint8 [N, ceil(K/2)] E2M1 codes, two per byte (low
+    nibble first); sb: [N, ceil(K/32)] weight scales (one per row and 32-long K block).
+
+        D[i, j] = C[i, j] + sum_b sa[i, b] * sum_{s in block b} sb[j, s] * P[i, j, s]
+        P[i, j, s] = sum_{k in 32-block s} dec(A[i, k]) * dec(B[j, k])
+
+    Every E4M3 x E2M1 product is a multiple of 2^-10 below 2^12 in magnitude, so each
+    32-long partial P is exact in float64 in any order.  Returns D float64 [M, N] (and T,
+    the sum of |A'_ik B'_jk| over the dequantized values, with ``want_abs``).
+    """
+    A = e4m3_decode(a_codes)
+    M, K = A.shape
+    B = e2m1_decode(unpack_fp4(b_packed, K))
+    N = B.shape[0]
+    sa = np.asarray(sa, dtype=np.float64)
+    sb = np.asarray(sb, dtype=np.float64)
+    assert sa.shape == (M, _sf_k(K))
+    n_sub = (K + BLOCK_K_FP4 - 1) // BLOCK_K_FP4
+    assert sb.shape == (N, n_sub)
+    D = np.zeros((M, N), dtype=np.float64)
+    T = np.zeros((M, N), dtype=np.float64) if want_abs else None
+    for s in range(n_sub):
+        ks = slice(s * BLOCK_K_FP4, min((s + 1) * BLOCK_K_FP4, K))
+        b = (s * BLOCK_K_FP4) // BLOCK_K
+        P = A[:, ks] @ B[:, ks].T                       # exact 32-long partial
+        S = sa[:, b][:, None] * sb[:, s][None, :]       # exact scale product
+        D += S * P
+        if want_abs:
+            T += np.abs(S) * (np.abs(A[:, ks]) @ np.abs(B[:, ks]).T)
+    if c is not None:
+        D = np.asarray(c, dtype=np.float64) + D
+    return (D, T) if want_abs else D
+
+
+def gemm_fp8_fp4_nt_points(a_codes, sa, b_packed, sb, ii, jj, c=None):
+    """gemm_fp8_fp4_nt evaluated only at output positions (ii[p], jj[p]); returns (D, T)."""
+    ii = np.asarray(ii, dtype=np.int64)
+    jj = np.asarray(jj, dtype=np.int64)
+    K = a_codes.shape[1]
+    n_sub = (K + BLOCK_K_FP4 - 1) // BLOCK_K_FP4
+    Kp = n_sub * BLOCK_K_FP4
+    prod = np.zeros((len(ii), Kp), dtype=np.float64)
+    prod[:, :K] = e4m3_decode(a_codes[ii]) * e2m1_decode(unpack_fp4(b_packed[jj], K))
+    blk = prod.reshape(len(ii), n_sub, BLOCK_K_FP4)
+    P, Pabs = blk.sum(axis=2), np.abs(blk).sum(axis=2)
+    sa = np.asarray(sa, dtype=np.float64)[ii]
+    S = sa[:, np.arange(n_sub) * BLOCK_K_FP4 // BLOCK_K] * np.asarray(sb, dtype=np.float64)[jj]
+    D = (S * P).sum(axis=1)
+    T = (np.abs(S) * Pabs).sum(axis=1)
+    if c is not None:
+        D = np.asarray(c, dtype=np.float64)[ii, jj] + D
+    return D, T
+
+
+def grouped_contiguous_fp8_fp4(a_codes, sa, b_packed, sb, grouped_layout, want_abs=False):
+    """M-grouped contiguous FP8 x FP4 (page "第13章 DeepGEMM" §13.6: only M is grouped):
+    row i uses group g = grouped_layout[i] >= 0, i.e. B[g] and sb[g]; negative rows produce no
+    output (NaN).  b_packed [G, N, ceil(K/2)], sb [G, N, ceil(K/32)]."""
+    gl = np.asarray(grouped_layout)
+    G, N, _ = b_packed.shape
+    D = np.full((a_codes.shape[0], N), np.nan)
+    T = np.full_like(D, np.nan) if want_abs else None
+    for g in range(G):                      # the per-expert loop
+        idx = np.nonzero(gl == g)[0]
+        if len(idx) == 0:
+            continue
+        r = gemm_fp8_fp4_nt(a_codes[idx], np.asarray(sa)[idx], b_packed[g], sb[g], want_abs=want_abs)
+        if want_abs:
+            D[idx], T[idx] = r
+        else:
+            D[idx] = r
+    return (D, T) if want_abs else D
+
+
+def grouped_masked_fp8_fp4(a_codes, sa, b_packed, sb, masked_m, want_abs=False):
+    """M-grouped masked FP8 x FP4 (page "02 · DeepGEMM 技术解析" §5.2): A [G, M_max, K];
+    rows i < clamp(masked_m[g], 0, M_max) of each group are computed, the others are NaN."""
+    G, Mmax, _ = a_codes.shape
+    N = b_packed.shape[1]
+    D = np.full((G, Mmax, N), np.nan)
+    T = np.full_like(D, np.nan) if want_abs else None
+    for g in range(G):
+        m = int(min(max(int(masked_m[g]), 0), Mmax))
+        if m == 0:
+            continue
+        r = gemm_fp8_fp4_nt(a_codes[g, :m], np.asarray(sa)[g, :m], b_packed[g], sb[g], want_abs=want_abs)
+        if want_abs:
+            D[g, :m], T[g, :m] = r
+        else:
+            D[g, :m] = r
     return (D, T) if want_abs else D

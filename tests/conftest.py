@@ -21,3 +21,17 @@ def pytest_collection_modifyitems(config, items):
     for it in items:
         if "gpu" in it.keywords:
             it.add_marker(skip)
+
+
+def pytest_terminal_summary(terminalreporter, exitstatus, config):
+    """One line of error statistics per parity check that recorded them (full-size workloads,
+    the precision measurement), so they appear in the run's tail."""
+    try:
+        from tests.tolerance import summary_lines
+    except Exception:
+        return
+    lines = summary_lines()
+    if lines:
+        terminalreporter.write_sep("-", "parity statistics")
+        for line in lines:
+            terminalreporter.write_line(line)

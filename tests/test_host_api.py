@@ -86,6 +86,8 @@ def _dense(**kw):
     (dict(d=None), DG_ERR_NULL),
     (dict(lda=200), DG_ERR_LAYOUT),
     (dict(lda=264), DG_ERR_LAYOUT),
+    (dict(lda=1 << 23), DG_ERR_LAYOUT),                       # 256 rows of it overflow a 32-bit range
+    (dict(ldb=1 << 23), DG_ERR_LAYOUT),
     (dict(a=P_MIS), DG_ERR_LAYOUT),
     (dict(sfa_stride=65), DG_ERR_LAYOUT),
     (dict(sfb_stride=1), DG_ERR_LAYOUT),
@@ -205,3 +207,14 @@ def test_k_grouped_validation():
     assert lib.dg_k_grouped_fp8_gemm_nt_contiguous(2, 8, 8, ks(128, 128), P, 128, P, P, 256, P, P, P, None) == DG_ERR_LAYOUT  # lda < sum
     assert lib.dg_k_grouped_fp8_gemm_nt_contiguous(1, 8, 8, ks(128), P_MIS, 128, P, P, 128, P, P, P, None) == DG_ERR_LAYOUT
     assert lib.dg_k_grouped_fp8_gemm_nt_contiguous(1, 0, 8, ks(128), None, 0, None, None, 0, None, None, None, None) == DG_OK
+
+
+def test_raw_weight_scale_granularity():
+    """Raw K-major weight scales: one row per 128-row block means 128x128 block scales, also
+    when n <= 128 (a single block row); one row per weight row means per-row scales."""
+    assert dg._raw_gran(1, 100) == 128
+    assert dg._raw_gran(1, 128) == 128
+    assert dg._raw_gran(2, 200) == 128
+    assert dg._raw_gran(100, 100) == 1
+    assert dg._raw_gran(200, 200) == 1
+    assert dg._raw_gran(1, 1) == 1          # one row either way: the broadcast is the same

@@ -60,7 +60,9 @@ def test_ue8m0_examples(fixture):
 
 def test_ue8m0_special_codes():
     assert np.isnan(codecs.ue8m0_decode(np.array([255], np.uint8))[0])
-    assert codecs.ue8m0_decode(np.array([0], np.uint8))[0] == 0.0
+    # the format is a bare exponent: code 0 is the smallest power of two, not zero
+    assert codecs.ue8m0_decode(np.array([0], np.uint8))[0] == 2.0 ** -127
+    assert codecs.ue8m0_decode(np.array([1], np.uint8))[0] == 2.0 ** -126
     # every code 1..254 decodes to 2^(code - 127)
     c = np.arange(1, 255, dtype=np.uint8)
     assert (codecs.ue8m0_decode(c) == np.ldexp(1.0, c.astype(np.int32) - 127)).all()
@@ -326,6 +328,36 @@ def test_tolerance_catches_planted_mistakes():
     bits = oracle.bf16_rne(D)
     assert check_bf16(bits, D, T)[0].all()
     assert not check_bf16(np.roll(bits, 1, axis=0), D, T)[0].all()
+
+
+def test_tolerance_gates_are_tight():
+    """The gates sit at the measured FP8-MFMA ceiling, not far above it: an FP32 error of
+    2^-12 * T passes, 2^-11 * T fails; a BF16 result two or three ulps off where |o| is not
+    small next to T fails; so does a flood of elements that pass only as cancellations."""
+    from tests.tolerance import bf16_ordered, CANCEL_RATIO
+    d = gen.dense(64, 256, 512, seed=13)
+    D, T = gemm.gemm_nt(d["a"], d["sa"], d["b"], d["sb"], 128, want_abs=True)
+    sign = np.where(D >= 0, 1.0, -1.0)
+    assert check_fp32(D + sign * 2.0 ** -12 * T, D, T)[0].all()
+    ok, st = check_fp32(D + sign * 2.0 ** -11 * T, D, T)
+    assert not ok.any() and st["within_1e5"] == 0.0
+    bits = oracle.bf16_rne(D)
+    big = np.abs(D) > CANCEL_RATIO * T
+    assert big.mean() > 0.5
+    for k in (2, 3):
+        moved = (bf16_ordered(bits) + k).astype(np.int64)
+        # back from the ordered image to bit patterns (moving away from zero keeps the sign)
+        shifted = np.where(moved < 0, ((-moved) | 0x8000), moved).astype(np.uint16)
+        ok, _ = check_bf16(shifted, D, T)
+        assert not ok[big & (D > 0)].any(), k
+    # elements that pass only as cancellations: within the cap they pass, above it they fail
+    tiny = np.zeros_like(D)
+    Tc = np.full_like(D, 1.0)
+    off = oracle.bf16_rne(np.full_like(D, 2.0 ** -14))     # |d - o| = 2^-14 <= EPS_MMA * T
+    ok, st = check_bf16(off, tiny, Tc)
+    assert st["cancellation_only"] == D.size and not ok.any()
+    ok, st = check_bf16(np.where(np.arange(D.size).reshape(D.shape) == 0, off, oracle.bf16_rne(tiny)), tiny, Tc)
+    assert st["cancellation_only"] == 1 and ok.all()
 
 
 # ---------------------------------------------------------------- the per-token-group cast
