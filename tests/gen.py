@@ -189,3 +189,92 @@ def k_grouped(m, n, ks, seed=0):
     b, sb = quantize_act(xb) if K else (np.zeros((n, 0), np.uint8), np.zeros((n, 0), np.float32))
     c = rng.standard_normal((len(ks), m, n), dtype=np.float32)
     return dict(a=a, sa=sa, b=b, sb=sb, c=c, ks=list(ks), m=m, n=n)
+
+
+# ---------------------------------------------------------------- FP8 activations x FP4 weights
+E2M1_MAX = 6.0
+_E2M1_POS = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+def e2m1_codes(x):
+    """float array -> E2M1 codes (uint8, 0..15): nearest of the eight magnitudes (ties to the
+    even code, i.e. the even mantissa), clamped to +-6, sign in bit 3 (zero is +0)."""
+    x = np.asarray(x, dtype=np.float64)
+    ax = np.minimum(np.abs(x), E2M1_MAX)
+    hi = np.clip(np.searchsorted(_E2M1_POS, ax), 1, 7)
+    lo = hi - 1
+    dlo, dhi = ax - _E2M1_POS[lo], _E2M1_POS[hi] - ax
+    pick = np.where(dlo < dhi, lo, np.where(dhi < dlo, hi, np.where(lo % 2 == 0, lo, hi)))
+    sign = ((x < 0) & (pick > 0)).astype(np.uint8) << np.uint8(3)
+    return (pick.astype(np.uint8) | sign)
+
+
+def pack_fp4(codes):
+    """codes [..., K] (K even) -> bytes [..., K/2], element 2t in the low nibble of byte t."""
+    c = np.asarray(codes, dtype=np.uint8)
+    return (c[..., 0::2] | (c[..., 1::2] << np.uint8(4))).astype(np.uint8)
+
+
+def pow2_ceil_scale(amax, qmax):
+    """Power-of-two scale for a group: the FP32 amax / qmax raised to the next power of two
+    (1 for an all-zero group), so every quotient stays within +-qmax (a UE8M0 scale)."""
+    s = (np.asarray(amax, dtype=np.float32) / np.float32(qmax)).astype(np.float32)
+    m, e = np.frexp(s.astype(np.float64))
+    p = np.where(m == 0.5, s, np.ldexp(1.0, e)).astype(np.float32)
+    return np.where(s == 0, np.float32(1.0), p).astype(np.float32)
+
+
+def quantize_act_pow2(x):
+    """Activations [M, K] -> (E4M3 codes, power-of-two scales [M, K/128]), 1x128 groups."""
+    x = np.asarray(x, dtype=np.float32)
+    M, K = x.shape
+    g = x.reshape(M, K // BLOCK, BLOCK)
+    s = pow2_ceil_scale(np.abs(g).max(axis=2), E4M3_MAX)
+    return e4m3_codes((g / s[:, :, None]).reshape(M, K)), s
+
+
+def quantize_weight_fp4(x):
+    """Weights [N, K] -> (packed E2M1 bytes [N, K/2], power-of-two scales [N, K/32]), one
+    scale per row and 32-long K group (the V4 routed-expert weight recipe)."""
+    x = np.asarray(x, dtype=np.float32)
+    N, K = x.shape
+    g = x.reshape(N, K // 32, 32)
+    s = pow2_ceil_scale(np.abs(g).max(axis=2), E2M1_MAX)
+    return pack_fp4(e2m1_codes((g / s[:, :, None]).reshape(N, K))), s
+
+
+def fp8_fp4(M, N, K, seed=0, b_std=0.02, with_c=False):
+    """Dense FP8 x FP4 problem: A ~ N(0,1) with 0.1% x50 outliers (E4M3, 1x128 power-of-two
+    scales), B ~ N(0, b_std) (E2M1, 1x32 power-of-two scales), optional C ~ N(0,1)."""
+    rng = np.random.default_rng(seed)
+    xa = _act_values(rng, M, K, True)
+    xb = rng.standard_normal((N, K), dtype=np.float32) * np.float32(b_std)
+    c = rng.standard_normal((M, N), dtype=np.float32) if with_c else None
+    a, sa = quantize_act_pow2(xa)
+    b, sb = quantize_weight_fp4(xb)
+    return dict(a=a, sa=sa, b=b, sb=sb, c=c, M=M, N=N, K=K)
+
+
+def fp8_fp4_grouped_contiguous(G, N, K, seed=0, m_units=(1, 8), unit=BLOCK):
+    rng = np.random.default_rng(seed)
+    sizes = rng.integers(m_units[0], m_units[1] + 1, size=G) * unit
+    Mt = int(sizes.sum())
+    a, sa = quantize_act_pow2(_act_values(rng, Mt, K, True))
+    b = np.empty((G, N, K // 2), dtype=np.uint8)
+    sb = np.empty((G, N, K // 32), dtype=np.float32)
+    for g in range(G):
+        b[g], sb[g] = quantize_weight_fp4(rng.standard_normal((N, K), dtype=np.float32) * np.float32(0.02))
+    layout = np.repeat(np.arange(G, dtype=np.int32), sizes)
+    return dict(a=a, sa=sa, b=b, sb=sb, layout=layout, sizes=sizes, G=G, N=N, K=K, M=Mt)
+
+
+def fp8_fp4_grouped_masked(G, M_max, N, K, seed=0):
+    rng = np.random.default_rng(seed)
+    a, sa = quantize_act_pow2(_act_values(rng, G * M_max, K, True))
+    b = np.empty((G, N, K // 2), dtype=np.uint8)
+    sb = np.empty((G, N, K // 32), dtype=np.float32)
+    for g in range(G):
+        b[g], sb[g] = quantize_weight_fp4(rng.standard_normal((N, K), dtype=np.float32) * np.float32(0.02))
+    masked_m = rng.integers(0, M_max + 1, size=G).astype(np.int32)
+    return dict(a=a.reshape(G, M_max, K), sa=sa.reshape(G, M_max, K // BLOCK), b=b, sb=sb, masked_m=masked_m,
+                G=G, M_max=M_max, N=N, K=K)

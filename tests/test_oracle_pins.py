@@ -489,3 +489,136 @@ def test_k_grouped_single_group_is_the_dense_product():
     halves = oracle.k_grouped(a, sa, b, sb, [256, 256], z)
     whole = oracle.k_grouped(a, sa, b, sb, [K], z[:1])[0]
     assert np.allclose(halves[0] + halves[1], whole, rtol=1e-13, atol=1e-13)
+
+
+# ---------------------------------------------------------------- FP8 activations x FP4 weights
+def test_e2m1_hand_values():
+    """The sixteen E2M1 (OCP MX FP4) values: 1 sign, 2 exponent (bias 1), 1 mantissa bit."""
+    want = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0, -0.0, -0.5, -1.0, -1.5, -2.0, -3.0, -4.0, -6.0]
+    t = codecs.e2m1_decode_table()
+    assert t.tolist() == want
+    assert np.signbit(t[8]) and not np.signbit(t[0])
+    # every E2M1 value is exactly an E4M3 value (so FP4 weights widen to FP8 losslessly)
+    e4 = codecs.e4m3_decode_table()
+    assert all(v in e4 for v in want)
+
+
+def test_unpack_fp4_hand_example():
+    # byte 0x21: element 0 = low nibble 1 (0.5), element 1 = high nibble 2 (1.0);
+    # byte 0xF7: element 2 = 7 (6.0), element 3 = 15 (-6.0); an odd K drops the last nibble
+    codes = codecs.unpack_fp4(np.array([[0x21, 0xF7]], np.uint8), 4)
+    assert codes.tolist() == [[1, 2, 7, 15]]
+    assert codecs.e2m1_decode(codes).tolist() == [[0.5, 1.0, 6.0, -6.0]]
+    assert codecs.unpack_fp4(np.array([[0x21, 0xF7]], np.uint8), 3).tolist() == [[1, 2, 7]]
+
+
+def test_fp4_generator_encoder_is_nearest_ties_to_even():
+    """The test generator's E2M1 encoder (the upstream quantizer, not the oracle): nearest
+    value, ties to the even code, on every midpoint and on random values."""
+    pos = codecs.e2m1_decode_table()[:8]
+    mids = (pos[1:] + pos[:-1]) / 2
+    got = gen.e2m1_codes(mids)
+    # at a midpoint the two neighbours are codes i and i+1: the even one wins
+    assert got.tolist() == [i if i % 2 == 0 else i + 1 for i in range(7)]
+    x = np.random.default_rng(0).uniform(-7, 7, 10000)
+    c = gen.e2m1_codes(x)
+    d = np.abs(codecs.e2m1_decode(c) - np.clip(x, -6, 6))
+    best = np.min(np.abs(np.concatenate([pos, -pos])[None, :] - np.clip(x, -6, 6)[:, None]), axis=1)
+    assert np.array_equal(d, best)
+
+
+def _fp8_fp4_brute(a, sa, b_packed, sb, K):
+    t8 = [Fraction(v) if np.isfinite(v) else None for v in codecs.e4m3_decode_table()]
+    t4 = [Fraction(v) for v in codecs.e2m1_decode_table()]
+    codes = codecs.unpack_fp4(b_packed, K)
+    M, N = a.shape[0], codes.shape[0]
+    out = np.empty((M, N))
+    for i in range(M):
+        for j in range(N):
+            acc = Fraction(0)
+            for k in range(K):
+                acc += Fraction(float(sa[i, k // 128])) * Fraction(float(sb[j, k // 32])) * t8[a[i, k]] * t4[codes[j, k]]
+            out[i, j] = float(acc)
+    return out
+
+
+@pytest.mark.parametrize("K", [128, 256])
+def test_fp8_fp4_gemm_vs_brute_force(K):
+    """Exact rationals on tiny inputs: every E4M3 code (subnormals, +-448 included), every
+    E2M1 code, power-of-two and arbitrary FP32 scales."""
+    rng = np.random.default_rng(K)
+    M, N = 5, 6
+    a = rng.choice(np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8), (M, K))
+    a[0, :4] = [0x7E, 0xFE, 0x01, 0x81]
+    codes = rng.integers(0, 16, (N, K)).astype(np.uint8)
+    b = gen.pack_fp4(codes)
+    sa = rng.uniform(0.01, 2.0, (M, K // 128)).astype(np.float32)
+    sb = np.exp2(rng.integers(-6, 3, (N, K // 32))).astype(np.float32)
+    sb[1] = rng.uniform(0.01, 2.0, K // 32).astype(np.float32)
+    D = gemm.gemm_fp8_fp4_nt(a, sa, b, sb)
+    want = _fp8_fp4_brute(a, sa, b, sb, K)
+    assert np.allclose(D, want, rtol=2.0 ** -48, atol=0)
+
+
+def test_fp8_fp4_reduces_to_the_fp8_gemm():
+    """With the four 32-long weight scales of every 128-long block equal, the FP8 x FP4 GEMM is
+    the FP8 GEMM of the same values (E2M1 values are E4M3 values) with per-row weight scales:
+    bitwise equal with power-of-two scales, where every step is exact."""
+    p = gen.fp8_fp4(40, 72, 512, seed=3)
+    sb128 = p["sb"].reshape(72, 4, 4)[:, :, 0]                      # one scale per 128 block
+    sb = np.repeat(sb128, 4, axis=1)
+    D4 = gemm.gemm_fp8_fp4_nt(p["a"], p["sa"], p["b"], sb)
+    vals = codecs.e2m1_decode(codecs.unpack_fp4(p["b"], 512))
+    e4 = codecs.e4m3_decode_table()
+    lut = {float(v): c for c, v in enumerate(e4) if not np.isnan(v) and (c != 0x80)}
+    b8 = np.vectorize(lambda v: lut[float(v)])(vals).astype(np.uint8)
+    D8 = gemm.gemm_nt(p["a"], p["sa"], b8, sb128, 1)
+    assert np.array_equal(D4, D8)
+
+
+def test_fp8_fp4_sub_block_scale_linearity():
+    """Doubling the weight scale of one 32-long block of one row adds exactly that block's
+    contribution to that output column, and changes nothing else."""
+    p = gen.fp8_fp4(16, 24, 256, seed=5)
+    D = gemm.gemm_fp8_fp4_nt(p["a"], p["sa"], p["b"], p["sb"])
+    sb2 = p["sb"].copy()
+    sb2[7, 5] *= 2
+    D2 = gemm.gemm_fp8_fp4_nt(p["a"], p["sa"], p["b"], sb2)
+    A = codecs.e4m3_decode(p["a"])
+    B = codecs.e2m1_decode(codecs.unpack_fp4(p["b"], 256))
+    contrib = p["sa"][:, 1].astype(np.float64) * float(p["sb"][7, 5]) * (A[:, 160:192] @ B[7, 160:192])
+    assert np.array_equal(D2[:, 7] - D[:, 7], contrib)
+    assert np.array_equal(np.delete(D2, 7, axis=1), np.delete(D, 7, axis=1))
+
+
+def test_fp8_fp4_dequantize_then_matmul():
+    """The dequantize-then-matmul formulation (page "LinearQaunt-分块量化矩阵乘法"), with the
+    weight scale expanded per 32 along K: agrees to float64 rounding."""
+    p = gen.fp8_fp4(33, 50, 384, seed=6, with_c=True)
+    A = codecs.e4m3_decode(p["a"]) * np.repeat(p["sa"].astype(np.float64), 128, axis=1)
+    B = codecs.e2m1_decode(codecs.unpack_fp4(p["b"], 384)) * np.repeat(p["sb"].astype(np.float64), 32, axis=1)
+    D = gemm.gemm_fp8_fp4_nt(p["a"], p["sa"], p["b"], p["sb"], c=p["c"])
+    assert np.allclose(D, p["c"] + A @ B.T, rtol=1e-13, atol=1e-13)
+
+
+def test_fp8_fp4_points_and_grouped_forms():
+    """The point evaluator equals the full product; the grouped forms equal per-group dense
+    products on their rows."""
+    p = gen.fp8_fp4(30, 40, 256, seed=7, with_c=True)
+    D, T = gemm.gemm_fp8_fp4_nt(p["a"], p["sa"], p["b"], p["sb"], c=p["c"], want_abs=True)
+    ii, jj = np.array([0, 29, 5, 17]), np.array([0, 39, 22, 3])
+    Dp, Tp = gemm.gemm_fp8_fp4_nt_points(p["a"], p["sa"], p["b"], p["sb"], ii, jj, c=p["c"])
+    assert np.allclose(Dp, D[ii, jj], rtol=1e-14) and np.allclose(Tp, T[ii, jj], rtol=1e-14)
+    q = gen.fp8_fp4_grouped_contiguous(3, 20, 256, seed=8, m_units=(1, 1), unit=8)
+    lay = q["layout"].copy()
+    lay[3] = -1
+    Dc = gemm.grouped_contiguous_fp8_fp4(q["a"], q["sa"], q["b"], q["sb"], lay)
+    assert np.isnan(Dc[3]).all()
+    for g in range(3):
+        rows = np.nonzero(lay == g)[0]
+        assert np.array_equal(Dc[rows], gemm.gemm_fp8_fp4_nt(q["a"][rows], q["sa"][rows], q["b"][g], q["sb"][g]))
+    r = gen.fp8_fp4_grouped_masked(3, 10, 20, 256, seed=9)
+    mm = np.array([0, 10, 4], np.int32)
+    Dm = gemm.grouped_masked_fp8_fp4(r["a"], r["sa"], r["b"], r["sb"], mm)
+    assert np.isnan(Dm[0]).all() and np.isnan(Dm[2, 4:]).all()
+    assert np.array_equal(Dm[2, :4], gemm.gemm_fp8_fp4_nt(r["a"][2, :4], r["sa"][2, :4], r["b"][2], r["sb"][2]))
