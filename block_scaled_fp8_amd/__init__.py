@@ -24,7 +24,8 @@ import torch
 __all__ = [
     "DGError", "lib", "fp8_gemm_nt", "m_grouped_fp8_gemm_nt_contiguous", "m_grouped_fp8_gemm_nt_masked",
     "transform_sf", "get_mn_major_tma_aligned_tensor", "get_mn_major_tma_aligned_packed_ue8m0_tensor",
-    "per_token_group_cast_fp8", "k_grouped_fp8_gemm_nt_contiguous", "transform_sf_into_required_layout", "get_tma_aligned_size", "get_mk_alignment_for_contiguous_layout", "set_num_sms", "get_num_sms",
+    "per_token_group_cast_fp8", "k_grouped_fp8_gemm_nt_contiguous", "transform_sf_into_required_layout",
+    "fp8_fp4_gemm_nt", "m_grouped_fp8_fp4_gemm_nt_contiguous", "m_grouped_fp8_fp4_gemm_nt_masked", "get_tma_aligned_size", "get_mk_alignment_for_contiguous_layout", "set_num_sms", "get_num_sms",
     "get_gemm_config", "LIB_PATH",
 ]
 
@@ -42,6 +43,12 @@ _SIGS = {
                                                    _p, _i64, _i64, _i32, _i32, _p, _i64, _i32, _p, _p]),
     "dg_m_grouped_fp8_gemm_nt_masked": (_i32, [_i32, _i32, _i32, _i32, _p, _i64, _i64, _p, _i64, _i64, _p, _i64,
                                                _i64, _p, _i64, _i64, _i32, _i32, _p, _i64, _i64, _i32, _p, _i32, _p]),
+    "dg_fp8_fp4_gemm_nt": (_i32, [_i32, _i32, _i32, _p, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _i64,
+                                  _i32, _p]),
+    "dg_m_grouped_fp8_fp4_gemm_nt_contiguous": (_i32, [_i32, _i32, _i32, _i32, _p, _i64, _p, _i64, _p, _i64, _i64,
+                                                       _p, _i64, _i64, _p, _i64, _i32, _p, _p]),
+    "dg_m_grouped_fp8_fp4_gemm_nt_masked": (_i32, [_i32, _i32, _i32, _i32, _p, _i64, _i64, _p, _i64, _i64, _p, _i64,
+                                                   _i64, _p, _i64, _i64, _p, _i64, _i64, _i32, _p, _i32, _p]),
     "dg_transform_sf": (_i32, [_p, _i32, _i32, _i32, _i32, _i32, _p, _p, _p]),
     "dg_k_grouped_fp8_gemm_nt_contiguous": (_i32, [_i32, _i32, _i32, _p, _p, _i64, _p, _p, _i64, _p, _p, _p, _p]),
     "dg_per_token_group_cast_fp8": (_i32, [_i32, _i32, _p, _i64, _i32, _p, _i64, _p, _i64, _i32, _p]),
@@ -378,5 +385,99 @@ def m_grouped_fp8_gemm_nt_masked(a, b, d, masked_m, expected_m=0, recipe=None, p
     _check(lib().dg_m_grouped_fp8_gemm_nt_masked(
         G, Mmax, N, K, _ptr(A), A.stride(1), A.stride(0), _ptr(sfa_t), sfa_t.stride(-1), sfa_t.stride(0),
         _ptr(B), B.stride(1), B.stride(0), _ptr(sfb_t), sfb_stride, sfb_t.stride(0), fmt, gran_n,
+        _ptr(d), d.stride(1), d.stride(0), _out_dtype(d), _ptr(masked_m), int(expected_m), _stream(d)))
+    return d
+
+
+# ---------------------------------------------------------------- FP8 activations x FP4 weights
+def _fp4_codes(t, k):
+    """Packed E2M1 weights: uint8 (or float4_e2m1fn_x2) [.., n, k // 2], K-contiguous."""
+    if t.dtype != torch.uint8 and str(t.dtype) != "torch.float4_e2m1fn_x2":
+        raise TypeError(f"FP4 weights must be uint8 bytes or float4_e2m1fn_x2 (two codes per byte), got {t.dtype}")
+    if t.stride(-1) != 1 or t.shape[-1] != k // 2:
+        raise ValueError(f"FP4 weights must be K-contiguous [.., n, k // 2] = [.., n, {k // 2}]")
+    return t
+
+
+def _fp4_act_scales(sfa, m):
+    """Activation scales of the FP8 x FP4 GEMM: packed UE8M0 words (MN-major), or raw FP32
+    power-of-two scales [.., m, k // 128] which the transform packs."""
+    if sfa.dtype == torch.int32:
+        if not _is_mn_major(sfa):
+            raise ValueError("packed UE8M0 scales must be MN-major")
+        return sfa
+    if sfa.dtype != torch.float32:
+        raise TypeError("scales must be float32 (powers of two) or int32 (packed UE8M0)")
+    return transform_sf(sfa.contiguous(), m, 1, True)
+
+
+def _fp4_weight_scales(sfb, n, k):
+    """Weight scales of FP4 weights, one per row and 32 K: int32 words [.., n, k // 128]
+    (MN-major, stride align4(n)), or raw FP32 [.., n, k // 32] which the transform packs
+    four 32-K codes per word."""
+    if sfb.dtype == torch.int32:
+        if not _is_mn_major(sfb) or sfb.shape[-1] != k // 128:
+            raise ValueError("packed FP4 weight scales must be MN-major int32 [.., n, k // 128]")
+        return sfb
+    if sfb.dtype != torch.float32 or sfb.shape[-1] != k // 32 or sfb.shape[-2] != n:
+        raise ValueError(f"raw FP4 weight scales must be float32 [.., {n}, {k // 32}]")
+    return transform_sf(sfb.contiguous(), n, 1, True)
+
+
+def fp8_fp4_gemm_nt(a, b, d, c=None):
+    """D = C + A @ B.T with FP8 activations and FP4 weights.  ``a = (A [M, K] E4M3, sfa)``,
+    sfa one power-of-two scale per row and 128 K; ``b = (B [N, K // 2] packed E2M1, sfb)``,
+    sfb one power-of-two scale per row and 32 K; ``d`` [M, N] BF16 or FP32; ``c`` optional FP32."""
+    A, sfa = a
+    B, sfb = b
+    _codes(A)
+    M, K = A.shape
+    _fp4_codes(B, K)
+    N = B.shape[0]
+    sfa_t = _fp4_act_scales(sfa, M)
+    sfb_t = _fp4_weight_scales(sfb, N, K)
+    _check(lib().dg_fp8_fp4_gemm_nt(M, N, K, _ptr(A), A.stride(0), _ptr(sfa_t), sfa_t.stride(-1) if M > 0 else 0,
+                                    _ptr(B), B.stride(0), _ptr(sfb_t), sfb_t.stride(-1) if N > 0 else 0,
+                                    _ptr(c), c.stride(0) if c is not None else 0,
+                                    _ptr(d), d.stride(0), _out_dtype(d), _stream(d)))
+    return d
+
+
+def m_grouped_fp8_fp4_gemm_nt_contiguous(a, b, d, grouped_layout):
+    """Rows of A [sum M_g, K] grouped by ``grouped_layout``; ``b = (B [G, N, K // 2] packed E2M1,
+    sfb [G, N, ..])``; D [sum M_g, N] BF16."""
+    A, sfa = a
+    B, sfb = b
+    _codes(A)
+    M, K = A.shape
+    _fp4_codes(B, K)
+    G, N, _ = B.shape
+    sfa_t = _fp4_act_scales(sfa, M)
+    sfb_t = _fp4_weight_scales(sfb, N, K)
+    if grouped_layout.dtype != torch.int32 or not grouped_layout.is_contiguous():
+        raise ValueError("grouped_layout must be contiguous int32")
+    _check(lib().dg_m_grouped_fp8_fp4_gemm_nt_contiguous(
+        M, N, K, G, _ptr(A), A.stride(0), _ptr(sfa_t), sfa_t.stride(-1), _ptr(B), B.stride(1), B.stride(0),
+        _ptr(sfb_t), sfb_t.stride(-1), sfb_t.stride(0), _ptr(d), d.stride(0), _out_dtype(d),
+        _ptr(grouped_layout), _stream(d)))
+    return d
+
+
+def m_grouped_fp8_fp4_gemm_nt_masked(a, b, d, masked_m, expected_m=0):
+    """A [G, M_max, K] with ``masked_m`` valid rows per group; ``b = (B [G, N, K // 2] packed E2M1,
+    sfb [G, N, ..])``; D [G, M_max, N] BF16 (rows past masked_m untouched)."""
+    A, sfa = a
+    B, sfb = b
+    _codes(A)
+    G, Mmax, K = A.shape
+    _fp4_codes(B, K)
+    N = B.shape[1]
+    sfa_t = _fp4_act_scales(sfa, Mmax)
+    sfb_t = _fp4_weight_scales(sfb, N, K)
+    if masked_m.dtype != torch.int32 or not masked_m.is_contiguous():
+        raise ValueError("masked_m must be contiguous int32")
+    _check(lib().dg_m_grouped_fp8_fp4_gemm_nt_masked(
+        G, Mmax, N, K, _ptr(A), A.stride(1), A.stride(0), _ptr(sfa_t), sfa_t.stride(-1), sfa_t.stride(0),
+        _ptr(B), B.stride(1), B.stride(0), _ptr(sfb_t), sfb_t.stride(-1), sfb_t.stride(0),
         _ptr(d), d.stride(1), d.stride(0), _out_dtype(d), _ptr(masked_m), int(expected_m), _stream(d)))
     return d

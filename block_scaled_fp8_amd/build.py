@@ -1,8 +1,9 @@
 """Build libdg.so (the gfx950 HIP kernels and the C ABI) in-tree with hipcc.
 
 Usage: ``python -m block_scaled_fp8_amd.build`` or ``build()`` from Python.
-The GEMM kernel file is compiled once per tile shape (``-DDG_TILE_ID=i``) so the
-template instantiations build in parallel, then everything is linked into
+The generic GEMM kernel file is compiled once per tile shape (``-DDG_TILE_ID=i``)
+and the pipelined one once per part (``-DDG_PIPE_PART=i``) so the template
+instantiations build in parallel, then everything is linked into
 ``block_scaled_fp8_amd/libdg.so``.
 """
 import os
@@ -15,6 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libdg.so")
 NUM_TILES = 9
+PIPE_PARTS = 4   # dg_gemm_pipe.hip: dense, contiguous, masked, FP4 weights
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -45,8 +47,11 @@ def build(verbose=False, jobs=None):
     # MFMA results in VGPRs: the block partials feed VALU promotion FMAs directly instead of
     # being copied out of accumulation registers (matters for the 4-wave tiles, whose
     # operands spill into AGPRs)
-    steps.append([HIPCC, *FLAGS, "-mllvm", "-amdgpu-mfma-vgpr-form", "-c", os.path.join(CSRC, "dg_gemm_pipe.hip"),
-                  "-o", os.path.join(bdir, "dg_gemm_pipe.o")])
+    for part in range(PIPE_PARTS):
+        steps.append([HIPCC, *FLAGS, "-mllvm", "-amdgpu-mfma-vgpr-form", f"-DDG_PIPE_PART={part}", "-c",
+                      os.path.join(CSRC, "dg_gemm_pipe.hip"), "-o", os.path.join(bdir, f"dg_gemm_pipe_p{part}.o")])
+    steps.append([HIPCC, *FLAGS, "-c", os.path.join(CSRC, "dg_gemm_pipe.hip"),
+                  "-o", os.path.join(bdir, "dg_gemm_pipe_dispatch.o")])
     steps.append([HIPCC, *FLAGS, "-c", os.path.join(CSRC, "dg_transform.hip"),
                   "-o", os.path.join(bdir, "dg_transform.o")])
     steps.append([HIPCC, *FLAGS, "-c", os.path.join(CSRC, "dg_quant.hip"),
@@ -58,7 +63,7 @@ def build(verbose=False, jobs=None):
         for out in ex.map(_run, steps):
             if verbose and out:
                 print(out)
-    objs = [s[-1] for s in steps]
+    objs = [s[-1] for s in steps]   # (stale objects left in _build are not linked)
     tmp = OUT + ".tmp"
     _run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs])
     os.replace(tmp, OUT)

@@ -206,6 +206,87 @@ int do_launch(dg::GemmParams& p, int kind, int32_t m_rows_for_plan, int32_t m_ma
   return ok();
 }
 
+// ---------------------------------------------------------------- FP8 x FP4
+// Tiles of the pipelined kernel that take FP4 weights, ranked with the same area model as
+// plan_gemm (one workgroup per CU: the LDS stages take most of the 160 KiB).
+struct Fp4Tile {
+  int bm, bn;
+};
+
+int launch_fp8_fp4(dg::GemmParams& p, int kind, int m_plan, int m_max, int out, hipStream_t stream) {
+  int num_sms = g_num_sms_override.load();
+  if (num_sms <= 0) num_sms = device_cu_count();
+  if (num_sms <= 0) return fail(DG_ERR_HIP, "could not query the device's compute-unit count");
+  static const Fp4Tile dense_tiles[] = {{256, 224}, {128, 192}};
+  static const Fp4Tile contig_tiles[] = {{128, 256}, {128, 224}};
+  static const Fp4Tile masked_tiles[] = {{256, 224}, {128, 224}};
+  const Fp4Tile* cand = kind == dg::GRP_DENSE ? dense_tiles : kind == dg::GRP_CONTIG ? contig_tiles : masked_tiles;
+  const char* force = getenv("DG_FORCE_TILE");
+  int fbm = 0, fbn = 0;
+  if (force && sscanf(force, "%dx%d", &fbm, &fbn) != 2) fbm = fbn = 0;
+  int best = -1;
+  double best_cost = 1e300;
+  for (int i = 0; i < 2; ++i) {
+    const Fp4Tile& t = cand[i];
+    if (fbm && (t.bm != fbm || t.bn != fbn)) continue;
+    if (!dg::pipe_instantiated(t.bm, t.bn, dg::SF_FP4_UE8M0, kind, out)) continue;
+    if (p.sf_k < dg::pipe_stages_b(t.bm, t.bn, kind)) continue;
+    const int64_t mt = (m_plan + t.bm - 1) / t.bm, nt = (p.n + t.bn - 1) / t.bn;
+    const int64_t tiles = (kind == dg::GRP_MASKED ? int64_t(p.num_groups) : 1) * mt * nt;
+    const int64_t waves = (tiles + num_sms - 1) / num_sms;
+    const double ai = double(t.bm) * t.bn / double(t.bm + t.bn);
+    double cost = double(waves) * t.bm * t.bn * (ai + 30.0) / ai;
+    // a masked tile that holds a whole group streams each weight slice once (see plan_gemm)
+    if (kind == dg::GRP_MASKED) cost *= t.bm >= m_max ? 0.01 : 1.0;
+    if (cost < best_cost - 1e-9) {
+      best_cost = cost;
+      best = i;
+    }
+  }
+  if (best < 0) return fail(DG_ERR_UNSUPPORTED, "no FP4-weight tile for this problem (k must be >= 256; check DG_FORCE_TILE)");
+  const Fp4Tile& t = cand[best];
+  p.num_n_tiles = (p.n + t.bn - 1) / t.bn;
+  p.num_m_tiles = ((kind == dg::GRP_MASKED ? m_max : p.m) + t.bm - 1) / t.bm;
+  const int64_t tiles = (kind == dg::GRP_MASKED ? int64_t(p.num_groups) : 1) * p.num_m_tiles * p.num_n_tiles;
+  p.total_tiles = int(tiles);
+  int sw = env_int("DG_SWIZZLE_M", 8);
+  if (sw < 1) sw = 1;
+  p.swizzle_m = sw < p.num_m_tiles ? sw : (p.num_m_tiles > 0 ? p.num_m_tiles : 1);
+  const int grid = int(tiles < num_sms ? (tiles < 1 ? 1 : tiles) : num_sms);
+  p.xcd_remap = (grid % 8 == 0) ? 1 : 0;
+  const int esz = out == dg::OUT_BF16 ? 2 : 4;
+  p.d_vec = (p.ldd % 4 == 0 && (p.d_gstride * esz) % 16 == 0 && aligned16(p.d)) ? 1 : 0;
+  p.c_vec = (p.c && p.ldc % 4 == 0 && aligned16(p.c)) ? 1 : 0;
+  p.d_vec16 = ((p.ldd * esz) % 16 == 0 && (p.d_gstride * esz) % 16 == 0 && aligned16(p.d)) ? 1 : 0;
+  if (env_int("DG_PRINT_CONFIGS", 0))
+    fprintf(stderr, "[dg] fp8 x fp4 kind=%d m=%d n=%d k=%d groups=%d out=%d -> tile %dx%d tiles=%d grid=%d\n", kind, p.m,
+            p.n, p.k, p.num_groups, out, t.bm, t.bn, p.total_tiles, grid);
+  const hipError_t e = dg::launch_pipe(p, t.bm, t.bn, dg::SF_FP4_UE8M0, kind, out, grid, stream);
+  if (e != hipSuccess) return fail(DG_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+// Checks shared by the three FP8 x FP4 entry points.
+int check_fp8_fp4(int32_t n, int32_t k, const void* a, int64_t lda, const void* sfa, const void* b, int64_t ldb,
+                  const void* sfb, int64_t sfb_stride, const void* d, int64_t ldd, int32_t d_dtype, bool empty) {
+  if (d_dtype != DG_OUT_BF16 && d_dtype != DG_OUT_F32) return fail(DG_ERR_DTYPE, "d_dtype %d is not DG_OUT_BF16 or DG_OUT_F32", d_dtype);
+  if (k <= 0 || k % 128 != 0) return fail(DG_ERR_SHAPE, "k = %d must be a positive multiple of 128", k);
+  if (k < 256) return fail(DG_ERR_UNSUPPORTED, "the FP8 x FP4 GEMM needs k >= 256 (two K blocks), got %d", k);
+  if (n < 0) return fail(DG_ERR_SHAPE, "n = %d is negative", n);
+  if (empty) return DG_OK;
+  if (!a || !sfa || !b || !sfb || !d) return fail(DG_ERR_NULL, "a, sfa, b, sfb and d must not be NULL");
+  if (lda < k || lda % 16 != 0) return fail(DG_ERR_LAYOUT, "lda = %lld must be >= k and a multiple of 16", (long long)lda);
+  if (ldb < k / 2 || ldb % 16 != 0) return fail(DG_ERR_LAYOUT, "ldb = %lld (bytes of packed FP4) must be >= k / 2 and a multiple of 16", (long long)ldb);
+  if (lda >= (int64_t(1) << 23) || ldb >= (int64_t(1) << 23)) return fail(DG_ERR_LAYOUT, "lda and ldb must be < 2^23 (tile byte ranges are 32-bit)");
+  if (!aligned16(a) || !aligned16(b)) return fail(DG_ERR_LAYOUT, "a and b must be 16-byte aligned");
+  if (!aligned16(sfa) || !aligned16(sfb)) return fail(DG_ERR_LAYOUT, "sfa and sfb must be 16-byte aligned");
+  if (sfb_stride != align4(n)) return fail(DG_ERR_LAYOUT, "sfb must be MN-major with stride align4(n) = %lld, got %lld", (long long)align4(n), (long long)sfb_stride);
+  if (ldd < n) return fail(DG_ERR_LAYOUT, "ldd = %lld must be >= n", (long long)ldd);
+  const uintptr_t esz = d_dtype == DG_OUT_BF16 ? 2 : 4;
+  if ((reinterpret_cast<uintptr_t>(d) & (esz - 1)) != 0) return fail(DG_ERR_LAYOUT, "d is not aligned to its element size");
+  return DG_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -350,6 +431,88 @@ int dg_k_grouped_fp8_gemm_nt_contiguous(int32_t num_groups, int32_t m, int32_t n
     }
   }
   return ok();
+}
+
+int dg_fp8_fp4_gemm_nt(int32_t m, int32_t n, int32_t k, const void* a, int64_t lda, const void* sfa,
+                       int64_t sfa_stride, const void* b, int64_t ldb, const void* sfb, int64_t sfb_stride,
+                       const float* c, int64_t ldc, void* d, int64_t ldd, int32_t d_dtype, hipStream_t stream) {
+  if (m < 0) return fail(DG_ERR_SHAPE, "m = %d is negative", m);
+  int st = check_fp8_fp4(n, k, a, lda, sfa, b, ldb, sfb, sfb_stride, d, ldd, d_dtype, m == 0 || n == 0);
+  if (st != DG_OK) return st;
+  if (m == 0 || n == 0) return ok();
+  if (sfa_stride != align4(m)) return fail(DG_ERR_LAYOUT, "sfa must be MN-major with stride align4(m) = %lld, got %lld", (long long)align4(m), (long long)sfa_stride);
+  if (c) {
+    if (d_dtype != DG_OUT_F32) return fail(DG_ERR_UNSUPPORTED, "a C term requires an FP32 output");
+    if (ldc < n || (reinterpret_cast<uintptr_t>(c) & 3u) != 0) return fail(DG_ERR_LAYOUT, "c needs ldc >= n and 4-byte alignment");
+    if ((const void*)c == d && ldc != ldd) return fail(DG_ERR_LAYOUT, "c aliases d, so ldc must equal ldd");
+  }
+  dg::GemmParams p{};
+  p.a = (const uint8_t*)a; p.lda = lda;
+  p.sfa = sfa; p.sfa_stride = sfa_stride;
+  p.b = (const uint8_t*)b; p.ldb = ldb;
+  p.sfb = sfb; p.sfb_stride = sfb_stride;
+  p.c = c; p.ldc = ldc;
+  p.d = d; p.ldd = ldd;
+  p.m = m; p.n = n; p.k = k; p.num_groups = 1; p.sf_k = k / 128;
+  const int out = c ? dg::OUT_F32_C : (d_dtype == DG_OUT_BF16 ? dg::OUT_BF16 : dg::OUT_F32);
+  return launch_fp8_fp4(p, dg::GRP_DENSE, m, 0, out, stream);
+}
+
+int dg_m_grouped_fp8_fp4_gemm_nt_contiguous(int32_t m_total, int32_t n, int32_t k, int32_t num_groups,
+                                            const void* a, int64_t lda, const void* sfa, int64_t sfa_stride,
+                                            const void* b, int64_t ldb, int64_t b_group_stride, const void* sfb,
+                                            int64_t sfb_stride, int64_t sfb_group_stride, void* d, int64_t ldd,
+                                            int32_t d_dtype, const int32_t* grouped_layout, hipStream_t stream) {
+  if (m_total < 0) return fail(DG_ERR_SHAPE, "m_total = %d is negative", m_total);
+  if (num_groups <= 0) return fail(DG_ERR_SHAPE, "num_groups = %d must be positive", num_groups);
+  int st = check_fp8_fp4(n, k, a, lda, sfa, b, ldb, sfb, sfb_stride, d, ldd, d_dtype, m_total == 0 || n == 0);
+  if (st != DG_OK) return st;
+  if (m_total == 0 || n == 0) return ok();
+  if (d_dtype != DG_OUT_BF16) return fail(DG_ERR_UNSUPPORTED, "the grouped FP8 x FP4 GEMMs write BF16");
+  if (!grouped_layout) return fail(DG_ERR_NULL, "grouped_layout must not be NULL");
+  if (sfa_stride != align4(m_total)) return fail(DG_ERR_LAYOUT, "sfa must be MN-major with stride align4(m_total) = %lld, got %lld", (long long)align4(m_total), (long long)sfa_stride);
+  if (b_group_stride < int64_t(n) * ldb || b_group_stride % 16 != 0) return fail(DG_ERR_LAYOUT, "b_group_stride must be >= n*ldb and a multiple of 16");
+  if (sfb_group_stride < int64_t(k / 128) * sfb_stride || sfb_group_stride % 4 != 0) return fail(DG_ERR_LAYOUT, "sfb_group_stride is smaller than one group's scales or not a multiple of 4");
+  dg::GemmParams p{};
+  p.a = (const uint8_t*)a; p.lda = lda;
+  p.sfa = sfa; p.sfa_stride = sfa_stride;
+  p.b = (const uint8_t*)b; p.ldb = ldb; p.b_gstride = b_group_stride;
+  p.sfb = sfb; p.sfb_stride = sfb_stride; p.sfb_gstride = sfb_group_stride;
+  p.d = d; p.ldd = ldd;
+  p.grouped_layout = grouped_layout;
+  p.m = m_total; p.n = n; p.k = k; p.num_groups = num_groups; p.sf_k = k / 128;
+  return launch_fp8_fp4(p, dg::GRP_CONTIG, m_total, 0, dg::OUT_BF16, stream);
+}
+
+int dg_m_grouped_fp8_fp4_gemm_nt_masked(int32_t num_groups, int32_t m_max, int32_t n, int32_t k, const void* a,
+                                        int64_t lda, int64_t a_group_stride, const void* sfa, int64_t sfa_stride,
+                                        int64_t sfa_group_stride, const void* b, int64_t ldb, int64_t b_group_stride,
+                                        const void* sfb, int64_t sfb_stride, int64_t sfb_group_stride, void* d,
+                                        int64_t ldd, int64_t d_group_stride, int32_t d_dtype, const int32_t* masked_m,
+                                        int32_t expected_m, hipStream_t stream) {
+  if (num_groups <= 0) return fail(DG_ERR_SHAPE, "num_groups = %d must be positive", num_groups);
+  if (m_max < 0) return fail(DG_ERR_SHAPE, "m_max = %d is negative", m_max);
+  int st = check_fp8_fp4(n, k, a, lda, sfa, b, ldb, sfb, sfb_stride, d, ldd, d_dtype, m_max == 0 || n == 0);
+  if (st != DG_OK) return st;
+  if (m_max == 0 || n == 0) return ok();
+  if (d_dtype != DG_OUT_BF16) return fail(DG_ERR_UNSUPPORTED, "the grouped FP8 x FP4 GEMMs write BF16");
+  if (!masked_m) return fail(DG_ERR_NULL, "masked_m must not be NULL");
+  if (sfa_stride != align4(m_max)) return fail(DG_ERR_LAYOUT, "sfa must be MN-major with stride align4(m_max) = %lld, got %lld", (long long)align4(m_max), (long long)sfa_stride);
+  if (a_group_stride < int64_t(m_max) * lda || a_group_stride % 16 != 0) return fail(DG_ERR_LAYOUT, "a_group_stride must be >= m_max*lda and a multiple of 16");
+  if (b_group_stride < int64_t(n) * ldb || b_group_stride % 16 != 0) return fail(DG_ERR_LAYOUT, "b_group_stride must be >= n*ldb and a multiple of 16");
+  if (sfa_group_stride < int64_t((k / 128 + 3) / 4) * sfa_stride || sfa_group_stride % 4 != 0) return fail(DG_ERR_LAYOUT, "sfa_group_stride is smaller than one group's scales or not a multiple of 4");
+  if (sfb_group_stride < int64_t(k / 128) * sfb_stride || sfb_group_stride % 4 != 0) return fail(DG_ERR_LAYOUT, "sfb_group_stride is smaller than one group's scales or not a multiple of 4");
+  if (d_group_stride < int64_t(m_max) * ldd) return fail(DG_ERR_LAYOUT, "d_group_stride must be >= m_max*ldd");
+  dg::GemmParams p{};
+  p.a = (const uint8_t*)a; p.lda = lda; p.a_gstride = a_group_stride;
+  p.sfa = sfa; p.sfa_stride = sfa_stride; p.sfa_gstride = sfa_group_stride;
+  p.b = (const uint8_t*)b; p.ldb = ldb; p.b_gstride = b_group_stride;
+  p.sfb = sfb; p.sfb_stride = sfb_stride; p.sfb_gstride = sfb_group_stride;
+  p.d = d; p.ldd = ldd; p.d_gstride = d_group_stride;
+  p.masked_m = masked_m;
+  p.m = m_max; p.n = n; p.k = k; p.num_groups = num_groups; p.sf_k = k / 128;
+  const int em = (expected_m > 0 && expected_m < m_max) ? expected_m : m_max;
+  return launch_fp8_fp4(p, dg::GRP_MASKED, em, m_max, dg::OUT_BF16, stream);
 }
 
 int dg_transform_sf(const float* sf_in, int32_t num_groups, int32_t mn, int32_t sf_k, int32_t gran_mn,

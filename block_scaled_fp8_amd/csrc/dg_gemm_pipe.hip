@@ -26,6 +26,10 @@
 //  * The 16-column fragments of a wave that straddle two 128-wide weight-scale blocks
 //    take the second block's scale from a compile-time split chosen once per tile
 //    (page "02 · DeepGEMM 技术解析" §2.3).
+//  * FP4 (E2M1) weights (page "第13章 DeepGEMM" §13.5) go into the same scaled MFMA as the
+//    FP8 activations, which takes mixed operand formats; a weight row then holds 64 bytes per
+//    K block, and its four power-of-two scales per block (one per 32 K) are applied by the
+//    matrix unit, lane group g supplying the scale of K [32g, 32g+32).
 #include <utility>
 
 #include "dg_internal.h"
@@ -47,11 +51,13 @@ constexpr int NA = 3;    // A stages
 // weights from HBM with little reuse, keep 3 in flight; up to 4 are supported)
 template <int BM, int BN, int WM, int WN, int SFM, int NB_ = 2>
 struct Geo {
+  static constexpr bool FP4B = SFM == SF_FP4_UE8M0;
+  static constexpr int BKB = FP4B ? BK / 2 : BK;  // bytes of a weight row per K block
   static constexpr int NB = NB_;
   static constexpr int NW = WM * WN;
   static constexpr int TM = BM / WM, TN = BN / WN;
   static constexpr int FM = TM / 16, FN = TN / 16;
-  static constexpr int A_SLOT = BM * BK, B_SLOT = BN * BK;
+  static constexpr int A_SLOT = BM * BK, B_SLOT = BN * BKB;
   static constexpr int SA_SLOT = (BM * 4 + 1023) / 1024 * 1024;
   static constexpr int SB_SLOT = (SFM == SF_1D2D_F32) ? 0 : (BN * 4 + 1023) / 1024 * 1024;
   static constexpr int A_OFF = 0;
@@ -61,7 +67,7 @@ struct Geo {
   static constexpr int TRASH_OFF = SB_OFF + NB * SB_SLOT;  // 1 KiB sink for padding copies
   static constexpr int LDS_BYTES = TRASH_OFF + 1024;
   static constexpr int A_ROWL = BM / 8;  // 1 KiB wave-loads of A rows per block
-  static constexpr int B_ROWL = BN / 8;
+  static constexpr int B_ROWL = BN * BKB / 1024;
   // wave-loads per wave and block: A rows + activation scales; B rows (+ per-row weight scales)
   static constexpr int LA = (A_ROWL + 1 + NW - 1) / NW;
   static constexpr int LB = (B_ROWL + (SFM == SF_1D2D_F32 ? 0 : 1) + NW - 1) / NW;
@@ -212,14 +218,14 @@ __device__ __forceinline__ void pin_src(Src& s) {
 
 __device__ __forceinline__ Src make_src(const uint8_t* X, int64_t ld, int r0, int rows_total, int R, int kb,
                                         bool valid, const void* sf, int64_t sf_stride, int64_t sf_row,
-                                        bool has_scales) {
+                                        bool has_scales, int bkb) {
   const int rows = valid ? max(0, min(rows_total - r0, R)) : 0;
-  const uint64_t base = (uint64_t)(X + (int64_t)r0 * ld + kb * BK);
+  const uint64_t base = (uint64_t)(X + (int64_t)r0 * ld + kb * bkb);
   const uint64_t sbase = (uint64_t)((const uint8_t*)sf + 4 * (sf_row * sf_stride + r0));
   Src s;
   s.lo = __builtin_amdgcn_readfirstlane((uint32_t)base);
   s.hi = __builtin_amdgcn_readfirstlane((uint32_t)(base >> 32));
-  s.bytes = __builtin_amdgcn_readfirstlane(rows > 0 ? rows * (int)ld - kb * BK : 0);
+  s.bytes = __builtin_amdgcn_readfirstlane(rows > 0 ? rows * (int)ld - kb * bkb : 0);
   s.slo = __builtin_amdgcn_readfirstlane((uint32_t)sbase);
   s.shi = __builtin_amdgcn_readfirstlane((uint32_t)(sbase >> 32));
   s.sbytes = __builtin_amdgcn_readfirstlane((has_scales && valid) ? 4 * max(0, min((int)sf_stride - r0, R)) : 0);
@@ -231,21 +237,21 @@ __device__ __forceinline__ const void* src_ptr(uint32_t lo, uint32_t hi) {
 }
 
 // Source of K block k (counted from the start of tile `c`; k >= nkb lies in the next tile
-// `n`) from the two tiles' block-0 sources: rows advance by k * 128 bytes, scales by
-// srow(k) scale rows of `sstep` bytes (srow = k, or k / 4 for UE8M0 words).  A few scalar
-// instructions instead of rebuilding the source from the tile position every block.
-template <bool UE8M0>
+// `n`) from the two tiles' block-0 sources: rows advance by k * BKB bytes, scales by
+// srow(k) scale rows of `sstep` bytes (srow = k, or k / 4 for words that pack four K blocks).
+// A few scalar instructions instead of rebuilding the source from the tile position every block.
+template <bool PACK4, int BKB>
 __device__ __forceinline__ Src src_at(const Src& c, const Src& n, int k, int nkb, uint32_t sstep) {
   const bool same = k < nkb;
   const int kk = same ? k : k - nkb;
-  const uint64_t base = ((uint64_t)(same ? c.hi : n.hi) << 32 | (same ? c.lo : n.lo)) + (uint32_t)(kk * BK);
-  const int srow = UE8M0 ? kk >> 2 : kk;
+  const uint64_t base = ((uint64_t)(same ? c.hi : n.hi) << 32 | (same ? c.lo : n.lo)) + (uint32_t)(kk * BKB);
+  const int srow = PACK4 ? kk >> 2 : kk;
   const uint64_t sbase = ((uint64_t)(same ? c.shi : n.shi) << 32 | (same ? c.slo : n.slo)) + (uint32_t)srow * sstep;
   Src s;
   s.lo = __builtin_amdgcn_readfirstlane((uint32_t)base);
   s.hi = __builtin_amdgcn_readfirstlane((uint32_t)(base >> 32));
   // (a tile with rows has bytes > (nkb-1) * 128)
-  s.bytes = __builtin_amdgcn_readfirstlane(max((same ? c.bytes : n.bytes) - kk * BK, 0));
+  s.bytes = __builtin_amdgcn_readfirstlane(max((same ? c.bytes : n.bytes) - kk * BKB, 0));
   s.slo = __builtin_amdgcn_readfirstlane((uint32_t)sbase);
   s.shi = __builtin_amdgcn_readfirstlane((uint32_t)(sbase >> 32));
   s.sbytes = __builtin_amdgcn_readfirstlane(same ? c.sbytes : n.sbytes);
@@ -275,8 +281,12 @@ template <int BM, int BN, int WM, int WN, int SFM, int OUT, int GRP, int NB>
 struct Kernel {
   // Per-row FP32 weight scales run on the generic kernel: here the B stage that holds a
   // block's scales is refilled before its last two partials are promoted.
-  static_assert(SFM == SF_1D2D_F32 || SFM == SF_1D1D_UE8M0, "1d2d FP32 or 1d1d UE8M0 scales only");
+  static_assert(SFM == SF_1D2D_F32 || SFM == SF_1D1D_UE8M0 || SFM == SF_FP4_UE8M0,
+                "1d2d FP32, 1d1d UE8M0 or FP4-weight UE8M0 scales only");
   using G = Geo<BM, BN, WM, WN, SFM, NB>;
+  static constexpr bool FP4B = G::FP4B;
+  // power-of-two scales applied by the matrix unit itself (no VALU promotion)
+  static constexpr bool UE = SFM == SF_1D1D_UE8M0 || FP4B;
   static constexpr int FM = G::FM, FN = G::FN, TM = G::TM, TN = G::TN, STEPS = G::STEPS;
   static constexpr int NW = G::NW;
   static __device__ __forceinline__ int next_b(int b) { return b == NB - 1 ? 0 : b + 1; }
@@ -292,6 +302,7 @@ struct Kernel {
   uint32_t a_lo, a_hi, b_lo, b_hi;  // per-lane LDS fragment bases (stage 0)
   uint32_t sa_lds;                  // per-lane LDS address of its rows' activation scales (stage 0)
   uint32_t ww_lds;                  // UE8M0: per-lane LDS address of its B row's packed weight scales (stage 0)
+  int wshift;                       // FP4 weights: bit offset of this lane's 32-K block scale in the packed word
   int ustep_a, ustep_b;             // 8 * NW * ld
   uint32_t sstep_a, sstep_b;        // bytes per K-block row of the activation / per-row weight scales
   // masked groups (at most 64): lane g holds group g's valid rows and the inclusive prefix
@@ -308,18 +319,39 @@ struct Kernel {
     const uint32_t r = (uint32_t)lane >> 3, c = (uint32_t)lane & 7, w = (uint32_t)wave & 1;
     const uint32_t chunk = (c ^ r ^ w) << 4;
     off_a = (8u * (uint32_t)wave + r) * (uint32_t)p.lda + chunk;
-    off_b = (8u * (uint32_t)wave + r) * (uint32_t)p.ldb + chunk;
     off_s = (uint32_t)lane << 4;
     ustep_a = __builtin_amdgcn_readfirstlane(8 * NW * (int)p.lda);
-    ustep_b = __builtin_amdgcn_readfirstlane(8 * NW * (int)p.ldb);
+    if constexpr (FP4B) {
+      // 64-byte weight rows: wave-load q fills rows 16q..16q+15; lane L writes row 16q + L/4,
+      // slot L%4, which holds chunk (L%4) ^ swz4(16q + L/4) = (L%4) ^ (L/16)
+      off_b = (16u * (uint32_t)wave + ((uint32_t)lane >> 2)) * (uint32_t)p.ldb +
+              ((((uint32_t)lane & 3u) ^ ((uint32_t)lane >> 4)) << 4);
+      ustep_b = __builtin_amdgcn_readfirstlane(16 * NW * (int)p.ldb);
+    } else {
+      off_b = (8u * (uint32_t)wave + r) * (uint32_t)p.ldb + chunk;
+      ustep_b = __builtin_amdgcn_readfirstlane(8 * NW * (int)p.ldb);
+    }
     sstep_a = __builtin_amdgcn_readfirstlane(4u * (uint32_t)p.sfa_stride);
     sstep_b = __builtin_amdgcn_readfirstlane(4u * (uint32_t)p.sfb_stride);
     const int sw = swz(lr);
-    const uint32_t lo = (uint32_t)(((2 * lg) ^ sw) * 16), hi = (uint32_t)(((2 * lg + 1) ^ sw) * 16);
+    // An FP8 operand of the 16x16x128 MFMA holds, in lane group lg, K [16 lg, +16) in its
+    // first four registers and K [64 + 16 lg, +16) in its last four (chunks lg and lg + 4 of a
+    // 128-byte row); an FP4 operand holds K [32 lg, +32) (chunk lg of a 64-byte row).  With FP8
+    // on both sides any assignment shared by the two operands gives the same dot products, and
+    // the kernel reads chunks 2 lg and 2 lg + 1; next to FP4 weights it must be the true one.
+    const int c_lo = FP4B ? lg : 2 * lg, c_hi = FP4B ? lg + 4 : 2 * lg + 1;
+    const uint32_t lo = (uint32_t)((c_lo ^ sw) * 16), hi = (uint32_t)((c_hi ^ sw) * 16);
     a_lo = G::A_OFF + (wm * TM + lr) * BK + lo;
     a_hi = G::A_OFF + (wm * TM + lr) * BK + hi;
-    b_lo = G::B_OFF + (wn * TN + lr) * BK + lo;
-    b_hi = G::B_OFF + (wn * TN + lr) * BK + hi;
+    if constexpr (FP4B) {
+      // rows r..r+15 of chunk lg sit in slots lg ^ swz4(r): with 64-byte rows, rows that share
+      // a bank group (r mod 4) get four different slots, so the reads are conflict-free
+      b_lo = b_hi = G::B_OFF + (wn * TN + lr) * G::BKB + ((lg ^ ((lr >> 2) & 3)) * 16);
+    } else {
+      b_lo = G::B_OFF + (wn * TN + lr) * BK + lo;
+      b_hi = G::B_OFF + (wn * TN + lr) * BK + hi;
+    }
+    wshift = 8 * lg;
     sa_lds = G::SA_OFF + 4 * (wm * TM + lr);
     ww_lds = G::SB_OFF + 4 * (wn * TN + lr);
     if (GRP == GRP_MASKED && p.num_groups <= 64) {
@@ -355,17 +387,18 @@ struct Kernel {
 
   // ---- copies HBM -> LDS --------------------------------------------------------------
   __device__ __forceinline__ Src a_src(const TilePos& t, int kb) const {
-    const int64_t srow = (SFM == SF_1D1D_UE8M0) ? (kb >> 2) : kb;  // UE8M0 words hold four K blocks
+    const int64_t srow = UE ? (kb >> 2) : kb;  // UE8M0 words hold four K blocks
     const uint8_t* A = p.a;
     const uint8_t* SA = (const uint8_t*)p.sfa;
     if (GRP == GRP_MASKED) {
       A += (int64_t)t.g * p.a_gstride;
       SA += 4 * (int64_t)t.g * p.sfa_gstride;
     }
-    return make_src(A, p.lda, t.m0, t.mv, BM, kb, t.valid, SA, p.sfa_stride, srow, true);
+    return make_src(A, p.lda, t.m0, t.mv, BM, kb, t.valid, SA, p.sfa_stride, srow, true, BK);
   }
   __device__ __forceinline__ Src b_src(const TilePos& t, int kb) const {
-    const int64_t srow = (SFM == SF_1D1D_UE8M0) ? (kb >> 2) : kb;
+    // (FP4 weights: one word per K block, holding its four 32-K scales)
+    const int64_t srow = SFM == SF_1D1D_UE8M0 ? (kb >> 2) : kb;
     const uint8_t* B = p.b;
     const uint8_t* SB = (const uint8_t*)p.sfb;
     if (GRP != GRP_DENSE) {
@@ -374,7 +407,7 @@ struct Kernel {
     }
     // (a skipped contiguous tile reads no weights either)
     const bool valid = GRP == GRP_CONTIG ? t.valid && t.mv > 0 : t.valid;
-    return make_src(B, p.ldb, t.n0, p.n, BN, kb, valid, SB, p.sfb_stride, srow, SFM != SF_1D2D_F32);
+    return make_src(B, p.ldb, t.n0, p.n, BN, kb, valid, SB, p.sfb_stride, srow, SFM != SF_1D2D_F32, G::BKB);
   }
 
   // Part U of the copy of one operand block into the stage at LDS offset `dst` (its scales
@@ -438,6 +471,11 @@ struct Kernel {
   }
   __device__ __forceinline__ v8i b_frag(int bslot, int j) const {
     const uint32_t so = (uint32_t)(bslot * G::B_SLOT);
+    if constexpr (FP4B) {
+      // 32 E2M1 codes in the first four registers; the MFMA does not read the others
+      const v4i x = *(const v4i*)(smem + b_lo + so + j * 16 * G::BKB);
+      return (v8i){x.x, x.y, x.z, x.w, 0, 0, 0, 0};
+    }
     return frag(b_lo + so, b_hi + so, j * 16 * BK);
   }
   // UE8M0: the packed weight-scale word of the lane's B row in fragment j of B stage bslot
@@ -557,17 +595,19 @@ struct Kernel {
         // matrix unit is fed first)
       } else if constexpr (i == 0 && j + 1 < FN) {
         bfn = b_frag(bs, j + 1);
-        if (SFM == SF_1D1D_UE8M0) ebwn = weight_word(bs, j + 1);
+        if (UE) ebwn = weight_word(bs, j + 1);
       }
       __builtin_amdgcn_sched_barrier(0);
       v4f acc = zero;
       if constexpr (i < FA) {
-        if constexpr (SFM == SF_1D1D_UE8M0) {
+        if constexpr (UE) {
           // power-of-two scales: the matrix unit applies 2^(e_b + e_a) to the block's products
-          // and adds them to the FP32 accumulator itself, so the promotion needs no VALU work
-          const int eb = (int)((ebw >> kshift) & 0xFFu);
+          // and adds them to the FP32 accumulator itself, so the promotion needs no VALU work.
+          // FP4 weights carry one scale per 32 K: lane group lg passes the one of its K range.
+          const int eb = (int)((ebw >> (FP4B ? wshift : kshift)) & 0xFFu);
           const v4f cin = {fin[i][j][0], fin[i][j][1], fin[i][j][2], fin[i][j][3]};
-          const v4f r = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf, c.af[i], cin, 0, 0, 0, eb, 0, ea[i]);
+          const v4f r = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf, c.af[i], cin, FP4B ? 4 : 0, 0, 0, eb, 0,
+                                                                         ea[i]);
 #pragma unroll
           for (int v = 0; v < 4; ++v) fin[i][j][v] = r[v];
         } else {
@@ -582,7 +622,7 @@ struct Kernel {
         if (kb == 0) copy_a_all(asrc, as2, std::make_integer_sequence<int, G::LA>{});
         // first B fragment and scales of block g+1
         bfn = b_frag(bs1, 0);
-        if (SFM == SF_1D1D_UE8M0) ebwn = weight_word(bs1, 0);
+        if (UE) ebwn = weight_word(bs1, 0);
         if (SFM == SF_1D2D_F32) {
           sbn0 = *wp0;
           sbn1 = *wp1;
@@ -590,11 +630,11 @@ struct Kernel {
         read_scales(c, as1);
       }
       if constexpr (t == 0) {
-        asrc = src_at<SFM == SF_1D1D_UE8M0>(sb.ac, sb.an, kb + 2, nkb, sstep_a);
+        asrc = src_at<UE, BK>(sb.ac, sb.an, kb + 2, nkb, sstep_a);
         pin_src(asrc);
       }
       if constexpr (t == 1) {
-        bsrc = src_at<SFM == SF_1D1D_UE8M0>(sb.bc, sb.bn, kb + NB, nkb, sstep_b);
+        bsrc = src_at<SFM == SF_1D1D_UE8M0, G::BKB>(sb.bc, sb.bn, kb + NB, nkb, sstep_b);
         pin_src(bsrc);
         if (SFM == SF_1D2D_F32) {
           const bool same = kb + 1 < nkb;
@@ -609,7 +649,7 @@ struct Kernel {
       // after its last use, fragment i of A is replaced by block g+1's
       if constexpr (t >= G::TB) c.af[i] = a_frag(as1, i);
       // promote the partial of MFMA t-2 (for t < 2: of the previous block, with its factor)
-      if constexpr (SFM != SF_1D1D_UE8M0 && t >= 2 && (t - 2) % FM < FA) {
+      if constexpr (!UE && t >= 2 && (t - 2) % FM < FA) {
         constexpr int tp = t - 2, jp = tp / FM, ip = tp % FM;
         const float sc = factor(ip, jp);
 #pragma unroll
@@ -621,7 +661,7 @@ struct Kernel {
         for (int v = 0; v < 4; ++v) fin[ip][jp][v] = __builtin_fmaf(c.pscale[t], r2[v], fin[ip][jp][v]);
         pin(fin[ip][jp]);
       }
-      if constexpr (SFM != SF_1D1D_UE8M0) {
+      if constexpr (!UE) {
         r2 = r1;
         r1 = acc;
       }
@@ -639,8 +679,8 @@ struct Kernel {
     c.ebw = ebwn;
     c.sbw0 = sbn0;
     c.sbw1 = sbn1;
-    c.acc1 = SFM == SF_1D1D_UE8M0 ? zero : r1;
-    c.acc2 = SFM == SF_1D1D_UE8M0 ? zero : r2;
+    c.acc1 = UE ? zero : r1;
+    c.acc2 = UE ? zero : r2;
     constexpr int t0 = STEPS - 2, t1 = STEPS - 1;
     c.pscale[0] = SFM == SF_1D2D_F32 ? factor(t0 % FM, t0 / FM) : 0.f;
     c.pscale[1] = SFM == SF_1D2D_F32 ? factor(t1 % FM, t1 / FM) : 0.f;
@@ -860,7 +900,7 @@ __global__ void __launch_bounds__(WM* WN * 64, 1) pipe_kernel(const GemmParams p
 #pragma unroll
   for (int i = 0; i < K::FM; ++i) c.af[i] = k.a_frag(0, i);
   c.bf = k.b_frag(0, 0);
-  c.ebw = SFM == SF_1D1D_UE8M0 ? k.weight_word(0, 0) : 0u;
+  c.ebw = K::UE ? k.weight_word(0, 0) : 0u;
   k.read_scales(c, 0);
   const v4f zero = {0.f, 0.f, 0.f, 0.f};
   c.acc1 = zero;
@@ -886,7 +926,7 @@ static hipError_t launch_one(const GemmParams& p, int grid, hipStream_t stream) 
   return hipGetLastError();
 }
 
-// dense tiles that also run UE8M0 scales (the planner's choices for large problems)
+// dense tiles that also run UE8M0 scales and FP4 weights (the planner's choices for large problems)
 constexpr bool dense_ue8m0_tile(int bm, int bn) { return (bm == 256 && bn == 224) || (bm == 128 && bn == 192); }
 
 template <int BM, int BN, int WM, int WN>
@@ -927,11 +967,66 @@ static hipError_t launch_masked(const GemmParams& p, int sfm, int out, int grid,
 
 }  // namespace pipe
 
+// The file is compiled once per part (DG_PIPE_PART: dense, contiguous, masked, FP4 weights) so
+// the instantiations build in parallel, and once without it for the dispatch functions.
+#if defined(DG_PIPE_PART)
+#if DG_PIPE_PART == 0
+hipError_t launch_pipe_dense(const GemmParams& p, int bm, int bn, int sfm, int out, int grid, hipStream_t s) {
+  if (bm == 256 && bn == 224) return pipe::launch_dense<256, 224, 4, 2>(p, sfm, out, grid, s);
+  if (bm == 256 && bn == 192) return pipe::launch_dense<256, 192, 4, 2>(p, sfm, out, grid, s);
+  if (bm == 128 && bn == 192) return pipe::launch_dense<128, 192, 2, 2>(p, sfm, out, grid, s);
+  if (bm == 128 && bn == 224) return pipe::launch_dense<128, 224, 2, 2>(p, sfm, out, grid, s);
+  if (bm == 128 && bn == 256) return pipe::launch_dense<128, 256, 2, 2>(p, sfm, out, grid, s);
+  if (bm == 128 && bn == 128) return pipe::launch_dense<128, 128, 2, 2>(p, sfm, out, grid, s);
+  return hipErrorInvalidValue;
+}
+#elif DG_PIPE_PART == 1
+hipError_t launch_pipe_contig(const GemmParams& p, int bm, int bn, int sfm, int out, int grid, hipStream_t s) {
+  if (bm == 128 && bn == 224) return pipe::launch_contig<128, 224, 2, 2>(p, sfm, out, grid, s);
+  if (bm == 128 && bn == 256) return pipe::launch_contig<128, 256, 2, 2>(p, sfm, out, grid, s);
+  return hipErrorInvalidValue;
+}
+#elif DG_PIPE_PART == 2
+hipError_t launch_pipe_masked(const GemmParams& p, int bm, int bn, int sfm, int out, int grid, hipStream_t s) {
+  if (bm == 128 && bn == 224) return pipe::launch_masked<128, 224, 2, 2, 3>(p, sfm, out, grid, s);
+  if (bm == 256 && bn == 224) return pipe::launch_masked<256, 224, 4, 2, 2>(p, sfm, out, grid, s);
+  return hipErrorInvalidValue;
+}
+#elif DG_PIPE_PART == 3
+hipError_t launch_pipe_fp4(const GemmParams& p, int bm, int bn, int grp, int out, int grid, hipStream_t s) {
+  using namespace pipe;
+  if (grp == GRP_DENSE) {
+    if (bm == 256 && bn == 224 && out == OUT_BF16) return launch_one<256, 224, 4, 2, SF_FP4_UE8M0, OUT_BF16, GRP_DENSE, 2>(p, grid, s);
+    if (bm == 256 && bn == 224 && out == OUT_F32) return launch_one<256, 224, 4, 2, SF_FP4_UE8M0, OUT_F32, GRP_DENSE, 2>(p, grid, s);
+    if (bm == 256 && bn == 224 && out == OUT_F32_C) return launch_one<256, 224, 4, 2, SF_FP4_UE8M0, OUT_F32_C, GRP_DENSE, 2>(p, grid, s);
+    if (bm == 128 && bn == 192 && out == OUT_BF16) return launch_one<128, 192, 2, 2, SF_FP4_UE8M0, OUT_BF16, GRP_DENSE, 2>(p, grid, s);
+    if (bm == 128 && bn == 192 && out == OUT_F32) return launch_one<128, 192, 2, 2, SF_FP4_UE8M0, OUT_F32, GRP_DENSE, 2>(p, grid, s);
+    if (bm == 128 && bn == 192 && out == OUT_F32_C) return launch_one<128, 192, 2, 2, SF_FP4_UE8M0, OUT_F32_C, GRP_DENSE, 2>(p, grid, s);
+  } else if (grp == GRP_CONTIG && out == OUT_BF16) {
+    if (bm == 128 && bn == 224) return launch_one<128, 224, 2, 2, SF_FP4_UE8M0, OUT_BF16, GRP_CONTIG, 2>(p, grid, s);
+    if (bm == 128 && bn == 256) return launch_one<128, 256, 2, 2, SF_FP4_UE8M0, OUT_BF16, GRP_CONTIG, 2>(p, grid, s);
+  } else if (grp == GRP_MASKED && out == OUT_BF16) {
+    if (bm == 128 && bn == 224) return launch_one<128, 224, 2, 2, SF_FP4_UE8M0, OUT_BF16, GRP_MASKED, 3>(p, grid, s);
+    if (bm == 256 && bn == 224) return launch_one<256, 224, 4, 2, SF_FP4_UE8M0, OUT_BF16, GRP_MASKED, 2>(p, grid, s);
+  }
+  return hipErrorInvalidValue;
+}
+#endif
+#else  // dispatch
+
 // Shapes with a deep-pipelined instantiation: dense problems (1d2d FP32 scales, any output;
 // UE8M0 scales with BF16 or FP32 output on two tiles), contiguous groups (1d2d FP32 scales
 // with BF16 or FP32 output, UE8M0 scales with BF16), and masked problems (1d2d FP32 or UE8M0
 // scales, BF16) on a 128-row tile streaming B through three stages or a 256-row tile with two.
+// FP4 weights: dense on the two UE8M0 tiles (BF16, FP32 or FP32 + C out), contiguous and
+// masked groups on the same tiles as FP8 (BF16 out).
 bool pipe_instantiated(int bm, int bn, int sfm, int grp, int out) {
+  if (sfm == SF_FP4_UE8M0) {
+    if (grp == GRP_DENSE) return out >= OUT_BF16 && out <= OUT_F32_C && pipe::dense_ue8m0_tile(bm, bn);
+    if (grp == GRP_CONTIG) return out == OUT_BF16 && bm == 128 && (bn == 224 || bn == 256);
+    if (grp == GRP_MASKED) return out == OUT_BF16 && (bm == 128 || bm == 256) && bn == 224;
+    return false;
+  }
   if (grp == GRP_CONTIG) {
     const bool ok = (sfm == SF_1D2D_F32 && (out == OUT_BF16 || out == OUT_F32)) ||
                     (sfm == SF_1D1D_UE8M0 && out == OUT_BF16);
@@ -957,28 +1052,18 @@ int pipe_stages_b(int bm, int bn, int grp) { return grp == GRP_MASKED && bm == 1
 int pipe_lds_bytes(int bm, int bn, int sfm, int grp) {
   const int sa_slot = (bm * 4 + 1023) / 1024 * 1024;
   const int sb_slot = sfm == SF_1D2D_F32 ? 0 : (bn * 4 + 1023) / 1024 * 1024;
-  return pipe::NA * (bm * pipe::BK + sa_slot) + pipe_stages_b(bm, bn, grp) * (bn * pipe::BK + sb_slot) + 1024;
+  const int bkb = sfm == SF_FP4_UE8M0 ? pipe::BK / 2 : pipe::BK;
+  return pipe::NA * (bm * pipe::BK + sa_slot) + pipe_stages_b(bm, bn, grp) * (bn * bkb + sb_slot) + 1024;
 }
 
 hipError_t launch_pipe(const GemmParams& p, int bm, int bn, int sfm, int grp, int out, int grid,
                        hipStream_t stream) {
-  if (grp == GRP_MASKED) {
-    if (bm == 128 && bn == 224) return pipe::launch_masked<128, 224, 2, 2, 3>(p, sfm, out, grid, stream);
-    if (bm == 256 && bn == 224) return pipe::launch_masked<256, 224, 4, 2, 2>(p, sfm, out, grid, stream);
-    return hipErrorInvalidValue;
-  }
-  if (grp == GRP_CONTIG) {
-    if (bm == 128 && bn == 224) return pipe::launch_contig<128, 224, 2, 2>(p, sfm, out, grid, stream);
-    if (bm == 128 && bn == 256) return pipe::launch_contig<128, 256, 2, 2>(p, sfm, out, grid, stream);
-    return hipErrorInvalidValue;
-  }
-  if (bm == 256 && bn == 224) return pipe::launch_dense<256, 224, 4, 2>(p, sfm, out, grid, stream);
-  if (bm == 256 && bn == 192) return pipe::launch_dense<256, 192, 4, 2>(p, sfm, out, grid, stream);
-  if (bm == 128 && bn == 192) return pipe::launch_dense<128, 192, 2, 2>(p, sfm, out, grid, stream);
-  if (bm == 128 && bn == 224) return pipe::launch_dense<128, 224, 2, 2>(p, sfm, out, grid, stream);
-  if (bm == 128 && bn == 256) return pipe::launch_dense<128, 256, 2, 2>(p, sfm, out, grid, stream);
-  if (bm == 128 && bn == 128) return pipe::launch_dense<128, 128, 2, 2>(p, sfm, out, grid, stream);
-  return hipErrorInvalidValue;
+  if (!pipe_instantiated(bm, bn, sfm, grp, out)) return hipErrorInvalidValue;
+  if (sfm == SF_FP4_UE8M0) return launch_pipe_fp4(p, bm, bn, grp, out, grid, stream);
+  if (grp == GRP_MASKED) return launch_pipe_masked(p, bm, bn, sfm, out, grid, stream);
+  if (grp == GRP_CONTIG) return launch_pipe_contig(p, bm, bn, sfm, out, grid, stream);
+  return launch_pipe_dense(p, bm, bn, sfm, out, grid, stream);
 }
+#endif
 
 }  // namespace dg

@@ -11,6 +11,10 @@ enum SfMode {
   SF_1D2D_F32 = 0,    // sfa FP32 MN-major per row; sfb FP32 per 128x128 block, K-major
   SF_1D1D_F32 = 1,    // sfa and sfb FP32 MN-major, one scale per row and K block
   SF_1D1D_UE8M0 = 2,  // sfa and sfb UE8M0 packed four per int32, MN-major
+  // FP4 (E2M1) weights, two per byte (page "第13章 DeepGEMM" §13.5): sfa UE8M0 per row and 128-K
+  // block packed four per int32 as above; sfb UE8M0 per row and 32-K block, the four codes of
+  // one 128-K block in one int32 (byte t = 32-block t), MN-major [k / 128][align4(n)]
+  SF_FP4_UE8M0 = 3,
 };
 
 enum GroupMode { GRP_DENSE = 0, GRP_CONTIG = 1, GRP_MASKED = 2 };
@@ -67,6 +71,11 @@ int pipe_stages_b(int bm, int bn, int group);
 int pipe_lds_bytes(int bm, int bn, int sf_mode, int group);
 hipError_t launch_pipe(const GemmParams& p, int bm, int bn, int sf_mode, int group, int out, int grid,
                        hipStream_t stream);
+// (dg_gemm_pipe.hip is compiled in parts, one per group of instantiations)
+hipError_t launch_pipe_dense(const GemmParams& p, int bm, int bn, int sf_mode, int out, int grid, hipStream_t s);
+hipError_t launch_pipe_contig(const GemmParams& p, int bm, int bn, int sf_mode, int out, int grid, hipStream_t s);
+hipError_t launch_pipe_masked(const GemmParams& p, int bm, int bn, int sf_mode, int out, int grid, hipStream_t s);
+hipError_t launch_pipe_fp4(const GemmParams& p, int bm, int bn, int group, int out, int grid, hipStream_t s);
 
 hipError_t launch_cast(const void* x, int64_t ldx, bool bf16, uint8_t* q, int64_t ldq, void* sf, int64_t sf_stride,
                        bool ue8m0, int m, int k, hipStream_t stream);

@@ -150,6 +150,67 @@ int dg_m_grouped_fp8_gemm_nt_masked(int32_t num_groups, int32_t m_max, int32_t n
                                     hipStream_t stream);
 
 /*
+ * FP8 activations x FP4 weights (page "第13章 DeepGEMM" §13.1: the V4 routed-expert recipe,
+ * FP8 activations and FP4 weights with one weight scale per 32 K elements; §13.5: the FP4
+ * weights go into the MMA next to the FP8 activations and the power-of-two scales are applied
+ * inside it; page "02 · DeepGEMM 技术解析" §3.1: UE8M0 scales packed four per int32):
+ *
+ *   D[i, j] = C[i, j] + sum_b sa[i, b] * sum_{t=0..3} sb[j, 4b+t] * sum_{k in K [128b+32t, +32)} A[i, k] * B[j, k]
+ *
+ *  m, n, k      : k % 128 == 0 and k >= 256 (two K blocks; DG_ERR_UNSUPPORTED below); m, n >= 0
+ *                 (m == 0 or n == 0 is a no-op).
+ *  a, lda       : A E4M3 [m, k] as in dg_fp8_gemm_nt.
+ *  sfa, sfa_stride : UE8M0 activation scales, one per row and 128-long K block, packed four per
+ *                 int32 and MN-major exactly as dg_fp8_gemm_nt's DG_SF_UE8M0X4 sfa
+ *                 (word (i, q) at sfa[q*sfa_stride + i], byte t = K block 4q+t); sfa_stride == align4(m).
+ *  b, ldb       : B E2M1 (FP4: 1 sign, 2 exponent, 1 mantissa bit; values 0, 0.5, 1, 1.5, 2, 3, 4, 6
+ *                 and their negatives) [n, k], two codes per byte: element (j, kk) is the low nibble
+ *                 of byte b[j*ldb + kk/2] for even kk and its high nibble for odd kk.  ldb (BYTES)
+ *                 >= k/2, ldb % 16 == 0, < 2^23; b 16-byte aligned.
+ *  sfb, sfb_stride : UE8M0 weight scales, one per row and 32-long K group: int32 word (j, b) at
+ *                 sfb[b*sfb_stride + j] holds row j's four codes of K block b, byte t for K
+ *                 [128b + 32t, +32) (dg_transform_sf with sf_k = k/32 and pack_ue8m0 = 1 produces
+ *                 this layout from FP32 per-32 scales); sfb_stride == align4(n).  16-byte aligned.
+ *                 A code c stands for 2^(c - 127).
+ *  c, ldc, d, ldd, d_dtype : as in dg_fp8_gemm_nt (C only with FP32 D; C may alias D).
+ * Returns DG_OK or a negative dg_status.
+ */
+int dg_fp8_fp4_gemm_nt(int32_t m, int32_t n, int32_t k,
+                       const void* a, int64_t lda, const void* sfa, int64_t sfa_stride,
+                       const void* b, int64_t ldb, const void* sfb, int64_t sfb_stride,
+                       const float* c, int64_t ldc,
+                       void* d, int64_t ldd, int32_t d_dtype,
+                       hipStream_t stream);
+
+/*
+ * M-grouped contiguous FP8 x FP4 GEMM (page "第13章 DeepGEMM" §13.6, the MoE prefill form with
+ * FP4 expert weights): rows grouped as in dg_m_grouped_fp8_gemm_nt_contiguous; operands and
+ * scales as in dg_fp8_fp4_gemm_nt; group g's packed weights start at b + g*b_group_stride
+ * (bytes) and its scale words at sfb + g*sfb_group_stride (>= (k/128)*sfb_stride).  BF16 D only.
+ */
+int dg_m_grouped_fp8_fp4_gemm_nt_contiguous(int32_t m_total, int32_t n, int32_t k, int32_t num_groups,
+                                            const void* a, int64_t lda, const void* sfa, int64_t sfa_stride,
+                                            const void* b, int64_t ldb, int64_t b_group_stride,
+                                            const void* sfb, int64_t sfb_stride, int64_t sfb_group_stride,
+                                            void* d, int64_t ldd, int32_t d_dtype,
+                                            const int32_t* grouped_layout, hipStream_t stream);
+
+/*
+ * M-grouped masked FP8 x FP4 GEMM (page "02 · DeepGEMM 技术解析" §5.2; page "第13章 DeepGEMM"
+ * §13.6, the decode form): groups and masked_m as in dg_m_grouped_fp8_gemm_nt_masked;
+ * operands and scales as in dg_fp8_fp4_gemm_nt, per group (sfa_group_stride >=
+ * ceil(k/512)*sfa_stride, sfb_group_stride >= (k/128)*sfb_stride).  BF16 D only.
+ */
+int dg_m_grouped_fp8_fp4_gemm_nt_masked(int32_t num_groups, int32_t m_max, int32_t n, int32_t k,
+                                        const void* a, int64_t lda, int64_t a_group_stride,
+                                        const void* sfa, int64_t sfa_stride, int64_t sfa_group_stride,
+                                        const void* b, int64_t ldb, int64_t b_group_stride,
+                                        const void* sfb, int64_t sfb_stride, int64_t sfb_group_stride,
+                                        void* d, int64_t ldd, int64_t d_group_stride, int32_t d_dtype,
+                                        const int32_t* masked_m, int32_t expected_m,
+                                        hipStream_t stream);
+
+/*
  * K-grouped contiguous GEMM, the MoE weight-gradient form (page "02 · DeepGEMM 技术解析" §3.3:
  * groups concatenated along K, two-dimensional [sum_sf_k, mn] FP32 scales, mn % 4 == 0, C
  * required and best passed as D itself; page "第13章 DeepGEMM" §13.6 and §13.13: M and N

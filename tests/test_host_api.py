@@ -218,3 +218,43 @@ def test_raw_weight_scale_granularity():
     assert dg._raw_gran(100, 100) == 1
     assert dg._raw_gran(200, 200) == 1
     assert dg._raw_gran(1, 1) == 1          # one row either way: the broadcast is the same
+
+
+def _fp4(**kw):
+    args = dict(m=64, n=128, k=256, a=P, lda=256, sfa=P, sfa_stride=64, b=P, ldb=128, sfb=P, sfb_stride=128,
+                c=None, ldc=0, d=P, ldd=128, d_dtype=1, stream=None)
+    args.update(kw)
+    return dg.lib().dg_fp8_fp4_gemm_nt(*args.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(k=128), DG_ERR_UNSUPPORTED),          # the pipelined kernel needs two K blocks
+    (dict(k=200), DG_ERR_SHAPE),
+    (dict(d_dtype=5), DG_ERR_DTYPE),
+    (dict(b=None), DG_ERR_NULL),
+    (dict(ldb=96), DG_ERR_LAYOUT),              # < k / 2 bytes
+    (dict(ldb=136), DG_ERR_LAYOUT),             # not a multiple of 16
+    (dict(sfb_stride=130), DG_ERR_LAYOUT),      # per-row words, stride align4(n)
+    (dict(sfa_stride=68), DG_ERR_LAYOUT),
+    (dict(c=P, ldc=128), DG_ERR_UNSUPPORTED),   # C with a BF16 output
+    (dict(b=P_MIS), DG_ERR_LAYOUT),
+])
+def test_fp8_fp4_validation(kw, code):
+    assert _fp4(**kw) == code
+    assert dg.lib().dg_get_last_error() != b""
+
+
+def test_fp8_fp4_grouped_validation():
+    lib = dg.lib()
+    # contiguous: FP32 output is not offered, a NULL layout is an error
+    args = [256, 128, 256, 2, P, 256, P, 256, P, 128, 128 * 128, P, 128, 2 * 128, P, 128, 2, P, None]
+    assert lib.dg_m_grouped_fp8_fp4_gemm_nt_contiguous(*args) == DG_ERR_UNSUPPORTED
+    args[16] = 1
+    args[17] = None
+    assert lib.dg_m_grouped_fp8_fp4_gemm_nt_contiguous(*args) == DG_ERR_NULL
+    # masked: too small a weight-scale group stride
+    margs = [2, 64, 128, 256, P, 256, 64 * 256, P, 64, 64, P, 128, 128 * 128, P, 128, 128, P, 128, 64 * 128, 1, P,
+             32, None]
+    assert lib.dg_m_grouped_fp8_fp4_gemm_nt_masked(*margs) == DG_ERR_LAYOUT
+    # empty problems are no-ops
+    assert _fp4(m=0, sfa_stride=0) == DG_OK
