@@ -34,8 +34,41 @@ def _run(cmd):
     return "\n".join(lines)
 
 
+# Pipelined instantiations that only a forced tile reaches (the planner never picks them):
+# the 256-row tiles with FP32 + C output, which spill to scratch.
+FORCED_ONLY = ("pipe_kernelILi256ELi224ELi4ELi2ELi0ELi2ELi0ELi2E", "pipe_kernelILi256ELi192ELi4ELi2ELi0ELi2ELi0ELi2E")
+
+
+def parse_resource_usage(text):
+    """Per-kernel figures from hipcc's -Rpass-analysis=kernel-resource-usage remarks."""
+    import re
+    rows, cur = [], None
+    keys = {"VGPRs": "vgpr", "AGPRs": "agpr", "ScratchSize [bytes/lane]": "scratch", "SGPRs Spill": "sgpr_spill",
+            "VGPRs Spill": "vgpr_spill", "Occupancy [waves/SIMD]": "occupancy", "LDS Size [bytes/block]": "lds"}
+    for line in text.splitlines():
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            cur = {"name": m.group(1)}
+            rows.append(cur)
+            continue
+        if cur is None:
+            continue
+        for k, short in keys.items():
+            m = re.search(re.escape(k) + r": (\d+)", line)
+            if m and short not in cur:
+                cur[short] = int(m.group(1))
+    return rows
+
+
+def _check_scratch(reports):
+    bad = [r["name"] for r in reports if r.get("scratch", 0) > 0 and not any(f in r["name"] for f in FORCED_ONLY)]
+    if bad:
+        raise RuntimeError("kernels the planner can pick use scratch memory (register spills): " + ", ".join(bad))
+
+
 def build(verbose=False, jobs=None):
-    """Compile every HIP source for gfx950 and link libdg.so.  Always rebuilds."""
+    """Compile every HIP source for gfx950 and link libdg.so.  Always rebuilds.  Fails if a
+    pipelined kernel the planner can pick spills registers to scratch."""
     bdir = os.path.join(HERE, "_build")
     os.makedirs(bdir, exist_ok=True)
     steps = []
@@ -48,10 +81,13 @@ def build(verbose=False, jobs=None):
     # being copied out of accumulation registers (matters for the 4-wave tiles, whose
     # operands spill into AGPRs)
     for part in range(PIPE_PARTS):
-        steps.append([HIPCC, *FLAGS, "-mllvm", "-amdgpu-mfma-vgpr-form", f"-DDG_PIPE_PART={part}", "-c",
+        steps.append([HIPCC, *FLAGS, "-mllvm", "-amdgpu-mfma-vgpr-form", f"-DDG_PIPE_PART={part}",
+                      "-Rpass-analysis=kernel-resource-usage", "-c",
                       os.path.join(CSRC, "dg_gemm_pipe.hip"), "-o", os.path.join(bdir, f"dg_gemm_pipe_p{part}.o")])
     steps.append([HIPCC, *FLAGS, "-c", os.path.join(CSRC, "dg_gemm_pipe.hip"),
                   "-o", os.path.join(bdir, "dg_gemm_pipe_dispatch.o")])
+    steps.append([HIPCC, *FLAGS, "-Rpass-analysis=kernel-resource-usage", "-c", os.path.join(CSRC, "dg_gemm_skinny.hip"),
+                  "-o", os.path.join(bdir, "dg_gemm_skinny.o")])
     steps.append([HIPCC, *FLAGS, "-c", os.path.join(CSRC, "dg_transform.hip"),
                   "-o", os.path.join(bdir, "dg_transform.o")])
     steps.append([HIPCC, *FLAGS, "-c", os.path.join(CSRC, "dg_quant.hip"),
@@ -59,10 +95,16 @@ def build(verbose=False, jobs=None):
     steps.append([HIPCC, "-O2", "-std=c++20", "-fPIC", f"--offload-arch={ARCH}", "-c", os.path.join(CSRC, "dg_api.cpp"),
                   "-o", os.path.join(bdir, "dg_api.o")])
     jobs = jobs or min(16, os.cpu_count() or 4)
+    reports = []
     with ThreadPoolExecutor(max_workers=jobs) as ex:
-        for out in ex.map(_run, steps):
-            if verbose and out:
+        for step, out in zip(steps, ex.map(_run, steps)):
+            if "-Rpass-analysis=kernel-resource-usage" in step:
+                reports += parse_resource_usage(out)
+            elif verbose and out:
                 print(out)
+    _check_scratch(reports)
+    global LAST_RESOURCE_USAGE
+    LAST_RESOURCE_USAGE = reports
     objs = [s[-1] for s in steps]   # (stale objects left in _build are not linked)
     tmp = OUT + ".tmp"
     _run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs])
@@ -78,6 +120,32 @@ def clean():
         os.remove(OUT)
 
 
+LAST_RESOURCE_USAGE = []
+
+_SF = {0: "1d2d FP32", 2: "UE8M0", 3: "FP4 weights"}
+_OUT = {0: "BF16", 1: "FP32", 2: "FP32+C"}
+_GRP = {0: "dense", 1: "contiguous", 2: "masked"}
+
+
+def resource_table(reports):
+    """One line per pipelined instantiation: tile, waves, scales, output, registers, scratch."""
+    import re
+    lines = []
+    for r in reports:
+        m = re.search(r"pipe_kernelILi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)E", r["name"])
+        if not m:
+            continue
+        bm, bn, wm, wn, sf, out, grp, nb = map(int, m.groups())
+        forced = any(f in r["name"] for f in FORCED_ONLY)
+        lines.append(f"{_GRP[grp]:10s} {bm}x{bn} {wm * wn} waves {_SF[sf]:11s} {_OUT[out]:6s} B stages {nb}: "
+                     f"VGPR {r.get('vgpr', 0):3d} AGPR {r.get('agpr', 0):3d} scratch {r.get('scratch', 0):3d} B/lane "
+                     f"SGPR spills {r.get('sgpr_spill', 0):2d} waves/SIMD {r.get('occupancy', 0)} LDS {r.get('lds', 0)}"
+                     + ("   (forced tiles only)" if forced else ""))
+    return lines
+
+
 if __name__ == "__main__":
-    build(verbose=True)
+    build(verbose="--resource-report" not in sys.argv)
+    if "--resource-report" in sys.argv:
+        print("\n".join(resource_table(LAST_RESOURCE_USAGE)))
     sys.exit(0)

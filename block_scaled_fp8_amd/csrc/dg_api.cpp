@@ -82,6 +82,9 @@ Plan plan_gemm(int kind, int m, int n, int k, int groups, int m_max, int sfm, in
     const dg::TileCfg& c = dg::kTiles[t];
     if (!dg::gemm_instantiated(t, sfm, kind, out)) continue;
     if (fbm && (c.bm != fbm || c.bn != fbn)) continue;
+    // the 256-row pipelined tiles (1d2d scales) run out of registers with FP32 + C output
+    // (the compiler spills them to scratch); they stay reachable only when forced
+    if (!fbm && kind == 0 && out == dg::OUT_F32_C && sfm == dg::SF_1D2D_F32 && c.bm > 128) continue;
     const int64_t mt = (kind == 2) ? (m + c.bm - 1) / c.bm : (m + c.bm - 1) / c.bm;
     const int64_t nt = (n + c.bn - 1) / c.bn;
     const int64_t tiles = (kind == 2) ? int64_t(groups) * mt * nt : mt * nt;
@@ -182,6 +185,17 @@ int do_launch(dg::GemmParams& p, int kind, int32_t m_rows_for_plan, int32_t m_ma
   p.d_vec = (p.ldd % 4 == 0 && (p.d_gstride * esz) % 16 == 0 && aligned16(p.d)) ? 1 : 0;
   p.c_vec = (p.c && p.ldc % 4 == 0 && aligned16(p.c)) ? 1 : 0;
   p.d_vec16 = ((p.ldd * esz) % 16 == 0 && (p.d_gstride * esz) % 16 == 0 && aligned16(p.d)) ? 1 : 0;
+  // decode-shaped dense problems (at most 64 rows, 1d2d scales) stream B with the skinny
+  // kernel: 16 or 32 columns per workgroup, so the grid covers the chip
+  if (kind == dg::GRP_DENSE && p.m <= 64 && sfm == dg::SF_1D2D_F32 && !getenv("DG_FORCE_TILE") && !env_int("DG_NO_SKINNY", 0)) {
+    // (32 columns measured faster than 16 at n = 7168 even with 224 workgroups on 256 CUs: every
+    // workgroup reads all of A, which is most of its traffic; 16 only when 32 leaves most CUs idle)
+    const int bn = env_int("DG_SKINNY_BN", 2 * ((p.n + 31) / 32) >= num_sms ? 32 : 16);
+    if (env_int("DG_PRINT_CONFIGS", 0)) fprintf(stderr, "[dg] skinny kernel bn=%d grid=%d\n", bn, (p.n + bn - 1) / bn);
+    const hipError_t e = dg::launch_skinny(p, bn, out, stream);
+    if (e != hipSuccess) return fail(DG_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+  }
   if (env_int("DG_PRINT_CONFIGS", 0))
     fprintf(stderr, "[dg] kind=%d m=%d n=%d k=%d groups=%d sf_mode=%d out=%d -> tile %dx%d (waves %dx%d) tiles=%d grid=%d swizzle_m=%d\n",
             kind, p.m, p.n, p.k, p.num_groups, sfm, out, c.bm, c.bn, c.wm, c.wn, p.total_tiles, pl.grid,

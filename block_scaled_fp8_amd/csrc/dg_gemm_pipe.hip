@@ -118,6 +118,14 @@ __device__ __forceinline__ void pin(float (&f)[4]) {
   asm volatile("" : "+v"(f[0]), "+v"(f[1]), "+v"(f[2]), "+v"(f[3]));
 }
 
+// A copy of v that the compiler cannot compute earlier: per-lane values derived from it stay
+// where they are used (the epilogue) instead of being hoisted to the kernel start and held
+// in registers through the whole main loop.
+__device__ __forceinline__ int fresh(int v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
 // Wait until at most N vector-memory operations of this wave are outstanding.
 template <int N>
 __device__ __forceinline__ void wait_vm() {
@@ -722,6 +730,8 @@ struct Kernel {
   static_assert(STORES_T < STORES_N && STORES_N < 64, "vmcnt is a 6-bit field; the two store counts must differ");
 
   __device__ __forceinline__ int epilogue(const float (&fin)[FM][FN][4], const TilePos& tr, int aslot) const {
+    const int ln = fresh(lane);
+    const int lr = ln & 15, lg = ln >> 4;  // (shadow the members: see fresh)
     const bool interior = tr.m0 + BM <= tr.mv && tr.n0 + BN <= p.n && !(GRP == GRP_CONTIG && tr.chk);
     const int esz = (OUT == OUT_BF16) ? 2 : 4;
     char* Dg = (char*)p.d;
@@ -743,7 +753,7 @@ struct Kernel {
           }
 #pragma unroll
           for (int k = 0; k < RD; ++k) {
-            const int cidx = lane + 64 * k;
+            const int cidx = ln + 64 * k;
             const int r = cidx / CH, cc = cidx - r * CH;
             if (cidx < 16 * CH && (ALL || 16 * i + r < rows)) {
               const v4i x = *(const v4i*)(smem + scr + r * RS + cc * 16);
@@ -764,6 +774,9 @@ struct Kernel {
     const int nw0 = tr.n0 + wn * TN;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
+      // (one fragment row at a time: batching every row's C loads ahead of the adds would
+      // hold a second tile of values in registers)
+      __builtin_amdgcn_sched_barrier(0);
       const int row = row0 + 16 * i;
       if (row >= tr.mv) continue;
       if (GRP == GRP_CONTIG && tr.chk && p.grouped_layout[row] != tr.g) continue;

@@ -77,6 +77,10 @@ hipError_t launch_pipe_contig(const GemmParams& p, int bm, int bn, int sf_mode, 
 hipError_t launch_pipe_masked(const GemmParams& p, int bm, int bn, int sf_mode, int out, int grid, hipStream_t s);
 hipError_t launch_pipe_fp4(const GemmParams& p, int bm, int bn, int group, int out, int grid, hipStream_t s);
 
+// Skinny kernel (dg_gemm_skinny.hip): dense problems with 1 <= m <= 64 rows and 1d2d FP32
+// scales, bn (16 or 32) columns per workgroup, the workgroup's waves splitting K.
+hipError_t launch_skinny(const GemmParams& p, int bn, int out, hipStream_t stream);
+
 hipError_t launch_cast(const void* x, int64_t ldx, bool bf16, uint8_t* q, int64_t ldq, void* sf, int64_t sf_stride,
                        bool ue8m0, int m, int k, hipStream_t stream);
 

@@ -796,3 +796,36 @@ def test_ue8m0_code_zero_is_two_to_the_minus_127():
     nz = o[:8] != 0
     assert nz.any() and (got[:8][nz] != 0).all()      # scaled by 2^-127, not dropped
     assert np.array_equal(got.astype(np.float64), o)  # and exactly so
+
+
+@contextlib.contextmanager
+def env_var(name, value):
+    old = os.environ.get(name)
+    os.environ[name] = str(value)
+    try:
+        yield
+    finally:
+        if old is None:
+            os.environ.pop(name, None)
+        else:
+            os.environ[name] = old
+
+
+@pytest.mark.parametrize("bn", [16, 32])
+@pytest.mark.parametrize("shape", [(1, 300, 128), (5, 100, 256), (17, 520, 2048), (64, 1000, 1152), (33, 7, 384)])
+def test_skinny_decode_shapes(bn, shape):
+    """Dense problems with at most 64 rows run the skinny kernel (each workgroup's waves split
+    K and add their partial sums at the end): ragged m and n (n below one column block too),
+    K from one block up, both column widths, BF16, FP32 and FP32 + C, with sentinels around D."""
+    M, N, K = shape
+    p = gen.dense(M, N, K, seed=M * 7 + N + K, with_c=True)
+    for out, with_c in ((torch.bfloat16, False), (torch.float32, False), (torch.float32, True)):
+        say("skinny", shape, bn, out, with_c)
+        big = torch.full((M, N + 12), float("nan"), dtype=out, device=DEV)
+        d = big[:, :N]
+        c = cuda(p["c"]) if with_c else None
+        with env_var("DG_SKINNY_BN", bn):
+            dg.fp8_gemm_nt((cuda(p["a"]), cuda(p["sa"])), (cuda(p["b"]), cuda(p["sb"])), d, c=c)
+        torch.cuda.synchronize()
+        st = check_dense(p, d, with_c=with_c, name=f"skinny {shape} {bn}")
+        assert torch.isnan(big[:, N:].float()).all()
