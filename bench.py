@@ -8,15 +8,28 @@ One step = the whole hot path on one batch: the activation-scale transform
 (dg_transform_sf: FP32 K-major -> MN-major) followed by the GEMM (persistent
 tile scheduling, LDS staging, FP8 MFMA, per-128-K promotion, BF16 epilogue).
 Inputs are resident in HBM before timing starts; each step uses the next of
-several input/output buffer sets (together larger than the 256 MB MALL) so no
-step reads data the previous step left in cache.
+several input/output buffer sets so no step reads data the previous step left
+in the caches.  --workload picks the other workloads (grouped, decode, FP8 x FP4,
+K-grouped, the activation cast).
+
+Timing: W untimed warm-up steps, then exactly K timed steps between two device
+synchronisations (wall clock -> "value").  The dominant kernel's launch duration
+comes from HIP events on the stream it is launched on: per launch (mean, median,
+min) when the host keeps ahead of the GPU, or, for kernels shorter than the
+binding's host time per call (decode, cast), from a captured graph of K launches
+replayed between two events (mean launch period, gaps between launches
+included).  After the timed region a sustained run samples the GPU clock and
+socket power with amd-smi, and a device-to-device copy of 1 GiB measures the
+practical HBM ceiling.
 
 Prints one JSON line (see the "roofline" and "cpu_baseline" objects).
 """
 import argparse
 import json
 import os
+import subprocess
 import sys
+import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -27,47 +40,31 @@ import torch  # noqa: E402
 
 PEAK_FP8_TFLOPS = 5000.0      # MI355X dense FP8 MFMA, published
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, published
+NOMINAL_SCLK_MHZ = 2400.0     # the clock the published peaks assume
 
 WORKLOADS = {
     "dense_4096x7168x2048": dict(kind="dense", M=4096, N=7168, K=2048),
-    "dense_64x7168x2048": dict(kind="dense", M=64, N=7168, K=2048),
+    "dense_64x7168x2048": dict(kind="dense", M=64, N=7168, K=2048, graph=True),
     "dense_c_4096x1536x7168": dict(kind="dense_c", M=4096, N=1536, K=7168),
     "masked_32x256x7168x2048": dict(kind="masked"),
     "contiguous_32x4096x7168": dict(kind="contig"),
-    "cast_4096x7168_bf16": dict(kind="cast", M=4096, K=7168),
-    "cast_ue8m0_4096x7168_bf16": dict(kind="cast", M=4096, K=7168, ue8m0=True),
+    "fp8_fp4_dense_4096x7168x2048": dict(kind="fp4_dense", M=4096, N=7168, K=2048),
+    "fp8_fp4_masked_32x256x7168x2048": dict(kind="fp4_masked"),
+    "cast_4096x7168_bf16": dict(kind="cast", M=4096, K=7168, graph=True),
+    "cast_ue8m0_4096x7168_bf16": dict(kind="cast", M=4096, K=7168, ue8m0=True, graph=True),
     # MoE weight gradient: 8 experts' token counts (multiples of 128, 16384 in all) split K
     "k_grouped_8x7168x2048_k16384": dict(kind="k_grouped", M=7168, N=2048,
                                          ks=[1792, 2304, 2048, 1536, 2560, 2048, 1920, 2176]),
 }
 DEFAULT = "dense_4096x7168x2048"
+HEADLINE_METRIC = "TFLOP/s + % FP8 MFMA peak, block-scaled FP8 GEMM M=4096 N=7168 K=2048"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
+GEMM_SOURCES = ("dg_gemm.hip", "dg_gemm_pipe.hip", "dg_gemm_skinny.hip", "dg_internal.h")
+CAST_SOURCES = ("dg_quant.hip", "dg_internal.h")
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
-
-
-GEMM_SOURCES = ("dg_gemm.hip", "dg_gemm_pipe.hip", "dg_internal.h")
-CAST_SOURCES = ("dg_quant.hip", "dg_internal.h")
-
-
-def read_traffic(workload, hash_key="kernel_source_sha1", sources=GEMM_SOURCES):
-    """HBM bytes per launch of the timed kernel from the committed rocprofv3 counter summary,
-    or None if absent or taken from an older kernel build."""
-    if not os.path.exists(TRAFFIC_FILE):
-        return None
-    vals = {}
-    for line in open(TRAFFIC_FILE):
-        line = line.strip()
-        if line and not line.startswith("#") and "=" in line:
-            k, v = line.split("=", 1)
-            vals[k.strip()] = v.strip()
-    key = f"{workload}.bytes_per_launch"
-    src_hash = vals.get(hash_key)
-    if key not in vals or src_hash != kernel_source_hash(sources):
-        return None
-    return float(vals[key])
 
 
 def kernel_source_hash(sources=GEMM_SOURCES):
@@ -79,26 +76,363 @@ def kernel_source_hash(sources=GEMM_SOURCES):
     return h.hexdigest()
 
 
-def make_dense(spec, nsets, dev):
+def read_traffic(workload, hash_key="kernel_source_sha1", sources=GEMM_SOURCES):
+    """HBM bytes per launch of the timed kernel from the committed rocprofv3 counter summary,
+    or None if absent or taken from another kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals = {}
+    for line in open(TRAFFIC_FILE):
+        line = line.strip()
+        if line and not line.startswith("#") and "=" in line:
+            k, v = line.split("=", 1)
+            vals[k.strip()] = v.strip()
+    key = f"{workload}.bytes_per_launch"
+    if key not in vals or vals.get(hash_key) != kernel_source_hash(sources):
+        return None
+    return float(vals[key])
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return int(max([i.get("num_threads", 1) for i in threadpool_info()] or [1]))
+    except Exception:
+        return os.cpu_count()
+
+
+class Workload:
+    """What one benchmark line measures: step i is ``pre(i)`` (work queued before the dominant
+    kernel, if any) then ``launch(i)`` (the dominant kernel) on the current stream; ``work``
+    is the metric's numerator per step (FLOPs or bytes)."""
+
+    def __init__(self, **kw):
+        self.pre = None
+        self.__dict__.update(kw)
+
+    def step(self, i):
+        if self.pre is not None:
+            self.pre(i)
+        self.launch(i)
+
+
+# ---------------------------------------------------------------- workloads
+def w_dense(spec, dg, dev):
     from tests import gen
     M, N, K = spec["M"], spec["N"], spec["K"]
-    p = gen.dense(M, N, K, seed=0, with_c=spec["kind"] == "dense_c")
-    out_dtype = torch.float32 if spec["kind"] == "dense_c" else torch.bfloat16
+    with_c = spec["kind"] == "dense_c"
+    p = gen.dense(M, N, K, seed=0, with_c=with_c)
+    out_dtype = torch.float32 if with_c else torch.bfloat16
+    nsets = 8 if M * K + N * K < 256 << 20 else 2
     sets = []
     for _ in range(nsets):
         s = dict(a=torch.from_numpy(p["a"]).to(dev), b=torch.from_numpy(p["b"]).to(dev),
                  sa_raw=torch.from_numpy(p["sa"]).to(dev), sb=torch.from_numpy(p["sb"]).to(dev),
                  d=torch.empty((M, N), dtype=out_dtype, device=dev))
-        if p["c"] is not None:
+        s["sa"] = dg.get_mn_major_tma_aligned_tensor(s["sa_raw"])
+        if with_c:
             s["c"] = torch.from_numpy(p["c"]).to(dev)
         sets.append(s)
-    flops = 2.0 * M * N * K
     esz = 2 if out_dtype == torch.bfloat16 else 4
     sf_k = K // 128
-    alg_bytes = M * K + N * K + 4 * M * sf_k + 4 * ((N + 127) // 128) * sf_k + esz * M * N
-    if p["c"] is not None:
-        alg_bytes += 4 * M * N
-    return p, sets, flops, alg_bytes
+    alg_bytes = M * K + N * K + 4 * M * sf_k + 4 * ((N + 127) // 128) * sf_k + esz * M * N + (4 * M * N if with_c else 0)
+    flops = 2.0 * M * N * K
+
+    def pre(i):
+        # path A: the activation scales are transformed on every call, and the GEMM reads them
+        s = sets[i % nsets]
+        s["sa_step"] = dg.get_mn_major_tma_aligned_tensor(s["sa_raw"])
+
+    def launch(i):
+        s = sets[i % nsets]
+        dg.fp8_gemm_nt((s["a"], s.get("sa_step", s["sa"])), (s["b"], s["sb"]), s["d"], c=s.get("c"))
+
+    def cpu(seconds):
+        import oracle
+        rows = max(1, min(M, 64))
+        t0 = time.perf_counter()
+        oracle.gemm_nt(p["a"][:rows], p["sa"][:rows], p["b"], p["sb"], 128, c=None if p["c"] is None else p["c"][:rows])
+        t = time.perf_counter() - t0
+        if t < seconds / 4 and rows < M:
+            rows = int(min(M, max(rows, rows * seconds / max(t, 1e-3))))
+            rows = max(8, rows - rows % 8)
+            t0 = time.perf_counter()
+            oracle.gemm_nt(p["a"][:rows], p["sa"][:rows], p["b"], p["sb"], 128,
+                           c=None if p["c"] is None else p["c"][:rows])
+            t = time.perf_counter() - t0
+        bound_work = 2.0 * rows * N * K if not spec.get("graph") else alg_bytes * rows / M
+        return bound_work / t, t, f"rows 0..{rows - 1} of the {M}x{N}x{K} problem (all N columns, full K), float64 numpy"
+
+    skinny = M <= 64
+    kernel = "dg::skinny::skinny_kernel" if skinny else "dg::pipe::pipe_kernel"
+    hbm = skinny
+    return Workload(pre=pre, launch=launch, work=alg_bytes if hbm else flops, flops=flops, alg_bytes=alg_bytes,
+                    bound="hbm" if hbm else "mfma", kernel=kernel, cpu=cpu,
+                    config={"workload": None, "M": M, "N": N, "K": K, "out": "fp32+C" if with_c else "bf16",
+                            "scales": "fp32 1x128 act, 128x128 weight",
+                            "step": "transform_sf(act scales) + gemm", "buffer_sets": nsets})
+
+
+def w_masked(spec, dg, dev, fp4=False):
+    from tests import gen
+    import oracle
+    if fp4:
+        p = gen.fp8_fp4_grouped_masked(32, 256, 7168, 2048, seed=0)
+    else:
+        p = gen.config5()
+    G, Mmax, N, K = 32, 256, 7168, 2048
+    a = torch.from_numpy(p["a"]).to(dev)
+    b = torch.from_numpy(p["b"]).to(dev)
+    mm = torch.from_numpy(p["masked_m"]).to(dev)
+    d = torch.empty((G, Mmax, N), dtype=torch.bfloat16, device=dev)
+    pk = (K // 128 + 3) // 4
+    valid = int(np.clip(p["masked_m"], 0, Mmax).sum())
+    active = int((p["masked_m"] > 0).sum())
+    if fp4:
+        sa = dg.transform_sf(torch.from_numpy(p["sa"]).to(dev), Mmax, 1, True)
+        sb = dg.transform_sf(torch.from_numpy(p["sb"]).to(dev), N, 1, True)
+        w_bytes = N * K // 2 + 4 * N * (K // 128)
+
+        def launch(i):
+            dg.m_grouped_fp8_fp4_gemm_nt_masked((a, sa), (b, sb), d, mm, expected_m=128)
+    else:
+        sa = dg.get_mn_major_tma_aligned_packed_ue8m0_tensor(torch.from_numpy(p["sa"]).to(dev))
+        sb = dg.get_mn_major_tma_aligned_packed_ue8m0_tensor(torch.from_numpy(p["sb"]).to(dev), gran_mn=128, mn=N)
+        w_bytes = N * K + 4 * N * pk
+
+        def launch(i):
+            dg.m_grouped_fp8_gemm_nt_masked((a, sa), (b, sb), d, mm, expected_m=128)
+    alg_bytes = active * w_bytes + valid * (K + 4 * pk + 2 * N) + 4 * G
+    flops = 2.0 * valid * N * K
+
+    def cpu(seconds):
+        gs = [g for g in range(G) if p["masked_m"][g] > 0][:4]
+        t0 = time.perf_counter()
+        for g in gs:
+            m = int(p["masked_m"][g])
+            if fp4:
+                oracle.gemm_fp8_fp4_nt(p["a"][g, :m], p["sa"][g, :m], p["b"][g], p["sb"][g])
+            else:
+                oracle.gemm_nt(p["a"][g, :m], p["sa"][g, :m], p["b"][g], p["sb"][g], 128)
+        t = time.perf_counter() - t0
+        rows = int(sum(p["masked_m"][g] for g in gs))
+        by = len(gs) * w_bytes + rows * (K + 4 * pk + 2 * N)
+        return by / t, t, f"groups {gs} of the seed-0 draw ({rows} valid rows, their whole weights), float64 numpy"
+
+    return Workload(launch=launch, work=alg_bytes, flops=flops, alg_bytes=alg_bytes, bound="hbm",
+                    kernel="dg::pipe::pipe_kernel (masked)", cpu=cpu,
+                    config={"workload": None, "groups": G, "m_max": Mmax, "N": N, "K": K, "valid_rows": valid,
+                            "weights": "fp4 e2m1, ue8m0 per 1x32" if fp4 else "fp8 e4m3, ue8m0 per 128x128",
+                            "scales": "ue8m0 packed x4, mn-major", "out": "bf16",
+                            "step": "gemm (scales pre-packed, as the cast emits them)"})
+
+
+def w_contig(spec, dg, dev):
+    from tests import gen
+    import oracle
+    p = gen.config4()
+    G, N, K = p["G"], p["N"], p["K"]
+    a = torch.from_numpy(p["a"]).to(dev)
+    b = torch.from_numpy(p["b"]).to(dev)
+    sa = dg.get_mn_major_tma_aligned_tensor(torch.from_numpy(p["sa"]).to(dev))
+    sb = torch.from_numpy(p["sb"]).to(dev)
+    lay = torch.from_numpy(p["layout"]).to(dev)
+    d = torch.empty((p["M"], N), dtype=torch.bfloat16, device=dev)
+    flops = 2.0 * p["M"] * N * K
+    alg_bytes = G * N * K + p["M"] * K + 2 * p["M"] * N
+
+    def launch(i):
+        dg.m_grouped_fp8_gemm_nt_contiguous((a, sa), (b, sb), d, lay)
+
+    def cpu(seconds):
+        rows = np.arange(0, p["M"], max(1, p["M"] // 96))
+        t0 = time.perf_counter()
+        oracle.grouped_contiguous(p["a"][rows], p["sa"][rows], p["b"], p["sb"], p["layout"][rows])
+        t = time.perf_counter() - t0
+        return 2.0 * len(rows) * N * K / t, t, f"{len(rows)} evenly spaced rows (every group's weights), float64 numpy"
+
+    return Workload(launch=launch, work=flops, flops=flops, alg_bytes=alg_bytes, bound="mfma",
+                    kernel="dg::pipe::pipe_kernel (contiguous)", cpu=cpu,
+                    config={"workload": None, "groups": G, "rows": p["M"], "N": N, "K": K, "out": "bf16",
+                            "scales": "fp32 1x128 act, 128x128 weight"})
+
+
+def w_fp4_dense(spec, dg, dev):
+    from tests import gen
+    import oracle
+    M, N, K = spec["M"], spec["N"], spec["K"]
+    p = gen.fp8_fp4(M, N, K, seed=0)
+    sets = []
+    for _ in range(8):
+        sets.append(dict(a=torch.from_numpy(p["a"]).to(dev), b=torch.from_numpy(p["b"]).to(dev),
+                         sa=dg.transform_sf(torch.from_numpy(p["sa"]).to(dev), M, 1, True),
+                         sb=dg.transform_sf(torch.from_numpy(p["sb"]).to(dev), N, 1, True),
+                         d=torch.empty((M, N), dtype=torch.bfloat16, device=dev)))
+    flops = 2.0 * M * N * K
+    alg_bytes = M * K + N * K // 2 + 4 * M * ((K // 128 + 3) // 4) + 4 * N * (K // 128) + 2 * M * N
+
+    def launch(i):
+        s = sets[i % len(sets)]
+        dg.fp8_fp4_gemm_nt((s["a"], s["sa"]), (s["b"], s["sb"]), s["d"])
+
+    def cpu(seconds):
+        rows = 48
+        t0 = time.perf_counter()
+        oracle.gemm_fp8_fp4_nt(p["a"][:rows], p["sa"][:rows], p["b"], p["sb"])
+        t = time.perf_counter() - t0
+        return 2.0 * rows * N * K / t, t, f"rows 0..{rows - 1} of the {M}x{N}x{K} problem, float64 numpy"
+
+    return Workload(launch=launch, work=flops, flops=flops, alg_bytes=alg_bytes, bound="mfma",
+                    kernel="dg::pipe::pipe_kernel (fp4 weights)", cpu=cpu,
+                    config={"workload": None, "M": M, "N": N, "K": K, "out": "bf16",
+                            "weights": "fp4 e2m1, ue8m0 per 1x32", "scales": "ue8m0 packed x4 (act per 1x128)",
+                            "step": "gemm (scales pre-packed)", "buffer_sets": len(sets)})
+
+
+def w_k_grouped(spec, dg, dev):
+    """The K-grouped GEMM of the MoE weight gradient, accumulating in place (C = D).  Both
+    operands are N(0, 1) activations cast per 1x128 group by the library's cast, whose scale
+    output is already the [sum ks / 128, mn] layout this GEMM takes."""
+    import oracle
+    M, N, ks = spec["M"], spec["N"], spec["ks"]
+    K, G = sum(ks), len(ks)
+    g = torch.Generator(device=dev).manual_seed(0)
+    sets = []
+    for _ in range(2):
+        qa, sa = dg.per_token_group_cast_fp8(torch.randn((M, K), generator=g, device=dev).to(torch.bfloat16))
+        qb, sb = dg.per_token_group_cast_fp8(torch.randn((N, K), generator=g, device=dev).to(torch.bfloat16))
+        sets.append(dict(a=qa, sa=sa.t(), b=qb, sb=sb.t(), d=torch.zeros((G, M, N), device=dev)))
+    flops = 2.0 * M * N * K
+    alg_bytes = M * K + N * K + 4 * (M + N) * (K // 128) + 2 * 4 * G * M * N
+
+    def launch(i):
+        s = sets[i % len(sets)]
+        dg.k_grouped_fp8_gemm_nt_contiguous((s["a"], s["sa"]), (s["b"], s["sb"]), s["d"], ks, s["d"])
+
+    def cpu(seconds):
+        rows = 256
+        s = sets[0]
+        a = s["a"][:rows].cpu().numpy()
+        sa = s["sa"][:, :rows].t().cpu().numpy()
+        b, sb = s["b"].cpu().numpy(), s["sb"].t().cpu().numpy()
+        c = np.zeros((G, rows, N), dtype=np.float32)
+        t0 = time.perf_counter()
+        oracle.k_grouped(a, sa, b, sb, ks, c)
+        t = time.perf_counter() - t0
+        return 2.0 * rows * N * K / t, t, f"rows 0..{rows - 1} of A (all {G} groups, all of B), float64 numpy"
+
+    return Workload(launch=launch, work=flops, flops=flops, alg_bytes=alg_bytes, bound="mfma",
+                    kernel="K-grouped GEMM (one step = every group)", cpu=cpu,
+                    config={"workload": None, "M": M, "N": N, "ks": ks, "out": "fp32, C = D in place",
+                            "scales": "fp32 1x128 on both operands", "buffer_sets": len(sets)})
+
+
+def w_cast(spec, dg, dev):
+    """The per-token-group FP8 cast of a BF16 activation matrix (the A operand of the dense
+    workload before quantization); HBM-bound."""
+    import oracle
+    M, K = spec["M"], spec["K"]
+    ue8m0 = spec.get("ue8m0", False)
+    g = torch.Generator(device=dev).manual_seed(0)
+    xs = [torch.randn((M, K), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16) for _ in range(8)]
+    outs = [dg.per_token_group_cast_fp8(xs[i], pack_ue8m0=ue8m0) for i in range(2)]
+    sf_bytes = 4 * (K // 512) if ue8m0 else 4 * (K // 128)
+    alg_bytes = M * K * 2 + M * K + M * sf_bytes
+
+    def launch(i):
+        dg.per_token_group_cast_fp8(xs[i % len(xs)], pack_ue8m0=ue8m0, out=outs[i % 2])
+
+    def cpu(seconds):
+        x = xs[0][:256].float().cpu().numpy()
+        t0 = time.perf_counter()
+        oracle.per_token_group_cast(x, ue8m0=ue8m0)
+        t = time.perf_counter() - t0
+        return 256 * (K * 3 + sf_bytes) / t, t, "rows 0..255 of the BF16 input, numpy"
+
+    return Workload(launch=launch, work=alg_bytes, flops=0.0, alg_bytes=alg_bytes, bound="hbm",
+                    kernel=f"dg::cast_kernel<true, {'true' if ue8m0 else 'false'}>", cpu=cpu,
+                    config={"workload": None, "M": M, "K": K, "scales": "ue8m0x4" if ue8m0 else "f32",
+                            "buffer_sets": len(xs)}, traffic_key=("cast_source_sha1", CAST_SOURCES))
+
+
+BUILDERS = {"dense": w_dense, "dense_c": w_dense, "masked": w_masked, "contig": w_contig,
+            "fp4_dense": w_fp4_dense, "fp4_masked": lambda s, dg, dev: w_masked(s, dg, dev, fp4=True),
+            "k_grouped": w_k_grouped, "cast": w_cast}
+
+
+# ---------------------------------------------------------------- measurement
+def capture(fn, count):
+    """A graph of ``count`` calls fn(0..count-1), captured on a side stream."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn(0)                                          # (the first call outside the graph)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(count):
+            fn(i)
+    torch.cuda.synchronize()
+    return g
+
+
+def sample_clock_power():
+    """(mean gfx clock over the XCDs in MHz, socket power in W) from amd-smi, or (None, None)."""
+    try:
+        r = subprocess.run(["amd-smi", "metric", "-g", "0", "-c", "-p", "--json"], capture_output=True, text=True,
+                           timeout=20)
+        j = json.loads(r.stdout[r.stdout.index("{"):])
+        gd = j["gpu_data"][0] if "gpu_data" in j else j[0]
+        clocks = [v["clk"]["value"] for k, v in gd["clock"].items() if k.startswith("gfx_") and isinstance(v, dict)
+                  and isinstance(v.get("clk"), dict) and isinstance(v["clk"].get("value"), (int, float))]
+        pw = gd["power"]["socket_power"]["value"]
+        return (float(np.mean(clocks)) if clocks else None), (float(pw) if isinstance(pw, (int, float)) else None)
+    except Exception as e:  # the tool is missing or its output differs: report nothing
+        log("amd-smi sample failed:", repr(e)[:200])
+        return None, None
+
+
+def sustained_clock_power(run_some, seconds=2.0):
+    """Keep the GPU busy with ``run_some()`` for about ``seconds`` while amd-smi samples it;
+    the median of the samples taken while the work ran."""
+    samples, stop = [], threading.Event()
+
+    def sampler():
+        time.sleep(0.3)
+        while not stop.is_set():
+            samples.append(sample_clock_power())
+
+    th = threading.Thread(target=sampler, daemon=True)
+    th.start()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds or (not samples and time.perf_counter() - t0 < 4 * seconds):
+        run_some()
+        torch.cuda.synchronize()
+    stop.set()
+    th.join(timeout=30)
+    clk = [c for c, _ in samples if c]
+    pw = [p for _, p in samples if p]
+    return (float(np.median(clk)) if clk else None), (float(np.median(pw)) if pw else None), len(samples)
+
+
+def copy_ceiling_gbs(dev, mib=1024):
+    """Read + write bytes per second of a plain 1 GiB device-to-device copy (best of 5)."""
+    src = torch.empty(mib << 20, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    best = 0.0
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        best = max(best, 2.0 * src.numel() / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    del src, dst
+    torch.cuda.empty_cache()
+    return best
 
 
 def copy_calibration(args, dev):
@@ -122,6 +456,8 @@ def main():
     ap.add_argument("--workload", default=DEFAULT, choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the sustained clock/power sampling and the copy ceiling (profiler runs)")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="also run one plain device copy of this many MiB (a known-size kernel that "
                          "calibrates the FETCH_SIZE / WRITE_SIZE counters)")
@@ -135,289 +471,113 @@ def main():
     dev = "cuda:0"
     torch.cuda.init()
     spec = WORKLOADS[args.workload]
-    if spec["kind"] == "cast":
-        return bench_cast(args, spec, dg, dev)
-    if spec["kind"] == "k_grouped":
-        return bench_k_grouped(args, spec, dg, dev)
-    if spec["kind"] not in ("dense", "dense_c"):
-        return bench_grouped(args, spec, dg, dev)
-
-    p, sets, flops, alg_bytes = make_dense(spec, 8, dev)
+    wl = BUILDERS[spec["kind"]](spec, dg, dev)
+    wl.config["workload"] = args.workload
+    K, W = args.steps, args.warmup
     stream = torch.cuda.current_stream()
-    M, N, K = spec["M"], spec["N"], spec["K"]
+    graph_mode = bool(spec.get("graph"))
 
-    def step(i, ev=None):
-        s = sets[i % len(sets)]
-        sa = dg.get_mn_major_tma_aligned_tensor(s["sa_raw"])
-        if ev is not None:
-            ev[0].record(stream)
-        dg.fp8_gemm_nt((s["a"], sa), (s["b"], s["sb"]), s["d"], c=s.get("c"))
-        if ev is not None:
-            ev[1].record(stream)
-
-    for i in range(args.warmup):
-        step(i)
+    for i in range(W):
+        wl.step(i)
     torch.cuda.synchronize()
     copy_calibration(args, dev)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i, evs[i])
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    elapsed = t1 - t0
-    gemm_ms = [a.elapsed_time(b) for a, b in evs]
-    gemm_avg_ms = float(np.mean(gemm_ms))
-    ms_per_step = elapsed * 1e3 / args.steps
-    value = flops * args.steps / elapsed / 1e12
-    achieved = flops / (gemm_avg_ms * 1e-3) / 1e12
-    traffic = read_traffic(args.workload)
 
+    if graph_mode:
+        # the host needs longer per call than these kernels run: time captured graphs
+        steps_graph = capture(wl.step, K)
+        steps_graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        steps_graph.replay()
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+        launch_graph = capture(wl.launch, K)
+        periods = []
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            launch_graph.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            periods.append(e0.elapsed_time(e1) / K)
+        kern_ms = dict(mean=float(np.mean(periods)), median=float(np.median(periods)), min=float(np.min(periods)),
+                       how=f"graph of {K} launches replayed between two events, 5 replays")
+
+        def run_some():
+            launch_graph.replay()
+    else:
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(K):
+            if wl.pre is not None:
+                wl.pre(i)
+            evs[i][0].record(stream)
+            wl.launch(i)
+            evs[i][1].record(stream)
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+        ms = [a.elapsed_time(b) for a, b in evs]
+        kern_ms = dict(mean=float(np.mean(ms)), median=float(np.median(ms)), min=float(np.min(ms)),
+                       how=f"HIP events around each of the {K} timed launches")
+
+        def run_some():
+            for i in range(20):
+                wl.launch(i)
+
+    ms_per_step = elapsed * 1e3 / K
+    unit = "GB/s" if wl.bound == "hbm" else "TFLOP/s"
+    scale = 1e9 if unit == "GB/s" else 1e12
+    value = wl.work * K / elapsed / scale
+    peak = PEAK_HBM_GBS if wl.bound == "hbm" else PEAK_FP8_TFLOPS
+    achieved = wl.work / (kern_ms["mean"] * 1e-3) / scale
+
+    extras = {}
+    if not args.no_extras:
+        sclk, power, nsamp = sustained_clock_power(run_some)
+        extras["sclk_mhz"] = None if sclk is None else round(sclk, 1)
+        extras["socket_power_w"] = power
+        extras["clock_samples"] = nsamp
+        extras["copy_ceiling_gbs"] = round(copy_ceiling_gbs(dev), 1)
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline_dense(p, args.cpu_seconds)
+        v, secs, sample = wl.cpu(args.cpu_seconds)
+        cpu = {"value": round(v / scale, 6), "unit": unit, "cores": blas_threads(), "kind": "oracle",
+               "seconds": round(secs, 2), "sample": sample}
 
+    tk = getattr(wl, "traffic_key", ("kernel_source_sha1", GEMM_SOURCES))
+    roof = {"bound": wl.bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4), "traffic": read_traffic(args.workload, *tk),
+            "kernel": wl.kernel, "kernel_ms_mean": round(kern_ms["mean"], 5),
+            "kernel_ms_median": round(kern_ms["median"], 5), "kernel_ms_min": round(kern_ms["min"], 5),
+            "frac_median": round(wl.work / (kern_ms["median"] * 1e-3) / scale / peak, 4),
+            "timing": kern_ms["how"], "alg_bytes": wl.alg_bytes, "alg_flops": wl.flops}
+    if extras.get("sclk_mhz"):
+        roof["frac_at_observed_clock"] = round(achieved / (peak * extras["sclk_mhz"] / NOMINAL_SCLK_MHZ), 4) \
+            if wl.bound != "hbm" else None
+    if wl.bound == "hbm" and extras.get("copy_ceiling_gbs"):
+        roof["frac_of_copy_ceiling"] = round(achieved / extras["copy_ceiling_gbs"], 4)
     out = {
-        "metric": "TFLOP/s + % FP8 MFMA peak, block-scaled FP8 GEMM M=4096 N=7168 K=2048"
-        if args.workload == DEFAULT else f"TFLOP/s, block-scaled FP8 GEMM {args.workload}",
+        "metric": HEADLINE_METRIC if args.workload == DEFAULT else f"{unit}, {args.workload}",
         "value": round(value, 2),
-        "unit": "TFLOP/s",
+        "unit": unit,
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": K,
+        "warmup": W,
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8_e4m3 (fp32 accumulate)",
+        "dtype": "fp8_e4m3 x fp4_e2m1 (fp32 accumulate)" if "fp4" in spec["kind"] else
+                 ("bf16 -> fp8_e4m3" if spec["kind"] == "cast" else "fp8_e4m3 (fp32 accumulate)"),
         "data": "synthetic",
-        "pct_fp8_peak": round(100.0 * value / PEAK_FP8_TFLOPS, 2),
-        "config": {"workload": args.workload, "M": M, "N": N, "K": K,
-                   "out": "fp32+C" if spec["kind"] == "dense_c" else "bf16",
-                   "scales": "fp32 1x128 act, 128x128 weight",
-                   "step": "transform_sf(act scales) + gemm", "buffer_sets": len(sets)},
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP8_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP8_TFLOPS, 4),
-                     "traffic": traffic, "kernel": "dg::pipe::pipe_kernel (GEMM launch alone)",
-                     "gemm_avg_ms": round(gemm_avg_ms, 5), "gemm_min_ms": round(float(np.min(gemm_ms)), 5),
-                     "alg_bytes": alg_bytes, "alg_flops": flops},
+        "config": wl.config,
+        "roofline": roof,
         "cpu_baseline": cpu,
+        "gpu": extras,
     }
-    print(json.dumps(out), flush=True)
-
-
-def bench_k_grouped(args, spec, dg, dev):
-    """The K-grouped GEMM of the MoE weight gradient, accumulating in place (C = D).  Both
-    operands are N(0, 1) activations cast per 1x128 group by the library's cast, whose scale
-    output is already the [sum ks / 128, mn] layout this GEMM takes."""
-    M, N, ks = spec["M"], spec["N"], spec["ks"]
-    K, G = sum(ks), len(ks)
-    g = torch.Generator(device=dev).manual_seed(0)
-    sets = []
-    for _ in range(2):
-        qa, sa = dg.per_token_group_cast_fp8(torch.randn((M, K), generator=g, device=dev).to(torch.bfloat16))
-        qb, sb = dg.per_token_group_cast_fp8(torch.randn((N, K), generator=g, device=dev).to(torch.bfloat16))
-        sets.append(dict(a=qa, sa=sa.t(), b=qb, sb=sb.t(), d=torch.zeros((G, M, N), device=dev)))
-    flops = 2.0 * M * N * K
-    alg_bytes = M * K + N * K + 4 * (M + N) * (K // 128) + 2 * 4 * G * M * N
-    stream = torch.cuda.current_stream()
-
-    def step(i, ev=None):
-        s = sets[i % len(sets)]
-        if ev is not None:
-            ev[0].record(stream)
-        dg.k_grouped_fp8_gemm_nt_contiguous((s["a"], s["sa"]), (s["b"], s["sb"]), s["d"], ks, s["d"])
-        if ev is not None:
-            ev[1].record(stream)
-
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    copy_calibration(args, dev)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i, evs[i])
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    avg = float(np.mean([a.elapsed_time(b) for a, b in evs]))
-    cpu = None
-    if not args.no_cpu_baseline:
-        import oracle
-        rows = 512
-        s = sets[0]
-        a = s["a"][:rows].cpu().numpy()
-        sa = s["sa"][:, :rows].t().cpu().numpy()
-        b, sb = s["b"].cpu().numpy(), s["sb"].t().cpu().numpy()
-        c = np.zeros((G, rows, N), dtype=np.float32)
-        t = time.perf_counter()
-        oracle.k_grouped(a, sa, b, sb, ks, c)
-        dt = time.perf_counter() - t
-        cpu = {"value": round(2.0 * rows * N * K / dt / 1e12, 6), "unit": "TFLOP/s", "cores": os.cpu_count(),
-               "kind": "oracle", "seconds": round(dt, 2),
-               "sample": f"rows 0..{rows - 1} of A (all {G} groups, all of B), float64 numpy"}
-    out = {
-        "metric": f"TFLOP/s, K-grouped FP8 GEMM {args.workload}",
-        "value": round(flops * args.steps / elapsed / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(elapsed * 1e3 / args.steps, 5),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "fp8_e4m3 (fp32 accumulate)", "data": "synthetic",
-        "config": {"workload": args.workload, "M": M, "N": N, "ks": ks, "out": "fp32, C = D in place",
-                   "scales": "fp32 1x128 on both operands", "buffer_sets": len(sets)},
-        "roofline": {"bound": "mfma", "achieved": round(flops / (avg * 1e-3) / 1e12, 2), "peak": PEAK_FP8_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(flops / (avg * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4),
-                     "traffic": read_traffic(args.workload),   # per step, like alg_bytes
-                     "kernel": f"dg::gemm_kernel, {G} launches per step (one per group)",
-                     "step_gpu_ms": round(avg, 5), "alg_bytes": alg_bytes, "alg_flops": flops},
-        "cpu_baseline": cpu,
-    }
-    print(json.dumps(out), flush=True)
-
-
-def bench_cast(args, spec, dg, dev):
-    """The per-token-group FP8 cast of a BF16 activation matrix (the A operand of the dense
-    workload before quantization); HBM-bound."""
-    M, K = spec["M"], spec["K"]
-    ue8m0 = spec.get("ue8m0", False)
-    g = torch.Generator(device=dev).manual_seed(0)
-    sets = [torch.randn((M, K), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16) for _ in range(8)]
-    sf_bytes = 4 * (K // 512) if ue8m0 else 4 * (K // 128)   # per row: packed codes or FP32 scales
-    alg_bytes = M * K * 2 + M * K + M * sf_bytes
-    copy_calibration(args, dev)
-    stream = torch.cuda.current_stream()
-    # two output sets, allocated once and overwritten in turn
-    outs = [dg.per_token_group_cast_fp8(sets[i], pack_ue8m0=ue8m0) for i in range(2)]
-    for i in range(args.warmup):
-        dg.per_token_group_cast_fp8(sets[i % len(sets)], pack_ue8m0=ue8m0, out=outs[i % 2])
-    torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        evs[i][0].record(stream)
-        dg.per_token_group_cast_fp8(sets[i % len(sets)], pack_ue8m0=ue8m0, out=outs[i % 2])
-        evs[i][1].record(stream)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    ms = [a.elapsed_time(b) for a, b in evs]
-    avg = float(np.mean(ms))
-    cpu = None
-    if not args.no_cpu_baseline:
-        import oracle
-        x = sets[0][:256].float().cpu().numpy()
-        t = time.perf_counter()
-        oracle.per_token_group_cast(x, ue8m0=ue8m0)
-        dt = time.perf_counter() - t
-        cpu = {"value": round(256 * (K * 3 + sf_bytes) / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
-               "kind": "oracle", "seconds": round(dt, 2), "sample": "rows 0..255 of the 4096x7168 BF16 input, numpy"}
-    out = {
-        "metric": f"GB/s, per-token-group FP8 cast {args.workload}",
-        "value": round(alg_bytes * args.steps / elapsed / 1e9, 2), "unit": "GB/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(elapsed * 1e3 / args.steps, 5),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16 -> fp8_e4m3",
-        "data": "synthetic",
-        "config": {"workload": args.workload, "M": M, "K": K, "buffer_sets": len(sets),
-                   "scales": "ue8m0x4" if ue8m0 else "f32"},
-        "roofline": {"bound": "hbm", "achieved": round(alg_bytes / (avg * 1e-3) / 1e9, 2), "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": round(alg_bytes / (avg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-                     "traffic": read_traffic(args.workload, "cast_source_sha1", CAST_SOURCES),
-                     "kernel": f"dg::cast_kernel<true, {'true' if ue8m0 else 'false'}>", "avg_ms": round(avg, 5), "alg_bytes": alg_bytes},
-        "cpu_baseline": cpu,
-    }
-    print(json.dumps(out), flush=True)
-
-
-def cpu_baseline_dense(p, seconds):
-    """The float64 oracle, as it stands, on a bounded row sample of the same problem."""
-    import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        threads = os.cpu_count()
-    M, N, K = p["M"], p["N"], p["K"]
-    rows = min(64, M)
-    t0 = time.perf_counter()
-    oracle.gemm_nt(p["a"][:rows], p["sa"][:rows], p["b"], p["sb"], 128, c=None if p["c"] is None else p["c"][:rows])
-    t = time.perf_counter() - t0
-    if t < seconds / 4 and rows < M:
-        rows = int(min(M, max(rows, rows * (seconds / max(t, 1e-3)))))
-        rows = max(1, rows - rows % 8) if rows >= 8 else rows
-        t0 = time.perf_counter()
-        oracle.gemm_nt(p["a"][:rows], p["sa"][:rows], p["b"], p["sb"], 128,
-                       c=None if p["c"] is None else p["c"][:rows])
-        t = time.perf_counter() - t0
-    fl = 2.0 * rows * N * K
-    return {"value": round(fl / t / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "seconds": round(t, 2),
-            "sample": f"rows 0..{rows - 1} of the {M}x{N}x{K} problem (all N columns, full K), float64 numpy"}
-
-
-def bench_grouped(args, spec, dg, dev):
-    from tests import gen
-    stream = torch.cuda.current_stream()
-    if spec["kind"] == "masked":
-        p = gen.config5()
-        G, Mmax, N, K = p["G"], p["M_max"], p["N"], p["K"]
-        a = torch.from_numpy(p["a"]).to(dev)
-        b = torch.from_numpy(p["b"]).to(dev)
-        sa = dg.get_mn_major_tma_aligned_packed_ue8m0_tensor(torch.from_numpy(p["sa"]).to(dev))
-        sb = dg.get_mn_major_tma_aligned_packed_ue8m0_tensor(torch.from_numpy(p["sb"]).to(dev), gran_mn=128, mn=N)
-        mm = torch.from_numpy(p["masked_m"]).to(dev)
-        d = torch.empty((G, Mmax, N), dtype=torch.bfloat16, device=dev)
-        valid = int(np.clip(p["masked_m"], 0, Mmax).sum())
-        pk = (K // 128 + 3) // 4
-        active = int((p["masked_m"] > 0).sum())
-        alg_bytes = active * (N * K + 4 * N * pk) + valid * (K + 4 * pk + 2 * N) + 4 * G
-        flops = 2.0 * valid * N * K
-
-        def launch():
-            dg.m_grouped_fp8_gemm_nt_masked((a, sa), (b, sb), d, mm, expected_m=128)
-        bound, peak, unit = "hbm", PEAK_HBM_GBS, "GB/s"
-    else:
-        p = gen.config4()
-        G, N, K = p["G"], p["N"], p["K"]
-        a = torch.from_numpy(p["a"]).to(dev)
-        b = torch.from_numpy(p["b"]).to(dev)
-        sa = dg.get_mn_major_tma_aligned_tensor(torch.from_numpy(p["sa"]).to(dev))
-        sb = torch.from_numpy(p["sb"]).to(dev)
-        lay = torch.from_numpy(p["layout"]).to(dev)
-        d = torch.empty((p["M"], N), dtype=torch.bfloat16, device=dev)
-        flops = 2.0 * p["M"] * N * K
-        alg_bytes = G * N * K + p["M"] * K + 2 * p["M"] * N
-
-        def launch():
-            dg.m_grouped_fp8_gemm_nt_contiguous((a, sa), (b, sb), d, lay)
-        bound, peak, unit = "mfma", PEAK_FP8_TFLOPS, "TFLOP/s"
-    for _ in range(args.warmup):
-        launch()
-    torch.cuda.synchronize()
-    copy_calibration(args, dev)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    e0.record(stream)
-    for _ in range(args.steps):
-        launch()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    avg_ms = e0.elapsed_time(e1) / args.steps
-    if bound == "hbm":
-        achieved = alg_bytes / (avg_ms * 1e-3) / 1e9
-        value = alg_bytes * args.steps / elapsed / 1e9
-    else:
-        achieved = flops / (avg_ms * 1e-3) / 1e12
-        value = flops * args.steps / elapsed / 1e12
-    out = {"metric": f"{unit}, block-scaled FP8 GEMM {args.workload}", "value": round(value, 2), "unit": unit,
-           "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-           "ms_per_step": round(elapsed * 1e3 / args.steps, 5), "higher_is_better": True, "scaling": "weak",
-           "vs_baseline": None, "dtype": "fp8_e4m3 (fp32 accumulate)", "data": "synthetic",
-           "config": {"workload": args.workload, "tflops": round(flops / (avg_ms * 1e-3) / 1e12, 2)},
-           "roofline": {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
-                        "frac": round(achieved / peak, 4), "traffic": read_traffic(args.workload),
-                        "avg_ms": round(avg_ms, 5), "alg_bytes": alg_bytes, "alg_flops": flops},
-           "cpu_baseline": None}
+    if args.workload == DEFAULT:
+        out["pct_fp8_peak"] = round(100.0 * value / PEAK_FP8_TFLOPS, 2)
     print(json.dumps(out), flush=True)
 
 
