@@ -416,7 +416,13 @@ int dg_k_grouped_fp8_gemm_nt_contiguous(int32_t num_groups, int32_t m, int32_t n
   // every group is checked before any is launched, so an error writes nothing
   const int64_t mn = (int64_t)m * n;
   int64_t k0 = 0;
-  for (int pass = 0; pass < 2; ++pass) {
+  int nonempty = 0;
+  for (int g = 0; g < num_groups; ++g) nonempty += ks[g] > 0;
+  // One launch over every non-empty group's tiles (the groups share the scheduler, page
+  // "02 · DeepGEMM 技术解析" §5.2); empty groups are D = C copies.  Beyond kMaxKGroups
+  // non-empty groups the groups run as one dense launch each.
+  const bool single = nonempty > 0 && nonempty <= dg::kMaxKGroups && !env_int("DG_KGROUP_LOOP", 0);
+  for (int pass = 0; pass < (single ? 1 : 2); ++pass) {
     k0 = 0;
     for (int g = 0; g < num_groups; ++g) {
       const float* cg = c + g * mn;
@@ -444,6 +450,55 @@ int dg_k_grouped_fp8_gemm_nt_contiguous(int32_t num_groups, int32_t m, int32_t n
       k0 += ks[g];
     }
   }
+  if (!single) return ok();
+  dg::GemmParams p{};
+  p.a = (const uint8_t*)a; p.lda = lda;
+  p.sfa = sfa; p.sfa_stride = m;
+  p.b = (const uint8_t*)b; p.ldb = ldb;
+  p.sfb = sfb; p.sfb_stride = n;
+  p.c = c; p.ldc = n; p.c_gstride = mn;
+  p.d = d; p.ldd = n; p.d_gstride = mn;
+  p.m = m; p.n = n; p.k = (int32_t)sum_k; p.num_groups = num_groups;
+  int kb = 0, max_nkb = 0;
+  for (int g = 0; g < num_groups; ++g) {
+    const int nkb = ks[g] / 128;
+    if (nkb > 0) {
+      p.kg_group[p.kg_count] = g;
+      p.kg_kb0[p.kg_count] = kb;
+      p.kg_nkb[p.kg_count] = nkb;
+      ++p.kg_count;
+    } else if (c != d) {
+      const hipError_t e = hipMemcpyAsync(d + g * mn, c + g * mn, mn * sizeof(float), hipMemcpyDeviceToDevice, stream);
+      if (e != hipSuccess) return fail(DG_ERR_HIP, "copy of C into D failed: %s", hipGetErrorString(e));
+    }
+    kb += nkb;
+    max_nkb = nkb > max_nkb ? nkb : max_nkb;
+  }
+  p.sf_k = max_nkb;
+  int num_sms = g_num_sms_override.load();
+  if (num_sms <= 0) num_sms = device_cu_count();
+  if (num_sms <= 0) return fail(DG_ERR_HIP, "could not query the device's compute-unit count");
+  // tile choice: the dense heuristic for one group's m x n output
+  Plan pl = plan_gemm(dg::GRP_KGROUP, m, n, (int)(sum_k / nonempty), 1, 0, dg::SF_1D1D_F32, dg::OUT_F32_C, num_sms);
+  if (pl.tile < 0) return fail(DG_ERR_UNSUPPORTED, "no tile configuration for the K-grouped GEMM");
+  const dg::TileCfg& tc = dg::kTiles[pl.tile];
+  p.num_m_tiles = (m + tc.bm - 1) / tc.bm;
+  p.num_n_tiles = (n + tc.bn - 1) / tc.bn;
+  const int64_t tiles = int64_t(p.kg_count) * p.num_m_tiles * p.num_n_tiles;
+  p.total_tiles = int(tiles);
+  const int sw = env_int("DG_SWIZZLE_M", 8);
+  p.swizzle_m = sw < 1 ? 1 : (sw < p.num_m_tiles ? sw : p.num_m_tiles);
+  const int64_t slots = int64_t(num_sms) * tile_occupancy(tc);
+  const int grid = int(tiles < slots ? tiles : slots);
+  p.xcd_remap = (grid % 8 == 0) ? 1 : 0;
+  p.d_vec = (n % 4 == 0 && aligned16(d)) ? 1 : 0;
+  p.c_vec = (n % 4 == 0 && aligned16(c)) ? 1 : 0;
+  p.d_vec16 = p.d_vec;
+  if (env_int("DG_PRINT_CONFIGS", 0))
+    fprintf(stderr, "[dg] k-grouped: %d non-empty groups, tile %dx%d, %lld tiles, grid %d\n", p.kg_count, tc.bm, tc.bn,
+            (long long)tiles, grid);
+  const hipError_t e = dg::launch_gemm(p, pl.tile, dg::SF_1D1D_F32, dg::GRP_KGROUP, dg::OUT_F32_C, grid, stream);
+  if (e != hipSuccess) return fail(DG_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return ok();
 }
 

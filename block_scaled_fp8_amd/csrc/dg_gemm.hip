@@ -78,6 +78,8 @@ struct Tile {
   int g;        // group
   int m0, n0;   // first row (within the group for masked) and first column
   int m_valid;  // rows < m_valid exist
+  int kb0;      // K-grouped: the group's first 128-long K block
+  int nkb;      // K blocks of this tile
   bool skip;
 };
 
@@ -98,6 +100,26 @@ __device__ __forceinline__ T load_uniform(const T* base, int64_t i) {
 template <int GRP, int BM, int BN>
 __device__ __forceinline__ bool get_tile(const GemmParams& p, int t, Tile& tl) {
   tl.skip = false;
+  tl.kb0 = 0;
+  tl.nkb = p.sf_k;
+  if (GRP == GRP_KGROUP) {
+    // K-grouped: the non-empty groups one after another, each walked like a dense problem
+    const int per_group = p.num_m_tiles * p.num_n_tiles;
+    const int gi = t / per_group;
+    if (gi >= p.kg_count) return false;
+    t -= gi * per_group;
+    tl.g = p.kg_group[gi];
+    tl.kb0 = p.kg_kb0[gi];
+    tl.nkb = p.kg_nkb[gi];
+    const int per_super = p.swizzle_m * p.num_n_tiles;
+    const int sr = t / per_super;
+    const int rem = t - sr * per_super;
+    const int rows = min(p.swizzle_m, p.num_m_tiles - sr * p.swizzle_m);
+    tl.m0 = (sr * p.swizzle_m + rem % rows) * BM;
+    tl.n0 = (rem / rows) * BN;
+    tl.m_valid = p.m;
+    return true;
+  }
   if (GRP == GRP_MASKED) {
     // Groups in order; within a group n tiles outer, m tiles inner, so the m tiles
     // that share a weight slice run next to each other.
@@ -167,13 +189,18 @@ struct Loader {
 template <int BM, int BN, int WM, int WN, int SFM, int GRP>
 __device__ __forceinline__ void make_loader(const GemmParams& p, const Tile& tl, Loader<BM, BN, WM, WN>& ld) {
   const uint8_t* A = p.a + (GRP == GRP_MASKED ? (int64_t)tl.g * p.a_gstride : 0);
-  const uint8_t* B = p.b + (GRP != GRP_DENSE ? (int64_t)tl.g * p.b_gstride : 0);
-  ld.a_tile = A + (int64_t)tl.m0 * p.lda;
-  ld.b_tile = B + (int64_t)tl.n0 * p.ldb;
+  const uint8_t* B = p.b + (GRP == GRP_CONTIG || GRP == GRP_MASKED ? (int64_t)tl.g * p.b_gstride : 0);
+  // (K-grouped: the group's K range starts kb0 blocks into every row, and its scales kb0
+  // scale rows into the [blocks, mn] scale arrays)
+  const int64_t kofs = (GRP == GRP_KGROUP) ? (int64_t)tl.kb0 * BK : 0;
+  ld.a_tile = A + (int64_t)tl.m0 * p.lda + kofs;
+  ld.b_tile = B + (int64_t)tl.n0 * p.ldb + kofs;
   ld.a_rows = p.m - tl.m0;  // m_max rows when masked
   ld.b_rows = p.n - tl.n0;
-  const int64_t sfa_goff = (GRP == GRP_MASKED) ? (int64_t)tl.g * p.sfa_gstride : 0;
-  const int64_t sfb_goff = (GRP != GRP_DENSE) ? (int64_t)tl.g * p.sfb_gstride : 0;
+  const int64_t sfa_goff = (GRP == GRP_MASKED) ? (int64_t)tl.g * p.sfa_gstride
+                           : (GRP == GRP_KGROUP ? (int64_t)tl.kb0 * p.sfa_stride : 0);
+  const int64_t sfb_goff = (GRP == GRP_CONTIG || GRP == GRP_MASKED) ? (int64_t)tl.g * p.sfb_gstride
+                           : (GRP == GRP_KGROUP ? (int64_t)tl.kb0 * p.sfb_stride : 0);
   ld.sa = (const uint8_t*)p.sfa + 4 * (sfa_goff + tl.m0);
   ld.sa_rows = (int)p.sfa_stride - tl.m0;
   if (SFM == SF_1D2D_F32) {
@@ -320,14 +347,14 @@ __device__ __forceinline__ void wait_and_barrier() {
 template <int BM, int BN, int WM, int WN, int SFM, int GRP, int OUT, int NF>
 __device__ __forceinline__ int gemm_tile(const GemmParams& p, uint8_t* smem, const Tile& tl,
                                          const Loader<BM, BN, WM, WN>& ld, const bool has_next,
-                                         const Loader<BM, BN, WM, WN>& ld_next, const int stage0, const bool pre2,
-                                         const int vm_after, bool& next_pre2, const int wave, const int lane,
-                                         const LaneOffsets lo) {
+                                         const Loader<BM, BN, WM, WN>& ld_next, const int nkb_next, const int stage0,
+                                         const bool pre2, const int vm_after, bool& next_pre2, const int wave,
+                                         const int lane, const LaneOffsets lo) {
   using S = Shape<BM, BN, WM, WN>;
   constexpr int FM = S::FM, FN = S::FN, TM = S::TM, TN = S::TN;
   const int wm = wave / WN, wn = wave % WN;
   const int lr = lane & 15, lg = lane >> 4;
-  const int nkb = p.sf_k;
+  const int nkb = tl.nkb;
   const int g = tl.g;
   const int row0 = tl.m0 + wm * TM + lr;  // lane's row in fragment 0
   const int nw0 = tl.n0 + wn * TN;        // wave's first column
@@ -470,7 +497,7 @@ __device__ __forceinline__ int gemm_tile(const GemmParams& p, uint8_t* smem, con
   // the next tile's second stage goes into the stage this tile read last, once every
   // wave is done with it
   next_pre2 = false;
-  if (has_next && nkb >= 2) {
+  if (has_next && nkb >= 2 && nkb_next >= 2) {
     wait_and_barrier<63>();
     issue_stage<BM, BN, WM, WN, SFM>(p, ld_next, smem, 1, (stage0 + nkb - 1) & 1, wave, lo);
     next_pre2 = true;
@@ -483,7 +510,8 @@ __device__ __forceinline__ int gemm_tile(const GemmParams& p, uint8_t* smem, con
                         tl.m0 + BM <= tl.m_valid && tl.n0 + BN <= p.n;
   char* Dg = (char*)p.d;
   const int esz = (OUT == OUT_BF16) ? 2 : 4;
-  if (GRP == GRP_MASKED) Dg += (int64_t)g * p.d_gstride * esz;
+  if (GRP == GRP_MASKED || GRP == GRP_KGROUP) Dg += (int64_t)g * p.d_gstride * esz;
+  const float* Cg = p.c + (GRP == GRP_KGROUP ? (int64_t)g * p.c_gstride : 0);
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
     const int row = row0 + 16 * i;
@@ -498,7 +526,7 @@ __device__ __forceinline__ int gemm_tile(const GemmParams& p, uint8_t* smem, con
       float o[4] = {fin[i][j][0], fin[i][j][1], fin[i][j][2], fin[i][j][3]};
       const bool full4 = col + 3 < p.n;
       if (OUT == OUT_F32_C) {
-        const float* crow = p.c + (int64_t)row * p.ldc;
+        const float* crow = Cg + (int64_t)row * p.ldc;
         if (full4 && p.c_vec) {
           const v4f cv = *(const v4f*)(crow + col);
           o[0] += cv.x; o[1] += cv.y; o[2] += cv.z; o[3] += cv.w;
@@ -569,6 +597,7 @@ __global__ void __launch_bounds__(WM* WN * 64, 1) gemm_kernel(const GemmParams p
     int tn = t + gridDim.x;
     const bool has_next = advance(tn, nxt);
     if (has_next) make_loader<BM, BN, WM, WN, SFM, GRP>(p, nxt, ld_next);
+    const int nkb_next = has_next ? nxt.nkb : 0;
     bool next_pre2 = false;
     if (SFM == SF_1D2D_F32) {
       // leading 16-column fragments of this wave that use the first weight-scale block
@@ -579,8 +608,8 @@ __global__ void __launch_bounds__(WM* WN * 64, 1) gemm_kernel(const GemmParams p
   case X:                                                                                               \
     if constexpr (X <= S::FN)                                                                           \
       vm_after = gemm_tile<BM, BN, WM, WN, SFM, GRP, OUT, X>(p, smem, cur, ld_cur, has_next, ld_next,   \
-                                                             stage0, pre2, vm_after, next_pre2, wave,   \
-                                                             lane, lo);                                 \
+                                                             nkb_next, stage0, pre2, vm_after,          \
+                                                             next_pre2, wave, lane, lo);                \
     break;
         DG_NF_CASE(1) DG_NF_CASE(2) DG_NF_CASE(3) DG_NF_CASE(4)
         DG_NF_CASE(5) DG_NF_CASE(6) DG_NF_CASE(7) DG_NF_CASE(8)
@@ -588,11 +617,11 @@ __global__ void __launch_bounds__(WM* WN * 64, 1) gemm_kernel(const GemmParams p
         default: break;
       }
     } else {
-      vm_after = gemm_tile<BM, BN, WM, WN, SFM, GRP, OUT, S::FN>(p, smem, cur, ld_cur, has_next, ld_next, stage0,
-                                                                pre2, vm_after, next_pre2, wave, lane, lo);
+      vm_after = gemm_tile<BM, BN, WM, WN, SFM, GRP, OUT, S::FN>(p, smem, cur, ld_cur, has_next, ld_next, nkb_next,
+                                                                stage0, pre2, vm_after, next_pre2, wave, lane, lo);
     }
     if (!has_next) break;
-    stage0 = (stage0 + p.sf_k) & 1;
+    stage0 = (stage0 + cur.nkb) & 1;
     pre2 = next_pre2;
     cur = nxt;
     ld_cur = ld_next;
@@ -634,6 +663,9 @@ static hipError_t launch_tile(const GemmParams& p, int sfm, int grp, int out, in
   DG_CASE(SF_1D1D_F32, GRP_MASKED, OUT_BF16)
   DG_CASE(SF_1D1D_UE8M0, GRP_MASKED, OUT_BF16)
   DG_CASE(SF_1D1D_UE8M0, GRP_MASKED, OUT_F32)
+  if constexpr (BN >= 224) {
+    DG_CASE(SF_1D1D_F32, GRP_KGROUP, OUT_F32_C)
+  }
 #undef DG_CASE
   return hipErrorInvalidValue;
 }
@@ -676,6 +708,7 @@ DG_DECL(0) DG_DECL(1) DG_DECL(2) DG_DECL(3) DG_DECL(4) DG_DECL(5) DG_DECL(6) DG_
 bool gemm_instantiated(int tile, int sfm, int grp, int out) {
   if (tile < 0 || tile >= kNumTiles) return false;
   if (sfm < 0 || sfm > 2 || out < 0 || out > 2) return false;
+  if (grp == GRP_KGROUP) return sfm == SF_1D1D_F32 && out == OUT_F32_C && kTiles[tile].bn >= 224;
   if (grp == GRP_CONTIG) {
     if (kTiles[tile].bm > 128) return false;
     if (out == OUT_F32_C) return false;

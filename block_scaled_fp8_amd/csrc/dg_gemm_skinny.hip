@@ -17,8 +17,6 @@
 //    added through LDS, C is added, and the tile is stored row-contiguously.
 // The column block of a workgroup lies inside one 128-wide weight-scale block (BN divides 128),
 // so the weight scale of a K block is one scalar.
-#include <cstdlib>
-
 #include "dg_internal.h"
 
 namespace dg {
@@ -202,10 +200,10 @@ static hipError_t launch_nw(const GemmParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
+// (8 waves per workgroup measured best: 4 leave less memory-level parallelism, 16 run out of
+// registers)
 template <int BN, int OUT>
-static hipError_t launch_one(const GemmParams& p, hipStream_t s, int nw) {
-  if (nw == 4) return launch_nw<BN, 4, OUT>(p, s);
-  if (nw == 16) return launch_nw<BN, 16, OUT>(p, s);
+static hipError_t launch_one(const GemmParams& p, hipStream_t s) {
   return launch_nw<BN, 8, OUT>(p, s);
 }
 
@@ -214,10 +212,8 @@ static hipError_t launch_one(const GemmParams& p, hipStream_t s, int nw) {
 // Dense problems with m <= 64 rows and 1d2d FP32 scales; bn: 16 or 32 columns per workgroup.
 hipError_t launch_skinny(const GemmParams& p, int bn, int out, hipStream_t stream) {
   if (p.m > 64 || p.m <= 0) return hipErrorInvalidValue;
-  const char* e = getenv("DG_SKINNY_NW");
-  const int nw = e ? atoi(e) : 8;
 #define DG_CASE(BN, O) \
-  if (bn == BN && out == O) return skinny::launch_one<BN, O>(p, stream, nw);
+  if (bn == BN && out == O) return skinny::launch_one<BN, O>(p, stream);
   DG_CASE(16, OUT_BF16)
   DG_CASE(16, OUT_F32)
   DG_CASE(16, OUT_F32_C)

@@ -17,7 +17,11 @@ enum SfMode {
   SF_FP4_UE8M0 = 3,
 };
 
-enum GroupMode { GRP_DENSE = 0, GRP_CONTIG = 1, GRP_MASKED = 2 };
+// GRP_KGROUP: the K-grouped form (groups concatenated along K, one output per group)
+enum GroupMode { GRP_DENSE = 0, GRP_CONTIG = 1, GRP_MASKED = 2, GRP_KGROUP = 3 };
+
+// K-grouped problems with at most this many non-empty groups run in one launch
+constexpr int kMaxKGroups = 64;
 
 enum OutMode { OUT_BF16 = 0, OUT_F32 = 1, OUT_F32_C = 2 };
 
@@ -48,6 +52,13 @@ struct GemmParams {
   int32_t d_vec;                  // 1: D rows allow 4-element vector stores (ldd % 4 == 0, 16-B base)
   int32_t c_vec;                  // 1: C rows allow 4-element vector loads
   int32_t d_vec16;                // 1: D rows and base are 16-byte aligned
+  // K-grouped: C between groups, and the non-empty groups in order (output index, first
+  // 128-long K block, number of K blocks); num_m_tiles * num_n_tiles tiles per group
+  int64_t c_gstride;
+  int32_t kg_count;
+  int32_t kg_group[kMaxKGroups];
+  int32_t kg_kb0[kMaxKGroups];
+  int32_t kg_nkb[kMaxKGroups];
 };
 
 struct TileCfg {

@@ -829,3 +829,50 @@ def test_skinny_decode_shapes(bn, shape):
         torch.cuda.synchronize()
         st = check_dense(p, d, with_c=with_c, name=f"skinny {shape} {bn}")
         assert torch.isnan(big[:, N:].float()).all()
+
+
+@pytest.mark.parametrize("G", [64, 66])
+def test_k_grouped_many_groups(G):
+    """Up to 64 non-empty groups run as one launch over every group's tiles; beyond that the
+    groups run one launch each.  Groups of one to three K blocks, some empty, C separate."""
+    rng = np.random.default_rng(G)
+    ks = [int(x) * 128 for x in rng.integers(0, 4, G)]
+    ks[0], ks[-1] = 128, 384
+    m, n = 96, 260
+    nonempty = sum(k > 0 for k in ks)
+    p = gen.k_grouped(m, n, ks, seed=G)
+    say("k-grouped many groups", G, nonempty)
+    c = cuda(p["c"])
+    d = torch.full_like(c, float("nan"))
+    dg.k_grouped_fp8_gemm_nt_contiguous((cuda(p["a"]), cuda(np.ascontiguousarray(p["sa"].T))),
+                                        (cuda(p["b"]), cuda(np.ascontiguousarray(p["sb"].T))), d, ks, c)
+    torch.cuda.synchronize()
+    o, T = oracle.k_grouped(p["a"], p["sa"], p["b"], p["sb"], ks, p["c"], want_abs=True)
+    got = d.cpu().numpy()
+    ok, st = check_fp32(got, o, T)
+    say("k-grouped many groups", st)
+    assert ok.all(), st
+    for g, k in enumerate(ks):
+        if k == 0:
+            assert np.array_equal(got[g], p["c"][g])
+
+
+def test_k_grouped_single_launch_equals_group_loop():
+    """The one-launch K-grouped kernel and one dense launch per group (same tile, same
+    per-element order of MFMAs and promotions) give the same bits."""
+    ks = [256, 0, 640, 128, 1024]
+    m, n = 516, 516
+    p = gen.k_grouped(m, n, ks, seed=77)
+    say("k-grouped single vs loop")
+    args = ((cuda(p["a"]), cuda(np.ascontiguousarray(p["sa"].T))), (cuda(p["b"]), cuda(np.ascontiguousarray(p["sb"].T))))
+    outs = []
+    for loop in (False, True):
+        d = torch.full_like(cuda(p["c"]), float("nan"))
+        with force_tile("256x256"), env_var("DG_KGROUP_LOOP", int(loop)):
+            dg.k_grouped_fp8_gemm_nt_contiguous(*args, d, ks, cuda(p["c"]))
+        torch.cuda.synchronize()
+        outs.append(d.cpu())
+    assert torch.equal(outs[0], outs[1])
+    o, T = oracle.k_grouped(p["a"], p["sa"], p["b"], p["sb"], ks, p["c"], want_abs=True)
+    ok, st = check_fp32(outs[0].numpy(), o, T)
+    assert ok.all(), st
