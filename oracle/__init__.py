@@ -23,8 +23,9 @@ Modules:
              float64 -> BF16 round-to-nearest-even
   layout  -- the scale-layout transform (MN-major, 4-aligned stride, UE8M0 x4 packing)
   gemm    -- dense NT, M-grouped contiguous, M-grouped masked and K-grouped references,
-             and the FP8 x FP4 GEMM (E2M1 weights with one scale per 32 K) in the dense and
-             M-grouped forms
+             the FP8 x FP4 GEMM (E2M1 weights with one scale per 32 K) in the dense and
+             M-grouped forms, and the nn / tn / tt operand layouts (operands stored
+             transposed)
   quant   -- the per-token-group FP8 cast (E4M3 codes and 1x128 FP32 scales)
 
 Parity pins: every function here is pinned by a `-m "not gpu"` test in
@@ -40,5 +41,6 @@ from .codecs import (e4m3_decode_table, e4m3_decode, ue8m0_encode, ue8m0_decode,
 from .layout import align4, transform_sf, unpack_ue8m0  # noqa: F401
 from .gemm import (gemm_nt, gemm_nt_points, grouped_contiguous, grouped_masked, k_grouped,
                    expand_scales_b, gemm_fp8_fp4_nt, gemm_fp8_fp4_nt_points, grouped_contiguous_fp8_fp4,
-                   grouped_masked_fp8_fp4)  # noqa: F401
+                   grouped_masked_fp8_fp4, LAYOUTS, as_mk, as_nk, gemm_layout, gemm_layout_points,
+                   grouped_contiguous_nn, k_grouped_tn, gemm_fp8_fp4_tt)  # noqa: F401
 from .quant import e4m3_encode_rne, per_token_group_cast  # noqa: F401

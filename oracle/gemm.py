@@ -291,3 +291,58 @@ def grouped_masked_fp8_fp4(a_codes, sa, b_packed, sb, masked_m, want_abs=False):
         else:
             D[g, :m] = r
     return (D, T) if want_abs else D
+
+
+# ---- operand layouts ---------------------------------------------------------------------
+# Page "第13章 DeepGEMM" §13.3: the two suffix letters give the transposition state of A and
+# B in D = C + A @ B, so fp8_gemm_nt is D = C + A @ B.T, and the family also has nn, tn and tt
+# (the K-grouped weight-gradient form is named tn, §13.13; page "02 · DeepGEMM 技术解析" §5.1
+# names an nn form of the M-grouped contiguous GEMM).  Reading taken here: "n" on A means A is
+# stored [M, K]; "t" on A means A is stored [K, M] and enters as its transpose; "n" on B means B
+# is stored [K, N]; "t" on B means B is stored [N, K] and enters as its transpose.  Scales keep
+# their logical meaning whatever the storage: one per row of the [M, K] operand and 128-long K
+# block, and one per 128x128 (or per row) block of the [N, K] operand; only where the bytes of
+# the operands sit changes.
+
+LAYOUTS = ("nt", "nn", "tn", "tt")
+
+
+def as_mk(a_stored, layout):
+    """The [M, K] operand A of D = C + A @ B^T from A as stored under ``layout``."""
+    assert layout in LAYOUTS
+    return a_stored if layout[0] == "n" else np.asarray(a_stored).T
+
+
+def as_nk(b_stored, layout):
+    """The [N, K] operand B of D = C + A @ B^T from B as stored under ``layout``."""
+    assert layout in LAYOUTS
+    return b_stored if layout[1] == "t" else np.swapaxes(np.asarray(b_stored), -1, -2)
+
+
+def gemm_layout(layout, a_stored, sa, b_stored, sb, gran_n=128, c=None, want_abs=False):
+    """Dense GEMM under one of the four operand layouts: the NT definition applied to the
+    operands read through their storage (``as_mk``, ``as_nk``)."""
+    return gemm_nt(as_mk(a_stored, layout), sa, as_nk(b_stored, layout), sb, gran_n, c=c, want_abs=want_abs)
+
+
+def gemm_layout_points(layout, a_stored, sa, b_stored, sb, ii, jj, gran_n=128, c=None):
+    """``gemm_layout`` at output positions (ii[p], jj[p]); returns (D, T)."""
+    a = np.ascontiguousarray(as_mk(a_stored, layout))
+    b = np.ascontiguousarray(as_nk(b_stored, layout))
+    return gemm_nt_points(a, sa, b, sb, ii, jj, gran_n, c=c)
+
+
+def grouped_contiguous_nn(a_codes, sa, b_stored, sb, grouped_layout, gran_n=128, want_abs=False):
+    """M-grouped contiguous GEMM with each group's B stored [K, N] (b_stored [G, K, N])."""
+    return grouped_contiguous(a_codes, sa, as_nk(b_stored, "nn"), sb, grouped_layout, gran_n, want_abs=want_abs)
+
+
+def k_grouped_tn(a_stored, sa, b_stored, sb, ks, c, want_abs=False):
+    """K-grouped contiguous GEMM with both operands stored K-outermost: A [sum K, M] and
+    B [sum K, N] (the weight-gradient operands as the forward pass leaves them, token-major)."""
+    return k_grouped(as_mk(a_stored, "tn"), sa, as_nk(b_stored, "tn"), sb, ks, c, want_abs=want_abs)
+
+
+def gemm_fp8_fp4_tt(a_stored, sa, b_packed, sb, c=None, want_abs=False):
+    """FP8 x FP4 GEMM with A stored [K, M] and the packed FP4 weights stored [N, K/2]."""
+    return gemm_fp8_fp4_nt(as_mk(a_stored, "tt"), sa, b_packed, sb, c=c, want_abs=want_abs)

@@ -622,3 +622,123 @@ def test_fp8_fp4_points_and_grouped_forms():
     Dm = gemm.grouped_masked_fp8_fp4(r["a"], r["sa"], r["b"], r["sb"], mm)
     assert np.isnan(Dm[0]).all() and np.isnan(Dm[2, 4:]).all()
     assert np.array_equal(Dm[2, :4], gemm.gemm_fp8_fp4_nt(r["a"][2, :4], r["sa"][2, :4], r["b"][2], r["sb"][2]))
+
+
+# ---------------------------------------------------------------- operand layouts
+def _brute_layout(layout, a_st, sa, b_st, sb, gran_n, c):
+    """Exact value of D = C + op(A) @ op(B) written with the stored index of every operand
+    element: A[i, k] is a_st[i, k] for an "n" A and a_st[k, i] for a "t" A; B's element of
+    output column j at depth k is b_st[j, k] for a "t" B and b_st[k, j] for an "n" B."""
+    t = codecs.e4m3_decode_table()
+    M = a_st.shape[0] if layout[0] == "n" else a_st.shape[1]
+    K = a_st.shape[1] if layout[0] == "n" else a_st.shape[0]
+    N = b_st.shape[0] if layout[1] == "t" else b_st.shape[1]
+    D = np.empty((M, N))
+    for i in range(M):
+        for j in range(N):
+            acc = Fraction(float(c[i, j]))
+            for k in range(K):
+                av = a_st[i, k] if layout[0] == "n" else a_st[k, i]
+                bv = b_st[j, k] if layout[1] == "t" else b_st[k, j]
+                acc += (Fraction(float(sa[i, k // 128])) * Fraction(float(sb[j // gran_n, k // 128])) *
+                        Fraction(float(t[av])) * Fraction(float(t[bv])))
+            D[i, j] = float(acc)
+    return D
+
+
+@pytest.mark.parametrize("layout", ["nt", "nn", "tn", "tt"])
+@pytest.mark.parametrize("gran_n", [128, 1])
+def test_gemm_layouts_vs_brute_force(layout, gran_n):
+    """Every layout against exact arithmetic on the stored operands; M, N and K all differ, so
+    reading an operand through the wrong storage changes the shape or the values."""
+    rng = np.random.default_rng(100 + 7 * len(layout) + gran_n + ord(layout[0]) + 3 * ord(layout[1]))
+    M, N, K = 3, 5, 256
+    a, sa, b, sb = _random_tiny(rng, M, N, K, gran_n)
+    a_st = a if layout[0] == "n" else np.ascontiguousarray(a.T)
+    b_st = b if layout[1] == "t" else np.ascontiguousarray(b.T)
+    c = rng.standard_normal((M, N)).astype(np.float32)
+    D, T = oracle.gemm_layout(layout, a_st, sa, b_st, sb, gran_n, c=c, want_abs=True)
+    assert D.shape == (M, N)
+    Dx = _brute_layout(layout, a_st, sa, b_st, sb, gran_n, c)
+    assert np.all(np.abs(D - Dx) <= 2.0 ** -48 * (T + np.abs(c)))
+    ii, jj = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
+    Dp, _ = oracle.gemm_layout_points(layout, a_st, sa, b_st, sb, ii.ravel(), jj.ravel(), gran_n, c=c)
+    assert np.all(np.abs(Dp - Dx.ravel()) <= 2.0 ** -48 * (T.ravel() + np.abs(c).ravel()))
+
+
+def test_gemm_layout_transpose_is_not_the_identity():
+    """A square stored A (M = K = 128) that is not symmetric: reading it under "tt" differs
+    from reading it under "nt", and "tt" on its transpose is "nt" on it."""
+    rng = np.random.default_rng(5)
+    a, sa, b, sb = _random_tiny(rng, 128, 4, 128, 1)
+    d_nt = oracle.gemm_layout("nt", a, sa, b, sb, 1)
+    d_tt = oracle.gemm_layout("tt", a, sa, b, sb, 1)
+    assert not np.allclose(d_nt, d_tt)
+    assert np.array_equal(d_nt, oracle.gemm_layout("tt", np.ascontiguousarray(a.T), sa, b, sb, 1))
+
+
+def test_grouped_contiguous_nn_vs_brute_force():
+    rng = np.random.default_rng(19)
+    G, N, K = 2, 5, 256
+    rows = np.array([1, 1, -1, 0, 0, 0], dtype=np.int32)
+    a, sa, _, _ = _random_tiny(rng, len(rows), 1, K, 128)
+    b = np.stack([np.ascontiguousarray(_random_tiny(rng, 1, N, K, 128)[2].T) for _ in range(G)])  # [G, K, N]
+    sb = np.stack([_random_tiny(rng, 1, N, K, 128)[3] for _ in range(G)])
+    D = oracle.grouped_contiguous_nn(a, sa, b, sb, rows)
+    for i, g in enumerate(rows):
+        if g < 0:
+            assert np.isnan(D[i]).all()
+            continue
+        Dx = _brute_layout("nn", a[i:i + 1], sa[i:i + 1], b[g], sb[g], 128, np.zeros((1, N)))
+        assert np.allclose(D[i], Dx[0], rtol=1e-13, atol=0)
+
+
+def test_k_grouped_tn_vs_brute_force():
+    """K-grouped with token-major operands (A [sum K, M], B [sum K, N]): each group sums its own
+    K range of the stored rows into its own output on top of its C."""
+    rng = np.random.default_rng(23)
+    M, N, ks = 3, 2, [128, 256, 0]
+    K = sum(ks)
+    a_st = rng.integers(0, 256, (K, M), dtype=np.uint8)
+    b_st = rng.integers(0, 256, (K, N), dtype=np.uint8)
+    a_st[(a_st & 0x7F) == 0x7F] = 0x31
+    b_st[(b_st & 0x7F) == 0x7F] = 0x31
+    sa = np.exp2(rng.uniform(-4, 2, (M, K // 128))).astype(np.float32)
+    sb = np.exp2(rng.uniform(-4, 2, (N, K // 128))).astype(np.float32)
+    c = rng.standard_normal((len(ks), M, N)).astype(np.float32)
+    got = oracle.k_grouped_tn(a_st, sa, b_st, sb, ks, c)
+    t = codecs.e4m3_decode_table()
+    k0 = 0
+    for g, kg in enumerate(ks):
+        for i in range(M):
+            for j in range(N):
+                exact, mag = Fraction(float(c[g, i, j])), abs(Fraction(float(c[g, i, j])))
+                for k in range(k0, k0 + kg):
+                    p = (Fraction(float(sa[i, k // 128])) * Fraction(float(sb[j, k // 128])) *
+                         Fraction(float(t[a_st[k, i]])) * Fraction(float(t[b_st[k, j]])))
+                    exact += p
+                    mag += abs(p)
+                assert abs(Fraction(float(got[g, i, j])) - exact) <= Fraction(1, 10 ** 14) * mag
+        k0 += kg
+
+
+def test_fp8_fp4_tt_vs_brute_force():
+    """FP8 x FP4 with A stored [K, M]: exact sum over the stored activations and the packed
+    weight nibbles (low nibble = even K), each 32-long group with its own weight scale."""
+    rng = np.random.default_rng(29)
+    M, N, K = 3, 4, 256
+    a_st = rng.integers(0, 256, (K, M), dtype=np.uint8)
+    a_st[(a_st & 0x7F) == 0x7F] = 0x2A
+    b = rng.integers(0, 256, (N, K // 2), dtype=np.uint8)
+    sa = np.exp2(rng.integers(-3, 3, (M, K // 128))).astype(np.float32)
+    sb = np.exp2(rng.integers(-3, 3, (N, K // 32))).astype(np.float32)
+    got = oracle.gemm_fp8_fp4_tt(a_st, sa, b, sb)
+    t8, t4 = codecs.e4m3_decode_table(), codecs.e2m1_decode_table()
+    for i in range(M):
+        for j in range(N):
+            exact = Fraction(0)
+            for k in range(K):
+                nib = (b[j, k // 2] >> (4 * (k % 2))) & 0xF
+                exact += (Fraction(float(sa[i, k // 128])) * Fraction(float(sb[j, k // 32])) *
+                          Fraction(float(t8[a_st[k, i]])) * Fraction(float(t4[nib])))
+            assert Fraction(float(got[i, j])) == exact        # every partial and sum is exact here
