@@ -22,7 +22,8 @@ import os
 import torch
 
 __all__ = [
-    "DGError", "lib", "fp8_gemm_nt", "m_grouped_fp8_gemm_nt_contiguous", "m_grouped_fp8_gemm_nt_masked",
+    "DGError", "lib", "fp8_gemm_nt", "fp8_gemm_nn", "fp8_gemm_tn", "fp8_gemm_tt", "m_grouped_fp8_gemm_nt_contiguous",
+    "m_grouped_fp8_gemm_nn_contiguous", "m_grouped_fp8_gemm_nt_masked", "fp8_fp4_gemm_tt",
     "transform_sf", "get_mn_major_tma_aligned_tensor", "get_mn_major_tma_aligned_packed_ue8m0_tensor",
     "per_token_group_cast_fp8", "k_grouped_fp8_gemm_nt_contiguous", "transform_sf_into_required_layout",
     "fp8_fp4_gemm_nt", "m_grouped_fp8_fp4_gemm_nt_contiguous", "m_grouped_fp8_fp4_gemm_nt_masked", "get_tma_aligned_size", "get_mk_alignment_for_contiguous_layout", "set_num_sms", "get_num_sms",
@@ -37,13 +38,17 @@ DG_IN_BF16, DG_IN_F32 = 1, 2
 
 _i32, _i64, _p = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
 _SIGS = {
-    "dg_fp8_gemm_nt": (_i32, [_i32, _i32, _i32, _p, _i64, _p, _i64, _p, _i64, _p, _i64, _i32, _i32,
-                              _p, _i64, _p, _i64, _i32, _p]),
+    **{f"dg_fp8_gemm_{lay}": (_i32, [_i32, _i32, _i32, _p, _i64, _p, _i64, _p, _i64, _p, _i64, _i32, _i32,
+                                     _p, _i64, _p, _i64, _i32, _p]) for lay in ("nt", "nn", "tn", "tt")},
     "dg_m_grouped_fp8_gemm_nt_contiguous": (_i32, [_i32, _i32, _i32, _i32, _p, _i64, _p, _i64, _p, _i64, _i64,
+                                                   _p, _i64, _i64, _i32, _i32, _p, _i64, _i32, _p, _p]),
+    "dg_m_grouped_fp8_gemm_nn_contiguous": (_i32, [_i32, _i32, _i32, _i32, _p, _i64, _p, _i64, _p, _i64, _i64,
                                                    _p, _i64, _i64, _i32, _i32, _p, _i64, _i32, _p, _p]),
     "dg_m_grouped_fp8_gemm_nt_masked": (_i32, [_i32, _i32, _i32, _i32, _p, _i64, _i64, _p, _i64, _i64, _p, _i64,
                                                _i64, _p, _i64, _i64, _i32, _i32, _p, _i64, _i64, _i32, _p, _i32, _p]),
     "dg_fp8_fp4_gemm_nt": (_i32, [_i32, _i32, _i32, _p, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _i64,
+                                  _i32, _p]),
+    "dg_fp8_fp4_gemm_tt": (_i32, [_i32, _i32, _i32, _p, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _i64,
                                   _i32, _p]),
     "dg_m_grouped_fp8_fp4_gemm_nt_contiguous": (_i32, [_i32, _i32, _i32, _i32, _p, _i64, _p, _i64, _p, _i64, _i64,
                                                        _p, _i64, _i64, _p, _i64, _i32, _p, _p]),
@@ -103,11 +108,11 @@ def _a4(x):
     return (int(x) + 3) // 4 * 4
 
 
-def _codes(t):
+def _codes(t, inner="K"):
     if t.dtype not in (torch.uint8, torch.float8_e4m3fn):
         raise TypeError(f"E4M3 operands must be uint8 codes or float8_e4m3fn, got {t.dtype}")
     if t.stride(-1) != 1:
-        raise ValueError("E4M3 operands must be K-contiguous")
+        raise ValueError(f"E4M3 operands must be contiguous along their last dimension ({inner})")
     return t
 
 
@@ -297,24 +302,54 @@ def _recipe_gran_n(recipe, sfa, sfb, n, pack):
 
 
 # ---------------------------------------------------------------- GEMMs
-def fp8_gemm_nt(a, b, d, c=None, recipe=None, pack_ue8m0=False):
-    """D = C + A @ B.T.  ``a = (A [M, K], sfa)``, ``b = (B [N, K], sfb)``, ``d`` [M, N]
-    BF16 or FP32 (preallocated); ``c`` optional FP32 [M, N] (may be ``d`` itself)."""
+def _fp8_gemm(layout, a, b, d, c, recipe, pack_ue8m0):
+    """The four operand layouts (page "第13章 DeepGEMM" §13.3): layout[0] "n" = A [M, K], "t" = A
+    stored [K, M]; layout[1] "t" = B [N, K], "n" = B stored [K, N].  Scales keep their meaning
+    (per row of the [M, K] operand, per block or row of the [N, K] one)."""
     A, sfa = a
     B, sfb = b
-    _codes(A)
-    _codes(B)
-    M, K = A.shape
-    N = B.shape[0]
+    _codes(A, "K" if layout[0] == "n" else "M")
+    _codes(B, "K" if layout[1] == "t" else "N")
+    M, K = A.shape if layout[0] == "n" else (A.shape[1], A.shape[0])
+    N = B.shape[0] if layout[1] == "t" else B.shape[1]
+    kb = B.shape[1] if layout[1] == "t" else B.shape[0]
+    if kb != K:
+        raise ValueError(f"A and B disagree on K ({K} and {kb})")
     sf_k = (K + 127) // 128
     gran_n = _recipe_gran_n(recipe, sfa, sfb, N, pack_ue8m0)
     sfa_t, fmt = _act_scales(sfa, M, sf_k, pack_ue8m0)
     sfb_t, sfb_stride = _weight_scales(sfb, N, sf_k, gran_n, fmt)
-    _check(lib().dg_fp8_gemm_nt(M, N, K, _ptr(A), A.stride(0), _ptr(sfa_t), sfa_t.stride(-1) if M > 0 else 0,
-                                _ptr(B), B.stride(0), _ptr(sfb_t), sfb_stride, fmt, gran_n,
-                                _ptr(c), c.stride(0) if c is not None else 0,
-                                _ptr(d), d.stride(0), _out_dtype(d), _stream(d)))
+    fn = getattr(lib(), "dg_fp8_gemm_" + layout)
+    _check(fn(M, N, K, _ptr(A), A.stride(0), _ptr(sfa_t), sfa_t.stride(-1) if M > 0 else 0,
+              _ptr(B), B.stride(0), _ptr(sfb_t), sfb_stride, fmt, gran_n,
+              _ptr(c), c.stride(0) if c is not None else 0,
+              _ptr(d), d.stride(0), _out_dtype(d), _stream(d)))
     return d
+
+
+def fp8_gemm_nt(a, b, d, c=None, recipe=None, pack_ue8m0=False):
+    """D = C + A @ B.T.  ``a = (A [M, K], sfa)``, ``b = (B [N, K], sfb)``, ``d`` [M, N]
+    BF16 or FP32 (preallocated); ``c`` optional FP32 [M, N] (may be ``d`` itself)."""
+    return _fp8_gemm("nt", a, b, d, c, recipe, pack_ue8m0)
+
+
+def fp8_gemm_nn(a, b, d, c=None, recipe=None, pack_ue8m0=False):
+    """D = C + A @ B with ``a = (A [M, K], sfa)`` and ``b = (B [K, N], sfb)`` (B N-contiguous);
+    scales as in ``fp8_gemm_nt``.  K must be at least 256."""
+    return _fp8_gemm("nn", a, b, d, c, recipe, pack_ue8m0)
+
+
+def fp8_gemm_tn(a, b, d, c=None, recipe=None, pack_ue8m0=False):
+    """D = C + A.T @ B with ``a = (A [K, M], sfa)`` and ``b = (B [K, N], sfb)`` (both stored
+    K-outermost, as token-major activations and gradients are); scales as in ``fp8_gemm_nt``
+    (sfa per output row m and 128-long K block).  K must be at least 256."""
+    return _fp8_gemm("tn", a, b, d, c, recipe, pack_ue8m0)
+
+
+def fp8_gemm_tt(a, b, d, c=None, recipe=None, pack_ue8m0=False):
+    """D = C + A.T @ B.T with ``a = (A [K, M], sfa)`` and ``b = (B [N, K], sfb)``; scales as in
+    ``fp8_gemm_nt``.  K must be at least 256."""
+    return _fp8_gemm("tt", a, b, d, c, recipe, pack_ue8m0)
 
 
 def k_grouped_fp8_gemm_nt_contiguous(a, b, d, ks, c):
@@ -348,19 +383,32 @@ def k_grouped_fp8_gemm_nt_contiguous(a, b, d, ks, c):
 def m_grouped_fp8_gemm_nt_contiguous(a, b, d, grouped_layout, recipe=None, pack_ue8m0=False):
     """Rows of A [sum M_g, K] grouped by ``grouped_layout`` (int32 [sum M_g], -1 = padding);
     ``b = (B [G, N, K], sfb [G, ...])``; D [sum M_g, N]."""
+    return _m_grouped_contiguous("nt", a, b, d, grouped_layout, recipe, pack_ue8m0)
+
+
+def m_grouped_fp8_gemm_nn_contiguous(a, b, d, grouped_layout, recipe=None, pack_ue8m0=False):
+    """As ``m_grouped_fp8_gemm_nt_contiguous`` with each group's weights stored [K, N]:
+    ``b = (B [G, K, N], sfb [G, ...])`` (page "02 · DeepGEMM 技术解析" §5.1).  K >= 256."""
+    return _m_grouped_contiguous("nn", a, b, d, grouped_layout, recipe, pack_ue8m0)
+
+
+def _m_grouped_contiguous(layout, a, b, d, grouped_layout, recipe, pack_ue8m0):
     A, sfa = a
     B, sfb = b
     _codes(A)
-    _codes(B)
+    _codes(B, "K" if layout == "nt" else "N")
     M, K = A.shape
-    G, N, _ = B.shape
+    G, N = B.shape[0], (B.shape[1] if layout == "nt" else B.shape[2])
+    if (B.shape[2] if layout == "nt" else B.shape[1]) != K:
+        raise ValueError("A and B disagree on K")
     sf_k = (K + 127) // 128
     gran_n = _recipe_gran_n(recipe, sfa, sfb, N, pack_ue8m0)
     sfa_t, fmt = _act_scales(sfa, M, sf_k, pack_ue8m0)
     sfb_t, sfb_stride = _weight_scales(sfb, N, sf_k, gran_n, fmt)
     if grouped_layout.dtype != torch.int32 or not grouped_layout.is_contiguous():
         raise ValueError("grouped_layout must be contiguous int32")
-    _check(lib().dg_m_grouped_fp8_gemm_nt_contiguous(
+    fn = getattr(lib(), f"dg_m_grouped_fp8_gemm_{layout}_contiguous")
+    _check(fn(
         M, N, K, G, _ptr(A), A.stride(0), _ptr(sfa_t), sfa_t.stride(-1), _ptr(B), B.stride(1), B.stride(0),
         _ptr(sfb_t), sfb_stride, sfb_t.stride(0), fmt, gran_n, _ptr(d), d.stride(0), _out_dtype(d),
         _ptr(grouped_layout), _stream(d)))
@@ -428,15 +476,24 @@ def fp8_fp4_gemm_nt(a, b, d, c=None):
     """D = C + A @ B.T with FP8 activations and FP4 weights.  ``a = (A [M, K] E4M3, sfa)``,
     sfa one power-of-two scale per row and 128 K; ``b = (B [N, K // 2] packed E2M1, sfb)``,
     sfb one power-of-two scale per row and 32 K; ``d`` [M, N] BF16 or FP32; ``c`` optional FP32."""
+    return _fp8_fp4_gemm("nt", a, b, d, c)
+
+
+def fp8_fp4_gemm_tt(a, b, d, c=None):
+    """As ``fp8_fp4_gemm_nt`` with the activations stored [K, M] (``a = (A [K, M], sfa)``)."""
+    return _fp8_fp4_gemm("tt", a, b, d, c)
+
+
+def _fp8_fp4_gemm(layout, a, b, d, c):
     A, sfa = a
     B, sfb = b
-    _codes(A)
-    M, K = A.shape
+    _codes(A, "K" if layout == "nt" else "M")
+    M, K = A.shape if layout == "nt" else (A.shape[1], A.shape[0])
     _fp4_codes(B, K)
     N = B.shape[0]
     sfa_t = _fp4_act_scales(sfa, M)
     sfb_t = _fp4_weight_scales(sfb, N, K)
-    _check(lib().dg_fp8_fp4_gemm_nt(M, N, K, _ptr(A), A.stride(0), _ptr(sfa_t), sfa_t.stride(-1) if M > 0 else 0,
+    _check(getattr(lib(), "dg_fp8_fp4_gemm_" + layout)(M, N, K, _ptr(A), A.stride(0), _ptr(sfa_t), sfa_t.stride(-1) if M > 0 else 0,
                                     _ptr(B), B.stride(0), _ptr(sfb_t), sfb_t.stride(-1) if N > 0 else 0,
                                     _ptr(c), c.stride(0) if c is not None else 0,
                                     _ptr(d), d.stride(0), _out_dtype(d), _stream(d)))

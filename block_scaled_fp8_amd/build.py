@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libdg.so")
 NUM_TILES = 9
-PIPE_PARTS = 4   # dg_gemm_pipe.hip: dense, contiguous, masked, FP4 weights
+PIPE_PARTS = 7   # dg_gemm_pipe.hip: dense, contiguous, masked, FP4 weights, MN-major A, B, both
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

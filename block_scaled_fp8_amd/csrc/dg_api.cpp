@@ -72,7 +72,7 @@ struct Plan {
 };
 
 // kind: 0 dense, 1 contiguous, 2 masked.  m: rows (masked: expected rows per group).
-Plan plan_gemm(int kind, int m, int n, int k, int groups, int m_max, int sfm, int out, int num_sms) {
+Plan plan_gemm(int kind, int m, int n, int k, int groups, int m_max, int sfm, int out, int num_sms, int layout = 0) {
   Plan best;
   double best_cost = 1e300;
   const char* force = getenv("DG_FORCE_TILE");
@@ -80,8 +80,12 @@ Plan plan_gemm(int kind, int m, int n, int k, int groups, int m_max, int sfm, in
   if (force && sscanf(force, "%dx%d", &fbm, &fbn) != 2) fbm = fbn = 0;
   for (int t = 0; t < dg::kNumTiles; ++t) {
     const dg::TileCfg& c = dg::kTiles[t];
-    if (!dg::gemm_instantiated(t, sfm, kind, out)) continue;
+    if (!layout && !dg::gemm_instantiated(t, sfm, kind, out)) continue;
     if (fbm && (c.bm != fbm || c.bn != fbn)) continue;
+    // operands stored MN-major run on the pipelined kernel only
+    if (layout && (!dg::pipe_instantiated(c.bm, c.bn, sfm, kind, out, layout) ||
+                   k / 128 < dg::pipe_stages_b(c.bm, c.bn, kind)))
+      continue;
     // the 256-row pipelined tiles (1d2d scales) run out of registers with FP32 + C output
     // (the compiler spills them to scratch); they stay reachable only when forced
     if (!fbm && kind == 0 && out == dg::OUT_F32_C && sfm == dg::SF_1D2D_F32 && c.bm > 128) continue;
@@ -125,9 +129,10 @@ int sf_mode_of(int32_t sf_format, int32_t gran_n) {
 }
 
 // Checks shared by the three GEMM entry points.
+// layout: dg::LayoutBits of the operands (m: rows of D, for an A stored [k, m]).
 int check_common(int32_t n, int32_t k, const void* a, int64_t lda, const void* sfa, const void* b,
                  int64_t ldb, const void* sfb, int64_t sfb_stride, int32_t sf_format, int32_t gran_n,
-                 const void* d, int64_t ldd, int32_t d_dtype, bool empty) {
+                 const void* d, int64_t ldd, int32_t d_dtype, bool empty, int layout = 0, int32_t m = 0) {
   if (d_dtype != DG_OUT_BF16 && d_dtype != DG_OUT_F32) return fail(DG_ERR_DTYPE, "d_dtype %d is not DG_OUT_BF16 or DG_OUT_F32", d_dtype);
   if (sf_format != DG_SF_F32 && sf_format != DG_SF_UE8M0X4) return fail(DG_ERR_DTYPE, "sf_format %d is not DG_SF_F32 or DG_SF_UE8M0X4", sf_format);
   if (gran_n != 1 && gran_n != 128) return fail(DG_ERR_UNSUPPORTED, "gran_n %d: weight scales are per 128x128 block (128) or per row (1)", gran_n);
@@ -137,10 +142,22 @@ int check_common(int32_t n, int32_t k, const void* a, int64_t lda, const void* s
   if (n < 0) return fail(DG_ERR_SHAPE, "n = %d is negative", n);
   if (empty) return DG_OK;  // nothing is read or written: pointers may be NULL
   if (!a || !sfa || !b || !sfb || !d) return fail(DG_ERR_NULL, "a, sfa, b, sfb and d must not be NULL");
-  if (lda < k || lda % 16 != 0) return fail(DG_ERR_LAYOUT, "lda = %lld must be >= k and a multiple of 16", (long long)lda);
-  if (ldb < k || ldb % 16 != 0) return fail(DG_ERR_LAYOUT, "ldb = %lld must be >= k and a multiple of 16", (long long)ldb);
+  const bool amn = (layout & dg::LAYOUT_A_MN) != 0, bmn = (layout & dg::LAYOUT_B_MN) != 0;
+  if (amn) {
+    if (lda < m || lda % 16 != 0) return fail(DG_ERR_LAYOUT, "lda = %lld must be >= m (A stored [k, m]) and a multiple of 16", (long long)lda);
+  } else if (lda < k || lda % 16 != 0) {
+    return fail(DG_ERR_LAYOUT, "lda = %lld must be >= k and a multiple of 16", (long long)lda);
+  }
+  if (bmn) {
+    if (ldb < n || ldb % 16 != 0) return fail(DG_ERR_LAYOUT, "ldb = %lld must be >= n (B stored [k, n]) and a multiple of 16", (long long)ldb);
+  } else if (ldb < k || ldb % 16 != 0) {
+    return fail(DG_ERR_LAYOUT, "ldb = %lld must be >= k and a multiple of 16", (long long)ldb);
+  }
   // a tile's byte range (up to 256 rows of ld bytes) is a 32-bit signed count
   if (lda >= (int64_t(1) << 23) || ldb >= (int64_t(1) << 23)) return fail(DG_ERR_LAYOUT, "lda and ldb must be < 2^23 (tile byte ranges are 32-bit)");
+  // an MN-major operand's byte range runs to its end
+  if ((amn && int64_t(k) * lda >= (int64_t(1) << 31)) || (bmn && int64_t(k) * ldb >= (int64_t(1) << 31)))
+    return fail(DG_ERR_LAYOUT, "an operand stored [k, m] or [k, n] must span less than 2^31 bytes (k * ld)");
   if (!aligned16(a) || !aligned16(b)) return fail(DG_ERR_LAYOUT, "a and b must be 16-byte aligned");
   if (!aligned16(sfa) || !aligned16(sfb)) return fail(DG_ERR_LAYOUT, "sfa and sfb must be 16-byte aligned");
   const int64_t sf_k = k / 128;
@@ -160,7 +177,7 @@ int do_launch(dg::GemmParams& p, int kind, int32_t m_rows_for_plan, int32_t m_ma
   int num_sms = g_num_sms_override.load();
   if (num_sms <= 0) num_sms = device_cu_count();
   if (num_sms <= 0) return fail(DG_ERR_HIP, "could not query the device's compute-unit count");
-  Plan pl = plan_gemm(kind, m_rows_for_plan, p.n, p.k, p.num_groups, m_max, sfm, out, num_sms);
+  Plan pl = plan_gemm(kind, m_rows_for_plan, p.n, p.k, p.num_groups, m_max, sfm, out, num_sms, p.layout);
   if (pl.tile < 0) return fail(DG_ERR_UNSUPPORTED, "no tile configuration for this combination (check DG_FORCE_TILE)");
   const dg::TileCfg& c = dg::kTiles[pl.tile];
   p.num_n_tiles = pl.num_n_tiles;
@@ -187,7 +204,8 @@ int do_launch(dg::GemmParams& p, int kind, int32_t m_rows_for_plan, int32_t m_ma
   p.d_vec16 = ((p.ldd * esz) % 16 == 0 && (p.d_gstride * esz) % 16 == 0 && aligned16(p.d)) ? 1 : 0;
   // decode-shaped dense problems (at most 64 rows, 1d2d scales) stream B with the skinny
   // kernel: 16 or 32 columns per workgroup, so the grid covers the chip
-  if (kind == dg::GRP_DENSE && p.m <= 64 && sfm == dg::SF_1D2D_F32 && !getenv("DG_FORCE_TILE") && !env_int("DG_NO_SKINNY", 0)) {
+  if (kind == dg::GRP_DENSE && p.m <= 64 && sfm == dg::SF_1D2D_F32 && p.layout == 0 && !getenv("DG_FORCE_TILE") &&
+      !env_int("DG_NO_SKINNY", 0)) {
     // (32 columns measured faster than 16 at n = 7168 even with 224 workgroups on 256 CUs: every
     // workgroup reads all of A, which is most of its traffic; 16 only when 32 leaves most CUs idle)
     const int bn = env_int("DG_SKINNY_BN", 2 * ((p.n + 31) / 32) >= num_sms ? 32 : 16);
@@ -203,8 +221,9 @@ int do_launch(dg::GemmParams& p, int kind, int32_t m_rows_for_plan, int32_t m_ma
   // problems with at least as many K blocks as the deep-pipelined kernel keeps B stages run
   // that kernel when it has the chosen tile (one workgroup per CU: its LDS stages take most
   // of the 160 KiB)
-  const bool use_pipe = p.sf_k >= dg::pipe_stages_b(c.bm, c.bn, kind) && !env_int("DG_NO_PIPE", 0) &&
-                        dg::pipe_instantiated(c.bm, c.bn, sfm, kind, out);
+  // (the planner only offers pipelined tiles for operands stored MN-major)
+  const bool use_pipe = p.sf_k >= dg::pipe_stages_b(c.bm, c.bn, kind) && (p.layout || !env_int("DG_NO_PIPE", 0)) &&
+                        dg::pipe_instantiated(c.bm, c.bn, sfm, kind, out, p.layout);
   if (use_pipe) {
     const int occ = (160 * 1024) / dg::pipe_lds_bytes(c.bm, c.bn, sfm, kind);
     const int64_t slots = int64_t(num_sms) * (occ < 1 ? 1 : occ);
@@ -243,7 +262,7 @@ int launch_fp8_fp4(dg::GemmParams& p, int kind, int m_plan, int m_max, int out, 
   for (int i = 0; i < 2; ++i) {
     const Fp4Tile& t = cand[i];
     if (fbm && (t.bm != fbm || t.bn != fbn)) continue;
-    if (!dg::pipe_instantiated(t.bm, t.bn, dg::SF_FP4_UE8M0, kind, out)) continue;
+    if (!dg::pipe_instantiated(t.bm, t.bn, dg::SF_FP4_UE8M0, kind, out, p.layout)) continue;
     if (p.sf_k < dg::pipe_stages_b(t.bm, t.bn, kind)) continue;
     const int64_t mt = (m_plan + t.bm - 1) / t.bm, nt = (p.n + t.bn - 1) / t.bn;
     const int64_t tiles = (kind == dg::GRP_MASKED ? int64_t(p.num_groups) : 1) * mt * nt;
@@ -282,14 +301,20 @@ int launch_fp8_fp4(dg::GemmParams& p, int kind, int m_plan, int m_max, int out, 
 
 // Checks shared by the three FP8 x FP4 entry points.
 int check_fp8_fp4(int32_t n, int32_t k, const void* a, int64_t lda, const void* sfa, const void* b, int64_t ldb,
-                  const void* sfb, int64_t sfb_stride, const void* d, int64_t ldd, int32_t d_dtype, bool empty) {
+                  const void* sfb, int64_t sfb_stride, const void* d, int64_t ldd, int32_t d_dtype, bool empty,
+                  int layout = 0, int32_t m = 0) {
   if (d_dtype != DG_OUT_BF16 && d_dtype != DG_OUT_F32) return fail(DG_ERR_DTYPE, "d_dtype %d is not DG_OUT_BF16 or DG_OUT_F32", d_dtype);
   if (k <= 0 || k % 128 != 0) return fail(DG_ERR_SHAPE, "k = %d must be a positive multiple of 128", k);
   if (k < 256) return fail(DG_ERR_UNSUPPORTED, "the FP8 x FP4 GEMM needs k >= 256 (two K blocks), got %d", k);
   if (n < 0) return fail(DG_ERR_SHAPE, "n = %d is negative", n);
   if (empty) return DG_OK;
   if (!a || !sfa || !b || !sfb || !d) return fail(DG_ERR_NULL, "a, sfa, b, sfb and d must not be NULL");
-  if (lda < k || lda % 16 != 0) return fail(DG_ERR_LAYOUT, "lda = %lld must be >= k and a multiple of 16", (long long)lda);
+  if (layout & dg::LAYOUT_A_MN) {
+    if (lda < m || lda % 16 != 0) return fail(DG_ERR_LAYOUT, "lda = %lld must be >= m (A stored [k, m]) and a multiple of 16", (long long)lda);
+    if (int64_t(k) * lda >= (int64_t(1) << 31)) return fail(DG_ERR_LAYOUT, "an A stored [k, m] must span less than 2^31 bytes (k * lda)");
+  } else if (lda < k || lda % 16 != 0) {
+    return fail(DG_ERR_LAYOUT, "lda = %lld must be >= k and a multiple of 16", (long long)lda);
+  }
   if (ldb < k / 2 || ldb % 16 != 0) return fail(DG_ERR_LAYOUT, "ldb = %lld (bytes of packed FP4) must be >= k / 2 and a multiple of 16", (long long)ldb);
   if (lda >= (int64_t(1) << 23) || ldb >= (int64_t(1) << 23)) return fail(DG_ERR_LAYOUT, "lda and ldb must be < 2^23 (tile byte ranges are 32-bit)");
   if (!aligned16(a) || !aligned16(b)) return fail(DG_ERR_LAYOUT, "a and b must be 16-byte aligned");
@@ -303,15 +328,80 @@ int check_fp8_fp4(int32_t n, int32_t k, const void* a, int64_t lda, const void* 
 
 }  // namespace
 
-extern "C" {
-
-int dg_fp8_gemm_nt(int32_t m, int32_t n, int32_t k, const void* a, int64_t lda, const void* sfa,
-                   int64_t sfa_stride, const void* b, int64_t ldb, const void* sfb, int64_t sfb_stride,
-                   int32_t sf_format, int32_t gran_n, const float* c, int64_t ldc, void* d, int64_t ldd,
-                   int32_t d_dtype, hipStream_t stream) {
+// The four operand layouts of the dense FP8 GEMM (layout: dg::LayoutBits).
+static int fp8_gemm(int layout, int32_t m, int32_t n, int32_t k, const void* a, int64_t lda, const void* sfa,
+                    int64_t sfa_stride, const void* b, int64_t ldb, const void* sfb, int64_t sfb_stride,
+                    int32_t sf_format, int32_t gran_n, const float* c, int64_t ldc, void* d, int64_t ldd,
+                    int32_t d_dtype, hipStream_t stream) {
   if (m < 0) return fail(DG_ERR_SHAPE, "m = %d is negative", m);
   int st = check_common(n, k, a, lda, sfa, b, ldb, sfb, sfb_stride, sf_format, gran_n, d, ldd, d_dtype,
-                        m == 0 || n == 0);
+                        m == 0 || n == 0, layout, m);
+  if (st != DG_OK) return st;
+  if (layout && k < 256) return fail(DG_ERR_UNSUPPORTED, "operands stored [k, m] or [k, n] need k >= 256 (two K blocks), got %d", k);
+  if (layout && sf_format == DG_SF_F32 && gran_n == 1)
+    return fail(DG_ERR_UNSUPPORTED, "operands stored [k, m] or [k, n] take 128x128 FP32 or per-row UE8M0 weight scales, not per-row FP32");
+  if (m == 0 || n == 0) return ok();
+  if (sfa_stride != align4(m)) return fail(DG_ERR_LAYOUT, "sfa must be MN-major with stride align4(m) = %lld, got %lld", (long long)align4(m), (long long)sfa_stride);
+  if (c) {
+    if (d_dtype != DG_OUT_F32) return fail(DG_ERR_UNSUPPORTED, "a C term requires an FP32 output");
+    if (ldc < n || (reinterpret_cast<uintptr_t>(c) & 3u) != 0) return fail(DG_ERR_LAYOUT, "c needs ldc >= n and 4-byte alignment");
+    if ((const void*)c == d && ldc != ldd) return fail(DG_ERR_LAYOUT, "c aliases d, so ldc must equal ldd");
+  }
+  dg::GemmParams p{};
+  p.a = (const uint8_t*)a; p.lda = lda;
+  p.sfa = sfa; p.sfa_stride = sfa_stride;
+  p.b = (const uint8_t*)b; p.ldb = ldb;
+  p.sfb = sfb; p.sfb_stride = sfb_stride;
+  p.c = c; p.ldc = ldc;
+  p.d = d; p.ldd = ldd;
+  p.m = m; p.n = n; p.k = k; p.num_groups = 1; p.sf_k = k / 128;
+  p.layout = layout;
+  const int out = c ? dg::OUT_F32_C : (d_dtype == DG_OUT_BF16 ? dg::OUT_BF16 : dg::OUT_F32);
+  return do_launch(p, dg::GRP_DENSE, m, 0, sf_mode_of(sf_format, gran_n), out, stream);
+}
+
+// M-grouped contiguous GEMM with K-major (layout 0) or MN-major (dg::LAYOUT_B_MN) weights.
+static int m_grouped_contiguous(int layout, int32_t m_total, int32_t n, int32_t k, int32_t num_groups,
+                                const void* a, int64_t lda, const void* sfa, int64_t sfa_stride,
+                                const void* b, int64_t ldb, int64_t b_group_stride,
+                                const void* sfb, int64_t sfb_stride, int64_t sfb_group_stride,
+                                int32_t sf_format, int32_t gran_n, void* d, int64_t ldd,
+                                int32_t d_dtype, const int32_t* grouped_layout, hipStream_t stream) {
+  if (m_total < 0) return fail(DG_ERR_SHAPE, "m_total = %d is negative", m_total);
+  if (num_groups <= 0) return fail(DG_ERR_SHAPE, "num_groups = %d must be positive", num_groups);
+  int st = check_common(n, k, a, lda, sfa, b, ldb, sfb, sfb_stride, sf_format, gran_n, d, ldd, d_dtype,
+                        m_total == 0 || n == 0, layout, m_total);
+  if (st != DG_OK) return st;
+  if (layout && k < 256) return fail(DG_ERR_UNSUPPORTED, "weights stored [k, n] need k >= 256 (two K blocks), got %d", k);
+  if (layout && sf_format == DG_SF_F32 && gran_n == 1)
+    return fail(DG_ERR_UNSUPPORTED, "weights stored [k, n] take 128x128 FP32 or per-row UE8M0 scales, not per-row FP32");
+  if (m_total == 0 || n == 0) return ok();
+  if (!grouped_layout) return fail(DG_ERR_NULL, "grouped_layout must not be NULL");
+  if (sfa_stride != align4(m_total)) return fail(DG_ERR_LAYOUT, "sfa must be MN-major with stride align4(m_total) = %lld, got %lld", (long long)align4(m_total), (long long)sfa_stride);
+  const int64_t b_rows = layout ? int64_t(k) : int64_t(n);
+  if (b_group_stride < b_rows * ldb || b_group_stride % 16 != 0) return fail(DG_ERR_LAYOUT, "b_group_stride must be >= (n or k)*ldb and a multiple of 16");
+  const int64_t sfb_min = gran_n == 128 ? int64_t((n + 127) / 128) * sfb_stride
+                                        : (sf_format == DG_SF_UE8M0X4 ? int64_t((k / 128 + 3) / 4) : int64_t(k / 128)) * sfb_stride;
+  if (sfb_group_stride < sfb_min || (gran_n == 1 && sfb_group_stride % 4 != 0)) return fail(DG_ERR_LAYOUT, "sfb_group_stride = %lld is smaller than one group's scales (%lld) or misaligned", (long long)sfb_group_stride, (long long)sfb_min);
+  dg::GemmParams p{};
+  p.a = (const uint8_t*)a; p.lda = lda;
+  p.sfa = sfa; p.sfa_stride = sfa_stride;
+  p.b = (const uint8_t*)b; p.ldb = ldb; p.b_gstride = b_group_stride;
+  p.sfb = sfb; p.sfb_stride = sfb_stride; p.sfb_gstride = sfb_group_stride;
+  p.d = d; p.ldd = ldd;
+  p.grouped_layout = grouped_layout;
+  p.m = m_total; p.n = n; p.k = k; p.num_groups = num_groups; p.sf_k = k / 128;
+  p.layout = layout;
+  const int out = d_dtype == DG_OUT_BF16 ? dg::OUT_BF16 : dg::OUT_F32;
+  return do_launch(p, dg::GRP_CONTIG, m_total, 0, sf_mode_of(sf_format, gran_n), out, stream);
+}
+
+// Dense FP8 x FP4 GEMM with A stored [m, k] (layout 0) or [k, m] (dg::LAYOUT_A_MN).
+static int fp8_fp4_gemm(int layout, int32_t m, int32_t n, int32_t k, const void* a, int64_t lda, const void* sfa,
+                        int64_t sfa_stride, const void* b, int64_t ldb, const void* sfb, int64_t sfb_stride,
+                        const float* c, int64_t ldc, void* d, int64_t ldd, int32_t d_dtype, hipStream_t stream) {
+  if (m < 0) return fail(DG_ERR_SHAPE, "m = %d is negative", m);
+  int st = check_fp8_fp4(n, k, a, lda, sfa, b, ldb, sfb, sfb_stride, d, ldd, d_dtype, m == 0 || n == 0, layout, m);
   if (st != DG_OK) return st;
   if (m == 0 || n == 0) return ok();
   if (sfa_stride != align4(m)) return fail(DG_ERR_LAYOUT, "sfa must be MN-major with stride align4(m) = %lld, got %lld", (long long)align4(m), (long long)sfa_stride);
@@ -328,8 +418,43 @@ int dg_fp8_gemm_nt(int32_t m, int32_t n, int32_t k, const void* a, int64_t lda, 
   p.c = c; p.ldc = ldc;
   p.d = d; p.ldd = ldd;
   p.m = m; p.n = n; p.k = k; p.num_groups = 1; p.sf_k = k / 128;
+  p.layout = layout;
   const int out = c ? dg::OUT_F32_C : (d_dtype == DG_OUT_BF16 ? dg::OUT_BF16 : dg::OUT_F32);
-  return do_launch(p, dg::GRP_DENSE, m, 0, sf_mode_of(sf_format, gran_n), out, stream);
+  return launch_fp8_fp4(p, dg::GRP_DENSE, m, 0, out, stream);
+}
+
+extern "C" {
+
+int dg_fp8_gemm_nt(int32_t m, int32_t n, int32_t k, const void* a, int64_t lda, const void* sfa,
+                   int64_t sfa_stride, const void* b, int64_t ldb, const void* sfb, int64_t sfb_stride,
+                   int32_t sf_format, int32_t gran_n, const float* c, int64_t ldc, void* d, int64_t ldd,
+                   int32_t d_dtype, hipStream_t stream) {
+  return fp8_gemm(0, m, n, k, a, lda, sfa, sfa_stride, b, ldb, sfb, sfb_stride, sf_format, gran_n, c, ldc, d, ldd,
+                  d_dtype, stream);
+}
+
+int dg_fp8_gemm_nn(int32_t m, int32_t n, int32_t k, const void* a, int64_t lda, const void* sfa,
+                   int64_t sfa_stride, const void* b, int64_t ldb, const void* sfb, int64_t sfb_stride,
+                   int32_t sf_format, int32_t gran_n, const float* c, int64_t ldc, void* d, int64_t ldd,
+                   int32_t d_dtype, hipStream_t stream) {
+  return fp8_gemm(dg::LAYOUT_B_MN, m, n, k, a, lda, sfa, sfa_stride, b, ldb, sfb, sfb_stride, sf_format, gran_n, c, ldc, d, ldd,
+                  d_dtype, stream);
+}
+
+int dg_fp8_gemm_tn(int32_t m, int32_t n, int32_t k, const void* a, int64_t lda, const void* sfa,
+                   int64_t sfa_stride, const void* b, int64_t ldb, const void* sfb, int64_t sfb_stride,
+                   int32_t sf_format, int32_t gran_n, const float* c, int64_t ldc, void* d, int64_t ldd,
+                   int32_t d_dtype, hipStream_t stream) {
+  return fp8_gemm(dg::LAYOUT_A_MN | dg::LAYOUT_B_MN, m, n, k, a, lda, sfa, sfa_stride, b, ldb, sfb, sfb_stride, sf_format, gran_n, c, ldc, d, ldd,
+                  d_dtype, stream);
+}
+
+int dg_fp8_gemm_tt(int32_t m, int32_t n, int32_t k, const void* a, int64_t lda, const void* sfa,
+                   int64_t sfa_stride, const void* b, int64_t ldb, const void* sfb, int64_t sfb_stride,
+                   int32_t sf_format, int32_t gran_n, const float* c, int64_t ldc, void* d, int64_t ldd,
+                   int32_t d_dtype, hipStream_t stream) {
+  return fp8_gemm(dg::LAYOUT_A_MN, m, n, k, a, lda, sfa, sfa_stride, b, ldb, sfb, sfb_stride, sf_format, gran_n, c, ldc, d, ldd,
+                  d_dtype, stream);
 }
 
 int dg_m_grouped_fp8_gemm_nt_contiguous(int32_t m_total, int32_t n, int32_t k, int32_t num_groups,
@@ -338,28 +463,18 @@ int dg_m_grouped_fp8_gemm_nt_contiguous(int32_t m_total, int32_t n, int32_t k, i
                                         const void* sfb, int64_t sfb_stride, int64_t sfb_group_stride,
                                         int32_t sf_format, int32_t gran_n, void* d, int64_t ldd,
                                         int32_t d_dtype, const int32_t* grouped_layout, hipStream_t stream) {
-  if (m_total < 0) return fail(DG_ERR_SHAPE, "m_total = %d is negative", m_total);
-  if (num_groups <= 0) return fail(DG_ERR_SHAPE, "num_groups = %d must be positive", num_groups);
-  int st = check_common(n, k, a, lda, sfa, b, ldb, sfb, sfb_stride, sf_format, gran_n, d, ldd, d_dtype,
-                        m_total == 0 || n == 0);
-  if (st != DG_OK) return st;
-  if (m_total == 0 || n == 0) return ok();
-  if (!grouped_layout) return fail(DG_ERR_NULL, "grouped_layout must not be NULL");
-  if (sfa_stride != align4(m_total)) return fail(DG_ERR_LAYOUT, "sfa must be MN-major with stride align4(m_total) = %lld, got %lld", (long long)align4(m_total), (long long)sfa_stride);
-  if (b_group_stride < int64_t(n) * ldb || b_group_stride % 16 != 0) return fail(DG_ERR_LAYOUT, "b_group_stride must be >= n*ldb and a multiple of 16");
-  const int64_t sfb_min = gran_n == 128 ? int64_t((n + 127) / 128) * sfb_stride
-                                        : (sf_format == DG_SF_UE8M0X4 ? int64_t((k / 128 + 3) / 4) : int64_t(k / 128)) * sfb_stride;
-  if (sfb_group_stride < sfb_min || (gran_n == 1 && sfb_group_stride % 4 != 0)) return fail(DG_ERR_LAYOUT, "sfb_group_stride = %lld is smaller than one group's scales (%lld) or misaligned", (long long)sfb_group_stride, (long long)sfb_min);
-  dg::GemmParams p{};
-  p.a = (const uint8_t*)a; p.lda = lda;
-  p.sfa = sfa; p.sfa_stride = sfa_stride;
-  p.b = (const uint8_t*)b; p.ldb = ldb; p.b_gstride = b_group_stride;
-  p.sfb = sfb; p.sfb_stride = sfb_stride; p.sfb_gstride = sfb_group_stride;
-  p.d = d; p.ldd = ldd;
-  p.grouped_layout = grouped_layout;
-  p.m = m_total; p.n = n; p.k = k; p.num_groups = num_groups; p.sf_k = k / 128;
-  const int out = d_dtype == DG_OUT_BF16 ? dg::OUT_BF16 : dg::OUT_F32;
-  return do_launch(p, dg::GRP_CONTIG, m_total, 0, sf_mode_of(sf_format, gran_n), out, stream);
+  return m_grouped_contiguous(0, m_total, n, k, num_groups, a, lda, sfa, sfa_stride, b, ldb, b_group_stride, sfb,
+                              sfb_stride, sfb_group_stride, sf_format, gran_n, d, ldd, d_dtype, grouped_layout, stream);
+}
+
+int dg_m_grouped_fp8_gemm_nn_contiguous(int32_t m_total, int32_t n, int32_t k, int32_t num_groups,
+                                        const void* a, int64_t lda, const void* sfa, int64_t sfa_stride,
+                                        const void* b, int64_t ldb, int64_t b_group_stride,
+                                        const void* sfb, int64_t sfb_stride, int64_t sfb_group_stride,
+                                        int32_t sf_format, int32_t gran_n, void* d, int64_t ldd,
+                                        int32_t d_dtype, const int32_t* grouped_layout, hipStream_t stream) {
+  return m_grouped_contiguous(dg::LAYOUT_B_MN, m_total, n, k, num_groups, a, lda, sfa, sfa_stride, b, ldb, b_group_stride, sfb,
+                              sfb_stride, sfb_group_stride, sf_format, gran_n, d, ldd, d_dtype, grouped_layout, stream);
 }
 
 int dg_m_grouped_fp8_gemm_nt_masked(int32_t num_groups, int32_t m_max, int32_t n, int32_t k, const void* a,
@@ -505,26 +620,13 @@ int dg_k_grouped_fp8_gemm_nt_contiguous(int32_t num_groups, int32_t m, int32_t n
 int dg_fp8_fp4_gemm_nt(int32_t m, int32_t n, int32_t k, const void* a, int64_t lda, const void* sfa,
                        int64_t sfa_stride, const void* b, int64_t ldb, const void* sfb, int64_t sfb_stride,
                        const float* c, int64_t ldc, void* d, int64_t ldd, int32_t d_dtype, hipStream_t stream) {
-  if (m < 0) return fail(DG_ERR_SHAPE, "m = %d is negative", m);
-  int st = check_fp8_fp4(n, k, a, lda, sfa, b, ldb, sfb, sfb_stride, d, ldd, d_dtype, m == 0 || n == 0);
-  if (st != DG_OK) return st;
-  if (m == 0 || n == 0) return ok();
-  if (sfa_stride != align4(m)) return fail(DG_ERR_LAYOUT, "sfa must be MN-major with stride align4(m) = %lld, got %lld", (long long)align4(m), (long long)sfa_stride);
-  if (c) {
-    if (d_dtype != DG_OUT_F32) return fail(DG_ERR_UNSUPPORTED, "a C term requires an FP32 output");
-    if (ldc < n || (reinterpret_cast<uintptr_t>(c) & 3u) != 0) return fail(DG_ERR_LAYOUT, "c needs ldc >= n and 4-byte alignment");
-    if ((const void*)c == d && ldc != ldd) return fail(DG_ERR_LAYOUT, "c aliases d, so ldc must equal ldd");
-  }
-  dg::GemmParams p{};
-  p.a = (const uint8_t*)a; p.lda = lda;
-  p.sfa = sfa; p.sfa_stride = sfa_stride;
-  p.b = (const uint8_t*)b; p.ldb = ldb;
-  p.sfb = sfb; p.sfb_stride = sfb_stride;
-  p.c = c; p.ldc = ldc;
-  p.d = d; p.ldd = ldd;
-  p.m = m; p.n = n; p.k = k; p.num_groups = 1; p.sf_k = k / 128;
-  const int out = c ? dg::OUT_F32_C : (d_dtype == DG_OUT_BF16 ? dg::OUT_BF16 : dg::OUT_F32);
-  return launch_fp8_fp4(p, dg::GRP_DENSE, m, 0, out, stream);
+  return fp8_fp4_gemm(0, m, n, k, a, lda, sfa, sfa_stride, b, ldb, sfb, sfb_stride, c, ldc, d, ldd, d_dtype, stream);
+}
+
+int dg_fp8_fp4_gemm_tt(int32_t m, int32_t n, int32_t k, const void* a, int64_t lda, const void* sfa,
+                       int64_t sfa_stride, const void* b, int64_t ldb, const void* sfb, int64_t sfb_stride,
+                       const float* c, int64_t ldc, void* d, int64_t ldd, int32_t d_dtype, hipStream_t stream) {
+  return fp8_fp4_gemm(dg::LAYOUT_A_MN, m, n, k, a, lda, sfa, sfa_stride, b, ldb, sfb, sfb_stride, c, ldc, d, ldd, d_dtype, stream);
 }
 
 int dg_m_grouped_fp8_fp4_gemm_nt_contiguous(int32_t m_total, int32_t n, int32_t k, int32_t num_groups,

@@ -111,6 +111,17 @@ __device__ __forceinline__ void copy_to_lds(const void* base, int bytes, uint32_
   __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(base, bytes), (DG_LDS void*)(smem + dst), 16, voff, 0, 0, 0);
 }
 
+typedef int v2i __attribute__((ext_vector_type(2)));
+
+// gfx950's transposing LDS read: in each group of 16 lanes, lane 2r + h names an 8-byte row
+// (r = 0..7, h = 0..1) and lane 8h + c receives byte c of rows 0..7 of its half h, so eight
+// bytes that sit one per row come back in one lane (measured lane layout of
+// ds_read_b64_tr_b8).  With rows = 8 consecutive K of an MN-major tile and the 16 bytes of a
+// row pair = 16 consecutive M, lane l gets 8 consecutive K of row l: an MFMA fragment piece.
+__device__ __forceinline__ v2i read_tr8(const uint8_t* smem, uint32_t addr) {
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((DG_LDS v2i*)(smem + addr));
+}
+
 // Keep a promoted fragment at this point of the instruction stream: its FMAs are pure
 // arithmetic that the compiler would otherwise sink to the end of the block, keeping every
 // block partial alive at once.
@@ -224,16 +235,25 @@ __device__ __forceinline__ void pin_src(Src& s) {
   asm volatile("" : "+s"(s.lo), "+s"(s.hi), "+s"(s.bytes), "+s"(s.slo), "+s"(s.shi), "+s"(s.sbytes));
 }
 
+// K-major operand (rows of K bytes): the block starts at byte kb * bkb of row r0 and the
+// range covers the tile's rows.  MN-major operand (mn: K rows of rows_total bytes, the tile
+// being columns r0..r0+R-1): the block starts at K row kb * 128, column r0, and the range ends
+// with the 16-byte granule that holds the last byte of the operand, so columns past rows_total
+// read the next K row (they only feed outputs that are never stored) or, past the end, zeros.
+// (The range check drops every dword that does not fit whole, so a range ending inside a
+// 16-byte copy would lose the valid bytes at its start; the granule shares its page with them.)
 __device__ __forceinline__ Src make_src(const uint8_t* X, int64_t ld, int r0, int rows_total, int R, int kb,
                                         bool valid, const void* sf, int64_t sf_stride, int64_t sf_row,
-                                        bool has_scales, int bkb) {
+                                        bool has_scales, int bkb, bool mn = false, int k = 0) {
   const int rows = valid ? max(0, min(rows_total - r0, R)) : 0;
-  const uint64_t base = (uint64_t)(X + (int64_t)r0 * ld + kb * bkb);
+  const uint64_t base = mn ? (uint64_t)(X + (int64_t)kb * BK * ld + r0) : (uint64_t)(X + (int64_t)r0 * ld + kb * bkb);
   const uint64_t sbase = (uint64_t)((const uint8_t*)sf + 4 * (sf_row * sf_stride + r0));
+  // (MN-major: k * ld < 2^31, checked on the host)
+  const int mn_bytes = (int)(((int64_t)(k - kb * BK - 1) * ld + rows_total - r0 + 15) & ~(int64_t)15);
   Src s;
   s.lo = __builtin_amdgcn_readfirstlane((uint32_t)base);
   s.hi = __builtin_amdgcn_readfirstlane((uint32_t)(base >> 32));
-  s.bytes = __builtin_amdgcn_readfirstlane(rows > 0 ? rows * (int)ld - kb * bkb : 0);
+  s.bytes = __builtin_amdgcn_readfirstlane(rows > 0 ? (mn ? mn_bytes : rows * (int)ld - kb * bkb) : 0);
   s.slo = __builtin_amdgcn_readfirstlane((uint32_t)sbase);
   s.shi = __builtin_amdgcn_readfirstlane((uint32_t)(sbase >> 32));
   s.sbytes = __builtin_amdgcn_readfirstlane((has_scales && valid) ? 4 * max(0, min((int)sf_stride - r0, R)) : 0);
@@ -245,21 +265,22 @@ __device__ __forceinline__ const void* src_ptr(uint32_t lo, uint32_t hi) {
 }
 
 // Source of K block k (counted from the start of tile `c`; k >= nkb lies in the next tile
-// `n`) from the two tiles' block-0 sources: rows advance by k * BKB bytes, scales by
-// srow(k) scale rows of `sstep` bytes (srow = k, or k / 4 for words that pack four K blocks).
-// A few scalar instructions instead of rebuilding the source from the tile position every block.
-template <bool PACK4, int BKB>
-__device__ __forceinline__ Src src_at(const Src& c, const Src& n, int k, int nkb, uint32_t sstep) {
+// `n`) from the two tiles' block-0 sources: rows advance by k * kstep bytes (the bytes of a
+// K block: BKB along a K-major row, 128 rows of an MN-major operand), scales by srow(k) scale
+// rows of `sstep` bytes (srow = k, or k / 4 for words that pack four K blocks).  A few scalar
+// instructions instead of rebuilding the source from the tile position every block.
+template <bool PACK4>
+__device__ __forceinline__ Src src_at(const Src& c, const Src& n, int k, int nkb, uint32_t sstep, uint32_t kstep) {
   const bool same = k < nkb;
   const int kk = same ? k : k - nkb;
-  const uint64_t base = ((uint64_t)(same ? c.hi : n.hi) << 32 | (same ? c.lo : n.lo)) + (uint32_t)(kk * BKB);
+  const uint64_t base = ((uint64_t)(same ? c.hi : n.hi) << 32 | (same ? c.lo : n.lo)) + (uint32_t)kk * kstep;
   const int srow = PACK4 ? kk >> 2 : kk;
   const uint64_t sbase = ((uint64_t)(same ? c.shi : n.shi) << 32 | (same ? c.slo : n.slo)) + (uint32_t)srow * sstep;
   Src s;
   s.lo = __builtin_amdgcn_readfirstlane((uint32_t)base);
   s.hi = __builtin_amdgcn_readfirstlane((uint32_t)(base >> 32));
-  // (a tile with rows has bytes > (nkb-1) * 128)
-  s.bytes = __builtin_amdgcn_readfirstlane(max((same ? c.bytes : n.bytes) - kk * BKB, 0));
+  // (a tile with rows has bytes > (nkb-1) * kstep)
+  s.bytes = __builtin_amdgcn_readfirstlane(max((same ? c.bytes : n.bytes) - kk * (int)kstep, 0));
   s.slo = __builtin_amdgcn_readfirstlane((uint32_t)sbase);
   s.shi = __builtin_amdgcn_readfirstlane((uint32_t)(sbase >> 32));
   s.sbytes = __builtin_amdgcn_readfirstlane(same ? c.sbytes : n.sbytes);
@@ -285,7 +306,7 @@ struct Carry {
   unsigned int ebw;     // UE8M0: packed weight-scale word of the lane's row in the first B fragment
 };
 
-template <int BM, int BN, int WM, int WN, int SFM, int OUT, int GRP, int NB>
+template <int BM, int BN, int WM, int WN, int SFM, int OUT, int GRP, int NB, int LAY>
 struct Kernel {
   // Per-row FP32 weight scales run on the generic kernel: here the B stage that holds a
   // block's scales is refilled before its last two partials are promoted.
@@ -295,6 +316,11 @@ struct Kernel {
   static constexpr bool FP4B = G::FP4B;
   // power-of-two scales applied by the matrix unit itself (no VALU promotion)
   static constexpr bool UE = SFM == SF_1D1D_UE8M0 || FP4B;
+  // operands stored MN-major (K rows of M or N bytes): staged as 16-column strips and read
+  // back with the transposing LDS read
+  static constexpr bool AMN = (LAY & LAYOUT_A_MN) != 0, BMN = (LAY & LAYOUT_B_MN) != 0;
+  static_assert(!(BMN && FP4B), "FP4 weights are K-major");
+  static constexpr int FBA = FP4B ? 4 : 5, FBB = 5;  // row-permutation bit of an MN-major stage
   static constexpr int FM = G::FM, FN = G::FN, TM = G::TM, TN = G::TN, STEPS = G::STEPS;
   static constexpr int NW = G::NW;
   static __device__ __forceinline__ int next_b(int b) { return b == NB - 1 ? 0 : b + 1; }
@@ -311,7 +337,8 @@ struct Kernel {
   uint32_t sa_lds;                  // per-lane LDS address of its rows' activation scales (stage 0)
   uint32_t ww_lds;                  // UE8M0: per-lane LDS address of its B row's packed weight scales (stage 0)
   int wshift;                       // FP4 weights: bit offset of this lane's 32-K block scale in the packed word
-  int ustep_a, ustep_b;             // 8 * NW * ld
+  int ustep_a, ustep_b;             // 8 * NW * ld (MN-major: 8 * NW)
+  uint32_t kstep_a, kstep_b;        // bytes of one K block along the source (BK or BKB; MN-major: BK * ld)
   uint32_t sstep_a, sstep_b;        // bytes per K-block row of the activation / per-row weight scales
   // masked groups (at most 64): lane g holds group g's valid rows and the inclusive prefix
   // sum of the tiles of groups 0..g, so a tile index maps to its group with one ballot
@@ -359,6 +386,39 @@ struct Kernel {
       b_lo = G::B_OFF + (wn * TN + lr) * BK + lo;
       b_hi = G::B_OFF + (wn * TN + lr) * BK + hi;
     }
+    kstep_a = BK;
+    kstep_b = G::BKB;
+    // MN-major operands.  A K block of a tile W columns wide sits in LDS as W/16 strips of
+    // 16 columns, each strip 128 rows of 16 bytes; K row k is stored at row position
+    // k ^ (bit FB of k) * 8.  The fragment reads of one 16-lane group take 8 K rows of one strip
+    // (128 contiguous bytes), and the two groups served together take rows whose bit FB
+    // differs, so the permutation puts them on the other half of the banks.  FB is 5 when a
+    // lane group holds K [32 lg, +32) (FP8 next to FP8) and 4 when it holds K [16 lg, +16) and
+    // K [64 + 16 lg, +16) (next to FP4 weights).  Wave-load q (1 KiB) fills strip q/2, row
+    // positions 64 (q % 2) + [0, 64): lane L copies 16 bytes of K row (64 (q % 2) + L) permuted.
+    auto mn_copy = [&](int64_t ld, int fb) -> uint32_t {
+      const uint32_t row = 64u * ((uint32_t)wave & 1u) + ((uint32_t)lane ^ ((((uint32_t)lane >> fb) & 1u) << 3));
+      return row * (uint32_t)ld + 16u * ((uint32_t)wave >> 1);
+    };
+    auto mn_read = [&](int off, int strip0, int fb, bool second) -> uint32_t {
+      const int l = lane & 15, flip = (lg & 1) ^ (second ? 1 : 0);
+      const int k0 = fb == 5 ? 32 * lg : 16 * lg;
+      return (uint32_t)(off + strip0 * 2048 + 16 * (k0 + 8 * flip + (l >> 1)) + 8 * (l & 1));
+    };
+    if constexpr (AMN) {
+      off_a = mn_copy(p.lda, FBA);
+      ustep_a = 8 * NW;
+      kstep_a = __builtin_amdgcn_readfirstlane(BK * (uint32_t)p.lda);
+      a_lo = mn_read(G::A_OFF, wm * TM / 16, FBA, false);
+      a_hi = mn_read(G::A_OFF, wm * TM / 16, FBA, true);
+    }
+    if constexpr (BMN) {
+      off_b = mn_copy(p.ldb, FBB);
+      ustep_b = 8 * NW;
+      kstep_b = __builtin_amdgcn_readfirstlane(BK * (uint32_t)p.ldb);
+      b_lo = mn_read(G::B_OFF, wn * TN / 16, FBB, false);
+      b_hi = mn_read(G::B_OFF, wn * TN / 16, FBB, true);
+    }
     wshift = 8 * lg;
     sa_lds = G::SA_OFF + 4 * (wm * TM + lr);
     ww_lds = G::SB_OFF + 4 * (wn * TN + lr);
@@ -402,7 +462,7 @@ struct Kernel {
       A += (int64_t)t.g * p.a_gstride;
       SA += 4 * (int64_t)t.g * p.sfa_gstride;
     }
-    return make_src(A, p.lda, t.m0, t.mv, BM, kb, t.valid, SA, p.sfa_stride, srow, true, BK);
+    return make_src(A, p.lda, t.m0, t.mv, BM, kb, t.valid, SA, p.sfa_stride, srow, true, BK, AMN, p.k);
   }
   __device__ __forceinline__ Src b_src(const TilePos& t, int kb) const {
     // (FP4 weights: one word per K block, holding its four 32-K scales)
@@ -415,7 +475,8 @@ struct Kernel {
     }
     // (a skipped contiguous tile reads no weights either)
     const bool valid = GRP == GRP_CONTIG ? t.valid && t.mv > 0 : t.valid;
-    return make_src(B, p.ldb, t.n0, p.n, BN, kb, valid, SB, p.sfb_stride, srow, SFM != SF_1D2D_F32, G::BKB);
+    return make_src(B, p.ldb, t.n0, p.n, BN, kb, valid, SB, p.sfb_stride, srow, SFM != SF_1D2D_F32, G::BKB, BMN,
+                    p.k);
   }
 
   // Part U of the copy of one operand block into the stage at LDS offset `dst` (its scales
@@ -473,8 +534,19 @@ struct Kernel {
     const v4i h4 = *(const v4i*)(smem + hi + off);
     return (v8i){l4.x, l4.y, l4.z, l4.w, h4.x, h4.y, h4.z, h4.w};
   }
+  // MN-major stage: four transposing reads of 8 K each; the second pair lies 16 rows
+  // further (FB = 5) or 64 rows further (FB = 4) than the first
+  template <int FB>
+  __device__ __forceinline__ v8i frag_tr(uint32_t lo, uint32_t hi, int off) const {
+    constexpr int D2 = FB == 5 ? 16 * 16 : 64 * 16;
+    const v2i x0 = read_tr8(smem, lo + off), x1 = read_tr8(smem, hi + off);
+    const v2i x2 = read_tr8(smem, lo + off + D2), x3 = read_tr8(smem, hi + off + D2);
+    return (v8i){x0.x, x0.y, x1.x, x1.y, x2.x, x2.y, x3.x, x3.y};
+  }
   __device__ __forceinline__ v8i a_frag(int aslot, int i) const {
     const uint32_t so = (uint32_t)(aslot * G::A_SLOT);
+    // (a 16-row fragment is 16 rows x 128 bytes, an MN-major strip 128 rows x 16 bytes)
+    if constexpr (AMN) return frag_tr<FBA>(a_lo + so, a_hi + so, i * 2048);
     return frag(a_lo + so, a_hi + so, i * 16 * BK);
   }
   __device__ __forceinline__ v8i b_frag(int bslot, int j) const {
@@ -484,6 +556,7 @@ struct Kernel {
       const v4i x = *(const v4i*)(smem + b_lo + so + j * 16 * G::BKB);
       return (v8i){x.x, x.y, x.z, x.w, 0, 0, 0, 0};
     }
+    if constexpr (BMN) return frag_tr<FBB>(b_lo + so, b_hi + so, j * 2048);
     return frag(b_lo + so, b_hi + so, j * 16 * BK);
   }
   // UE8M0: the packed weight-scale word of the lane's B row in fragment j of B stage bslot
@@ -638,11 +711,11 @@ struct Kernel {
         read_scales(c, as1);
       }
       if constexpr (t == 0) {
-        asrc = src_at<UE, BK>(sb.ac, sb.an, kb + 2, nkb, sstep_a);
+        asrc = src_at<UE>(sb.ac, sb.an, kb + 2, nkb, sstep_a, kstep_a);
         pin_src(asrc);
       }
       if constexpr (t == 1) {
-        bsrc = src_at<SFM == SF_1D1D_UE8M0, G::BKB>(sb.bc, sb.bn, kb + NB, nkb, sstep_b);
+        bsrc = src_at<SFM == SF_1D1D_UE8M0>(sb.bc, sb.bn, kb + NB, nkb, sstep_b, kstep_b);
         pin_src(bsrc);
         if (SFM == SF_1D2D_F32) {
           const bool same = kb + 1 < nkb;
@@ -881,10 +954,10 @@ struct Kernel {
   }
 };
 
-template <int BM, int BN, int WM, int WN, int SFM, int OUT, int GRP, int NB>
+template <int BM, int BN, int WM, int WN, int SFM, int OUT, int GRP, int NB, int LAY = 0>
 __global__ void __launch_bounds__(WM* WN * 64, 1) pipe_kernel(const GemmParams p) {
   using G = Geo<BM, BN, WM, WN, SFM, NB>;
-  using K = Kernel<BM, BN, WM, WN, SFM, OUT, GRP, NB>;
+  using K = Kernel<BM, BN, WM, WN, SFM, OUT, GRP, NB, LAY>;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[G::LDS_BYTES];
   const K k(p, smem);
   int bid = blockIdx.x;
@@ -933,9 +1006,10 @@ __global__ void __launch_bounds__(WM* WN * 64, 1) pipe_kernel(const GemmParams p
   __builtin_amdgcn_s_waitcnt(0 | (7 << 4));
 }
 
-template <int BM, int BN, int WM, int WN, int SFM, int OUT, int GRP, int NB>
+template <int BM, int BN, int WM, int WN, int SFM, int OUT, int GRP, int NB, int LAY = 0>
 static hipError_t launch_one(const GemmParams& p, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((pipe_kernel<BM, BN, WM, WN, SFM, OUT, GRP, NB>), dim3(grid), dim3(WM * WN * 64), 0, stream, p);
+  hipLaunchKernelGGL((pipe_kernel<BM, BN, WM, WN, SFM, OUT, GRP, NB, LAY>), dim3(grid), dim3(WM * WN * 64), 0, stream,
+                     p);
   return hipGetLastError();
 }
 
@@ -968,6 +1042,43 @@ static hipError_t launch_contig(const GemmParams& p, int sfm, int out, int grid,
   return hipErrorInvalidValue;
 }
 
+// Operands stored MN-major: dense problems on the two tiles the planner uses for large and
+// for small FP8 problems, FP4 weights next to an MN-major A (fp8_fp4 tt), and contiguous groups
+// with MN-major weights (m_grouped nn).
+template <int LAY>
+static hipError_t launch_layout(const GemmParams& p, int bm, int bn, int sfm, int grp, int out, int grid,
+                                hipStream_t s) {
+#define DG_CASE(BM_, BN_, WM_, WN_, SF, O, GR)                           \
+  if (bm == BM_ && bn == BN_ && sfm == SF && out == O && grp == GR) \
+    return launch_one<BM_, BN_, WM_, WN_, SF, O, GR, 2, LAY>(p, grid, s);
+  DG_CASE(256, 224, 4, 2, SF_1D2D_F32, OUT_BF16, GRP_DENSE)
+  DG_CASE(256, 224, 4, 2, SF_1D2D_F32, OUT_F32, GRP_DENSE)
+  DG_CASE(256, 224, 4, 2, SF_1D1D_UE8M0, OUT_BF16, GRP_DENSE)
+  DG_CASE(256, 224, 4, 2, SF_1D1D_UE8M0, OUT_F32, GRP_DENSE)
+  DG_CASE(128, 192, 2, 2, SF_1D2D_F32, OUT_BF16, GRP_DENSE)
+  DG_CASE(128, 192, 2, 2, SF_1D2D_F32, OUT_F32, GRP_DENSE)
+  DG_CASE(128, 192, 2, 2, SF_1D2D_F32, OUT_F32_C, GRP_DENSE)
+  DG_CASE(128, 192, 2, 2, SF_1D1D_UE8M0, OUT_BF16, GRP_DENSE)
+  DG_CASE(128, 192, 2, 2, SF_1D1D_UE8M0, OUT_F32, GRP_DENSE)
+  if constexpr (LAY == LAYOUT_A_MN) {
+    DG_CASE(256, 224, 4, 2, SF_FP4_UE8M0, OUT_BF16, GRP_DENSE)
+    DG_CASE(256, 224, 4, 2, SF_FP4_UE8M0, OUT_F32, GRP_DENSE)
+    DG_CASE(128, 192, 2, 2, SF_FP4_UE8M0, OUT_BF16, GRP_DENSE)
+    DG_CASE(128, 192, 2, 2, SF_FP4_UE8M0, OUT_F32, GRP_DENSE)
+    DG_CASE(128, 192, 2, 2, SF_FP4_UE8M0, OUT_F32_C, GRP_DENSE)
+  }
+  if constexpr (LAY == LAYOUT_B_MN) {
+    DG_CASE(128, 224, 2, 2, SF_1D2D_F32, OUT_BF16, GRP_CONTIG)
+    DG_CASE(128, 224, 2, 2, SF_1D2D_F32, OUT_F32, GRP_CONTIG)
+    DG_CASE(128, 224, 2, 2, SF_1D1D_UE8M0, OUT_BF16, GRP_CONTIG)
+    DG_CASE(128, 256, 2, 2, SF_1D2D_F32, OUT_BF16, GRP_CONTIG)
+    DG_CASE(128, 256, 2, 2, SF_1D2D_F32, OUT_F32, GRP_CONTIG)
+    DG_CASE(128, 256, 2, 2, SF_1D1D_UE8M0, OUT_BF16, GRP_CONTIG)
+  }
+#undef DG_CASE
+  return hipErrorInvalidValue;
+}
+
 template <int BM, int BN, int WM, int WN, int NB>
 static hipError_t launch_masked(const GemmParams& p, int sfm, int out, int grid, hipStream_t s) {
 #define DG_CASE(SF, O) \
@@ -980,8 +1091,9 @@ static hipError_t launch_masked(const GemmParams& p, int sfm, int out, int grid,
 
 }  // namespace pipe
 
-// The file is compiled once per part (DG_PIPE_PART: dense, contiguous, masked, FP4 weights) so
-// the instantiations build in parallel, and once without it for the dispatch functions.
+// The file is compiled once per part (DG_PIPE_PART: dense, contiguous, masked, FP4 weights, and
+// the three MN-major layouts) so the instantiations build in parallel, and once without it for
+// the dispatch functions.
 #if defined(DG_PIPE_PART)
 #if DG_PIPE_PART == 0
 hipError_t launch_pipe_dense(const GemmParams& p, int bm, int bn, int sfm, int out, int grid, hipStream_t s) {
@@ -1024,6 +1136,21 @@ hipError_t launch_pipe_fp4(const GemmParams& p, int bm, int bn, int grp, int out
   }
   return hipErrorInvalidValue;
 }
+#elif DG_PIPE_PART == 4
+hipError_t launch_pipe_layout(const GemmParams& p, int bm, int bn, int sfm, int grp, int out, int grid, hipStream_t s) {
+  return p.layout == LAYOUT_A_MN ? pipe::launch_layout<LAYOUT_A_MN>(p, bm, bn, sfm, grp, out, grid, s)
+                                 : hipErrorInvalidValue;
+}
+#elif DG_PIPE_PART == 5
+hipError_t launch_pipe_layout_b(const GemmParams& p, int bm, int bn, int sfm, int grp, int out, int grid,
+                                hipStream_t s) {
+  return pipe::launch_layout<LAYOUT_B_MN>(p, bm, bn, sfm, grp, out, grid, s);
+}
+#elif DG_PIPE_PART == 6
+hipError_t launch_pipe_layout_ab(const GemmParams& p, int bm, int bn, int sfm, int grp, int out, int grid,
+                                 hipStream_t s) {
+  return pipe::launch_layout<LAYOUT_A_MN | LAYOUT_B_MN>(p, bm, bn, sfm, grp, out, grid, s);
+}
 #endif
 #else  // dispatch
 
@@ -1033,7 +1160,19 @@ hipError_t launch_pipe_fp4(const GemmParams& p, int bm, int bn, int grp, int out
 // scales, BF16) on a 128-row tile streaming B through three stages or a 256-row tile with two.
 // FP4 weights: dense on the two UE8M0 tiles (BF16, FP32 or FP32 + C out), contiguous and
 // masked groups on the same tiles as FP8 (BF16 out).
-bool pipe_instantiated(int bm, int bn, int sfm, int grp, int out) {
+bool pipe_instantiated(int bm, int bn, int sfm, int grp, int out, int layout) {
+  if (layout != 0) {
+    // (launch_layout's list)
+    const bool big = bm == 256 && bn == 224, small = bm == 128 && bn == 192;
+    if (grp == GRP_DENSE && (sfm == SF_1D2D_F32 || sfm == SF_1D1D_UE8M0))
+      return (big && (out == OUT_BF16 || out == OUT_F32)) ||
+             (small && (out == OUT_BF16 || out == OUT_F32 || (out == OUT_F32_C && sfm == SF_1D2D_F32)));
+    if (grp == GRP_DENSE && sfm == SF_FP4_UE8M0 && layout == LAYOUT_A_MN)
+      return (big && (out == OUT_BF16 || out == OUT_F32)) || (small && out >= OUT_BF16 && out <= OUT_F32_C);
+    if (grp == GRP_CONTIG && layout == LAYOUT_B_MN && bm == 128 && (bn == 224 || bn == 256))
+      return (sfm == SF_1D2D_F32 && (out == OUT_BF16 || out == OUT_F32)) || (sfm == SF_1D1D_UE8M0 && out == OUT_BF16);
+    return false;
+  }
   if (sfm == SF_FP4_UE8M0) {
     if (grp == GRP_DENSE) return out >= OUT_BF16 && out <= OUT_F32_C && pipe::dense_ue8m0_tile(bm, bn);
     if (grp == GRP_CONTIG) return out == OUT_BF16 && bm == 128 && (bn == 224 || bn == 256);
@@ -1071,7 +1210,10 @@ int pipe_lds_bytes(int bm, int bn, int sfm, int grp) {
 
 hipError_t launch_pipe(const GemmParams& p, int bm, int bn, int sfm, int grp, int out, int grid,
                        hipStream_t stream) {
-  if (!pipe_instantiated(bm, bn, sfm, grp, out)) return hipErrorInvalidValue;
+  if (!pipe_instantiated(bm, bn, sfm, grp, out, p.layout)) return hipErrorInvalidValue;
+  if (p.layout == LAYOUT_A_MN) return launch_pipe_layout(p, bm, bn, sfm, grp, out, grid, stream);
+  if (p.layout == LAYOUT_B_MN) return launch_pipe_layout_b(p, bm, bn, sfm, grp, out, grid, stream);
+  if (p.layout == (LAYOUT_A_MN | LAYOUT_B_MN)) return launch_pipe_layout_ab(p, bm, bn, sfm, grp, out, grid, stream);
   if (sfm == SF_FP4_UE8M0) return launch_pipe_fp4(p, bm, bn, grp, out, grid, stream);
   if (grp == GRP_MASKED) return launch_pipe_masked(p, bm, bn, sfm, out, grid, stream);
   if (grp == GRP_CONTIG) return launch_pipe_contig(p, bm, bn, sfm, out, grid, stream);

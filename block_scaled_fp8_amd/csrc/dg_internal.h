@@ -25,6 +25,11 @@ constexpr int kMaxKGroups = 64;
 
 enum OutMode { OUT_BF16 = 0, OUT_F32 = 1, OUT_F32_C = 2 };
 
+// Operand storage (page "第13章 DeepGEMM" §13.3: the two letters of fp8_gemm_{nt,nn,tn,tt}):
+// LAYOUT_A_MN: A stored [K, M] (element (i, kk) at a[kk*lda + i]); LAYOUT_B_MN: B stored [K, N]
+// (element (j, kk) at b[kk*ldb + j]).  0 is the NT form, both operands K-major.
+enum LayoutBits { LAYOUT_A_MN = 1, LAYOUT_B_MN = 2 };
+
 // Everything a GEMM launch needs.  Sizes in elements; pointers are device memory.
 struct GemmParams {
   const uint8_t* a;
@@ -52,6 +57,7 @@ struct GemmParams {
   int32_t d_vec;                  // 1: D rows allow 4-element vector stores (ldd % 4 == 0, 16-B base)
   int32_t c_vec;                  // 1: C rows allow 4-element vector loads
   int32_t d_vec16;                // 1: D rows and base are 16-byte aligned
+  int32_t layout;                 // LayoutBits (pipelined kernel only)
   // K-grouped: C between groups, and the non-empty groups in order (output index, first
   // 128-long K block, number of K blocks); num_m_tiles * num_n_tiles tiles per group
   int64_t c_gstride;
@@ -77,7 +83,7 @@ int gemm_lds_bytes(int tile);
 
 // Deep-pipelined kernels (dg_gemm_pipe.hip): dense problems, contiguous and masked groups.
 // A tile needs at least pipe_stages_b(bm, bn, group) K blocks.
-bool pipe_instantiated(int bm, int bn, int sf_mode, int group, int out);
+bool pipe_instantiated(int bm, int bn, int sf_mode, int group, int out, int layout = 0);
 int pipe_stages_b(int bm, int bn, int group);
 int pipe_lds_bytes(int bm, int bn, int sf_mode, int group);
 hipError_t launch_pipe(const GemmParams& p, int bm, int bn, int sf_mode, int group, int out, int grid,
@@ -87,6 +93,13 @@ hipError_t launch_pipe_dense(const GemmParams& p, int bm, int bn, int sf_mode, i
 hipError_t launch_pipe_contig(const GemmParams& p, int bm, int bn, int sf_mode, int out, int grid, hipStream_t s);
 hipError_t launch_pipe_masked(const GemmParams& p, int bm, int bn, int sf_mode, int out, int grid, hipStream_t s);
 hipError_t launch_pipe_fp4(const GemmParams& p, int bm, int bn, int group, int out, int grid, hipStream_t s);
+// operands stored MN-major (p.layout != 0): one part per layout (A, B, both)
+hipError_t launch_pipe_layout(const GemmParams& p, int bm, int bn, int sf_mode, int group, int out, int grid,
+                              hipStream_t s);
+hipError_t launch_pipe_layout_b(const GemmParams& p, int bm, int bn, int sf_mode, int group, int out, int grid,
+                                hipStream_t s);
+hipError_t launch_pipe_layout_ab(const GemmParams& p, int bm, int bn, int sf_mode, int group, int out, int grid,
+                                 hipStream_t s);
 
 // Skinny kernel (dg_gemm_skinny.hip): dense problems with 1 <= m <= 64 rows and 1d2d FP32
 // scales, bn (16 or 32) columns per workgroup, the workgroup's waves splitting K.

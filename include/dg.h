@@ -97,6 +97,30 @@ int dg_fp8_gemm_nt(int32_t m, int32_t n, int32_t k,
                    hipStream_t stream);
 
 /*
+ * The other three operand layouts (page "第13章 DeepGEMM" §13.3: D = C + A @ B, the suffix
+ * letters giving the transposition of A and of B; fp8_gemm_nn / tn / tt).  Same arguments and
+ * the same D as dg_fp8_gemm_nt except where A or B sits in memory:
+ *  - "t" on A (dg_fp8_gemm_tn, dg_fp8_gemm_tt): A stored [k, m], element (i, kk) at
+ *    a[kk*lda + i]; m <= lda < 2^23, lda % 16 == 0, k * lda < 2^31, a 16-byte aligned.
+ *  - "n" on B (dg_fp8_gemm_nn, dg_fp8_gemm_tn): B stored [k, n], element (j, kk) at
+ *    b[kk*ldb + j]; n <= ldb < 2^23, ldb % 16 == 0, k * ldb < 2^31, b 16-byte aligned.
+ * Scales keep their meaning and layout: sfa per row i of D and 128-long K block, sfb per
+ * 128x128 block (FP32) or per row j of D (packed UE8M0 only: per-row FP32 weight scales return
+ * DG_ERR_UNSUPPORTED here).  k >= 256 (DG_ERR_UNSUPPORTED below).  The operands stored
+ * [k, x] are staged in LDS as 16-column strips and fed to the matrix unit with the
+ * transposing LDS read, so no transposed copy is made and no workspace is used.
+ */
+int dg_fp8_gemm_nn(int32_t m, int32_t n, int32_t k, const void* a, int64_t lda, const void* sfa, int64_t sfa_stride,
+                   const void* b, int64_t ldb, const void* sfb, int64_t sfb_stride, int32_t sf_format, int32_t gran_n,
+                   const float* c, int64_t ldc, void* d, int64_t ldd, int32_t d_dtype, hipStream_t stream);
+int dg_fp8_gemm_tn(int32_t m, int32_t n, int32_t k, const void* a, int64_t lda, const void* sfa, int64_t sfa_stride,
+                   const void* b, int64_t ldb, const void* sfb, int64_t sfb_stride, int32_t sf_format, int32_t gran_n,
+                   const float* c, int64_t ldc, void* d, int64_t ldd, int32_t d_dtype, hipStream_t stream);
+int dg_fp8_gemm_tt(int32_t m, int32_t n, int32_t k, const void* a, int64_t lda, const void* sfa, int64_t sfa_stride,
+                   const void* b, int64_t ldb, const void* sfb, int64_t sfb_stride, int32_t sf_format, int32_t gran_n,
+                   const float* c, int64_t ldc, void* d, int64_t ldd, int32_t d_dtype, hipStream_t stream);
+
+/*
  * M-grouped contiguous GEMM (page "02 · DeepGEMM 技术解析" §5.1; page "第13章 DeepGEMM"
  * §13.6): the rows of A are the concatenated tokens of num_groups experts; row i uses
  * expert g = grouped_layout[i], i.e. D[i, :] = A[i, :] . B[g]^T with g's scales.  Only M is
@@ -123,6 +147,20 @@ int dg_m_grouped_fp8_gemm_nt_contiguous(int32_t m_total, int32_t n, int32_t k, i
                                         void* d, int64_t ldd, int32_t d_dtype,
                                         const int32_t* grouped_layout,
                                         hipStream_t stream);
+
+/*
+ * M-grouped contiguous GEMM with each group's weights stored [k, n] (page "02 · DeepGEMM
+ * 技术解析" §5.1 names m_grouped_fp8_gemm_{nt, nn}_contiguous): element (j, kk) of group g at
+ * b[g*b_group_stride + kk*ldb + j], n <= ldb < 2^23, ldb % 16 == 0, k * ldb < 2^31,
+ * b_group_stride >= k*ldb.  Everything else as in dg_m_grouped_fp8_gemm_nt_contiguous;
+ * k >= 256, 128x128 FP32 or per-row UE8M0 weight scales.
+ */
+int dg_m_grouped_fp8_gemm_nn_contiguous(int32_t m_total, int32_t n, int32_t k, int32_t num_groups,
+                                        const void* a, int64_t lda, const void* sfa, int64_t sfa_stride,
+                                        const void* b, int64_t ldb, int64_t b_group_stride,
+                                        const void* sfb, int64_t sfb_stride, int64_t sfb_group_stride,
+                                        int32_t sf_format, int32_t gran_n, void* d, int64_t ldd, int32_t d_dtype,
+                                        const int32_t* grouped_layout, hipStream_t stream);
 
 /*
  * M-grouped masked GEMM (page "02 · DeepGEMM 技术解析" §5.2): A is [num_groups, m_max, k]
@@ -181,6 +219,17 @@ int dg_fp8_fp4_gemm_nt(int32_t m, int32_t n, int32_t k,
                        const float* c, int64_t ldc,
                        void* d, int64_t ldd, int32_t d_dtype,
                        hipStream_t stream);
+
+/*
+ * FP8 x FP4 GEMM with the activations stored [k, m] (page "第13章 DeepGEMM" §13.3 and §13.5:
+ * fp8_fp4_gemm_{nt,nn,tn,tt}; the FP4 weights stay [n, k/2], K-packed): element (i, kk) of A
+ * at a[kk*lda + i], m <= lda < 2^23, lda % 16 == 0, k * lda < 2^31.  Everything else as in
+ * dg_fp8_fp4_gemm_nt.  (Weights stored [k, n] would pack two N values per byte; that form is
+ * not provided.)
+ */
+int dg_fp8_fp4_gemm_tt(int32_t m, int32_t n, int32_t k, const void* a, int64_t lda, const void* sfa,
+                       int64_t sfa_stride, const void* b, int64_t ldb, const void* sfb, int64_t sfb_stride,
+                       const float* c, int64_t ldc, void* d, int64_t ldd, int32_t d_dtype, hipStream_t stream);
 
 /*
  * M-grouped contiguous FP8 x FP4 GEMM (page "第13章 DeepGEMM" §13.6, the MoE prefill form with

@@ -1,0 +1,204 @@
+"""GPU parity of the nn / tn / tt operand layouts (page "第13章 DeepGEMM" §13.3: D = C + A @ B with
+the suffix letters giving the transposition of A and B; page "02 · DeepGEMM 技术解析" §5.1: the nn
+form of the M-grouped contiguous GEMM) through the C ABI.
+
+An operand stored [K, M] or [K, N] is staged differently from a [M, K] one but feeds the matrix
+unit the same bytes in the same registers, so each layout must reproduce the NT result on the same
+tile bit for bit; each is also checked against the float64 oracle read through its storage.  The
+stored operands carry padding columns (ld > M or N) filled with E4M3 NaN codes: a kernel that read
+them into a stored output would fail both checks."""
+import numpy as np
+import pytest
+import torch
+
+import block_scaled_fp8_amd as dg
+import oracle
+from tests import gen
+from tests.test_gpu_parity import DEV, assert_full_size, bf16_bits, cuda, force_tile, say
+from tests.tolerance import check_bf16, check_fp32
+
+pytestmark = pytest.mark.gpu
+
+NAN_CODE = 0x7F
+
+
+def stored_t(x, pad=16):
+    """[R, K] logical operand -> [K, R] stored with row stride align16(R) + pad; the padding
+    columns hold NaN codes.  Returns the device view [K, R]."""
+    R, K = x.shape
+    ld = (R + 15) // 16 * 16 + pad
+    buf = np.full((K, ld), NAN_CODE, np.uint8)
+    buf[:, :R] = x.T
+    return cuda(buf)[:, :R]
+
+
+def operands(layout, p, pad=16):
+    a = cuda(p["a"]) if layout[0] == "n" else stored_t(p["a"], pad)
+    b = cuda(p["b"]) if layout[1] == "t" else stored_t(p["b"], pad)
+    return a, b
+
+
+def run(layout, p, out, tile, with_c=False, pack=False, pad=16):
+    a, b = operands(layout, p, pad)
+    d = torch.full((p["M"], p["N"]), float("nan"), dtype=out, device=DEV)
+    c = cuda(p["c"]) if with_c else None
+    with force_tile(tile):
+        getattr(dg, "fp8_gemm_" + layout)((a, cuda(p["sa"])), (b, cuda(p["sb"])), d, c=c, pack_ue8m0=pack)
+    torch.cuda.synchronize()
+    return d
+
+
+def check(p, d, with_c, name=None):
+    o, T = oracle.gemm_nt(p["a"], p["sa"], p["b"], p["sb"], 128, c=p["c"] if with_c else None, want_abs=True)
+    if d.dtype == torch.bfloat16:
+        return check_bf16(bf16_bits(d), o, T, name=name)
+    return check_fp32(d.cpu().numpy(), o, T, name=name)
+
+
+@pytest.mark.parametrize("layout", ["nn", "tn", "tt"])
+@pytest.mark.parametrize("tile", ["256x224", "128x192"])
+@pytest.mark.parametrize("shape", [(200, 300, 384), (257, 513, 256), (33, 129, 640), (64, 32, 1024), (130, 260, 512)])
+def test_layout_equals_nt_bitwise_and_oracle(layout, tile, shape):
+    """Ragged m and n on every tile (including fewer rows or columns than one tile), K from
+    the two-block minimum up, BF16 and FP32 out (and FP32 + C on the tile that has it)."""
+    M, N, K = shape
+    p = gen.dense(M, N, K, seed=M * 7 + N + K, with_c=True)
+    outs = [(torch.bfloat16, False), (torch.float32, False)] + ([(torch.float32, True)] if tile == "128x192" else [])
+    for out, with_c in outs:
+        say("layout", layout, shape, tile, out, "C" if with_c else "")
+        d_nt = run("nt", p, out, tile, with_c)
+        d = run(layout, p, out, tile, with_c)
+        assert torch.equal(d.view(torch.int16) if out == torch.bfloat16 else d.view(torch.int32),
+                           d_nt.view(torch.int16) if out == torch.bfloat16 else d_nt.view(torch.int32)), \
+            (layout, shape, tile, out)
+        ok, st = check(p, d, with_c)
+        say("layout", layout, st)
+        assert ok.all(), st
+
+
+@pytest.mark.parametrize("layout", ["nn", "tn", "tt"])
+@pytest.mark.parametrize("tile", ["256x224", "128x192"])
+def test_layout_ue8m0_scales(layout, tile):
+    """Packed UE8M0 scales (applied by the matrix unit) with operands stored [K, x]."""
+    M, N, K = 300, 450, 768
+    p = gen.pow2_exact(M, N, K, seed=3)
+    p["sb"] = oracle.expand_scales_b(p["sb"], N, 128).astype(np.float32)   # one scale per weight row
+    for out in (torch.bfloat16, torch.float32):
+        say("layout ue8m0", layout, tile, out)
+        a, b = operands(layout, p)
+        d = torch.full((M, N), float("nan"), dtype=out, device=DEV)
+        with force_tile(tile):
+            getattr(dg, "fp8_gemm_" + layout)((a, cuda(p["sa"])), (b, cuda(p["sb"])), d, recipe=(1, 1, 128),
+                                              pack_ue8m0=True)
+        torch.cuda.synchronize()
+        o = oracle.gemm_nt(p["a"], p["sa"], p["b"], p["sb"], 1)
+        if out == torch.float32:
+            assert np.array_equal(d.cpu().numpy().astype(np.float64), o)     # every partial is exact
+        else:
+            assert np.array_equal(bf16_bits(d), oracle.bf16_rne(o))
+
+
+def test_layout_planner_tiles_and_c_aliasing():
+    """The planner's own tile choice (no forced tile) for a small and a large problem, and C
+    accumulated in place in D with A stored [K, M]."""
+    for (M, N, K) in [(16, 48, 256), (1000, 1500, 512)]:
+        p = gen.dense(M, N, K, seed=M + 1, with_c=True)
+        for layout in ("nn", "tn", "tt"):
+            say("layout planner", layout, M, N, K)
+            d = run(layout, p, torch.bfloat16, None)
+            ok, st = check(p, d, False)
+            assert ok.all(), (layout, st)
+    p = gen.dense(192, 320, 512, seed=9, with_c=True)
+    a, b = operands("tt", p)
+    d = cuda(p["c"]).clone()
+    say("layout tt C aliased")
+    dg.fp8_gemm_tt((a, cuda(p["sa"])), (b, cuda(p["sb"])), d, c=d)
+    torch.cuda.synchronize()
+    ok, st = check(p, d, True)
+    assert ok.all(), st
+
+
+def test_layout_tn_full_size_sampled_rows():
+    """tn (both operands stored K-outermost, the weight-gradient storage) at the dense benchmark
+    size, M = 4096, N = 7168, K = 2048, BF16 out, in the planner's launch configuration; rows
+    are independent, so 384 sampled rows (first and last included) are checked."""
+    p = gen.dense(4096, 7168, 2048, seed=0)
+    say("layout tn full size")
+    d = run("tn", p, torch.bfloat16, None, pad=0)
+    rows = np.unique(np.concatenate([[0, 4095], np.random.default_rng(4).choice(4096, 382, replace=False)]))
+    o, T = oracle.gemm_nt(p["a"][rows], p["sa"][rows], p["b"], p["sb"], 128, want_abs=True)
+    ok, st = check_bf16(bf16_bits(d)[rows], o, T, name=f"tn 4096x7168x2048 ({len(rows)} rows) bf16")
+    say("layout tn full size", st)
+    assert ok.all(), st
+    assert_full_size(st, "tn dense")
+
+
+def test_m_grouped_nn_contiguous_ragged():
+    """Contiguous groups with each group's weights stored [K, N]: equal to the NT form bit for
+    bit on the same tile, and to the oracle; padding rows, a skipped block, m_total cut inside
+    the last block, ragged n, NaN sentinels on rows that produce no output."""
+    G, N, K = 4, 300, 512
+    p = gen.grouped_contiguous(G, N, K, seed=31, m_units=(1, 3))
+    starts = np.concatenate([[0], np.cumsum(p["sizes"])])
+    layout = p["layout"].copy()
+    layout[starts[2] - 40:starts[2]] = -1
+    if p["sizes"][2] > 128:
+        layout[starts[2]:starts[2] + 128] = -1
+    M = p["M"] - 30
+    a, sa, layout = p["a"][:M], p["sa"][:M], layout[:M]
+    ld = (N + 15) // 16 * 16 + 16
+    bt = np.full((G, K, ld), NAN_CODE, np.uint8)
+    bt[:, :, :N] = np.swapaxes(p["b"], 1, 2)
+    b_nn = cuda(bt)[:, :, :N]
+    for tile in ("128x256", "128x224"):
+        for out in (torch.bfloat16, torch.float32):
+            say("m-grouped nn", tile, out, p["sizes"].tolist(), M)
+            ds = []
+            for form, b in (("nt", cuda(p["b"])), ("nn", b_nn)):
+                d = torch.full((M, N), float("nan"), dtype=out, device=DEV)
+                with force_tile(tile):
+                    getattr(dg, f"m_grouped_fp8_gemm_{form}_contiguous")((cuda(a), cuda(sa)), (b, cuda(p["sb"])), d,
+                                                                          cuda(layout))
+                torch.cuda.synchronize()
+                ds.append(d)
+            assert torch.equal(ds[0].float().isnan(), ds[1].float().isnan())
+            assert torch.equal(torch.nan_to_num(ds[0].float()), torch.nan_to_num(ds[1].float()))
+            o, T = oracle.grouped_contiguous_nn(a, sa, np.swapaxes(p["b"], 1, 2), p["sb"], layout, want_abs=True)
+            live = ~np.isnan(o)
+            got = ds[1]
+            if out == torch.bfloat16:
+                ok, st = check_bf16(bf16_bits(got)[live], o[live], T[live])
+            else:
+                ok, st = check_fp32(got.cpu().numpy()[live], o[live], T[live])
+            say("m-grouped nn", st)
+            assert ok.all(), st
+            assert np.isnan(got.float().cpu().numpy()[~live]).all()
+
+
+@pytest.mark.parametrize("tile", ["256x224", "128x192"])
+@pytest.mark.parametrize("shape", [(200, 300, 384), (33, 129, 640), (257, 64, 256)])
+def test_fp8_fp4_tt_equals_nt_bitwise_and_oracle(tile, shape):
+    """FP8 x FP4 with the activations stored [K, M] next to K-packed FP4 weights."""
+    M, N, K = shape
+    p = gen.fp8_fp4(M, N, K, seed=M + N, with_c=True)
+    outs = [(torch.bfloat16, False), (torch.float32, False)] + ([(torch.float32, True)] if tile == "128x192" else [])
+    for out, with_c in outs:
+        say("fp8 x fp4 tt", shape, tile, out, with_c)
+        res = []
+        for form, a in (("nt", cuda(p["a"])), ("tt", stored_t(p["a"]))):
+            d = torch.full((M, N), float("nan"), dtype=out, device=DEV)
+            with force_tile(tile):
+                getattr(dg, "fp8_fp4_gemm_" + form)((a, cuda(p["sa"])), (cuda(p["b"]), cuda(p["sb"])), d,
+                                                    c=cuda(p["c"]) if with_c else None)
+            torch.cuda.synchronize()
+            res.append(d)
+        assert torch.equal(res[0].view(torch.int16) if out == torch.bfloat16 else res[0].view(torch.int32),
+                           res[1].view(torch.int16) if out == torch.bfloat16 else res[1].view(torch.int32))
+        o, T = oracle.gemm_fp8_fp4_tt(np.ascontiguousarray(p["a"].T), p["sa"], p["b"], p["sb"],
+                                      c=p["c"] if with_c else None, want_abs=True)
+        if out == torch.bfloat16:
+            ok, st = check_bf16(bf16_bits(res[1]), o, T)
+        else:
+            ok, st = check_fp32(res[1].cpu().numpy(), o, T)
+        say("fp8 x fp4 tt", st)
+        assert ok.all(), st

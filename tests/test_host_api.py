@@ -258,3 +258,62 @@ def test_fp8_fp4_grouped_validation():
     assert lib.dg_m_grouped_fp8_fp4_gemm_nt_masked(*margs) == DG_ERR_LAYOUT
     # empty problems are no-ops
     assert _fp4(m=0, sfa_stride=0) == DG_OK
+
+
+# ---------------------------------------------------------------- operand layouts
+def _layout(name, **kw):
+    # m = 64, n = 128, k = 256; A stored [k, m] for "t", B stored [k, n] for "n"
+    args = dict(m=64, n=128, k=256, a=P, lda=64 if name[0] == "t" else 256, sfa=P, sfa_stride=64, b=P,
+                ldb=128 if name[1] == "n" else 256, sfb=P, sfb_stride=2, sf_format=0, gran_n=128, c=None, ldc=0,
+                d=P, ldd=128, d_dtype=1, stream=None)
+    args.update(kw)
+    return getattr(dg.lib(), "dg_fp8_gemm_" + name)(*args.values())
+
+
+@pytest.mark.parametrize("name,kw,code", [
+    ("tn", dict(lda=48), DG_ERR_LAYOUT),                  # an A stored [k, m] needs lda >= m
+    ("tt", dict(lda=72), DG_ERR_LAYOUT),                  # not a multiple of 16
+    ("nn", dict(ldb=112), DG_ERR_LAYOUT),                 # a B stored [k, n] needs ldb >= n
+    ("tn", dict(k=1 << 16, lda=1 << 15, m=1 << 15, sfa_stride=1 << 15, sfb_stride=512), DG_ERR_LAYOUT),  # k*lda = 2^31
+    ("nn", dict(k=128, sfb_stride=1), DG_ERR_UNSUPPORTED),  # two K blocks at least
+    ("tt", dict(gran_n=1, sfb_stride=128), DG_ERR_UNSUPPORTED),  # per-row FP32 weight scales
+    ("tn", dict(a=P_MIS), DG_ERR_LAYOUT),
+    ("nn", dict(c=P, ldc=128), DG_ERR_UNSUPPORTED),       # C with a BF16 output
+])
+def test_layout_validation(name, kw, code):
+    assert _layout(name, **kw) == code
+    assert dg.lib().dg_get_last_error() != b""
+
+
+def test_layout_stride_rules_follow_the_storage():
+    # lda = 64 is a [k, m] stride for m = 64, not an [m, k] one for k = 256; ldb = 128 likewise
+    # (each call fails validation, so nothing is launched)
+    assert _layout("nt", lda=64) == DG_ERR_LAYOUT
+    assert _layout("nt", ldb=128) == DG_ERR_LAYOUT
+    assert _layout("tt", lda=32) == DG_ERR_LAYOUT
+    assert _layout("tn", ldb=96) == DG_ERR_LAYOUT
+
+
+def test_layout_empty_problems_are_noops():
+    for name in ("nn", "tn", "tt"):
+        assert _layout(name, m=0, sfa_stride=0) == DG_OK
+
+
+def test_grouped_nn_and_fp4_tt_validation():
+    lib = dg.lib()
+    # contiguous nn: B [G, k, n], group stride must cover k*ldb
+    args = [256, 128, 256, 2, P, 256, P, 256, P, 128, 256 * 128, P, 2, 2, 0, 128, P, 128, 1, P, None]
+    bad = list(args)
+    bad[10] = 128 * 128
+    assert lib.dg_m_grouped_fp8_gemm_nn_contiguous(*bad) == DG_ERR_LAYOUT
+    bad = list(args)
+    bad[9] = 100
+    assert lib.dg_m_grouped_fp8_gemm_nn_contiguous(*bad) == DG_ERR_LAYOUT
+    # fp8 x fp4 tt: A stored [k, m]
+    fargs = dict(m=64, n=128, k=256, a=P, lda=48, sfa=P, sfa_stride=64, b=P, ldb=128, sfb=P, sfb_stride=128,
+                 c=None, ldc=0, d=P, ldd=128, d_dtype=1, stream=None)
+    assert lib.dg_fp8_fp4_gemm_tt(*fargs.values()) == DG_ERR_LAYOUT
+    fargs["lda"] = 64
+    fargs["m"] = 0
+    fargs["sfa_stride"] = 0
+    assert lib.dg_fp8_fp4_gemm_tt(*fargs.values()) == DG_OK
