@@ -25,7 +25,7 @@ __all__ = [
     "DGError", "lib", "fp8_gemm_nt", "fp8_gemm_nn", "fp8_gemm_tn", "fp8_gemm_tt", "m_grouped_fp8_gemm_nt_contiguous",
     "m_grouped_fp8_gemm_nn_contiguous", "m_grouped_fp8_gemm_nt_masked", "fp8_fp4_gemm_tt",
     "transform_sf", "get_mn_major_tma_aligned_tensor", "get_mn_major_tma_aligned_packed_ue8m0_tensor",
-    "per_token_group_cast_fp8", "k_grouped_fp8_gemm_nt_contiguous", "transform_sf_into_required_layout",
+    "per_token_group_cast_fp8", "k_grouped_fp8_gemm_nt_contiguous", "k_grouped_fp8_gemm_tn_contiguous", "transform_sf_into_required_layout",
     "fp8_fp4_gemm_nt", "m_grouped_fp8_fp4_gemm_nt_contiguous", "m_grouped_fp8_fp4_gemm_nt_masked", "get_tma_aligned_size", "get_mk_alignment_for_contiguous_layout", "set_num_sms", "get_num_sms",
     "get_gemm_config", "LIB_PATH",
 ]
@@ -56,6 +56,7 @@ _SIGS = {
                                                    _i64, _p, _i64, _i64, _p, _i64, _i64, _i32, _p, _i32, _p]),
     "dg_transform_sf": (_i32, [_p, _i32, _i32, _i32, _i32, _i32, _p, _p, _p]),
     "dg_k_grouped_fp8_gemm_nt_contiguous": (_i32, [_i32, _i32, _i32, _p, _p, _i64, _p, _p, _i64, _p, _p, _p, _p]),
+    "dg_k_grouped_fp8_gemm_tn_contiguous": (_i32, [_i32, _i32, _i32, _p, _p, _i64, _p, _p, _i64, _p, _p, _p, _p]),
     "dg_per_token_group_cast_fp8": (_i32, [_i32, _i32, _p, _i64, _i32, _p, _i64, _p, _i64, _i32, _p]),
     "dg_get_tma_aligned_size": (_i64, [_i64, _i32]),
     "dg_get_mk_alignment_for_contiguous_layout": (_i32, []),
@@ -357,13 +358,24 @@ def k_grouped_fp8_gemm_nt_contiguous(a, b, d, ks, c):
     ``b = (B [n, sum ks], sfb [sum ks // 128, n])`` with FP32 per-row scales, ``ks`` the K of
     each group (multiples of 128), ``d`` and ``c`` FP32 [G, m, n]; ``c`` is required and may be
     ``d`` itself.  D[g] = C[g] + A[:, group g] @ B[:, group g].T (scaled per 128-long block)."""
+    return _k_grouped("nt", a, b, d, ks, c)
+
+
+def k_grouped_fp8_gemm_tn_contiguous(a, b, d, ks, c):
+    """As ``k_grouped_fp8_gemm_nt_contiguous`` with both operands stored K-outermost:
+    ``a = (A [sum ks, m], sfa)``, ``b = (B [sum ks, n], sfb)`` (the token-major activations and
+    gradients of the forward pass); D[g] = C[g] + A[group g].T @ B[group g]."""
+    return _k_grouped("tn", a, b, d, ks, c)
+
+
+def _k_grouped(layout, a, b, d, ks, c):
     A, sfa = a
     B, sfb = b
-    _codes(A)
-    _codes(B)
+    _codes(A, "K" if layout == "nt" else "M")
+    _codes(B, "K" if layout == "nt" else "N")
     ks = [int(k) for k in ks]
     G = len(ks)
-    m, n = A.shape[0], B.shape[0]
+    m, n = (A.shape[0], B.shape[0]) if layout == "nt" else (A.shape[1], B.shape[1])
     if c is None:
         raise ValueError("the K-grouped GEMM requires c (pass d itself to accumulate in place)")
     for t, name in ((sfa, "sfa"), (sfb, "sfb"), (c, "c"), (d, "d")):
@@ -374,9 +386,9 @@ def k_grouped_fp8_gemm_nt_contiguous(a, b, d, ks, c):
     if tuple(sfa.shape) != (sum(ks) // 128, m) or tuple(sfb.shape) != (sum(ks) // 128, n):
         raise ValueError("sfa and sfb must be [sum(ks) // 128, m] and [sum(ks) // 128, n]")
     ks_host = (ctypes.c_int32 * G)(*ks)
-    _check(lib().dg_k_grouped_fp8_gemm_nt_contiguous(G, m, n, ks_host, _ptr(A), A.stride(0), _ptr(sfa),
-                                                     _ptr(B), B.stride(0), _ptr(sfb), _ptr(c), _ptr(d),
-                                                     _stream(d)))
+    fn = getattr(lib(), f"dg_k_grouped_fp8_gemm_{layout}_contiguous")
+    _check(fn(G, m, n, ks_host, _ptr(A), A.stride(0), _ptr(sfa), _ptr(B), B.stride(0), _ptr(sfb), _ptr(c), _ptr(d),
+              _stream(d)))
     return d
 
 

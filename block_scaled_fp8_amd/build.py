@@ -68,13 +68,13 @@ def _check_scratch(reports):
 
 def build(verbose=False, jobs=None):
     """Compile every HIP source for gfx950 and link libdg.so.  Always rebuilds.  Fails if a
-    pipelined kernel the planner can pick spills registers to scratch."""
+    GEMM kernel the planner can pick spills registers to scratch."""
     bdir = os.path.join(HERE, "_build")
     os.makedirs(bdir, exist_ok=True)
     steps = []
     for t in range(NUM_TILES):
-        steps.append([HIPCC, *FLAGS, f"-DDG_TILE_ID={t}", "-c", os.path.join(CSRC, "dg_gemm.hip"),
-                      "-o", os.path.join(bdir, f"dg_gemm_t{t}.o")])
+        steps.append([HIPCC, *FLAGS, f"-DDG_TILE_ID={t}", "-Rpass-analysis=kernel-resource-usage", "-c",
+                      os.path.join(CSRC, "dg_gemm.hip"), "-o", os.path.join(bdir, f"dg_gemm_t{t}.o")])
     steps.append([HIPCC, *FLAGS, "-c", os.path.join(CSRC, "dg_gemm.hip"),
                   "-o", os.path.join(bdir, "dg_gemm_dispatch.o")])
     # MFMA results in VGPRs: the block partials feed VALU promotion FMAs directly instead of

@@ -80,18 +80,24 @@ Plan plan_gemm(int kind, int m, int n, int k, int groups, int m_max, int sfm, in
   if (force && sscanf(force, "%dx%d", &fbm, &fbn) != 2) fbm = fbn = 0;
   for (int t = 0; t < dg::kNumTiles; ++t) {
     const dg::TileCfg& c = dg::kTiles[t];
-    if (!layout && !dg::gemm_instantiated(t, sfm, kind, out)) continue;
+    // (operands stored MN-major: the pipelined kernel, except for the K-grouped form)
+    if (layout && kind == dg::GRP_KGROUP) {
+      if (!dg::gemm_instantiated(t, sfm, kind, out, layout)) continue;
+    } else if (!layout && !dg::gemm_instantiated(t, sfm, kind, out)) {
+      continue;
+    }
     if (fbm && (c.bm != fbm || c.bn != fbn)) continue;
     // operands stored MN-major run on the pipelined kernel only
-    if (layout && (!dg::pipe_instantiated(c.bm, c.bn, sfm, kind, out, layout) ||
-                   k / 128 < dg::pipe_stages_b(c.bm, c.bn, kind)))
+    if (layout && kind != dg::GRP_KGROUP &&
+        (!dg::pipe_instantiated(c.bm, c.bn, sfm, kind, out, layout) || k / 128 < dg::pipe_stages_b(c.bm, c.bn, kind)))
       continue;
     // the 256-row pipelined tiles (1d2d scales) run out of registers with FP32 + C output
     // (the compiler spills them to scratch); they stay reachable only when forced
     if (!fbm && kind == 0 && out == dg::OUT_F32_C && sfm == dg::SF_1D2D_F32 && c.bm > 128) continue;
     const int64_t mt = (kind == 2) ? (m + c.bm - 1) / c.bm : (m + c.bm - 1) / c.bm;
     const int64_t nt = (n + c.bn - 1) / c.bn;
-    const int64_t tiles = (kind == 2) ? int64_t(groups) * mt * nt : mt * nt;
+    // (masked and K-grouped: every group has its own mt x nt tiles)
+    const int64_t tiles = (kind == 2 || kind == dg::GRP_KGROUP) ? int64_t(groups) * mt * nt : mt * nt;
     const int occ = tile_occupancy(c);
     const int64_t slots = int64_t(num_sms) * occ;
     const int64_t waves = (tiles + slots - 1) / slots;
@@ -423,6 +429,108 @@ static int fp8_fp4_gemm(int layout, int32_t m, int32_t n, int32_t k, const void*
   return launch_fp8_fp4(p, dg::GRP_DENSE, m, 0, out, stream);
 }
 
+// K-grouped contiguous GEMM: operands K-major (layout 0, A [m, sum K], B [n, sum K]) or both
+// stored K-outermost (dg::LAYOUT_A_MN | dg::LAYOUT_B_MN: A [sum K, m], B [sum K, n]).
+static int k_grouped(int layout, int32_t num_groups, int32_t m, int32_t n, const int32_t* ks, const void* a,
+                     int64_t lda, const float* sfa, const void* b, int64_t ldb, const float* sfb, const float* c,
+                     float* d, hipStream_t stream) {
+  if (num_groups <= 0) return fail(DG_ERR_SHAPE, "num_groups = %d must be positive", num_groups);
+  if (m < 0 || n < 0) return fail(DG_ERR_SHAPE, "m = %d and n = %d must not be negative", m, n);
+  if (!ks) return fail(DG_ERR_NULL, "ks (host array of num_groups K sizes) must not be NULL");
+  int64_t sum_k = 0;
+  for (int g = 0; g < num_groups; ++g) {
+    if (ks[g] < 0 || ks[g] % 128 != 0) return fail(DG_ERR_SHAPE, "ks[%d] = %d must be a non-negative multiple of 128", g, ks[g]);
+    sum_k += ks[g];
+  }
+  if (m % 4 != 0 || n % 4 != 0) return fail(DG_ERR_SHAPE, "m = %d and n = %d must be multiples of 4", m, n);
+  if (m == 0 || n == 0) return ok();
+  if (!c || !d) return fail(DG_ERR_NULL, "c and d must not be NULL (c may equal d)");
+  if ((reinterpret_cast<uintptr_t>(c) & 3u) != 0 || (reinterpret_cast<uintptr_t>(d) & 3u) != 0)
+    return fail(DG_ERR_LAYOUT, "c and d must be 4-byte aligned");
+  const int64_t mn = (int64_t)m * n;
+  if (sum_k > 0) {
+    if (!a || !b || !sfa || !sfb) return fail(DG_ERR_NULL, "a, sfa, b and sfb must not be NULL");
+    if (sum_k >= (int64_t(1) << 31)) return fail(DG_ERR_SHAPE, "sum(ks) must be < 2^31");
+    if (layout) {
+      if (lda < m || ldb < n) return fail(DG_ERR_LAYOUT, "A stored [sum(ks), m] and B stored [sum(ks), n] need lda >= m and ldb >= n");
+      if (sum_k * lda >= (int64_t(1) << 31) || sum_k * ldb >= (int64_t(1) << 31))
+        return fail(DG_ERR_LAYOUT, "operands stored [sum(ks), x] must span less than 2^31 bytes (sum(ks) * ld)");
+    } else if (lda < sum_k || ldb < sum_k) {
+      return fail(DG_ERR_LAYOUT, "lda and ldb must be >= sum(ks) = %lld", (long long)sum_k);
+    }
+    if (lda % 16 != 0 || ldb % 16 != 0) return fail(DG_ERR_LAYOUT, "lda and ldb must be multiples of 16");
+    if (lda >= (int64_t(1) << 23) || ldb >= (int64_t(1) << 23)) return fail(DG_ERR_LAYOUT, "lda and ldb must be < 2^23 (tile byte ranges are 32-bit)");
+    if (!aligned16(a) || !aligned16(b) || !aligned16(sfa) || !aligned16(sfb))
+      return fail(DG_ERR_LAYOUT, "a, b, sfa and sfb must be 16-byte aligned");
+  }
+  // everything is validated above, so an error below is a launch failure only
+  for (int g = 0; g < num_groups; ++g) {
+    if (ks[g] == 0 && c != d) {   // an empty group is D = C
+      const hipError_t e = hipMemcpyAsync(d + g * mn, c + g * mn, mn * sizeof(float), hipMemcpyDeviceToDevice, stream);
+      if (e != hipSuccess) return fail(DG_ERR_HIP, "copy of C into D failed: %s", hipGetErrorString(e));
+    }
+  }
+  if (sum_k == 0) return ok();
+  int num_sms = g_num_sms_override.load();
+  if (num_sms <= 0) num_sms = device_cu_count();
+  if (num_sms <= 0) return fail(DG_ERR_HIP, "could not query the device's compute-unit count");
+  int nonempty = 0;
+  for (int g = 0; g < num_groups; ++g) nonempty += ks[g] > 0;
+  // tile choice: the area model over the tiles of one launch (up to kMaxKGroups groups)
+  const int plan_groups = nonempty < dg::kMaxKGroups ? nonempty : dg::kMaxKGroups;
+  Plan pl = plan_gemm(dg::GRP_KGROUP, m, n, (int)(sum_k / nonempty), plan_groups, 0, dg::SF_1D1D_F32, dg::OUT_F32_C,
+                      num_sms, layout);
+  if (pl.tile < 0) return fail(DG_ERR_UNSUPPORTED, "no tile configuration for the K-grouped GEMM");
+  const dg::TileCfg& tc = dg::kTiles[pl.tile];
+  // One launch over the tiles of up to kMaxKGroups non-empty groups (the groups share the
+  // scheduler, page "02 · DeepGEMM 技术解析" §5.2); more groups take more launches.
+  const int per_launch = env_int("DG_KGROUP_LOOP", 0) ? 1 : dg::kMaxKGroups;
+  int g = 0, kb = 0;
+  while (g < num_groups) {
+    dg::GemmParams p{};
+    p.a = (const uint8_t*)a; p.lda = lda;
+    p.sfa = sfa; p.sfa_stride = m;
+    p.b = (const uint8_t*)b; p.ldb = ldb;
+    p.sfb = sfb; p.sfb_stride = n;
+    p.c = c; p.ldc = n; p.c_gstride = mn;
+    p.d = d; p.ldd = n; p.d_gstride = mn;
+    p.m = m; p.n = n; p.k = (int32_t)sum_k; p.num_groups = num_groups;
+    p.layout = layout;
+    int max_nkb = 0;
+    for (; g < num_groups && p.kg_count < per_launch; ++g) {
+      const int nkb = ks[g] / 128;
+      if (nkb > 0) {
+        p.kg_group[p.kg_count] = g;
+        p.kg_kb0[p.kg_count] = kb;
+        p.kg_nkb[p.kg_count] = nkb;
+        ++p.kg_count;
+      }
+      kb += nkb;
+      max_nkb = nkb > max_nkb ? nkb : max_nkb;
+    }
+    if (p.kg_count == 0) break;
+    p.sf_k = max_nkb;
+    p.num_m_tiles = (m + tc.bm - 1) / tc.bm;
+    p.num_n_tiles = (n + tc.bn - 1) / tc.bn;
+    const int64_t tiles = int64_t(p.kg_count) * p.num_m_tiles * p.num_n_tiles;
+    p.total_tiles = int(tiles);
+    const int sw = env_int("DG_SWIZZLE_M", 8);
+    p.swizzle_m = sw < 1 ? 1 : (sw < p.num_m_tiles ? sw : p.num_m_tiles);
+    const int64_t slots = int64_t(num_sms) * tile_occupancy(tc);
+    const int grid = int(tiles < slots ? tiles : slots);
+    p.xcd_remap = (grid % 8 == 0) ? 1 : 0;
+    p.d_vec = (n % 4 == 0 && aligned16(d)) ? 1 : 0;
+    p.c_vec = (n % 4 == 0 && aligned16(c)) ? 1 : 0;
+    p.d_vec16 = p.d_vec;
+    if (env_int("DG_PRINT_CONFIGS", 0))
+      fprintf(stderr, "[dg] k-grouped (layout %d): %d non-empty groups, tile %dx%d, %lld tiles, grid %d\n", layout,
+              p.kg_count, tc.bm, tc.bn, (long long)tiles, grid);
+    const hipError_t e = dg::launch_gemm(p, pl.tile, dg::SF_1D1D_F32, dg::GRP_KGROUP, dg::OUT_F32_C, grid, stream);
+    if (e != hipSuccess) return fail(DG_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  }
+  return ok();
+}
+
 extern "C" {
 
 int dg_fp8_gemm_nt(int32_t m, int32_t n, int32_t k, const void* a, int64_t lda, const void* sfa,
@@ -515,106 +623,13 @@ int dg_m_grouped_fp8_gemm_nt_masked(int32_t num_groups, int32_t m_max, int32_t n
 int dg_k_grouped_fp8_gemm_nt_contiguous(int32_t num_groups, int32_t m, int32_t n, const int32_t* ks,
                                         const void* a, int64_t lda, const float* sfa, const void* b, int64_t ldb,
                                         const float* sfb, const float* c, float* d, hipStream_t stream) {
-  if (num_groups <= 0) return fail(DG_ERR_SHAPE, "num_groups = %d must be positive", num_groups);
-  if (m < 0 || n < 0) return fail(DG_ERR_SHAPE, "m = %d and n = %d must not be negative", m, n);
-  if (!ks) return fail(DG_ERR_NULL, "ks (host array of num_groups K sizes) must not be NULL");
-  int64_t sum_k = 0;
-  for (int g = 0; g < num_groups; ++g) {
-    if (ks[g] < 0 || ks[g] % 128 != 0) return fail(DG_ERR_SHAPE, "ks[%d] = %d must be a non-negative multiple of 128", g, ks[g]);
-    sum_k += ks[g];
-  }
-  if (m % 4 != 0 || n % 4 != 0) return fail(DG_ERR_SHAPE, "m = %d and n = %d must be multiples of 4", m, n);
-  if (m == 0 || n == 0) return ok();
-  if (!c || !d) return fail(DG_ERR_NULL, "c and d must not be NULL (c may equal d)");
-  if (sum_k > 0 && (!a || !b || !sfa || !sfb)) return fail(DG_ERR_NULL, "a, sfa, b and sfb must not be NULL");
-  if (lda < sum_k || ldb < sum_k) return fail(DG_ERR_LAYOUT, "lda and ldb must be >= sum(ks) = %lld", (long long)sum_k);
-  // every group is checked before any is launched, so an error writes nothing
-  const int64_t mn = (int64_t)m * n;
-  int64_t k0 = 0;
-  int nonempty = 0;
-  for (int g = 0; g < num_groups; ++g) nonempty += ks[g] > 0;
-  // One launch over every non-empty group's tiles (the groups share the scheduler, page
-  // "02 · DeepGEMM 技术解析" §5.2); empty groups are D = C copies.  Beyond kMaxKGroups
-  // non-empty groups the groups run as one dense launch each.
-  const bool single = nonempty > 0 && nonempty <= dg::kMaxKGroups && !env_int("DG_KGROUP_LOOP", 0);
-  for (int pass = 0; pass < (single ? 1 : 2); ++pass) {
-    k0 = 0;
-    for (int g = 0; g < num_groups; ++g) {
-      const float* cg = c + g * mn;
-      float* dg = d + g * mn;
-      if (ks[g] == 0) {
-        if (pass == 1 && cg != dg) {
-          const hipError_t e = hipMemcpyAsync(dg, cg, mn * sizeof(float), hipMemcpyDeviceToDevice, stream);
-          if (e != hipSuccess) return fail(DG_ERR_HIP, "copy of C into D failed: %s", hipGetErrorString(e));
-        }
-        continue;
-      }
-      const uint8_t* ag = (const uint8_t*)a + k0;
-      const uint8_t* bg = (const uint8_t*)b + k0;
-      const float* sag = sfa + (k0 / 128) * m;
-      const float* sbg = sfb + (k0 / 128) * n;
-      if (pass == 0) {
-        const int st = check_common(n, ks[g], ag, lda, sag, bg, ldb, sbg, n, DG_SF_F32, 1, dg, n, DG_OUT_F32, false);
-        if (st != DG_OK) return st;
-        if ((reinterpret_cast<uintptr_t>(cg) & 3u) != 0) return fail(DG_ERR_LAYOUT, "c must be 4-byte aligned");
-      } else {
-        const int st = dg_fp8_gemm_nt(m, n, ks[g], ag, lda, sag, m, bg, ldb, sbg, n, DG_SF_F32, 1, cg, n, dg, n,
-                                      DG_OUT_F32, stream);
-        if (st != DG_OK) return st;
-      }
-      k0 += ks[g];
-    }
-  }
-  if (!single) return ok();
-  dg::GemmParams p{};
-  p.a = (const uint8_t*)a; p.lda = lda;
-  p.sfa = sfa; p.sfa_stride = m;
-  p.b = (const uint8_t*)b; p.ldb = ldb;
-  p.sfb = sfb; p.sfb_stride = n;
-  p.c = c; p.ldc = n; p.c_gstride = mn;
-  p.d = d; p.ldd = n; p.d_gstride = mn;
-  p.m = m; p.n = n; p.k = (int32_t)sum_k; p.num_groups = num_groups;
-  int kb = 0, max_nkb = 0;
-  for (int g = 0; g < num_groups; ++g) {
-    const int nkb = ks[g] / 128;
-    if (nkb > 0) {
-      p.kg_group[p.kg_count] = g;
-      p.kg_kb0[p.kg_count] = kb;
-      p.kg_nkb[p.kg_count] = nkb;
-      ++p.kg_count;
-    } else if (c != d) {
-      const hipError_t e = hipMemcpyAsync(d + g * mn, c + g * mn, mn * sizeof(float), hipMemcpyDeviceToDevice, stream);
-      if (e != hipSuccess) return fail(DG_ERR_HIP, "copy of C into D failed: %s", hipGetErrorString(e));
-    }
-    kb += nkb;
-    max_nkb = nkb > max_nkb ? nkb : max_nkb;
-  }
-  p.sf_k = max_nkb;
-  int num_sms = g_num_sms_override.load();
-  if (num_sms <= 0) num_sms = device_cu_count();
-  if (num_sms <= 0) return fail(DG_ERR_HIP, "could not query the device's compute-unit count");
-  // tile choice: the dense heuristic for one group's m x n output
-  Plan pl = plan_gemm(dg::GRP_KGROUP, m, n, (int)(sum_k / nonempty), 1, 0, dg::SF_1D1D_F32, dg::OUT_F32_C, num_sms);
-  if (pl.tile < 0) return fail(DG_ERR_UNSUPPORTED, "no tile configuration for the K-grouped GEMM");
-  const dg::TileCfg& tc = dg::kTiles[pl.tile];
-  p.num_m_tiles = (m + tc.bm - 1) / tc.bm;
-  p.num_n_tiles = (n + tc.bn - 1) / tc.bn;
-  const int64_t tiles = int64_t(p.kg_count) * p.num_m_tiles * p.num_n_tiles;
-  p.total_tiles = int(tiles);
-  const int sw = env_int("DG_SWIZZLE_M", 8);
-  p.swizzle_m = sw < 1 ? 1 : (sw < p.num_m_tiles ? sw : p.num_m_tiles);
-  const int64_t slots = int64_t(num_sms) * tile_occupancy(tc);
-  const int grid = int(tiles < slots ? tiles : slots);
-  p.xcd_remap = (grid % 8 == 0) ? 1 : 0;
-  p.d_vec = (n % 4 == 0 && aligned16(d)) ? 1 : 0;
-  p.c_vec = (n % 4 == 0 && aligned16(c)) ? 1 : 0;
-  p.d_vec16 = p.d_vec;
-  if (env_int("DG_PRINT_CONFIGS", 0))
-    fprintf(stderr, "[dg] k-grouped: %d non-empty groups, tile %dx%d, %lld tiles, grid %d\n", p.kg_count, tc.bm, tc.bn,
-            (long long)tiles, grid);
-  const hipError_t e = dg::launch_gemm(p, pl.tile, dg::SF_1D1D_F32, dg::GRP_KGROUP, dg::OUT_F32_C, grid, stream);
-  if (e != hipSuccess) return fail(DG_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
-  return ok();
+  return k_grouped(0, num_groups, m, n, ks, a, lda, sfa, b, ldb, sfb, c, d, stream);
+}
+
+int dg_k_grouped_fp8_gemm_tn_contiguous(int32_t num_groups, int32_t m, int32_t n, const int32_t* ks,
+                                        const void* a, int64_t lda, const float* sfa, const void* b, int64_t ldb,
+                                        const float* sfb, const float* c, float* d, hipStream_t stream) {
+  return k_grouped(dg::LAYOUT_A_MN | dg::LAYOUT_B_MN, num_groups, m, n, ks, a, lda, sfa, b, ldb, sfb, c, d, stream);
 }
 
 int dg_fp8_fp4_gemm_nt(int32_t m, int32_t n, int32_t k, const void* a, int64_t lda, const void* sfa,

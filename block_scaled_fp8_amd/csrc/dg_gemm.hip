@@ -40,6 +40,7 @@ namespace dg {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v2i __attribute__((ext_vector_type(2)));
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 typedef unsigned int v2u __attribute__((ext_vector_type(2)));
 typedef float v4f __attribute__((ext_vector_type(4)));
@@ -82,6 +83,13 @@ struct Tile {
   int nkb;      // K blocks of this tile
   bool skip;
 };
+
+// gfx950's transposing LDS read: in each group of 16 lanes, lane 2r + h names an 8-byte row and
+// lane 8h + c receives byte c of rows 0..7 of its half h (measured lane layout of
+// ds_read_b64_tr_b8): 8 K values of one M (or N) column of an MN-major tile in one lane.
+__device__ __forceinline__ v2i read_tr8(const uint8_t* smem, uint32_t addr) {
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((DG_LDS v2i*)(smem + addr));
+}
 
 // LDS slot of 16-byte chunk c of stage row r is c ^ swz(r).
 __device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
@@ -181,12 +189,13 @@ struct Loader {
   const uint8_t* b_tile;  // row tile.n0 of B
   const uint8_t* sa;      // activation scale of row tile.m0, K block 0
   const uint8_t* sb;      // per-row: weight scale of row tile.n0, K block 0; 1d2d: block scale (n0/128, 0)
-  int a_rows, b_rows;     // rows of A / B that exist from the tile start
+  int a_rows, b_rows;     // rows of A / B that exist from the tile start (MN-major: columns)
+  int a_krows, b_krows;   // MN-major operands: K rows from the tile's first K row to the operand's end
   int sa_rows, sb_rows;   // scale entries that exist from the tile start (align4 padded)
   int sb_blocks;          // 1d2d: weight-scale blocks that exist from n0/128
 };
 
-template <int BM, int BN, int WM, int WN, int SFM, int GRP>
+template <int BM, int BN, int WM, int WN, int SFM, int GRP, int LAY = 0>
 __device__ __forceinline__ void make_loader(const GemmParams& p, const Tile& tl, Loader<BM, BN, WM, WN>& ld) {
   const uint8_t* A = p.a + (GRP == GRP_MASKED ? (int64_t)tl.g * p.a_gstride : 0);
   const uint8_t* B = p.b + (GRP == GRP_CONTIG || GRP == GRP_MASKED ? (int64_t)tl.g * p.b_gstride : 0);
@@ -195,6 +204,11 @@ __device__ __forceinline__ void make_loader(const GemmParams& p, const Tile& tl,
   const int64_t kofs = (GRP == GRP_KGROUP) ? (int64_t)tl.kb0 * BK : 0;
   ld.a_tile = A + (int64_t)tl.m0 * p.lda + kofs;
   ld.b_tile = B + (int64_t)tl.n0 * p.ldb + kofs;
+  // MN-major operands (K rows of M or N bytes): the tile starts at K row kofs, column m0 / n0
+  if (LAY & LAYOUT_A_MN) ld.a_tile = A + kofs * p.lda + tl.m0;
+  if (LAY & LAYOUT_B_MN) ld.b_tile = B + kofs * p.ldb + tl.n0;
+  ld.a_krows = p.k - (int)kofs;
+  ld.b_krows = p.k - (int)kofs;
   ld.a_rows = p.m - tl.m0;  // m_max rows when masked
   ld.b_rows = p.n - tl.n0;
   const int64_t sfa_goff = (GRP == GRP_MASKED) ? (int64_t)tl.g * p.sfa_gstride
@@ -228,6 +242,16 @@ struct LaneOffsets {
   uint32_t s;  // scale wave-loads: lane L copies 4-byte entries 4L..4L+3
 };
 
+// An operand stored MN-major (K rows of M or N bytes) sits in its stage region as 16-column
+// strips of 128 rows x 16 bytes; K row k is stored at row position k ^ 8 * (bit 5 of k), which
+// spreads the transposing fragment reads of the two lane groups served together over all banks.
+// Wave-load q fills strip q/2, row positions 64 (q % 2) + [0, 64): lane L copies 16 bytes of K
+// row 64 (q % 2) + (L ^ 8 * (bit 5 of L)), so the lane offset depends on the parity of q only.
+__device__ __forceinline__ uint32_t mn_lane_row(int lane, uint32_t parity) {
+  return 64u * parity + ((uint32_t)lane ^ ((((uint32_t)lane >> 5) & 1u) << 3));
+}
+
+template <int LAY = 0>
 __device__ __forceinline__ LaneOffsets make_lane_offsets(const GemmParams& p, int wave, int lane) {
   LaneOffsets o;
   const uint32_t r = (uint32_t)lane >> 3, c = (uint32_t)lane & 7, w = (uint32_t)wave & 1;
@@ -235,6 +259,14 @@ __device__ __forceinline__ LaneOffsets make_lane_offsets(const GemmParams& p, in
   o.a_flip = r * (uint32_t)p.lda + ((c ^ r ^ w ^ 1u) << 4);
   o.b_same = r * (uint32_t)p.ldb + ((c ^ r ^ w) << 4);
   o.b_flip = r * (uint32_t)p.ldb + ((c ^ r ^ w ^ 1u) << 4);
+  if (LAY & LAYOUT_A_MN) {
+    o.a_same = mn_lane_row(lane, w) * (uint32_t)p.lda;
+    o.a_flip = mn_lane_row(lane, w ^ 1u) * (uint32_t)p.lda;
+  }
+  if (LAY & LAYOUT_B_MN) {
+    o.b_same = mn_lane_row(lane, w) * (uint32_t)p.ldb;
+    o.b_flip = mn_lane_row(lane, w ^ 1u) * (uint32_t)p.ldb;
+  }
   o.s = (uint32_t)lane << 4;
   return o;
 }
@@ -257,7 +289,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
 // branch-free instruction stream.  Which kind a slot is depends on the wave only in the
 // last slot; all address arithmetic is on wave-uniform values and the only per-lane term
 // is the fixed lane offset.
-template <int U, int BM, int BN, int WM, int WN, int SFM>
+template <int U, int BM, int BN, int WM, int WN, int SFM, int LAY = 0>
 __device__ __forceinline__ void issue_part(const GemmParams& p, const Loader<BM, BN, WM, WN>& ld, uint8_t* smem,
                                            int kb, int s, const int wave, const LaneOffsets lo) {
   using S = Shape<BM, BN, WM, WN>;
@@ -274,6 +306,13 @@ __device__ __forceinline__ void issue_part(const GemmParams& p, const Loader<BM,
     const int rem = ld.a_rows - 8 * q;
     base = ld.a_tile + (int64_t)(8 * q) * p.lda + kb * BK;
     bytes = rem > 0 ? min(rem, 8) * (int)p.lda - kb * BK : 0;
+    if constexpr ((LAY & LAYOUT_A_MN) != 0) {
+      // strip q/2: K rows kb*128.. of columns 16 (q/2).. ; the range ends with the 16-byte
+      // granule holding the operand's last byte (columns past the end only feed outputs that
+      // are never stored; a range ending inside a copy would drop its valid dwords)
+      base = ld.a_tile + (int64_t)kb * BK * p.lda + 16 * (q >> 1);
+      bytes = (int)((((int64_t)(ld.a_krows - kb * BK - 1)) * p.lda + ld.a_rows - 16 * (q >> 1) + 15) & ~(int64_t)15);
+    }
     voff = FLIP ? lo.a_flip : lo.a_same;
     dst = s * S::STAGE_BYTES + q * 1024;
   } else {
@@ -281,7 +320,12 @@ __device__ __forceinline__ void issue_part(const GemmParams& p, const Loader<BM,
     const int r0 = 8 * q - BM;
     const int rem = ld.b_rows - r0;
     const uint8_t* b_base = ld.b_tile + (int64_t)r0 * p.ldb + kb * BK;
-    const int b_bytes = rem > 0 ? min(rem, 8) * (int)p.ldb - kb * BK : 0;
+    int b_bytes = rem > 0 ? min(rem, 8) * (int)p.ldb - kb * BK : 0;
+    if constexpr ((LAY & LAYOUT_B_MN) != 0) {
+      const int st = (q - BM / 8) >> 1;  // (BM / 8 is even: the parity of q is the strip half)
+      b_base = ld.b_tile + (int64_t)kb * BK * p.ldb + 16 * st;
+      b_bytes = (int)((((int64_t)(ld.b_krows - kb * BK - 1)) * p.ldb + ld.b_rows - 16 * st + 15) & ~(int64_t)15);
+    }
     const uint32_t b_voff = FLIP ? lo.b_flip : lo.b_same;
     if constexpr (ALL_B) {
       base = b_base;
@@ -310,19 +354,19 @@ __device__ __forceinline__ void issue_part(const GemmParams& p, const Loader<BM,
   __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(base, bytes), (DG_LDS void*)(smem + dst), 16, voff, 0, 0, 0);
 }
 
-template <int BM, int BN, int WM, int WN, int SFM, int... Us>
+template <int BM, int BN, int WM, int WN, int SFM, int LAY, int... Us>
 __device__ __forceinline__ void issue_parts(const GemmParams& p, const Loader<BM, BN, WM, WN>& ld, uint8_t* smem,
                                             int kb, int s, const int wave, const LaneOffsets lo,
                                             std::integer_sequence<int, Us...>) {
-  (issue_part<Us, BM, BN, WM, WN, SFM>(p, ld, smem, kb, s, wave, lo), ...);
+  (issue_part<Us, BM, BN, WM, WN, SFM, LAY>(p, ld, smem, kb, s, wave, lo), ...);
 }
 
 // The whole copy of K block kb into stage s at once (prologue and tile hand-over).
-template <int BM, int BN, int WM, int WN, int SFM>
+template <int BM, int BN, int WM, int WN, int SFM, int LAY = 0>
 __device__ __forceinline__ void issue_stage(const GemmParams& p, const Loader<BM, BN, WM, WN>& ld, uint8_t* smem,
                                             int kb, int s, const int wave, const LaneOffsets lo) {
   using S = Shape<BM, BN, WM, WN>;
-  issue_parts<BM, BN, WM, WN, SFM>(p, ld, smem, kb, s, wave, lo, std::make_integer_sequence<int, S::LPW>{});
+  issue_parts<BM, BN, WM, WN, SFM, LAY>(p, ld, smem, kb, s, wave, lo, std::make_integer_sequence<int, S::LPW>{});
 }
 
 // Wait until at most N vector-memory operations of this wave are outstanding and no
@@ -344,7 +388,7 @@ __device__ __forceinline__ void wait_and_barrier() {
 //    once every wave has read the last stage, the next tile's second stage too.
 // Returns the number of vector-memory operations this wave's epilogue issued (a lower
 // bound) and sets `next_pre2`.
-template <int BM, int BN, int WM, int WN, int SFM, int GRP, int OUT, int NF>
+template <int BM, int BN, int WM, int WN, int SFM, int GRP, int OUT, int NF, int LAY = 0>
 __device__ __forceinline__ int gemm_tile(const GemmParams& p, uint8_t* smem, const Tile& tl,
                                          const Loader<BM, BN, WM, WN>& ld, const bool has_next,
                                          const Loader<BM, BN, WM, WN>& ld_next, const int nkb_next, const int stage0,
@@ -373,6 +417,12 @@ __device__ __forceinline__ int gemm_tile(const GemmParams& p, uint8_t* smem, con
   const v4f zero = {0.f, 0.f, 0.f, 0.f};
   const int sw = swz(lr);  // fragment rows start on multiples of 16: swz(row) == swz(lr)
   const int off_lo = ((2 * lg) ^ sw) * 16, off_hi = ((2 * lg + 1) ^ sw) * 16;
+  // MN-major strips: lane 2b + h of lane group lg reads 8 bytes (columns 8h..) of the row
+  // position holding K row 32 lg + 8 r + b (read r = 0 at mn_lo, r = 1 at mn_hi, r = 2 and 3
+  // 16 rows further)
+  const int l16 = lane & 15, flip = lg & 1;
+  const uint32_t mn_lo = (uint32_t)(16 * (32 * lg + 8 * flip + (l16 >> 1)) + 8 * (l16 & 1));
+  const uint32_t mn_hi = (uint32_t)(16 * (32 * lg + 8 * (flip ^ 1) + (l16 >> 1)) + 8 * (l16 & 1));
 
   // One K block.  SPREAD: the copy of K block kb+1 of this tile into the other stage goes
   // out spread evenly over the block's MFMAs (the memory pipe is the scarcest unit).
@@ -383,11 +433,11 @@ __device__ __forceinline__ int gemm_tile(const GemmParams& p, uint8_t* smem, con
     // stage s has landed everywhere and nobody still reads stage s^1
     if ((kb == 0 || (kb == 1 && pre2)) && vm_after >= FM * FN) wait_and_barrier<FM * FN>();
     else wait_and_barrier<0>();
-    if (!SPREAD && kb + 1 >= nkb && has_next) issue_stage<BM, BN, WM, WN, SFM>(p, ld_next, smem, 0, s ^ 1, wave, lo);
+    if (!SPREAD && kb + 1 >= nkb && has_next) issue_stage<BM, BN, WM, WN, SFM, LAY>(p, ld_next, smem, 0, s ^ 1, wave, lo);
     // slot U goes out just before MFMA number U * FM * FN / LPW of the block
     auto issue_before = [&]<int U>(const int t) {
       if constexpr (SPREAD) {
-        if ((U * FM * FN) / S::LPW == t) issue_part<U, BM, BN, WM, WN, SFM>(p, ld, smem, kb + 1, s ^ 1, wave, lo);
+        if ((U * FM * FN) / S::LPW == t) issue_part<U, BM, BN, WM, WN, SFM, LAY>(p, ld, smem, kb + 1, s ^ 1, wave, lo);
       }
     };
     auto issue_all_before = [&]<int... Us>(const int t, std::integer_sequence<int, Us...>) {
@@ -400,12 +450,27 @@ __device__ __forceinline__ int gemm_tile(const GemmParams& p, uint8_t* smem, con
       const v4i hi4 = *(const v4i*)(rp + off_hi);
       return (v8i){lo4.x, lo4.y, lo4.z, lo4.w, hi4.x, hi4.y, hi4.z, hi4.w};
     };
+    // MN-major region at byte `region`: fragment of the 16 columns of strip `strip`, four
+    // transposing reads of 8 K each (lane group lg holds K [32 lg, +32), as the K-major reads)
+    auto read_frag_mn = [&](int region, int strip) -> v8i {
+      const uint32_t a0 = (uint32_t)(s * S::STAGE_BYTES + region + strip * 2048) + mn_lo;
+      const uint32_t a1 = (uint32_t)(s * S::STAGE_BYTES + region + strip * 2048) + mn_hi;
+      const v2i x0 = read_tr8(smem, a0), x1 = read_tr8(smem, a1);
+      const v2i x2 = read_tr8(smem, a0 + 256), x3 = read_tr8(smem, a1 + 256);
+      return (v8i){x0.x, x0.y, x1.x, x1.y, x2.x, x2.y, x3.x, x3.y};
+    };
     // fragments needed by the first MFMA first, so it waits for as few reads as possible
+    // (the K-major reads are written out at each use: routing them through a helper that also
+    // holds the MN-major form costs the K-grouped kernel about 45 registers)
     v8i af[FM];
-    v8i bf = read_frag(BM + wn * TN + lr);
-    af[0] = read_frag(wm * TM + lr);
+    v8i bf;
+    if constexpr ((LAY & LAYOUT_B_MN) != 0) bf = read_frag_mn(BM * BK, (wn * TN) / 16);
+    else bf = read_frag(BM + wn * TN + lr);
 #pragma unroll
-    for (int i = 1; i < FM; ++i) af[i] = read_frag(wm * TM + 16 * i + lr);
+    for (int i = 0; i < FM; ++i) {
+      if constexpr ((LAY & LAYOUT_A_MN) != 0) af[i] = read_frag_mn(0, (wm * TM) / 16 + i);
+      else af[i] = read_frag(wm * TM + 16 * i + lr);
+    }
 
     // promotion factors for this block: activation scales from the stage's scale region,
     // 128x128 weight-block scales (two per wave at most) by scalar loads
@@ -464,7 +529,8 @@ __device__ __forceinline__ int gemm_tile(const GemmParams& p, uint8_t* smem, con
       v8i bf_next = bf;
       int eb_next = eb;
       if (j + 1 < FN) {
-        bf_next = read_frag(BM + wn * TN + 16 * (j + 1) + lr);
+        if constexpr ((LAY & LAYOUT_B_MN) != 0) bf_next = read_frag_mn(BM * BK, (wn * TN) / 16 + j + 1);
+        else bf_next = read_frag(BM + wn * TN + 16 * (j + 1) + lr);
         if (SFM == SF_1D1D_UE8M0) eb_next = weight_code(j + 1);
       }
 #pragma unroll
@@ -499,7 +565,7 @@ __device__ __forceinline__ int gemm_tile(const GemmParams& p, uint8_t* smem, con
   next_pre2 = false;
   if (has_next && nkb >= 2 && nkb_next >= 2) {
     wait_and_barrier<63>();
-    issue_stage<BM, BN, WM, WN, SFM>(p, ld_next, smem, 1, (stage0 + nkb - 1) & 1, wave, lo);
+    issue_stage<BM, BN, WM, WN, SFM, LAY>(p, ld_next, smem, 1, (stage0 + nkb - 1) & 1, wave, lo);
     next_pre2 = true;
   }
 
@@ -563,14 +629,14 @@ __device__ __forceinline__ int gemm_tile(const GemmParams& p, uint8_t* smem, con
   return interior ? FM * FN : 0;
 }
 
-template <int BM, int BN, int WM, int WN, int SFM, int GRP, int OUT>
+template <int BM, int BN, int WM, int WN, int SFM, int GRP, int OUT, int LAY = 0>
 __global__ void __launch_bounds__(WM* WN * 64, 1) gemm_kernel(const GemmParams p) {
   using S = Shape<BM, BN, WM, WN>;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[S::LDS_BYTES];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int wn = wave % WN;
-  const LaneOffsets lo = make_lane_offsets(p, wave, lane);
+  const LaneOffsets lo = make_lane_offsets<LAY>(p, wave, lane);
   int bid = blockIdx.x;
   if (p.xcd_remap) {  // workgroups are dealt round-robin to the 8 XCDs
     const int per = gridDim.x / 8;
@@ -587,8 +653,8 @@ __global__ void __launch_bounds__(WM* WN * 64, 1) gemm_kernel(const GemmParams p
   Tile cur;
   if (!advance(t, cur)) return;
   Loader<BM, BN, WM, WN> ld_cur, ld_next;
-  make_loader<BM, BN, WM, WN, SFM, GRP>(p, cur, ld_cur);
-  issue_stage<BM, BN, WM, WN, SFM>(p, ld_cur, smem, 0, 0, wave, lo);
+  make_loader<BM, BN, WM, WN, SFM, GRP, LAY>(p, cur, ld_cur);
+  issue_stage<BM, BN, WM, WN, SFM, LAY>(p, ld_cur, smem, 0, 0, wave, lo);
   int stage0 = 0;
   int vm_after = 0;
   bool pre2 = false;
@@ -596,7 +662,7 @@ __global__ void __launch_bounds__(WM* WN * 64, 1) gemm_kernel(const GemmParams p
     Tile nxt;
     int tn = t + gridDim.x;
     const bool has_next = advance(tn, nxt);
-    if (has_next) make_loader<BM, BN, WM, WN, SFM, GRP>(p, nxt, ld_next);
+    if (has_next) make_loader<BM, BN, WM, WN, SFM, GRP, LAY>(p, nxt, ld_next);
     const int nkb_next = has_next ? nxt.nkb : 0;
     bool next_pre2 = false;
     if (SFM == SF_1D2D_F32) {
@@ -607,7 +673,7 @@ __global__ void __launch_bounds__(WM* WN * 64, 1) gemm_kernel(const GemmParams p
 #define DG_NF_CASE(X)                                                                                   \
   case X:                                                                                               \
     if constexpr (X <= S::FN)                                                                           \
-      vm_after = gemm_tile<BM, BN, WM, WN, SFM, GRP, OUT, X>(p, smem, cur, ld_cur, has_next, ld_next,   \
+      vm_after = gemm_tile<BM, BN, WM, WN, SFM, GRP, OUT, X, LAY>(p, smem, cur, ld_cur, has_next, ld_next, \
                                                              nkb_next, stage0, pre2, vm_after,          \
                                                              next_pre2, wave, lane, lo);                \
     break;
@@ -617,8 +683,9 @@ __global__ void __launch_bounds__(WM* WN * 64, 1) gemm_kernel(const GemmParams p
         default: break;
       }
     } else {
-      vm_after = gemm_tile<BM, BN, WM, WN, SFM, GRP, OUT, S::FN>(p, smem, cur, ld_cur, has_next, ld_next, nkb_next,
-                                                                stage0, pre2, vm_after, next_pre2, wave, lane, lo);
+      vm_after = gemm_tile<BM, BN, WM, WN, SFM, GRP, OUT, S::FN, LAY>(p, smem, cur, ld_cur, has_next, ld_next,
+                                                                     nkb_next, stage0, pre2, vm_after, next_pre2,
+                                                                     wave, lane, lo);
     }
     if (!has_next) break;
     stage0 = (stage0 + cur.nkb) & 1;
@@ -632,9 +699,9 @@ __global__ void __launch_bounds__(WM* WN * 64, 1) gemm_kernel(const GemmParams p
 // ------------------------------------------------------------------ dispatch
 // The file is compiled once per tile shape with DG_TILE_ID set (so the kernel
 // instantiations build in parallel) and once without it for the dispatch table.
-template <int BM, int BN, int WM, int WN, int SFM, int GRP, int OUT>
+template <int BM, int BN, int WM, int WN, int SFM, int GRP, int OUT, int LAY = 0>
 static hipError_t launch_one(const GemmParams& p, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, SFM, GRP, OUT>), dim3(grid), dim3(WM * WN * 64), 0,
+  hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, SFM, GRP, OUT, LAY>), dim3(grid), dim3(WM * WN * 64), 0,
                      stream, p);
   return hipGetLastError();
 }
@@ -664,8 +731,18 @@ static hipError_t launch_tile(const GemmParams& p, int sfm, int grp, int out, in
   DG_CASE(SF_1D1D_UE8M0, GRP_MASKED, OUT_BF16)
   DG_CASE(SF_1D1D_UE8M0, GRP_MASKED, OUT_F32)
   if constexpr (BN >= 224) {
-    DG_CASE(SF_1D1D_F32, GRP_KGROUP, OUT_F32_C)
+    // K-grouped: NT, or both operands stored K-outermost (TN, the weight-gradient storage; on the
+    // 224-wide tiles, where its registers fit without spilling)
+    if (sfm == SF_1D1D_F32 && grp == GRP_KGROUP && out == OUT_F32_C) {
+      if constexpr (BN == 224) {
+        if (p.layout == (LAYOUT_A_MN | LAYOUT_B_MN))
+          return launch_one<BM, BN, WM, WN, SF_1D1D_F32, GRP_KGROUP, OUT_F32_C, LAYOUT_A_MN | LAYOUT_B_MN>(p, grid, s);
+      }
+      if (p.layout == 0) return launch_one<BM, BN, WM, WN, SF_1D1D_F32, GRP_KGROUP, OUT_F32_C>(p, grid, s);
+      return hipErrorInvalidValue;
+    }
   }
+  if (p.layout != 0) return hipErrorInvalidValue;
 #undef DG_CASE
   return hipErrorInvalidValue;
 }
@@ -705,10 +782,14 @@ const TileCfg kTiles[kNumTiles] = {
 DG_DECL(0) DG_DECL(1) DG_DECL(2) DG_DECL(3) DG_DECL(4) DG_DECL(5) DG_DECL(6) DG_DECL(7) DG_DECL(8)
 #undef DG_DECL
 
-bool gemm_instantiated(int tile, int sfm, int grp, int out) {
+bool gemm_instantiated(int tile, int sfm, int grp, int out, int layout) {
   if (tile < 0 || tile >= kNumTiles) return false;
   if (sfm < 0 || sfm > 2 || out < 0 || out > 2) return false;
-  if (grp == GRP_KGROUP) return sfm == SF_1D1D_F32 && out == OUT_F32_C && kTiles[tile].bn >= 224;
+  if (grp == GRP_KGROUP) {
+    if (layout == (LAYOUT_A_MN | LAYOUT_B_MN)) return sfm == SF_1D1D_F32 && out == OUT_F32_C && kTiles[tile].bn == 224;
+    return layout == 0 && sfm == SF_1D1D_F32 && out == OUT_F32_C && kTiles[tile].bn >= 224;
+  }
+  if (layout != 0) return false;
   if (grp == GRP_CONTIG) {
     if (kTiles[tile].bm > 128) return false;
     if (out == OUT_F32_C) return false;
@@ -730,7 +811,7 @@ int gemm_lds_bytes(int tile) {
 
 hipError_t launch_gemm(const GemmParams& p, int tile, int sfm, int grp, int out, int grid,
                        hipStream_t stream) {
-  if (!gemm_instantiated(tile, sfm, grp, out)) return hipErrorInvalidValue;
+  if (!gemm_instantiated(tile, sfm, grp, out, p.layout)) return hipErrorInvalidValue;
   switch (tile) {
     case 0: return launch_tile_0(p, sfm, grp, out, grid, stream);
     case 1: return launch_tile_1(p, sfm, grp, out, grid, stream);

@@ -78,7 +78,7 @@ extern const TileCfg kTiles[kNumTiles];
 // hipErrorInvalidValue for a combination that is not instantiated.
 hipError_t launch_gemm(const GemmParams& p, int tile, int sf_mode, int group, int out, int grid,
                        hipStream_t stream);
-bool gemm_instantiated(int tile, int sf_mode, int group, int out);
+bool gemm_instantiated(int tile, int sf_mode, int group, int out, int layout = 0);
 int gemm_lds_bytes(int tile);
 
 // Deep-pipelined kernels (dg_gemm_pipe.hip): dense problems, contiguous and masked groups.

@@ -286,6 +286,21 @@ int dg_k_grouped_fp8_gemm_nt_contiguous(int32_t num_groups, int32_t m, int32_t n
                                         const float* c, float* d, hipStream_t stream);
 
 /*
+ * K-grouped contiguous GEMM with both operands stored K-outermost (page "第13章 DeepGEMM"
+ * §13.6 and §13.13: k_grouped_fp8_gemm_tn_contiguous, the weight-gradient form whose operands
+ * are the token-major activations and output gradients as the forward pass leaves them):
+ *  a, lda : A E4M3 [sum(ks), m], element (i, kk) at a[kk*lda + i]; m <= lda < 2^23, lda % 16 == 0,
+ *           sum(ks) * lda < 2^31, 16-byte aligned.
+ *  b, ldb : B E4M3 [sum(ks), n], element (j, kk) at b[kk*ldb + j]; the same rules with n.
+ * Scales, C, D, groups and errors as in dg_k_grouped_fp8_gemm_nt_contiguous; the same D.
+ * Problems with more than 64 non-empty groups (either layout) take one launch per 64 groups.
+ */
+int dg_k_grouped_fp8_gemm_tn_contiguous(int32_t num_groups, int32_t m, int32_t n, const int32_t* ks,
+                                        const void* a, int64_t lda, const float* sfa,
+                                        const void* b, int64_t ldb, const float* sfb,
+                                        const float* c, float* d, hipStream_t stream);
+
+/*
  * Per-token-group FP8 cast (page "02 · DeepGEMM 技术解析" §1.1: activations in 1x128 groups
  * along K, one FP32 scale per group; page "第13章 DeepGEMM" §13.3: the scale is amax / 448):
  * produces the A operand and its scales for the GEMMs above, already in their layout.

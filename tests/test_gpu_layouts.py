@@ -202,3 +202,57 @@ def test_fp8_fp4_tt_equals_nt_bitwise_and_oracle(tile, shape):
             ok, st = check_fp32(res[1].cpu().numpy(), o, T)
         say("fp8 x fp4 tt", st)
         assert ok.all(), st
+
+
+def _k_grouped_operands(p, layout, pad=16):
+    if layout == "nt":
+        return cuda(p["a"]), cuda(p["b"])
+    return stored_t(p["a"], pad), stored_t(p["b"], pad)
+
+
+@pytest.mark.parametrize("m,n,ks", [(260, 196, [256, 0, 384, 128, 512]), (64, 520, [128]), (4, 4, [0, 128, 0]),
+                                    (516, 388, [1024, 128, 0, 640])])
+def test_k_grouped_tn_equals_nt_bitwise_and_oracle(m, n, ks):
+    """K-grouped GEMM with both operands stored K-outermost ([sum K, m] and [sum K, n], the
+    token-major storage of the weight-gradient operands): the NT result bit for bit on the same
+    tile, and the oracle read through the storage; empty groups give C, C accumulated in place."""
+    p = gen.k_grouped(m, n, ks, seed=m + n + 3 * len(ks))
+    sfa, sfb = cuda(np.ascontiguousarray(p["sa"].T)), cuda(np.ascontiguousarray(p["sb"].T))
+    outs = {}
+    for layout in ("nt", "tn"):
+        say("k-grouped", layout, m, n, ks)
+        a, b = _k_grouped_operands(p, layout)
+        d = cuda(p["c"]).clone()
+        getattr(dg, f"k_grouped_fp8_gemm_{layout}_contiguous")((a, sfa), (b, sfb), d, ks, d)
+        torch.cuda.synchronize()
+        outs[layout] = d.cpu()
+    assert torch.equal(outs["nt"].view(torch.int32), outs["tn"].view(torch.int32))
+    o, T = oracle.k_grouped_tn(np.ascontiguousarray(p["a"].T), p["sa"], np.ascontiguousarray(p["b"].T), p["sb"],
+                               ks, p["c"], want_abs=True)
+    ok, st = check_fp32(outs["tn"].numpy(), o, T)
+    say("k-grouped tn", st)
+    assert ok.all(), st
+    for g, k in enumerate(ks):
+        if k == 0:
+            assert np.array_equal(outs["tn"].numpy()[g], p["c"][g])
+
+
+def test_k_grouped_tn_more_than_64_groups():
+    """70 groups (some empty) with token-major operands: two launches of up to 64 groups, each
+    group into its own output, against the oracle; C read separately."""
+    rng = np.random.default_rng(70)
+    ks = [int(x) * 128 for x in rng.integers(0, 3, 70)]
+    ks[0], ks[-1] = 256, 128
+    m, n = 96, 132
+    p = gen.k_grouped(m, n, ks, seed=70)
+    say("k-grouped tn 70 groups", sum(k > 0 for k in ks))
+    a, b = _k_grouped_operands(p, "tn", pad=0)
+    c = cuda(p["c"])
+    d = torch.full_like(c, float("nan"))
+    dg.k_grouped_fp8_gemm_tn_contiguous((a, cuda(np.ascontiguousarray(p["sa"].T))),
+                                        (b, cuda(np.ascontiguousarray(p["sb"].T))), d, ks, c)
+    torch.cuda.synchronize()
+    o, T = oracle.k_grouped(p["a"], p["sa"], p["b"], p["sb"], ks, p["c"], want_abs=True)
+    ok, st = check_fp32(d.cpu().numpy(), o, T)
+    say("k-grouped tn 70 groups", st)
+    assert ok.all(), st

@@ -833,8 +833,8 @@ def test_skinny_decode_shapes(bn, shape):
 
 @pytest.mark.parametrize("G", [64, 66])
 def test_k_grouped_many_groups(G):
-    """Up to 64 non-empty groups run as one launch over every group's tiles; beyond that the
-    groups run one launch each.  Groups of one to three K blocks, some empty, C separate."""
+    """Up to 64 non-empty groups run as one launch over every group's tiles; beyond that, one
+    launch per 64 groups.  Groups of one to three K blocks, some empty, C separate."""
     rng = np.random.default_rng(G)
     ks = [int(x) * 128 for x in rng.integers(0, 4, G)]
     ks[0], ks[-1] = 128, 384
@@ -858,8 +858,8 @@ def test_k_grouped_many_groups(G):
 
 
 def test_k_grouped_single_launch_equals_group_loop():
-    """The one-launch K-grouped kernel and one dense launch per group (same tile, same
-    per-element order of MFMAs and promotions) give the same bits."""
+    """The one-launch K-grouped kernel and one launch per group (same tile, same per-element
+    order of MFMAs and promotions) give the same bits."""
     ks = [256, 0, 640, 128, 1024]
     m, n = 516, 516
     p = gen.k_grouped(m, n, ks, seed=77)

@@ -317,3 +317,20 @@ def test_grouped_nn_and_fp4_tt_validation():
     fargs["m"] = 0
     fargs["sfa_stride"] = 0
     assert lib.dg_fp8_fp4_gemm_tt(*fargs.values()) == DG_OK
+
+
+def test_k_grouped_tn_validation():
+    lib = dg.lib()
+    ks = lambda *v: (ctypes.c_int32 * len(v))(*v)
+    fn = lib.dg_k_grouped_fp8_gemm_tn_contiguous
+    # A stored [sum ks, m], B stored [sum ks, n]: lda >= m, ldb >= n (not >= sum ks)
+    assert fn(1, 32, 48, ks(128), P, 16, P, P, 48, P, P, P, None) == DG_ERR_LAYOUT      # lda < m
+    assert fn(1, 32, 48, ks(128), P, 32, P, P, 32, P, P, P, None) == DG_ERR_LAYOUT      # ldb < n
+    assert fn(1, 32, 48, ks(128), P, 40, P, P, 48, P, P, P, None) == DG_ERR_LAYOUT      # lda % 16
+    assert fn(1, 8, 8, ks(1 << 20), P, 4096, P, P, 16, P, P, P, None) == DG_ERR_LAYOUT  # sum ks * lda >= 2^31
+    assert fn(1, 32, 48, ks(128), P_MIS, 32, P, P, 48, P, P, P, None) == DG_ERR_LAYOUT
+    assert fn(2, 8, 8, ks(128, 64), P, 16, P, P, 16, P, P, P, None) == DG_ERR_SHAPE
+    assert fn(1, 8, 8, ks(128), P, 16, P, P, 16, P, None, P, None) == DG_ERR_NULL       # C required
+    # the NT rule (lda >= sum ks) does not apply to the TN storage, and vice versa
+    assert lib.dg_k_grouped_fp8_gemm_nt_contiguous(1, 32, 48, ks(256), P, 32, P, P, 48, P, P, P, None) == DG_ERR_LAYOUT
+    assert fn(1, 0, 8, ks(128), None, 0, None, None, 0, None, None, None, None) == DG_OK
