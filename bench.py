@@ -46,6 +46,10 @@ WORKLOADS = {
     "dense_4096x7168x2048": dict(kind="dense", M=4096, N=7168, K=2048),
     "dense_64x7168x2048": dict(kind="dense", M=64, N=7168, K=2048, graph=True),
     "dense_c_4096x1536x7168": dict(kind="dense_c", M=4096, N=1536, K=7168),
+    # the other operand layouts (A stored [K, M] for "t", B stored [K, N] for "n")
+    "dense_nn_4096x7168x2048": dict(kind="dense", M=4096, N=7168, K=2048, layout="nn"),
+    "dense_tn_4096x7168x2048": dict(kind="dense", M=4096, N=7168, K=2048, layout="tn"),
+    "dense_tt_4096x7168x2048": dict(kind="dense", M=4096, N=7168, K=2048, layout="tt"),
     "masked_32x256x7168x2048": dict(kind="masked"),
     "contiguous_32x4096x7168": dict(kind="contig"),
     "fp8_fp4_dense_4096x7168x2048": dict(kind="fp4_dense", M=4096, N=7168, K=2048),
@@ -55,6 +59,9 @@ WORKLOADS = {
     # MoE weight gradient: 8 experts' token counts (multiples of 128, 16384 in all) split K
     "k_grouped_8x7168x2048_k16384": dict(kind="k_grouped", M=7168, N=2048,
                                          ks=[1792, 2304, 2048, 1536, 2560, 2048, 1920, 2176]),
+    # the same with token-major operands (A stored [sum ks, M], B stored [sum ks, N])
+    "k_grouped_tn_8x7168x2048_k16384": dict(kind="k_grouped", M=7168, N=2048, layout="tn",
+                                            ks=[1792, 2304, 2048, 1536, 2560, 2048, 1920, 2176]),
 }
 DEFAULT = "dense_4096x7168x2048"
 HEADLINE_METRIC = "TFLOP/s + % FP8 MFMA peak, block-scaled FP8 GEMM M=4096 N=7168 K=2048"
@@ -76,9 +83,15 @@ def kernel_source_hash(sources=GEMM_SOURCES):
     return h.hexdigest()
 
 
-def read_traffic(workload, hash_key="kernel_source_sha1", sources=GEMM_SOURCES):
-    """HBM bytes per launch of the timed kernel from the committed rocprofv3 counter summary,
-    or None if absent or taken from another kernel source."""
+def sources_for(workload):
+    """The kernel sources whose traffic a workload measures: the cast kernel's or the GEMMs'."""
+    return CAST_SOURCES if workload.startswith("cast") else GEMM_SOURCES
+
+
+def read_traffic(workload):
+    """HBM bytes per launch of the timed kernel from the committed rocprofv3 counter summary
+    (profiles/hbm_traffic.txt, written by profile_counters.py), or None if absent or taken from
+    another kernel source than the current one."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     vals = {}
@@ -88,7 +101,7 @@ def read_traffic(workload, hash_key="kernel_source_sha1", sources=GEMM_SOURCES):
             k, v = line.split("=", 1)
             vals[k.strip()] = v.strip()
     key = f"{workload}.bytes_per_launch"
-    if key not in vals or vals.get(hash_key) != kernel_source_hash(sources):
+    if key not in vals or vals.get(f"{workload}.source_sha1") != kernel_source_hash(sources_for(workload)):
         return None
     return float(vals[key])
 
@@ -124,9 +137,14 @@ def w_dense(spec, dg, dev):
     p = gen.dense(M, N, K, seed=0, with_c=with_c)
     out_dtype = torch.float32 if with_c else torch.bfloat16
     nsets = 8 if M * K + N * K < 256 << 20 else 2
+    layout = spec.get("layout", "nt")
+    # operands as the layout stores them: A [K, M] for "t", B [K, N] for "n"
+    a_st = p["a"] if layout[0] == "n" else np.ascontiguousarray(p["a"].T)
+    b_st = p["b"] if layout[1] == "t" else np.ascontiguousarray(p["b"].T)
+    gemm = getattr(dg, "fp8_gemm_" + layout)
     sets = []
     for _ in range(nsets):
-        s = dict(a=torch.from_numpy(p["a"]).to(dev), b=torch.from_numpy(p["b"]).to(dev),
+        s = dict(a=torch.from_numpy(a_st).to(dev), b=torch.from_numpy(b_st).to(dev),
                  sa_raw=torch.from_numpy(p["sa"]).to(dev), sb=torch.from_numpy(p["sb"]).to(dev),
                  d=torch.empty((M, N), dtype=out_dtype, device=dev))
         s["sa"] = dg.get_mn_major_tma_aligned_tensor(s["sa_raw"])
@@ -145,21 +163,24 @@ def w_dense(spec, dg, dev):
 
     def launch(i):
         s = sets[i % nsets]
-        dg.fp8_gemm_nt((s["a"], s.get("sa_step", s["sa"])), (s["b"], s["sb"]), s["d"], c=s.get("c"))
+        gemm((s["a"], s.get("sa_step", s["sa"])), (s["b"], s["sb"]), s["d"], c=s.get("c"))
 
     def cpu(seconds):
         import oracle
         rows = max(1, min(M, 64))
-        t0 = time.perf_counter()
-        oracle.gemm_nt(p["a"][:rows], p["sa"][:rows], p["b"], p["sb"], 128, c=None if p["c"] is None else p["c"][:rows])
-        t = time.perf_counter() - t0
+
+        def run_oracle(r):
+            # the oracle on the operands as stored (rows 0..r-1 of D)
+            a_rows = a_st[:r] if layout[0] == "n" else a_st[:, :r]
+            t0 = time.perf_counter()
+            oracle.gemm_layout(layout, a_rows, p["sa"][:r], b_st, p["sb"], 128, c=None if p["c"] is None else p["c"][:r])
+            return time.perf_counter() - t0
+
+        t = run_oracle(rows)
         if t < seconds / 4 and rows < M:
             rows = int(min(M, max(rows, rows * seconds / max(t, 1e-3))))
             rows = max(8, rows - rows % 8)
-            t0 = time.perf_counter()
-            oracle.gemm_nt(p["a"][:rows], p["sa"][:rows], p["b"], p["sb"], 128,
-                           c=None if p["c"] is None else p["c"][:rows])
-            t = time.perf_counter() - t0
+            t = run_oracle(rows)
         bound_work = 2.0 * rows * N * K if not spec.get("graph") else alg_bytes * rows / M
         return bound_work / t, t, f"rows 0..{rows - 1} of the {M}x{N}x{K} problem (all N columns, full K), float64 numpy"
 
@@ -169,7 +190,7 @@ def w_dense(spec, dg, dev):
     return Workload(pre=pre, launch=launch, work=alg_bytes if hbm else flops, flops=flops, alg_bytes=alg_bytes,
                     bound="hbm" if hbm else "mfma", kernel=kernel, cpu=cpu,
                     config={"workload": None, "M": M, "N": N, "K": K, "out": "fp32+C" if with_c else "bf16",
-                            "scales": "fp32 1x128 act, 128x128 weight",
+                            "layout": layout, "scales": "fp32 1x128 act, 128x128 weight",
                             "step": "transform_sf(act scales) + gemm", "buffer_sets": nsets})
 
 
@@ -296,34 +317,43 @@ def w_k_grouped(spec, dg, dev):
     import oracle
     M, N, ks = spec["M"], spec["N"], spec["ks"]
     K, G = sum(ks), len(ks)
+    layout = spec.get("layout", "nt")
+    gemm = getattr(dg, f"k_grouped_fp8_gemm_{layout}_contiguous")
     g = torch.Generator(device=dev).manual_seed(0)
     sets = []
     for _ in range(2):
         qa, sa = dg.per_token_group_cast_fp8(torch.randn((M, K), generator=g, device=dev).to(torch.bfloat16))
         qb, sb = dg.per_token_group_cast_fp8(torch.randn((N, K), generator=g, device=dev).to(torch.bfloat16))
+        if layout == "tn":   # token-major storage: [sum ks, M] and [sum ks, N]
+            qa, qb = qa.t().contiguous(), qb.t().contiguous()
         sets.append(dict(a=qa, sa=sa.t(), b=qb, sb=sb.t(), d=torch.zeros((G, M, N), device=dev)))
     flops = 2.0 * M * N * K
     alg_bytes = M * K + N * K + 4 * (M + N) * (K // 128) + 2 * 4 * G * M * N
 
     def launch(i):
         s = sets[i % len(sets)]
-        dg.k_grouped_fp8_gemm_nt_contiguous((s["a"], s["sa"]), (s["b"], s["sb"]), s["d"], ks, s["d"])
+        gemm((s["a"], s["sa"]), (s["b"], s["sb"]), s["d"], ks, s["d"])
 
     def cpu(seconds):
         rows = 256
         s = sets[0]
-        a = s["a"][:rows].cpu().numpy()
         sa = s["sa"][:, :rows].t().cpu().numpy()
         b, sb = s["b"].cpu().numpy(), s["sb"].t().cpu().numpy()
         c = np.zeros((G, rows, N), dtype=np.float32)
-        t0 = time.perf_counter()
-        oracle.k_grouped(a, sa, b, sb, ks, c)
+        if layout == "tn":   # the oracle on the operands as stored
+            a = s["a"][:, :rows].cpu().numpy()
+            t0 = time.perf_counter()
+            oracle.k_grouped_tn(a, sa, b, sb, ks, c)
+        else:
+            a = s["a"][:rows].cpu().numpy()
+            t0 = time.perf_counter()
+            oracle.k_grouped(a, sa, b, sb, ks, c)
         t = time.perf_counter() - t0
         return 2.0 * rows * N * K / t, t, f"rows 0..{rows - 1} of A (all {G} groups, all of B), float64 numpy"
 
     return Workload(launch=launch, work=flops, flops=flops, alg_bytes=alg_bytes, bound="mfma",
                     kernel="K-grouped GEMM (one step = every group)", cpu=cpu,
-                    config={"workload": None, "M": M, "N": N, "ks": ks, "out": "fp32, C = D in place",
+                    config={"workload": None, "M": M, "N": N, "ks": ks, "layout": layout, "out": "fp32, C = D in place",
                             "scales": "fp32 1x128 on both operands", "buffer_sets": len(sets)})
 
 
@@ -352,7 +382,7 @@ def w_cast(spec, dg, dev):
     return Workload(launch=launch, work=alg_bytes, flops=0.0, alg_bytes=alg_bytes, bound="hbm",
                     kernel=f"dg::cast_kernel<true, {'true' if ue8m0 else 'false'}>", cpu=cpu,
                     config={"workload": None, "M": M, "K": K, "scales": "ue8m0x4" if ue8m0 else "f32",
-                            "buffer_sets": len(xs)}, traffic_key=("cast_source_sha1", CAST_SOURCES))
+                            "buffer_sets": len(xs)})
 
 
 BUILDERS = {"dense": w_dense, "dense_c": w_dense, "masked": w_masked, "contig": w_contig,
@@ -545,9 +575,8 @@ def main():
         cpu = {"value": round(v / scale, 6), "unit": unit, "cores": blas_threads(), "kind": "oracle",
                "seconds": round(secs, 2), "sample": sample}
 
-    tk = getattr(wl, "traffic_key", ("kernel_source_sha1", GEMM_SOURCES))
     roof = {"bound": wl.bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
-            "frac": round(achieved / peak, 4), "traffic": read_traffic(args.workload, *tk),
+            "frac": round(achieved / peak, 4), "traffic": read_traffic(args.workload),
             "kernel": wl.kernel, "kernel_ms_mean": round(kern_ms["mean"], 5),
             "kernel_ms_median": round(kern_ms["median"], 5), "kernel_ms_min": round(kern_ms["min"], 5),
             "frac_median": round(wl.work / (kern_ms["median"] * 1e-3) / scale / peak, 4),

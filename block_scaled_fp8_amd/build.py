@@ -122,30 +122,51 @@ def clean():
 
 LAST_RESOURCE_USAGE = []
 
-_SF = {0: "1d2d FP32", 2: "UE8M0", 3: "FP4 weights"}
+_SF = {0: "1d2d FP32", 1: "1d1d FP32", 2: "UE8M0", 3: "FP4 weights"}
 _OUT = {0: "BF16", 1: "FP32", 2: "FP32+C"}
 _GRP = {0: "dense", 1: "contiguous", 2: "masked"}
 
 
+_LAY = {0: "nt", 1: "A [K,M]", 2: "B [K,N]", 3: "A [K,M], B [K,N]"}
+
+
 def resource_table(reports):
-    """One line per pipelined instantiation: tile, waves, scales, output, registers, scratch."""
+    """One line per GEMM instantiation: kernel, tile, waves, scales, output, operand storage,
+    registers, scratch, occupancy and LDS."""
     import re
     lines = []
     for r in reports:
-        m = re.search(r"pipe_kernelILi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)E", r["name"])
-        if not m:
+        regs = (f"VGPR {r.get('vgpr', 0):3d} AGPR {r.get('agpr', 0):3d} scratch {r.get('scratch', 0):3d} B/lane "
+                f"SGPR spills {r.get('sgpr_spill', 0):2d} waves/SIMD {r.get('occupancy', 0)} LDS {r.get('lds', 0)}")
+        m = re.search(r"pipe_kernelILi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)E", r["name"])
+        if m:
+            bm, bn, wm, wn, sf, out, grp, nb, lay = map(int, m.groups())
+            forced = any(f in r["name"] for f in FORCED_ONLY)
+            lines.append(f"pipelined {_GRP[grp]:10s} {bm}x{bn} {wm * wn} waves {_SF[sf]:11s} {_OUT[out]:6s} "
+                         f"{_LAY[lay]:16s} B stages {nb}: {regs}" + ("   (forced tiles only)" if forced else ""))
             continue
-        bm, bn, wm, wn, sf, out, grp, nb = map(int, m.groups())
-        forced = any(f in r["name"] for f in FORCED_ONLY)
-        lines.append(f"{_GRP[grp]:10s} {bm}x{bn} {wm * wn} waves {_SF[sf]:11s} {_OUT[out]:6s} B stages {nb}: "
-                     f"VGPR {r.get('vgpr', 0):3d} AGPR {r.get('agpr', 0):3d} scratch {r.get('scratch', 0):3d} B/lane "
-                     f"SGPR spills {r.get('sgpr_spill', 0):2d} waves/SIMD {r.get('occupancy', 0)} LDS {r.get('lds', 0)}"
-                     + ("   (forced tiles only)" if forced else ""))
+        m = re.search(r"gemm_kernelILi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)E", r["name"])
+        if m:
+            bm, bn, wm, wn, sf, grp, out, lay = map(int, m.groups())
+            sfn = {0: "1d2d FP32", 1: "1d1d FP32", 2: "UE8M0"}[sf]
+            grn = {0: "dense", 1: "contiguous", 2: "masked", 3: "K-grouped"}[grp]
+            lines.append(f"generic   {grn:10s} {bm}x{bn} {wm * wn} waves {sfn:11s} {_OUT[out]:6s} {_LAY[lay]:16s}"
+                         f"           : {regs}")
+            continue
+        m = re.search(r"skinny_kernelILi(\d+)ELi(\d+)ELi(\d+)E", r["name"])
+        if m:
+            bn, nw, out = map(int, m.groups())
+            lines.append(f"skinny    dense      <=64x{bn} {nw} waves 1d2d FP32   {_OUT[out]:6s} nt"
+                         f"                          : {regs}")
     return lines
 
 
 if __name__ == "__main__":
     build(verbose="--resource-report" not in sys.argv)
     if "--resource-report" in sys.argv:
-        print("\n".join(resource_table(LAST_RESOURCE_USAGE)))
+        print("# Register, scratch, occupancy and LDS figures of every GEMM instantiation in libdg.so, from")
+        print("# hipcc's -Rpass-analysis=kernel-resource-usage remarks (gfx950).  Made by:")
+        print("#   python -m block_scaled_fp8_amd.build --resource-report")
+        print("# The build fails if a kernel the planner can pick uses scratch (register spills).")
+        print("\n".join(sorted(resource_table(LAST_RESOURCE_USAGE))))
     sys.exit(0)

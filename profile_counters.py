@@ -43,16 +43,48 @@ KERNEL = {
     "contiguous_32x4096x7168": "pipe_kernel", "fp8_fp4_dense_4096x7168x2048": "pipe_kernel",
     "fp8_fp4_masked_32x256x7168x2048": "pipe_kernel", "cast_4096x7168_bf16": "cast_kernel",
     "cast_ue8m0_4096x7168_bf16": "cast_kernel", "k_grouped_8x7168x2048_k16384": "gemm_kernel",
+    "dense_nn_4096x7168x2048": "pipe_kernel", "dense_tn_4096x7168x2048": "pipe_kernel",
+    "dense_tt_4096x7168x2048": "pipe_kernel", "k_grouped_tn_8x7168x2048_k16384": "gemm_kernel",
 }
-SOURCES = ("dg_gemm.hip", "dg_gemm_pipe.hip", "dg_gemm_skinny.hip", "dg_quant.hip", "dg_internal.h")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
+TRAFFIC_HEADER = """# HBM traffic of the timed kernel launch from rocprofv3 counters, one MI355X.
+# Per workload, two runs of one counter each (written by profile_counters.py):
+#   rocprofv3 --pmc FETCH_SIZE -f csv -d <out> -o run -- python3 bench.py --workload <w> --steps 5 --warmup 2 --no-cpu-baseline --no-extras --copy-calibration-mb 512
+#   rocprofv3 --pmc WRITE_SIZE -f csv -d <out> -o run -- python3 bench.py --workload <w> --steps 5 --warmup 2 --no-cpu-baseline --no-extras --copy-calibration-mb 512
+# Calibration: the same runs copy 512 MiB device-to-device once (a kernel of known traffic,
+#   512 MiB read and 512 MiB written); its counter reading gives the bytes per counter KiB.
+# Bytes = counter KiB x 1024 x factor.  <w>.source_sha1 ties a workload's figures to the kernel
+# sources they were taken from (bench.py's kernel_source_hash); bench.py reports traffic as null
+# when the current sources differ.
+"""
 
 
-def source_hash():
-    h = hashlib.sha1()
-    for f in SOURCES:
-        with open(os.path.join(ROOT, "block_scaled_fp8_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()
+def source_hash(workload):
+    sys.path.insert(0, ROOT)
+    from bench import kernel_source_hash, sources_for
+    return kernel_source_hash(sources_for(workload))
+
+
+def update_traffic_file(workload, res):
+    """Replace the workload's lines in profiles/hbm_traffic.txt (other workloads are kept)."""
+    keep = []
+    if os.path.exists(TRAFFIC_FILE):
+        for line in open(TRAFFIC_FILE):
+            t = line.strip()
+            if t and not t.startswith("#") and "=" in t and not t.startswith(workload + "."):
+                keep.append(t)
+    keep.append(f"{workload}.source_sha1 = {source_hash(workload)}")
+    for k, name in (("FETCH_SIZE", "fetch_kib_per_launch"), ("WRITE_SIZE", "write_kib_per_launch")):
+        if k in res:
+            keep.append(f"{workload}.{name} = {res[k]:.0f}")
+    for k, name in (("fetch_factor", "fetch_factor"), ("write_factor", "write_factor")):
+        if k in res:
+            keep.append(f"{workload}.{name} = {res[k]:.4f}")
+    keep.append(f"{workload}.read_bytes_per_launch = {res.get('FETCH_SIZE_bytes', 0.0):.0f}")
+    keep.append(f"{workload}.write_bytes_per_launch = {res.get('WRITE_SIZE_bytes', 0.0):.0f}")
+    keep.append(f"{workload}.bytes_per_launch = {res['bytes_per_launch']:.0f}")
+    with open(TRAFFIC_FILE, "w") as f:
+        f.write(TRAFFIC_HEADER + "\n".join(sorted(keep, key=lambda x: x.split(".")[0])) + "\n")
 
 
 def bench_args(workload):
@@ -127,7 +159,7 @@ def main():
     kernel = KERNEL[args.workload]
     passes = args.passes.split(",")
     out = [f"# rocprofv3 summary: bench.py --workload {args.workload}, one MI355X ({NUM_CU} CUs)",
-           f"# kernel source sha1 (dg_gemm*.hip, dg_quant.hip, dg_internal.h) = {source_hash()}",
+           f"# kernel source sha1 (bench.py's kernel_source_hash for this workload) = {source_hash(args.workload)}",
            f"# made by: python profile_counters.py {args.workload} --passes {args.passes}", ""]
     res = {}
     for name in passes:
@@ -159,6 +191,7 @@ def main():
                 factor = (512 * 1024 if name == "fetch" else 512 * 1024) / cal
                 key = "FETCH_SIZE" if name == "fetch" else "WRITE_SIZE"
                 res[key + "_bytes"] = vals.get(key, 0.0) * 1024 * factor
+                res[name + "_factor"] = factor
                 out.append(f"  calibration copy of 512 MiB read {cal:.6g} KiB -> {factor:.4f} bytes per counter byte; "
                            f"{key} = {res[key + '_bytes'] / 1e6:.2f} MB per dispatch")
         out.append("")
@@ -201,8 +234,9 @@ def main():
         with open(path, "w") as f:
             f.write("\n".join(out) + "\n")
         print(f"[profile] wrote {path}", flush=True)
-    if "bytes_per_launch" in res:
-        print(f"[profile] {args.workload}.bytes_per_launch = {res['bytes_per_launch']:.0f}", flush=True)
+    if "FETCH_SIZE_bytes" in res and "WRITE_SIZE_bytes" in res:
+        update_traffic_file(args.workload, res)
+        print(f"[profile] {args.workload}.bytes_per_launch = {res['bytes_per_launch']:.0f} -> {TRAFFIC_FILE}", flush=True)
 
 
 if __name__ == "__main__":
