@@ -321,6 +321,21 @@ struct Kernel {
   static constexpr bool AMN = (LAY & LAYOUT_A_MN) != 0, BMN = (LAY & LAYOUT_B_MN) != 0;
   static_assert(!(BMN && FP4B), "FP4 weights are K-major");
   static constexpr int FBA = FP4B ? 4 : 5, FBB = 5;  // row-permutation bit of an MN-major stage
+  // MN-major operands 128 or 256 columns wide are staged row-major with an XOR key per K row
+  // (the copies then read whole 256-byte row segments); other widths as 16-column strips.
+  // (Measured on 4096x7168x2048: tt 91-93 -> 79-81 us; with both operands MN-major, B in
+  // strips, row-XOR A was 6% slower than strips, so that case keeps strips.)
+  static constexpr bool ARX = AMN && !BMN && (BM == 256 || BM == 128), BRX = BMN && (BN == 256 || BN == 128);
+  // Row-XOR staging of an MN-major operand W columns wide: wave-load q fills K rows
+  // q * (1024 / W) + [0, 1024 / W), and the XOR key of row r has bit FB of r as its top bit.
+  // Which copy offset wave-load part U uses: -1 when that bit of q comes from the wave index
+  // (the lane offset already holds it), else the bit of U it comes from.
+  template <int W, int FB>
+  static constexpr int rx_ubit(int U) {
+    constexpr int sh = W == 256 ? 2 : 3;  // log2 of the K rows per wave-load
+    constexpr int lnw = NW == 8 ? 3 : 2;
+    return FB - sh < lnw ? -1 : (U >> (FB - sh - lnw)) & 1;
+  }
   static constexpr int FM = G::FM, FN = G::FN, TM = G::TM, TN = G::TN, STEPS = G::STEPS;
   static constexpr int NW = G::NW;
   static __device__ __forceinline__ int next_b(int b) { return b == NB - 1 ? 0 : b + 1; }
@@ -339,6 +354,7 @@ struct Kernel {
   int wshift;                       // FP4 weights: bit offset of this lane's 32-K block scale in the packed word
   int ustep_a, ustep_b;             // 8 * NW * ld (MN-major: 8 * NW)
   uint32_t kstep_a, kstep_b;        // bytes of one K block along the source (BK or BKB; MN-major: BK * ld)
+  uint32_t off_a1, off_b1;          // row-XOR staging: the copy offsets of parts whose key bit comes from U = 1
   uint32_t sstep_a, sstep_b;        // bytes per K-block row of the activation / per-row weight scales
   // masked groups (at most 64): lane g holds group g's valid rows and the inclusive prefix
   // sum of the tiles of groups 0..g, so a tile index maps to its group with one ballot
@@ -405,12 +421,43 @@ struct Kernel {
       const int k0 = fb == 5 ? 32 * lg : 16 * lg;
       return (uint32_t)(off + strip0 * 2048 + 16 * (k0 + 8 * flip + (l >> 1)) + 8 * (l & 1));
     };
+    // Row-XOR staging (W = 128 or 256 columns): K row r sits at LDS row r, W bytes, its
+    // 16-byte chunk s at position s ^ key(r): key = (r & 7) | bit_FB(r) << 3 for W = 256,
+    // ((r >> 1) & 3) | bit_FB(r) << 2 for W = 128.  The 16 K rows one transposing read takes in
+    // a cycle (8 per lane group, the two groups differing in bit FB) then land on 16 different
+    // 4-bank groups.  Lane L of wave-load q copies chunk (L % C) ^ key(r) of row
+    // r = q * (1024 / W) + L / C (C = W / 16): consecutive lanes read consecutive bytes of a row.
+    auto rx_copy = [&](int64_t ld, int w, int fb, int ubit) -> uint32_t {
+      const uint32_t C = (uint32_t)w / 16, rw = 1024u / (uint32_t)w, L = (uint32_t)lane;
+      const uint32_t r = (uint32_t)wave * rw + L / C;  // (part U adds U * NW * rw rows)
+      const uint32_t bfb = ubit < 0 ? (r >> fb) & 1u : (uint32_t)ubit;
+      const uint32_t key = w == 256 ? (r & 7u) | (bfb << 3) : ((r >> 1) & 3u) | (bfb << 2);
+      return r * (uint32_t)ld + 16u * ((L % C) ^ key);
+    };
+    // the transposing reads: lane 2b + h of lane group g reads columns 8h.. of K row k0(g) + b
+    // (+ 8, 16, 24 rows for reads 1-3; FB = 4: + 8, 64, 72), chunk (s0 + i) ^ key
+    auto rx_base = [&](int off, int w, int fb) -> uint32_t {
+      const int l = lane & 15, k0 = fb == 5 ? 32 * lg : 16 * lg;
+      return (uint32_t)(off + (k0 + (l >> 1)) * w + 8 * (l & 1));
+    };
+    auto rx_key16 = [&](int w) -> uint32_t {
+      const int b = (lane & 15) >> 1;
+      return (uint32_t)(16 * (w == 256 ? (b | ((lg & 1) << 3)) : (((b >> 1) & 3) | ((lg & 1) << 2))));
+    };
     if constexpr (AMN) {
       off_a = mn_copy(p.lda, FBA);
       ustep_a = 8 * NW;
       kstep_a = __builtin_amdgcn_readfirstlane(BK * (uint32_t)p.lda);
       a_lo = mn_read(G::A_OFF, wm * TM / 16, FBA, false);
       a_hi = mn_read(G::A_OFF, wm * TM / 16, FBA, true);
+      if constexpr (ARX) {
+        constexpr bool from_u = rx_ubit<BM, FBA>(0) >= 0 || rx_ubit<BM, FBA>(1) >= 0;
+        off_a = rx_copy(p.lda, BM, FBA, from_u ? 0 : -1);
+        off_a1 = from_u ? rx_copy(p.lda, BM, FBA, 1) : off_a;
+        ustep_a = __builtin_amdgcn_readfirstlane(NW * (1024 / BM) * (int)p.lda);
+        a_lo = rx_base(G::A_OFF, BM, FBA);
+        a_hi = rx_key16(BM);
+      }
     }
     if constexpr (BMN) {
       off_b = mn_copy(p.ldb, FBB);
@@ -418,6 +465,14 @@ struct Kernel {
       kstep_b = __builtin_amdgcn_readfirstlane(BK * (uint32_t)p.ldb);
       b_lo = mn_read(G::B_OFF, wn * TN / 16, FBB, false);
       b_hi = mn_read(G::B_OFF, wn * TN / 16, FBB, true);
+      if constexpr (BRX) {
+        constexpr bool from_u = rx_ubit<BN, FBB>(0) >= 0 || rx_ubit<BN, FBB>(1) >= 0;
+        off_b = rx_copy(p.ldb, BN, FBB, from_u ? 0 : -1);
+        off_b1 = from_u ? rx_copy(p.ldb, BN, FBB, 1) : off_b;
+        ustep_b = __builtin_amdgcn_readfirstlane(NW * (1024 / BN) * (int)p.ldb);
+        b_lo = rx_base(G::B_OFF, BN, FBB);
+        b_hi = rx_key16(BN);
+      }
     }
     wshift = 8 * lg;
     sa_lds = G::SA_OFF + 4 * (wm * TM + lr);
@@ -484,11 +539,12 @@ struct Kernel {
   // scales for the one right after (when the operand carries them), empty otherwise.  Which
   // case applies is fixed at compile time except for the one part that straddles them.
   template <int U, int ROWL, bool SCALES>
-  __device__ __forceinline__ void copy_part(const Src& s, int dst, int sdst, uint32_t off, int ustep) const {
+  __device__ __forceinline__ void copy_part(const Src& s, int dst, int sdst, uint32_t off, int ustep,
+                                            uint32_t off1 = 0, bool use1 = false) const {
     constexpr int Q0 = U * NW;
     const int q = wave + Q0;
     const int row_dst = dst + q * 1024;
-    const uint32_t row_off = off + (uint32_t)U * (uint32_t)ustep;
+    const uint32_t row_off = (use1 ? off1 : off) + (uint32_t)U * (uint32_t)ustep;
     if constexpr (Q0 + NW <= ROWL) {
       copy_to_lds(src_ptr(s.lo, s.hi), s.bytes, row_off, smem, row_dst);
     } else if constexpr (Q0 >= ROWL) {
@@ -506,12 +562,15 @@ struct Kernel {
   }
   template <int U>
   __device__ __forceinline__ void copy_a(const Src& s, int slot) const {
-    copy_part<U, G::A_ROWL, true>(s, G::A_OFF + slot * G::A_SLOT, G::SA_OFF + slot * G::SA_SLOT, off_a, ustep_a);
+    constexpr bool use1 = ARX && rx_ubit<BM, FBA>(U) == 1;
+    copy_part<U, G::A_ROWL, true>(s, G::A_OFF + slot * G::A_SLOT, G::SA_OFF + slot * G::SA_SLOT, off_a, ustep_a,
+                                  off_a1, use1);
   }
   template <int U>
   __device__ __forceinline__ void copy_b(const Src& s, int slot) const {
+    constexpr bool use1 = BRX && rx_ubit<BN, FBB>(U) == 1;
     copy_part<U, G::B_ROWL, SFM != SF_1D2D_F32>(s, G::B_OFF + slot * G::B_SLOT, G::SB_OFF + slot * G::SB_SLOT,
-                                                 off_b, ustep_b);
+                                                 off_b, ustep_b, off_b1, use1);
   }
   template <int... Us>
   __device__ __forceinline__ void copy_a_all(const Src& s, int slot, std::integer_sequence<int, Us...>) const {
@@ -543,9 +602,20 @@ struct Kernel {
     const v2i x2 = read_tr8(smem, lo + off + D2), x3 = read_tr8(smem, hi + off + D2);
     return (v8i){x0.x, x0.y, x1.x, x1.y, x2.x, x2.y, x3.x, x3.y};
   }
+  // row-XOR stage W bytes wide: the fragment of chunk c (16 columns) is four transposing reads
+  // at base + ((16 c) ^ key16), 8 K rows apart (FB = 5) or 8 and 64 apart (FB = 4)
+  template <int FB, int W>
+  __device__ __forceinline__ v8i frag_rx(uint32_t base, uint32_t key16, uint32_t c16) const {
+    const uint32_t a = base + (c16 ^ key16);
+    constexpr int R1 = 8 * W, R2 = (FB == 5 ? 16 : 64) * W, R3 = (FB == 5 ? 24 : 72) * W;
+    const v2i x0 = read_tr8(smem, a), x1 = read_tr8(smem, a + R1);
+    const v2i x2 = read_tr8(smem, a + R2), x3 = read_tr8(smem, a + R3);
+    return (v8i){x0.x, x0.y, x1.x, x1.y, x2.x, x2.y, x3.x, x3.y};
+  }
   __device__ __forceinline__ v8i a_frag(int aslot, int i) const {
     const uint32_t so = (uint32_t)(aslot * G::A_SLOT);
     // (a 16-row fragment is 16 rows x 128 bytes, an MN-major strip 128 rows x 16 bytes)
+    if constexpr (ARX) return frag_rx<FBA, BM>(a_lo + so, a_hi, (uint32_t)(wm * TM + 16 * i));
     if constexpr (AMN) return frag_tr<FBA>(a_lo + so, a_hi + so, i * 2048);
     return frag(a_lo + so, a_hi + so, i * 16 * BK);
   }
@@ -556,6 +626,7 @@ struct Kernel {
       const v4i x = *(const v4i*)(smem + b_lo + so + j * 16 * G::BKB);
       return (v8i){x.x, x.y, x.z, x.w, 0, 0, 0, 0};
     }
+    if constexpr (BRX) return frag_rx<FBB, BN>(b_lo + so, b_hi, (uint32_t)(wn * TN + 16 * j));
     if constexpr (BMN) return frag_tr<FBB>(b_lo + so, b_hi + so, j * 2048);
     return frag(b_lo + so, b_hi + so, j * 16 * BK);
   }
