@@ -84,8 +84,16 @@ def kernel_source_hash(sources=GEMM_SOURCES):
 
 
 def sources_for(workload):
-    """The kernel sources whose traffic a workload measures: the cast kernel's or the GEMMs'."""
-    return CAST_SOURCES if workload.startswith("cast") else GEMM_SOURCES
+    """The kernel sources whose traffic a workload measures: the file of its dominant kernel
+    (the cast, the decode kernel, the generic kernel for the K-grouped GEMM, the pipelined
+    kernel for every other GEMM) and the shared header."""
+    if workload.startswith("cast"):
+        return CAST_SOURCES
+    if workload.startswith("dense_64x"):
+        return ("dg_gemm_skinny.hip", "dg_internal.h")
+    if workload.startswith("k_grouped"):
+        return ("dg_gemm.hip", "dg_internal.h")
+    return ("dg_gemm_pipe.hip", "dg_internal.h")
 
 
 def read_traffic(workload):

@@ -65,7 +65,20 @@ def source_hash(workload):
     return kernel_source_hash(sources_for(workload))
 
 
-def update_traffic_file(workload, res):
+def run_source_hash(workload, outdir, no_run):
+    """The kernel-source hash of the run whose output is summarised: recorded in --outdir when
+    the passes run, read back from there by --no-run (the sources may have changed since)."""
+    f = os.path.join(outdir, f"{workload}_source_sha1.txt")
+    if no_run and os.path.exists(f):
+        return open(f).read().strip()
+    sha = source_hash(workload)
+    if not no_run:
+        with open(f, "w") as fh:
+            fh.write(sha + "\n")
+    return sha
+
+
+def update_traffic_file(workload, res, sha):
     """Replace the workload's lines in profiles/hbm_traffic.txt (other workloads are kept)."""
     keep = []
     if os.path.exists(TRAFFIC_FILE):
@@ -73,7 +86,7 @@ def update_traffic_file(workload, res):
             t = line.strip()
             if t and not t.startswith("#") and "=" in t and not t.startswith(workload + "."):
                 keep.append(t)
-    keep.append(f"{workload}.source_sha1 = {source_hash(workload)}")
+    keep.append(f"{workload}.source_sha1 = {sha}")
     for k, name in (("FETCH_SIZE", "fetch_kib_per_launch"), ("WRITE_SIZE", "write_kib_per_launch")):
         if k in res:
             keep.append(f"{workload}.{name} = {res[k]:.0f}")
@@ -158,8 +171,9 @@ def main():
     os.makedirs(args.outdir, exist_ok=True)
     kernel = KERNEL[args.workload]
     passes = args.passes.split(",")
+    sha = run_source_hash(args.workload, args.outdir, args.no_run)
     out = [f"# rocprofv3 summary: bench.py --workload {args.workload}, one MI355X ({NUM_CU} CUs)",
-           f"# kernel source sha1 (bench.py's kernel_source_hash for this workload) = {source_hash(args.workload)}",
+           f"# kernel source sha1 (bench.py's kernel_source_hash for this workload) = {sha}",
            f"# made by: python profile_counters.py {args.workload} --passes {args.passes}", ""]
     res = {}
     for name in passes:
@@ -235,7 +249,7 @@ def main():
             f.write("\n".join(out) + "\n")
         print(f"[profile] wrote {path}", flush=True)
     if "FETCH_SIZE_bytes" in res and "WRITE_SIZE_bytes" in res:
-        update_traffic_file(args.workload, res)
+        update_traffic_file(args.workload, res, sha)
         print(f"[profile] {args.workload}.bytes_per_launch = {res['bytes_per_launch']:.0f} -> {TRAFFIC_FILE}", flush=True)
 
 
