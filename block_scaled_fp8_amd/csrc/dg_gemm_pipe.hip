@@ -83,9 +83,14 @@ struct Geo {
 };
 
 // LDS slot of 16-byte chunk c of row r (rows counted within an operand stage) is
-// c ^ swz(r).  With this key the fragment reads of gfx950's 64-bank LDS are free of bank
-// conflicts: 16 lanes read rows r..r+15 of one chunk column in the same cycle.
+// c ^ swz(r).  gfx950's LDS has 64 four-byte banks; a 16-byte read (ds_read_b128) is served
+// 16 lanes at a time, and a probe of every lane pair on the box showed which 16: lanes whose
+// index has the same bit 5 and the same parity of bits 2..4 (lanes 0-3, 12-15, 20-23 and 24-27
+// go together).  Those 16 lanes must touch 16 different 16-byte bank groups.  An FP8 fragment
+// read (chunks 2g and 2g + 1 of rows r..r+15 in lane group g) is conflict-free under swz;
+// next to FP4 weights the activation reads chunks g and g + 4, which swz4a keeps apart.
 __device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+__device__ __forceinline__ int swz4a(int r) { return (r & 7) ^ (((r >> 3) & 1) << 1); }
 
 template <class T>
 __device__ __forceinline__ T load_uniform(const T* base, int64_t i) {
@@ -369,14 +374,15 @@ struct Kernel {
     lg = lane >> 4;
     const uint32_t r = (uint32_t)lane >> 3, c = (uint32_t)lane & 7, w = (uint32_t)wave & 1;
     const uint32_t chunk = (c ^ r ^ w) << 4;
-    off_a = (8u * (uint32_t)wave + r) * (uint32_t)p.lda + chunk;
+    // (next to FP4 weights the activation rows use swz4a: (L%8) ^ (L/8) ^ 2 (q&1))
+    off_a = (8u * (uint32_t)wave + r) * (uint32_t)p.lda + (FP4B ? (c ^ r ^ (w << 1)) << 4 : chunk);
     off_s = (uint32_t)lane << 4;
     ustep_a = __builtin_amdgcn_readfirstlane(8 * NW * (int)p.lda);
     if constexpr (FP4B) {
       // 64-byte weight rows: wave-load q fills rows 16q..16q+15; lane L writes row 16q + L/4,
-      // slot L%4, which holds chunk (L%4) ^ swz4(16q + L/4) = (L%4) ^ (L/16)
+      // slot L%4, which holds chunk (L%4) ^ swz4b(16q + L/4) = (L%4) ^ 2 ((L/16) & 1)
       off_b = (16u * (uint32_t)wave + ((uint32_t)lane >> 2)) * (uint32_t)p.ldb +
-              ((((uint32_t)lane & 3u) ^ ((uint32_t)lane >> 4)) << 4);
+              ((((uint32_t)lane & 3u) ^ ((((uint32_t)lane >> 4) & 1u) << 1)) << 4);
       ustep_b = __builtin_amdgcn_readfirstlane(16 * NW * (int)p.ldb);
     } else {
       off_b = (8u * (uint32_t)wave + r) * (uint32_t)p.ldb + chunk;
@@ -384,7 +390,7 @@ struct Kernel {
     }
     sstep_a = __builtin_amdgcn_readfirstlane(4u * (uint32_t)p.sfa_stride);
     sstep_b = __builtin_amdgcn_readfirstlane(4u * (uint32_t)p.sfb_stride);
-    const int sw = swz(lr);
+    const int sw = FP4B ? swz4a(lr) : swz(lr);
     // An FP8 operand of the 16x16x128 MFMA holds, in lane group lg, K [16 lg, +16) in its
     // first four registers and K [64 + 16 lg, +16) in its last four (chunks lg and lg + 4 of a
     // 128-byte row); an FP4 operand holds K [32 lg, +32) (chunk lg of a 64-byte row).  With FP8
@@ -395,9 +401,10 @@ struct Kernel {
     a_lo = G::A_OFF + (wm * TM + lr) * BK + lo;
     a_hi = G::A_OFF + (wm * TM + lr) * BK + hi;
     if constexpr (FP4B) {
-      // rows r..r+15 of chunk lg sit in slots lg ^ swz4(r): with 64-byte rows, rows that share
-      // a bank group (r mod 4) get four different slots, so the reads are conflict-free
-      b_lo = b_hi = G::B_OFF + (wn * TN + lr) * G::BKB + ((lg ^ ((lr >> 2) & 3)) * 16);
+      // rows r..r+15 of chunk lg sit in slots lg ^ swz4b(r), swz4b(r) = 2 ((r >> 2) & 1): of the
+      // 16 lanes served together (see swz), the four that share a bank group (r mod 4) then take
+      // four different slots
+      b_lo = b_hi = G::B_OFF + (wn * TN + lr) * G::BKB + ((lg ^ (((lr >> 2) & 1) << 1)) * 16);
     } else {
       b_lo = G::B_OFF + (wn * TN + lr) * BK + lo;
       b_hi = G::B_OFF + (wn * TN + lr) * BK + hi;
