@@ -236,8 +236,11 @@ struct Src {
   int sbytes;
 };
 
+// (SC = false: an operand without staged scales; only its row fields are kept)
+template <bool SC = true>
 __device__ __forceinline__ void pin_src(Src& s) {
-  asm volatile("" : "+s"(s.lo), "+s"(s.hi), "+s"(s.bytes), "+s"(s.slo), "+s"(s.shi), "+s"(s.sbytes));
+  if constexpr (SC) asm volatile("" : "+s"(s.lo), "+s"(s.hi), "+s"(s.bytes), "+s"(s.slo), "+s"(s.shi), "+s"(s.sbytes));
+  else asm volatile("" : "+s"(s.lo), "+s"(s.hi), "+s"(s.bytes));
 }
 
 // K-major operand (rows of K bytes): the block starts at byte kb * bkb of row r0 and the
@@ -296,7 +299,7 @@ __device__ __forceinline__ Src src_at(const Src& c, const Src& n, int k, int nkb
 // of their block 0.
 struct Bases {
   Src ac, an, bc, bn;
-  int wc0, wc1, wn0, wn1;
+  int wc0, wc1, wn0, wn1;  // (wn0, wn1: minus the current tile's block count)
 };
 
 // State carried from one K block to the next (and across tiles).
@@ -556,7 +559,11 @@ struct Kernel {
       copy_to_lds(src_ptr(s.lo, s.hi), s.bytes, row_off, smem, row_dst);
     } else if constexpr (Q0 >= ROWL) {
       const bool is_s = SCALES && q == ROWL;
-      copy_to_lds(src_ptr(s.slo, s.shi), is_s ? s.sbytes : 0, off_s, smem, is_s ? sdst : (int)G::TRASH_OFF);
+      if constexpr (SCALES) {
+        copy_to_lds(src_ptr(s.slo, s.shi), is_s ? s.sbytes : 0, off_s, smem, is_s ? sdst : (int)G::TRASH_OFF);
+      } else {
+        copy_to_lds(src_ptr(s.lo, s.hi), 0, off_s, smem, (int)G::TRASH_OFF);  // (empty: keeps the copy count)
+      }
     } else {
       const bool is_row = q < ROWL, is_s = SCALES && q == ROWL;
       if (SCALES) {
@@ -704,8 +711,7 @@ struct Kernel {
     // first steps (in the shadow of the MFMAs) and pinned, so the scalar work does not pile
     // up right after the barrier
     Src asrc = {}, bsrc = {};
-    const __attribute__((address_space(4))) float* wp0 = nullptr;  // 1d2d: weight-block scales of block g+1
-    const __attribute__((address_space(4))) float* wp1 = nullptr;
+    uint32_t wo0 = 0, wo1 = 0;  // 1d2d: byte offsets in sfb of the weight-block scales of block g+1
     const int as2 = as >= NA - 2 ? as - (NA - 2) : as + 2;
     const int as1 = as >= NA - 1 ? as - (NA - 1) : as + 1;
     const int bs1 = next_b(bs);
@@ -783,8 +789,9 @@ struct Kernel {
         bfn = b_frag(bs1, 0);
         if (UE) ebwn = weight_word(bs1, 0);
         if (SFM == SF_1D2D_F32) {
-          sbn0 = *wp0;
-          sbn1 = *wp1;
+          const __attribute__((address_space(4))) uint8_t* sfb = (const __attribute__((address_space(4))) uint8_t*)p.sfb;
+          sbn0 = *(const __attribute__((address_space(4))) float*)(sfb + wo0);
+          sbn1 = *(const __attribute__((address_space(4))) float*)(sfb + wo1);
         }
         read_scales(c, as1);
       }
@@ -794,15 +801,13 @@ struct Kernel {
       }
       if constexpr (t == 1) {
         bsrc = src_at<SFM == SF_1D1D_UE8M0>(sb.bc, sb.bn, kb + NB, nkb, sstep_b, kstep_b);
-        pin_src(bsrc);
+        pin_src<SFM != SF_1D2D_F32>(bsrc);
         if (SFM == SF_1D2D_F32) {
+          // (the next tile's indices are stored minus nkb, so both count blocks from this tile's start)
           const bool same = kb + 1 < nkb;
-          const int k1 = same ? kb + 1 : kb + 1 - nkb;
-          const int wi0 = __builtin_amdgcn_readfirstlane((same ? sb.wc0 : sb.wn0) + k1);
-          const int wi1 = __builtin_amdgcn_readfirstlane((same ? sb.wc1 : sb.wn1) + k1);
-          wp0 = (const __attribute__((address_space(4))) float*)p.sfb + wi0;
-          wp1 = (const __attribute__((address_space(4))) float*)p.sfb + wi1;
-          asm volatile("" : "+s"(wp0), "+s"(wp1));
+          wo0 = 4u * (uint32_t)__builtin_amdgcn_readfirstlane((same ? sb.wc0 : sb.wn0) + kb + 1);
+          wo1 = 4u * (uint32_t)__builtin_amdgcn_readfirstlane((same ? sb.wc1 : sb.wn1) + kb + 1);
+          asm volatile("" : "+s"(wo0), "+s"(wo1));
         }
       }
       // after its last use, fragment i of A is replaced by block g+1's
@@ -998,6 +1003,8 @@ struct Kernel {
     if (SFM == SF_1D2D_F32) {
       weight_block_index(cur, 0, sb.wc0, sb.wc1);
       weight_block_index(nxt, 0, sb.wn0, sb.wn1);
+      sb.wn0 -= nkb;
+      sb.wn1 -= nkb;
     }
     auto run = [&]<int NF, int FA>() {
       for (int kb = 0; kb < nkb; ++kb) {
