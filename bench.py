@@ -13,14 +13,15 @@ in the caches.  --workload picks the other workloads (grouped, decode, FP8 x FP4
 K-grouped, the activation cast).
 
 Timing: W untimed warm-up steps, then exactly K timed steps between two device
-synchronisations (wall clock -> "value").  The dominant kernel's launch duration
-comes from HIP events on the stream it is launched on: per launch (mean, median,
-min) when the host keeps ahead of the GPU, or, for kernels shorter than the
-binding's host time per call (decode, cast), from a captured graph of K launches
-replayed between two events (mean launch period, gaps between launches
-included).  After the timed region a sustained run samples the GPU clock and
-socket power with amd-smi, and a device-to-device copy of 1 GiB measures the
-practical HBM ceiling.
+synchronisations and nothing else on the stream (wall clock -> "value"; a timing
+event between two kernels would make the queue drain first).  The dominant
+kernel's launch duration comes from HIP events on the stream it is launched on,
+right after the timed region: 5 runs of K back-to-back launches between two
+events (mean, median and min of the runs' launch periods), or, for kernels
+shorter than the binding's host time per call (decode, cast), a captured graph
+of K launches replayed between two events.  After that a sustained run samples
+the GPU clock and socket power with amd-smi, and a device-to-device copy of
+1 GiB measures the practical HBM ceiling.
 
 Prints one JSON line (see the "roofline" and "cpu_baseline" objects).
 """
@@ -544,20 +545,28 @@ def main():
         def run_some():
             launch_graph.replay()
     else:
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+        # the timed region holds the K steps and nothing else: a timing event between two
+        # kernels makes the queue drain before the next one starts (about 6 us per event on
+        # this GPU), which is instrumentation, not part of the job
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(K):
-            if wl.pre is not None:
-                wl.pre(i)
-            evs[i][0].record(stream)
-            wl.launch(i)
-            evs[i][1].record(stream)
+            wl.step(i)
         torch.cuda.synchronize()
         elapsed = time.perf_counter() - t0
-        ms = [a.elapsed_time(b) for a, b in evs]
-        kern_ms = dict(mean=float(np.mean(ms)), median=float(np.median(ms)), min=float(np.min(ms)),
-                       how=f"HIP events around each of the {K} timed launches")
+        # the dominant kernel's own duration, live: HIP events on its stream around runs of K
+        # back-to-back launches (the same buffer rotation as the steps), 5 runs
+        periods = []
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for i in range(K):
+                wl.launch(i)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            periods.append(e0.elapsed_time(e1) / K)
+        kern_ms = dict(mean=float(np.mean(periods)), median=float(np.median(periods)), min=float(np.min(periods)),
+                       how=f"HIP events around {K} back-to-back launches, 5 runs")
 
         def run_some():
             for i in range(20):
