@@ -492,6 +492,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--settle-ms", type=float, default=200.0,
+                    help="after the warm-up steps, keep running untimed steps for this long so that the "
+                         "timed region starts at the GPU's sustained clock (0: no settling)")
     ap.add_argument("--workload", default=DEFAULT, choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -519,6 +522,16 @@ def main():
     for i in range(W):
         wl.step(i)
     torch.cuda.synchronize()
+    # Under sustained load the board's power control first pulls the shader clock well below
+    # its steady value and settles within some 20 ms (a kernel trace of this benchmark shows
+    # the GEMM at 62 us, then 74-77 us for a few ms, then back to 61-62 us): untimed steps
+    # carry the GPU through that transient before the timed region starts.
+    settled, t_settle = 0, time.perf_counter()
+    while (time.perf_counter() - t_settle) * 1e3 < args.settle_ms:
+        for _ in range(8):
+            wl.step(W + settled)
+            settled += 1
+        torch.cuda.synchronize()
     copy_calibration(args, dev)
 
     if graph_mode:
@@ -622,6 +635,7 @@ def main():
         "cpu_baseline": cpu,
         "gpu": extras,
     }
+    out["gpu"]["settle"] = {"ms": args.settle_ms, "untimed_steps": settled}
     if args.workload == DEFAULT:
         out["pct_fp8_peak"] = round(100.0 * value / PEAK_FP8_TFLOPS, 2)
     print(json.dumps(out), flush=True)

@@ -49,8 +49,8 @@ KERNEL = {
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
 TRAFFIC_HEADER = """# HBM traffic of the timed kernel launch from rocprofv3 counters, one MI355X.
 # Per workload, two runs of one counter each (written by profile_counters.py):
-#   rocprofv3 --pmc FETCH_SIZE -f csv -d <out> -o run -- python3 bench.py --workload <w> --steps 5 --warmup 2 --no-cpu-baseline --no-extras --copy-calibration-mb 512
-#   rocprofv3 --pmc WRITE_SIZE -f csv -d <out> -o run -- python3 bench.py --workload <w> --steps 5 --warmup 2 --no-cpu-baseline --no-extras --copy-calibration-mb 512
+#   rocprofv3 --pmc FETCH_SIZE -f csv -d <out> -o run -- python3 bench.py --workload <w> --steps 5 --warmup 2 --settle-ms 0 --no-cpu-baseline --no-extras --copy-calibration-mb 512
+#   rocprofv3 --pmc WRITE_SIZE -f csv -d <out> -o run -- python3 bench.py --workload <w> --steps 5 --warmup 2 --settle-ms 0 --no-cpu-baseline --no-extras --copy-calibration-mb 512
 # Calibration: the same runs copy 512 MiB device-to-device once (a kernel of known traffic,
 #   512 MiB read and 512 MiB written); its counter reading gives the bytes per counter KiB.
 # Bytes = counter KiB x 1024 x factor.  <w>.source_sha1 ties a workload's figures to the kernel
@@ -102,7 +102,7 @@ def update_traffic_file(workload, res, sha):
 
 def bench_args(workload):
     return ["python3", os.path.join(ROOT, "bench.py"), "--workload", workload, "--steps", "5", "--warmup", "2",
-            "--no-cpu-baseline", "--no-extras", "--copy-calibration-mb", "512"]
+            "--settle-ms", "0", "--no-cpu-baseline", "--no-extras", "--copy-calibration-mb", "512"]
 
 
 def pass_command(name, d, workload):
