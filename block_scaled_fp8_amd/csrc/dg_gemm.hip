@@ -239,8 +239,24 @@ __device__ __forceinline__ void make_loader(const GemmParams& p, const Tile& tl,
 // runtime choice between members can turn into a memory access.)
 struct LaneOffsets {
   uint32_t a_same, a_flip, b_same, b_flip;
+  uint32_t a_rx0, a_rx1, b_rx0, b_rx1;  // row-XOR staging: parts whose key bit is 0 / 1
   uint32_t s;  // scale wave-loads: lane L copies 4-byte entries 4L..4L+3
 };
+
+// An MN-major operand 256 columns wide with 8 waves sits in its stage region row-XOR'd
+// instead: K row r is stored whole at byte 256 r, its 16-byte chunk c at position c ^ key(r),
+// key(r) = (r & 7) | (bit 5 of r) << 3.  Wave-load q fills K rows 4q .. 4q+3 and lane L
+// copies chunk (L % 16) ^ key(r) of row r = 4q + L/16, so consecutive lanes read consecutive
+// bytes of a K row.  With q = wave + 8U, r & 7 = 4 (wave & 1) + L/16 and bit 5 of r is U & 1,
+// so a lane needs one offset per parity of U.  The 16 K rows one transposing read takes in a
+// pass (8 per lane group, the two groups differing in bit 5) land on 16 different 4-bank groups.
+template <int LAY, int W, int NW>
+constexpr bool row_xor = LAY != 0 && W == 256 && NW == 8;
+__device__ __forceinline__ uint32_t rx_lane_offset(int lane, int wave, int64_t ld, uint32_t ubit) {
+  const uint32_t j = (uint32_t)lane >> 4, c = (uint32_t)lane & 15u;
+  const uint32_t key = (4u * ((uint32_t)wave & 1u) + j) | (ubit << 3);
+  return (4u * (uint32_t)wave + j) * (uint32_t)ld + 16u * (c ^ key);
+}
 
 // An operand stored MN-major (K rows of M or N bytes) sits in its stage region as 16-column
 // strips of 128 rows x 16 bytes; K row k is stored at row position k ^ 8 * (bit 5 of k), which
@@ -259,13 +275,18 @@ __device__ __forceinline__ LaneOffsets make_lane_offsets(const GemmParams& p, in
   o.a_flip = r * (uint32_t)p.lda + ((c ^ r ^ w ^ 1u) << 4);
   o.b_same = r * (uint32_t)p.ldb + ((c ^ r ^ w) << 4);
   o.b_flip = r * (uint32_t)p.ldb + ((c ^ r ^ w ^ 1u) << 4);
+  o.a_rx0 = o.a_rx1 = o.b_rx0 = o.b_rx1 = 0;
   if (LAY & LAYOUT_A_MN) {
     o.a_same = mn_lane_row(lane, w) * (uint32_t)p.lda;
     o.a_flip = mn_lane_row(lane, w ^ 1u) * (uint32_t)p.lda;
+    o.a_rx0 = rx_lane_offset(lane, wave, p.lda, 0u);
+    o.a_rx1 = rx_lane_offset(lane, wave, p.lda, 1u);
   }
   if (LAY & LAYOUT_B_MN) {
     o.b_same = mn_lane_row(lane, w) * (uint32_t)p.ldb;
     o.b_flip = mn_lane_row(lane, w ^ 1u) * (uint32_t)p.ldb;
+    o.b_rx0 = rx_lane_offset(lane, wave, p.ldb, 0u);
+    o.b_rx1 = rx_lane_offset(lane, wave, p.ldb, 1u);
   }
   o.s = (uint32_t)lane << 4;
   return o;
@@ -306,14 +327,19 @@ __device__ __forceinline__ void issue_part(const GemmParams& p, const Loader<BM,
     const int rem = ld.a_rows - 8 * q;
     base = ld.a_tile + (int64_t)(8 * q) * p.lda + kb * BK;
     bytes = rem > 0 ? min(rem, 8) * (int)p.lda - kb * BK : 0;
-    if constexpr ((LAY & LAYOUT_A_MN) != 0) {
+    voff = FLIP ? lo.a_flip : lo.a_same;
+    if constexpr ((LAY & LAYOUT_A_MN) != 0 && row_xor<LAY & LAYOUT_A_MN, BM, S::NW>) {
+      // K rows kb*128 + 4q .. of all BM columns; the range runs to the operand's end as for strips
+      base = ld.a_tile + (int64_t)kb * BK * p.lda;
+      bytes = (int)((((int64_t)(ld.a_krows - kb * BK - 1)) * p.lda + ld.a_rows + 15) & ~(int64_t)15);
+      voff = ((U & 1) ? lo.a_rx1 : lo.a_rx0) + (uint32_t)(32 * U) * (uint32_t)p.lda;
+    } else if constexpr ((LAY & LAYOUT_A_MN) != 0) {
       // strip q/2: K rows kb*128.. of columns 16 (q/2).. ; the range ends with the 16-byte
       // granule holding the operand's last byte (columns past the end only feed outputs that
       // are never stored; a range ending inside a copy would drop its valid dwords)
       base = ld.a_tile + (int64_t)kb * BK * p.lda + 16 * (q >> 1);
       bytes = (int)((((int64_t)(ld.a_krows - kb * BK - 1)) * p.lda + ld.a_rows - 16 * (q >> 1) + 15) & ~(int64_t)15);
     }
-    voff = FLIP ? lo.a_flip : lo.a_same;
     dst = s * S::STAGE_BYTES + q * 1024;
   } else {
     // B rows 8q - BM .. 8q - BM + 7 of the tile
@@ -321,12 +347,17 @@ __device__ __forceinline__ void issue_part(const GemmParams& p, const Loader<BM,
     const int rem = ld.b_rows - r0;
     const uint8_t* b_base = ld.b_tile + (int64_t)r0 * p.ldb + kb * BK;
     int b_bytes = rem > 0 ? min(rem, 8) * (int)p.ldb - kb * BK : 0;
-    if constexpr ((LAY & LAYOUT_B_MN) != 0) {
+    uint32_t b_voff = FLIP ? lo.b_flip : lo.b_same;
+    if constexpr ((LAY & LAYOUT_B_MN) != 0 && row_xor<LAY & LAYOUT_B_MN, BN, S::NW>) {
+      constexpr int UB = U - UA;  // B row loads q - BM/8 = wave + 8 UB
+      b_base = ld.b_tile + (int64_t)kb * BK * p.ldb;
+      b_bytes = (int)((((int64_t)(ld.b_krows - kb * BK - 1)) * p.ldb + ld.b_rows + 15) & ~(int64_t)15);
+      b_voff = ((UB & 1) ? lo.b_rx1 : lo.b_rx0) + (uint32_t)(32 * UB) * (uint32_t)p.ldb;
+    } else if constexpr ((LAY & LAYOUT_B_MN) != 0) {
       const int st = (q - BM / 8) >> 1;  // (BM / 8 is even: the parity of q is the strip half)
       b_base = ld.b_tile + (int64_t)kb * BK * p.ldb + 16 * st;
       b_bytes = (int)((((int64_t)(ld.b_krows - kb * BK - 1)) * p.ldb + ld.b_rows - 16 * st + 15) & ~(int64_t)15);
     }
-    const uint32_t b_voff = FLIP ? lo.b_flip : lo.b_same;
     if constexpr (ALL_B) {
       base = b_base;
       bytes = b_bytes;
@@ -423,6 +454,12 @@ __device__ __forceinline__ int gemm_tile(const GemmParams& p, uint8_t* smem, con
   const int l16 = lane & 15, flip = lg & 1;
   const uint32_t mn_lo = (uint32_t)(16 * (32 * lg + 8 * flip + (l16 >> 1)) + 8 * (l16 & 1));
   const uint32_t mn_hi = (uint32_t)(16 * (32 * lg + 8 * (flip ^ 1) + (l16 >> 1)) + 8 * (l16 & 1));
+  // row-XOR regions: lane 2b + h of lane group lg reads 8 bytes (columns 8h..) of K rows
+  // 32 lg + b + {0, 8, 16, 24}, whose XOR key is the same: b | (lg & 1) << 3
+  const uint32_t rx_lo = (uint32_t)((32 * lg + (l16 >> 1)) * 256 + 8 * (l16 & 1));
+  const uint32_t rx_key = (uint32_t)(16 * ((l16 >> 1) | ((lg & 1) << 3)));
+  constexpr bool RXA = (LAY & LAYOUT_A_MN) != 0 && row_xor<LAY & LAYOUT_A_MN, BM, S::NW>;
+  constexpr bool RXB = (LAY & LAYOUT_B_MN) != 0 && row_xor<LAY & LAYOUT_B_MN, BN, S::NW>;
 
   // One K block.  SPREAD: the copy of K block kb+1 of this tile into the other stage goes
   // out spread evenly over the block's MFMAs (the memory pipe is the scarcest unit).
@@ -459,16 +496,26 @@ __device__ __forceinline__ int gemm_tile(const GemmParams& p, uint8_t* smem, con
       const v2i x2 = read_tr8(smem, a0 + 256), x3 = read_tr8(smem, a1 + 256);
       return (v8i){x0.x, x0.y, x1.x, x1.y, x2.x, x2.y, x3.x, x3.y};
     };
+    // row-XOR region at byte `region`: fragment of the 16 columns starting at byte c16 of the
+    // rows, four transposing reads 8 K rows apart
+    auto read_frag_rx = [&](int region, int c16) -> v8i {
+      const uint32_t a = (uint32_t)(s * S::STAGE_BYTES + region) + rx_lo + ((uint32_t)c16 ^ rx_key);
+      const v2i x0 = read_tr8(smem, a), x1 = read_tr8(smem, a + 2048);
+      const v2i x2 = read_tr8(smem, a + 4096), x3 = read_tr8(smem, a + 6144);
+      return (v8i){x0.x, x0.y, x1.x, x1.y, x2.x, x2.y, x3.x, x3.y};
+    };
     // fragments needed by the first MFMA first, so it waits for as few reads as possible
     // (the K-major reads are written out at each use: routing them through a helper that also
     // holds the MN-major form costs the K-grouped kernel about 45 registers)
     v8i af[FM];
     v8i bf;
-    if constexpr ((LAY & LAYOUT_B_MN) != 0) bf = read_frag_mn(BM * BK, (wn * TN) / 16);
+    if constexpr (RXB) bf = read_frag_rx(BM * BK, wn * TN);
+    else if constexpr ((LAY & LAYOUT_B_MN) != 0) bf = read_frag_mn(BM * BK, (wn * TN) / 16);
     else bf = read_frag(BM + wn * TN + lr);
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
-      if constexpr ((LAY & LAYOUT_A_MN) != 0) af[i] = read_frag_mn(0, (wm * TM) / 16 + i);
+      if constexpr (RXA) af[i] = read_frag_rx(0, wm * TM + 16 * i);
+      else if constexpr ((LAY & LAYOUT_A_MN) != 0) af[i] = read_frag_mn(0, (wm * TM) / 16 + i);
       else af[i] = read_frag(wm * TM + 16 * i + lr);
     }
 
@@ -529,7 +576,8 @@ __device__ __forceinline__ int gemm_tile(const GemmParams& p, uint8_t* smem, con
       v8i bf_next = bf;
       int eb_next = eb;
       if (j + 1 < FN) {
-        if constexpr ((LAY & LAYOUT_B_MN) != 0) bf_next = read_frag_mn(BM * BK, (wn * TN) / 16 + j + 1);
+        if constexpr (RXB) bf_next = read_frag_rx(BM * BK, wn * TN + 16 * (j + 1));
+        else if constexpr ((LAY & LAYOUT_B_MN) != 0) bf_next = read_frag_mn(BM * BK, (wn * TN) / 16 + j + 1);
         else bf_next = read_frag(BM + wn * TN + 16 * (j + 1) + lr);
         if (SFM == SF_1D1D_UE8M0) eb_next = weight_code(j + 1);
       }
@@ -732,7 +780,8 @@ static hipError_t launch_tile(const GemmParams& p, int sfm, int grp, int out, in
   DG_CASE(SF_1D1D_UE8M0, GRP_MASKED, OUT_F32)
   if constexpr (BN >= 224) {
     // K-grouped: NT, or both operands stored K-outermost (TN, the weight-gradient storage; on the
-    // 224-wide tiles, where its registers fit without spilling)
+    // 224-wide tiles, where its registers fit without spilling: on 256x256 the transposing
+    // reads of both operands spill)
     if (sfm == SF_1D1D_F32 && grp == GRP_KGROUP && out == OUT_F32_C) {
       if constexpr (BN == 224) {
         if (p.layout == (LAYOUT_A_MN | LAYOUT_B_MN))

@@ -210,20 +210,26 @@ def _k_grouped_operands(p, layout, pad=16):
     return stored_t(p["a"], pad), stored_t(p["b"], pad)
 
 
-@pytest.mark.parametrize("m,n,ks", [(260, 196, [256, 0, 384, 128, 512]), (64, 520, [128]), (4, 4, [0, 128, 0]),
-                                    (516, 388, [1024, 128, 0, 640])])
-def test_k_grouped_tn_equals_nt_bitwise_and_oracle(m, n, ks):
+@pytest.mark.parametrize("m,n,ks,tile", [(260, 196, [256, 0, 384, 128, 512], None), (64, 520, [128], None),
+                                         (4, 4, [0, 128, 0], None), (516, 388, [1024, 128, 0, 640], None),
+                                         (516, 388, [1024, 128, 0, 640], "256x224"),
+                                         (300, 452, [384, 256, 0, 128], "256x224"),
+                                         (300, 452, [384, 256, 0, 128], "128x224")])
+def test_k_grouped_tn_equals_nt_bitwise_and_oracle(m, n, ks, tile):
     """K-grouped GEMM with both operands stored K-outermost ([sum K, m] and [sum K, n], the
-    token-major storage of the weight-gradient operands): the NT result bit for bit on the same
-    tile, and the oracle read through the storage; empty groups give C, C accumulated in place."""
+    token-major storage of the weight-gradient operands): the NT result bit for bit, and the
+    oracle read through the storage; empty groups give C, C accumulated in place.  Forced to the
+    256-row tile (A staged row-XOR, B in strips) and to the 128-row one (both in strips) on
+    ragged shapes."""
     p = gen.k_grouped(m, n, ks, seed=m + n + 3 * len(ks))
     sfa, sfb = cuda(np.ascontiguousarray(p["sa"].T)), cuda(np.ascontiguousarray(p["sb"].T))
     outs = {}
     for layout in ("nt", "tn"):
-        say("k-grouped", layout, m, n, ks)
+        say("k-grouped", layout, m, n, ks, tile)
         a, b = _k_grouped_operands(p, layout)
         d = cuda(p["c"]).clone()
-        getattr(dg, f"k_grouped_fp8_gemm_{layout}_contiguous")((a, sfa), (b, sfb), d, ks, d)
+        with force_tile(tile if layout == "tn" else None):
+            getattr(dg, f"k_grouped_fp8_gemm_{layout}_contiguous")((a, sfa), (b, sfb), d, ks, d)
         torch.cuda.synchronize()
         outs[layout] = d.cpu()
     assert torch.equal(outs["nt"].view(torch.int32), outs["tn"].view(torch.int32))
@@ -235,6 +241,27 @@ def test_k_grouped_tn_equals_nt_bitwise_and_oracle(m, n, ks):
     for g, k in enumerate(ks):
         if k == 0:
             assert np.array_equal(outs["tn"].numpy()[g], p["c"][g])
+
+
+def test_k_grouped_tn_full_size_equals_nt():
+    """The K-grouped weight-gradient workload at the size the benchmark times (m = 7168,
+    n = 2048, eight groups, K = 16384 in all), with token-major operands on the tile the planner
+    picks: the whole output bit for bit equal to the NT form's (whose full-size result is
+    checked against the oracle on sampled outputs), C accumulated in place."""
+    ks = [1792, 2304, 2048, 1536, 2560, 2048, 1920, 2176]
+    m, n = 7168, 2048
+    p = gen.k_grouped(m, n, ks, seed=9)
+    sfa, sfb = cuda(np.ascontiguousarray(p["sa"].T)), cuda(np.ascontiguousarray(p["sb"].T))
+    outs = {}
+    for layout in ("nt", "tn"):
+        say("k-grouped full size", layout)
+        a, b = _k_grouped_operands(p, layout, pad=0)
+        d = cuda(p["c"])
+        getattr(dg, f"k_grouped_fp8_gemm_{layout}_contiguous")((a, sfa), (b, sfb), d, ks, d)
+        torch.cuda.synchronize()
+        outs[layout] = d
+        del a, b
+    assert torch.equal(outs["nt"].view(torch.int32), outs["tn"].view(torch.int32))
 
 
 def test_k_grouped_tn_more_than_64_groups():
