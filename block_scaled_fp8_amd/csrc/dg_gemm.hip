@@ -499,7 +499,11 @@ __device__ __forceinline__ int gemm_tile(const GemmParams& p, uint8_t* smem, con
     // row-XOR region at byte `region`: fragment of the 16 columns starting at byte c16 of the
     // rows, four transposing reads 8 K rows apart
     auto read_frag_rx = [&](int region, int c16) -> v8i {
-      const uint32_t a = (uint32_t)(s * S::STAGE_BYTES + region) + rx_lo + ((uint32_t)c16 ^ rx_key);
+      // (the key is re-read at each use, so the compiler computes each fragment's address where
+      // it is needed instead of keeping one register per fragment live through the loop)
+      uint32_t key = rx_key;
+      asm volatile("" : "+v"(key));
+      const uint32_t a = (uint32_t)(s * S::STAGE_BYTES + region) + rx_lo + ((uint32_t)c16 ^ key);
       const v2i x0 = read_tr8(smem, a), x1 = read_tr8(smem, a + 2048);
       const v2i x2 = read_tr8(smem, a + 4096), x3 = read_tr8(smem, a + 6144);
       return (v8i){x0.x, x0.y, x1.x, x1.y, x2.x, x2.y, x3.x, x3.y};
@@ -780,10 +784,9 @@ static hipError_t launch_tile(const GemmParams& p, int sfm, int grp, int out, in
   DG_CASE(SF_1D1D_UE8M0, GRP_MASKED, OUT_F32)
   if constexpr (BN >= 224) {
     // K-grouped: NT, or both operands stored K-outermost (TN, the weight-gradient storage; on the
-    // 224-wide tiles, where its registers fit without spilling: on 256x256 the transposing
-    // reads of both operands spill)
+    // 224-wide tiles, and on 256x256, where both operands are row-XOR staged)
     if (sfm == SF_1D1D_F32 && grp == GRP_KGROUP && out == OUT_F32_C) {
-      if constexpr (BN == 224) {
+      if constexpr (BN == 224 || (BM == 256 && BN == 256)) {
         if (p.layout == (LAYOUT_A_MN | LAYOUT_B_MN))
           return launch_one<BM, BN, WM, WN, SF_1D1D_F32, GRP_KGROUP, OUT_F32_C, LAYOUT_A_MN | LAYOUT_B_MN>(p, grid, s);
       }
@@ -835,7 +838,9 @@ bool gemm_instantiated(int tile, int sfm, int grp, int out, int layout) {
   if (tile < 0 || tile >= kNumTiles) return false;
   if (sfm < 0 || sfm > 2 || out < 0 || out > 2) return false;
   if (grp == GRP_KGROUP) {
-    if (layout == (LAYOUT_A_MN | LAYOUT_B_MN)) return sfm == SF_1D1D_F32 && out == OUT_F32_C && kTiles[tile].bn == 224;
+    if (layout == (LAYOUT_A_MN | LAYOUT_B_MN))
+      return sfm == SF_1D1D_F32 && out == OUT_F32_C &&
+             (kTiles[tile].bn == 224 || (kTiles[tile].bm == 256 && kTiles[tile].bn == 256));
     return layout == 0 && sfm == SF_1D1D_F32 && out == OUT_F32_C && kTiles[tile].bn >= 224;
   }
   if (layout != 0) return false;

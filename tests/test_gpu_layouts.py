@@ -213,14 +213,16 @@ def _k_grouped_operands(p, layout, pad=16):
 @pytest.mark.parametrize("m,n,ks,tile", [(260, 196, [256, 0, 384, 128, 512], None), (64, 520, [128], None),
                                          (4, 4, [0, 128, 0], None), (516, 388, [1024, 128, 0, 640], None),
                                          (516, 388, [1024, 128, 0, 640], "256x224"),
+                                         (516, 388, [1024, 128, 0, 640], "256x256"),
                                          (300, 452, [384, 256, 0, 128], "256x224"),
+                                         (300, 452, [384, 256, 0, 128], "256x256"),
                                          (300, 452, [384, 256, 0, 128], "128x224")])
 def test_k_grouped_tn_equals_nt_bitwise_and_oracle(m, n, ks, tile):
     """K-grouped GEMM with both operands stored K-outermost ([sum K, m] and [sum K, n], the
     token-major storage of the weight-gradient operands): the NT result bit for bit, and the
-    oracle read through the storage; empty groups give C, C accumulated in place.  Forced to the
-    256-row tile (A staged row-XOR, B in strips) and to the 128-row one (both in strips) on
-    ragged shapes."""
+    oracle read through the storage; empty groups give C, C accumulated in place.  Forced on
+    ragged shapes to 256x256 (both operands staged row-XOR), 256x224 (A row-XOR, B in strips)
+    and 128x224 (both in strips)."""
     p = gen.k_grouped(m, n, ks, seed=m + n + 3 * len(ks))
     sfa, sfb = cuda(np.ascontiguousarray(p["sa"].T)), cuda(np.ascontiguousarray(p["sb"].T))
     outs = {}
