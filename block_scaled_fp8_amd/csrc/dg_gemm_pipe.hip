@@ -876,8 +876,16 @@ struct Kernel {
   // of scratch (the A stage of the tile's last K block, which no wave reads any more), reads
   // it back row-major, 16 bytes per lane, and stores it with consecutive lanes on
   // consecutive addresses.
-  static constexpr int RS = 2 * TN + 16;       // scratch row stride in bytes (spreads rows over banks)
+  // Scratch row r holds 16-byte chunk c at position c ^ ekey(r), ekey(r) = (r mod 16) * PX / 16
+  // with PX the largest power of two (at most 16) that divides the chunk count, so the XOR
+  // stays inside the row.  The 8-byte writes (16 consecutive lanes, rows 0..15 of one chunk,
+  // served together) then spread over the banks, and the read-back gives each group of 16
+  // lanes that LDS serves together (same bit 5, same parity of bits 2..4) 16 consecutive
+  // chunks of the fragment row: both conflict-free on the 64 banks.
+  static constexpr int RS = 2 * TN;            // scratch row stride in bytes
   static constexpr int CH = TN / 8;            // 16-byte chunks per scratch row
+  static constexpr int PX = CH % 16 == 0 ? 16 : CH % 8 == 0 ? 8 : CH % 4 == 0 ? 4 : CH % 2 == 0 ? 2 : 1;
+  static __device__ __forceinline__ int ekey(int r) { return ((r & 15) * PX) >> 4; }
   static constexpr int SCR = G::A_SLOT / NW;   // scratch bytes per wave
   static constexpr bool TRANSPOSE = OUT == OUT_BF16 && 16 * RS <= SCR && TN % 8 == 0;
   static constexpr int RD = (16 * CH + 63) / 64;  // read-back rounds per fragment row
@@ -897,6 +905,11 @@ struct Kernel {
     if (TRANSPOSE && tr.n0 + BN <= p.n && p.d_vec16 && (GRP == GRP_MASKED || interior)) {
       const uint32_t scr = G::A_OFF + aslot * G::A_SLOT + wave * SCR;
       uint8_t* drow0 = (uint8_t*)Dg + ((int64_t)(tr.m0 + wm * TM) * p.ldd + tr.n0 + wn * TN) * 2;
+      // the lane's chunk in each 64-chunk round of the read-back: lane group b = ln / 4 is served
+      // with the groups of the same bit 3 and parity of bits 0..2, and takes 4 of their 16
+      // consecutive chunks
+      const int lb = ln >> 2;
+      const int lpos = 16 * (2 * (lb >> 3) + (__builtin_popcount(lb & 7) & 1)) + 4 * ((lb & 7) >> 1) + (ln & 3);
       // rows of this wave's part that exist (all of them for interior tiles)
       const int rows = interior ? TM : tr.mv - tr.m0 - wm * TM;
       auto store_rows = [&]<bool ALL>() {
@@ -905,14 +918,14 @@ struct Kernel {
 #pragma unroll
           for (int j = 0; j < FN; ++j) {
             const v2u w = {pack_bf16x2(fin[i][j][0], fin[i][j][1]), pack_bf16x2(fin[i][j][2], fin[i][j][3])};
-            *(v2u*)(smem + scr + lr * RS + (16 * j + 4 * lg) * 2) = w;
+            *(v2u*)(smem + scr + lr * RS + 16 * ((2 * j + (lg >> 1)) ^ ekey(lr)) + 8 * (lg & 1)) = w;
           }
 #pragma unroll
           for (int k = 0; k < RD; ++k) {
-            const int cidx = ln + 64 * k;
+            const int cidx = lpos + 64 * k;
             const int r = cidx / CH, cc = cidx - r * CH;
             if (cidx < 16 * CH && (ALL || 16 * i + r < rows)) {
-              const v4i x = *(const v4i*)(smem + scr + r * RS + cc * 16);
+              const v4i x = *(const v4i*)(smem + scr + r * RS + 16 * (cc ^ ekey(r)));
               *(v4i*)(drow0 + ((int64_t)(16 * i + r) * p.ldd + 8 * cc) * 2) = x;
             }
           }
