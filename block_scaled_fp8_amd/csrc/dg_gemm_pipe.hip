@@ -1214,7 +1214,7 @@ hipError_t launch_pipe_dense(const GemmParams& p, int bm, int bn, int sfm, int o
 #elif DG_PIPE_PART == 1
 hipError_t launch_pipe_contig(const GemmParams& p, int bm, int bn, int sfm, int out, int grid, hipStream_t s) {
   if (bm == 128 && bn == 224) return pipe::launch_contig<128, 224, 2, 2>(p, sfm, out, grid, s);
-  if (bm == 128 && bn == 256) return pipe::launch_contig<128, 256, 4, 2>(p, sfm, out, grid, s);
+  if (bm == 128 && bn == 256) return pipe::launch_contig<128, 256, 2, 4>(p, sfm, out, grid, s);
   return hipErrorInvalidValue;
 }
 #elif DG_PIPE_PART == 2
