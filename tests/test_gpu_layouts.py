@@ -204,6 +204,37 @@ def test_fp8_fp4_tt_equals_nt_bitwise_and_oracle(tile, shape):
         assert ok.all(), st
 
 
+@pytest.mark.parametrize("layout,tile", [("nt", "256x224"), ("nt", "128x192"), ("tt", "256x224"), ("nn", "256x224"),
+                                         ("tn", "128x192")])
+def test_largest_leading_dimension(layout, tile):
+    """Operands at the largest leading dimension the boundary accepts, every other byte of their
+    buffers a NaN code: a K-major operand with ld = 2^23 - 16 bytes (the byte range of a
+    256-row tile is then 2^31 - 4096, the most a signed 32-bit range holds) and an MN-major one
+    with k * ld just below 2^31 (k = 256).  Checked element by element against the oracle."""
+    M, N, K = 256, 224, 256
+    LD = (1 << 23) - 16
+    p = gen.dense(M, N, K, seed=23)
+
+    def place(x, mn_major):
+        src = cuda(np.ascontiguousarray(x.T) if mn_major else x)
+        buf = torch.full((src.shape[0], LD), NAN_CODE, dtype=torch.uint8, device=DEV)
+        buf[:, :src.shape[1]] = src
+        return buf[:, :src.shape[1]]
+
+    say("largest ld", layout, tile, LD)
+    a = place(p["a"], layout[0] == "t")
+    b = place(p["b"], layout[1] == "n")
+    d = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=DEV)
+    with force_tile(tile):
+        getattr(dg, "fp8_gemm_" + layout)((a, cuda(p["sa"])), (b, cuda(p["sb"])), d)
+    torch.cuda.synchronize()
+    del a, b
+    o, T = oracle.gemm_nt(p["a"], p["sa"], p["b"], p["sb"], 128, want_abs=True)
+    ok, st = check_bf16(bf16_bits(d), o, T)
+    say("largest ld", layout, tile, st)
+    assert ok.all(), st
+
+
 def _k_grouped_operands(p, layout, pad=16):
     if layout == "nt":
         return cuda(p["a"]), cuda(p["b"])
