@@ -414,22 +414,30 @@ struct Kernel {
     }
     kstep_a = BK;
     kstep_b = G::BKB;
-    // MN-major operands.  A K block of a tile W columns wide sits in LDS as W/16 strips of
-    // 16 columns, each strip 128 rows of 16 bytes; K row k is stored at row position
-    // k ^ (bit FB of k) * 8.  The fragment reads of one 16-lane group take 8 K rows of one strip
-    // (128 contiguous bytes), and the two groups served together take rows whose bit FB
-    // differs, so the permutation puts them on the other half of the banks.  FB is 5 when a
-    // lane group holds K [32 lg, +32) (FP8 next to FP8) and 4 when it holds K [16 lg, +16) and
-    // K [64 + 16 lg, +16) (next to FP4 weights).  Wave-load q (1 KiB) fills strip q/2, row
-    // positions 64 (q % 2) + [0, 64): lane L copies 16 bytes of K row (64 (q % 2) + L) permuted.
+    // MN-major operands.  A K block of a tile W columns wide sits in LDS as W/32 strips of
+    // 32 columns, strip s at byte 4096 s, each strip 128 K rows of 32 bytes; the 16-column
+    // half h of K row k is stored at 32 k + 16 (h ^ bit FB of k).  The fragment reads of one
+    // 16-lane group take 8 K rows of one half-strip, and the two groups served together take
+    // rows whose bit FB differs, so the swap puts them on the other half of the banks.  FB is 5
+    // when a lane group holds K [32 lg, +32) (FP8 next to FP8) and 4 when it holds K [16 lg, +16)
+    // and K [64 + 16 lg, +16) (next to FP4 weights).  Wave-load q (1 KiB) fills strip q/4, K rows
+    // 32 (q % 4) + [0, 32): lane L copies 16 bytes of K row 32 (q % 4) + L/2, so lane pairs read
+    // whole 32-byte row segments.  (q % 4 = wave % 4, and part U adds 8 NW bytes of columns.)
     auto mn_copy = [&](int64_t ld, int fb) -> uint32_t {
-      const uint32_t row = 64u * ((uint32_t)wave & 1u) + ((uint32_t)lane ^ ((((uint32_t)lane >> fb) & 1u) << 3));
-      return row * (uint32_t)ld + 16u * ((uint32_t)wave >> 1);
+      const uint32_t L = (uint32_t)lane, w = (uint32_t)wave;
+      const uint32_t row = 32u * (w & 3u) + (L >> 1);
+      const uint32_t sh = fb == 5 ? ((L & 1u) ^ (w & 1u)) : ((L & 1u) ^ ((L >> 5) & 1u));
+      return row * (uint32_t)ld + 32u * (w >> 2) + 16u * sh;
     };
-    auto mn_read = [&](int off, int strip0, int fb, bool second) -> uint32_t {
-      const int l = lane & 15, flip = (lg & 1) ^ (second ? 1 : 0);
-      const int k0 = fb == 5 ? 32 * lg : 16 * lg;
-      return (uint32_t)(off + strip0 * 2048 + 16 * (k0 + 8 * flip + (l >> 1)) + 8 * (l & 1));
+    // the transposing reads: lane 2b + h of lane group lg reads columns 8h.. of K row k0 + b
+    // (+ 8, 16, 24 rows for reads 1-3; FB = 4: + 8, 64, 72) of one 16-column half; a wave whose
+    // first 16-column chunk is c0 keeps one base for its even and one for its odd fragments
+    auto mn_read = [&](int off, int c0, int fb, bool odd) -> uint32_t {
+      const int l = lane & 15;
+      const int k0 = (fb == 5 ? 32 * lg : 16 * lg) + (l >> 1);
+      const int p0 = c0 & 1;
+      const int strip = (c0 >> 1) + (odd ? p0 : 0), half = odd ? 1 - p0 : p0;
+      return (uint32_t)(off + strip * 4096 + 32 * k0 + 16 * (half ^ (lg & 1)) + 8 * (l & 1));
     };
     // Row-XOR staging (W = 128 or 256 columns): K row r sits at LDS row r, W bytes, its
     // 16-byte chunk s at position s ^ key(r): key = (r & 7) | bit_FB(r) << 3 for W = 256,
@@ -607,13 +615,13 @@ struct Kernel {
     const v4i h4 = *(const v4i*)(smem + hi + off);
     return (v8i){l4.x, l4.y, l4.z, l4.w, h4.x, h4.y, h4.z, h4.w};
   }
-  // MN-major stage: four transposing reads of 8 K each; the second pair lies 16 rows
-  // further (FB = 5) or 64 rows further (FB = 4) than the first
+  // MN-major strip stage: four transposing reads of 8 K each, 8 K rows apart (FB = 5) or 8
+  // and 64 apart (FB = 4), from the lane's base for the fragment's half-strip
   template <int FB>
-  __device__ __forceinline__ v8i frag_tr(uint32_t lo, uint32_t hi, int off) const {
-    constexpr int D2 = FB == 5 ? 16 * 16 : 64 * 16;
-    const v2i x0 = read_tr8(smem, lo + off), x1 = read_tr8(smem, hi + off);
-    const v2i x2 = read_tr8(smem, lo + off + D2), x3 = read_tr8(smem, hi + off + D2);
+  __device__ __forceinline__ v8i frag_tr(uint32_t base, int off) const {
+    constexpr int D2 = FB == 5 ? 16 * 32 : 64 * 32, D3 = D2 + 8 * 32;
+    const v2i x0 = read_tr8(smem, base + off), x1 = read_tr8(smem, base + off + 8 * 32);
+    const v2i x2 = read_tr8(smem, base + off + D2), x3 = read_tr8(smem, base + off + D3);
     return (v8i){x0.x, x0.y, x1.x, x1.y, x2.x, x2.y, x3.x, x3.y};
   }
   // row-XOR stage W bytes wide: the fragment of chunk c (16 columns) is four transposing reads
@@ -628,9 +636,9 @@ struct Kernel {
   }
   __device__ __forceinline__ v8i a_frag(int aslot, int i) const {
     const uint32_t so = (uint32_t)(aslot * G::A_SLOT);
-    // (a 16-row fragment is 16 rows x 128 bytes, an MN-major strip 128 rows x 16 bytes)
+    // (a 16-row fragment is 16 rows x 128 bytes; an MN-major strip holds two fragments)
     if constexpr (ARX) return frag_rx<FBA, BM>(a_lo + so, a_hi, (uint32_t)(wm * TM + 16 * i));
-    if constexpr (AMN) return frag_tr<FBA>(a_lo + so, a_hi + so, i * 2048);
+    if constexpr (AMN) return frag_tr<FBA>(((i & 1) ? a_hi : a_lo) + so, 4096 * (i >> 1));
     return frag(a_lo + so, a_hi + so, i * 16 * BK);
   }
   __device__ __forceinline__ v8i b_frag(int bslot, int j) const {
@@ -641,7 +649,7 @@ struct Kernel {
       return (v8i){x.x, x.y, x.z, x.w, 0, 0, 0, 0};
     }
     if constexpr (BRX) return frag_rx<FBB, BN>(b_lo + so, b_hi, (uint32_t)(wn * TN + 16 * j));
-    if constexpr (BMN) return frag_tr<FBB>(b_lo + so, b_hi + so, j * 2048);
+    if constexpr (BMN) return frag_tr<FBB>(((j & 1) ? b_hi : b_lo) + so, 4096 * (j >> 1));
     return frag(b_lo + so, b_hi + so, j * 16 * BK);
   }
   // UE8M0: the packed weight-scale word of the lane's B row in fragment j of B stage bslot
