@@ -76,11 +76,17 @@ def log(*a):
 
 
 def kernel_source_hash(sources=GEMM_SOURCES):
+    """sha1 of the kernel sources with comments and whitespace removed (so an edit of a comment
+    does not orphan the traffic figures taken from the same code)."""
     import hashlib
+    import re
     h = hashlib.sha1()
     for f in sources:
-        with open(os.path.join(ROOT, "block_scaled_fp8_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "block_scaled_fp8_amd", "csrc", f), encoding="utf-8") as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()
 
 

@@ -324,15 +324,16 @@ struct Kernel {
   static constexpr bool FP4B = G::FP4B;
   // power-of-two scales applied by the matrix unit itself (no VALU promotion)
   static constexpr bool UE = SFM == SF_1D1D_UE8M0 || FP4B;
-  // operands stored MN-major (K rows of M or N bytes): staged as 16-column strips and read
-  // back with the transposing LDS read
+  // operands stored MN-major (K rows of M or N bytes): staged as 32-column strips (or row-XOR,
+  // below) and read back with the transposing LDS read
   static constexpr bool AMN = (LAY & LAYOUT_A_MN) != 0, BMN = (LAY & LAYOUT_B_MN) != 0;
   static_assert(!(BMN && FP4B), "FP4 weights are K-major");
   static constexpr int FBA = FP4B ? 4 : 5, FBB = 5;  // row-permutation bit of an MN-major stage
   // MN-major operands 128 or 256 columns wide are staged row-major with an XOR key per K row
-  // (the copies then read whole 256-byte row segments); other widths as 16-column strips.
-  // (Measured on 4096x7168x2048: tt 91-93 -> 79-81 us; with both operands MN-major, B in
-  // strips, row-XOR A was 6% slower than strips, so that case keeps strips.)
+  // (the copies then read whole row segments); other widths as 32-column strips.  (Measured
+  // on 4096x7168x2048 at the sustained clock: tt 70.2 us with row-XOR A against 74.4 with
+  // strips; with both operands MN-major and B in strips, row-XOR A took 117.0 against 104.8,
+  // so that case keeps strips.)
   static constexpr bool ARX = AMN && !BMN && (BM == 256 || BM == 128), BRX = BMN && (BN == 256 || BN == 128);
   // Row-XOR staging of an MN-major operand W columns wide: wave-load q fills K rows
   // q * (1024 / W) + [0, 1024 / W), and the XOR key of row r has bit FB of r as its top bit.

@@ -107,7 +107,7 @@ int dg_fp8_gemm_nt(int32_t m, int32_t n, int32_t k,
  * Scales keep their meaning and layout: sfa per row i of D and 128-long K block, sfb per
  * 128x128 block (FP32) or per row j of D (packed UE8M0 only: per-row FP32 weight scales return
  * DG_ERR_UNSUPPORTED here).  k >= 256 (DG_ERR_UNSUPPORTED below).  The operands stored
- * [k, x] are staged in LDS (as 16-column strips, or as whole K rows with an XOR key per row
+ * [k, x] are staged in LDS (as 32-column strips, or as whole K rows with an XOR key per row
  * when the tile side is 128 or 256 wide) and fed to the matrix unit with the transposing LDS
  * read, so no transposed copy is made and no workspace is used.
  */
