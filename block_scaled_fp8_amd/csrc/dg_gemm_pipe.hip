@@ -885,16 +885,20 @@ struct Kernel {
   // of scratch (the A stage of the tile's last K block, which no wave reads any more), reads
   // it back row-major, 16 bytes per lane, and stores it with consecutive lanes on
   // consecutive addresses.
-  // Scratch row r holds 16-byte chunk c at position c ^ ekey(r), ekey(r) = (r mod 16) * PX / 16
-  // with PX the largest power of two (at most 16) that divides the chunk count, so the XOR
-  // stays inside the row.  The 8-byte writes (16 consecutive lanes, rows 0..15 of one chunk,
-  // served together) then spread over the banks, and the read-back gives each group of 16
-  // lanes that LDS serves together (same bit 5, same parity of bits 2..4) 16 consecutive
-  // chunks of the fragment row: both conflict-free on the 64 banks.
+  // Scratch row r holds 16-byte chunk c at position c ^ ekey(r), with its two 8-byte halves
+  // swapped when hkey(r) is 1: ekey(r) = (r mod 16) * PX / 16 with PX the largest power of two
+  // (at most 8) that divides the chunk count, so the XOR stays inside the row, and hkey(r) is
+  // the bit of r just below the ones ekey uses.  The 8-byte writes (16 consecutive lanes,
+  // rows 0..15 of one chunk half) are served 128 bytes at a time (measured), and these keys
+  // give the 16 lanes 16 different 8-byte slots of a 128-byte window; the read-back gives
+  // each group of 16 lanes that LDS serves together (same bit 5, same parity of bits 2..4)
+  // 16 consecutive chunks of the fragment row.  Both are conflict-free.
   static constexpr int RS = 2 * TN;            // scratch row stride in bytes
   static constexpr int CH = TN / 8;            // 16-byte chunks per scratch row
-  static constexpr int PX = CH % 16 == 0 ? 16 : CH % 8 == 0 ? 8 : CH % 4 == 0 ? 4 : CH % 2 == 0 ? 2 : 1;
+  static constexpr int PX = CH % 8 == 0 ? 8 : CH % 4 == 0 ? 4 : CH % 2 == 0 ? 2 : 1;
+  static constexpr int PXB = PX == 8 ? 3 : PX == 4 ? 2 : PX == 2 ? 1 : 0;
   static __device__ __forceinline__ int ekey(int r) { return ((r & 15) * PX) >> 4; }
+  static __device__ __forceinline__ int hkey(int r) { return PX > 1 ? (r >> (3 - PXB)) & 1 : 0; }
   static constexpr int SCR = G::A_SLOT / NW;   // scratch bytes per wave
   static constexpr bool TRANSPOSE = OUT == OUT_BF16 && 16 * RS <= SCR && TN % 8 == 0;
   static constexpr int RD = (16 * CH + 63) / 64;  // read-back rounds per fragment row
@@ -927,14 +931,15 @@ struct Kernel {
 #pragma unroll
           for (int j = 0; j < FN; ++j) {
             const v2u w = {pack_bf16x2(fin[i][j][0], fin[i][j][1]), pack_bf16x2(fin[i][j][2], fin[i][j][3])};
-            *(v2u*)(smem + scr + lr * RS + 16 * ((2 * j + (lg >> 1)) ^ ekey(lr)) + 8 * (lg & 1)) = w;
+            *(v2u*)(smem + scr + lr * RS + 16 * ((2 * j + (lg >> 1)) ^ ekey(lr)) + 8 * ((lg & 1) ^ hkey(lr))) = w;
           }
 #pragma unroll
           for (int k = 0; k < RD; ++k) {
             const int cidx = lpos + 64 * k;
             const int r = cidx / CH, cc = cidx - r * CH;
             if (cidx < 16 * CH && (ALL || 16 * i + r < rows)) {
-              const v4i x = *(const v4i*)(smem + scr + r * RS + 16 * (cc ^ ekey(r)));
+              v4i x = *(const v4i*)(smem + scr + r * RS + 16 * (cc ^ ekey(r)));
+              if (hkey(r)) x = (v4i){x.z, x.w, x.x, x.y};
               *(v4i*)(drow0 + ((int64_t)(16 * i + r) * p.ldd + 8 * cc) * 2) = x;
             }
           }
