@@ -56,9 +56,11 @@ double tile_efficiency(const dg::TileCfg& t) {
   return ai / (ai + 30.0);
 }
 
-int tile_occupancy(const dg::TileCfg& t) {
+// generic kernel, tile kTiles[tile]
+int tile_occupancy(int tile) {
+  const dg::TileCfg& t = dg::kTiles[tile];
   // workgroups per CU: limited by the 160 KiB of LDS and by one wave per SIMD (4 SIMDs)
-  const int lds = dg::gemm_lds_bytes(int(&t - dg::kTiles));
+  const int lds = dg::gemm_lds_bytes(tile);
   const int by_lds = (160 * 1024) / lds;
   const int waves = t.wm * t.wn;
   const int by_simd = waves >= 4 ? 1 : 4 / waves;
@@ -98,7 +100,7 @@ Plan plan_gemm(int kind, int m, int n, int k, int groups, int m_max, int sfm, in
     const int64_t nt = (n + c.bn - 1) / c.bn;
     // (masked and K-grouped: every group has its own mt x nt tiles)
     const int64_t tiles = (kind == 2 || kind == dg::GRP_KGROUP) ? int64_t(groups) * mt * nt : mt * nt;
-    const int occ = tile_occupancy(c);
+    const int occ = tile_occupancy(t);
     const int64_t slots = int64_t(num_sms) * occ;
     const int64_t waves = (tiles + slots - 1) / slots;
     // compute time per wave of tiles ~ tile area / efficiency; occupancy shares a CU
@@ -192,7 +194,7 @@ int do_launch(dg::GemmParams& p, int kind, int32_t m_rows_for_plan, int32_t m_ma
     const int64_t mt = (m_max + c.bm - 1) / c.bm;
     p.num_m_tiles = int(mt);
     const int64_t upper = int64_t(p.num_groups) * mt * p.num_n_tiles;
-    const int64_t slots = int64_t(num_sms) * tile_occupancy(c);
+    const int64_t slots = int64_t(num_sms) * tile_occupancy(pl.tile);
     pl.grid = int(upper < slots ? (upper < 1 ? 1 : upper) : slots);
   } else {
     p.num_m_tiles = pl.num_m_tiles;
@@ -516,7 +518,7 @@ static int k_grouped(int layout, int32_t num_groups, int32_t m, int32_t n, const
     p.total_tiles = int(tiles);
     const int sw = env_int("DG_SWIZZLE_M", 8);
     p.swizzle_m = sw < 1 ? 1 : (sw < p.num_m_tiles ? sw : p.num_m_tiles);
-    const int64_t slots = int64_t(num_sms) * tile_occupancy(tc);
+    const int64_t slots = int64_t(num_sms) * tile_occupancy(pl.tile);
     const int grid = int(tiles < slots ? tiles : slots);
     p.xcd_remap = (grid % 8 == 0) ? 1 : 0;
     p.d_vec = (n % 4 == 0 && aligned16(d)) ? 1 : 0;

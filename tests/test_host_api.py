@@ -14,7 +14,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "dg.h")
 GOLDEN = os.path.join(ROOT, "tests", "golden")
 
-DG_OK, DG_ERR_NULL, DG_ERR_DTYPE, DG_ERR_SHAPE, DG_ERR_LAYOUT, DG_ERR_UNSUPPORTED = 0, -1, -2, -3, -4, -5
+DG_OK, DG_ERR_NULL, DG_ERR_DTYPE, DG_ERR_SHAPE, DG_ERR_LAYOUT, DG_ERR_UNSUPPORTED, DG_ERR_HIP = 0, -1, -2, -3, -4, -5, -6
 
 
 def declared_functions():
@@ -207,6 +207,31 @@ def test_k_grouped_validation():
     assert lib.dg_k_grouped_fp8_gemm_nt_contiguous(2, 8, 8, ks(128, 128), P, 128, P, P, 256, P, P, P, None) == DG_ERR_LAYOUT  # lda < sum
     assert lib.dg_k_grouped_fp8_gemm_nt_contiguous(1, 8, 8, ks(128), P_MIS, 128, P, P, 128, P, P, P, None) == DG_ERR_LAYOUT
     assert lib.dg_k_grouped_fp8_gemm_nt_contiguous(1, 0, 8, ks(128), None, 0, None, None, 0, None, None, None, None) == DG_OK
+
+
+@pytest.mark.skipif(dg.torch.cuda.is_available(), reason="would launch kernels on host buffers")
+@pytest.mark.parametrize("ks", [(256, 0, 384, 128, 512), (256, 0, 384, 256, 512)])
+def test_k_grouped_planning_on_the_host(ks):
+    """Past validation the K-grouped entry plans its launch on the host (tile, occupancy,
+    grid) and only then launches: without a device it ends in a launch error (DG_ERR_HIP), not
+    in a crash of the host code (the occupancy lookup takes the tile's index in the table)."""
+    import numpy as np
+    lib = dg.lib()
+    m, n, G, K = 260, 196, len(ks), sum(ks)
+    keep = []
+
+    def buf(nbytes):
+        b = np.zeros(nbytes + 64, np.uint8)
+        keep.append(b)
+        return ctypes.c_void_p(b.ctypes.data + (-b.ctypes.data) % 16)
+
+    a, b, sfa, sfb, c = buf(m * K), buf(n * K), buf(4 * K // 128 * m), buf(4 * K // 128 * n), buf(4 * G * m * n)
+    assert lib.dg_set_num_sms(256) == DG_OK
+    try:
+        r = lib.dg_k_grouped_fp8_gemm_nt_contiguous(G, m, n, (ctypes.c_int32 * G)(*ks), a, K, sfa, b, K, sfb, c, c, None)
+    finally:
+        lib.dg_set_num_sms(0)
+    assert r == DG_ERR_HIP
 
 
 def test_raw_weight_scale_granularity():
