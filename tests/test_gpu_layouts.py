@@ -55,12 +55,14 @@ def check(p, d, with_c, name=None):
     return check_fp32(d.cpu().numpy(), o, T, name=name)
 
 
-@pytest.mark.parametrize("layout", ["nn", "tn", "tt"])
-@pytest.mark.parametrize("tile", ["256x224", "128x192"])
+@pytest.mark.parametrize("layout,tile", [(l, t) for l in ("nn", "tn", "tt") for t in ("256x224", "128x192")] +
+                         [("nn", "128x256")])
 @pytest.mark.parametrize("shape", [(200, 300, 384), (257, 513, 256), (33, 129, 640), (64, 32, 1024), (130, 260, 512)])
 def test_layout_equals_nt_bitwise_and_oracle(layout, tile, shape):
     """Ragged m and n on every tile (including fewer rows or columns than one tile), K from
-    the two-block minimum up, BF16 and FP32 out (and FP32 + C on the tile that has it)."""
+    the two-block minimum up, BF16 and FP32 out (and FP32 + C on the tile that has it).  On
+    128x256 (nn), B stored [K, N] takes the row-XOR staging and 8 waves, the NT kernel 4 waves:
+    the same partials promoted in the same order, so still the same bits."""
     M, N, K = shape
     p = gen.dense(M, N, K, seed=M * 7 + N + K, with_c=True)
     outs = [(torch.bfloat16, False), (torch.float32, False)] + ([(torch.float32, True)] if tile == "128x192" else [])
@@ -118,19 +120,21 @@ def test_layout_planner_tiles_and_c_aliasing():
     assert ok.all(), st
 
 
-def test_layout_tn_full_size_sampled_rows():
-    """tn (both operands stored K-outermost, the weight-gradient storage) at the dense benchmark
-    size, M = 4096, N = 7168, K = 2048, BF16 out, in the planner's launch configuration; rows
-    are independent, so 384 sampled rows (first and last included) are checked."""
+@pytest.mark.parametrize("layout", ["tn", "nn"])
+def test_layout_full_size_sampled_rows(layout):
+    """tn (both operands stored K-outermost, the weight-gradient storage) and nn (B stored
+    [K, N]) at the dense benchmark size, M = 4096, N = 7168, K = 2048, BF16 out, in the
+    planner's launch configuration (nn: the 256-wide tile); rows are independent, so 384
+    sampled rows (first and last included) are checked."""
     p = gen.dense(4096, 7168, 2048, seed=0)
-    say("layout tn full size")
-    d = run("tn", p, torch.bfloat16, None, pad=0)
+    say("layout full size", layout)
+    d = run(layout, p, torch.bfloat16, None, pad=0)
     rows = np.unique(np.concatenate([[0, 4095], np.random.default_rng(4).choice(4096, 382, replace=False)]))
     o, T = oracle.gemm_nt(p["a"][rows], p["sa"][rows], p["b"], p["sb"], 128, want_abs=True)
-    ok, st = check_bf16(bf16_bits(d)[rows], o, T, name=f"tn 4096x7168x2048 ({len(rows)} rows) bf16")
-    say("layout tn full size", st)
+    ok, st = check_bf16(bf16_bits(d)[rows], o, T, name=f"{layout} 4096x7168x2048 ({len(rows)} rows) bf16")
+    say("layout full size", layout, st)
     assert ok.all(), st
-    assert_full_size(st, "tn dense")
+    assert_full_size(st, f"{layout} dense")
 
 
 def test_m_grouped_nn_contiguous_ragged():

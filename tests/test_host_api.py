@@ -234,6 +234,38 @@ def test_k_grouped_planning_on_the_host(ks):
     assert r == DG_ERR_HIP
 
 
+@pytest.mark.skipif(dg.torch.cuda.is_available(), reason="would launch kernels on host buffers")
+@pytest.mark.parametrize("M,N,K,tile", [(4096, 7168, 2048, "128x256"), (4096, 2048, 7168, "128x256"),
+                                        (512, 7168, 2048, "128x192"), (16, 48, 256, "128x192")])
+def test_nn_planner_tile(M, N, K, tile, capfd, monkeypatch):
+    """B stored [K, N]: the planner favours the 256-wide tile (B row-XOR staged) once the
+    problem fills the chip twice, and leaves smaller problems to the area model.  The plan is
+    printed before the launch, which fails here without a device."""
+    import numpy as np
+    lib = dg.lib()
+    keep = []
+
+    def buf(nbytes):
+        b = np.zeros(nbytes + 64, np.uint8)
+        keep.append(b)
+        return ctypes.c_void_p(b.ctypes.data + (-b.ctypes.data) % 16)
+
+    monkeypatch.setenv("DG_PRINT_CONFIGS", "1")
+    monkeypatch.delenv("DG_FORCE_TILE", raising=False)
+    a4, nkb = (M + 3) // 4 * 4, K // 128
+    args = (M, N, K, buf(M * K), ctypes.c_int64(K), buf(4 * nkb * a4), ctypes.c_int64(a4), buf(N * K), ctypes.c_int64(N),
+            buf(4 * nkb * ((N + 127) // 128)), ctypes.c_int64(nkb), 0, 128, None, ctypes.c_int64(0), buf(2 * M * N),
+            ctypes.c_int64(N), 1, None)
+    assert lib.dg_set_num_sms(256) == DG_OK
+    try:
+        capfd.readouterr()
+        r = lib.dg_fp8_gemm_nn(*args)
+    finally:
+        lib.dg_set_num_sms(0)
+    assert r == DG_ERR_HIP
+    assert f"-> tile {tile} " in capfd.readouterr().err
+
+
 def test_raw_weight_scale_granularity():
     """Raw K-major weight scales: one row per 128-row block means 128x128 block scales, also
     when n <= 128 (a single block row); one row per weight row means per-row scales."""
