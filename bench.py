@@ -53,6 +53,8 @@ WORKLOADS = {
     "dense_tt_4096x7168x2048": dict(kind="dense", M=4096, N=7168, K=2048, layout="tt"),
     "masked_32x256x7168x2048": dict(kind="masked"),
     "contiguous_32x4096x7168": dict(kind="contig"),
+    # the same with every group's weights stored [K, N] (m_grouped_fp8_gemm_nn_contiguous)
+    "contiguous_nn_32x4096x7168": dict(kind="contig", layout="nn"),
     "fp8_fp4_dense_4096x7168x2048": dict(kind="fp4_dense", M=4096, N=7168, K=2048),
     "fp8_fp4_masked_32x256x7168x2048": dict(kind="fp4_masked"),
     "cast_4096x7168_bf16": dict(kind="cast", M=4096, K=7168, graph=True),
@@ -276,21 +278,29 @@ def w_contig(spec, dg, dev):
     d = torch.empty((p["M"], N), dtype=torch.bfloat16, device=dev)
     flops = 2.0 * p["M"] * N * K
     alg_bytes = G * N * K + p["M"] * K + 2 * p["M"] * N
+    form = spec.get("layout", "nt")
+    if form == "nn":
+        b = b.transpose(1, 2).contiguous()   # [G, K, N]
+    gemm = getattr(dg, f"m_grouped_fp8_gemm_{form}_contiguous")
 
     def launch(i):
-        dg.m_grouped_fp8_gemm_nt_contiguous((a, sa), (b, sb), d, lay)
+        gemm((a, sa), (b, sb), d, lay)
 
     def cpu(seconds):
         rows = np.arange(0, p["M"], max(1, p["M"] // 96))
         t0 = time.perf_counter()
-        oracle.grouped_contiguous(p["a"][rows], p["sa"][rows], p["b"], p["sb"], p["layout"][rows])
+        if form == "nn":
+            oracle.grouped_contiguous_nn(p["a"][rows], p["sa"][rows], np.swapaxes(p["b"], 1, 2), p["sb"],
+                                         p["layout"][rows])
+        else:
+            oracle.grouped_contiguous(p["a"][rows], p["sa"][rows], p["b"], p["sb"], p["layout"][rows])
         t = time.perf_counter() - t0
         return 2.0 * len(rows) * N * K / t, t, f"{len(rows)} evenly spaced rows (every group's weights), float64 numpy"
 
     return Workload(launch=launch, work=flops, flops=flops, alg_bytes=alg_bytes, bound="mfma",
                     kernel="dg::pipe::pipe_kernel (contiguous)", cpu=cpu,
                     config={"workload": None, "groups": G, "rows": p["M"], "N": N, "K": K, "out": "bf16",
-                            "scales": "fp32 1x128 act, 128x128 weight"})
+                            "layout": form, "scales": "fp32 1x128 act, 128x128 weight"})
 
 
 def w_fp4_dense(spec, dg, dev):

@@ -137,6 +137,23 @@ def test_layout_full_size_sampled_rows(layout):
     assert_full_size(st, f"{layout} dense")
 
 
+def test_m_grouped_nn_contiguous_full_size_equals_nt():
+    """The contiguous workload the benchmark times (32 groups, 4096 x 7168 weights) with the
+    weights stored [K, N], in the planner's launch configuration: every output equals the NT
+    form's bit for bit (the NT form is checked against the oracle at this size elsewhere)."""
+    p = gen.config4()
+    say("m-grouped nn full size", p["M"], p["N"], p["K"])
+    a, sa, lay = cuda(p["a"]), cuda(p["sa"]), cuda(p["layout"])
+    outs = []
+    for form, b in (("nt", cuda(p["b"])), ("nn", cuda(np.ascontiguousarray(np.swapaxes(p["b"], 1, 2))))):
+        d = torch.full((p["M"], p["N"]), float("nan"), dtype=torch.bfloat16, device=DEV)
+        getattr(dg, f"m_grouped_fp8_gemm_{form}_contiguous")((a, sa), (b, cuda(p["sb"])), d, lay)
+        torch.cuda.synchronize()
+        outs.append(d.view(torch.int16).cpu())
+        del b
+    assert torch.equal(outs[0], outs[1])
+
+
 def test_m_grouped_nn_contiguous_ragged():
     """Contiguous groups with each group's weights stored [K, N]: equal to the NT form bit for
     bit on the same tile, and to the oracle; padding rows, a skipped block, m_total cut inside
