@@ -55,6 +55,8 @@ WORKLOADS = {
     "contiguous_32x4096x7168": dict(kind="contig"),
     # the same with every group's weights stored [K, N] (m_grouped_fp8_gemm_nn_contiguous)
     "contiguous_nn_32x4096x7168": dict(kind="contig", layout="nn"),
+    # FP8 activations x FP4 weights, contiguous groups (m_grouped_fp8_fp4_gemm_nt_contiguous)
+    "fp8_fp4_contiguous_32x4096x7168": dict(kind="contig", fp4=True),
     "fp8_fp4_dense_4096x7168x2048": dict(kind="fp4_dense", M=4096, N=7168, K=2048),
     "fp8_fp4_masked_32x256x7168x2048": dict(kind="fp4_masked"),
     "cast_4096x7168_bf16": dict(kind="cast", M=4096, K=7168, graph=True),
@@ -268,20 +270,29 @@ def w_masked(spec, dg, dev, fp4=False):
 def w_contig(spec, dg, dev):
     from tests import gen
     import oracle
-    p = gen.config4()
+    fp4 = spec.get("fp4", False)
+    p = gen.fp8_fp4_grouped_contiguous(32, 4096, 7168, seed=0) if fp4 else gen.config4()
     G, N, K = p["G"], p["N"], p["K"]
     a = torch.from_numpy(p["a"]).to(dev)
     b = torch.from_numpy(p["b"]).to(dev)
-    sa = dg.get_mn_major_tma_aligned_tensor(torch.from_numpy(p["sa"]).to(dev))
-    sb = torch.from_numpy(p["sb"]).to(dev)
+    if fp4:   # scales packed once (UE8M0), as the FP4 benchmark lines do
+        sa = dg.transform_sf(torch.from_numpy(p["sa"]).to(dev), p["M"], 1, True)
+        sb = dg.transform_sf(torch.from_numpy(p["sb"]).to(dev), N, 1, True)
+    else:
+        sa = dg.get_mn_major_tma_aligned_tensor(torch.from_numpy(p["sa"]).to(dev))
+        sb = torch.from_numpy(p["sb"]).to(dev)
     lay = torch.from_numpy(p["layout"]).to(dev)
     d = torch.empty((p["M"], N), dtype=torch.bfloat16, device=dev)
     flops = 2.0 * p["M"] * N * K
-    alg_bytes = G * N * K + p["M"] * K + 2 * p["M"] * N
+    if fp4:
+        alg_bytes = G * N * K // 2 + p["M"] * K + 4 * p["M"] * ((K // 128 + 3) // 4) + 4 * G * N * (K // 128) \
+            + 2 * p["M"] * N
+    else:
+        alg_bytes = G * N * K + p["M"] * K + 2 * p["M"] * N
     form = spec.get("layout", "nt")
     if form == "nn":
         b = b.transpose(1, 2).contiguous()   # [G, K, N]
-    gemm = getattr(dg, f"m_grouped_fp8_gemm_{form}_contiguous")
+    gemm = dg.m_grouped_fp8_fp4_gemm_nt_contiguous if fp4 else getattr(dg, f"m_grouped_fp8_gemm_{form}_contiguous")
 
     def launch(i):
         gemm((a, sa), (b, sb), d, lay)
@@ -289,7 +300,9 @@ def w_contig(spec, dg, dev):
     def cpu(seconds):
         rows = np.arange(0, p["M"], max(1, p["M"] // 96))
         t0 = time.perf_counter()
-        if form == "nn":
+        if fp4:
+            oracle.grouped_contiguous_fp8_fp4(p["a"][rows], p["sa"][rows], p["b"], p["sb"], p["layout"][rows])
+        elif form == "nn":
             oracle.grouped_contiguous_nn(p["a"][rows], p["sa"][rows], np.swapaxes(p["b"], 1, 2), p["sb"],
                                          p["layout"][rows])
         else:
@@ -300,7 +313,9 @@ def w_contig(spec, dg, dev):
     return Workload(launch=launch, work=flops, flops=flops, alg_bytes=alg_bytes, bound="mfma",
                     kernel="dg::pipe::pipe_kernel (contiguous)", cpu=cpu,
                     config={"workload": None, "groups": G, "rows": p["M"], "N": N, "K": K, "out": "bf16",
-                            "layout": form, "scales": "fp32 1x128 act, 128x128 weight"})
+                            "layout": form,
+                            "scales": ("ue8m0 packed x4 (act per 1x128), fp4 e2m1 weights with ue8m0 per 1x32" if fp4
+                                       else "fp32 1x128 act, 128x128 weight")})
 
 
 def w_fp4_dense(spec, dg, dev):

@@ -45,7 +45,7 @@ KERNEL = {
     "cast_ue8m0_4096x7168_bf16": "cast_kernel", "k_grouped_8x7168x2048_k16384": "gemm_kernel",
     "dense_nn_4096x7168x2048": "pipe_kernel", "dense_tn_4096x7168x2048": "pipe_kernel",
     "dense_tt_4096x7168x2048": "pipe_kernel", "k_grouped_tn_8x7168x2048_k16384": "gemm_kernel",
-    "contiguous_nn_32x4096x7168": "pipe_kernel",
+    "contiguous_nn_32x4096x7168": "pipe_kernel", "fp8_fp4_contiguous_32x4096x7168": "pipe_kernel",
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
 TRAFFIC_HEADER = """# HBM traffic of the timed kernel launch from rocprofv3 counters, one MI355X.
