@@ -166,6 +166,28 @@ def test_fp8_fp4_dense_full_size_sampled_rows():
     assert_full_size(st, "fp8 x fp4 dense")
 
 
+def test_fp8_fp4_contiguous_full_size_sampled_rows():
+    """Contiguous groups with FP4 weights at the size the benchmark times (32 groups of 128 to
+    1024 rows, 4096 x 7168 weights), in the planner's launch configuration: the first and last
+    row of every group and 8 more rows per group against the oracle."""
+    p = gen.fp8_fp4_grouped_contiguous(32, 4096, 7168, seed=0)
+    say("fp8 x fp4 contiguous full size", p["M"])
+    d = torch.full((p["M"], p["N"]), float("nan"), dtype=torch.bfloat16, device=DEV)
+    dg.m_grouped_fp8_fp4_gemm_nt_contiguous((cuda(p["a"]), cuda(p["sa"])), (cuda(p["b"]), cuda(p["sb"])), d,
+                                            cuda(p["layout"]))
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(3)
+    starts = np.concatenate([[0], np.cumsum(p["sizes"])])
+    rows = np.unique(np.concatenate([np.concatenate([[s, e - 1], rng.integers(s, e, 8)])
+                                     for s, e in zip(starts[:-1], starts[1:])]))
+    o, T = oracle.grouped_contiguous_fp8_fp4(p["a"][rows], p["sa"][rows], p["b"], p["sb"], p["layout"][rows],
+                                             want_abs=True)
+    ok, st = check_bf16(bf16_bits(d)[rows], o, T, name=f"fp8 x fp4 contiguous 32x4096x7168 ({len(rows)} rows) bf16")
+    say("fp8 x fp4 contiguous full size", st)
+    assert ok.all(), st
+    assert_full_size(st, "fp8 x fp4 contiguous")
+
+
 def test_fp8_fp4_masked_full_size_sampled():
     """The masked decode with FP4 weights at the size the benchmark times (32 groups x 256,
     N = 7168, K = 2048): all rows of 4 groups and 32 rows of every other group."""
