@@ -155,7 +155,11 @@ def w_dense(spec, dg, dev):
     with_c = spec["kind"] == "dense_c"
     p = gen.dense(M, N, K, seed=0, with_c=with_c)
     out_dtype = torch.float32 if with_c else torch.bfloat16
-    nsets = 8 if M * K + N * K < 256 << 20 else 2
+    # buffer sets rotated through the steps: enough that one rotation moves at least 512 MiB, so
+    # no step finds its operands in the 8 x 4 MB of L2 or the 256 MB of last-level cache (the
+    # decode's 15.7 MB per set takes 35 sets); two for operands of 256 MiB and more
+    set_bytes = M * K + N * K + (4 if with_c else 2) * M * N + (4 * M * N if with_c else 0)
+    nsets = 2 if M * K + N * K >= 256 << 20 else max(8, min(64, -(-(512 << 20) // set_bytes)))
     layout = spec.get("layout", "nt")
     # operands as the layout stores them: A [K, M] for "t", B [K, N] for "n"
     a_st = p["a"] if layout[0] == "n" else np.ascontiguousarray(p["a"].T)
