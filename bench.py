@@ -225,27 +225,33 @@ def w_masked(spec, dg, dev, fp4=False):
     else:
         p = gen.config5()
     G, Mmax, N, K = 32, 256, 7168, 2048
-    a = torch.from_numpy(p["a"]).to(dev)
-    b = torch.from_numpy(p["b"]).to(dev)
     mm = torch.from_numpy(p["masked_m"]).to(dev)
-    d = torch.empty((G, Mmax, N), dtype=torch.bfloat16, device=dev)
     pk = (K // 128 + 3) // 4
     valid = int(np.clip(p["masked_m"], 0, Mmax).sum())
     active = int((p["masked_m"] > 0).sum())
+    w_set = (N * K // 2 + 4 * N * (K // 128)) if fp4 else (N * K + 4 * N * pk)
+    step_bytes = active * w_set + valid * (K + 4 * pk + 2 * N)
+    # buffer sets rotated through the steps: one rotation moves at least 1 GiB, so a step's
+    # weights (313 MB with FP4, 542 MB with FP8) are not found in the 256 MB last-level cache
+    nsets = max(2, -(-(1 << 30) // step_bytes))
+    sets = [dict(a=torch.from_numpy(p["a"]).to(dev), b=torch.from_numpy(p["b"]).to(dev),
+                 d=torch.empty((G, Mmax, N), dtype=torch.bfloat16, device=dev)) for _ in range(nsets)]
     if fp4:
         sa = dg.transform_sf(torch.from_numpy(p["sa"]).to(dev), Mmax, 1, True)
         sb = dg.transform_sf(torch.from_numpy(p["sb"]).to(dev), N, 1, True)
         w_bytes = N * K // 2 + 4 * N * (K // 128)
 
         def launch(i):
-            dg.m_grouped_fp8_fp4_gemm_nt_masked((a, sa), (b, sb), d, mm, expected_m=128)
+            s = sets[i % nsets]
+            dg.m_grouped_fp8_fp4_gemm_nt_masked((s["a"], sa), (s["b"], sb), s["d"], mm, expected_m=128)
     else:
         sa = dg.get_mn_major_tma_aligned_packed_ue8m0_tensor(torch.from_numpy(p["sa"]).to(dev))
         sb = dg.get_mn_major_tma_aligned_packed_ue8m0_tensor(torch.from_numpy(p["sb"]).to(dev), gran_mn=128, mn=N)
         w_bytes = N * K + 4 * N * pk
 
         def launch(i):
-            dg.m_grouped_fp8_gemm_nt_masked((a, sa), (b, sb), d, mm, expected_m=128)
+            s = sets[i % nsets]
+            dg.m_grouped_fp8_gemm_nt_masked((s["a"], sa), (s["b"], sb), s["d"], mm, expected_m=128)
     alg_bytes = active * w_bytes + valid * (K + 4 * pk + 2 * N) + 4 * G
     flops = 2.0 * valid * N * K
 
@@ -268,7 +274,7 @@ def w_masked(spec, dg, dev, fp4=False):
                     config={"workload": None, "groups": G, "m_max": Mmax, "N": N, "K": K, "valid_rows": valid,
                             "weights": "fp4 e2m1, ue8m0 per 1x32" if fp4 else "fp8 e4m3, ue8m0 per 128x128",
                             "scales": "ue8m0 packed x4, mn-major", "out": "bf16",
-                            "step": "gemm (scales pre-packed, as the cast emits them)"})
+                            "step": "gemm (scales pre-packed, as the cast emits them)", "buffer_sets": nsets})
 
 
 def w_contig(spec, dg, dev):
