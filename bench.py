@@ -292,7 +292,6 @@ def w_contig(spec, dg, dev):
         sa = dg.get_mn_major_tma_aligned_tensor(torch.from_numpy(p["sa"]).to(dev))
         sb = torch.from_numpy(p["sb"]).to(dev)
     lay = torch.from_numpy(p["layout"]).to(dev)
-    d = torch.empty((p["M"], N), dtype=torch.bfloat16, device=dev)
     flops = 2.0 * p["M"] * N * K
     if fp4:
         alg_bytes = G * N * K // 2 + p["M"] * K + 4 * p["M"] * ((K // 128 + 3) // 4) + 4 * G * N * (K // 128) \
@@ -303,9 +302,16 @@ def w_contig(spec, dg, dev):
     if form == "nn":
         b = b.transpose(1, 2).contiguous()   # [G, K, N]
     gemm = dg.m_grouped_fp8_fp4_gemm_nt_contiguous if fp4 else getattr(dg, f"m_grouped_fp8_gemm_{form}_contiguous")
+    # buffer sets rotated through the steps: one rotation moves at least 1 GiB (FP8 weights: one
+    # set, 1.24 GB per step; FP4 weights: two sets of 0.80 GB), past the 256 MB last-level cache
+    nsets = max(1, -(-(1 << 30) // alg_bytes))
+    sets = [dict(a=a, b=b, d=torch.empty((p["M"], N), dtype=torch.bfloat16, device=dev))]
+    for _ in range(nsets - 1):
+        sets.append(dict(a=a.clone(), b=b.clone(), d=torch.empty((p["M"], N), dtype=torch.bfloat16, device=dev)))
 
     def launch(i):
-        gemm((a, sa), (b, sb), d, lay)
+        s = sets[i % nsets]
+        gemm((s["a"], sa), (s["b"], sb), s["d"], lay)
 
     def cpu(seconds):
         rows = np.arange(0, p["M"], max(1, p["M"] // 96))
@@ -323,7 +329,7 @@ def w_contig(spec, dg, dev):
     return Workload(launch=launch, work=flops, flops=flops, alg_bytes=alg_bytes, bound="mfma",
                     kernel="dg::pipe::pipe_kernel (contiguous)", cpu=cpu,
                     config={"workload": None, "groups": G, "rows": p["M"], "N": N, "K": K, "out": "bf16",
-                            "layout": form,
+                            "layout": form, "buffer_sets": nsets,
                             "scales": ("ue8m0 packed x4 (act per 1x128), fp4 e2m1 weights with ue8m0 per 1x32" if fp4
                                        else "fp32 1x128 act, 128x128 weight")})
 
@@ -414,13 +420,16 @@ def w_cast(spec, dg, dev):
     M, K = spec["M"], spec["K"]
     ue8m0 = spec.get("ue8m0", False)
     g = torch.Generator(device=dev).manual_seed(0)
-    xs = [torch.randn((M, K), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16) for _ in range(8)]
-    outs = [dg.per_token_group_cast_fp8(xs[i], pack_ue8m0=ue8m0) for i in range(2)]
     sf_bytes = 4 * (K // 512) if ue8m0 else 4 * (K // 128)
     alg_bytes = M * K * 2 + M * K + M * sf_bytes
+    # input and output sets rotated through the steps: one rotation moves at least 1 GiB, so no
+    # step finds its input in the 256 MB last-level cache
+    nsets = max(8, -(-(1 << 30) // alg_bytes))
+    xs = [torch.randn((M, K), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16) for _ in range(nsets)]
+    outs = [dg.per_token_group_cast_fp8(xs[i], pack_ue8m0=ue8m0) for i in range(nsets)]
 
     def launch(i):
-        dg.per_token_group_cast_fp8(xs[i % len(xs)], pack_ue8m0=ue8m0, out=outs[i % 2])
+        dg.per_token_group_cast_fp8(xs[i % nsets], pack_ue8m0=ue8m0, out=outs[i % nsets])
 
     def cpu(seconds):
         x = xs[0][:256].float().cpu().numpy()
