@@ -1182,8 +1182,9 @@ static hipError_t launch_layout(const GemmParams& p, int bm, int bn, int sfm, in
     DG_CASE(128, 192, 2, 2, SF_FP4_UE8M0, OUT_F32_C, GRP_DENSE)
   }
   if constexpr (LAY == LAYOUT_B_MN) {
-    // (contiguous nn on 128x256 with 8 waves as 2x4: 1086 us against 1822 with 4 waves on
-    // 32 groups, 4096 x 7168 weights, at the sustained clock in one process)
+    // (contiguous nn on 128x256 with 8 waves as 2x4: 1084 us against 1822 with 4 waves on 32
+    // groups of 4096 x 7168 weights at the sustained clock in one process.  As 1x8, like dense
+    // nn below, it ran 920 us but spills registers (40 to 144 bytes per lane), so it stays 2x4.)
     DG_CASE(128, 224, 2, 2, SF_1D2D_F32, OUT_BF16, GRP_CONTIG)
     DG_CASE(128, 224, 2, 2, SF_1D2D_F32, OUT_F32, GRP_CONTIG)
     DG_CASE(128, 224, 2, 2, SF_1D1D_UE8M0, OUT_BF16, GRP_CONTIG)
@@ -1192,11 +1193,14 @@ static hipError_t launch_layout(const GemmParams& p, int bm, int bn, int sfm, in
     DG_CASE(128, 256, 2, 4, SF_1D1D_UE8M0, OUT_BF16, GRP_CONTIG)
   }
   if constexpr (LAY == LAYOUT_B_MN) {
-    // nn on a 256-wide tile, where B takes the row-XOR staging (8 waves as 2x4): 110.5 against
-    // 115.0 us for 256x224 on 4096x7168x2048 at the sustained clock.  (tn on this tile: 116.3 us
-    // with A in strips, 113.1 with both operands row-XOR, against 104.4 on 256x224.)
-    DG_CASE(128, 256, 2, 4, SF_1D2D_F32, OUT_BF16, GRP_DENSE)
-    DG_CASE(128, 256, 2, 4, SF_1D2D_F32, OUT_F32, GRP_DENSE)
+    // nn on a 256-wide tile, where B takes the row-XOR staging, with 8 waves as 1x8, each wave
+    // 128 rows x 32 columns: a wave reads the B columns of its own N range once per block with
+    // the transposing read, and with a single wave row no two waves transpose the same columns
+    // (every wave reads all 128 A rows with plain 16-byte reads instead).  91.9 us against 110.5
+    // as 2x4 and 115.0 for 256x224 (4x2) on 4096x7168x2048 at the sustained clock.  (tn on this tile, 2x4:
+    // 116.3 us with A in strips, 113.1 with both operands row-XOR, against 104.4 on 256x224.)
+    DG_CASE(128, 256, 1, 8, SF_1D2D_F32, OUT_BF16, GRP_DENSE)
+    DG_CASE(128, 256, 1, 8, SF_1D2D_F32, OUT_F32, GRP_DENSE)
   }
 #undef DG_CASE
   return hipErrorInvalidValue;
