@@ -1042,9 +1042,12 @@ struct Kernel {
       }
     };
     if constexpr (GRP == GRP_CONTIG) {
-      // a skipped tile runs its K blocks without MFMAs (its copies are empty)
-      if (cur.mv == 0) {
-        run.template operator()<FN, 0>();
+      // a skipped tile runs its K blocks without MFMAs (its copies are empty).  With a single
+      // wave row (128 rows per wave) that third copy of the block loop pushes the kernel past
+      // 256 VGPRs into scratch, so there a skipped tile runs the ordinary loop on its empty
+      // (zero) copies instead; it stores nothing either way.
+      if (WM > 1 && cur.mv == 0) {
+        if constexpr (WM > 1) run.template operator()<FN, 0>();
       } else {
         [&]<int... Ns>(std::integer_sequence<int, Ns...>) {
           ((nf == Ns + 1 ? run.template operator()<Ns + 1, FM>() : void()), ...);
@@ -1182,15 +1185,14 @@ static hipError_t launch_layout(const GemmParams& p, int bm, int bn, int sfm, in
     DG_CASE(128, 192, 2, 2, SF_FP4_UE8M0, OUT_F32_C, GRP_DENSE)
   }
   if constexpr (LAY == LAYOUT_B_MN) {
-    // (contiguous nn on 128x256 with 8 waves as 2x4: 1084 us against 1822 with 4 waves on 32
-    // groups of 4096 x 7168 weights at the sustained clock in one process.  As 1x8, like dense
-    // nn below, it ran 920 us but spills registers (40 to 144 bytes per lane), so it stays 2x4.)
+    // (contiguous nn on 128x256 with 8 waves as 1x8, like dense nn below: 839 us against 1084
+    // as 2x4 and 1822 with 4 waves, on 32 groups of 4096 x 7168 weights at the sustained clock)
     DG_CASE(128, 224, 2, 2, SF_1D2D_F32, OUT_BF16, GRP_CONTIG)
     DG_CASE(128, 224, 2, 2, SF_1D2D_F32, OUT_F32, GRP_CONTIG)
     DG_CASE(128, 224, 2, 2, SF_1D1D_UE8M0, OUT_BF16, GRP_CONTIG)
-    DG_CASE(128, 256, 2, 4, SF_1D2D_F32, OUT_BF16, GRP_CONTIG)
-    DG_CASE(128, 256, 2, 4, SF_1D2D_F32, OUT_F32, GRP_CONTIG)
-    DG_CASE(128, 256, 2, 4, SF_1D1D_UE8M0, OUT_BF16, GRP_CONTIG)
+    DG_CASE(128, 256, 1, 8, SF_1D2D_F32, OUT_BF16, GRP_CONTIG)
+    DG_CASE(128, 256, 1, 8, SF_1D2D_F32, OUT_F32, GRP_CONTIG)
+    DG_CASE(128, 256, 1, 8, SF_1D1D_UE8M0, OUT_BF16, GRP_CONTIG)
   }
   if constexpr (LAY == LAYOUT_B_MN) {
     // nn on a 256-wide tile, where B takes the row-XOR staging, with 8 waves as 1x8, each wave
