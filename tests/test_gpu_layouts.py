@@ -196,6 +196,45 @@ def test_m_grouped_nn_contiguous_ragged():
             assert np.isnan(got.float().cpu().numpy()[~live]).all()
 
 
+def test_m_grouped_nn_contiguous_ue8m0():
+    """Contiguous groups with weights stored [K, N] and packed UE8M0 scales (power-of-two scales,
+    one per weight row), on both nn tiles: bit for bit equal to the NT form on the same tile, and
+    to the oracle evaluated with the same scales; a skipped block and rows past m_total."""
+    G, N, K = 4, 300, 512
+    p = gen.grouped_contiguous(G, N, K, seed=41, m_units=(1, 3))
+    pow2 = lambda x: np.exp2(np.ceil(np.log2(x))).astype(np.float32)   # scales rounded up to 2^e
+    sa = pow2(p["sa"])
+    sb = np.stack([oracle.expand_scales_b(pow2(p["sb"][g]), N, 128) for g in range(G)]).astype(np.float32)
+    starts = np.concatenate([[0], np.cumsum(p["sizes"])])
+    layout = p["layout"].copy()
+    if p["sizes"][1] > 128:
+        layout[starts[1]:starts[1] + 128] = -1
+    M = p["M"] - 20
+    a, sa, layout = p["a"][:M], sa[:M], layout[:M]
+    ld = (N + 15) // 16 * 16                             # rows of [K, N] padded to 16 bytes
+    bt = np.full((G, K, ld), NAN_CODE, np.uint8)
+    bt[:, :, :N] = np.swapaxes(p["b"], 1, 2)
+    b_nn = cuda(bt)[:, :, :N]
+    o, T = oracle.grouped_contiguous(a, sa, p["b"], sb, layout, gran_n=1, want_abs=True)
+    live = ~np.isnan(o)
+    for tile in ("128x256", "128x224"):
+        say("m-grouped nn ue8m0", tile, p["sizes"].tolist(), M)
+        ds = []
+        for form, b in (("nt", cuda(p["b"])), ("nn", b_nn)):
+            d = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=DEV)
+            with force_tile(tile):
+                getattr(dg, f"m_grouped_fp8_gemm_{form}_contiguous")((cuda(a), cuda(sa)), (b, cuda(sb)), d,
+                                                                      cuda(layout), recipe=(1, 1, 128), pack_ue8m0=True)
+            torch.cuda.synchronize()
+            ds.append(d.view(torch.int16).cpu())
+        assert torch.equal(ds[0], ds[1]), tile
+        bits = ds[1].numpy().view(np.uint16)
+        ok, st = check_bf16(bits[live], o[live], T[live])
+        say("m-grouped nn ue8m0", st)
+        assert ok.all(), st
+        assert (bits[~live] == np.uint16(0x7FC0)).all()      # rows that produce no output keep the NaN
+
+
 @pytest.mark.parametrize("tile", ["256x224", "128x192"])
 @pytest.mark.parametrize("shape", [(200, 300, 384), (33, 129, 640), (257, 64, 256)])
 def test_fp8_fp4_tt_equals_nt_bitwise_and_oracle(tile, shape):
