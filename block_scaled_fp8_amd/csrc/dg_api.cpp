@@ -118,12 +118,12 @@ Plan plan_gemm(int kind, int m, int n, int k, int groups, int m_max, int sfm, in
     // 136 against 143 us for 32 groups of up to 256 rows, so such a tile is taken outright.
     if (kind == 2 && k / 128 >= dg::pipe_stages_b(c.bm, c.bn, kind) && dg::pipe_instantiated(c.bm, c.bn, sfm, kind, out))
       cost *= c.bm >= m_max ? 0.01 : 0.8;
-    // B stored [K, N] (nn): every B fragment costs four transposing LDS reads, and on the
-    // 256-wide tile B takes the row-XOR staging whose copies read whole row segments, which
-    // the area model cannot see: measured 110.5 against 115.0 us for 256x224 on 4096x7168x2048
-    // (896 against 512 tiles), so the 256-wide tile is favoured once the problem fills the chip
-    // at least twice (with fewer tiles than workgroup slots the area model already decides)
-    if (kind == 0 && layout == dg::LAYOUT_B_MN && c.bm == 128 && c.bn == 256 && waves >= 2) cost *= 0.75;
+    // B stored [K, N] (nn): every B fragment costs four transposing LDS reads; the 256-wide
+    // tile stages B row-XOR and runs 8 waves as one wave row, so each B column is transposed
+    // once per block, which the area model cannot see.  Measured against the planner's other
+    // tiles: 91.9 against 115.0 us (256x224) on 4096x7168x2048, 24.2 against 39.7 us (128x192,
+    // 4 waves) on 512x7168x2048, 86.5 against 168.8 us on 768x4096x7168; so nn takes it.
+    if (kind == 0 && layout == dg::LAYOUT_B_MN && c.bm == 128 && c.bn == 256) cost *= 0.4;
     if (cost < best_cost - 1e-9) {
       best_cost = cost;
       best.tile = t;
