@@ -122,8 +122,9 @@ Plan plan_gemm(int kind, int m, int n, int k, int groups, int m_max, int sfm, in
     // tile stages B row-XOR and runs 8 waves as one wave row, so each B column is transposed
     // once per block, which the area model cannot see.  Measured against the planner's other
     // tiles: 91.9 against 115.0 us (256x224) on 4096x7168x2048, 24.2 against 39.7 us (128x192,
-    // 4 waves) on 512x7168x2048, 86.5 against 168.8 us on 768x4096x7168; so nn takes it.
-    if (kind == 0 && layout == dg::LAYOUT_B_MN && c.bm == 128 && c.bn == 256) cost *= 0.4;
+    // 4 waves) on 512x7168x2048, 86.5 against 168.8 us on 768x4096x7168; so nn takes it, and
+    // so do contiguous groups with weights stored [K, N] (839 us against 1822 with 4 waves).
+    if ((kind == 0 || kind == 1) && layout == dg::LAYOUT_B_MN && c.bm == 128 && c.bn == 256) cost *= 0.4;
     if (cost < best_cost - 1e-9) {
       best_cost = cost;
       best.tile = t;
