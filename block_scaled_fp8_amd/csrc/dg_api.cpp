@@ -80,9 +80,9 @@ Plan plan_gemm(int kind, int m, int n, int k, int groups, int m_max, int sfm, in
   const char* force = getenv("DG_FORCE_TILE");
   int fbm = 0, fbn = 0;
   if (force && sscanf(force, "%dx%d", &fbm, &fbn) != 2) fbm = fbn = 0;
-  // dense K-major problems: whether some tile runs on the pipelined kernel (see below)
+  // dense and contiguous K-major problems: whether some tile runs on the pipelined kernel (see below)
   bool any_pipe = false;
-  if (kind == 0 && !layout)
+  if ((kind == 0 || kind == 1) && !layout)
     for (int t = 0; t < dg::kNumTiles; ++t)
       any_pipe = any_pipe || (dg::gemm_instantiated(t, sfm, kind, out) && k / 128 >= dg::pipe_stages_b(dg::kTiles[t].bm, dg::kTiles[t].bn, kind) &&
                               dg::pipe_instantiated(dg::kTiles[t].bm, dg::kTiles[t].bn, sfm, kind, out, 0));
@@ -116,10 +116,12 @@ Plan plan_gemm(int kind, int m, int n, int k, int groups, int m_max, int sfm, in
       const double rows_done = double(mt) * c.bm;
       cost *= 1.0 + 0.15 * (rows_done / (m > 0 ? m : 1) - 1.0);
     }
-    // dense problems that the pipelined kernel can run: a tile only the generic kernel has is
-    // slower than the area model says (measured at M = 128..256 with N = 2048..7168: the
-    // generic 64x32 tile 18.9-64.6 us against 13.1-42.4 us for the pipelined 128x128)
-    if (any_pipe && !dg::pipe_instantiated(c.bm, c.bn, sfm, kind, out, 0)) cost *= 1.6;
+    // dense and contiguous problems that the pipelined kernel can run: a tile only the generic
+    // kernel has is much slower than the area model says.  Measured: dense at M = 128..256 with
+    // N = 2048..7168, the generic 64x32 tile 18.9-64.6 us against 13.1-42.4 us for the
+    // pipelined 128x128; contiguous groups of 640 to 2688 rows, the generic 128x128 and 64x128
+    // tiles 30.1-92.3 us against 20.1-59.6 us for the pipelined 128x256.
+    if (any_pipe && !dg::pipe_instantiated(c.bm, c.bn, sfm, kind, out, 0)) cost *= 3.0;
     // masked problems stream their weights: the pipelined kernel is worth some extra tiles,
     // and a pipelined tile that holds a whole group (m_max rows) streams each weight slice
     // exactly once whatever the group's row count, while its padding fragments issue no
